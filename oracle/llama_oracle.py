@@ -1,0 +1,270 @@
+"""CPU fp64 oracle of the LLaMA pre-norm decoder block, final norm, output head
+and KV-cache decode step.
+
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and bench.py's
+cpu_baseline leg may import or call this module. The product path (the HIP
+library and its Python binding) never does; it shares no code, table or
+constant with this file.
+
+Everything is plain NumPy float64 with no intermediate rounding, written from
+the definitions on the pages:
+
+  [P1] paperfordummies.in, "LLaMA: Open and Efficient Foundation Language
+       Models" (the "explained as a diff" page), sections "The one formula",
+       "RMSNorm: LayerNorm minus the mean", "SwiGLU: a gate in the FFN ...",
+       "RoPE: rotate Q and K, leave V alone", "6.7B parameters, 1T tokens: the
+       arithmetic" and "The code".
+  [P4] chenyuan1125.github.io, "LLaMA: No Architecture Revolution, Yet It
+       Became the Open-Model Foundation", section "An Architecture Recipe
+       Without an Invention Myth" (RMSNorm-with-gain, SwiGLU and RoPE
+       equations) and "GQA Was Not an Original LLaMA Feature" (KV cache).
+
+Readings where the pages leave a step open (softmax scale, mask, head split,
+weight layout, per-head RoPE frequencies) are listed in the repository's design
+notes; each function below states the one it takes.
+
+Layouts: activations are [tokens, dim] with token = b*seq + s; head h owns
+columns [h*hd, (h+1)*hd). Weights are [out, in], so linear(x, W) = x W^T (the
+[P1] code writes x @ W with W [in, out]: the same map).
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Dict, Tuple
+
+import numpy as np
+
+
+def f64(a) -> np.ndarray:
+    """Widen a host array (or a CPU torch tensor of any float dtype) to fp64 exactly."""
+    if hasattr(a, "detach"):
+        import torch  # only for the dtype widening of torch inputs
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------- sizes
+def llama_hidden(dim: int, multiple_of: int = 256) -> int:
+    """SwiGLU hidden width: two thirds of 4*dim, truncated, then rounded up to a
+    multiple of `multiple_of` ([P1] "SwiGLU ..." and `llama_hidden` in "The code")."""
+    hidden = (2 * 4 * dim) // 3
+    return multiple_of * ((hidden + multiple_of - 1) // multiple_of)
+
+
+def count_params(dim: int, n_layers: int, hidden: int, vocab: int = 32000, bias: bool = False) -> int:
+    """Parameter count of the model ([P1] "6.7B parameters ... the arithmetic").
+
+    Per layer: four dim x dim attention matrices, three dim x hidden FFN
+    matrices and two norm gains; plus an embedding table and an untied output
+    head (vocab x dim each) and the final norm gain. With bias=True every block
+    linear gets an output bias (q, k, v, o: 4*dim; gate, up: 2*hidden; down:
+    dim) and each of the two block norms a shift (2*dim); this reading
+    reproduces the page's +1,622,016 at 7B."""
+    per_layer = 4 * dim * dim + 3 * dim * hidden + 2 * dim
+    if bias:
+        per_layer += 4 * dim + 2 * hidden + dim + 2 * dim
+    return n_layers * per_layer + 2 * vocab * dim + dim
+
+
+# --------------------------------------------------------------------------- primitives
+def rmsnorm(x: np.ndarray, g: np.ndarray | None, eps: float) -> np.ndarray:
+    """x / sqrt(mean(x^2) + eps) * g over the last axis ([P1] `rms_norm`; [P4]
+    RMSNorm equation with gain g). eps sits inside the square root."""
+    x = f64(x)
+    rms = np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    y = x / rms
+    if g is not None:
+        y = y * f64(g)
+    return y
+
+
+def layernorm(x: np.ndarray, eps: float = 0.0) -> np.ndarray:
+    """LayerNorm without affine terms, only used to pin rmsnorm on a centred vector
+    ([P1] "RMSNorm: LayerNorm minus the mean")."""
+    x = f64(x)
+    mu = x.mean(axis=-1, keepdims=True)
+    var = ((x - mu) ** 2).mean(axis=-1, keepdims=True)
+    return (x - mu) / np.sqrt(var + eps)
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """x / (1 + e^-x) ([P1] `silu`). Written with exp of -|x| so large |x| gives
+    no overflow warning; mathematically the same function."""
+    x = f64(x)
+    e = np.exp(-np.abs(x))
+    return np.where(x >= 0, x / (1.0 + e), x * e / (1.0 + e))
+
+
+def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """y[t, o] = sum_k x[t, k] * W[o, k] (weights stored [out, in])."""
+    return f64(x) @ f64(w).T
+
+
+def rope(x: np.ndarray, positions: np.ndarray, head_dim: int, theta: float = 10000.0) -> np.ndarray:
+    """Rotary position embedding, applied per head ([P1] `rope`; [P4] RoPE).
+
+    Pair i of each head (channels 2i, 2i+1, interleaved as in [P1]'s
+    x[..., 0::2] / x[..., 1::2]) is rotated by the angle pos * theta^(-2i/hd),
+    with hd the head dimension (reading: [P1]'s `d = x.shape[-1]` is the head
+    width when x is laid out per head)."""
+    x = f64(x)
+    t, width = x.shape
+    assert width % head_dim == 0 and head_dim % 2 == 0
+    xh = x.reshape(t, width // head_dim, head_dim)
+    inv = theta ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)   # (hd/2,)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]     # (t, hd/2)
+    cos, sin = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
+    a, b = xh[..., 0::2], xh[..., 1::2]
+    out = np.empty_like(xh)
+    out[..., 0::2] = a * cos - b * sin
+    out[..., 1::2] = a * sin + b * cos
+    return out.reshape(t, width)
+
+
+def causal_attention(q, k, v, batch: int, seq: int, n_heads: int) -> np.ndarray:
+    """Scaled dot-product attention with a causal mask, per (sequence, head).
+
+    Readings: scores are q.k / sqrt(hd); key j is visible to query i iff j <= i
+    (diagonal included) and masked keys get exactly zero weight; head h owns
+    columns [h*hd, (h+1)*hd) and heads are concatenated back in that order
+    ([P1] "LLaMA is a pull request ...": the 2017 attention with a causal mask,
+    untouched)."""
+    q, k, v = f64(q), f64(k), f64(v)
+    d = q.shape[1]
+    hd = d // n_heads
+    out = np.empty_like(q)
+    mask = np.triu(np.ones((seq, seq), dtype=bool), 1)        # True above the diagonal
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for h in range(n_heads):
+            cols = slice(h * hd, (h + 1) * hd)
+            s = q[rows, cols] @ k[rows, cols].T / math.sqrt(hd)
+            s[mask] = -np.inf
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            out[rows, cols] = p @ v[rows, cols]
+    return out
+
+
+def attention_over_cache(q, k_cache, v_cache, q_pos, n_heads: int) -> np.ndarray:
+    """Attention of one query row per sequence over that sequence's cached keys
+    0..q_pos[b] (inclusive). q [B, dim]; caches [B, H, max_seq, hd]."""
+    q = f64(q)
+    B, d = q.shape
+    hd = d // n_heads
+    out = np.empty_like(q)
+    for b in range(B):
+        p_end = int(q_pos[b]) + 1
+        for h in range(n_heads):
+            kk = f64(k_cache[b, h, :p_end])
+            vv = f64(v_cache[b, h, :p_end])
+            s = kk @ q[b, h * hd:(h + 1) * hd] / math.sqrt(hd)
+            s = s - s.max()
+            p = np.exp(s)
+            p /= p.sum()
+            out[b, h * hd:(h + 1) * hd] = p @ vv
+    return out
+
+
+def swiglu_ffn(z, w_gate, w_up, w_down) -> np.ndarray:
+    """(silu(z Wg^T) * (z Wu^T)) Wd^T ([P1] `swiglu_ffn`; [P4] SwiGLU)."""
+    return linear(silu(linear(z, w_gate)) * linear(z, w_up), w_down)
+
+
+# --------------------------------------------------------------------------- block
+def block_forward(x, w: Dict[str, np.ndarray], batch: int, seq: int, n_heads: int,
+                  eps: float, theta: float = 10000.0, return_parts: bool = False):
+    """One pre-norm LLaMA block ([P1] "The one formula" and `pre_norm_block`):
+
+        h = x + Wo . CausalAttn(RoPE(Wq z), RoPE(Wk z), Wv z),  z  = RMSNorm(x; g1)
+        y = h + Wdown (SiLU(Wgate z2) * Wup z2),                 z2 = RMSNorm(h; g2)
+
+    No biases. RoPE positions are 0..seq-1 within every sequence; V is not
+    rotated ([P1] "RoPE: rotate Q and K, leave V alone")."""
+    x = f64(x)
+    d = x.shape[1]
+    hd = d // n_heads
+    pos = np.tile(np.arange(seq, dtype=np.float64), batch)
+    z = rmsnorm(x, w["attn_norm"], eps)
+    q = rope(linear(z, w["wq"]), pos, hd, theta)
+    k = rope(linear(z, w["wk"]), pos, hd, theta)
+    v = linear(z, w["wv"])
+    a = causal_attention(q, k, v, batch, seq, n_heads)
+    h = x + linear(a, w["wo"])
+    z2 = rmsnorm(h, w["ffn_norm"], eps)
+    y = h + swiglu_ffn(z2, w["w_gate"], w["w_up"], w["w_down"])
+    if return_parts:
+        return y, {"z": z, "q": q, "k": k, "v": v, "attn": a, "h": h, "z2": z2}
+    return y
+
+
+def block_step_with_cache(x, w, pos, k_cache, v_cache, n_heads: int, eps: float,
+                          theta: float = 10000.0) -> np.ndarray:
+    """One block applied to a single new token per sequence (decode).
+
+    x [B, dim] (fp64 residual). The rotated key and the value of the new token
+    are written into cache slot pos[b] of each sequence (k_cache, v_cache are
+    fp64 [B, H, max_seq, hd] and are modified in place), then the token attends
+    over slots 0..pos[b] ([P4] "GQA Was Not an Original LLaMA Feature": the
+    cache keeps keys and values of every previous token; LLaMA-1 is plain
+    multi-head attention, one KV head per query head)."""
+    x = f64(x)
+    B, d = x.shape
+    hd = d // n_heads
+    z = rmsnorm(x, w["attn_norm"], eps)
+    q = rope(linear(z, w["wq"]), pos, hd, theta)
+    k = rope(linear(z, w["wk"]), pos, hd, theta)
+    v = linear(z, w["wv"])
+    for b in range(B):
+        p = int(pos[b])
+        k_cache[b, :, p, :] = k[b].reshape(n_heads, hd)
+        v_cache[b, :, p, :] = v[b].reshape(n_heads, hd)
+    a = attention_over_cache(q, k_cache, v_cache, pos, n_heads)
+    h = x + linear(a, w["wo"])
+    z2 = rmsnorm(h, w["ffn_norm"], eps)
+    return h + swiglu_ffn(z2, w["w_gate"], w["w_up"], w["w_down"])
+
+
+def head(x, final_norm, output, eps: float) -> np.ndarray:
+    """One final RMSNorm, then the untied vocab-wide output head ([P1] "The one
+    formula": after the last block). Returns logits, no softmax."""
+    return linear(rmsnorm(x, final_norm, eps), output)
+
+
+# --------------------------------------------------------------------------- model
+LayerFn = Callable[[int], Tuple[Dict[str, np.ndarray], np.ndarray, np.ndarray]]
+
+
+def model_decode(tokens, pos, emb, get_layer: LayerFn, n_layers: int, final_norm, output,
+                 n_heads: int, eps: float, theta: float = 10000.0) -> np.ndarray:
+    """One decode step of the whole model: embedding rows of `tokens` [B], then
+    every block with its cache, then final norm and head -> logits [B, vocab].
+
+    `get_layer(l)` returns (weights, k_cache, v_cache) of layer l as fp64
+    arrays; the caches are written in place at slot pos[b]. Streaming the
+    layers through a callable keeps host memory at one layer."""
+    x = f64(emb)[np.asarray(tokens, dtype=np.int64)]
+    for l in range(n_layers):
+        w, kc, vc = get_layer(l)
+        x = block_step_with_cache(x, w, pos, kc, vc, n_heads, eps, theta)
+    return head(x, final_norm, output, eps)
+
+
+def model_forward(tokens, emb, get_layer: LayerFn, n_layers: int, final_norm, output,
+                  n_heads: int, eps: float, theta: float = 10000.0) -> np.ndarray:
+    """Prefill of the whole model over tokens [B, T] from position 0: the
+    embedding rows, every block (writing each layer's rotated keys and values
+    into cache slots 0..T-1), final norm and head -> logits [B, T, vocab]."""
+    tokens = np.asarray(tokens, dtype=np.int64)
+    B, T = tokens.shape
+    x = f64(emb)[tokens.reshape(-1)]
+    d = x.shape[1]
+    hd = d // n_heads
+    for l in range(n_layers):
+        w, kc, vc = get_layer(l)
+        y, parts = block_forward(x, w, B, T, n_heads, eps, theta, return_parts=True)
+        kc[:, :, :T, :] = parts["k"].reshape(B, T, n_heads, hd).transpose(0, 2, 1, 3)
+        vc[:, :, :T, :] = parts["v"].reshape(B, T, n_heads, hd).transpose(0, 2, 1, 3)
+        x = y
+    return head(x, final_norm, output, eps).reshape(B, T, -1)

@@ -1,0 +1,283 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix:
+printed worked examples (tests/golden/), closed forms, invariants, library
+routines for special cases, and an independent explicit-loop brute force on
+tiny inputs. No GPU."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import llama_oracle as O
+from tests import brute_force as BF
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return [ln.strip() for ln in f if ln.strip() and not ln.startswith("#")]
+
+
+# ----------------------------------------------------------------- RMSNorm
+@pytest.mark.parametrize("eps", [1e-5, 1e-6])
+def test_rmsnorm_worked_example(eps):
+    for row in _rows("rmsnorm_worked_example.txt"):
+        name, xin, want, mean = [c.strip() for c in row.split("|")]
+        x = np.array([float(v) for v in xin.split()])
+        want = np.array([float(v) for v in want.split()])
+        y = O.rmsnorm(x, None, eps) if name == "rms_norm" else O.layernorm(x, 0.0)
+        np.testing.assert_allclose(y, want, atol=5e-5)
+        assert abs(y.mean() - float(mean)) < 5e-5
+
+
+def test_rmsnorm_closed_form_and_layernorm_equivalence():
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    np.testing.assert_allclose(O.rmsnorm(x, None, 0.0), x / math.sqrt(7.5), rtol=1e-15)
+    xc = x - x.mean()
+    ln = torch.nn.functional.layer_norm(torch.tensor(xc, dtype=torch.float64), (4,), eps=0.0).numpy()
+    np.testing.assert_allclose(O.rmsnorm(xc, None, 0.0), ln, rtol=1e-14)
+    # on an uncentred vector the two differ
+    assert not np.allclose(O.rmsnorm(x, None, 0.0), O.layernorm(x))
+
+
+def test_rmsnorm_zero_row_eps():
+    assert np.all(np.isnan(O.rmsnorm(np.zeros(4), None, 0.0)))
+    np.testing.assert_array_equal(O.rmsnorm(np.zeros(4), None, 1e-5), np.zeros(4))
+
+
+def test_rmsnorm_scale_invariance_and_gain():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((3, 64))
+    g = 1 + 0.1 * rng.standard_normal(64)
+    np.testing.assert_allclose(O.rmsnorm(7.25 * x, g, 0.0), O.rmsnorm(x, g, 0.0), rtol=1e-13)
+    y = O.rmsnorm(x, g, 0.0)
+    # RMS of the un-gained output is exactly 1
+    np.testing.assert_allclose(np.sqrt(((y / g) ** 2).mean(axis=1)), 1.0, rtol=1e-13)
+
+
+# ----------------------------------------------------------------- sizes / counts
+def test_hidden_and_param_counts():
+    for row in _rows("sizes_and_param_counts.txt"):
+        f = row.split()
+        kind, vals = f[0], f[1:]
+        if kind == "hidden":
+            assert O.llama_hidden(int(vals[0])) == int(vals[1])
+        elif kind == "count_params":
+            d, L, h, want = map(int, vals)
+            assert O.count_params(d, L, h) == want
+        elif kind == "count_params_bias":
+            d, L, h, want = map(int, vals)
+            assert O.count_params(d, L, h, bias=True) == want
+            assert want - O.count_params(d, L, h) == 1622016
+        elif kind == "ffn_relu":
+            d = int(vals[0])
+            assert 2 * d * (4 * d) == int(vals[1])
+        elif kind == "ffn_swiglu":
+            d = int(vals[0])
+            assert 3 * d * O.llama_hidden(d) == int(vals[1])
+        elif kind == "ffn_swiglu_hidden_4d":
+            d = int(vals[0])
+            assert 3 * d * (4 * d) == int(vals[1])
+        elif kind == "flops_per_token_7b":
+            n = O.count_params(4096, 32, 11008)
+            assert f"{2 * n:.2e}" == "1.35e+10"
+
+
+def test_oracle_matmul_flops_match_2n_per_token():
+    """The oracle's per-token multiply-adds over all weight matrices of the 7B
+    model (blocks + head, excluding the embedding gather and the norm gains)
+    account for ~2N FLOPs/token minus the embedding table."""
+    d, L, h, V = 4096, 32, 11008, 32000
+    matmul_flops = L * 2 * (4 * d * d + 3 * d * h) + 2 * V * d
+    n = O.count_params(d, L, h, V)
+    assert matmul_flops == 2 * (n - V * d - (2 * L + 1) * d)
+
+
+# ----------------------------------------------------------------- SiLU
+def test_silu_closed_forms():
+    assert O.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.silu(np.array([1.0])), 1.0 / (1.0 + math.exp(-1.0)), rtol=1e-15)
+    np.testing.assert_allclose(O.silu(np.array([40.0])), 40.0, rtol=1e-15)
+    assert abs(O.silu(np.array([-800.0]))[0]) == 0.0
+    x = np.linspace(-30, 30, 1001)
+    np.testing.assert_allclose(O.silu(x), torch.nn.functional.silu(torch.tensor(x)).numpy(),
+                               rtol=1e-13, atol=1e-300)
+
+
+# ----------------------------------------------------------------- RoPE
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def test_rope_complex_closed_form():
+    """Pair i of a head is the complex number x[2i] + i x[2i+1] multiplied by
+    exp(i * pos * theta^(-2i/hd))."""
+    hd, H, T = 16, 3, 7
+    x = _rand((T, H * hd), 1)
+    pos = np.array([0, 1, 2, 5, 100, 1000, 2047], dtype=float)
+    y = O.rope(x, pos, hd, 10000.0)
+    z = x.reshape(T, H, hd // 2, 2)
+    zc = z[..., 0] + 1j * z[..., 1]
+    freq = np.array([10000.0 ** (-(2.0 * i) / hd) for i in range(hd // 2)])
+    rot = np.exp(1j * pos[:, None, None] * freq[None, None, :])
+    want = zc * rot
+    yc = y.reshape(T, H, hd // 2, 2)
+    np.testing.assert_allclose(yc[..., 0], want.real, atol=1e-12)
+    np.testing.assert_allclose(yc[..., 1], want.imag, atol=1e-12)
+
+
+def test_rope_invariants():
+    hd = 8
+    x = _rand((4, 2 * hd), 2)
+    np.testing.assert_array_equal(O.rope(x, np.zeros(4), hd), x)            # position 0: identity
+    y = O.rope(x, np.array([0.0, 1.0, 3.0, 2047.0]), hd)
+    pn = lambda a: np.hypot(a[:, 0::2], a[:, 1::2])
+    np.testing.assert_allclose(pn(y), pn(x), rtol=1e-13)                   # per-pair norms kept
+    # pair 0 rotates by exactly pos radians
+    for t, p in enumerate([0.0, 1.0, 3.0, 2047.0]):
+        a0 = math.atan2(x[t, 1], x[t, 0])
+        a1 = math.atan2(y[t, 1], y[t, 0])
+        assert abs(math.remainder(a1 - a0 - p, 2 * math.pi)) < 1e-9
+
+
+def test_rope_relative_offsets_golden():
+    hd = 64
+    q, k = _rand((1, hd), 3), _rand((1, hd), 4)
+
+    def score(qp, kp):
+        return float(O.rope(q, np.array([qp], float), hd)[0] @ O.rope(k, np.array([kp], float), hd)[0])
+
+    for row in _rows("rope_offsets.txt"):
+        a, b, rel = [c.strip() for c in row.split("|")]
+        (qa, ka), (qb, kb) = map(int, a.split()), map(int, b.split())
+        s1, s2 = score(qa, ka), score(qb, kb)
+        if rel == "equal":
+            assert abs(s1 - s2) < 1e-12
+        else:
+            assert abs(s1 - s2) > 1e-6
+    # (R_m q)^T (R_n k) = q^T R_(n-m) k
+    for m, n in [(3, 1), (10, 250), (2047, 0)]:
+        lhs = score(m, n)
+        rhs = float(q[0] @ O.rope(k, np.array([float(n - m)]), hd)[0])
+        assert abs(lhs - rhs) < 1e-10
+
+
+# ----------------------------------------------------------------- attention
+def test_attention_against_library_sdpa():
+    B, S, H, hd = 2, 9, 3, 8
+    q, k, v = (_rand((B * S, H * hd), s) for s in (5, 6, 7))
+    got = O.causal_attention(q, k, v, B, S, H)
+    tq = lambda a: torch.tensor(a).reshape(B, S, H, hd).transpose(1, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq(q), tq(k), tq(v), is_causal=True)
+    ref = ref.transpose(1, 2).reshape(B * S, H * hd).numpy()
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_invariants():
+    B, S, H, hd = 1, 12, 2, 8
+    q, k, v = (_rand((B * S, H * hd), s) for s in (8, 9, 10))
+    o = O.causal_attention(q, k, v, B, S, H)
+    np.testing.assert_array_equal(o[0], v[0])                               # row 0 sees only key 0
+    kk = np.tile(k[:1], (S, 1))                                             # all keys equal
+    o2 = O.causal_attention(q, kk, v, B, S, H)
+    prefix_mean = np.cumsum(v, axis=0) / np.arange(1, S + 1)[:, None]
+    np.testing.assert_allclose(o2, prefix_mean, rtol=1e-12, atol=1e-14)
+    # shifting every position by c before RoPE leaves attention unchanged
+    pos = np.arange(S, dtype=float)
+    a1 = O.causal_attention(O.rope(q, pos, hd), O.rope(k, pos, hd), v, B, S, H)
+    a2 = O.causal_attention(O.rope(q, pos + 37, hd), O.rope(k, pos + 37, hd), v, B, S, H)
+    np.testing.assert_allclose(a1, a2, rtol=1e-9, atol=1e-11)
+
+
+def test_attention_brute_force():
+    B, S, H, hd = 2, 6, 2, 4
+    q, k, v = (_rand((B * S, H * hd), s) for s in (11, 12, 13))
+    np.testing.assert_allclose(O.causal_attention(q, k, v, B, S, H),
+                               np.array(BF.attention(q.tolist(), k.tolist(), v.tolist(), B, S, H)),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_attention_over_cache_matches_causal_rows():
+    B, S, H, hd = 2, 7, 2, 4
+    q, k, v = (_rand((B * S, H * hd), s) for s in (14, 15, 16))
+    full = O.causal_attention(q, k, v, B, S, H)
+    kc = k.reshape(B, S, H, hd).transpose(0, 2, 1, 3)
+    vc = v.reshape(B, S, H, hd).transpose(0, 2, 1, 3)
+    for p in range(S):
+        rows = [b * S + p for b in range(B)]
+        got = O.attention_over_cache(q[rows], kc, vc, [p] * B, H)
+        np.testing.assert_allclose(got, full[rows], rtol=1e-12, atol=1e-13)
+
+
+# ----------------------------------------------------------------- block
+def _tiny_block(seed, d=16, H=2, hidden=48, gain_std=0.1):
+    r = np.random.default_rng(seed)
+    w = {k: 0.3 * r.standard_normal(s) for k, s in
+         [("wq", (d, d)), ("wk", (d, d)), ("wv", (d, d)), ("wo", (d, d)),
+          ("w_gate", (hidden, d)), ("w_up", (hidden, d)), ("w_down", (d, hidden))]}
+    w["attn_norm"] = 1 + gain_std * r.standard_normal(d)
+    w["ffn_norm"] = 1 + gain_std * r.standard_normal(d)
+    return w
+
+
+def test_block_brute_force():
+    B, S, d, H = 2, 5, 16, 2
+    w = _tiny_block(20, d, H)
+    x = _rand((B * S, d), 21)
+    got = O.block_forward(x, w, B, S, H, 1e-6, 10000.0)
+    want = BF.block(x.tolist(), {k: v.tolist() for k, v in w.items()}, B, S, H, 1e-6, 10000.0)
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-11, atol=1e-12)
+
+
+def test_swiglu_ffn_matches_block_ffn_branch():
+    d, hidden = 16, 48
+    w = _tiny_block(22, d)
+    z = _rand((3, d), 23)
+    got = O.swiglu_ffn(z, w["w_gate"], w["w_up"], w["w_down"])
+    g = z @ w["w_gate"].T
+    u = g / (1 + np.exp(-g)) * (z @ w["w_up"].T)
+    np.testing.assert_allclose(got, u @ w["w_down"].T, rtol=1e-12)
+
+
+def _tiny_model(seed, L=2, d=16, H=2, hidden=48, V=50, max_seq=12):
+    r = np.random.default_rng(seed)
+    layers = [_tiny_block(seed + 1 + l, d, H, hidden) for l in range(L)]
+    emb = r.standard_normal((V, d))
+    fn = 1 + 0.1 * r.standard_normal(d)
+    out = 0.3 * r.standard_normal((V, d))
+    return layers, emb, fn, out
+
+
+def test_decode_equals_prefill_last_row():
+    """Decode at position p over a cache filled by prefilling tokens 0..p-1
+    equals row p of a (p+1)-token prefill."""
+    L, d, H, hd, V, max_seq, B = 2, 16, 2, 8, 50, 12, 3
+    layers, emb, fn, out = _tiny_model(30, L, d, H, 48, V, max_seq)
+    toks = np.random.default_rng(31).integers(0, V, (B, 9))
+    caches = [(np.zeros((B, H, max_seq, hd)), np.zeros((B, H, max_seq, hd))) for _ in range(L)]
+    get = lambda l: (layers[l], caches[l][0], caches[l][1])
+    full = O.model_forward(toks, emb, get, L, fn, out, H, 1e-6)
+    caches2 = [(np.zeros((B, H, max_seq, hd)), np.zeros((B, H, max_seq, hd))) for _ in range(L)]
+    get2 = lambda l: (layers[l], caches2[l][0], caches2[l][1])
+    O.model_forward(toks[:, :8], emb, get2, L, fn, out, H, 1e-6)
+    dec = O.model_decode(toks[:, 8], np.full(B, 8), emb, get2, L, fn, out, H, 1e-6)
+    np.testing.assert_allclose(dec, full[:, 8], rtol=1e-10, atol=1e-11)
+    for l in range(L):   # the decode step wrote the same cache slot 8 as the prefill
+        np.testing.assert_allclose(caches2[l][0][:, :, :9], caches[l][0][:, :, :9], rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(caches2[l][1][:, :, :9], caches[l][1][:, :, :9], rtol=1e-10, atol=1e-12)
+
+
+def test_model_forward_is_block_stack_then_head():
+    L, d, H, V = 2, 16, 2, 50
+    layers, emb, fn, out = _tiny_model(40, L, d, H, 48, V, 12)
+    toks = np.array([[3, 7, 1, 49, 0]])
+    caches = [(np.zeros((1, H, 12, 8)), np.zeros((1, H, 12, 8))) for _ in range(L)]
+    logits = O.model_forward(toks, emb, lambda l: (layers[l], *caches[l]), L, fn, out, H, 1e-6)
+    x = emb[toks[0]]
+    for l in range(L):
+        x = np.array(BF.block(x.tolist(), {k: v.tolist() for k, v in layers[l].items()}, 1, 5, H, 1e-6, 1e4))
+    xn = np.array(BF.rmsnorm_rows(x.tolist(), fn.tolist(), 1e-6))
+    np.testing.assert_allclose(logits[0], np.array(BF.matvec_rows(xn.tolist(), out.tolist())),
+                               rtol=1e-10, atol=1e-11)
