@@ -1,0 +1,100 @@
+"""ctypes binding of libllama_mi355x.so (declared in include/llama_mi355x.h).
+
+Argument marshalling only: every computation runs inside the library's HIP
+kernels. Loading fails loudly when the library has not been built; there is no
+other implementation to fall back to.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libllama_mi355x.so")
+
+LLAMA_F32, LLAMA_BF16 = 0, 1
+LLAMA_OK = 0
+LLAMA_ERR_NULL, LLAMA_ERR_SHAPE, LLAMA_ERR_DTYPE, LLAMA_ERR_WORKSPACE = -1, -2, -3, -4
+LLAMA_ERR_POSITION, LLAMA_ERR_UNSUPPORTED, LLAMA_ERR_HIP = -5, -6, -7
+OP_CAUSAL_ATTN, OP_SWIGLU_FFN, OP_BLOCK_FORWARD, OP_MODEL_FORWARD, OP_MODEL_DECODE = 1, 2, 3, 4, 5
+
+NUM_DEFAULT = 0
+NUM_EXPLICIT = 1 << 31
+NUM_QKV_A_PAIR, NUM_QK_PAIR, NUM_V_PAIR = 1 << 0, 1 << 1, 1 << 2
+NUM_O_A_PAIR, NUM_FFN_A_PAIR, NUM_DOWN_A_PAIR = 1 << 3, 1 << 4, 1 << 5
+
+EXPORTS = (
+    "llama_hidden_dim", "llama_rmsnorm", "llama_rope", "llama_linear", "llama_causal_attn",
+    "llama_swiglu_ffn", "llama_block_forward", "llama_model_forward", "llama_model_decode",
+    "llama_workspace_size", "llama_status_string", "llama_last_error", "llama_trace_begin", "llama_trace_end",
+)
+
+
+class LlamaConfig(ctypes.Structure):
+    _fields_ = [("dim", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("hidden", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("numerics", ctypes.c_uint32)]
+
+
+class BlockWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")]
+
+
+class ModelWeights(ctypes.Structure):
+    _fields_ = [("tok_embeddings", ctypes.c_void_p), ("layers", ctypes.POINTER(BlockWeights)),
+                ("final_norm", ctypes.c_void_p), ("output", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load the library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m decoder_only_transformer_llama_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    cfgp = ctypes.POINTER(LlamaConfig)
+    sig = {
+        "llama_hidden_dim": [i32, i32],
+        "llama_rmsnorm": [i32, i32, vp, vp, vp, i64, i32, f32, vp],
+        "llama_rope": [i32, vp, vp, vp, i64, i32, i32, f32, vp],
+        "llama_linear": [i32, i32, i32, vp, vp, vp, i64, i32, i32, vp],
+        "llama_causal_attn": [i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp],
+        "llama_swiglu_ffn": [i32, i32, vp, vp, vp, vp, vp, i64, i32, i32, vp, sz, vp],
+        "llama_block_forward": [cfgp, ctypes.POINTER(BlockWeights), i32, vp, vp, i32, i32, vp, sz, vp],
+        "llama_model_forward": [cfgp, ctypes.POINTER(ModelWeights), vp, i32, i32, vp, vp, vp, vp, sz, vp],
+        "llama_model_decode": [cfgp, ctypes.POINTER(ModelWeights), vp, vp, i32, vp, vp, vp, vp, sz, vp],
+        "llama_workspace_size": [cfgp, i32, i32, i32, ctypes.POINTER(sz)],
+        "llama_status_string": [i32],
+        "llama_last_error": [],
+        "llama_trace_begin": [ctypes.POINTER(vp), i32],
+        "llama_trace_end": [],
+    }
+    for name, args in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_char_p if name in ("llama_status_string", "llama_last_error") else ctypes.c_int
+    _lib = lib
+    return lib
+
+
+class LlamaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        lib = load()
+        msg = lib.llama_status_string(status).decode()
+        if status == LLAMA_ERR_HIP:
+            msg += ": " + lib.llama_last_error().decode()
+        super().__init__(f"{what}: {msg} (status {status})")
+        self.status = status
+
+
+def check(status: int, what: str) -> None:
+    if status != LLAMA_OK:
+        raise LlamaError(status, what)

@@ -1,0 +1,737 @@
+// C-ABI entry points: host-side validation, workspace carving and the launch
+// sequence of each operation on the caller's stream. No allocation, no
+// synchronisation, no global mutable state except the per-thread text of the
+// last HIP error.
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "internal.h"
+
+using namespace llama;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+// Optional launch trace (per thread): an event recorded after every kernel.
+thread_local hipEvent_t const *g_trace_ev = nullptr;
+thread_local int g_trace_cap = 0, g_trace_n = 0;
+
+int hip_fail(hipError_t e, const char *where) {
+  g_last_error = std::string(where) + ": " + hipGetErrorString(e);
+  return LLAMA_ERR_HIP;
+}
+
+hipError_t traced(hipError_t e, hipStream_t s) {
+  if (e == hipSuccess && g_trace_ev && g_trace_n < g_trace_cap) e = hipEventRecord(g_trace_ev[g_trace_n++], s);
+  return e;
+}
+
+// Every kernel launch goes through HIP_TRY with the launch stream named `s`.
+#define HIP_TRY(expr, where)                              \
+  do {                                                    \
+    hipError_t e_ = traced((expr), s);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, where);     \
+  } while (0)
+
+bool dtype_ok(int d) { return d == LLAMA_F32 || d == LLAMA_BF16; }
+size_t dsize(int d) { return d == LLAMA_F32 ? 4 : 2; }
+
+// Bump allocator over the caller's workspace (256-byte aligned pieces).
+struct Carve {
+  char *base;
+  size_t off = 0;
+  explicit Carve(void *b) : base((char *)b) {}
+  template <class T>
+  T *take(size_t count) {
+    off = (off + 255) & ~(size_t)255;
+    T *p = base ? (T *)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+uint32_t numerics_of(const llama_config *c) {
+  if (c->numerics & LLAMA_NUM_EXPLICIT) return c->numerics;
+  return LLAMA_NUM_QK_PAIR | LLAMA_NUM_V_PAIR | LLAMA_NUM_O_A_PAIR;
+}
+
+int round_up(int v, int m) { return (v + m - 1) / m * m; }
+
+// ------------------------------------------------------------------ validation
+int check_block_cfg(const llama_config *c, int batch, int seq) {
+  if (!c) return LLAMA_ERR_NULL;
+  if (!dtype_ok(c->dtype)) return LLAMA_ERR_DTYPE;
+  if (c->dim <= 0 || c->n_heads <= 0 || c->hidden <= 0 || batch <= 0 || seq <= 0) return LLAMA_ERR_SHAPE;
+  if (c->dim % c->n_heads) return LLAMA_ERR_SHAPE;
+  const int hd = c->dim / c->n_heads;
+  if (hd != 64 && hd != 128) return LLAMA_ERR_UNSUPPORTED;
+  if (!(c->norm_eps >= 0.f) || !(c->rope_theta > 0.f)) return LLAMA_ERR_SHAPE;
+  if ((int64_t)batch * seq > (1 << 24)) return LLAMA_ERR_SHAPE;
+  if (c->dtype == LLAMA_BF16) {
+    if (c->dim % 256 || c->hidden % 128) return LLAMA_ERR_UNSUPPORTED;
+  }
+  return LLAMA_OK;
+}
+
+int check_block_w(const llama_block_weights *w) {
+  if (!w) return LLAMA_ERR_NULL;
+  if (!w->attn_norm || !w->wq || !w->wk || !w->wv || !w->wo || !w->ffn_norm || !w->w_gate || !w->w_up ||
+      !w->w_down)
+    return LLAMA_ERR_NULL;
+  return LLAMA_OK;
+}
+
+int check_model_cfg(const llama_config *c, int batch, int seq) {
+  int st = check_block_cfg(c, batch, seq);
+  if (st) return st;
+  if (c->n_layers <= 0 || c->vocab <= 0 || c->max_seq <= 0) return LLAMA_ERR_SHAPE;
+  if (c->dtype != LLAMA_BF16) return LLAMA_ERR_UNSUPPORTED;
+  return LLAMA_OK;
+}
+
+int check_model_w(const llama_config *c, const llama_model_weights *w) {
+  if (!w || !w->tok_embeddings || !w->layers || !w->final_norm || !w->output) return LLAMA_ERR_NULL;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const int st = check_block_w(&w->layers[l]);
+    if (st) return st;
+  }
+  return LLAMA_OK;
+}
+
+// ------------------------------------------------------------------ workspace layouts
+struct BlockWs {
+  float2 *rope_tab;
+  uint16_t *qh, *ql, *kh, *kl, *vth, *vtl, *a_hi, *a_lo, *u_hi, *u_lo;
+  float *h;
+  // fp32 path
+  float *z, *q, *k, *v, *att, *gate, *up;
+};
+
+int vt_stride_of(int seq) { return round_up(seq, 64); }
+
+BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq) {
+  BlockWs b{};
+  const int64_t n = (int64_t)batch * seq;
+  const int d = c->dim, hd = d / c->n_heads;
+  if (c->dtype == LLAMA_BF16) {
+    b.rope_tab = cv.take<float2>((size_t)seq * hd / 2);
+    b.qh = cv.take<uint16_t>(n * d);
+    b.ql = cv.take<uint16_t>(n * d);
+    b.kh = cv.take<uint16_t>(n * d);
+    b.kl = cv.take<uint16_t>(n * d);
+    const size_t vt = (size_t)batch * d * vt_stride_of(seq);
+    b.vth = cv.take<uint16_t>(vt);
+    b.vtl = cv.take<uint16_t>(vt);
+    b.a_hi = cv.take<uint16_t>(n * d);
+    b.a_lo = cv.take<uint16_t>(n * d);
+    b.h = cv.take<float>(n * d);
+    b.u_hi = cv.take<uint16_t>(n * c->hidden);
+    b.u_lo = cv.take<uint16_t>(n * c->hidden);
+  } else {
+    b.z = cv.take<float>(n * d);
+    b.q = cv.take<float>(n * d);
+    b.k = cv.take<float>(n * d);
+    b.v = cv.take<float>(n * d);
+    b.att = cv.take<float>(n * d);
+    b.h = cv.take<float>(n * d);
+    b.gate = cv.take<float>(n * c->hidden);
+    b.up = cv.take<float>(n * c->hidden);
+  }
+  return b;
+}
+
+struct DecodeWs {
+  float *x, *h, *rstd, *q, *part, *o_part, *ml;
+  uint16_t *ag_hi, *ag_lo;
+  float2 *rope_tab;
+};
+
+constexpr int kDecChunk = 256;
+
+void gemv_split(int N, int K, int &splits, int &k_chunk) {
+  const int n_wg = (N + 127) / 128;
+  const int ksteps = K / 64;
+  int s = std::max(1, std::min(ksteps, (512 + n_wg - 1) / n_wg));
+  const int per = (ksteps + s - 1) / s;
+  k_chunk = per * 64;
+  splits = (K + k_chunk - 1) / k_chunk;
+}
+
+size_t dec_part_floats(const llama_config *c, int batch) {
+  const int d = c->dim, h = c->hidden;
+  const int NK[5][2] = {{3 * d, d}, {d, d}, {2 * h, d}, {d, h}, {c->vocab, d}};
+  size_t mx = 0;
+  for (int i = 0; i < 5; ++i) {
+    int sp, kc;
+    gemv_split(NK[i][0], NK[i][1], sp, kc);
+    mx = std::max(mx, (size_t)sp * batch * NK[i][0]);
+  }
+  return mx;
+}
+
+DecodeWs carve_decode(Carve &cv, const llama_config *c, int batch) {
+  DecodeWs w{};
+  const int d = c->dim, hd = d / c->n_heads;
+  const int n_chunks = (c->max_seq + kDecChunk - 1) / kDecChunk;
+  w.x = cv.take<float>((size_t)batch * d);
+  w.h = cv.take<float>((size_t)batch * d);
+  w.rstd = cv.take<float>(batch);
+  w.q = cv.take<float>((size_t)batch * d);
+  w.part = cv.take<float>(dec_part_floats(c, batch));
+  w.o_part = cv.take<float>((size_t)batch * c->n_heads * n_chunks * hd);
+  w.ml = cv.take<float>((size_t)batch * c->n_heads * n_chunks * 2);
+  const int wmax = std::max(d, c->hidden);
+  w.ag_hi = cv.take<uint16_t>((size_t)batch * wmax);
+  w.ag_lo = cv.take<uint16_t>((size_t)batch * wmax);
+  w.rope_tab = cv.take<float2>((size_t)batch * hd / 2);
+  return w;
+}
+
+size_t ws_bytes_of(const llama_config *c, int op, int batch, int seq) {
+  Carve cv(nullptr);
+  const int64_t n = (int64_t)batch * seq;
+  switch (op) {
+    case LLAMA_OP_CAUSAL_ATTN: {
+      const int d = c->dim;
+      if (c->dtype == LLAMA_BF16) {
+        for (int i = 0; i < 4; ++i) cv.take<uint16_t>(n * d);
+        const size_t vt = (size_t)batch * d * vt_stride_of(seq);
+        cv.take<uint16_t>(vt);
+        cv.take<uint16_t>(vt);
+      } else {
+        cv.take<float>(n * d);
+      }
+      break;
+    }
+    case LLAMA_OP_SWIGLU_FFN:
+      if (c->dtype == LLAMA_BF16) {
+        cv.take<uint16_t>(n * c->hidden);
+        cv.take<uint16_t>(n * c->hidden);
+      } else {
+        cv.take<float>(n * c->hidden);
+        cv.take<float>(n * c->hidden);
+      }
+      break;
+    case LLAMA_OP_BLOCK_FORWARD:
+      carve_block(cv, c, batch, seq);
+      break;
+    case LLAMA_OP_MODEL_FORWARD:
+      cv.take<float>(n * c->dim);
+      cv.take<float>(n * c->dim);
+      carve_block(cv, c, batch, seq);
+      break;
+    case LLAMA_OP_MODEL_DECODE:
+      carve_decode(cv, c, batch);
+      break;
+    default:
+      return 0;
+  }
+  return cv.off + 256;
+}
+
+// ------------------------------------------------------------------ block launch sequences
+int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype, const void *x, float *y,
+               int batch, int seq, const BlockWs &b, uint16_t *kcache, uint16_t *vcache, int max_seq,
+               hipStream_t s) {
+  const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq;
+  const uint32_t num = numerics_of(c);
+  const int vts = vt_stride_of(seq);
+  HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");
+
+  GemmArgs q{};
+  q.M = M;
+  q.N = 3 * d;
+  q.K = d;
+  q.A = x;
+  q.lda = d;
+  q.gain = (const uint16_t *)w->attn_norm;
+  q.eps = c->norm_eps;
+  q.b_mode = BMODE_CONCAT3;
+  q.B0 = (const uint16_t *)w->wq;
+  q.B1 = (const uint16_t *)w->wk;
+  q.B2 = (const uint16_t *)w->wv;
+  q.n_seg = d;
+  q.qh = b.qh;
+  q.ql = b.ql;
+  q.kh = b.kh;
+  q.kl = b.kl;
+  q.vth = b.vth;
+  q.vtl = b.vtl;
+  q.rope_tab = b.rope_tab;
+  q.seq = seq;
+  q.n_heads = H;
+  q.head_dim = hd;
+  q.dim = d;
+  q.vt_stride = vts;
+  q.kcache = kcache;
+  q.vcache = vcache;
+  q.max_seq = max_seq;
+  const GemmKey kq{256, x_dtype == LLAMA_F32 ? ASRC_F32 : ASRC_BF16, (num & LLAMA_NUM_QKV_A_PAIR) ? 1 : 0, 1,
+                   EPI_QKV};
+  HIP_TRY(gemm_launch(kq, q, s), "qkv projection");
+
+  AttnArgs at{};
+  at.qh = b.qh;
+  at.ql = b.ql;
+  at.kh = b.kh;
+  at.kl = b.kl;
+  at.vth = b.vth;
+  at.vtl = b.vtl;
+  at.o = b.a_hi;
+  at.o_lo = (num & LLAMA_NUM_O_A_PAIR) ? b.a_lo : nullptr;
+  at.o_f32 = 0;
+  at.batch = batch;
+  at.seq = seq;
+  at.n_heads = H;
+  at.head_dim = hd;
+  at.dim = d;
+  at.vt_stride = vts;
+  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  HIP_TRY(attn_prefill_launch(at, (num & LLAMA_NUM_QK_PAIR) ? 1 : 0, (num & LLAMA_NUM_V_PAIR) ? 1 : 0, s),
+          "attention");
+
+  const bool opair = num & LLAMA_NUM_O_A_PAIR;
+  GemmArgs o{};
+  o.M = M;
+  o.N = d;
+  o.K = d;
+  o.A = b.a_hi;
+  o.A_lo = b.a_lo;
+  o.lda = d;
+  o.b_mode = BMODE_PLAIN;
+  o.B0 = (const uint16_t *)w->wo;
+  o.C = b.h;
+  o.ldc = d;
+  o.R = x;
+  o.r_f32 = x_dtype == LLAMA_F32;
+  const GemmKey ko{128, opair ? ASRC_BF16PAIR : ASRC_BF16, opair ? 1 : 0, 0, EPI_RESID};
+  HIP_TRY(gemm_launch(ko, o, s), "output projection");
+
+  const bool dpair = num & LLAMA_NUM_DOWN_A_PAIR;
+  GemmArgs f{};
+  f.M = M;
+  f.N = 2 * c->hidden;
+  f.K = d;
+  f.A = b.h;
+  f.lda = d;
+  f.gain = (const uint16_t *)w->ffn_norm;
+  f.eps = c->norm_eps;
+  f.b_mode = BMODE_GATEUP;
+  f.B0 = (const uint16_t *)w->w_gate;
+  f.B1 = (const uint16_t *)w->w_up;
+  f.C = b.u_hi;
+  f.C_lo = dpair ? b.u_lo : nullptr;
+  f.ldc = c->hidden;
+  const GemmKey kf{256, ASRC_F32, (num & LLAMA_NUM_FFN_A_PAIR) ? 1 : 0, 1, EPI_SILU};
+  HIP_TRY(gemm_launch(kf, f, s), "gate/up projection");
+
+  GemmArgs dn{};
+  dn.M = M;
+  dn.N = d;
+  dn.K = c->hidden;
+  dn.A = b.u_hi;
+  dn.A_lo = b.u_lo;
+  dn.lda = c->hidden;
+  dn.b_mode = BMODE_PLAIN;
+  dn.B0 = (const uint16_t *)w->w_down;
+  dn.C = y;
+  dn.ldc = d;
+  dn.R = b.h;
+  dn.r_f32 = 1;
+  const GemmKey kd{128, dpair ? ASRC_BF16PAIR : ASRC_BF16, dpair ? 1 : 0, 0, EPI_RESID};
+  HIP_TRY(gemm_launch(kd, dn, s), "down projection");
+  return LLAMA_OK;
+}
+
+int block_f32(const llama_config *c, const llama_block_weights *w, const float *x, float *y, int batch,
+              int seq, const BlockWs &b, hipStream_t s) {
+  const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq, hid = c->hidden;
+  HIP_TRY(rmsnorm_launch(1, 1, x, w->attn_norm, b.z, M, d, c->norm_eps, s), "rmsnorm");
+  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->wq, b.q, nullptr, M, d, d, s), "q projection");
+  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->wk, b.k, nullptr, M, d, d, s), "k projection");
+  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->wv, b.v, nullptr, M, d, d, s), "v projection");
+  HIP_TRY(rope_launch(1, b.q, b.q, nullptr, M, H, hd, c->rope_theta, seq, s), "rope q");
+  HIP_TRY(rope_launch(1, b.k, b.k, nullptr, M, H, hd, c->rope_theta, seq, s), "rope k");
+  HIP_TRY(attn_f32_launch(b.q, b.k, b.v, b.att, batch, seq, H, hd, s), "attention");
+  HIP_TRY(gemm_f32_launch(b.att, (const float *)w->wo, b.h, x, M, d, d, s), "output projection");
+  HIP_TRY(rmsnorm_launch(1, 1, b.h, w->ffn_norm, b.z, M, d, c->norm_eps, s), "rmsnorm");
+  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->w_gate, b.gate, nullptr, M, hid, d, s), "gate");
+  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->w_up, b.up, nullptr, M, hid, d, s), "up");
+  HIP_TRY(silu_mul_f32_launch(b.gate, b.up, b.gate, (int64_t)M * hid, s), "silu");
+  HIP_TRY(gemm_f32_launch(b.gate, (const float *)w->w_down, y, b.h, M, d, hid, s), "down projection");
+  return LLAMA_OK;
+}
+
+}  // namespace
+
+// ====================================================================== C ABI
+extern "C" {
+
+int llama_hidden_dim(int dim, int multiple_of) {
+  if (dim <= 0 || multiple_of <= 0) return -1;
+  const long long hidden = (2LL * 4 * dim) / 3;
+  return (int)(multiple_of * ((hidden + multiple_of - 1) / multiple_of));
+}
+
+const char *llama_status_string(int st) {
+  switch (st) {
+    case LLAMA_OK: return "ok";
+    case LLAMA_ERR_NULL: return "null pointer argument";
+    case LLAMA_ERR_SHAPE: return "invalid or inconsistent size";
+    case LLAMA_ERR_DTYPE: return "unsupported dtype";
+    case LLAMA_ERR_WORKSPACE: return "workspace missing or too small";
+    case LLAMA_ERR_POSITION: return "position or sequence length exceeds max_seq";
+    case LLAMA_ERR_UNSUPPORTED: return "shape or mode not implemented by this build";
+    case LLAMA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char *llama_last_error(void) { return g_last_error.c_str(); }
+
+int llama_trace_begin(void *const *events, int capacity) {
+  if (!events && capacity > 0) return LLAMA_ERR_NULL;
+  if (capacity < 0) return LLAMA_ERR_SHAPE;
+  g_trace_ev = (hipEvent_t const *)events;
+  g_trace_cap = capacity;
+  g_trace_n = 0;
+  return LLAMA_OK;
+}
+
+int llama_trace_end(void) {
+  const int n = g_trace_n;
+  g_trace_ev = nullptr;
+  g_trace_cap = 0;
+  g_trace_n = 0;
+  return n;
+}
+
+int llama_workspace_size(const llama_config *c, int op, int batch, int seq, size_t *bytes) {
+  if (!c || !bytes) return LLAMA_ERR_NULL;
+  int st = LLAMA_OK;
+  switch (op) {
+    case LLAMA_OP_CAUSAL_ATTN:
+    case LLAMA_OP_SWIGLU_FFN:
+      if (!dtype_ok(c->dtype)) return LLAMA_ERR_DTYPE;
+      if (c->dim <= 0 || batch <= 0 || seq <= 0 || (op == LLAMA_OP_SWIGLU_FFN && c->hidden <= 0))
+        return LLAMA_ERR_SHAPE;
+      break;
+    case LLAMA_OP_BLOCK_FORWARD:
+      st = check_block_cfg(c, batch, seq);
+      break;
+    case LLAMA_OP_MODEL_FORWARD:
+      st = check_model_cfg(c, batch, seq);
+      if (!st && seq > c->max_seq) st = LLAMA_ERR_POSITION;
+      break;
+    case LLAMA_OP_MODEL_DECODE:
+      st = check_model_cfg(c, batch, 1);
+      if (!st && batch > 32) st = LLAMA_ERR_UNSUPPORTED;
+      break;
+    default:
+      return LLAMA_ERR_UNSUPPORTED;
+  }
+  if (st) return st;
+  *bytes = ws_bytes_of(c, op, batch, seq);
+  return LLAMA_OK;
+}
+
+int llama_rmsnorm(int in_dtype, int out_dtype, const void *x, const void *g, void *y, int64_t rows, int dim,
+                  float eps, void *stream) {
+  if (!x || !y) return LLAMA_ERR_NULL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LLAMA_ERR_DTYPE;
+  if (rows < 0 || dim <= 0) return LLAMA_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(rmsnorm_launch(in_dtype == LLAMA_F32, out_dtype == LLAMA_F32, x, g, y, rows, dim, eps, s),
+          "llama_rmsnorm");
+  return LLAMA_OK;
+}
+
+int llama_rope(int dtype, const void *x, void *y, const int32_t *positions, int64_t tokens, int n_heads,
+               int head_dim, float theta, void *stream) {
+  if (!x || !y || !positions) return LLAMA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LLAMA_ERR_DTYPE;
+  if (tokens < 0 || n_heads <= 0 || head_dim <= 0 || (head_dim & 1) || !(theta > 0.f)) return LLAMA_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(rope_launch(dtype == LLAMA_F32, x, y, positions, tokens, n_heads, head_dim, theta, 0, s), "llama_rope");
+  return LLAMA_OK;
+}
+
+int llama_linear(int x_dtype, int w_dtype, int y_dtype, const void *x, const void *w, void *y, int64_t rows,
+                 int n, int k, void *stream) {
+  if (!x || !w || !y) return LLAMA_ERR_NULL;
+  if (!dtype_ok(x_dtype) || !dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return LLAMA_ERR_DTYPE;
+  if (rows <= 0 || n <= 0 || k <= 0 || rows > (1 << 24)) return LLAMA_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (w_dtype == LLAMA_F32) {
+    if (x_dtype != LLAMA_F32 || y_dtype != LLAMA_F32) return LLAMA_ERR_DTYPE;
+    HIP_TRY(gemm_f32_launch((const float *)x, (const float *)w, (float *)y, nullptr, (int)rows, n, k, s),
+            "llama_linear");
+    return LLAMA_OK;
+  }
+  if (k % 64) return LLAMA_ERR_SHAPE;
+  GemmArgs a{};
+  a.M = (int)rows;
+  a.N = n;
+  a.K = k;
+  a.A = x;
+  a.lda = k;
+  a.b_mode = BMODE_PLAIN;
+  a.B0 = (const uint16_t *)w;
+  a.C = y;
+  a.c_f32 = y_dtype == LLAMA_F32;
+  a.ldc = n;
+  const GemmKey key{128, x_dtype == LLAMA_F32 ? ASRC_F32 : ASRC_BF16, x_dtype == LLAMA_F32 ? 1 : 0, 0,
+                    EPI_STORE};
+  HIP_TRY(gemm_launch(key, a, s), "llama_linear");
+  return LLAMA_OK;
+}
+
+int llama_causal_attn(int in_dtype, int out_dtype, const void *q, const void *k, const void *v, void *o,
+                      int batch, int seq, int n_heads, int head_dim, void *ws, size_t ws_bytes,
+                      void *stream) {
+  if (!q || !k || !v || !o) return LLAMA_ERR_NULL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LLAMA_ERR_DTYPE;
+  if (batch <= 0 || seq <= 0 || n_heads <= 0 || head_dim <= 0) return LLAMA_ERR_SHAPE;
+  if (head_dim != 64 && head_dim != 128) return LLAMA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * seq > (1 << 24)) return LLAMA_ERR_SHAPE;
+  llama_config c{};
+  c.dim = n_heads * head_dim;
+  c.n_heads = n_heads;
+  c.dtype = in_dtype;
+  const size_t need = ws_bytes_of(&c, LLAMA_OP_CAUSAL_ATTN, batch, seq);
+  if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv(ws);
+  const int64_t n = (int64_t)batch * seq;
+  const int d = c.dim;
+  if (in_dtype == LLAMA_F32) {
+    float *of = out_dtype == LLAMA_F32 ? (float *)o : cv.take<float>(n * d);
+    HIP_TRY(attn_f32_launch((const float *)q, (const float *)k, (const float *)v, of, batch, seq, n_heads,
+                            head_dim, s),
+            "llama_causal_attn");
+    if (out_dtype != LLAMA_F32) HIP_TRY(convert_launch(1, 0, of, o, n * d, s), "llama_causal_attn");
+    return LLAMA_OK;
+  }
+  uint16_t *qh = cv.take<uint16_t>(n * d), *ql = cv.take<uint16_t>(n * d);
+  uint16_t *kh = cv.take<uint16_t>(n * d), *kl = cv.take<uint16_t>(n * d);
+  const int vts = vt_stride_of(seq);
+  const size_t vt = (size_t)batch * d * vts;
+  uint16_t *vth = cv.take<uint16_t>(vt), *vtl = cv.take<uint16_t>(vt);
+  HIP_TRY(attn_pack_launch(0, q, k, v, qh, ql, kh, kl, vth, vtl, batch, seq, n_heads, head_dim, vts, s),
+          "llama_causal_attn");
+  AttnArgs at{};
+  at.qh = qh;
+  at.ql = ql;
+  at.kh = kh;
+  at.kl = kl;
+  at.vth = vth;
+  at.vtl = vtl;
+  at.o = o;
+  at.o_f32 = out_dtype == LLAMA_F32;
+  at.batch = batch;
+  at.seq = seq;
+  at.n_heads = n_heads;
+  at.head_dim = head_dim;
+  at.dim = d;
+  at.vt_stride = vts;
+  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
+  // bf16 inputs are exact, so their lo parts are zero: one pass each.
+  HIP_TRY(attn_prefill_launch(at, 0, 0, s), "llama_causal_attn");
+  return LLAMA_OK;
+}
+
+int llama_swiglu_ffn(int in_dtype, int out_dtype, const void *z, const void *w_gate, const void *w_up,
+                     const void *w_down, void *y, int64_t tokens, int dim, int hidden, void *ws,
+                     size_t ws_bytes, void *stream) {
+  if (!z || !w_gate || !w_up || !w_down || !y) return LLAMA_ERR_NULL;
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype)) return LLAMA_ERR_DTYPE;
+  if (tokens <= 0 || dim <= 0 || hidden <= 0 || tokens > (1 << 24)) return LLAMA_ERR_SHAPE;
+  llama_config c{};
+  c.dim = dim;
+  c.hidden = hidden;
+  c.dtype = in_dtype;
+  const size_t need = ws_bytes_of(&c, LLAMA_OP_SWIGLU_FFN, (int)tokens, 1);
+  if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv(ws);
+  const int M = (int)tokens;
+  if (in_dtype == LLAMA_F32) {
+    if (out_dtype != LLAMA_F32) return LLAMA_ERR_DTYPE;
+    float *g = cv.take<float>((size_t)M * hidden), *u = cv.take<float>((size_t)M * hidden);
+    HIP_TRY(gemm_f32_launch((const float *)z, (const float *)w_gate, g, nullptr, M, hidden, dim, s), "gate");
+    HIP_TRY(gemm_f32_launch((const float *)z, (const float *)w_up, u, nullptr, M, hidden, dim, s), "up");
+    HIP_TRY(silu_mul_f32_launch(g, u, g, (int64_t)M * hidden, s), "silu");
+    HIP_TRY(gemm_f32_launch(g, (const float *)w_down, (float *)y, nullptr, M, dim, hidden, s), "down");
+    return LLAMA_OK;
+  }
+  if (dim % 64 || hidden % 128) return LLAMA_ERR_UNSUPPORTED;
+  uint16_t *uh = cv.take<uint16_t>((size_t)M * hidden), *ul = cv.take<uint16_t>((size_t)M * hidden);
+  GemmArgs f{};
+  f.M = M;
+  f.N = 2 * hidden;
+  f.K = dim;
+  f.A = z;
+  f.lda = dim;
+  f.b_mode = BMODE_GATEUP;
+  f.B0 = (const uint16_t *)w_gate;
+  f.B1 = (const uint16_t *)w_up;
+  f.C = uh;
+  f.C_lo = ul;
+  f.ldc = hidden;
+  HIP_TRY(gemm_launch(GemmKey{256, ASRC_BF16, 0, 0, EPI_SILU}, f, s), "gate/up projection");
+  GemmArgs dn{};
+  dn.M = M;
+  dn.N = dim;
+  dn.K = hidden;
+  dn.A = uh;
+  dn.A_lo = ul;
+  dn.lda = hidden;
+  dn.b_mode = BMODE_PLAIN;
+  dn.B0 = (const uint16_t *)w_down;
+  dn.C = y;
+  dn.c_f32 = out_dtype == LLAMA_F32;
+  dn.ldc = dim;
+  HIP_TRY(gemm_launch(GemmKey{128, ASRC_BF16PAIR, 1, 0, EPI_STORE}, dn, s), "down projection");
+  return LLAMA_OK;
+}
+
+int llama_block_forward(const llama_config *c, const llama_block_weights *w, int x_dtype, const void *x,
+                        float *y, int batch, int seq, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_block_cfg(c, batch, seq);
+  if (st) return st;
+  if ((st = check_block_w(w))) return st;
+  if (!x || !y) return LLAMA_ERR_NULL;
+  if (!dtype_ok(x_dtype)) return LLAMA_ERR_DTYPE;
+  if (c->dtype == LLAMA_F32 && x_dtype != LLAMA_F32) return LLAMA_ERR_DTYPE;
+  const size_t need = ws_bytes_of(c, LLAMA_OP_BLOCK_FORWARD, batch, seq);
+  if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
+  Carve cv(ws);
+  const BlockWs b = carve_block(cv, c, batch, seq);
+  hipStream_t s = (hipStream_t)stream;
+  if (c->dtype == LLAMA_F32) return block_f32(c, w, (const float *)x, y, batch, seq, b, s);
+  return block_bf16(c, w, x_dtype, x, y, batch, seq, b, nullptr, nullptr, 0, s);
+}
+
+int llama_model_forward(const llama_config *c, const llama_model_weights *w, const int32_t *tokens, int batch,
+                        int seq, void *k_cache, void *v_cache, float *logits, void *ws, size_t ws_bytes,
+                        void *stream) {
+  int st = check_model_cfg(c, batch, seq);
+  if (st) return st;
+  if ((st = check_model_w(c, w))) return st;
+  if (!tokens || !k_cache || !v_cache || !logits) return LLAMA_ERR_NULL;
+  if (seq > c->max_seq) return LLAMA_ERR_POSITION;
+  const size_t need = ws_bytes_of(c, LLAMA_OP_MODEL_FORWARD, batch, seq);
+  if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t n = (int64_t)batch * seq;
+  const int d = c->dim, hd = d / c->n_heads;
+  Carve cv(ws);
+  float *xa = cv.take<float>(n * d), *xb = cv.take<float>(n * d);
+  const BlockWs b = carve_block(cv, c, batch, seq);
+  HIP_TRY(embed_launch(0, w->tok_embeddings, tokens, n, d, c->vocab, xa, s), "embedding");
+  const size_t layer_elems = (size_t)batch * c->n_heads * c->max_seq * hd;
+  for (int l = 0; l < c->n_layers; ++l) {
+    st = block_bf16(c, &w->layers[l], LLAMA_F32, xa, xb, batch, seq, b,
+                    (uint16_t *)k_cache + l * layer_elems, (uint16_t *)v_cache + l * layer_elems, c->max_seq, s);
+    if (st) return st;
+    std::swap(xa, xb);
+  }
+  GemmArgs hd_{};
+  hd_.M = (int)n;
+  hd_.N = c->vocab;
+  hd_.K = d;
+  hd_.A = xa;
+  hd_.lda = d;
+  hd_.gain = (const uint16_t *)w->final_norm;
+  hd_.eps = c->norm_eps;
+  hd_.b_mode = BMODE_PLAIN;
+  hd_.B0 = (const uint16_t *)w->output;
+  hd_.C = logits;
+  hd_.c_f32 = 1;
+  hd_.ldc = c->vocab;
+  HIP_TRY(gemm_launch(GemmKey{256, ASRC_F32, 1, 1, EPI_STORE}, hd_, s), "output head");
+  return LLAMA_OK;
+}
+
+int llama_model_decode(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                       const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits, void *ws,
+                       size_t ws_bytes, void *stream) {
+  int st = check_model_cfg(c, batch, 1);
+  if (st) return st;
+  if (batch > 32) return LLAMA_ERR_UNSUPPORTED;
+  if ((st = check_model_w(c, w))) return st;
+  if (!tokens || !pos || !k_cache || !v_cache || !logits) return LLAMA_ERR_NULL;
+  const size_t need = ws_bytes_of(c, LLAMA_OP_MODEL_DECODE, batch, 1);
+  if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = c->dim, hd = d / c->n_heads;
+  Carve cv(ws);
+  const DecodeWs dw = carve_decode(cv, c, batch);
+  DecodeArgs da{};
+  da.batch = batch;
+  da.dim = d;
+  da.n_heads = c->n_heads;
+  da.head_dim = hd;
+  da.hidden = c->hidden;
+  da.max_seq = c->max_seq;
+  da.vocab = c->vocab;
+  da.eps = c->norm_eps;
+  da.pos = pos;
+  da.rope_tab = dw.rope_tab;
+  const int n_chunks = (c->max_seq + kDecChunk - 1) / kDecChunk;
+  const size_t layer_elems = (size_t)batch * c->n_heads * c->max_seq * hd;
+
+  HIP_TRY(rope_table_pos_launch(dw.rope_tab, pos, batch, hd, c->rope_theta, c->max_seq, s), "rope table");
+  HIP_TRY(dec_embed_norm_launch(da, (const uint16_t *)w->tok_embeddings, tokens,
+                                (const uint16_t *)w->layers[0].attn_norm, dw.x, dw.rstd, dw.ag_hi, dw.ag_lo, s),
+          "embedding");
+  auto gemv = [&](int N, int K, int mode, const void *b0, const void *b1, const void *b2, int &splits) {
+    GemvArgs g{};
+    int kc;
+    gemv_split(N, K, splits, kc);
+    g.M = batch;
+    g.N = N;
+    g.K = K;
+    g.k_chunk = kc;
+    g.splits = splits;
+    g.A_hi = dw.ag_hi;
+    g.A_lo = dw.ag_lo;
+    g.b_mode = mode;
+    g.B0 = (const uint16_t *)b0;
+    g.B1 = (const uint16_t *)b1;
+    g.B2 = (const uint16_t *)b2;
+    g.n_seg = d;
+    g.part = dw.part;
+    return gemv_launch(g, s);
+  };
+  for (int l = 0; l < c->n_layers; ++l) {
+    const llama_block_weights &L = w->layers[l];
+    uint16_t *kc = (uint16_t *)k_cache + l * layer_elems, *vc = (uint16_t *)v_cache + l * layer_elems;
+    int sp;
+    HIP_TRY(gemv(3 * d, d, BMODE_CONCAT3, L.wq, L.wk, L.wv, sp), "qkv projection");
+    HIP_TRY(dec_qkv_combine_launch(da, dw.part, sp, dw.rstd, dw.q, kc, vc, s), "qkv combine");
+    HIP_TRY(dec_attn_launch(da, dw.q, kc, vc, kDecChunk, n_chunks, dw.o_part, dw.ml, s), "attention");
+    HIP_TRY(dec_attn_combine_launch(da, dw.o_part, dw.ml, n_chunks, dw.ag_hi, dw.ag_lo, s), "attention merge");
+    HIP_TRY(gemv(d, d, BMODE_PLAIN, L.wo, nullptr, nullptr, sp), "output projection");
+    HIP_TRY(dec_resid_norm_launch(da, dw.x, dw.part, sp, (const uint16_t *)L.ffn_norm, dw.h, dw.rstd, dw.ag_hi,
+                                  dw.ag_lo, s),
+            "residual");
+    HIP_TRY(gemv(2 * c->hidden, d, BMODE_GATEUP, L.w_gate, L.w_up, nullptr, sp), "gate/up projection");
+    HIP_TRY(dec_gateup_combine_launch(da, dw.part, sp, dw.rstd, dw.ag_hi, dw.ag_lo, s), "silu");
+    HIP_TRY(gemv(d, c->hidden, BMODE_PLAIN, L.w_down, nullptr, nullptr, sp), "down projection");
+    const void *gnext = l + 1 < c->n_layers ? w->layers[l + 1].attn_norm : w->final_norm;
+    HIP_TRY(dec_resid_norm_launch(da, dw.h, dw.part, sp, (const uint16_t *)gnext, dw.x, dw.rstd, dw.ag_hi,
+                                  dw.ag_lo, s),
+            "residual");
+  }
+  int sp;
+  HIP_TRY(gemv(c->vocab, d, BMODE_PLAIN, w->output, nullptr, nullptr, sp), "output head");
+  HIP_TRY(dec_head_combine_launch(da, dw.part, sp, dw.rstd, logits, s), "head");
+  return LLAMA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Device-side helpers shared by the gfx950 kernels: bf16 conversions, the
+// hi/lo pair split, vector types of the matrix-core builtins and wavefront
+// reductions. Wavefronts are 64 lanes wide.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef uint16_t u16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define DEV __device__ __forceinline__
+
+DEV float bf2f(u16 h) { return __uint_as_float(((uint32_t)h) << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+DEV u16 f2bf(float f) {
+  __bf16 b = (__bf16)f;
+  return __builtin_bit_cast(u16, b);
+}
+
+// f = hi + lo + O(2^-16 |f|): hi = bf16(f), lo = bf16(f - hi).
+DEV void split_pair(float f, u16 &hi, u16 &lo) {
+  hi = f2bf(f);
+  lo = f2bf(f - bf2f(hi));
+}
+
+// Two packed bf16 (low half = first element) from two floats.
+DEV uint32_t pack2(float a, float b) { return (uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16); }
+
+DEV void unpack8(const u32x4 &v, float *f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(v[i] << 16);
+    f[2 * i + 1] = __uint_as_float(v[i] & 0xffff0000u);
+  }
+}
+
+DEV u32x4 pack8(const float *f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack2(f[2 * i], f[2 * i + 1]);
+  return r;
+}
+
+DEV void pack8_pair(const float *f, u32x4 &hi, u32x4 &lo) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u16 h0, l0, h1, l1;
+    split_pair(f[2 * i], h0, l0);
+    split_pair(f[2 * i + 1], h1, l1);
+    hi[i] = (uint32_t)h0 | ((uint32_t)h1 << 16);
+    lo[i] = (uint32_t)l0 | ((uint32_t)l1 << 16);
+  }
+}
+
+DEV bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+DEV f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// 1 / sqrt(mean + eps) in IEEE fp32 (correctly rounded sqrt and divide).
+DEV float rstd_of(float sumsq, int n, float eps) {
+  return 1.0f / __fsqrt_rn(sumsq / (float)n + eps);
+}
+
+// SiLU(t) = t / (1 + e^-t); e^-t overflows to +inf for very negative t and
+// the quotient is then -0, never NaN.
+DEV float silu(float t) { return t / (1.0f + expf(-t)); }
+
+// Round a workgroup count up and remap a linear workgroup id so that ids the
+// hardware sends to one XCD (id % 8) get a contiguous range of tiles.
+DEV int xcd_remap(int bid, int nb) {
+  const int per = nb / 8, rem = nb % 8;
+  const int x = bid % 8, i = bid / 8;
+  return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
+}

@@ -1,0 +1,352 @@
+// Standalone and helper kernels: RMSNorm (wavefront reduction), RoPE and its
+// cos/sin tables, attention operand packing, embedding gather, dtype
+// conversion, and the plain fp32 path used by fp32 workloads (VALU kernels).
+//
+// RMSNorm with gain: paperfordummies.in LLaMA page "RMSNorm: LayerNorm minus the
+// mean" (rms_norm in "The code") and the chenyuan1125.github.io page's RMSNorm
+// equation. RoPE: the same pages' "RoPE: rotate Q and K, leave V alone" /
+// rope() and the RoPE equation: interleaved channel pairs (2i, 2i+1) of each
+// head rotate by pos * theta^(-2i/head_dim).
+#include "common.h"
+#include "internal.h"
+
+namespace llama {
+
+// ------------------------------------------------------------------ RoPE tables
+// tab[p * hd/2 + i] = (cos, sin)(p * theta^(-2i/hd)), angles in fp64.
+__global__ void rope_table_kernel(float2 *tab, int positions, int hd, double theta) {
+  const int half = hd >> 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)positions * half) return;
+  const int p = (int)(idx / half), i = (int)(idx % half);
+  const double ang = (double)p * pow(theta, -(2.0 * i) / hd);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  tab[idx] = make_float2((float)cs, (float)sn);
+}
+
+__global__ void rope_table_pos_kernel(float2 *tab, const int32_t *pos, int n, int hd, double theta) {
+  const int half = hd >> 1;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * half) return;
+  const int b = idx / half, i = idx % half;
+  const double ang = (double)pos[b] * pow(theta, -(2.0 * i) / hd);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  tab[idx] = make_float2((float)cs, (float)sn);
+}
+
+hipError_t rope_table_launch(float2 *tab, int positions, int head_dim, float theta, hipStream_t s) {
+  const int64_t n = (int64_t)positions * (head_dim / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, tab,
+                     positions, head_dim, (double)theta);
+  return hipGetLastError();
+}
+
+hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int head_dim, float theta,
+                                 int max_seq, hipStream_t s) {
+  (void)max_seq;
+  const int tot = n * (head_dim / 2);
+  if (tot == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_pos_kernel, dim3((tot + 255) / 256), dim3(256), 0, s, tab, pos, n,
+                     head_dim, (double)theta);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ RMSNorm
+// One 64-lane wavefront per row; the sum of squares is reduced across lanes.
+template <bool IN_F32, bool OUT_F32>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, const void *g, void *y, int64_t rows,
+                                                      int dim, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  auto ld = [&](const void *p, int64_t i) -> float {
+    return IN_F32 ? ((const float *)p)[i] : bf2f(((const u16 *)p)[i]);
+  };
+  const int64_t base = row * dim;
+  float ss = 0.f;
+  for (int c = lane; c < dim; c += 64) {
+    const float v = ld(x, base + c);
+    ss += v * v;
+  }
+  ss = wave_sum(ss);
+  const float r = rstd_of(ss, dim, eps);
+  for (int c = lane; c < dim; c += 64) {
+    float v = ld(x, base + c) * r;
+    if (g) v *= ld(g, c);
+    if (OUT_F32)
+      ((float *)y)[base + c] = v;
+    else
+      ((u16 *)y)[base + c] = f2bf(v);
+  }
+}
+
+hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,
+                          int dim, float eps, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  dim3 grid((unsigned)((rows + 3) / 4));
+#define RMS_CASE(I, O)                                                                       \
+  if (!!in_f32 == I && !!out_f32 == O) {                                                     \
+    hipLaunchKernelGGL((rmsnorm_kernel<I, O>), grid, dim3(256), 0, s, x, g, y, rows, dim, eps); \
+    return hipGetLastError();                                                                \
+  }
+  RMS_CASE(true, true)
+  RMS_CASE(true, false)
+  RMS_CASE(false, true)
+  RMS_CASE(false, false)
+#undef RMS_CASE
+  return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------------------------ RoPE
+template <bool F32>
+__global__ void rope_kernel(const void *x, void *y, const int32_t *pos, int64_t tokens, int n_heads,
+                            int hd, double theta, int seq_mod) {
+  const int half = hd >> 1;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_tok = (int64_t)n_heads * half;
+  if (idx >= tokens * per_tok) return;
+  const int64_t t = idx / per_tok;
+  const int rem = (int)(idx % per_tok);
+  const int h = rem / half, i = rem % half;
+  const int p = pos ? pos[t] : (int)(t % seq_mod);
+  const double ang = (double)p * pow(theta, -(2.0 * i) / hd);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  const float c = (float)cs, sv = (float)sn;
+  const int64_t o = t * (int64_t)n_heads * hd + h * hd + 2 * i;
+  float a, b;
+  if (F32) {
+    a = ((const float *)x)[o];
+    b = ((const float *)x)[o + 1];
+  } else {
+    a = bf2f(((const u16 *)x)[o]);
+    b = bf2f(((const u16 *)x)[o + 1]);
+  }
+  const float ra = a * c - b * sv, rb = a * sv + b * c;
+  if (F32) {
+    ((float *)y)[o] = ra;
+    ((float *)y)[o + 1] = rb;
+  } else {
+    ((u16 *)y)[o] = f2bf(ra);
+    ((u16 *)y)[o + 1] = f2bf(rb);
+  }
+}
+
+hipError_t rope_launch(int f32, const void *x, void *y, const int32_t *pos, int64_t tokens, int n_heads,
+                       int head_dim, float theta, int seq_mod, hipStream_t s) {
+  const int64_t n = tokens * n_heads * (head_dim / 2);
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (f32)
+    hipLaunchKernelGGL(rope_kernel<true>, grid, dim3(256), 0, s, x, y, pos, tokens, n_heads, head_dim,
+                       (double)theta, seq_mod);
+  else
+    hipLaunchKernelGGL(rope_kernel<false>, grid, dim3(256), 0, s, x, y, pos, tokens, n_heads, head_dim,
+                       (double)theta, seq_mod);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ attention operand packing
+// q, k -> hi/lo bf16 [n, d]; v -> hi/lo bf16 transposed [b, h, hd, vt_stride].
+template <bool F32>
+__global__ void attn_pack_kernel(const void *q, const void *k, const void *v, u16 *qh, u16 *ql, u16 *kh,
+                                 u16 *kl, u16 *vth, u16 *vtl, int batch, int seq, int n_heads, int hd,
+                                 int vt_stride) {
+  const int d = n_heads * hd;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)batch * seq * d) return;
+  auto ld = [&](const void *p) -> float { return F32 ? ((const float *)p)[idx] : bf2f(((const u16 *)p)[idx]); };
+  u16 hi, lo;
+  split_pair(ld(q), hi, lo);
+  qh[idx] = hi;
+  ql[idx] = lo;
+  split_pair(ld(k), hi, lo);
+  kh[idx] = hi;
+  kl[idx] = lo;
+  split_pair(ld(v), hi, lo);
+  const int64_t tok = idx / d;
+  const int c = (int)(idx % d);
+  const int b = (int)(tok / seq), s = (int)(tok % seq);
+  const int h = c / hd, e = c % hd;
+  const int64_t o = (((int64_t)b * n_heads + h) * hd + e) * vt_stride + s;
+  vth[o] = hi;
+  vtl[o] = lo;
+}
+
+hipError_t attn_pack_launch(int in_f32, const void *q, const void *k, const void *v, uint16_t *qh,
+                            uint16_t *ql, uint16_t *kh, uint16_t *kl, uint16_t *vth, uint16_t *vtl,
+                            int batch, int seq, int n_heads, int head_dim, int vt_stride, hipStream_t s) {
+  const int64_t n = (int64_t)batch * seq * n_heads * head_dim;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (in_f32)
+    hipLaunchKernelGGL(attn_pack_kernel<true>, grid, dim3(256), 0, s, q, k, v, qh, ql, kh, kl, vth, vtl,
+                       batch, seq, n_heads, head_dim, vt_stride);
+  else
+    hipLaunchKernelGGL(attn_pack_kernel<false>, grid, dim3(256), 0, s, q, k, v, qh, ql, kh, kl, vth, vtl,
+                       batch, seq, n_heads, head_dim, vt_stride);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ embedding gather
+// x[t] = emb[tokens[t]] widened to f32; an id outside [0, vocab) gives a NaN row.
+template <bool F32>
+__global__ void embed_kernel(const void *emb, const int32_t *tokens, int64_t n, int dim, int vocab,
+                             float *x) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * dim) return;
+  const int64_t t = idx / dim;
+  const int c = (int)(idx % dim);
+  const int tok = tokens[t];
+  float v = __builtin_nanf("");
+  if (tok >= 0 && tok < vocab) {
+    const int64_t o = (int64_t)tok * dim + c;
+    v = F32 ? ((const float *)emb)[o] : bf2f(((const u16 *)emb)[o]);
+  }
+  x[idx] = v;
+}
+
+hipError_t embed_launch(int w_f32, const void *emb, const int32_t *tokens, int64_t n, int dim, int vocab,
+                        float *x, hipStream_t s) {
+  const int64_t tot = n * dim;
+  if (tot == 0) return hipSuccess;
+  const dim3 grid((unsigned)((tot + 255) / 256));
+  if (w_f32)
+    hipLaunchKernelGGL(embed_kernel<true>, grid, dim3(256), 0, s, emb, tokens, n, dim, vocab, x);
+  else
+    hipLaunchKernelGGL(embed_kernel<false>, grid, dim3(256), 0, s, emb, tokens, n, dim, vocab, x);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ dtype conversion
+__global__ void convert_kernel(int in_f32, int out_f32, const void *x, void *y, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const float v = in_f32 ? ((const float *)x)[i] : bf2f(((const u16 *)x)[i]);
+  if (out_f32)
+    ((float *)y)[i] = v;
+  else
+    ((u16 *)y)[i] = f2bf(v);
+}
+
+hipError_t convert_launch(int in_f32, int out_f32, const void *x, void *y, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(convert_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, in_f32, out_f32,
+                     x, y, n);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ fp32 path
+// C[M, N] = A[M, K] B[N, K]^T (+ R), 64x64 tiles through LDS, 4x4 outputs per thread.
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float *A, const float *B, float *C,
+                                                       const float *R, int M, int N, int K) {
+  __shared__ float As[16][65], Bs[16][65];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    for (int i = threadIdx.x; i < 64 * 16; i += 256) {
+      const int r = i / 16, c = i % 16;
+      As[c][r] = (m0 + r < M && k0 + c < K) ? A[(int64_t)(m0 + r) * K + k0 + c] : 0.f;
+      Bs[c][r] = (n0 + r < N && k0 + c < K) ? B[(int64_t)(n0 + r) * K + k0 + c] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) av[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bv[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(av[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = m0 + ty * 4 + i, n = n0 + tx * 4 + j;
+      if (m < M && n < N) {
+        const int64_t o = (int64_t)m * N + n;
+        C[o] = acc[i][j] + (R ? R[o] : 0.f);
+      }
+    }
+}
+
+hipError_t gemm_f32_launch(const float *A, const float *B, float *C, const float *R, int M, int N, int K,
+                           hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  hipLaunchKernelGGL(gemm_f32_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, A, B, C, R, M,
+                     N, K);
+  return hipGetLastError();
+}
+
+__global__ void silu_mul_kernel(const float *g, const float *u, float *out, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) out[i] = silu(g[i]) * u[i];
+}
+
+hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(silu_mul_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, g, u, out, n);
+  return hipGetLastError();
+}
+
+// Causal attention in fp32, one thread per (sequence, head, query), online softmax.
+template <int HD>
+__global__ __launch_bounds__(64) void attn_f32_kernel(const float *q, const float *k, const float *v,
+                                                      float *o, int batch, int seq, int n_heads) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= batch * n_heads * seq) return;
+  const int i = idx % seq, h = (idx / seq) % n_heads, b = idx / (seq * n_heads);
+  const int d = n_heads * HD;
+  const float *qi = q + ((int64_t)b * seq + i) * d + h * HD;
+  float qr[HD], acc[HD];
+#pragma unroll
+  for (int e = 0; e < HD; ++e) {
+    qr[e] = qi[e];
+    acc[e] = 0.f;
+  }
+  const float sc = 1.0f / sqrtf((float)HD);
+  float m = -INFINITY, l = 0.f;
+  for (int j = 0; j <= i; ++j) {
+    const float *kj = k + ((int64_t)b * seq + j) * d + h * HD;
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < HD; ++e) s = fmaf(qr[e], kj[e], s);
+    s *= sc;
+    const float mn = fmaxf(m, s);
+    const float al = expf(m - mn), p = expf(s - mn);
+    l = l * al + p;
+    const float *vj = v + ((int64_t)b * seq + j) * d + h * HD;
+#pragma unroll
+    for (int e = 0; e < HD; ++e) acc[e] = acc[e] * al + p * vj[e];
+    m = mn;
+  }
+  float *oi = o + ((int64_t)b * seq + i) * d + h * HD;
+#pragma unroll
+  for (int e = 0; e < HD; ++e) oi[e] = acc[e] / l;
+}
+
+hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float *o, int batch, int seq,
+                           int n_heads, int head_dim, hipStream_t s) {
+  const int n = batch * n_heads * seq;
+  if (n == 0) return hipSuccess;
+  const dim3 grid((n + 63) / 64);
+  if (head_dim == 64)
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, o, batch, seq, n_heads);
+  else if (head_dim == 128)
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, o, batch, seq, n_heads);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace llama

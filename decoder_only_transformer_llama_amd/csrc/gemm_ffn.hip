@@ -1,0 +1,11 @@
+// Instances of the bf16 GEMM with the SiLU(gate)*up epilogue.
+#include "gemm_kernel.h"
+
+namespace llama {
+hipError_t gemm_launch_ffn(const GemmKey &key, const GemmArgs &a, hipStream_t s) {
+  GEMM_CASE(256, ASRC_F32, 0, 1, EPI_SILU)
+  GEMM_CASE(256, ASRC_F32, 1, 1, EPI_SILU)
+  GEMM_CASE(256, ASRC_BF16, 0, 0, EPI_SILU)
+  return hipErrorInvalidValue;
+}
+}  // namespace llama

@@ -1,0 +1,21 @@
+// Instances of the bf16 GEMM with plain-store and residual-add epilogues, and
+// the dispatcher over every instance.
+#include "gemm_kernel.h"
+
+namespace llama {
+hipError_t gemm_launch_misc(const GemmKey &key, const GemmArgs &a, hipStream_t s) {
+  GEMM_CASE(128, ASRC_BF16, 0, 0, EPI_RESID)
+  GEMM_CASE(128, ASRC_BF16PAIR, 1, 0, EPI_RESID)
+  GEMM_CASE(256, ASRC_F32, 1, 1, EPI_STORE)
+  GEMM_CASE(128, ASRC_BF16, 0, 0, EPI_STORE)
+  GEMM_CASE(128, ASRC_F32, 1, 0, EPI_STORE)
+  GEMM_CASE(128, ASRC_BF16PAIR, 1, 0, EPI_STORE)
+  return hipErrorInvalidValue;
+}
+
+hipError_t gemm_launch(const GemmKey &key, const GemmArgs &a, hipStream_t s) {
+  if (key.epi == EPI_QKV) return gemm_launch_qkv(key, a, s);
+  if (key.epi == EPI_SILU) return gemm_launch_ffn(key, a, s);
+  return gemm_launch_misc(key, a, s);
+}
+}  // namespace llama

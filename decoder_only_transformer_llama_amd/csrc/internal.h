@@ -1,0 +1,129 @@
+// Host-side internal interface between the C-ABI layer (api.hip) and the
+// kernel translation units. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/llama_mi355x.h"
+
+namespace llama {
+
+// ---------------------------------------------------------------- GEMM
+// C[M, N] = A[M, K] * B[N, K]^T on bf16 matrix cores, fp32 accumulate.
+enum ASrc { ASRC_BF16 = 0, ASRC_F32 = 1, ASRC_BF16PAIR = 2 };
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_QKV = 3 };
+enum BMode { BMODE_PLAIN = 0, BMODE_CONCAT3 = 1, BMODE_GATEUP = 2 };
+
+struct GemmArgs {
+  int M, N, K;
+  const void *A;       // [M, lda] bf16 or f32 (ASRC_BF16PAIR: hi part)
+  const uint16_t *A_lo;  // ASRC_BF16PAIR: lo part, same layout
+  int64_t lda;
+  const uint16_t *gain;  // [K] bf16 (norm fold) or null
+  float eps;             // norm fold: rstd = 1/sqrt(mean(A^2) + eps), applied in the epilogue
+  int b_mode;
+  const uint16_t *B0, *B1, *B2;  // weights [rows, K] bf16
+  int n_seg;                     // BMODE_CONCAT3: rows per segment
+  // EPI_STORE / EPI_RESID / EPI_SILU outputs
+  void *C;            // f32 or bf16 (EPI_SILU: bf16 hi)
+  uint16_t *C_lo;     // EPI_SILU / EPI_STORE bf16: optional lo part
+  int c_f32;          // EPI_STORE: 1 -> f32 output, 0 -> bf16
+  int64_t ldc;
+  const void *R;      // EPI_RESID residual [M, ldc]
+  int r_f32;
+  // EPI_QKV
+  uint16_t *qh, *ql, *kh, *kl;   // [M, dim] hi/lo of rotated q and k
+  uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, seq] hi/lo of v (transposed)
+  const float2 *rope_tab;        // [seq, head_dim/2] (cos, sin)
+  int seq, n_heads, head_dim, dim;
+  int vt_stride;                 // row stride of the transposed v (>= seq, multiple of 64)
+  uint16_t *kcache, *vcache;     // optional: [batch, n_heads, max_seq, head_dim] of this layer
+  int max_seq;
+};
+
+struct GemmKey {
+  int bn, asrc, apair, norm, epi;
+};
+
+// Returns a hipError_t; hipErrorInvalidValue when no instance matches `key`.
+hipError_t gemm_launch(const GemmKey &key, const GemmArgs &a, hipStream_t s);
+hipError_t gemm_launch_qkv(const GemmKey &key, const GemmArgs &a, hipStream_t s);
+hipError_t gemm_launch_ffn(const GemmKey &key, const GemmArgs &a, hipStream_t s);
+hipError_t gemm_launch_misc(const GemmKey &key, const GemmArgs &a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  const uint16_t *qh, *ql, *kh, *kl;   // [batch*seq, dim]
+  const uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, seq]
+  void *o;                             // [batch*seq, dim] f32 or bf16 (hi)
+  uint16_t *o_lo;                      // optional lo part (bf16 output only)
+  int o_f32;
+  int batch, seq, n_heads, head_dim, dim;
+  int vt_stride;                       // row stride of v^T (>= seq, multiple of 64)
+  float scale_log2;                    // log2(e) / sqrt(head_dim)
+};
+hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, hipStream_t s);
+
+// ---------------------------------------------------------------- small kernels
+hipError_t rope_table_launch(float2 *tab, int positions, int head_dim, float theta, hipStream_t s);
+hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int head_dim, float theta,
+                                 int max_seq, hipStream_t s);
+hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,
+                          int dim, float eps, hipStream_t s);
+// pos == nullptr: the position of token t is t % seq_mod.
+hipError_t rope_launch(int f32, const void *x, void *y, const int32_t *pos, int64_t tokens, int n_heads,
+                       int head_dim, float theta, int seq_mod, hipStream_t s);
+hipError_t attn_pack_launch(int in_f32, const void *q, const void *k, const void *v, uint16_t *qh,
+                            uint16_t *ql, uint16_t *kh, uint16_t *kl, uint16_t *vth, uint16_t *vtl,
+                            int batch, int seq, int n_heads, int head_dim, int vt_stride, hipStream_t s);
+hipError_t embed_launch(int w_f32, const void *emb, const int32_t *tokens, int64_t n, int dim, int vocab,
+                        float *x, hipStream_t s);
+
+// fp32 path (small workloads, plain VALU kernels)
+hipError_t gemm_f32_launch(const float *A, const float *B, float *C, const float *R, int M, int N, int K,
+                           hipStream_t s);
+hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64_t n, hipStream_t s);
+hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float *o, int batch, int seq,
+                           int n_heads, int head_dim, hipStream_t s);
+hipError_t convert_launch(int in_f32, int out_f32, const void *x, void *y, int64_t n, hipStream_t s);
+
+// ---------------------------------------------------------------- decode
+struct GemvArgs {
+  int M, N, K, k_chunk, splits;
+  const uint16_t *A_hi, *A_lo;   // [M, K] bf16 pair
+  int b_mode;
+  const uint16_t *B0, *B1, *B2;
+  int n_seg;
+  float *part;                   // [splits, M, N]
+};
+hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
+
+struct DecodeArgs {
+  int batch, dim, n_heads, head_dim, hidden, max_seq, vocab;
+  float eps;
+  const int32_t *pos;            // [batch]
+  const float2 *rope_tab;        // [batch, head_dim/2] for pos[b]
+};
+// x[b] = emb[tok[b]] (f32), rstd[b], xg pair = x*g
+hipError_t dec_embed_norm_launch(const DecodeArgs &d, const uint16_t *emb, const int32_t *tok,
+                                 const uint16_t *g, float *x, float *rstd, uint16_t *xg_hi,
+                                 uint16_t *xg_lo, hipStream_t s);
+// q (f32), cache writes of k, v for slot pos[b]
+hipError_t dec_qkv_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *rstd,
+                                  float *q, uint16_t *kc, uint16_t *vc, hipStream_t s);
+hipError_t dec_attn_launch(const DecodeArgs &d, const float *q, const uint16_t *kc, const uint16_t *vc,
+                           int chunk, int n_chunks, float *o_part, float *ml_part, hipStream_t s);
+// out = res + sum(part); rstd of out; out*g as pair (g may be null -> no pair written)
+hipError_t dec_resid_norm_launch(const DecodeArgs &d, const float *res, const float *part, int splits,
+                                 const uint16_t *g, float *out, float *rstd, uint16_t *og_hi,
+                                 uint16_t *og_lo, hipStream_t s);
+hipError_t dec_gateup_combine_launch(const DecodeArgs &d, const float *part, int splits,
+                                     const float *rstd, uint16_t *u_hi, uint16_t *u_lo, hipStream_t s);
+hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *rstd,
+                                   float *logits, hipStream_t s);
+hipError_t dec_attn_combine_launch(const DecodeArgs &d, const float *o_part, const float *ml_part,
+                                   int n_chunks, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s);
+
+}  // namespace llama

@@ -1,0 +1,203 @@
+"""Torch-facing wrappers over the C ABI: they check tensors, allocate outputs
+and workspaces with torch (device memory only), pass raw pointers and the
+current HIP stream, and raise on a non-OK status. Every computation happens in
+libllama_mi355x.so's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+_DT = {torch.float32: L.LLAMA_F32, torch.bfloat16: L.LLAMA_BF16}
+_TORCH = {L.LLAMA_F32: torch.float32, L.LLAMA_BF16: torch.bfloat16}
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return _DT[t.dtype]
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream() -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ws(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def config(dim: int, n_heads: int, hidden: int, *, dtype: torch.dtype = torch.bfloat16, n_layers: int = 1,
+           vocab: int = 0, max_seq: int = 0, eps: float = 1e-6, theta: float = 10000.0,
+           numerics: int = L.NUM_DEFAULT) -> L.LlamaConfig:
+    return L.LlamaConfig(dim, n_heads, hidden, n_layers, vocab, max_seq, eps, theta, _DT[dtype], numerics)
+
+
+def workspace_bytes(cfg: L.LlamaConfig, op: int, batch: int, seq: int) -> int:
+    lib = L.load()
+    n = ctypes.c_size_t(0)
+    L.check(lib.llama_workspace_size(ctypes.byref(cfg), op, batch, seq, ctypes.byref(n)),
+            "llama_workspace_size")
+    return n.value
+
+
+def hidden_dim(dim: int, multiple_of: int = 256) -> int:
+    return L.load().llama_hidden_dim(dim, multiple_of)
+
+
+def rmsnorm(x: torch.Tensor, g: Optional[torch.Tensor], eps: float,
+            out_dtype: Optional[torch.dtype] = None) -> torch.Tensor:
+    _dev(x, g)
+    dim = x.shape[-1]
+    y = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    if g is not None and g.dtype != x.dtype:
+        raise TypeError("gain dtype must match x")
+    L.check(L.load().llama_rmsnorm(_dt(x), _dt(y), _p(x), _p(g), _p(y), x.numel() // dim, dim, eps, _stream()),
+            "llama_rmsnorm")
+    return y
+
+
+def rope(x: torch.Tensor, positions: torch.Tensor, n_heads: int, theta: float = 10000.0,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    _dev(x, positions)
+    if positions.dtype != torch.int32:
+        raise TypeError("positions must be int32")
+    tokens = x.shape[0]
+    head_dim = x.shape[-1] // n_heads
+    y = torch.empty_like(x) if out is None else out
+    L.check(L.load().llama_rope(_dt(x), _p(x), _p(y), _p(positions), tokens, n_heads, head_dim, theta,
+                                _stream()), "llama_rope")
+    return y
+
+
+def linear(x: torch.Tensor, w: torch.Tensor, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    _dev(x, w)
+    rows, k = x.shape
+    n = w.shape[0]
+    y = torch.empty((rows, n), dtype=out_dtype, device=x.device)
+    L.check(L.load().llama_linear(_dt(x), _dt(w), _DT[out_dtype], _p(x), _p(w), _p(y), rows, n, k, _stream()),
+            "llama_linear")
+    return y
+
+
+def causal_attn(q, k, v, batch: int, seq: int, n_heads: int,
+                out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    _dev(q, k, v)
+    d = q.shape[-1]
+    hd = d // n_heads
+    o = torch.empty((batch * seq, d), dtype=out_dtype, device=q.device)
+    cfg = config(d, n_heads, 1, dtype=q.dtype)
+    ws = _ws(workspace_bytes(cfg, L.OP_CAUSAL_ATTN, batch, seq), q.device)
+    L.check(L.load().llama_causal_attn(_dt(q), _DT[out_dtype], _p(q), _p(k), _p(v), _p(o), batch, seq, n_heads,
+                                       hd, _p(ws), ws.numel(), _stream()), "llama_causal_attn")
+    return o
+
+
+def swiglu_ffn(z, w_gate, w_up, w_down, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    _dev(z, w_gate, w_up, w_down)
+    tokens, dim = z.shape
+    hidden = w_gate.shape[0]
+    y = torch.empty((tokens, dim), dtype=out_dtype, device=z.device)
+    cfg = config(dim, 1, hidden, dtype=z.dtype)
+    ws = _ws(workspace_bytes(cfg, L.OP_SWIGLU_FFN, tokens, 1), z.device)
+    L.check(L.load().llama_swiglu_ffn(_dt(z), _DT[out_dtype], _p(z), _p(w_gate), _p(w_up), _p(w_down), _p(y),
+                                      tokens, dim, hidden, _p(ws), ws.numel(), _stream()), "llama_swiglu_ffn")
+    return y
+
+
+BLOCK_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+def block_weights_struct(w: Dict[str, torch.Tensor]) -> L.BlockWeights:
+    _dev(*[w[k] for k in BLOCK_KEYS])
+    return L.BlockWeights(*[w[k].data_ptr() for k in BLOCK_KEYS])
+
+
+class Block:
+    """A block's weights and config with a reusable workspace (no allocation per call)."""
+
+    def __init__(self, cfg: L.LlamaConfig, weights: Dict[str, torch.Tensor], batch: int, seq: int):
+        self.cfg, self.weights, self.batch, self.seq = cfg, weights, batch, seq
+        self.wstruct = block_weights_struct(weights)
+        dev = weights["wq"].device
+        self.ws = _ws(workspace_bytes(cfg, L.OP_BLOCK_FORWARD, batch, seq), dev)
+        self.y = torch.empty((batch * seq, cfg.dim), dtype=torch.float32, device=dev)
+
+    def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
+        _dev(x)
+        y = self.y if y is None else y
+        L.check(L.load().llama_block_forward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _dt(x), _p(x),
+                                             _p(y), self.batch, self.seq, _p(self.ws), self.ws.numel(), _stream()),
+                "llama_block_forward")
+        return y
+
+
+def block_forward(cfg: L.LlamaConfig, weights: Dict[str, torch.Tensor], x: torch.Tensor, batch: int,
+                  seq: int) -> torch.Tensor:
+    return Block(cfg, weights, batch, seq)(x).clone()
+
+
+class Model:
+    """Whole-model weights (device tensors) plus the host-side layer table."""
+
+    def __init__(self, cfg: L.LlamaConfig, layers: Sequence[Dict[str, torch.Tensor]],
+                 tok_embeddings: torch.Tensor, final_norm: torch.Tensor, output: torch.Tensor):
+        self.cfg = cfg
+        self.layers = list(layers)
+        self.tensors = (tok_embeddings, final_norm, output)
+        arr = (L.BlockWeights * len(self.layers))(*[block_weights_struct(w) for w in self.layers])
+        self._arr = arr
+        _dev(tok_embeddings, final_norm, output)
+        self.wstruct = L.ModelWeights(tok_embeddings.data_ptr(), ctypes.cast(arr, ctypes.POINTER(L.BlockWeights)),
+                                      final_norm.data_ptr(), output.data_ptr())
+        self._ws = {}
+
+    def workspace(self, op: int, batch: int, seq: int, device) -> torch.Tensor:
+        key = (op, batch, seq)
+        if key not in self._ws:
+            self._ws[key] = _ws(workspace_bytes(self.cfg, op, batch, seq), device)
+        return self._ws[key]
+
+    def new_cache(self, batch: int, device) -> torch.Tensor:
+        c = self.cfg
+        hd = c.dim // c.n_heads
+        return torch.zeros((c.n_layers, batch, c.n_heads, c.max_seq, hd), dtype=_TORCH[c.dtype], device=device)
+
+    def forward(self, tokens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor) -> torch.Tensor:
+        _dev(tokens, k_cache, v_cache)
+        B, T = tokens.shape
+        logits = torch.empty((B, T, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        ws = self.workspace(L.OP_MODEL_FORWARD, B, T, tokens.device)
+        L.check(L.load().llama_model_forward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(tokens), B, T,
+                                             _p(k_cache), _p(v_cache), _p(logits), _p(ws), ws.numel(), _stream()),
+                "llama_model_forward")
+        return logits
+
+    def decode(self, tokens: torch.Tensor, pos: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+               logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+        _dev(tokens, pos, k_cache, v_cache)
+        B = tokens.shape[0]
+        if logits is None:
+            logits = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        ws = self.workspace(L.OP_MODEL_DECODE, B, 1, tokens.device)
+        L.check(L.load().llama_model_decode(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(tokens), _p(pos),
+                                            B, _p(k_cache), _p(v_cache), _p(logits), _p(ws), ws.numel(), _stream()),
+                "llama_model_decode")
+        return logits

@@ -1,0 +1,229 @@
+/*
+ * llama_mi355x.h — C ABI of the MI355X (gfx950) LLaMA pre-norm decoder block
+ * forward library (libllama_mi355x.so).
+ *
+ * What is computed follows these pages:
+ *  [P1] paperfordummies.in, "LLaMA: Open and Efficient Foundation Language
+ *       Models" (explained as a diff): sections "The one formula",
+ *       "RMSNorm: LayerNorm minus the mean", "SwiGLU: a gate in the FFN, paid
+ *       for with a narrower hidden layer", "RoPE: rotate Q and K, leave V
+ *       alone", "6.7B parameters, 1T tokens: the arithmetic", "The code".
+ *  [P4] chenyuan1125.github.io, "LLaMA: No Architecture Revolution, Yet It
+ *       Became the Open-Model Foundation": section "An Architecture Recipe
+ *       Without an Invention Myth" (RMSNorm with gain g, SwiGLU, RoPE
+ *       equations) and "GQA Was Not an Original LLaMA Feature" (KV cache).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers named in the argument list are DEVICE pointers (memory the
+ *    caller allocated on the current HIP device) unless marked "host".
+ *    The library never allocates, frees or synchronises: scratch memory comes
+ *    from a caller-provided workspace whose size llama_workspace_size reports.
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *    null stream). Buffers must stay valid until the stream passes the call.
+ *  - Activations are [tokens, dim] row-major with token = b*seq + s. Head h
+ *    owns columns [h*head_dim, (h+1)*head_dim). Weights are [out, in]
+ *    row-major, so a projection is y = x W^T ([P1] writes x @ W with W
+ *    [in, out]: the same map). Norm gains are [dim] in the weight dtype.
+ *  - bf16 is IEEE binary32 truncated to its top 16 bits (round to nearest
+ *    even when the library narrows). Accumulation, softmax, norm statistics
+ *    and RoPE run in fp32.
+ *  - Every entry point returns a llama_status. Arguments are validated on the
+ *    host before anything is enqueued; a failed validation enqueues nothing.
+ *    A HIP launch error returns LLAMA_ERR_HIP and its text is kept for
+ *    llama_last_error() (per thread). No C++ exception crosses the ABI.
+ *  - Floating-point special values in the data are data: eps = 0 on an
+ *    all-zero row gives NaN, as the mathematics says ([P1] "RMSNorm ...").
+ */
+#ifndef LLAMA_MI355X_H
+#define LLAMA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { LLAMA_F32 = 0, LLAMA_BF16 = 1 } llama_dtype;
+
+typedef enum {
+  LLAMA_OK = 0,
+  LLAMA_ERR_NULL = -1,        /* a required pointer is NULL */
+  LLAMA_ERR_SHAPE = -2,       /* a size is <= 0, inconsistent, or does not fit the kernels' tiling */
+  LLAMA_ERR_DTYPE = -3,       /* unknown dtype or unsupported dtype combination */
+  LLAMA_ERR_WORKSPACE = -4,   /* workspace NULL or smaller than llama_workspace_size */
+  LLAMA_ERR_POSITION = -5,    /* a position or sequence length exceeds max_seq */
+  LLAMA_ERR_UNSUPPORTED = -6, /* valid request outside what this build implements */
+  LLAMA_ERR_HIP = -7          /* the HIP runtime reported an error; see llama_last_error */
+} llama_status;
+
+/* Operations for llama_workspace_size. */
+typedef enum {
+  LLAMA_OP_CAUSAL_ATTN = 1,
+  LLAMA_OP_SWIGLU_FFN = 2,
+  LLAMA_OP_BLOCK_FORWARD = 3,
+  LLAMA_OP_MODEL_FORWARD = 4,
+  LLAMA_OP_MODEL_DECODE = 5
+} llama_op;
+
+/* Numerics options of the bf16 path (llama_config.numerics). Weights are
+ * exact bf16 inputs; an activation operand of a bf16 matrix-core product is
+ * either rounded to bf16 or carried as an exact-to-2^-16 pair hi + lo of two
+ * bf16 values (two products, same fp32 accumulator). LLAMA_NUM_DEFAULT (0)
+ * selects the library's default set; LLAMA_NUM_EXPLICIT plus any of the bits
+ * selects exactly those pairs. */
+#define LLAMA_NUM_DEFAULT 0u
+#define LLAMA_NUM_EXPLICIT (1u << 31)
+#define LLAMA_NUM_QKV_A_PAIR (1u << 0)  /* x*g1 operand of the Q/K/V projection */
+#define LLAMA_NUM_QK_PAIR (1u << 1)     /* q and k of the attention scores (3 products) */
+#define LLAMA_NUM_V_PAIR (1u << 2)      /* v of the probability-weighted sum */
+#define LLAMA_NUM_O_A_PAIR (1u << 3)    /* attention output into the Wo projection */
+#define LLAMA_NUM_FFN_A_PAIR (1u << 4)  /* h*g2 operand of the gate/up projection */
+#define LLAMA_NUM_DOWN_A_PAIR (1u << 5) /* SiLU(gate)*up operand of the down projection */
+
+/* Model / block configuration. head_dim = dim / n_heads. */
+typedef struct llama_config {
+  int32_t dim;        /* model width d */
+  int32_t n_heads;    /* attention heads (one K/V head per query head) */
+  int32_t hidden;     /* SwiGLU hidden width (llama_hidden_dim(dim, 256) for LLaMA) */
+  int32_t n_layers;   /* blocks in the model (model entry points only) */
+  int32_t vocab;      /* embedding rows / output-head width (model entry points only) */
+  int32_t max_seq;    /* KV-cache positions per sequence (model entry points only) */
+  float norm_eps;     /* RMSNorm epsilon, inside the square root */
+  float rope_theta;   /* RoPE base (10000 for LLaMA) */
+  int32_t dtype;      /* llama_dtype of weights, gains, inputs and KV cache */
+  uint32_t numerics;  /* LLAMA_NUM_* (bf16 path only; ignored for LLAMA_F32) */
+} llama_config;
+
+/* Weights of one block, device pointers in config dtype ([P1] "The one
+ * formula"; parameter set of [P1] "6.7B parameters ..."): two norm gains
+ * [dim], wq/wk/wv/wo [dim, dim], w_gate/w_up [hidden, dim], w_down [dim, hidden]. */
+typedef struct llama_block_weights {
+  const void *attn_norm, *wq, *wk, *wv, *wo;
+  const void *ffn_norm, *w_gate, *w_up, *w_down;
+} llama_block_weights;
+
+/* Whole-model weights: token embedding [vocab, dim], `layers` is a HOST
+ * array of n_layers block-weight structs (holding device pointers), the final
+ * norm gain [dim] and the untied output head [vocab, dim]. */
+typedef struct llama_model_weights {
+  const void *tok_embeddings;
+  const llama_block_weights *layers;
+  const void *final_norm;
+  const void *output;
+} llama_model_weights;
+
+/* SwiGLU hidden width: int(2*4*dim/3) rounded up to a multiple of
+ * multiple_of ([P1] "SwiGLU ..." and llama_hidden in "The code").
+ * Host only. Returns -1 for dim <= 0 or multiple_of <= 0. */
+int llama_hidden_dim(int dim, int multiple_of);
+
+/* RMSNorm with gain ([P1] rms_norm; [P4] RMSNorm equation):
+ *   y[r, :] = x[r, :] / sqrt(mean(x[r, :]^2) + eps) * g
+ * x [rows, dim] in in_dtype; g [dim] in in_dtype, or NULL for g = 1;
+ * y [rows, dim] in out_dtype (may alias x when the dtypes match).
+ * Errors: NULL x/y, rows < 0 or dim <= 0, unknown dtypes. rows == 0 is a no-op. */
+int llama_rmsnorm(int in_dtype, int out_dtype, const void *x, const void *g, void *y,
+                  int64_t rows, int dim, float eps, void *stream);
+
+/* Rotary position embedding on each head ([P1] rope; [P4] RoPE):
+ * channels (2i, 2i+1) of every head are rotated by the angle
+ * positions[t] * theta^(-2i/head_dim), i < head_dim/2 (interleaved pairs).
+ * x, y [tokens, n_heads*head_dim] in dtype (y may alias x);
+ * positions [tokens] int32 (device). Angles are formed in fp64.
+ * Errors: NULL pointers, tokens < 0, n_heads <= 0, odd head_dim, bad dtype. */
+int llama_rope(int dtype, const void *x, void *y, const int32_t *positions, int64_t tokens,
+               int n_heads, int head_dim, float theta, void *stream);
+
+/* Projection y = x W^T (the matrix products of [P1] "The code").
+ * x [rows, k] in x_dtype (bf16 or f32); w [n, k] in w_dtype; y [rows, n] in
+ * y_dtype. bf16 weights run on the matrix cores (an f32 x is carried as a
+ * bf16 hi/lo pair); f32 weights need x_dtype f32 and run in fp32.
+ * Errors: NULL pointers, sizes <= 0, k % 64 != 0 for bf16 weights, bad dtypes. */
+int llama_linear(int x_dtype, int w_dtype, int y_dtype, const void *x, const void *w, void *y,
+                 int64_t rows, int n, int k, void *stream);
+
+/* Causal scaled-dot-product attention per (sequence, head) ([P1] "LLaMA is a
+ * pull request ...": the 2017 attention with a causal mask):
+ *   o_i = sum_{j<=i} softmax_j(q_i . k_j / sqrt(head_dim)) v_j
+ * q, k, v [batch*seq, n_heads*head_dim] in in_dtype (bf16 or f32);
+ * o [batch*seq, n_heads*head_dim] in out_dtype (f32 or bf16).
+ * ws / ws_bytes: workspace of at least llama_workspace_size(LLAMA_OP_CAUSAL_ATTN).
+ * head_dim must be 64 or 128. Errors: NULL pointers, sizes <= 0,
+ * unsupported head_dim, workspace too small, bad dtypes. */
+int llama_causal_attn(int in_dtype, int out_dtype, const void *q, const void *k, const void *v,
+                      void *o, int batch, int seq, int n_heads, int head_dim, void *ws,
+                      size_t ws_bytes, void *stream);
+
+/* SwiGLU feed-forward ([P1] swiglu_ffn; [P4] SwiGLU):
+ *   y = (SiLU(z W_gate^T) * (z W_up^T)) W_down^T,  SiLU(t) = t / (1 + e^-t)
+ * z [tokens, dim] in in_dtype; w_gate, w_up [hidden, dim] and w_down
+ * [dim, hidden] in in_dtype; y [tokens, dim] in out_dtype (f32 or bf16).
+ * bf16: dim % 64 == 0, hidden % 128 == 0. ws as llama_workspace_size(LLAMA_OP_SWIGLU_FFN)
+ * with config {dim, hidden, dtype = in_dtype} and batch*seq = tokens. */
+int llama_swiglu_ffn(int in_dtype, int out_dtype, const void *z, const void *w_gate,
+                     const void *w_up, const void *w_down, void *y, int64_t tokens, int dim,
+                     int hidden, void *ws, size_t ws_bytes, void *stream);
+
+/* One pre-norm LLaMA block ([P1] "The one formula", pre_norm_block):
+ *   h = x + Wo CausalAttn(RoPE(Wq z), RoPE(Wk z), Wv z),  z  = RMSNorm(x; attn_norm)
+ *   y = h + W_down (SiLU(W_gate z2) * W_up z2),           z2 = RMSNorm(h; ffn_norm)
+ * RoPE positions are 0..seq-1 in every sequence; V is not rotated.
+ * x [batch*seq, dim] in x_dtype (config dtype, or f32); y [batch*seq, dim] f32.
+ * Requirements: head_dim 64 or 128; bf16: dim % 256 == 0, hidden % 128 == 0.
+ * ws: llama_workspace_size(c, LLAMA_OP_BLOCK_FORWARD, batch, seq). */
+int llama_block_forward(const llama_config *c, const llama_block_weights *w, int x_dtype,
+                        const void *x, float *y, int batch, int seq, void *ws, size_t ws_bytes,
+                        void *stream);
+
+/* Whole-model prefill from an empty cache: embedding rows of tokens
+ * [batch, seq] (int32, device), n_layers blocks at positions 0..seq-1, final
+ * RMSNorm and output head ([P1] "The one formula": one final RMSNorm, then the
+ * output head). Each layer's rotated keys and values are written to cache
+ * slots 0..seq-1. k_cache, v_cache: [n_layers][batch][n_heads][max_seq][head_dim]
+ * in config dtype. logits [batch, seq, vocab] f32.
+ * bf16 configs only (LLAMA_ERR_UNSUPPORTED for f32). seq <= max_seq. */
+int llama_model_forward(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                        int batch, int seq, void *k_cache, void *v_cache, float *logits, void *ws,
+                        size_t ws_bytes, void *stream);
+
+/* One decode step ([P4] "GQA Was Not an Original LLaMA Feature": keys and
+ * values of earlier tokens are cached; LLaMA-1 has one K/V head per query
+ * head): for each sequence b, token tokens[b] at position pos[b] (int32
+ * arrays [batch], device) runs through every block, its rotated key and value
+ * are written to cache slot pos[b], attention covers slots 0..pos[b], then the
+ * final norm and head give logits [batch, vocab] f32. The caches have the
+ * layout of llama_model_forward. A pos[b] outside [0, max_seq) cannot be
+ * checked on the host: for such a row nothing is written to the cache and
+ * its logits are NaN. batch <= 32. bf16 configs only. The cache-slot write
+ * is idempotent, so a step can be re-run. */
+int llama_model_decode(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                       const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/* Workspace bytes for `op` at the given batch and seq (seq ignored for decode).
+ * Writes *bytes (host pointer). Errors as the matching entry point would report
+ * for the config and sizes. */
+int llama_workspace_size(const llama_config *c, int op, int batch, int seq, size_t *bytes);
+
+/* Static text for a status code. */
+const char *llama_status_string(int status);
+
+/* Text of the last LLAMA_ERR_HIP on the calling thread ("" if none). */
+const char *llama_last_error(void);
+
+/* Launch trace for profiling, per calling thread, off by default.
+ * llama_trace_begin(events, capacity): after every kernel the library then
+ * enqueues, it records events[i] (hipEvent_t handles the caller created;
+ * i = 0, 1, ...) on that kernel's stream, until `capacity` are used. The
+ * elapsed time between consecutive events is the duration of one kernel plus
+ * its launch gap. llama_trace_end() stops tracing and returns the number of
+ * events recorded. Errors: NULL events with capacity > 0, capacity < 0. */
+int llama_trace_begin(void *const *events, int capacity);
+int llama_trace_end(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LLAMA_MI355X_H */

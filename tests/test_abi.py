@@ -1,0 +1,128 @@
+"""The C-ABI library without a GPU: it loads, exports every entry point the
+header declares, the header compiles as C and C++, and host-side validation
+returns its status codes before anything touches the device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from decoder_only_transformer_llama_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llama_mi355x.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(llama_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_bound_entry_points():
+    assert _declared() == sorted(L.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = L.load()
+    out = subprocess.run(["nm", "-D", "--defined-only", L.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (llama_\w+)", out))
+    for name in _declared():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+@pytest.mark.parametrize("lang,compiler", [("c", "gcc"), ("c++", "g++")])
+def test_header_compiles(lang, compiler, tmp_path):
+    src = tmp_path / ("t.c" if lang == "c" else "t.cpp")
+    src.write_text('#include "llama_mi355x.h"\nint main(void){llama_config c; (void)c; return 0;}\n')
+    r = subprocess.run([compiler, "-fsyntax-only", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_struct_layout_matches_header():
+    assert ctypes.sizeof(L.LlamaConfig) == 40
+    assert ctypes.sizeof(L.BlockWeights) == 9 * 8
+    assert ctypes.sizeof(L.ModelWeights) == 4 * 8
+
+
+def test_hidden_dim_and_status_strings():
+    lib = L.load()
+    for d, h in [(256, 768), (4096, 11008), (5120, 13824), (6656, 17920), (8192, 22016)]:
+        assert lib.llama_hidden_dim(d, 256) == h
+    assert lib.llama_hidden_dim(0, 256) == -1
+    assert lib.llama_status_string(0) == b"ok"
+    assert b"workspace" in lib.llama_status_string(L.LLAMA_ERR_WORKSPACE)
+    assert lib.llama_last_error() == b""
+
+
+def _cfg(**kw):
+    base = dict(dim=4096, n_heads=32, hidden=11008, n_layers=32, vocab=32000, max_seq=2048, norm_eps=1e-6,
+                rope_theta=1e4, dtype=L.LLAMA_BF16, numerics=0)
+    base.update(kw)
+    return L.LlamaConfig(*[base[k] for k, _ in L.LlamaConfig._fields_])
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def test_workspace_size_and_validation():
+    lib = L.load()
+    n = ctypes.c_size_t()
+    c = _cfg()
+    assert lib.llama_workspace_size(ctypes.byref(c), L.OP_BLOCK_FORWARD, 1, 2048, ctypes.byref(n)) == 0
+    # q,k hi/lo, v^T hi/lo, attention out hi/lo (2 B each) + h f32 + u hi/lo + rope table
+    assert n.value >= 2048 * 4096 * (2 * 8 + 4) + 2048 * 11008 * 4
+    assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 32, 1, ctypes.byref(n)) == 0
+    assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 33, 1, ctypes.byref(n)) == \
+        L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_FORWARD, 1, 4096, ctypes.byref(n)) == \
+        L.LLAMA_ERR_POSITION
+    assert lib.llama_workspace_size(ctypes.byref(_cfg(dim=4001)), L.OP_BLOCK_FORWARD, 1, 8,
+                                    ctypes.byref(n)) == L.LLAMA_ERR_SHAPE
+    assert lib.llama_workspace_size(ctypes.byref(_cfg(n_heads=16)), L.OP_BLOCK_FORWARD, 1, 8,
+                                    ctypes.byref(n)) == L.LLAMA_ERR_UNSUPPORTED      # head_dim 256
+    assert lib.llama_workspace_size(ctypes.byref(_cfg(dtype=7)), L.OP_BLOCK_FORWARD, 1, 8,
+                                    ctypes.byref(n)) == L.LLAMA_ERR_DTYPE
+    assert lib.llama_workspace_size(None, L.OP_BLOCK_FORWARD, 1, 8, ctypes.byref(n)) == L.LLAMA_ERR_NULL
+
+
+def test_entry_points_reject_bad_arguments_before_any_launch():
+    lib = L.load()
+    c = _cfg()
+    w = L.BlockWeights(*([0x1000] * 9))
+    assert lib.llama_rmsnorm(L.LLAMA_BF16, L.LLAMA_F32, None, None, FAKE, 4, 4096, 1e-6, None) == L.LLAMA_ERR_NULL
+    assert lib.llama_rmsnorm(5, L.LLAMA_F32, FAKE, None, FAKE, 4, 4096, 1e-6, None) == L.LLAMA_ERR_DTYPE
+    assert lib.llama_rmsnorm(L.LLAMA_F32, L.LLAMA_F32, FAKE, None, FAKE, -1, 4096, 1e-6, None) == L.LLAMA_ERR_SHAPE
+    assert lib.llama_rope(L.LLAMA_F32, FAKE, FAKE, FAKE, 4, 2, 7, 1e4, None) == L.LLAMA_ERR_SHAPE   # odd head_dim
+    assert lib.llama_linear(L.LLAMA_BF16, L.LLAMA_BF16, L.LLAMA_F32, FAKE, FAKE, FAKE, 4, 64, 100, None) == \
+        L.LLAMA_ERR_SHAPE                                                                              # k % 64
+    assert lib.llama_causal_attn(L.LLAMA_BF16, L.LLAMA_F32, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 96, FAKE, 1 << 30,
+                                 None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_causal_attn(L.LLAMA_BF16, L.LLAMA_F32, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, FAKE, 16,
+                                 None) == L.LLAMA_ERR_WORKSPACE
+    assert lib.llama_swiglu_ffn(L.LLAMA_BF16, L.LLAMA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 4096, 11000, FAKE,
+                                1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_block_forward(ctypes.byref(c), ctypes.byref(w), L.LLAMA_BF16, FAKE, FAKE, 1, 16, FAKE, 16,
+                                   None) == L.LLAMA_ERR_WORKSPACE
+    assert lib.llama_block_forward(ctypes.byref(c), None, L.LLAMA_BF16, FAKE, FAKE, 1, 16, FAKE, 1 << 40,
+                                   None) == L.LLAMA_ERR_NULL
+    wn = L.BlockWeights(*([0x1000] * 8 + [0]))
+    assert lib.llama_block_forward(ctypes.byref(c), ctypes.byref(wn), L.LLAMA_BF16, FAKE, FAKE, 1, 16, FAKE,
+                                   1 << 40, None) == L.LLAMA_ERR_NULL
+    cf = _cfg(dtype=L.LLAMA_F32)
+    assert lib.llama_block_forward(ctypes.byref(cf), ctypes.byref(w), L.LLAMA_BF16, FAKE, FAKE, 1, 16, FAKE,
+                                   1 << 40, None) == L.LLAMA_ERR_DTYPE
+    layers = (L.BlockWeights * 32)(*([w] * 32))
+    mw = L.ModelWeights(0x1000, ctypes.cast(layers, ctypes.POINTER(L.BlockWeights)), 0x1000, 0x1000)
+    assert lib.llama_model_forward(ctypes.byref(c), ctypes.byref(mw), FAKE, 1, 4096, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 40, None) == L.LLAMA_ERR_POSITION
+    assert lib.llama_model_forward(ctypes.byref(cf), ctypes.byref(mw), FAKE, 1, 16, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 33, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, None, 4, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None) == L.LLAMA_ERR_NULL
+    assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE,
+                                  16, None) == L.LLAMA_ERR_WORKSPACE

@@ -1,0 +1,277 @@
+"""GPU parity: every entry point of the C-ABI library against the fp64 CPU
+oracle on the same seeded inputs.
+
+Statistic: max |gpu - oracle| / RMS(oracle output), bounded by 1e-4 for fp32
+workloads and 2e-2 for bf16 workloads (fp32 accumulation). Standalone
+attention normalises by RMS(v) instead (its output is a convex combination of
+v rows, whose own RMS shrinks with averaging). Outputs are pre-filled with NaN
+so a tile the kernels forget to write fails the comparison."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from decoder_only_transformer_llama_amd import inputs as I
+from decoder_only_transformer_llama_amd import _lib as L
+from oracle import llama_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 1e-4
+TOL_BF16 = 2e-2
+
+
+def ops():
+    from decoder_only_transformer_llama_amd import ops as _ops
+    return _ops
+
+
+def rel_err(got, want, scale=None):
+    got = got.detach().to("cpu", torch.float64).numpy() if hasattr(got, "detach") else np.asarray(got)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (got.shape, want.shape)
+    assert np.all(np.isfinite(got)), "non-finite output (unwritten or overflowed)"
+    scale = np.sqrt(np.mean(want ** 2)) if scale is None else scale
+    return float(np.max(np.abs(got - want)) / scale)
+
+
+def host(t):
+    return O.f64(t.cpu())
+
+
+def assert_bf16_rounded(got, want):
+    """Every element within half a bf16 ulp (2^-8 relative) of the fp64 value,
+    plus a small fp32-arithmetic allowance."""
+    g = got.detach().to("cpu", torch.float64).numpy()
+    err = np.abs(g - want)
+    bound = np.abs(want) * 2.0 ** -8 * (1 + 1e-3) + 1e-6 * np.sqrt(np.mean(want ** 2))
+    assert np.all(err <= bound), float(np.max(err / np.maximum(bound, 1e-300)))
+
+
+def tol_of(w):
+    return TOL_F32 if w.dtype == "f32" else TOL_BF16
+
+
+# ---------------------------------------------------------------- RMSNorm
+@pytest.mark.parametrize("dtype,out", [(torch.float32, torch.float32), (torch.bfloat16, torch.float32),
+                                       (torch.bfloat16, torch.bfloat16)])
+@pytest.mark.parametrize("rows,dim", [(1, 4), (37, 256), (2048, 4096), (5, 8192)])
+def test_rmsnorm(dtype, out, rows, dim):
+    x = I.normal((rows, dim), 900, 0, 0, dtype=dtype, device="cuda")
+    g = I.normal((dim,), 900, 0, 1, std=0.1, mean=1.0, dtype=dtype, device="cuda")
+    y = ops().rmsnorm(x, g, 1e-6, out)
+    want = O.rmsnorm(host(x), host(g), 1e-6)
+    if out == torch.bfloat16:
+        assert_bf16_rounded(y, want)
+    else:
+        assert rel_err(y, want) < 2e-6
+
+
+def test_rmsnorm_page_example_and_zero_row():
+    x = torch.tensor([[1.0, 2.0, 3.0, 4.0], [0, 0, 0, 0]], device="cuda")
+    y = ops().rmsnorm(x, None, 1e-5).cpu()
+    np.testing.assert_allclose(y[0].numpy(), [0.3651, 0.7303, 1.0954, 1.4606], atol=5e-5)
+    assert torch.all(y[1] == 0)
+    y0 = ops().rmsnorm(x, None, 0.0).cpu()
+    assert torch.all(torch.isnan(y0[1]))
+
+
+# ---------------------------------------------------------------- RoPE
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_rope(dtype):
+    T, H, hd = 300, 4, 128
+    x = I.normal((T, H * hd), 901, 0, 0, dtype=dtype, device="cuda")
+    pos = torch.randint(0, 2048, (T,), generator=torch.Generator().manual_seed(3), dtype=torch.int32).cuda()
+    y = ops().rope(x, pos, H)
+    want = O.rope(host(x), pos.cpu().numpy(), hd)
+    if dtype == torch.bfloat16:
+        assert_bf16_rounded(y, want)
+    else:
+        assert rel_err(y, want) < 2e-6
+    # in place
+    x2 = x.clone()
+    ops().rope(x2, pos, H, out=x2)
+    assert torch.equal(x2, y)
+
+
+# ---------------------------------------------------------------- projections
+@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rows,n,k", [(1, 128, 64), (300, 384, 256), (2048, 4096, 4096), (33, 1000, 512)])
+def test_linear_bf16_weights(xdt, rows, n, k):
+    x = I.normal((rows, k), 902, 0, 0, dtype=xdt, device="cuda")
+    w = I.normal((n, k), 902, 0, 1, std=0.02, dtype=torch.bfloat16, device="cuda")
+    y = ops().linear(x, w)
+    want = O.linear(host(x), host(w))
+    # bf16 x: exact operands, fp32 accumulation only; f32 x: carried as a bf16
+    # hi/lo pair (about 2^-17 relative per element)
+    assert rel_err(y, want) < (1e-5 if xdt == torch.bfloat16 else 5e-5)
+
+
+def test_linear_f32():
+    x = I.normal((70, 96), 903, 0, 0, device="cuda")
+    w = I.normal((130, 96), 903, 0, 1, std=0.02, device="cuda")
+    assert rel_err(ops().linear(x, w), O.linear(host(x), host(w))) < 5e-6
+
+
+# ---------------------------------------------------------------- attention
+@pytest.mark.parametrize("B,S,H,hd", [(1, 1, 1, 64), (2, 200, 3, 64), (1, 130, 2, 128), (1, 2048, 4, 128)])
+def test_causal_attn_bf16(B, S, H, hd):
+    w = I.Workload(904, "attn", dim=H * hd, n_heads=H, hidden=0, batch=B, seq=S, dtype="bf16")
+    q, k, v = I.qkv_inputs(w, device="cuda")
+    o = ops().causal_attn(q, k, v, B, S, H)
+    want = O.causal_attention(host(q), host(k), host(v), B, S, H)
+    assert rel_err(o, want, scale=float(np.sqrt(np.mean(host(v) ** 2)))) < TOL_BF16
+    # row 0 of every sequence/head attends to key 0 only
+    o = o.cpu().double()
+    for b in range(B):
+        np.testing.assert_allclose(o[b * S].numpy(), host(v)[b * S], rtol=0, atol=2e-2)
+
+
+def test_causal_attn_f32():
+    B, S, H, hd = 2, 70, 2, 64
+    w = I.Workload(905, "attn32", dim=H * hd, n_heads=H, hidden=0, batch=B, seq=S, dtype="f32")
+    q, k, v = I.qkv_inputs(w, device="cuda")
+    o = ops().causal_attn(q, k, v, B, S, H)
+    want = O.causal_attention(host(q), host(k), host(v), B, S, H)
+    assert rel_err(o, want, scale=float(np.sqrt(np.mean(host(v) ** 2)))) < TOL_F32
+
+
+# ---------------------------------------------------------------- SwiGLU FFN
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_swiglu_ffn(dtype):
+    T, d, h = 300, 512, 1536
+    z = I.normal((T, d), 906, 0, 0, dtype=dtype, device="cuda")
+    wg, wu, wd = (I.normal(s, 906, 0, t, std=0.02, dtype=dtype, device="cuda")
+                  for t, s in ((1, (h, d)), (2, (h, d)), (3, (d, h))))
+    y = ops().swiglu_ffn(z, wg, wu, wd)
+    want = O.swiglu_ffn(host(z), host(wg), host(wu), host(wd))
+    assert rel_err(y, want) < (TOL_F32 if dtype == torch.float32 else 5e-3)
+
+
+# ---------------------------------------------------------------- block
+def run_block(wid, numerics=L.NUM_DEFAULT, seq_slice=None):
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
+                       numerics=numerics)
+    blk = ops().Block(cfg, wt, w.batch, w.seq)
+    y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
+    blk(x, y)
+    torch.cuda.synchronize()
+    if seq_slice is None:
+        want = O.block_forward(host(x), {k: host(v) for k, v in wt.items()}, w.batch, w.seq, w.n_heads,
+                               w.eps, w.theta)
+        return y, want, w
+    b = seq_slice
+    rows = slice(b * w.seq, (b + 1) * w.seq)
+    want = O.block_forward(host(x[rows]), {k: host(v) for k, v in wt.items()}, 1, w.seq, w.n_heads,
+                           w.eps, w.theta)
+    return y[rows], want, w
+
+
+@pytest.mark.parametrize("wid", [0, 100, 103])
+def test_block_small(wid):
+    y, want, w = run_block(wid)
+    err = rel_err(y, want)
+    print(f"block {w.name}: max|d|/rms = {err:.3e}")
+    assert err < tol_of(w)
+
+
+def test_block_deterministic():
+    w = I.workload(100)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps)
+    blk = ops().Block(cfg, wt, w.batch, w.seq)
+    y1 = blk(x).clone()
+    y2 = blk(x).clone()
+    assert torch.equal(y1, y2)
+
+
+@pytest.mark.slow
+def test_block_7b_full():
+    y, want, w = run_block(1)
+    err = rel_err(y, want)
+    print(f"block {w.name}: max|d|/rms = {err:.3e}")
+    assert err < TOL_BF16
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("wid,b", [(2, 3), (3, 1)])
+def test_block_13b_65b_sampled_sequence(wid, b):
+    y, want, w = run_block(wid, seq_slice=b)
+    err = rel_err(y, want)
+    print(f"block {w.name} (sequence {b}): max|d|/rms = {err:.3e}")
+    assert err < TOL_BF16
+
+
+# ---------------------------------------------------------------- model prefill + decode
+def small_model(wid=101):
+    w = I.workload(wid)
+    layers = [I.block_weights(w, l, device="cuda") for l in range(w.n_layers)]
+    gl = I.model_globals(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, n_layers=w.n_layers, vocab=w.vocab,
+                       max_seq=w.max_seq, eps=w.eps, theta=w.theta)
+    m = ops().Model(cfg, layers, gl["tok_embeddings"], gl["final_norm"], gl["output"])
+    return w, m, layers, gl
+
+
+def test_model_prefill_then_decode():
+    w, m, layers, gl = small_model()
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    logits = m.forward(toks[:, :T].contiguous(), kc, vc)
+    pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    dec = m.decode(toks[:, T].contiguous(), pos, kc, vc)
+    torch.cuda.synchronize()
+
+    hd = w.head_dim
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    caches = [(np.zeros((B, w.n_heads, w.max_seq, hd)), np.zeros((B, w.n_heads, w.max_seq, hd)))
+              for _ in range(w.n_layers)]
+    get = lambda l: (lw[l], caches[l][0], caches[l][1])
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    want = O.model_forward(toks[:, :T].cpu().numpy(), emb, get, w.n_layers, fn, out, w.n_heads, w.eps)
+    e1 = rel_err(logits, want)
+    # the oracle continues from its own (exact) cache; the GPU's bf16 cache must agree with it
+    for l in range(w.n_layers):
+        for got, ref in ((kc[l], caches[l][0]), (vc[l], caches[l][1])):
+            g = O.f64(got.cpu())
+            assert np.max(np.abs(g[:, :, :T] - ref[:, :, :T])) < 0.02 * np.abs(ref).max()
+            assert np.all(g[:, :, T + 1:] == 0)
+    want_dec = O.model_decode(toks[:, T].cpu().numpy(), np.full(B, T), emb, get, w.n_layers, fn, out, w.n_heads,
+                              w.eps)
+    e2 = rel_err(dec, want_dec)
+    print(f"prefill logits {e1:.3e}, decode logits {e2:.3e}")
+    assert e1 < TOL_BF16 and e2 < TOL_BF16
+
+
+def test_decode_invalid_position_gives_nan_row():
+    w, m, layers, gl = small_model()
+    B = w.batch
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    toks = I.tokens(w, (B,), device="cuda")
+    pos = torch.tensor([3, w.max_seq, 5][:B], dtype=torch.int32, device="cuda")
+    before = kc.clone()
+    logits = m.decode(toks, pos, kc, vc).cpu()
+    assert torch.all(torch.isnan(logits[1])) and torch.all(torch.isfinite(logits[0]))
+    assert torch.equal(kc[:, 1], before[:, 1])   # nothing written for the bad row
+
+
+@pytest.mark.slow
+def test_model_decode_7b_sampled_sequences():
+    """Full 7B-shape decode step (batch 32, cache of 2047 positions); the oracle
+    recomputes two of the 32 sequences layer by layer."""
+    from decoder_only_transformer_llama_amd.workloads import decode_workload
+    from tests.oracle_runs import oracle_decode_rows
+    wl = decode_workload(4, "cuda")
+    logits = wl.model.decode(wl.tokens, wl.pos, wl.k_cache, wl.v_cache)
+    torch.cuda.synchronize()
+    rows = [0, 17]
+    want = oracle_decode_rows(wl, rows)
+    err = rel_err(logits[rows], want)
+    print(f"7b decode logits (rows {rows}): max|d|/rms = {err:.3e}")
+    assert err < TOL_BF16
