@@ -110,7 +110,7 @@ def bench_prefill(args, torch):
     ms = ev.elapsed_ms(0, 1) / args.steps
     torch.cuda.synchronize()
 
-    names = ["rope_table", "qkv", "attention", "o", "gate_up", "down"]
+    names = ["attn_norm", "rope_table", "qkv", "attention", "o", "ffn_norm", "gate_up", "down"]
     kms = traced_kernel_ms(_lib.load(), lambda: bw.block(bw.x), stream, len(names), max(3, args.steps // 2))
     fl = block_flops(w)
     total = sum(fl.values())
@@ -124,7 +124,7 @@ def bench_prefill(args, torch):
         "w": w, "ms": ms, "tokens_per_s": w.tokens / (ms * 1e-3),
         "block_tflops": total / (ms * 1e-3) / 1e12,
         "per_kernel": per_kernel,
-        "roofline": {"bound": "mfma", "kernel": "gemm_bf16 gate/up (norm fold + SiLU*up epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "gemm_bf16 gate/up (rstd row scale + SiLU*up epilogue)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": fl[dom]},
@@ -179,7 +179,7 @@ def bench_decode(args, torch):
     L = w.n_layers
     per_layer = ["qkv", "qkv_combine", "attention", "attn_merge", "o", "resid1", "gate_up", "silu", "down",
                  "resid2"]
-    names = ["rope_table", "embed"] + [f"{n}" for _ in range(L) for n in per_layer] + ["head", "head_combine"]
+    names = ["rope_table", "embed"] + [n for _ in range(L) for n in per_layer] + ["head", "head_combine"]
     kms = traced_kernel_ms(_lib.load(), run, stream, len(names), 2)
     agg = {}
     for n, t in zip(names, kms):

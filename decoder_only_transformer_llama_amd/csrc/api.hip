@@ -105,8 +105,8 @@ int check_model_w(const llama_config *c, const llama_model_weights *w) {
 // ------------------------------------------------------------------ workspace layouts
 struct BlockWs {
   float2 *rope_tab;
-  uint16_t *qh, *ql, *kh, *kl, *vth, *vtl, *a_hi, *a_lo, *u_hi, *u_lo;
-  float *h;
+  uint16_t *xg_hi, *xg_lo, *qh, *ql, *kh, *kl, *vth, *vtl, *a_hi, *a_lo, *u_hi, *u_lo;
+  float *h, *rstd1, *rstd2;
   // fp32 path
   float *z, *q, *k, *v, *att, *gate, *up;
 };
@@ -119,6 +119,10 @@ BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq) {
   const int d = c->dim, hd = d / c->n_heads;
   if (c->dtype == LLAMA_BF16) {
     b.rope_tab = cv.take<float2>((size_t)seq * hd / 2);
+    b.rstd1 = cv.take<float>(n);
+    b.rstd2 = cv.take<float>(n);
+    b.xg_hi = cv.take<uint16_t>(n * d);
+    b.xg_lo = cv.take<uint16_t>(n * d);
     b.qh = cv.take<uint16_t>(n * d);
     b.ql = cv.take<uint16_t>(n * d);
     b.kh = cv.take<uint16_t>(n * d);
@@ -153,10 +157,11 @@ struct DecodeWs {
 constexpr int kDecChunk = 256;
 
 void gemv_split(int N, int K, int &splits, int &k_chunk) {
-  const int n_wg = (N + 127) / 128;
+  const int per_wg = 128 * gemv_ntw(N);
+  const int n_wg = (N + per_wg - 1) / per_wg;
   const int ksteps = K / 64;
-  int s = std::max(1, std::min(ksteps, (512 + n_wg - 1) / n_wg));
-  const int per = (ksteps + s - 1) / s;
+  const int s = std::max(1, std::min(ksteps, (512 + n_wg - 1) / n_wg));
+  const int per = std::min((ksteps + s - 1) / s, kGemvMaxChunk / 64);
   k_chunk = per * 64;
   splits = (K + k_chunk - 1) / k_chunk;
 }
@@ -179,7 +184,7 @@ DecodeWs carve_decode(Carve &cv, const llama_config *c, int batch) {
   const int n_chunks = (c->max_seq + kDecChunk - 1) / kDecChunk;
   w.x = cv.take<float>((size_t)batch * d);
   w.h = cv.take<float>((size_t)batch * d);
-  w.rstd = cv.take<float>(batch);
+  w.rstd = cv.take<float>((size_t)batch * ((c->dim + 1023) / 1024));
   w.q = cv.take<float>((size_t)batch * d);
   w.part = cv.take<float>(dec_part_floats(c, batch));
   w.o_part = cv.take<float>((size_t)batch * c->n_heads * n_chunks * hd);
@@ -239,17 +244,24 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
                hipStream_t s) {
   const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq;
   const uint32_t num = numerics_of(c);
+  const bool qkv_pair = num & LLAMA_NUM_QKV_A_PAIR, ffn_pair = num & LLAMA_NUM_FFN_A_PAIR;
+  const bool opair = num & LLAMA_NUM_O_A_PAIR, dpair = num & LLAMA_NUM_DOWN_A_PAIR;
   const int vts = vt_stride_of(seq);
+
+  // z = RMSNorm(x; g1): statistic + gained operand; the rstd multiply happens in the QKV epilogue
+  HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, (const uint16_t *)w->attn_norm, M, d, c->norm_eps, b.rstd1,
+                           b.xg_hi, qkv_pair ? b.xg_lo : nullptr, s),
+          "attention norm");
   HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");
 
   GemmArgs q{};
   q.M = M;
   q.N = 3 * d;
   q.K = d;
-  q.A = x;
+  q.A = b.xg_hi;
+  q.A_lo = qkv_pair ? b.xg_lo : nullptr;
   q.lda = d;
-  q.gain = (const uint16_t *)w->attn_norm;
-  q.eps = c->norm_eps;
+  q.rstd = b.rstd1;
   q.b_mode = BMODE_CONCAT3;
   q.B0 = (const uint16_t *)w->wq;
   q.B1 = (const uint16_t *)w->wk;
@@ -270,9 +282,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.kcache = kcache;
   q.vcache = vcache;
   q.max_seq = max_seq;
-  const GemmKey kq{256, x_dtype == LLAMA_F32 ? ASRC_F32 : ASRC_BF16, (num & LLAMA_NUM_QKV_A_PAIR) ? 1 : 0, 1,
-                   EPI_QKV};
-  HIP_TRY(gemm_launch(kq, q, s), "qkv projection");
+  HIP_TRY(gemm_launch(GemmKey{256, qkv_pair, EPI_QKV}, q, s), "qkv projection");
 
   AttnArgs at{};
   at.qh = b.qh;
@@ -282,7 +292,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   at.vth = b.vth;
   at.vtl = b.vtl;
   at.o = b.a_hi;
-  at.o_lo = (num & LLAMA_NUM_O_A_PAIR) ? b.a_lo : nullptr;
+  at.o_lo = opair ? b.a_lo : nullptr;
   at.o_f32 = 0;
   at.batch = batch;
   at.seq = seq;
@@ -294,13 +304,12 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   HIP_TRY(attn_prefill_launch(at, (num & LLAMA_NUM_QK_PAIR) ? 1 : 0, (num & LLAMA_NUM_V_PAIR) ? 1 : 0, s),
           "attention");
 
-  const bool opair = num & LLAMA_NUM_O_A_PAIR;
   GemmArgs o{};
   o.M = M;
   o.N = d;
   o.K = d;
   o.A = b.a_hi;
-  o.A_lo = b.a_lo;
+  o.A_lo = opair ? b.a_lo : nullptr;
   o.lda = d;
   o.b_mode = BMODE_PLAIN;
   o.B0 = (const uint16_t *)w->wo;
@@ -308,33 +317,34 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   o.ldc = d;
   o.R = x;
   o.r_f32 = x_dtype == LLAMA_F32;
-  const GemmKey ko{128, opair ? ASRC_BF16PAIR : ASRC_BF16, opair ? 1 : 0, 0, EPI_RESID};
-  HIP_TRY(gemm_launch(ko, o, s), "output projection");
+  HIP_TRY(gemm_launch(GemmKey{128, opair, EPI_RESID}, o, s), "output projection");
 
-  const bool dpair = num & LLAMA_NUM_DOWN_A_PAIR;
+  // z2 = RMSNorm(h; g2), operand reuses the x*g1 buffers
+  HIP_TRY(norm_prep_launch(1, b.h, (const uint16_t *)w->ffn_norm, M, d, c->norm_eps, b.rstd2, b.xg_hi,
+                           ffn_pair ? b.xg_lo : nullptr, s),
+          "ffn norm");
   GemmArgs f{};
   f.M = M;
   f.N = 2 * c->hidden;
   f.K = d;
-  f.A = b.h;
+  f.A = b.xg_hi;
+  f.A_lo = ffn_pair ? b.xg_lo : nullptr;
   f.lda = d;
-  f.gain = (const uint16_t *)w->ffn_norm;
-  f.eps = c->norm_eps;
+  f.rstd = b.rstd2;
   f.b_mode = BMODE_GATEUP;
   f.B0 = (const uint16_t *)w->w_gate;
   f.B1 = (const uint16_t *)w->w_up;
   f.C = b.u_hi;
   f.C_lo = dpair ? b.u_lo : nullptr;
   f.ldc = c->hidden;
-  const GemmKey kf{256, ASRC_F32, (num & LLAMA_NUM_FFN_A_PAIR) ? 1 : 0, 1, EPI_SILU};
-  HIP_TRY(gemm_launch(kf, f, s), "gate/up projection");
+  HIP_TRY(gemm_launch(GemmKey{256, ffn_pair, EPI_SILU}, f, s), "gate/up projection");
 
   GemmArgs dn{};
   dn.M = M;
   dn.N = d;
   dn.K = c->hidden;
   dn.A = b.u_hi;
-  dn.A_lo = b.u_lo;
+  dn.A_lo = dpair ? b.u_lo : nullptr;
   dn.lda = c->hidden;
   dn.b_mode = BMODE_PLAIN;
   dn.B0 = (const uint16_t *)w->w_down;
@@ -342,8 +352,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   dn.ldc = d;
   dn.R = b.h;
   dn.r_f32 = 1;
-  const GemmKey kd{128, dpair ? ASRC_BF16PAIR : ASRC_BF16, dpair ? 1 : 0, 0, EPI_RESID};
-  HIP_TRY(gemm_launch(kd, dn, s), "down projection");
+  HIP_TRY(gemm_launch(GemmKey{128, dpair, EPI_RESID}, dn, s), "down projection");
   return LLAMA_OK;
 }
 
@@ -472,21 +481,20 @@ int llama_linear(int x_dtype, int w_dtype, int y_dtype, const void *x, const voi
             "llama_linear");
     return LLAMA_OK;
   }
+  if (x_dtype != LLAMA_BF16) return LLAMA_ERR_DTYPE;
   if (k % 64) return LLAMA_ERR_SHAPE;
   GemmArgs a{};
   a.M = (int)rows;
   a.N = n;
   a.K = k;
-  a.A = x;
+  a.A = (const uint16_t *)x;
   a.lda = k;
   a.b_mode = BMODE_PLAIN;
   a.B0 = (const uint16_t *)w;
   a.C = y;
   a.c_f32 = y_dtype == LLAMA_F32;
   a.ldc = n;
-  const GemmKey key{128, x_dtype == LLAMA_F32 ? ASRC_F32 : ASRC_BF16, x_dtype == LLAMA_F32 ? 1 : 0, 0,
-                    EPI_STORE};
-  HIP_TRY(gemm_launch(key, a, s), "llama_linear");
+  HIP_TRY(gemm_launch(GemmKey{128, 0, EPI_STORE}, a, s), "llama_linear");
   return LLAMA_OK;
 }
 
@@ -574,7 +582,7 @@ int llama_swiglu_ffn(int in_dtype, int out_dtype, const void *z, const void *w_g
   f.M = M;
   f.N = 2 * hidden;
   f.K = dim;
-  f.A = z;
+  f.A = (const uint16_t *)z;
   f.lda = dim;
   f.b_mode = BMODE_GATEUP;
   f.B0 = (const uint16_t *)w_gate;
@@ -582,7 +590,7 @@ int llama_swiglu_ffn(int in_dtype, int out_dtype, const void *z, const void *w_g
   f.C = uh;
   f.C_lo = ul;
   f.ldc = hidden;
-  HIP_TRY(gemm_launch(GemmKey{256, ASRC_BF16, 0, 0, EPI_SILU}, f, s), "gate/up projection");
+  HIP_TRY(gemm_launch(GemmKey{256, 0, EPI_SILU}, f, s), "gate/up projection");
   GemmArgs dn{};
   dn.M = M;
   dn.N = dim;
@@ -595,7 +603,7 @@ int llama_swiglu_ffn(int in_dtype, int out_dtype, const void *z, const void *w_g
   dn.C = y;
   dn.c_f32 = out_dtype == LLAMA_F32;
   dn.ldc = dim;
-  HIP_TRY(gemm_launch(GemmKey{128, ASRC_BF16PAIR, 1, 0, EPI_STORE}, dn, s), "down projection");
+  HIP_TRY(gemm_launch(GemmKey{128, 1, EPI_STORE}, dn, s), "down projection");
   return LLAMA_OK;
 }
 
@@ -640,20 +648,23 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
     if (st) return st;
     std::swap(xa, xb);
   }
+  HIP_TRY(norm_prep_launch(1, xa, (const uint16_t *)w->final_norm, n, d, c->norm_eps, b.rstd1, b.xg_hi, b.xg_lo,
+                           s),
+          "final norm");
   GemmArgs hd_{};
   hd_.M = (int)n;
   hd_.N = c->vocab;
   hd_.K = d;
-  hd_.A = xa;
+  hd_.A = b.xg_hi;
+  hd_.A_lo = b.xg_lo;
   hd_.lda = d;
-  hd_.gain = (const uint16_t *)w->final_norm;
-  hd_.eps = c->norm_eps;
+  hd_.rstd = b.rstd1;
   hd_.b_mode = BMODE_PLAIN;
   hd_.B0 = (const uint16_t *)w->output;
   hd_.C = logits;
   hd_.c_f32 = 1;
   hd_.ldc = c->vocab;
-  HIP_TRY(gemm_launch(GemmKey{256, ASRC_F32, 1, 1, EPI_STORE}, hd_, s), "output head");
+  HIP_TRY(gemm_launch(GemmKey{256, 1, EPI_STORE}, hd_, s), "output head");
   return LLAMA_OK;
 }
 

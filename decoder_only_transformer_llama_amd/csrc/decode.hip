@@ -28,15 +28,33 @@ namespace llama {
 DEV bool pos_ok(int p, int max_seq) { return p >= 0 && p < max_seq; }
 
 // ------------------------------------------------------------------ skinny GEMM
-template <int NTW>
-__global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+// Workgroup = 4 wavefronts x (NTW x 32) output columns over one K range of at
+// most KC_MAX. The activation pair for that K range sits in LDS (loaded once,
+// rows XOR-swizzled); weights stream from HBM into a DEPTH-deep ring of
+// B-operand registers, so DEPTH steps of 64 K are in flight per wavefront.
+constexpr int KC_MAX = 512;
+
+template <int NTW, int DEPTH>
+__global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
+  __shared__ u32x4 sA[2][32][KC_MAX / 8];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
-  const int nw0 = (blockIdx.x * 4 + w) * 32 * NTW;
-  if (nw0 >= a.N) return;
   const int ks = blockIdx.y * a.k_chunk;
   const int ke = min(a.K, ks + a.k_chunk);
+  const int kc8 = (ke - ks) >> 3;
 
+  // activation pair of this K range -> LDS (rows past M are zero)
+  for (int idx = tid; idx < 2 * 32 * kc8; idx += 256) {
+    const int part = idx / (32 * kc8), rem = idx % (32 * kc8);
+    const int m = rem / kc8, c = rem % kc8;
+    u32x4 v = {0, 0, 0, 0};
+    if (m < a.M) v = *(const u32x4 *)((part ? a.A_lo : a.A_hi) + (int64_t)m * a.K + ks + 8 * c);
+    sA[part][m][c ^ (m & 15)] = v;
+  }
+  __syncthreads();
+
+  const int nw0 = (blockIdx.x * 4 + w) * 32 * NTW;
+  if (nw0 >= a.N) return;
   const u16 *brow[NTW];
   bool bok[NTW];
 #pragma unroll
@@ -54,11 +72,8 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
     } else {
       p = a.B0 + (int64_t)nn * a.K;
     }
-    brow[j] = p + 32 * g;
+    brow[j] = p + ks + 32 * g;
   }
-  const bool aok = l32 < a.M;
-  const u16 *ah = a.A_hi + (int64_t)(aok ? l32 : 0) * a.K + 32 * g;
-  const u16 *al = a.A_lo + (int64_t)(aok ? l32 : 0) * a.K + 32 * g;
 
   f32x16 acc[NTW];
 #pragma unroll
@@ -66,46 +81,42 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
 
-  u32x4 cb[NTW][4], ca[4], cl[4];
-  u32x4 nbv[NTW][4], na[4], nl[4];
-  const u32x4 z = {0, 0, 0, 0};
-  auto load = [&](int kb, u32x4 (&B)[NTW][4], u32x4 (&A)[4], u32x4 (&L)[4]) {
+  // K order inside a 64-step: lane group g supplies k = 32 g + 8 q + (0..7) at
+  // matrix-core step q, identically for the activation and the weights.
+  u32x4 ring[DEPTH][NTW][4];
+  const int nit = (ke - ks) >> 6;
+  auto load = [&](u32x4 (&B)[NTW][4], int it) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) B[j][q] = bok[j] ? *(const u32x4 *)(brow[j] + kb + 8 * q) : z;
+      for (int q = 0; q < 4; ++q)
+        B[j][q] = bok[j] ? *(const u32x4 *)(brow[j] + 64 * it + 8 * q) : u32x4{0, 0, 0, 0};
+  };
+  auto compute = [&](u32x4 (&B)[NTW][4], int it) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      A[q] = aok ? *(const u32x4 *)(ah + kb + 8 * q) : z;
-      L[q] = aok ? *(const u32x4 *)(al + kb + 8 * q) : z;
-    }
-  };
-  auto compute = [&](u32x4 (&B)[NTW][4], u32x4 (&A)[4], u32x4 (&L)[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
+      const int c = (8 * it + 4 * g + q) ^ (l32 & 15);
+      const bf16x8 ah = as_bf16x8(sA[0][l32][c]);
+      const bf16x8 al = as_bf16x8(sA[1][l32][c]);
 #pragma unroll
       for (int j = 0; j < NTW; ++j) {
-        acc[j] = mfma32(as_bf16x8(A[q]), as_bf16x8(B[j][q]), acc[j]);
-        acc[j] = mfma32(as_bf16x8(L[q]), as_bf16x8(B[j][q]), acc[j]);
-      }
-  };
-
-  int kb = ks;
-  if (kb < ke) load(kb, cb, ca, cl);
-  while (kb < ke) {
-    const int kn = kb + 64;
-    if (kn < ke) load(kn, nbv, na, nl);
-    compute(cb, ca, cl);
-    if (kn < ke) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        ca[q] = na[q];
-        cl[q] = nl[q];
-#pragma unroll
-        for (int j = 0; j < NTW; ++j) cb[j][q] = nbv[j][q];
+        acc[j] = mfma32(ah, as_bf16x8(B[j][q]), acc[j]);
+        acc[j] = mfma32(al, as_bf16x8(B[j][q]), acc[j]);
       }
     }
-    kb = kn;
+  };
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d)
+    if (d < nit) load(ring[d], d);
+  for (int it0 = 0; it0 < nit; it0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int it = it0 + d;
+      if (it < nit) {
+        compute(ring[d], it);
+        if (it + DEPTH < nit) load(ring[d], it + DEPTH);
+      }
+    }
   }
 
   float *out = a.part + (int64_t)blockIdx.y * a.M * a.N;
@@ -121,11 +132,17 @@ __global__ __launch_bounds__(256) void gemv_kernel(const GemvArgs a) {
   }
 }
 
+int gemv_ntw(int N) { return N > 8192 ? 2 : 1; }
+
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t s) {
-  constexpr int NTW = 1;
-  const int per_wg = 4 * 32 * NTW;
+  if (a.k_chunk > KC_MAX || a.k_chunk % 64 || a.K % 64 || a.M > 32) return hipErrorInvalidValue;
+  const int ntw = gemv_ntw(a.N);
+  const int per_wg = 4 * 32 * ntw;
   dim3 grid((a.N + per_wg - 1) / per_wg, a.splits);
-  hipLaunchKernelGGL(gemv_kernel<NTW>, grid, dim3(256), 0, s, a);
+  if (ntw == 2)
+    hipLaunchKernelGGL((gemv_kernel<2, 4>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemv_kernel<1, 4>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -141,81 +158,97 @@ DEV float block_sum(float v, float *red) {
   return t;
 }
 
-// One workgroup per sequence: x = emb[tok] (f32), rstd, and the pair of x*g.
+// Row statistics are kept as partial sums of squares, one per 1024-channel
+// chunk of the row (ss[b][chunk]); consumers finish rstd in a fixed order.
+DEV float rstd_from_parts(const float *ss, int b, int nss, int dim, float eps) {
+  float t = 0.f;
+  for (int i = 0; i < nss; ++i) t += ss[b * nss + i];
+  return rstd_of(t, dim, eps);
+}
+
+DEV void chunk_sumsq_store(float v, float *ss, int b, int nss) {
+  __shared__ float red[4];
+  v = wave_sum(v);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) ss[b * nss + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+// grid (dim/1024, batch): x = emb[tok] (f32), pair of x*g, partial sums of squares.
 __global__ __launch_bounds__(256) void dec_embed_norm_kernel(const DecodeArgs d, const u16 *emb,
                                                              const int32_t *tok, const u16 *g, float *x,
-                                                             float *rstd, u16 *xg_hi, u16 *xg_lo) {
-  __shared__ float red[8];
-  const int b = blockIdx.x;
+                                                             float *ss, u16 *xg_hi, u16 *xg_lo) {
+  const int b = blockIdx.y;
+  const int c = blockIdx.x * 1024 + threadIdx.x * 4;
   const int t = tok[b];
   const bool ok = t >= 0 && t < d.vocab;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < d.dim; c += blockDim.x) {
-    const float v = ok ? bf2f(emb[(int64_t)t * d.dim + c]) : __builtin_nanf("");
-    x[(int64_t)b * d.dim + c] = v;
-    ss += v * v;
+  float q = 0.f;
+  if (c < d.dim) {
+    const int64_t o = (int64_t)b * d.dim + c;
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = ok ? bf2f(emb[(int64_t)t * d.dim + c + i]) : __builtin_nanf("");
+      q += v[i] * v[i];
+    }
+    *(f32x4 *)(x + o) = f32x4{v[0], v[1], v[2], v[3]};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u16 hi, lo;
+      split_pair(v[i] * bf2f(g[c + i]), hi, lo);
+      xg_hi[o + i] = hi;
+      xg_lo[o + i] = lo;
+    }
   }
-  ss = block_sum(ss, red);
-  const float r = rstd_of(ss, d.dim, d.eps);
-  if (threadIdx.x == 0) rstd[b] = r;
-  for (int c = threadIdx.x; c < d.dim; c += blockDim.x) {
-    const float v = x[(int64_t)b * d.dim + c] * bf2f(g[c]);
-    u16 hi, lo;
-    split_pair(v, hi, lo);
-    xg_hi[(int64_t)b * d.dim + c] = hi;
-    xg_lo[(int64_t)b * d.dim + c] = lo;
-  }
+  chunk_sumsq_store(q, ss, b, gridDim.x);
 }
 
 hipError_t dec_embed_norm_launch(const DecodeArgs &d, const uint16_t *emb, const int32_t *tok,
-                                 const uint16_t *g, float *x, float *rstd, uint16_t *xg_hi,
-                                 uint16_t *xg_lo, hipStream_t s) {
-  hipLaunchKernelGGL(dec_embed_norm_kernel, dim3(d.batch), dim3(256), 0, s, d, emb, tok, g, x, rstd, xg_hi,
-                     xg_lo);
+                                 const uint16_t *g, float *x, float *ss, uint16_t *xg_hi, uint16_t *xg_lo,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(dec_embed_norm_kernel, dim3((d.dim + 1023) / 1024, d.batch), dim3(256), 0, s, d, emb, tok,
+                     g, x, ss, xg_hi, xg_lo);
   return hipGetLastError();
 }
 
-// out = res + sum_s part[s]; rstd of out; pair of out*g (when g is given).
+// grid (dim/1024, batch): out = res + sum_s part[s] (fixed split order),
+// pair of out*g, partial sums of squares of out.
 __global__ __launch_bounds__(256) void dec_resid_norm_kernel(const DecodeArgs d, const float *res,
                                                              const float *part, int splits, const u16 *g,
-                                                             float *out, float *rstd, u16 *og_hi,
-                                                             u16 *og_lo) {
-  __shared__ float red[8];
-  const int b = blockIdx.x;
+                                                             float *out, float *ss, u16 *og_hi, u16 *og_lo) {
+  const int b = blockIdx.y;
+  const int c = blockIdx.x * 1024 + threadIdx.x * 4;
   const int64_t stride = (int64_t)d.batch * d.dim;
-  float ss = 0.f;
-  for (int c = threadIdx.x; c < d.dim; c += blockDim.x) {
+  float q = 0.f;
+  if (c < d.dim) {
     const int64_t o = (int64_t)b * d.dim + c;
-    float v = res[o];
-    for (int sp = 0; sp < splits; ++sp) v += part[sp * stride + o];
-    out[o] = v;
-    ss += v * v;
+    f32x4 v = *(const f32x4 *)(res + o);
+    for (int sp = 0; sp < splits; ++sp) v += *(const f32x4 *)(part + sp * stride + o);
+    *(f32x4 *)(out + o) = v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q += v[i] * v[i];
+      u16 hi, lo;
+      split_pair(v[i] * bf2f(g[c + i]), hi, lo);
+      og_hi[o + i] = hi;
+      og_lo[o + i] = lo;
+    }
   }
-  ss = block_sum(ss, red);
-  const float r = rstd_of(ss, d.dim, d.eps);
-  if (threadIdx.x == 0) rstd[b] = r;
-  if (!g) return;
-  for (int c = threadIdx.x; c < d.dim; c += blockDim.x) {
-    const int64_t o = (int64_t)b * d.dim + c;
-    u16 hi, lo;
-    split_pair(out[o] * bf2f(g[c]), hi, lo);
-    og_hi[o] = hi;
-    og_lo[o] = lo;
-  }
+  chunk_sumsq_store(q, ss, b, gridDim.x);
 }
 
 hipError_t dec_resid_norm_launch(const DecodeArgs &d, const float *res, const float *part, int splits,
-                                 const uint16_t *g, float *out, float *rstd, uint16_t *og_hi,
-                                 uint16_t *og_lo, hipStream_t s) {
-  hipLaunchKernelGGL(dec_resid_norm_kernel, dim3(d.batch), dim3(256), 0, s, d, res, part, splits, g, out,
-                     rstd, og_hi, og_lo);
+                                 const uint16_t *g, float *out, float *ss, uint16_t *og_hi, uint16_t *og_lo,
+                                 hipStream_t s) {
+  hipLaunchKernelGGL(dec_resid_norm_kernel, dim3((d.dim + 1023) / 1024, d.batch), dim3(256), 0, s, d, res, part,
+                     splits, g, out, ss, og_hi, og_lo);
   return hipGetLastError();
 }
 
 // q = RoPE(rstd * sum part[:, :, 0:d]); k = RoPE(rstd * ...[d:2d]); v = rstd * ...[2d:3d].
 // One thread per channel pair; k and v go to cache slot pos[b] (bf16).
 __global__ void dec_qkv_combine_kernel(const DecodeArgs d, const float *part, int splits,
-                                       const float *rstd, float *q, u16 *kc, u16 *vc) {
+                                       const float *ss, float *q, u16 *kc, u16 *vc) {
   const int pairs = 3 * d.dim / 2;
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= d.batch * pairs) return;
@@ -229,7 +262,7 @@ __global__ void dec_qkv_combine_kernel(const DecodeArgs d, const float *part, in
     v0 += p2.x;
     v1 += p2.y;
   }
-  const float r = rstd[b];
+  const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
   v0 *= r;
   v1 *= r;
   const int seg = n / d.dim, c = n - seg * d.dim;
@@ -262,7 +295,7 @@ hipError_t dec_qkv_combine_launch(const DecodeArgs &d, const float *part, int sp
 
 // u = SiLU(rstd * gate) * (rstd * up); gate/up partials are interleaved in blocks of 32.
 __global__ void dec_gateup_combine_kernel(const DecodeArgs d, const float *part, int splits,
-                                          const float *rstd, u16 *u_hi, u16 *u_lo) {
+                                          const float *ss, u16 *u_hi, u16 *u_lo) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= d.batch * d.hidden) return;
   const int b = idx / d.hidden, j = idx % d.hidden;
@@ -275,7 +308,7 @@ __global__ void dec_gateup_combine_kernel(const DecodeArgs d, const float *part,
     gt += pp[ng];
     up += pp[ng + 32];
   }
-  const float r = rstd[b];
+  const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
   const float u = silu(gt * r) * (up * r);
   u16 hi, lo;
   split_pair(u, hi, lo);
@@ -292,14 +325,15 @@ hipError_t dec_gateup_combine_launch(const DecodeArgs &d, const float *part, int
 }
 
 __global__ void dec_head_combine_kernel(const DecodeArgs d, const float *part, int splits,
-                                        const float *rstd, float *logits) {
+                                        const float *ss, float *logits) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= d.batch * d.vocab) return;
   const int b = idx / d.vocab;
   const int64_t stride = (int64_t)d.batch * d.vocab;
   float v = 0.f;
   for (int sp = 0; sp < splits; ++sp) v += part[sp * stride + idx];
-  logits[idx] = pos_ok(d.pos[b], d.max_seq) ? v * rstd[b] : __builtin_nanf("");
+  const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
+  logits[idx] = pos_ok(d.pos[b], d.max_seq) ? v * r : __builtin_nanf("");
 }
 
 hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *rstd,

@@ -54,6 +54,70 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ norm prep
+// One 64-lane wavefront per row, 8 consecutive channels per lane and step:
+// rstd = 1/sqrt(mean(x^2) + eps) (sum reduced across the wavefront) and the
+// GEMM operand x * g as bf16 hi (+ lo). The product's consumer multiplies its
+// fp32 accumulator by rstd, which completes RMSNorm(x; g) W^T. dim % 8 == 0.
+template <bool IN_F32, bool PAIR>
+__global__ __launch_bounds__(256) void norm_prep_kernel(const void *x, const u16 *g, int64_t rows, int dim,
+                                                        float eps, float *rstd, u16 *xg_hi, u16 *xg_lo) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t base = row * dim;
+  float ss = 0.f;
+  for (int c = 8 * lane; c < dim; c += 512) {
+    float f[8], gf[8];
+    if (IN_F32) {
+      const f32x4 a0 = *(const f32x4 *)((const float *)x + base + c);
+      const f32x4 a1 = *(const f32x4 *)((const float *)x + base + c + 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f[i] = a0[i];
+        f[4 + i] = a1[i];
+      }
+    } else {
+      unpack8(*(const u32x4 *)((const u16 *)x + base + c), f);
+    }
+    unpack8(*(const u32x4 *)(g + c), gf);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ss += f[i] * f[i];
+      f[i] *= gf[i];
+    }
+    if (PAIR) {
+      u32x4 hi, lo;
+      pack8_pair(f, hi, lo);
+      *(u32x4 *)(xg_hi + base + c) = hi;
+      *(u32x4 *)(xg_lo + base + c) = lo;
+    } else {
+      *(u32x4 *)(xg_hi + base + c) = pack8(f);
+    }
+  }
+  ss = wave_sum(ss);
+  if (lane == 0) rstd[row] = rstd_of(ss, dim, eps);
+}
+
+hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
+                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (dim % 8) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+#define NP_CASE(F, P)                                                                                     \
+  if (!!in_f32 == F && (xg_lo != nullptr) == P) {                                                         \
+    hipLaunchKernelGGL((norm_prep_kernel<F, P>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, xg_hi, \
+                       xg_lo);                                                                            \
+    return hipGetLastError();                                                                             \
+  }
+  NP_CASE(true, true)
+  NP_CASE(true, false)
+  NP_CASE(false, true)
+  NP_CASE(false, false)
+#undef NP_CASE
+  return hipErrorInvalidValue;
+}
+
 // ------------------------------------------------------------------ RMSNorm
 // One 64-lane wavefront per row; the sum of squares is reduced across lanes.
 template <bool IN_F32, bool OUT_F32>

@@ -3,9 +3,8 @@
 
 namespace llama {
 hipError_t gemm_launch_ffn(const GemmKey &key, const GemmArgs &a, hipStream_t s) {
-  GEMM_CASE(256, ASRC_F32, 0, 1, EPI_SILU)
-  GEMM_CASE(256, ASRC_F32, 1, 1, EPI_SILU)
-  GEMM_CASE(256, ASRC_BF16, 0, 0, EPI_SILU)
+  GEMM_CASE(256, 0, EPI_SILU)
+  GEMM_CASE(256, 1, EPI_SILU)
   return hipErrorInvalidValue;
 }
 }  // namespace llama

@@ -4,12 +4,12 @@
 
 namespace llama {
 hipError_t gemm_launch_misc(const GemmKey &key, const GemmArgs &a, hipStream_t s) {
-  GEMM_CASE(128, ASRC_BF16, 0, 0, EPI_RESID)
-  GEMM_CASE(128, ASRC_BF16PAIR, 1, 0, EPI_RESID)
-  GEMM_CASE(256, ASRC_F32, 1, 1, EPI_STORE)
-  GEMM_CASE(128, ASRC_BF16, 0, 0, EPI_STORE)
-  GEMM_CASE(128, ASRC_F32, 1, 0, EPI_STORE)
-  GEMM_CASE(128, ASRC_BF16PAIR, 1, 0, EPI_STORE)
+  GEMM_CASE(128, 0, EPI_RESID)
+  GEMM_CASE(128, 1, EPI_RESID)
+  GEMM_CASE(128, 0, EPI_STORE)
+  GEMM_CASE(128, 1, EPI_STORE)
+  GEMM_CASE(256, 0, EPI_STORE)
+  GEMM_CASE(256, 1, EPI_STORE)
   return hipErrorInvalidValue;
 }
 

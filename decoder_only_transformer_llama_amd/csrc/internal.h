@@ -12,17 +12,15 @@ namespace llama {
 
 // ---------------------------------------------------------------- GEMM
 // C[M, N] = A[M, K] * B[N, K]^T on bf16 matrix cores, fp32 accumulate.
-enum ASrc { ASRC_BF16 = 0, ASRC_F32 = 1, ASRC_BF16PAIR = 2 };
 enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_QKV = 3 };
 enum BMode { BMODE_PLAIN = 0, BMODE_CONCAT3 = 1, BMODE_GATEUP = 2 };
 
 struct GemmArgs {
-  int M, N, K;
-  const void *A;       // [M, lda] bf16 or f32 (ASRC_BF16PAIR: hi part)
-  const uint16_t *A_lo;  // ASRC_BF16PAIR: lo part, same layout
+  int M, N, K;                   // K % 32 == 0
+  const uint16_t *A;             // [M, lda] bf16 (hi part when A_lo is set)
+  const uint16_t *A_lo;          // optional lo part of a bf16 pair, same layout
   int64_t lda;
-  const uint16_t *gain;  // [K] bf16 (norm fold) or null
-  float eps;             // norm fold: rstd = 1/sqrt(mean(A^2) + eps), applied in the epilogue
+  const float *rstd;             // optional per-row scale applied to the accumulator
   int b_mode;
   const uint16_t *B0, *B1, *B2;  // weights [rows, K] bf16
   int n_seg;                     // BMODE_CONCAT3: rows per segment
@@ -35,7 +33,7 @@ struct GemmArgs {
   int r_f32;
   // EPI_QKV
   uint16_t *qh, *ql, *kh, *kl;   // [M, dim] hi/lo of rotated q and k
-  uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, seq] hi/lo of v (transposed)
+  uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, vt_stride] hi/lo of v (transposed)
   const float2 *rope_tab;        // [seq, head_dim/2] (cos, sin)
   int seq, n_heads, head_dim, dim;
   int vt_stride;                 // row stride of the transposed v (>= seq, multiple of 64)
@@ -44,7 +42,7 @@ struct GemmArgs {
 };
 
 struct GemmKey {
-  int bn, asrc, apair, norm, epi;
+  int bn, apair, epi;
 };
 
 // Returns a hipError_t; hipErrorInvalidValue when no instance matches `key`.
@@ -70,6 +68,10 @@ hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, hipSt
 hipError_t rope_table_launch(float2 *tab, int positions, int head_dim, float theta, hipStream_t s);
 hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int head_dim, float theta,
                                  int max_seq, hipStream_t s);
+// Norm prep (one wavefront per row): rstd[r] = 1/sqrt(mean(x[r]^2) + eps) and the
+// product x[r] * g as bf16 (hi, and lo when xg_lo is non-null).
+hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
+                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s);
 hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,
                           int dim, float eps, hipStream_t s);
 // pos == nullptr: the position of token t is t % seq_mod.
@@ -99,6 +101,8 @@ struct GemvArgs {
   float *part;                   // [splits, M, N]
 };
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
+int gemv_ntw(int N);               // 32-column tiles per wavefront used for N
+constexpr int kGemvMaxChunk = 512; // largest K range of one workgroup
 
 struct DecodeArgs {
   int batch, dim, n_heads, head_dim, hidden, max_seq, vocab;
@@ -106,22 +110,23 @@ struct DecodeArgs {
   const int32_t *pos;            // [batch]
   const float2 *rope_tab;        // [batch, head_dim/2] for pos[b]
 };
-// x[b] = emb[tok[b]] (f32), rstd[b], xg pair = x*g
+// Row statistics travel as partial sums of squares ss[b][dim/1024 chunks].
+// x[b] = emb[tok[b]] (f32), ss, xg pair = x*g
 hipError_t dec_embed_norm_launch(const DecodeArgs &d, const uint16_t *emb, const int32_t *tok,
-                                 const uint16_t *g, float *x, float *rstd, uint16_t *xg_hi,
+                                 const uint16_t *g, float *x, float *ss, uint16_t *xg_hi,
                                  uint16_t *xg_lo, hipStream_t s);
 // q (f32), cache writes of k, v for slot pos[b]
-hipError_t dec_qkv_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *rstd,
+hipError_t dec_qkv_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *ss,
                                   float *q, uint16_t *kc, uint16_t *vc, hipStream_t s);
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *q, const uint16_t *kc, const uint16_t *vc,
                            int chunk, int n_chunks, float *o_part, float *ml_part, hipStream_t s);
-// out = res + sum(part); rstd of out; out*g as pair (g may be null -> no pair written)
+// out = res + sum(part); ss of out; out*g as pair
 hipError_t dec_resid_norm_launch(const DecodeArgs &d, const float *res, const float *part, int splits,
-                                 const uint16_t *g, float *out, float *rstd, uint16_t *og_hi,
+                                 const uint16_t *g, float *out, float *ss, uint16_t *og_hi,
                                  uint16_t *og_lo, hipStream_t s);
 hipError_t dec_gateup_combine_launch(const DecodeArgs &d, const float *part, int splits,
-                                     const float *rstd, uint16_t *u_hi, uint16_t *u_lo, hipStream_t s);
-hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *rstd,
+                                     const float *ss, uint16_t *u_hi, uint16_t *u_lo, hipStream_t s);
+hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *ss,
                                    float *logits, hipStream_t s);
 hipError_t dec_attn_combine_launch(const DecodeArgs &d, const float *o_part, const float *ml_part,
                                    int n_chunks, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s);

@@ -136,10 +136,10 @@ int llama_rope(int dtype, const void *x, void *y, const int32_t *positions, int6
                int n_heads, int head_dim, float theta, void *stream);
 
 /* Projection y = x W^T (the matrix products of [P1] "The code").
- * x [rows, k] in x_dtype (bf16 or f32); w [n, k] in w_dtype; y [rows, n] in
- * y_dtype. bf16 weights run on the matrix cores (an f32 x is carried as a
- * bf16 hi/lo pair); f32 weights need x_dtype f32 and run in fp32.
- * Errors: NULL pointers, sizes <= 0, k % 64 != 0 for bf16 weights, bad dtypes. */
+ * x [rows, k] and w [n, k] in the same dtype; y [rows, n] in y_dtype.
+ * bf16 runs on the matrix cores with fp32 accumulation (y f32 or bf16);
+ * f32 runs in fp32 on the vector ALUs (y f32).
+ * Errors: NULL pointers, sizes <= 0, k % 64 != 0 for bf16, mixed or bad dtypes. */
 int llama_linear(int x_dtype, int w_dtype, int y_dtype, const void *x, const void *w, void *y,
                  int64_t rows, int n, int k, void *stream);
 

@@ -96,16 +96,23 @@ def test_rope(dtype):
 
 
 # ---------------------------------------------------------------- projections
-@pytest.mark.parametrize("xdt", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("rows,n,k", [(1, 128, 64), (300, 384, 256), (2048, 4096, 4096), (33, 1000, 512)])
-def test_linear_bf16_weights(xdt, rows, n, k):
-    x = I.normal((rows, k), 902, 0, 0, dtype=xdt, device="cuda")
+def test_linear_bf16(rows, n, k):
+    x = I.normal((rows, k), 902, 0, 0, dtype=torch.bfloat16, device="cuda")
     w = I.normal((n, k), 902, 0, 1, std=0.02, dtype=torch.bfloat16, device="cuda")
     y = ops().linear(x, w)
     want = O.linear(host(x), host(w))
-    # bf16 x: exact operands, fp32 accumulation only; f32 x: carried as a bf16
-    # hi/lo pair (about 2^-17 relative per element)
-    assert rel_err(y, want) < (1e-5 if xdt == torch.bfloat16 else 5e-5)
+    assert rel_err(y, want) < 1e-5        # exact bf16 operands: fp32 accumulation error only
+    yb = ops().linear(x, w, torch.bfloat16)
+    assert_bf16_rounded(yb, want) if rows * n < 10 ** 6 else None
+
+
+def test_linear_mixed_dtypes_rejected():
+    x = torch.zeros((4, 64), device="cuda")
+    w = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(L.LlamaError) as e:
+        ops().linear(x, w)
+    assert e.value.status == L.LLAMA_ERR_DTYPE
 
 
 def test_linear_f32():
