@@ -78,11 +78,11 @@ def decode_bytes(w) -> dict:
 
 def traced_kernel_ms(lib, run, stream, n_kernels: int, reps: int):
     """Average per-kernel duration (ms) over `reps` traced runs of `run`."""
-    ev = HipEvents(n_kernels + 1)
+    ev = HipEvents(n_kernels + 2)
     tot = [0.0] * n_kernels
     for _ in range(reps):
         ev.record(0, stream)
-        lib.llama_trace_begin(ev.pointer_from(1), n_kernels)
+        lib.llama_trace_begin(ev.pointer_from(1), n_kernels + 1)   # one spare slot detects extra kernels
         run()
         got = lib.llama_trace_end()
         if got != n_kernels:

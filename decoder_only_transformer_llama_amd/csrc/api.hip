@@ -61,6 +61,30 @@ uint32_t numerics_of(const llama_config *c) {
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
 
+// Compute units of the current device (queried once per process).
+int cu_count() {
+  static const int n = [] {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    return cus;
+  }();
+  return n;
+}
+
+// Tile width (256 or 128 output columns) whose tile count fills the last
+// round of workgroups best; ties go to the wider tile (less operand re-reading).
+int choose_bn(int M, int N) {
+  const int cus = cu_count();
+  auto eff = [&](int bn) {
+    const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
+    const long rounds = (tiles + cus - 1) / cus;
+    return (double)tiles / (double)(rounds * cus);
+  };
+  return eff(128) > eff(256) + 1e-9 ? 128 : 256;
+}
+
 // ------------------------------------------------------------------ validation
 int check_block_cfg(const llama_config *c, int batch, int seq) {
   if (!c) return LLAMA_ERR_NULL;
@@ -282,7 +306,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.kcache = kcache;
   q.vcache = vcache;
   q.max_seq = max_seq;
-  HIP_TRY(gemm_launch(GemmKey{256, qkv_pair, EPI_QKV}, q, s), "qkv projection");
+  HIP_TRY(gemm_launch(GemmKey{choose_bn(M, 3 * d), qkv_pair, EPI_QKV}, q, s), "qkv projection");
 
   AttnArgs at{};
   at.qh = b.qh;

@@ -25,7 +25,12 @@
 namespace llama {
 
 DEV int perm23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
-DEV int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+// LDS chunk swizzles (gfx950 serves a 16-byte read 16 lanes per pass over a
+// 256-byte bank window): rows of 256 bytes XOR the chunk with row mod 16, rows
+// of 128 bytes with (row / 2) mod 8, so any 16 consecutive rows read at one
+// logical chunk hit 16 distinct 16-byte slots.
+template <int CHUNKS>
+DEV int rswz(int row) { return CHUNKS == 16 ? (row & 15) : ((row >> 1) & 7); }
 
 template <int HD, bool QKPAIR, bool VPAIR>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) {
@@ -91,7 +96,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
         v = *(const u32x4 *)(a.kh + o);
         if (QKPAIR) vl = *(const u32x4 *)(a.kl + o);
       }
-      const int so = row * KCH + (ch ^ kswz(row));
+      const int so = row * KCH + (ch ^ rswz<KCH>(row));
       sk[so] = v;
       if (QKPAIR) skl[so] = vl;
     }
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
           vl[i] = lv[2 * i] | (lv[2 * i + 1] << 16);
         }
       }
-      const int so = e * 8 + (ch ^ (e & 7));
+      const int so = e * 8 + (ch ^ rswz<8>(e));
       sv[so] = v;
       if (VPAIR) svl[so] = vl;
     }
@@ -136,7 +141,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       const int krow = 32 * t + perm23(l32);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int so = krow * KCH + ((2 * kk + g) ^ kswz(krow));
+        const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
         const bf16x8 kf = as_bf16x8(sk[so]);
         s[t] = mfma32(kf, qh[kk], s[t]);
         if (QKPAIR) {
@@ -192,7 +197,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
 #pragma unroll
         for (int e = 0; e < NEB; ++e) {
           const int row = 32 * e + l32;
-          const int so = row * 8 + (ch ^ (row & 7));
+          const int so = row * 8 + (ch ^ rswz<8>(row));
           acc_o[e] = mfma32(as_bf16x8(sv[so]), pf, acc_o[e]);
           if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), pf, acc_o[e]);
         }

@@ -1,13 +1,15 @@
 // bf16 matrix-core GEMM for gfx950: C[M, N] = A[M, K] * B[N, K]^T, fp32 accumulate.
 //
-// One workgroup = 4 wavefronts (2 x 2) computing a 256 x BN tile with
-// v_mfma_f32_32x32x16_bf16 (each wavefront 128 x BN/2: 4 x BN/64 accumulator
-// tiles). A and B move HBM -> LDS with global_load_lds_dwordx4 (no register
-// staging): every wavefront instruction drops 64 lanes x 16 bytes into one
-// contiguous 1 KB block of LDS, and the row/chunk each lane fetches is chosen
-// so the block lands already XOR-swizzled. K is consumed in steps of 32 with a
-// ring of STAGES LDS buffers, STAGES-1 steps of loads in flight while the
-// matrix cores work; one barrier per step, explicit vmcnt waits.
+// One workgroup = 8 wavefronts (2 x 4, two per SIMD so one wavefront's LDS and
+// barrier waits overlap the other's matrix-core work) computing a 256 x BN tile
+// with v_mfma_f32_32x32x16_bf16 (each wavefront 128 x BN/4). A and B move
+// HBM -> LDS with global_load_lds_dwordx4 (no register staging): every
+// wavefront instruction drops 64 lanes x 16 bytes into one contiguous 1 KB
+// block of LDS, and the row/chunk each lane fetches is chosen so the block
+// lands already XOR-swizzled. K is consumed in steps of 32 with a ring of
+// STAGES LDS buffers (STAGES-1 steps of loads in flight); operand reads of the
+// next substep are interleaved with the current substep's MFMAs; one barrier
+// per step with explicit vmcnt/lgkmcnt waits.
 //
 // A may be a bf16 hi/lo pair (A_lo non-null): both parts are multiplied into
 // the same accumulator, which carries an fp32 activation at ~2^-16 relative
@@ -42,29 +44,45 @@ template <int BN, bool APAIR>
 struct GemmCfg {
   static constexpr int BM = 256, BK = 32;
   static constexpr int CH = 4;                     // 16-byte chunks per LDS row (64 bytes)
-  static constexpr int WM = BM / 2, WN = BN / 2;
+  static constexpr int NW = 8;                     // wavefronts: 2 (M) x 4 (N)
+  static constexpr int WM = BM / 2, WN = BN / 4;
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_TILE = BM * CH;           // u32x4 per A tile
   static constexpr int B_TILE = BN * CH;
   static constexpr int STAGE = A_TILE * (APAIR ? 2 : 1) + B_TILE;
-  static constexpr int STAGES = (STAGE * 16 * 4 <= 136 * 1024) ? 4 : 3;
-  static constexpr int A_LD = BM / 16 / 4;         // 1 KB loads per wavefront per A tile
-  static constexpr int B_LD = BN / 16 / 4;
+  static constexpr int STAGES = (STAGE * 16 * 5 <= 160 * 1024) ? 5 : ((STAGE * 16 * 4 <= 160 * 1024) ? 4 : 3);
+  static constexpr int A_LD = BM / 16 / NW;        // 1 KB loads per wavefront per A tile
+  static constexpr int B_LD = BN / 16 / NW;
   static constexpr int LPS = A_LD * (APAIR ? 2 : 1) + B_LD;  // loads per stage per wavefront
 };
 
-// Swizzle of the 4 chunks of a 64-byte LDS row: conflict-free operand reads
-// for both 8-lane/32-bank and 16-lane/64-bank service of 16-byte reads.
-DEV int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+// Swizzle of the 4 chunks of a 64-byte LDS row. gfx950 LDS serves a 16-byte
+// read 16 lanes per pass across 64 four-byte banks (256 bytes): the 16 rows
+// read together (same logical chunk) must land on 16 distinct 16-byte slots
+// of the 256-byte bank window, i.e. distinct (row mod 4, chunk) pairs.
+DEV int swz4(int row) { return (row >> 2) & 3; }
+
+// Scheduling hint: alternate one MFMA with one LDS read, then the remainder.
+template <int NMF, int NRD, int ID>
+DEV void interleave() {
+  constexpr int P = NMF < NRD ? NMF : NRD;
+#pragma unroll
+  for (int i = 0; i < P; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);  // one LDS read
+  }
+  if (NMF > P) __builtin_amdgcn_sched_group_barrier(0x008, NMF - P, ID);
+  if (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, ID);
+}
 
 template <int BN, bool APAIR, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
   using G = GemmCfg<BN, APAIR>;
   constexpr int BM = G::BM, BK = G::BK, CH = G::CH, STAGES = G::STAGES;
   __shared__ u32x4 smem[STAGES * G::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 2, wn = wave & 3;
   const int g = lane >> 5, l32 = lane & 31;
 
   const int tiles_m = (a.M + BM - 1) / BM;
@@ -105,7 +123,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmArgs a) {
   }
 
   auto issue = [&](int kt) {
-    const int k0 = kt * BK;
+    const int k0 = min(kt, a.K / BK - 1) * BK;   // past the end: reload the last step (never read)
     u32x4 *st = smem + (kt % STAGES) * G::STAGE;
 #pragma unroll
     for (int q = 0; q < G::A_LD; ++q)
@@ -132,49 +150,73 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_kernel(const GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int kt) {
+  // Operand fragments of one 16-deep k-substep: A (and its lo part) for the
+  // wavefront's 4 row tiles, B for its TN column tiles.
+  struct Frag {
+    bf16x8 a[G::TM], al[APAIR ? G::TM : 1], b[G::TN];
+  };
+  auto read_frag = [&](Frag &f, int kt, int ks) {
     const u32x4 *sa = smem + (kt % STAGES) * G::STAGE;
     const u32x4 *sal = sa + G::A_TILE;
     const u32x4 *sb = sa + G::A_TILE * (APAIR ? 2 : 1);
+    const int c = ks * 2 + g;
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int c = ks * 2 + g;
-      bf16x8 bfr[G::TN];
+    for (int j = 0; j < G::TN; ++j) {
+      const int r = wn * G::WN + j * 32 + l32;
+      f.b[j] = as_bf16x8(sb[r * CH + (c ^ swz4(r))]);
+    }
 #pragma unroll
-      for (int j = 0; j < G::TN; ++j) {
-        const int r = wn * G::WN + j * 32 + l32;
-        bfr[j] = as_bf16x8(sb[r * CH + (c ^ swz4(r))]);
-      }
+    for (int i = 0; i < G::TM; ++i) {
+      const int r = wm * G::WM + i * 32 + l32;
+      const int off = r * CH + (c ^ swz4(r));
+      f.a[i] = as_bf16x8(sa[off]);
+      if (APAIR) f.al[i] = as_bf16x8(sal[off]);
+    }
+  };
+  auto mma = [&](const Frag &f) {
 #pragma unroll
-      for (int i = 0; i < G::TM; ++i) {
-        const int r = wm * G::WM + i * 32 + l32;
-        const int off = r * CH + (c ^ swz4(r));
-        const bf16x8 af = as_bf16x8(sa[off]);
+    for (int i = 0; i < G::TM; ++i) {
 #pragma unroll
-        for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma32(af, bfr[j], acc[i][j]);
-        if (APAIR) {
-          const bf16x8 al = as_bf16x8(sal[off]);
+      for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+      if (APAIR) {
 #pragma unroll
-          for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma32(al, bfr[j], acc[i][j]);
-        }
+        for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma32(f.al[i], f.b[j], acc[i][j]);
       }
     }
   };
 
+  // Pipeline per K step kt (two 16-deep substeps, fragments F0/F1), one barrier:
+  //   issue loads of stage kt+S-1 | [mma F0(kt) interleaved with reads of F1(kt)]
+  //   wait own stage-(kt+1) loads, drain own LDS reads, barrier
+  //   [mma F1(kt) interleaved with reads of F0(kt+1)]
+  // The buffer refilled at step kt held stage kt-1; every wavefront drained its
+  // reads of it before the previous barrier. Loads past the last step re-read
+  // the last step into buffers nobody reads, so the body has no branches.
   const int nk = a.K / BK;
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + STAGES - 2 < nk) {
-      WAIT_VMCNT((STAGES - 2) * G::LPS);
-    } else {
-      WAIT_VMCNT(0);
-    }
+  for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  WAIT_VMCNT((STAGES - 2) * G::LPS);
+  __builtin_amdgcn_s_barrier();
+  Frag f0, f1;
+  read_frag(f0, 0, 0);
+  constexpr int NMF = G::TM * G::TN * (APAIR ? 2 : 1);     // MFMAs per substep
+  constexpr int NRD = G::TM * (APAIR ? 2 : 1) + G::TN;      // LDS reads per substep
+  for (int kt = 0; kt < nk - 1; ++kt) {
+    issue(kt + STAGES - 1);
+    read_frag(f1, kt, 1);
+    mma(f0);
+    interleave<NMF, NRD, 0>();
+    WAIT_VMCNT((STAGES - 2) * G::LPS);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-    compute(kt);
+    read_frag(f0, kt + 1, 0);
+    mma(f1);
+    interleave<NMF, NRD, 1>();
   }
+  read_frag(f1, nk - 1, 1);
+  mma(f0);
+  mma(f1);
+  WAIT_VMCNT(0);   // drain the reloads past the end before LDS is reused
 
   // ---------------------------------------------------------------- epilogue
   if (EPI == EPI_QKV) {
@@ -338,7 +380,7 @@ hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   using G = GemmCfg<BN, APAIR>;
   const int nb = ((a.M + G::BM - 1) / G::BM) * ((a.N + BN - 1) / BN);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI>), dim3(nb), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI>), dim3(nb), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
