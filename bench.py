@@ -177,8 +177,7 @@ def bench_decode(args, torch):
     ms_eager = ev.elapsed_ms(0, 1) / max(2, args.steps // 4)
 
     L = w.n_layers
-    per_layer = ["qkv", "qkv_combine", "attention", "attn_merge", "o", "resid1", "gate_up", "silu", "down",
-                 "resid2"]
+    per_layer = ["qkv", "attention", "o", "resid1", "gate_up", "silu", "down", "resid2"]
     names = ["rope_table", "embed"] + [n for _ in range(L) for n in per_layer] + ["head", "head_combine"]
     kms = traced_kernel_ms(_lib.load(), run, stream, len(names), 2)
     agg = {}

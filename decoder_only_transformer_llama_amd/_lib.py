@@ -27,6 +27,7 @@ EXPORTS = (
     "llama_hidden_dim", "llama_rmsnorm", "llama_rope", "llama_linear", "llama_causal_attn",
     "llama_swiglu_ffn", "llama_block_forward", "llama_model_forward", "llama_model_decode",
     "llama_workspace_size", "llama_status_string", "llama_last_error", "llama_trace_begin", "llama_trace_end",
+    "llama_decode_pack_size", "llama_pack_decode_weights",
 )
 
 
@@ -44,7 +45,7 @@ class BlockWeights(ctypes.Structure):
 
 class ModelWeights(ctypes.Structure):
     _fields_ = [("tok_embeddings", ctypes.c_void_p), ("layers", ctypes.POINTER(BlockWeights)),
-                ("final_norm", ctypes.c_void_p), ("output", ctypes.c_void_p)]
+                ("final_norm", ctypes.c_void_p), ("output", ctypes.c_void_p), ("decode_pack", ctypes.c_void_p)]
 
 
 _lib = None
@@ -76,6 +77,8 @@ def load() -> ctypes.CDLL:
         "llama_last_error": [],
         "llama_trace_begin": [ctypes.POINTER(vp), i32],
         "llama_trace_end": [],
+        "llama_decode_pack_size": [cfgp, ctypes.POINTER(sz)],
+        "llama_pack_decode_weights": [cfgp, ctypes.POINTER(ModelWeights), vp, sz, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

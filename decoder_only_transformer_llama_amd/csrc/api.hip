@@ -173,12 +173,12 @@ BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq) {
 }
 
 struct DecodeWs {
-  float *x, *h, *rstd, *q, *part, *o_part, *ml;
+  float *x, *h, *rstd, *part;
   uint16_t *ag_hi, *ag_lo;
   float2 *rope_tab;
 };
 
-constexpr int kDecChunk = 256;
+constexpr int kDecMaxSeq = 2048;   // decode attention keeps one score per cached position in LDS
 
 void gemv_split(int N, int K, int &splits, int &k_chunk) {
   const int per_wg = 128 * gemv_ntw(N);
@@ -205,14 +205,10 @@ size_t dec_part_floats(const llama_config *c, int batch) {
 DecodeWs carve_decode(Carve &cv, const llama_config *c, int batch) {
   DecodeWs w{};
   const int d = c->dim, hd = d / c->n_heads;
-  const int n_chunks = (c->max_seq + kDecChunk - 1) / kDecChunk;
   w.x = cv.take<float>((size_t)batch * d);
   w.h = cv.take<float>((size_t)batch * d);
   w.rstd = cv.take<float>((size_t)batch * ((c->dim + 1023) / 1024));
-  w.q = cv.take<float>((size_t)batch * d);
   w.part = cv.take<float>(dec_part_floats(c, batch));
-  w.o_part = cv.take<float>((size_t)batch * c->n_heads * n_chunks * hd);
-  w.ml = cv.take<float>((size_t)batch * c->n_heads * n_chunks * 2);
   const int wmax = std::max(d, c->hidden);
   w.ag_hi = cv.take<uint16_t>((size_t)batch * wmax);
   w.ag_lo = cv.take<uint16_t>((size_t)batch * wmax);
@@ -260,6 +256,29 @@ size_t ws_bytes_of(const llama_config *c, int op, int batch, int seq) {
       return 0;
   }
   return cv.off + 256;
+}
+
+// ------------------------------------------------------------------ decode weight pack
+// Per layer: Wq|Wk|Wv (3d rows, K = d), Wo (d, d), W_gate/W_up interleaved by
+// 32 rows (2h, d), W_down (d, h); then the output head (vocab, d). Each matrix
+// holds ceil(rows/32)*32 rows in tile order.
+size_t tile_elems(int rows, int K) { return (size_t)((rows + 31) / 32) * 32 * K; }
+
+struct PackLayout {
+  size_t qkv, o, gu, down, layer, head_off, total;   // element offsets / sizes (u16)
+};
+
+PackLayout pack_layout(const llama_config *c) {
+  PackLayout p{};
+  const int d = c->dim, h = c->hidden;
+  p.qkv = 0;
+  p.o = tile_elems(3 * d, d);
+  p.gu = p.o + tile_elems(d, d);
+  p.down = p.gu + tile_elems(2 * h, d);
+  p.layer = p.down + tile_elems(d, h);
+  p.head_off = p.layer * c->n_layers;
+  p.total = p.head_off + tile_elems(c->vocab, d);
+  return p;
 }
 
 // ------------------------------------------------------------------ block launch sequences
@@ -462,7 +481,7 @@ int llama_workspace_size(const llama_config *c, int op, int batch, int seq, size
       break;
     case LLAMA_OP_MODEL_DECODE:
       st = check_model_cfg(c, batch, 1);
-      if (!st && batch > 32) st = LLAMA_ERR_UNSUPPORTED;
+      if (!st && (batch > 32 || c->max_seq > kDecMaxSeq)) st = LLAMA_ERR_UNSUPPORTED;
       break;
     default:
       return LLAMA_ERR_UNSUPPORTED;
@@ -697,7 +716,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
                        size_t ws_bytes, void *stream) {
   int st = check_model_cfg(c, batch, 1);
   if (st) return st;
-  if (batch > 32) return LLAMA_ERR_UNSUPPORTED;
+  if (batch > 32 || c->max_seq > kDecMaxSeq) return LLAMA_ERR_UNSUPPORTED;
   if ((st = check_model_w(c, w))) return st;
   if (!tokens || !pos || !k_cache || !v_cache || !logits) return LLAMA_ERR_NULL;
   const size_t need = ws_bytes_of(c, LLAMA_OP_MODEL_DECODE, batch, 1);
@@ -717,15 +736,18 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   da.eps = c->norm_eps;
   da.pos = pos;
   da.rope_tab = dw.rope_tab;
-  const int n_chunks = (c->max_seq + kDecChunk - 1) / kDecChunk;
   const size_t layer_elems = (size_t)batch * c->n_heads * c->max_seq * hd;
 
   HIP_TRY(rope_table_pos_launch(dw.rope_tab, pos, batch, hd, c->rope_theta, c->max_seq, s), "rope table");
   HIP_TRY(dec_embed_norm_launch(da, (const uint16_t *)w->tok_embeddings, tokens,
                                 (const uint16_t *)w->layers[0].attn_norm, dw.x, dw.rstd, dw.ag_hi, dw.ag_lo, s),
           "embedding");
+  const uint16_t *pack = (const uint16_t *)w->decode_pack;
+  const PackLayout pl = pack_layout(c);
+  const uint16_t *packed_mat = nullptr;   // set before each projection when the pack is present
   auto gemv = [&](int N, int K, int mode, const void *b0, const void *b1, const void *b2, int &splits) {
     GemvArgs g{};
+    g.packed = packed_mat;
     int kc;
     gemv_split(N, K, splits, kc);
     g.M = batch;
@@ -747,16 +769,19 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
     const llama_block_weights &L = w->layers[l];
     uint16_t *kc = (uint16_t *)k_cache + l * layer_elems, *vc = (uint16_t *)v_cache + l * layer_elems;
     int sp;
+    const uint16_t *lp = pack ? pack + (size_t)l * pl.layer : nullptr;
+    packed_mat = lp ? lp + pl.qkv : nullptr;
     HIP_TRY(gemv(3 * d, d, BMODE_CONCAT3, L.wq, L.wk, L.wv, sp), "qkv projection");
-    HIP_TRY(dec_qkv_combine_launch(da, dw.part, sp, dw.rstd, dw.q, kc, vc, s), "qkv combine");
-    HIP_TRY(dec_attn_launch(da, dw.q, kc, vc, kDecChunk, n_chunks, dw.o_part, dw.ml, s), "attention");
-    HIP_TRY(dec_attn_combine_launch(da, dw.o_part, dw.ml, n_chunks, dw.ag_hi, dw.ag_lo, s), "attention merge");
+    HIP_TRY(dec_attn_launch(da, dw.part, sp, dw.rstd, kc, vc, dw.ag_hi, dw.ag_lo, s), "attention");
+    packed_mat = lp ? lp + pl.o : nullptr;
     HIP_TRY(gemv(d, d, BMODE_PLAIN, L.wo, nullptr, nullptr, sp), "output projection");
     HIP_TRY(dec_resid_norm_launch(da, dw.x, dw.part, sp, (const uint16_t *)L.ffn_norm, dw.h, dw.rstd, dw.ag_hi,
                                   dw.ag_lo, s),
             "residual");
+    packed_mat = lp ? lp + pl.gu : nullptr;
     HIP_TRY(gemv(2 * c->hidden, d, BMODE_GATEUP, L.w_gate, L.w_up, nullptr, sp), "gate/up projection");
     HIP_TRY(dec_gateup_combine_launch(da, dw.part, sp, dw.rstd, dw.ag_hi, dw.ag_lo, s), "silu");
+    packed_mat = lp ? lp + pl.down : nullptr;
     HIP_TRY(gemv(d, c->hidden, BMODE_PLAIN, L.w_down, nullptr, nullptr, sp), "down projection");
     const void *gnext = l + 1 < c->n_layers ? w->layers[l + 1].attn_norm : w->final_norm;
     HIP_TRY(dec_resid_norm_launch(da, dw.h, dw.part, sp, (const uint16_t *)gnext, dw.x, dw.rstd, dw.ag_hi,
@@ -764,8 +789,48 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
             "residual");
   }
   int sp;
+  packed_mat = pack ? pack + pl.head_off : nullptr;
   HIP_TRY(gemv(c->vocab, d, BMODE_PLAIN, w->output, nullptr, nullptr, sp), "output head");
   HIP_TRY(dec_head_combine_launch(da, dw.part, sp, dw.rstd, logits, s), "head");
+  return LLAMA_OK;
+}
+
+int llama_decode_pack_size(const llama_config *c, size_t *bytes) {
+  if (!c || !bytes) return LLAMA_ERR_NULL;
+  const int st = check_model_cfg(c, 1, 1);
+  if (st) return st;
+  *bytes = pack_layout(c).total * sizeof(uint16_t);
+  return LLAMA_OK;
+}
+
+int llama_pack_decode_weights(const llama_config *c, const llama_model_weights *w, void *dst, size_t dst_bytes,
+                              void *stream) {
+  int st = check_model_cfg(c, 1, 1);
+  if (st) return st;
+  if ((st = check_model_w(c, w))) return st;
+  if (!dst) return LLAMA_ERR_NULL;
+  const PackLayout pl = pack_layout(c);
+  if (dst_bytes < pl.total * sizeof(uint16_t)) return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = c->dim, h = c->hidden;
+  uint16_t *out = (uint16_t *)dst;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const llama_block_weights &L = w->layers[l];
+    uint16_t *lp = out + (size_t)l * pl.layer;
+    HIP_TRY(pack_tiles_launch(BMODE_CONCAT3, (const uint16_t *)L.wq, (const uint16_t *)L.wk, (const uint16_t *)L.wv,
+                              d, 3 * d, d, lp + pl.qkv, s),
+            "pack qkv");
+    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.wo, nullptr, nullptr, d, d, d, lp + pl.o, s),
+            "pack o");
+    HIP_TRY(pack_tiles_launch(BMODE_GATEUP, (const uint16_t *)L.w_gate, (const uint16_t *)L.w_up, nullptr, d, 2 * h, d,
+                              lp + pl.gu, s),
+            "pack gate/up");
+    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.w_down, nullptr, nullptr, d, d, h, lp + pl.down, s),
+            "pack down");
+  }
+  HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)w->output, nullptr, nullptr, d, c->vocab, d,
+                            out + pl.head_off, s),
+          "pack head");
   return LLAMA_OK;
 }
 

@@ -29,10 +29,15 @@ DEV bool pos_ok(int p, int max_seq) { return p >= 0 && p < max_seq; }
 
 // ------------------------------------------------------------------ skinny GEMM
 // Workgroup = 4 wavefronts x (NTW x 32) output columns over one K range of at
-// most KC_MAX. The activation pair for that K range sits in LDS (loaded once,
-// rows XOR-swizzled); weights stream from HBM into a DEPTH-deep ring of
-// B-operand registers, so DEPTH steps of 64 K are in flight per wavefront.
+// most KC_MAX. The activation pair for that K range is dropped into LDS with
+// global_load_lds_dwordx4 (rows XOR-swizzled) while the first DEPTH steps of
+// weights are already streaming from HBM into a ring of B-operand registers,
+// so the two latencies overlap; afterwards DEPTH steps of 64 K stay in flight
+// per wavefront.
 constexpr int KC_MAX = 512;
+
+#define GEMV_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+#define GEMV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 template <int NTW, int DEPTH>
 __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
@@ -41,25 +46,21 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
   const int g = lane >> 5, l32 = lane & 31;
   const int ks = blockIdx.y * a.k_chunk;
   const int ke = min(a.K, ks + a.k_chunk);
-  const int kc8 = (ke - ks) >> 3;
-
-  // activation pair of this K range -> LDS (rows past M are zero)
-  for (int idx = tid; idx < 2 * 32 * kc8; idx += 256) {
-    const int part = idx / (32 * kc8), rem = idx % (32 * kc8);
-    const int m = rem / kc8, c = rem % kc8;
-    u32x4 v = {0, 0, 0, 0};
-    if (m < a.M) v = *(const u32x4 *)((part ? a.A_lo : a.A_hi) + (int64_t)m * a.K + ks + 8 * c);
-    sA[part][m][c ^ (m & 15)] = v;
-  }
-  __syncthreads();
+  const int nit = (ke - ks) >> 6;
 
   const int nw0 = (blockIdx.x * 4 + w) * 32 * NTW;
-  if (nw0 >= a.N) return;
   const u16 *brow[NTW];
   bool bok[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
     const int n = nw0 + 32 * j + l32;
+    if (a.packed) {
+      // tile t = nw0/32 + j: 4 KB per 64-wide K step, this lane's 16 bytes at 16 * lane
+      const int t = (nw0 >> 5) + j;
+      bok[j] = 32 * t < a.N;   // wavefront-uniform
+      brow[j] = a.packed + ((int64_t)t * (a.K >> 6) + (ks >> 6)) * 2048 + lane * 8;
+      continue;
+    }
     bok[j] = n < a.N;
     const int nn = bok[j] ? n : 0;
     const u16 *p;
@@ -75,6 +76,20 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
     brow[j] = p + ks + 32 * g;
   }
 
+  // activation pair -> LDS: one 1 KB load per (part, row); lane i lands in
+  // chunk i of the row and fetches logical chunk i ^ (row & 15). Rows past M
+  // and chunks past the range load valid addresses whose results are never used.
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int rr = w * 16 + q;          // 0..63 = part * 32 + row
+    const int part = rr >> 5, m = rr & 31;
+    const int c = lane ^ (m & 15);
+    const int k = ks + min(8 * c, (ke - ks) - 8);
+    const int mm = m < a.M ? m : 0;
+    const u16 *src = (part ? a.A_lo : a.A_hi) + (int64_t)mm * a.K + k;
+    __builtin_amdgcn_global_load_lds((const void *)src, GEMV_LDS(&sA[part][m][0]), 16, 0, 0);
+  }
+
   f32x16 acc[NTW];
 #pragma unroll
   for (int j = 0; j < NTW; ++j)
@@ -84,13 +99,13 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
   // K order inside a 64-step: lane group g supplies k = 32 g + 8 q + (0..7) at
   // matrix-core step q, identically for the activation and the weights.
   u32x4 ring[DEPTH][NTW][4];
-  const int nit = (ke - ks) >> 6;
   auto load = [&](u32x4 (&B)[NTW][4], int it) {
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        B[j][q] = bok[j] ? *(const u32x4 *)(brow[j] + 64 * it + 8 * q) : u32x4{0, 0, 0, 0};
+        B[j][q] = bok[j] ? *(const u32x4 *)(brow[j] + (a.packed ? 2048 * it + 512 * q : 64 * it + 8 * q))
+                         : u32x4{0, 0, 0, 0};
   };
   auto compute = [&](u32x4 (&B)[NTW][4], int it) {
 #pragma unroll
@@ -108,6 +123,11 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
 #pragma unroll
   for (int d = 0; d < DEPTH; ++d)
     if (d < nit) load(ring[d], d);
+  // wait for this wavefront's loads (the activation rows it staged, and the
+  // ring prologue the first step needs anyway), then for everyone's rows
+  GEMV_WAIT_VMCNT(0);
+  __syncthreads();
+
   for (int it0 = 0; it0 < nit; it0 += DEPTH) {
 #pragma unroll
     for (int d = 0; d < DEPTH; ++d) {
@@ -118,12 +138,13 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
       }
     }
   }
+  if (nw0 >= a.N) return;
 
   float *out = a.part + (int64_t)blockIdx.y * a.M * a.N;
 #pragma unroll
   for (int j = 0; j < NTW; ++j) {
     const int n = nw0 + 32 * j + l32;
-    if (!bok[j]) continue;
+    if (!bok[j] || n >= a.N) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int m = 8 * (r >> 2) + 4 * g + (r & 3);
@@ -133,6 +154,43 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
 }
 
 int gemv_ntw(int N) { return N > 8192 ? 2 : 1; }
+
+// One thread per 16-byte piece of the tile-ordered copy.
+__global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, const u16 *B2, int n_seg, int N,
+                                  int K, u16 *dst, int64_t pieces) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= pieces) return;
+  const int lane = (int)(idx & 63), q = (int)((idx >> 6) & 3);
+  const int64_t blk = idx >> 8;               // (tile, step)
+  const int ksteps = K >> 6;
+  const int t = (int)(blk / ksteps), st = (int)(blk % ksteps);
+  const int n = 32 * t + (lane & 31);
+  const int k = 64 * st + 32 * (lane >> 5) + 8 * q;
+  u32x4 v = {0, 0, 0, 0};
+  if (n < N) {
+    const u16 *row;
+    if (b_mode == BMODE_GATEUP) {
+      const int b32 = n >> 5;
+      row = ((b32 & 1) ? B1 : B0) + (int64_t)((b32 >> 1) * 32 + (n & 31)) * K;
+    } else if (b_mode == BMODE_CONCAT3) {
+      const int seg = n / n_seg;
+      row = (seg == 0 ? B0 : (seg == 1 ? B1 : B2)) + (int64_t)(n - seg * n_seg) * K;
+    } else {
+      row = B0 + (int64_t)n * K;
+    }
+    v = *(const u32x4 *)(row + k);
+  }
+  *(u32x4 *)(dst + idx * 8) = v;
+}
+
+hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
+                             int N, int K, uint16_t *dst, hipStream_t s) {
+  if (K % 64) return hipErrorInvalidValue;
+  const int64_t pieces = (int64_t)((N + 31) / 32) * (K / 64) * 256;
+  hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, b_mode, B0, B1,
+                     B2, n_seg, N, K, dst, pieces);
+  return hipGetLastError();
+}
 
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t s) {
   if (a.k_chunk > KC_MAX || a.k_chunk % 64 || a.K % 64 || a.M > 32) return hipErrorInvalidValue;
@@ -245,54 +303,6 @@ hipError_t dec_resid_norm_launch(const DecodeArgs &d, const float *res, const fl
   return hipGetLastError();
 }
 
-// q = RoPE(rstd * sum part[:, :, 0:d]); k = RoPE(rstd * ...[d:2d]); v = rstd * ...[2d:3d].
-// One thread per channel pair; k and v go to cache slot pos[b] (bf16).
-__global__ void dec_qkv_combine_kernel(const DecodeArgs d, const float *part, int splits,
-                                       const float *ss, float *q, u16 *kc, u16 *vc) {
-  const int pairs = 3 * d.dim / 2;
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= d.batch * pairs) return;
-  const int b = idx / pairs, pc = idx % pairs;
-  const int n = 2 * pc;
-  const int N = 3 * d.dim;
-  const int64_t stride = (int64_t)d.batch * N;
-  float v0 = 0.f, v1 = 0.f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float2 p2 = *(const float2 *)(part + sp * stride + (int64_t)b * N + n);
-    v0 += p2.x;
-    v1 += p2.y;
-  }
-  const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
-  v0 *= r;
-  v1 *= r;
-  const int seg = n / d.dim, c = n - seg * d.dim;
-  const int hh = c / d.head_dim, e = c % d.head_dim;
-  if (seg < 2) {
-    const float2 cs = d.rope_tab[b * (d.head_dim / 2) + (e >> 1)];
-    const float a0 = v0 * cs.x - v1 * cs.y, a1 = v0 * cs.y + v1 * cs.x;
-    v0 = a0;
-    v1 = a1;
-  }
-  if (seg == 0) {
-    q[(int64_t)b * d.dim + c] = v0;
-    q[(int64_t)b * d.dim + c + 1] = v1;
-    return;
-  }
-  const int p = d.pos[b];
-  if (!pos_ok(p, d.max_seq)) return;
-  u16 *cache = seg == 1 ? kc : vc;
-  const int64_t o = (((int64_t)b * d.n_heads + hh) * d.max_seq + p) * d.head_dim + e;
-  *(uint32_t *)(cache + o) = pack2(v0, v1);
-}
-
-hipError_t dec_qkv_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *rstd,
-                                  float *q, uint16_t *kc, uint16_t *vc, hipStream_t s) {
-  const int n = d.batch * 3 * d.dim / 2;
-  hipLaunchKernelGGL(dec_qkv_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d, part, splits, rstd,
-                     q, kc, vc);
-  return hipGetLastError();
-}
-
 // u = SiLU(rstd * gate) * (rstd * up); gate/up partials are interleaved in blocks of 32.
 __global__ void dec_gateup_combine_kernel(const DecodeArgs d, const float *part, int splits,
                                           const float *ss, u16 *u_hi, u16 *u_lo) {
@@ -345,134 +355,167 @@ hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int s
 }
 
 // ------------------------------------------------------------------ cache attention
-// grid (chunk, head, sequence). 16 lanes share one cached key (8 channels
-// each), a wavefront covers 4 keys per step. Partial result of the chunk:
-// o_part = sum_j e^(s_j - m) v_j, ml_part = (m, sum_j e^(s_j - m)).
+// One workgroup per (head, sequence), fused with the Q/K/V split-K finish:
+//  1. q, k, v of the new token for this head: rstd * (sum of the projection
+//     partials in split order), RoPE on q and k at pos[b]; k and v (bf16) go to
+//     cache slot pos[b] and stay in LDS for the new key's own term;
+//  2. scores of the fp32 query against cached bf16 keys 0..pos-1 (16 lanes per
+//     key, 4 keys per wavefront instruction) plus the new key;
+//  3. softmax in fp32 (exp2, log2(e)/sqrt(hd) prescale), weighted sum of the
+//     cached values plus the new value;
+//  4. the normalised head output is written as the bf16 hi/lo pair the Wo
+//     projection consumes.
+// An invalid position writes nothing to the cache and yields NaN outputs.
 template <int HD>
-__global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const float *q, const u16 *kc,
-                                                       const u16 *vc, int chunk, int n_chunks,
-                                                       float *o_part, float *ml_part) {
+__global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
+                                                       const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
+                                                       u16 *a_lo) {
   constexpr int LPK = HD / 8;          // lanes per key
-  constexpr int KPW = 64 / LPK;        // keys per wavefront step
-  __shared__ float sc[1024];
+  constexpr int KPW = 64 / LPK;        // keys per wavefront instruction
+  constexpr int UNR = 4;               // instructions in flight per wavefront
+  __shared__ float sq[HD], sknew[HD], svnew[HD];
+  __shared__ float sc[2048 + 1];
   __shared__ float red[8];
   __shared__ float osum[4][KPW][HD];
-  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int kg = lane / LPK, d8 = lane % LPK;
   const int p = d.pos[b];
-  const int n_keys = pos_ok(p, d.max_seq) ? p + 1 : 0;
-  const int k0 = c * chunk;
-  const int k1 = min(n_keys, k0 + chunk);
+  const bool ok = pos_ok(p, d.max_seq) && p <= 2048;
   const int64_t cbase = ((int64_t)b * d.n_heads + h) * d.max_seq * HD;
-  const int64_t slot = (int64_t)((b * d.n_heads + h) * n_chunks + c);
-
-  float qv[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) qv[i] = q[(int64_t)b * d.dim + h * HD + d8 * 8 + i];
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
-  // scores (log2 domain)
-  for (int kb = k0 + w * KPW; kb < k1; kb += 4 * KPW) {
-    const int key = kb + kg;
-    float s = 0.f;
-    if (key < k1) {
-      float kv[8];
-      unpack8(*(const u32x4 *)(kc + cbase + (int64_t)key * HD + d8 * 8), kv);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], kv[i], s);
+  // ---- 1. q, k, v of the new token (threads 0..HD-1: channel e)
+  if (tid < HD) {
+    const int e = tid;
+    const int N = 3 * d.dim;
+    const int64_t stride = (int64_t)d.batch * N;
+    const float *pp = part + (int64_t)b * N + h * HD + e;
+    float q = 0.f, k = 0.f, v = 0.f;
+    for (int sp = 0; sp < splits; ++sp) {
+      q += pp[sp * stride];
+      k += pp[sp * stride + d.dim];
+      v += pp[sp * stride + 2 * d.dim];
     }
-#pragma unroll
-    for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o, 64);
-    if (d8 == 0 && key < k1) sc[key - k0] = s * scale;
+    const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
+    q *= r;
+    k *= r;
+    v *= r;
+    const float qp = __shfl_xor(q, 1, 64), kp = __shfl_xor(k, 1, 64);
+    const float2 cs = d.rope_tab[b * (HD / 2) + (e >> 1)];
+    q = (e & 1) ? qp * cs.y + q * cs.x : q * cs.x - qp * cs.y;
+    k = (e & 1) ? kp * cs.y + k * cs.x : k * cs.x - kp * cs.y;
+    // the cache holds bf16: the new key/value enter attention as stored
+    const u16 kb = f2bf(k), vb = f2bf(v);
+    sq[e] = q;
+    sknew[e] = bf2f(kb);
+    svnew[e] = bf2f(vb);
+    if (ok) {
+      kc[cbase + (int64_t)p * HD + e] = kb;
+      vc[cbase + (int64_t)p * HD + e] = vb;
+    }
   }
   __syncthreads();
-  const int nk = max(k1 - k0, 0);
+  const int nk = ok ? p : 0;    // cached keys 0..p-1; key p is the new one
+
+  // ---- 2. scores (log2 domain) of cached keys
+  const int kg = lane / LPK, d8 = lane % LPK;
+  float qv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) qv[i] = sq[d8 * 8 + i];
+  for (int kb0 = w * KPW * UNR; kb0 < nk; kb0 += 4 * KPW * UNR) {
+    u32x4 kr[UNR];
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int key = kb0 + u * KPW + kg;
+      kr[u] = key < nk ? *(const u32x4 *)(kc + cbase + (int64_t)key * HD + d8 * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int key = kb0 + u * KPW + kg;
+      float kv[8];
+      unpack8(kr[u], kv);
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], kv[i], s);
+#pragma unroll
+      for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o, 64);
+      if (d8 == 0 && key < nk) sc[key] = s * scale;
+    }
+  }
+  if (tid < 64) {   // the new key's score (one wavefront)
+    float s = 0.f;
+    for (int e = lane; e < HD; e += 64) s += sq[e] * sknew[e];
+    s = wave_sum(s);
+    if (lane == 0) sc[nk] = s * scale;
+  }
+  __syncthreads();
+
+  // ---- 3. softmax over nk + 1 scores
+  const int tot = nk + 1;
   float mx = -INFINITY;
-  for (int i = tid; i < nk; i += 256) mx = fmaxf(mx, sc[i]);
+  for (int i = tid; i < tot; i += 256) mx = fmaxf(mx, sc[i]);
   mx = wave_max(mx);
   if (lane == 0) red[w] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
   float ls = 0.f;
-  for (int i = tid; i < nk; i += 256) {
+  for (int i = tid; i < tot; i += 256) {
     const float e = exp2f(sc[i] - mx);
     sc[i] = e;
     ls += e;
   }
-  ls = block_sum(ls, red);  // block_sum syncs before use of sc below
+  ls = block_sum(ls, red);   // contains barriers: sc is complete afterwards
 
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int kb = k0 + w * KPW; kb < k1; kb += 4 * KPW) {
-    const int key = kb + kg;
-    if (key < k1) {
-      float vv[8];
-      unpack8(*(const u32x4 *)(vc + cbase + (int64_t)key * HD + d8 * 8), vv);
-      const float pr = sc[key - k0];
+  for (int kb0 = w * KPW * UNR; kb0 < nk; kb0 += 4 * KPW * UNR) {
+    u32x4 vr[UNR];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pr, vv[i], acc[i]);
+    for (int u = 0; u < UNR; ++u) {
+      const int key = kb0 + u * KPW + kg;
+      vr[u] = key < nk ? *(const u32x4 *)(vc + cbase + (int64_t)key * HD + d8 * 8) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int u = 0; u < UNR; ++u) {
+      const int key = kb0 + u * KPW + kg;
+      if (key < nk) {
+        float vv[8];
+        unpack8(vr[u], vv);
+        const float pr = sc[key];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(pr, vv[i], acc[i]);
+      }
     }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) osum[w][kg][d8 * 8 + i] = acc[i];
   __syncthreads();
-  for (int e = tid; e < HD; e += 256) {
-    float t = 0.f;
+
+  // ---- 4. normalised output (+ the new value's term) as a bf16 pair
+  if (tid < HD) {
+    const int e = tid;
+    float o = sc[nk] * svnew[e];
     for (int ww = 0; ww < 4; ++ww)
-      for (int g2 = 0; g2 < KPW; ++g2) t += osum[ww][g2][e];
-    o_part[slot * HD + e] = t;
-  }
-  if (tid == 0) {
-    ml_part[slot * 2] = nk > 0 ? mx : -INFINITY;
-    ml_part[slot * 2 + 1] = nk > 0 ? ls : 0.f;
-  }
-}
-
-hipError_t dec_attn_launch(const DecodeArgs &d, const float *q, const uint16_t *kc, const uint16_t *vc,
-                           int chunk, int n_chunks, float *o_part, float *ml_part, hipStream_t s) {
-  if (chunk > 1024) return hipErrorInvalidValue;
-  dim3 grid(n_chunks, d.n_heads, d.batch);
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(dec_attn_kernel<128>, grid, dim3(256), 0, s, d, q, kc, vc, chunk, n_chunks, o_part,
-                       ml_part);
-  else if (d.head_dim == 64)
-    hipLaunchKernelGGL(dec_attn_kernel<64>, grid, dim3(256), 0, s, d, q, kc, vc, chunk, n_chunks, o_part,
-                       ml_part);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
-}
-
-// Merge the chunks of one (sequence, head) in chunk order; output as bf16 pair.
-__global__ void dec_attn_combine_kernel(const DecodeArgs d, const float *o_part, const float *ml_part,
-                                        int n_chunks, u16 *a_hi, u16 *a_lo) {
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int64_t slot0 = (int64_t)(b * d.n_heads + h) * n_chunks;
-  float m = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, ml_part[(slot0 + c) * 2]);
-  for (int e = threadIdx.x; e < d.head_dim; e += blockDim.x) {
-    float l = 0.f, o = 0.f;
-    for (int c = 0; c < n_chunks; ++c) {
-      const float mc = ml_part[(slot0 + c) * 2];
-      if (mc == -INFINITY) continue;
-      const float f = exp2f(mc - m);
-      l += ml_part[(slot0 + c) * 2 + 1] * f;
-      o += o_part[(slot0 + c) * d.head_dim + e] * f;
-    }
-    const float v = o / l;  // no keys (invalid position): 0/0 = NaN
+      for (int g2 = 0; g2 < KPW; ++g2) o += osum[ww][g2][e];
+    const float v = ok ? o / ls : __builtin_nanf("");
     u16 hi, lo;
     split_pair(v, hi, lo);
-    const int64_t oo = (int64_t)b * d.dim + h * d.head_dim + e;
+    const int64_t oo = (int64_t)b * d.dim + h * HD + e;
     a_hi[oo] = hi;
     a_lo[oo] = lo;
   }
 }
 
-hipError_t dec_attn_combine_launch(const DecodeArgs &d, const float *o_part, const float *ml_part,
-                                   int n_chunks, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s) {
-  hipLaunchKernelGGL(dec_attn_combine_kernel, dim3(d.n_heads, d.batch), dim3(128), 0, s, d, o_part,
-                     ml_part, n_chunks, a_hi, a_lo);
+hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
+                           uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s) {
+  if (d.max_seq > 2048 + 1) return hipErrorInvalidValue;
+  dim3 grid(d.n_heads, d.batch);
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL(dec_attn_kernel<128>, grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo);
+  else if (d.head_dim == 64)
+    hipLaunchKernelGGL(dec_attn_kernel<64>, grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -98,9 +98,15 @@ struct GemvArgs {
   int b_mode;
   const uint16_t *B0, *B1, *B2;
   int n_seg;
+  const uint16_t *packed;        // optional: the same matrix in 32-row tile order (see pack_tiles_launch)
   float *part;                   // [splits, M, N]
 };
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
+// Copy B (row mapping b_mode as in GemvArgs) into tile order: 4 KB block per
+// (32-row tile t, 64-wide K step s), piece (q, lane g*32+j) = B[32t+j][64s+32g+8q..+7];
+// rows >= N are zero. dst holds ceil(N/32)*32 x K elements.
+hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
+                             int N, int K, uint16_t *dst, hipStream_t s);
 int gemv_ntw(int N);               // 32-column tiles per wavefront used for N
 constexpr int kGemvMaxChunk = 512; // largest K range of one workgroup
 
@@ -115,11 +121,11 @@ struct DecodeArgs {
 hipError_t dec_embed_norm_launch(const DecodeArgs &d, const uint16_t *emb, const int32_t *tok,
                                  const uint16_t *g, float *x, float *ss, uint16_t *xg_hi,
                                  uint16_t *xg_lo, hipStream_t s);
-// q (f32), cache writes of k, v for slot pos[b]
-hipError_t dec_qkv_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *ss,
-                                  float *q, uint16_t *kc, uint16_t *vc, hipStream_t s);
-hipError_t dec_attn_launch(const DecodeArgs &d, const float *q, const uint16_t *kc, const uint16_t *vc,
-                           int chunk, int n_chunks, float *o_part, float *ml_part, hipStream_t s);
+// Attention of one new token per sequence over the KV cache, fused with the
+// finish of the Q/K/V split-K partials (rstd, RoPE, cache append at pos[b]);
+// writes the head outputs as a bf16 pair [batch, dim]. max_seq <= 2048.
+hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
+                           uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s);
 // out = res + sum(part); ss of out; out*g as pair
 hipError_t dec_resid_norm_launch(const DecodeArgs &d, const float *res, const float *part, int splits,
                                  const uint16_t *g, float *out, float *ss, uint16_t *og_hi,
@@ -128,7 +134,6 @@ hipError_t dec_gateup_combine_launch(const DecodeArgs &d, const float *part, int
                                      const float *ss, uint16_t *u_hi, uint16_t *u_lo, hipStream_t s);
 hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *ss,
                                    float *logits, hipStream_t s);
-hipError_t dec_attn_combine_launch(const DecodeArgs &d, const float *o_part, const float *ml_part,
-                                   int n_chunks, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s);
+
 
 }  // namespace llama

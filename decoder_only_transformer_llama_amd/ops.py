@@ -166,8 +166,22 @@ class Model:
         self._arr = arr
         _dev(tok_embeddings, final_norm, output)
         self.wstruct = L.ModelWeights(tok_embeddings.data_ptr(), ctypes.cast(arr, ctypes.POINTER(L.BlockWeights)),
-                                      final_norm.data_ptr(), output.data_ptr())
+                                      final_norm.data_ptr(), output.data_ptr(), None)
         self._ws = {}
+        self.decode_pack = None
+
+    def pack_for_decode(self) -> torch.Tensor:
+        """Repack the projections into matrix-core tile order for decode (a
+        load-time copy of the weights); later decode calls stream from it."""
+        lib = L.load()
+        n = ctypes.c_size_t(0)
+        L.check(lib.llama_decode_pack_size(ctypes.byref(self.cfg), ctypes.byref(n)), "llama_decode_pack_size")
+        pack = torch.empty(n.value, dtype=torch.uint8, device=self.tensors[0].device)
+        L.check(lib.llama_pack_decode_weights(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(pack),
+                                              pack.numel(), _stream()), "llama_pack_decode_weights")
+        self.decode_pack = pack
+        self.wstruct.decode_pack = pack.data_ptr()
+        return pack
 
     def workspace(self, op: int, batch: int, seq: int, device) -> torch.Tensor:
         key = (op, batch, seq)

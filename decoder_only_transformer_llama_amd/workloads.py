@@ -41,9 +41,11 @@ class DecodeWorkload:
     v_cache: torch.Tensor
 
 
-def decode_workload(wid: int, device="cuda") -> DecodeWorkload:
+def decode_workload(wid: int, device="cuda", pack: bool = True) -> DecodeWorkload:
     """Model decode step: every sequence at position decode_pos with cache slots
-    0..decode_pos-1 pre-filled with seeded N(0, 1) keys and values."""
+    0..decode_pos-1 pre-filled with seeded N(0, 1) keys and values. With
+    `pack`, the projections are also repacked into tile order for decode (a
+    load-time copy of the weights)."""
     w = I.workload(wid)
     layers = [I.block_weights(w, l, device=device) for l in range(w.n_layers)]
     gl = I.model_globals(w, device=device)
@@ -58,6 +60,8 @@ def decode_workload(wid: int, device="cuda") -> DecodeWorkload:
         kc[l].copy_(k)
         vc[l].copy_(v)
         del k, v
+    if pack:
+        m.pack_for_decode()
     toks = I.tokens(w, (w.batch,), device=device)
     pos = torch.full((w.batch,), w.decode_pos, dtype=torch.int32, device=device)
     return DecodeWorkload(w, layers, gl, m, toks, pos, kc, vc)

@@ -105,12 +105,15 @@ typedef struct llama_block_weights {
 
 /* Whole-model weights: token embedding [vocab, dim], `layers` is a HOST
  * array of n_layers block-weight structs (holding device pointers), the final
- * norm gain [dim] and the untied output head [vocab, dim]. */
+ * norm gain [dim] and the untied output head [vocab, dim]. decode_pack is
+ * NULL, or a device buffer filled by llama_pack_decode_weights from these same
+ * weights: llama_model_decode then streams the projections from it. */
 typedef struct llama_model_weights {
   const void *tok_embeddings;
   const llama_block_weights *layers;
   const void *final_norm;
   const void *output;
+  const void *decode_pack;
 } llama_model_weights;
 
 /* SwiGLU hidden width: int(2*4*dim/3) rounded up to a multiple of
@@ -195,11 +198,26 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
  * final norm and head give logits [batch, vocab] f32. The caches have the
  * layout of llama_model_forward. A pos[b] outside [0, max_seq) cannot be
  * checked on the host: for such a row nothing is written to the cache and
- * its logits are NaN. batch <= 32. bf16 configs only. The cache-slot write
+ * its logits are NaN. batch <= 32, max_seq <= 2048. bf16 configs only. The cache-slot write
  * is idempotent, so a step can be re-run. */
 int llama_model_decode(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
                        const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* Decode weight pack: every projection of every block (Wq|Wk|Wv, Wo,
+ * W_gate/W_up interleaved in blocks of 32 rows, W_down) and the output head,
+ * copied into matrix-core tile order: for each 32-row tile and each 64-wide
+ * K step one 4 KB block whose 16-byte piece for lane (g, j), step q is
+ * W[32 t + j][64 s + 32 g + 8 q .. +7]. One decode step then reads every
+ * weight byte in contiguous 1 KB runs. This is a load-time transform of the
+ * model (the pack costs the size of the weights once more in HBM); it does
+ * not change any result. Rows past a matrix's height are zero.
+ * llama_decode_pack_size: bytes of the pack for config c (host, *bytes).
+ * llama_pack_decode_weights: fill dst (device, dst_bytes >= that size) from
+ * w on `stream`. bf16 configs only. Errors as llama_model_decode validates. */
+int llama_decode_pack_size(const llama_config *c, size_t *bytes);
+int llama_pack_decode_weights(const llama_config *c, const llama_model_weights *w, void *dst,
+                              size_t dst_bytes, void *stream);
 
 /* Workspace bytes for `op` at the given batch and seq (seq ignored for decode).
  * Writes *bytes (host pointer). Errors as the matching entry point would report

@@ -44,7 +44,7 @@ def test_header_compiles(lang, compiler, tmp_path):
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(L.LlamaConfig) == 40
     assert ctypes.sizeof(L.BlockWeights) == 9 * 8
-    assert ctypes.sizeof(L.ModelWeights) == 4 * 8
+    assert ctypes.sizeof(L.ModelWeights) == 5 * 8
 
 
 def test_hidden_dim_and_status_strings():
@@ -126,3 +126,10 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                                   1 << 40, None) == L.LLAMA_ERR_NULL
     assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE,
                                   16, None) == L.LLAMA_ERR_WORKSPACE
+    n = ctypes.c_size_t()
+    assert lib.llama_decode_pack_size(ctypes.byref(c), ctypes.byref(n)) == 0
+    # 32 layers of (3d + d + 2h) x d + d x h, plus the head: exactly the weight bytes (all heights are multiples of 32)
+    assert n.value == (32 * (4 * 4096 * 4096 + 3 * 4096 * 11008) + 32000 * 4096) * 2
+    assert lib.llama_pack_decode_weights(ctypes.byref(c), ctypes.byref(mw), FAKE, 16, None) == L.LLAMA_ERR_WORKSPACE
+    assert lib.llama_pack_decode_weights(ctypes.byref(cf), ctypes.byref(mw), FAKE, 1 << 40, None) == \
+        L.LLAMA_ERR_UNSUPPORTED

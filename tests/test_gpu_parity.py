@@ -256,6 +256,25 @@ def test_model_prefill_then_decode():
     assert e1 < TOL_BF16 and e2 < TOL_BF16
 
 
+def test_decode_packed_weights_bitwise_equal():
+    """The tile-ordered weight pack feeds the same products in the same order:
+    decode logits and cache writes are bitwise identical with and without it."""
+    w, m, layers, gl = small_model()
+    B = w.batch
+    toks = I.tokens(w, (B,), device="cuda")
+    pos = torch.tensor([5, 17, 0][:B], dtype=torch.int32, device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    kc.normal_(generator=torch.Generator("cuda").manual_seed(7))
+    vc.normal_(generator=torch.Generator("cuda").manual_seed(8))
+    kc2, vc2 = kc.clone(), vc.clone()
+    ref = m.decode(toks, pos, kc, vc).clone()
+    m.pack_for_decode()
+    got = m.decode(toks, pos, kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, got)
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+
+
 def test_decode_invalid_position_gives_nan_row():
     w, m, layers, gl = small_model()
     B = w.batch
