@@ -229,6 +229,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
+    ap.add_argument("--decode-only", action="store_true", help="skip the prefill leg (diagnostic runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path here runs on a single MI355X with no sharding or "
@@ -237,6 +238,11 @@ def main() -> int:
     import torch
     torch.cuda.set_device(0)
     t_start = time.time()
+    if args.decode_only:
+        dec = bench_decode(args, torch)
+        print(f"# decode: {dec['ms']:.3f} ms/step (eager {dec['ms_eager']:.3f}), {dec['tokens_per_s']:.0f} tok/s, "
+              f"{dec['hbm_gbs']:.0f} GB/s; kernels {json.dumps(dec['per_kernel_ms'])}", file=sys.stderr, flush=True)
+        return 0
     pf = bench_prefill(args, torch)
     print(f"# prefill: {pf['ms']:.3f} ms/step, {pf['tokens_per_s']:.0f} tok/s, block {pf['block_tflops']:.1f} "
           f"TFLOP/s; kernels {json.dumps(pf['per_kernel'])}", file=sys.stderr, flush=True)

@@ -10,7 +10,8 @@ import ctypes
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libllama_mi355x.so")
+# LLAMA_MI355X_LIB may point at another build of the same library (A/B timing).
+LIB_PATH = os.environ.get("LLAMA_MI355X_LIB") or os.path.join(HERE, "libllama_mi355x.so")
 
 LLAMA_F32, LLAMA_BF16 = 0, 1
 LLAMA_OK = 0

@@ -184,7 +184,10 @@ void gemv_split(int N, int K, int &splits, int &k_chunk) {
   const int per_wg = 128 * gemv_ntw(N);
   const int n_wg = (N + per_wg - 1) / per_wg;
   const int ksteps = K / 64;
-  const int s = std::max(1, std::min(ksteps, (512 + n_wg - 1) / n_wg));
+#ifndef GEMV_TARGET_WGS
+#define GEMV_TARGET_WGS 256
+#endif
+  const int s = std::max(1, std::min(ksteps, (GEMV_TARGET_WGS + n_wg - 1) / n_wg));
   const int per = std::min((ksteps + s - 1) / s, kGemvMaxChunk / 64);
   k_chunk = per * 64;
   splits = (K + k_chunk - 1) / k_chunk;

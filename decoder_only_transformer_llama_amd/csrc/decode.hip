@@ -34,13 +34,16 @@ DEV bool pos_ok(int p, int max_seq) { return p >= 0 && p < max_seq; }
 // weights are already streaming from HBM into a ring of B-operand registers,
 // so the two latencies overlap; afterwards DEPTH steps of 64 K stay in flight
 // per wavefront.
-constexpr int KC_MAX = 512;
+#ifndef GEMV_KC_MAX
+#define GEMV_KC_MAX 512
+#endif
+constexpr int KC_MAX = GEMV_KC_MAX;
 
 #define GEMV_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 #define GEMV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
 template <int NTW, int DEPTH>
-__global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const GemvArgs a) {
   __shared__ u32x4 sA[2][32][KC_MAX / 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -79,15 +82,17 @@ __global__ __launch_bounds__(256, 2) void gemv_kernel(const GemvArgs a) {
   // activation pair -> LDS: one 1 KB load per (part, row); lane i lands in
   // chunk i of the row and fetches logical chunk i ^ (row & 15). Rows past M
   // and chunks past the range load valid addresses whose results are never used.
+  constexpr int SEGS = KC_MAX / 512;   // 1 KB segments per staged row
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int rr = w * 16 + q;          // 0..63 = part * 32 + row
+  for (int q = 0; q < 16 * SEGS; ++q) {
+    const int rr = w * 16 + q % 16;     // 0..63 = part * 32 + row
+    const int seg = q / 16;
     const int part = rr >> 5, m = rr & 31;
-    const int c = lane ^ (m & 15);
+    const int c = (seg * 64 + lane) ^ (m & 15);
     const int k = ks + min(8 * c, (ke - ks) - 8);
     const int mm = m < a.M ? m : 0;
     const u16 *src = (part ? a.A_lo : a.A_hi) + (int64_t)mm * a.K + k;
-    __builtin_amdgcn_global_load_lds((const void *)src, GEMV_LDS(&sA[part][m][0]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const void *)src, GEMV_LDS(&sA[part][m][seg * 64]), 16, 0, 0);
   }
 
   f32x16 acc[NTW];
@@ -372,7 +377,10 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
                                                        u16 *a_lo) {
   constexpr int LPK = HD / 8;          // lanes per key
   constexpr int KPW = 64 / LPK;        // keys per wavefront instruction
-  constexpr int UNR = 4;               // instructions in flight per wavefront
+#ifndef DEC_ATTN_UNROLL
+#define DEC_ATTN_UNROLL 4
+#endif
+  constexpr int UNR = DEC_ATTN_UNROLL; // instructions in flight per wavefront
   __shared__ float sq[HD], sknew[HD], svnew[HD];
   __shared__ float sc[2048 + 1];
   __shared__ float red[8];

@@ -108,7 +108,10 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
 hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
                              int N, int K, uint16_t *dst, hipStream_t s);
 int gemv_ntw(int N);               // 32-column tiles per wavefront used for N
-constexpr int kGemvMaxChunk = 512; // largest K range of one workgroup
+#ifndef GEMV_KC_MAX
+#define GEMV_KC_MAX 512
+#endif
+constexpr int kGemvMaxChunk = GEMV_KC_MAX; // largest K range of one workgroup
 
 struct DecodeArgs {
   int batch, dim, n_heads, head_dim, hidden, max_seq, vocab;
