@@ -26,46 +26,102 @@ namespace llama {
 
 DEV int perm23(int i) { return (i & ~12) | ((i & 4) << 1) | ((i & 8) >> 1); }
 // LDS chunk swizzles (gfx950 serves a 16-byte read 16 lanes per pass over a
-// 256-byte bank window): rows of 256 bytes XOR the chunk with row mod 16, rows
-// of 128 bytes with (row / 2) mod 8, so any 16 consecutive rows read at one
-// logical chunk hit 16 distinct 16-byte slots.
+// 256-byte bank window): K rows of 256 bytes XOR the chunk with row mod 16,
+// K rows of 128 bytes with (row / 2) mod 8, v^T rows of 64 bytes with
+// (row / 4) mod 4, so any 16 consecutive rows read at one logical chunk hit 16
+// distinct 16-byte slots.
 template <int CHUNKS>
 DEV int rswz(int row) { return CHUNKS == 16 ? (row & 15) : ((row >> 1) & 7); }
+DEV int vswz(int row) { return (row >> 2) & 3; }
+
+#define ATT_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+#define ATT_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// (sequence*head, query tile) of workgroup `k`. Causal work grows with the
+// query tile, so when the tile count is even the first half of the grid takes
+// the long tiles nqt-1-i, longest first, and the second half the short tile i:
+// when the dispatcher fills CUs round-robin, workgroups k and k + total/2 share
+// a CU and every CU gets about the same number of key tiles.
+DEV void attn_tile_of(int k, int nqt, int bh_count, int &bh, int &qt) {
+  if ((nqt & 1) == 0) {
+    const int halfn = (nqt >> 1) * bh_count;
+    const int half = k / halfn, j = k % halfn;
+    bh = j / (nqt >> 1);
+    const int i = j % (nqt >> 1);
+    qt = half == 0 ? nqt - 1 - i : i;
+  } else {
+    bh = k / nqt;
+    qt = nqt - 1 - k % nqt;
+  }
+}
 
 template <int HD, bool QKPAIR, bool VPAIR>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) {
-  constexpr int KT = 64;            // keys per tile
-  constexpr int KCH = HD / 8;       // 16-byte chunks per K row
-  constexpr int NKK = HD / 16;      // k-steps of the score product
-  constexpr int NEB = HD / 32;      // 32-wide blocks of the head dimension
-  constexpr int KTILE = KT * KCH;   // u32x4 per K tile
-  constexpr int VTILE = HD * 8;     // u32x4 per V^T tile (8 chunks of 8 keys)
-  __shared__ u32x4 sk[KTILE], skl[QKPAIR ? KTILE : 1], sv[VTILE], svl[VPAIR ? VTILE : 1];
+  constexpr int KT = 32;                         // keys per tile
+  constexpr int KCH = HD / 8;                    // 16-byte chunks per K row
+  constexpr int NKK = HD / 16;                   // k-steps of the score product
+  constexpr int NEB = HD / 32;                   // 32-wide blocks of the head dimension
+  constexpr int KTILE = KT * KCH;                // u32x4 per K tile
+  constexpr int VTILE = HD * 4;                  // u32x4 per v^T tile (4 chunks of 8 keys)
+  constexpr int STAGE = KTILE * (QKPAIR ? 2 : 1) + VTILE * (VPAIR ? 2 : 1);
+  constexpr int NST = 2;
+  constexpr int KBLK = KTILE / 64, VBLK = VTILE / 64;       // 1 KB blocks per tile
+  constexpr int NBLK = KBLK * (QKPAIR ? 2 : 1) + VBLK * (VPAIR ? 2 : 1);
+  static_assert(NBLK % 4 == 0, "blocks split evenly over 4 wavefronts");
+  __shared__ u32x4 smem[NST * STAGE];
 
   const int S = a.seq;
   const int nqt = (S + 127) / 128;
-  const int qt = nqt - 1 - blockIdx.x;  // longest (most keys) first
-  const int h = blockIdx.y, b = blockIdx.z;
+  int bh, qt;
+  attn_tile_of(blockIdx.x, nqt, a.batch * a.n_heads, bh, qt);
+  const int b = bh / a.n_heads, h = bh % a.n_heads;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
   const int q0 = qt * 128;
   const int qi = q0 + 32 * w + l32;          // this lane's query
   const int qwave_max = q0 + 32 * w + 31;
   const int64_t tok0 = (int64_t)b * S;
+  const int64_t vbase = ((int64_t)b * a.n_heads + h) * HD * a.vt_stride;
+
+  // ---- direct-to-LDS tile loads: block q of this wavefront, lane i -> LDS slot i
+  auto issue = [&](int kt) {
+    u32x4 *st = smem + (kt % NST) * STAGE;
+#pragma unroll
+    for (int qb = 0; qb < NBLK / 4; ++qb) {
+      const int blk = w * (NBLK / 4) + qb;
+      const u16 *src;
+      u32x4 *dst;
+      if (blk < KBLK * (QKPAIR ? 2 : 1)) {
+        const int part = blk / KBLK, kb = blk % KBLK;
+        const int row = kb * (64 / KCH) + lane / KCH;
+        const int c = (lane % KCH) ^ rswz<KCH>(row);
+        const int key = min(kt * KT + row, S - 1);   // rows past S load a valid key; masked later
+        src = (part ? a.kl : a.kh) + (tok0 + key) * a.dim + h * HD + 8 * c;
+        dst = st + part * KTILE + kb * 64;
+      } else {
+        const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
+        const int part = vblk / VBLK, vb = vblk % VBLK;
+        const int e = vb * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ vswz(e);
+        src = (part ? a.vtl : a.vth) + vbase + (int64_t)e * a.vt_stride + kt * KT + 8 * c;
+        dst = st + KTILE * (QKPAIR ? 2 : 1) + part * VTILE + vb * 64;
+      }
+      __builtin_amdgcn_global_load_lds((const void *)src, ATT_LDS(dst), 16, 0, 0);
+    }
+  };
+
+  const int kend = min(S, q0 + 128);
+  const int n_kt = (kend + KT - 1) / KT;
+  issue(0);
 
   // q fragments (B operand of S^T = K Q^T): q[qi][16kk + 8g .. +7]
   bf16x8 qh[NKK], ql[QKPAIR ? NKK : 1];
   {
-    const int64_t base = (tok0 + qi) * a.dim + h * HD + 8 * g;
+    const int64_t base = (tok0 + min(qi, S - 1)) * a.dim + h * HD + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 v = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
-      if (qi < S) {
-        v = *(const u32x4 *)(a.qh + base + 16 * kk);
-        if (QKPAIR) vl = *(const u32x4 *)(a.ql + base + 16 * kk);
-      }
-      qh[kk] = as_bf16x8(v);
-      if (QKPAIR) ql[kk] = as_bf16x8(vl);
+      qh[kk] = as_bf16x8(*(const u32x4 *)(a.qh + base + 16 * kk));
+      if (QKPAIR) ql[kk] = as_bf16x8(*(const u32x4 *)(a.ql + base + 16 * kk));
     }
   }
 
@@ -76,92 +132,42 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     for (int r = 0; r < 16; ++r) acc_o[e][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
-
-  const int kend = min(S, q0 + 128);
-  const int n_kt = (kend + KT - 1) / KT;
-  const int64_t vbase = ((int64_t)b * a.n_heads + h) * HD * a.vt_stride;
+  const int krow = perm23(l32);   // key (within the tile) this lane supplies as A-operand row
 
   for (int kt = 0; kt < n_kt; ++kt) {
+    ATT_WAIT_VMCNT(0);                 // this wavefront's loads of tile kt (and the q fragments)
+    __builtin_amdgcn_s_barrier();      // everyone's; everyone is done with tile kt-1
+    if (kt + 1 < n_kt) issue(kt + 1);  // overwrites the buffer of tile kt-1
     const int kt0 = kt * KT;
-    __syncthreads();
-    // ---- stage K (and lo) rows and V^T (and lo) rows of this key tile
-#pragma unroll
-    for (int p = 0; p < KTILE / 256; ++p) {
-      const int idx = tid + p * 256;
-      const int row = idx / KCH, ch = idx % KCH;
-      const int key = kt0 + row;
-      u32x4 v = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
-      if (key < S) {
-        const int64_t o = (tok0 + key) * a.dim + h * HD + ch * 8;
-        v = *(const u32x4 *)(a.kh + o);
-        if (QKPAIR) vl = *(const u32x4 *)(a.kl + o);
-      }
-      const int so = row * KCH + (ch ^ rswz<KCH>(row));
-      sk[so] = v;
-      if (QKPAIR) skl[so] = vl;
-    }
-#pragma unroll
-    for (int p = 0; p < VTILE / 256; ++p) {
-      const int idx = tid + p * 256;
-      const int e = idx >> 3, ch = idx & 7;
-      const int key = kt0 + ch * 8;
-      u32x4 v = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
-      const int64_t o = vbase + (int64_t)e * a.vt_stride + key;
-      if (key + 8 <= S) {
-        v = *(const u32x4 *)(a.vth + o);
-        if (VPAIR) vl = *(const u32x4 *)(a.vtl + o);
-      } else if (key < S) {
-        uint32_t hv[8], lv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          hv[i] = key + i < S ? a.vth[o + i] : 0;
-          lv[i] = (VPAIR && key + i < S) ? a.vtl[o + i] : 0;
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[i] = hv[2 * i] | (hv[2 * i + 1] << 16);
-          vl[i] = lv[2 * i] | (lv[2 * i + 1] << 16);
-        }
-      }
-      const int so = e * 8 + (ch ^ rswz<8>(e));
-      sv[so] = v;
-      if (VPAIR) svl[so] = vl;
-    }
-    __syncthreads();
+    if (kt0 > qwave_max) continue;     // whole tile above this wavefront's diagonal
+    const u32x4 *sk = smem + (kt % NST) * STAGE;
+    const u32x4 *skl = sk + KTILE;
+    const u32x4 *sv = sk + KTILE * (QKPAIR ? 2 : 1);
+    const u32x4 *svl = sv + VTILE;
 
-    // ---- scores S^T for the two 32-key halves
-    f32x16 s[2];
-    bool live[2];
+    // ---- scores S^T (32 keys x 32 queries)
+    f32x16 sc;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      live[t] = kt0 + 32 * t <= qwave_max && kt0 + 32 * t < S;
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[t][r] = 0.f;
-      if (!live[t]) continue;
-      const int krow = 32 * t + perm23(l32);
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
-        const bf16x8 kf = as_bf16x8(sk[so]);
-        s[t] = mfma32(kf, qh[kk], s[t]);
-        if (QKPAIR) {
-          s[t] = mfma32(as_bf16x8(skl[so]), qh[kk], s[t]);
-          s[t] = mfma32(kf, ql[kk], s[t]);
-        }
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
+      const bf16x8 kf = as_bf16x8(sk[so]);
+      sc = mfma32(kf, qh[kk], sc);
+      if (QKPAIR) {
+        sc = mfma32(as_bf16x8(skl[so]), qh[kk], sc);
+        sc = mfma32(kf, ql[kk], sc);
       }
     }
 
-    // ---- online softmax (fp32); lane holds keys of query qi
+    // ---- online softmax (fp32); lane holds 16 keys of query qi
     float mx = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt0 + 32 * t + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
-        const bool ok = live[t] && key <= qi && key < S;
-        s[t][r] = ok ? s[t][r] : -INFINITY;
-        mx = fmaxf(mx, s[t][r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt0 + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
+      const bool ok = key <= qi && key < S;
+      sc[r] = ok ? sc[r] : -INFINITY;
+      mx = fmaxf(mx, sc[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
@@ -170,13 +176,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2f((s[t][r] - m_use) * c);   // exp2(-inf) = 0 for masked keys
-        s[t][r] = p;
-        psum += p;
-      }
+    for (int r = 0; r < 16; ++r) {
+      const float pr = exp2f((sc[r] - m_use) * c);   // exp2(-inf) = 0 for masked keys
+      sc[r] = pr;
+      psum += pr;
+    }
     l_run = l_run * alpha + psum;
 #pragma unroll
     for (int e = 0; e < NEB; ++e)
@@ -185,22 +189,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
 
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      if (!live[t]) continue;
+    for (int s2 = 0; s2 < 2; ++s2) {
+      float pv[8];
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        float pv[8];
+      for (int i = 0; i < 8; ++i) pv[i] = sc[8 * s2 + i];
+      const bf16x8 pf = as_bf16x8(pack8(pv));
+      const int ch = 2 * s2 + g;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) pv[i] = s[t][8 * s2 + i];
-        const bf16x8 pf = as_bf16x8(pack8(pv));
-        const int ch = 4 * t + 2 * s2 + g;
-#pragma unroll
-        for (int e = 0; e < NEB; ++e) {
-          const int row = 32 * e + l32;
-          const int so = row * 8 + (ch ^ rswz<8>(row));
-          acc_o[e] = mfma32(as_bf16x8(sv[so]), pf, acc_o[e]);
-          if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), pf, acc_o[e]);
-        }
+      for (int e = 0; e < NEB; ++e) {
+        const int row = 32 * e + l32;
+        const int so = row * 4 + (ch ^ vswz(row));
+        acc_o[e] = mfma32(as_bf16x8(sv[so]), pf, acc_o[e]);
+        if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), pf, acc_o[e]);
       }
     }
   }
@@ -234,15 +234,33 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   }
 }
 
+// Zero v^T columns [seq, vt_stride) so partial key tiles multiply finite zeros.
+__global__ void vt_pad_zero_kernel(u16 *vth, u16 *vtl, int64_t rows, int seq, int vt_stride) {
+  const int pad = vt_stride - seq;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= rows * pad) return;
+  const int64_t o = (idx / pad) * vt_stride + seq + idx % pad;
+  vth[o] = 0;
+  if (vtl) vtl[o] = 0;
+}
+
 template <int HD, bool QKPAIR, bool VPAIR>
 static hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
-  dim3 grid((a.seq + 127) / 128, a.n_heads, a.batch);
-  hipLaunchKernelGGL((attn_prefill_kernel<HD, QKPAIR, VPAIR>), grid, dim3(256), 0, s, a);
+  const int nqt = (a.seq + 127) / 128;
+  hipLaunchKernelGGL((attn_prefill_kernel<HD, QKPAIR, VPAIR>), dim3(nqt * a.batch * a.n_heads), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, hipStream_t s) {
   if (a.batch * a.seq == 0) return hipSuccess;
+  if (a.seq % 32) {
+    const int64_t rows = (int64_t)a.batch * a.n_heads * a.head_dim;
+    const int64_t n = rows * (a.vt_stride - a.seq);
+    hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                       (u16 *)a.vth, v_pair ? (u16 *)a.vtl : (u16 *)nullptr, rows, a.seq, a.vt_stride);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
 #define ATTN_CASE(HD_, QK_, V_) \
   if (a.head_dim == HD_ && !!qk_pair == QK_ && !!v_pair == V_) return launch_t<HD_, QK_, V_>(a, s);
   ATTN_CASE(128, true, true)
