@@ -25,6 +25,33 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+COPY_CALIBRATION_BYTES = 1 << 30   # bytes read and written by each calibration copy
+
+# HBM bytes per launch of the roofline kernels, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE runs (decoder_only_transformer_llama_amd/profile_summary.py);
+# reported only while the kernel sources match the ones profiled.
+TRAFFIC_PROFILES = {
+    "gate_up": os.path.join(ROOT, "profiles", "gemm_gate_up_7b_s2048_traffic.txt"),
+    "dec_attn": os.path.join(ROOT, "profiles", "dec_attn_7b_decode_b32_traffic.txt"),
+}
+
+
+def stored_traffic(key: str):
+    from decoder_only_transformer_llama_amd.profile_summary import stored_traffic as st
+    v = st(TRAFFIC_PROFILES[key])
+    return None if v is None else round(v)
+
+
+def copy_calibration(torch) -> None:
+    """A plain device copy of known size (read and write COPY_CALIBRATION_BYTES
+    each) for scaling the HBM byte counters; run under rocprofv3 --pmc."""
+    n = COPY_CALIBRATION_BYTES // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    print(f"# copy calibration: 3 copies of {COPY_CALIBRATION_BYTES} bytes (kernel MulFunctor)", flush=True)
 
 
 class HipEvents:
@@ -77,10 +104,14 @@ def decode_bytes(w) -> dict:
 
 
 def traced_kernel_ms(lib, run, stream, n_kernels: int, reps: int):
-    """Average per-kernel duration (ms) over `reps` traced runs of `run`."""
+    """Average per-kernel duration (ms) over `reps` traced runs of `run`. An
+    untraced run goes first so the GPU is busy while the traced run is
+    enqueued: the first traced kernel then starts as soon as the start event
+    completes, and its time holds no host launch latency."""
     ev = HipEvents(n_kernels + 2)
     tot = [0.0] * n_kernels
     for _ in range(reps):
+        run()
         ev.record(0, stream)
         lib.llama_trace_begin(ev.pointer_from(1), n_kernels + 1)   # one spare slot detects extra kernels
         run()
@@ -126,7 +157,7 @@ def bench_prefill(args, torch):
         "per_kernel": per_kernel,
         "roofline": {"bound": "mfma", "kernel": "gemm_bf16 gate/up (rstd row scale + SiLU*up epilogue)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic("gate_up"),
                      "flops_per_launch": fl[dom]},
         "block": bw,
     }
@@ -145,6 +176,8 @@ def bench_decode(args, torch):
     torch.cuda.synchronize()
     graph = None
     try:
+        if args.eager:
+            raise RuntimeError("--eager")
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(s):
@@ -156,7 +189,8 @@ def bench_decode(args, torch):
             run()
         torch.cuda.synchronize()
     except Exception as e:  # pragma: no cover - reported, eager timing still valid
-        print(f"# decode graph capture failed ({e}); timing eager launches", file=sys.stderr)
+        if not args.eager:
+            print(f"# decode graph capture failed ({e}); timing eager launches", file=sys.stderr)
         graph = None
     step = graph.replay if graph is not None else run
     for _ in range(args.warmup):
@@ -194,9 +228,9 @@ def bench_decode(args, torch):
         "hbm_gbs": total_bytes / (ms * 1e-3) / 1e9,
         "bytes": total_bytes,
         "per_kernel_ms": {k: round(v, 4) for k, v in agg.items()},
-        "roofline": {"bound": "hbm", "kernel": "dec_attn (split-sequence cache attention)",
+        "roofline": {"bound": "hbm", "kernel": "dec_attn (fused q/k/v finish, RoPE, cache append, attention)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic("dec_attn"),
                      "bytes_per_launch": att_bytes_launch},
     }
 
@@ -230,6 +264,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="skip the prefill leg (diagnostic runs)")
+    ap.add_argument("--eager", action="store_true", help="decode: time eager launches, no HIP graph")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run the plain copy used to scale HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the hot path here runs on a single MI355X with no sharding or "
@@ -238,6 +275,9 @@ def main() -> int:
     import torch
     torch.cuda.set_device(0)
     t_start = time.time()
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
     if args.decode_only:
         dec = bench_decode(args, torch)
         print(f"# decode: {dec['ms']:.3f} ms/step (eager {dec['ms_eager']:.3f}), {dec['tokens_per_s']:.0f} tok/s, "
