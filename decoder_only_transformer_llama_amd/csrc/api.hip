@@ -178,7 +178,7 @@ struct DecodeWs {
   float2 *rope_tab;
 };
 
-constexpr int kDecMaxSeq = 2048;   // decode attention keeps one score per cached position in LDS
+constexpr int kDecMaxSeq = 2048;   // longest cache the decode path is validated for
 
 void gemv_split(int N, int K, int &splits, int &k_chunk) {
   const int per_wg = 128 * gemv_ntw(N);

@@ -3,18 +3,22 @@
 //
 //  - gemv_kernel: skinny split-K product part[s][m][n] = sum_{k in split s}
 //    A[m][k] B[n][k] with the batch as the 32 rows of one v_mfma_f32_32x32x16
-//    tile. Weights stream from HBM straight into the B-operand registers (each
-//    lane reads 64 contiguous bytes of one weight row per step, register
-//    double-buffered); the activation operand is a bf16 hi/lo pair so the
-//    product is fp32-accurate at bf16 matrix-core rate. K order inside a step
-//    is permuted identically for A and B, which leaves the sum unchanged.
+//    tile. Weights stream from HBM (tile-packed: one contiguous 4 KB block per
+//    32 columns x 64 K) into a ring of B-operand registers, DEPTH steps deep;
+//    the activation operand is a bf16 hi/lo pair staged in LDS, so the product
+//    is fp32-accurate at bf16 matrix-core rate. K order inside a step is
+//    permuted identically for A and B, which leaves the sum unchanged.
 //  - the *_combine / resid_norm kernels reduce the split-K partials in a fixed
 //    order (deterministic, no atomics) and apply the elementwise work: RMSNorm
-//    statistics and gain, RoPE at pos[b], the KV-cache append, SiLU(gate)*up,
-//    and the residual adds of the pre-norm block.
-//  - dec_attn_kernel: split-sequence attention of one fp32 query over the
-//    cached bf16 keys/values (chunks of the cache in parallel, each with its
-//    own max and sum), followed by a fixed-order merge of the chunks.
+//    statistics and gain, SiLU(gate)*up, the residual adds of the pre-norm
+//    block, the head's row scale.
+//  - dec_attn_kernel: per (head, sequence) the Q/K/V split-K finish, RoPE at
+//    pos, the cache append, and one pass of online-softmax attention over the
+//    cached keys and values.
+//
+// Loads in the streaming loops are never placed under a branch and their
+// loops unroll into straight-line code: at a control-flow join the compiler
+// waits for every outstanding load, which would serialise the stream.
 //
 // The per-layer formula is the pre-norm block of the paperfordummies.in LLaMA
 // page ("The one formula"); the cache of keys and values of earlier tokens is
@@ -50,7 +54,12 @@ __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const G
   const int ks = blockIdx.y * a.k_chunk;
   const int ke = min(a.K, ks + a.k_chunk);
   const int nit = (ke - ks) >> 6;
+  const int n_tiles = (a.N + 31) >> 5;
 
+  // Every load below is unconditional: columns past N read the last valid
+  // tile (or row) and their results are never stored. Loads under branches
+  // would make the compiler wait for all outstanding loads at each join,
+  // which serialises the weight stream.
   const int nw0 = (blockIdx.x * 4 + w) * 32 * NTW;
   const u16 *brow[NTW];
   bool bok[NTW];
@@ -58,14 +67,14 @@ __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const G
   for (int j = 0; j < NTW; ++j) {
     const int n = nw0 + 32 * j + l32;
     if (a.packed) {
-      // tile t = nw0/32 + j: 4 KB per 64-wide K step, this lane's 16 bytes at 16 * lane
+      // tile t: 4 KB per 64-wide K step, this lane's 16 bytes at 16 * lane
       const int t = (nw0 >> 5) + j;
-      bok[j] = 32 * t < a.N;   // wavefront-uniform
-      brow[j] = a.packed + ((int64_t)t * (a.K >> 6) + (ks >> 6)) * 2048 + lane * 8;
+      bok[j] = t < n_tiles;   // wavefront-uniform
+      brow[j] = a.packed + ((int64_t)min(t, n_tiles - 1) * (a.K >> 6) + (ks >> 6)) * 2048 + lane * 8;
       continue;
     }
     bok[j] = n < a.N;
-    const int nn = bok[j] ? n : 0;
+    const int nn = bok[j] ? n : a.N - 1;
     const u16 *p;
     if (a.b_mode == BMODE_GATEUP) {
       const int blk = nn >> 5;
@@ -81,7 +90,8 @@ __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const G
 
   // activation pair -> LDS: one 1 KB load per (part, row); lane i lands in
   // chunk i of the row and fetches logical chunk i ^ (row & 15). Rows past M
-  // and chunks past the range load valid addresses whose results are never used.
+  // and chunks past the range load valid addresses, so the whole staged
+  // region holds finite values.
   constexpr int SEGS = KC_MAX / 512;   // 1 KB segments per staged row
 #pragma unroll
   for (int q = 0; q < 16 * SEGS; ++q) {
@@ -104,13 +114,12 @@ __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const G
   // K order inside a 64-step: lane group g supplies k = 32 g + 8 q + (0..7) at
   // matrix-core step q, identically for the activation and the weights.
   u32x4 ring[DEPTH][NTW][4];
-  auto load = [&](u32x4 (&B)[NTW][4], int it) {
+  auto load = [&](u32x4 (&B)[NTW][4], int it) {   // it is clamped to the range by the caller
 #pragma unroll
     for (int j = 0; j < NTW; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        B[j][q] = bok[j] ? *(const u32x4 *)(brow[j] + (a.packed ? 2048 * it + 512 * q : 64 * it + 8 * q))
-                         : u32x4{0, 0, 0, 0};
+        B[j][q] = *(const u32x4 *)(brow[j] + (a.packed ? 2048 * it + 512 * q : 64 * it + 8 * q));
   };
   auto compute = [&](u32x4 (&B)[NTW][4], int it) {
 #pragma unroll
@@ -126,22 +135,29 @@ __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const G
     }
   };
 #pragma unroll
-  for (int d = 0; d < DEPTH; ++d)
-    if (d < nit) load(ring[d], d);
-  // wait for this wavefront's loads (the activation rows it staged, and the
-  // ring prologue the first step needs anyway), then for everyone's rows
-  GEMV_WAIT_VMCNT(0);
-  __syncthreads();
+  for (int d = 0; d < DEPTH; ++d) {
+    load(ring[d], min(d, nit - 1));
+    __builtin_amdgcn_sched_barrier(0);   // issue order = the loop's refill order
+  }
+  // the activation rows were issued first: once at most the ring's loads are
+  // outstanding, this wavefront's rows are in LDS; the barrier covers the others
+  GEMV_WAIT_VMCNT(DEPTH * NTW * 4);
+  __builtin_amdgcn_s_barrier();
 
-  for (int it0 = 0; it0 < nit; it0 += DEPTH) {
+  // The K range has at most KC_MAX / 64 steps, so the step loop unrolls into
+  // straight-line code whose only branches leave it: with no join inside,
+  // each step waits for exactly its own weights while the next DEPTH - 1
+  // steps stay in flight. Refills past the range re-read the last step (never
+  // used) rather than branching around the load.
+  constexpr int NSTEP = KC_MAX / 64;
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int it = it0 + d;
-      if (it < nit) {
-        compute(ring[d], it);
-        if (it + DEPTH < nit) load(ring[d], it + DEPTH);
-      }
-    }
+  for (int it = 0; it < NSTEP; ++it) {
+    if (it >= nit) break;
+    compute(ring[it % DEPTH], it);
+    if (it + DEPTH < NSTEP) load(ring[it % DEPTH], min(it + DEPTH, nit - 1));
+    // keep each refill right behind the step that frees its registers (the
+    // scheduler would otherwise sink all refills together)
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (nw0 >= a.N) return;
 
@@ -158,7 +174,17 @@ __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const G
   }
 }
 
-int gemv_ntw(int N) { return N > 8192 ? 2 : 1; }
+#ifndef GEMV_DEPTH
+#define GEMV_DEPTH 4
+#endif
+
+int gemv_ntw(int N) {
+#ifdef GEMV_NTW_FORCE
+  return GEMV_NTW_FORCE;
+#else
+  return N > 8192 ? 2 : 1;
+#endif
+}
 
 // One thread per 16-byte piece of the tile-ordered copy.
 __global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, const u16 *B2, int n_seg, int N,
@@ -203,9 +229,9 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s) {
   const int per_wg = 4 * 32 * ntw;
   dim3 grid((a.N + per_wg - 1) / per_wg, a.splits);
   if (ntw == 2)
-    hipLaunchKernelGGL((gemv_kernel<2, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<2, GEMV_DEPTH>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<1, 4>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<1, GEMV_DEPTH>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -221,12 +247,39 @@ DEV float block_sum(float v, float *red) {
   return t;
 }
 
+// init + p[0] + p[stride] + ... + p[(n-1) stride], added in that order. The
+// loads go out eight at a time (indices past n re-read the last element and
+// add zero), so a long split-K reduction costs a few memory round trips, not
+// one per split.
+DEV float sum_parts(float init, const float *p, int64_t stride, int n) {
+  float t = init;
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = p[(int64_t)min(s0 + i, n - 1) * stride];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) t += s0 + i < n ? v[i] : 0.f;
+  }
+  return t;
+}
+
+DEV f32x4 sum_parts4(f32x4 init, const float *p, int64_t stride, int n) {
+  f32x4 t = init;
+  for (int s0 = 0; s0 < n; s0 += 8) {
+    f32x4 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = *(const f32x4 *)(p + (int64_t)min(s0 + i, n - 1) * stride);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (s0 + i < n) t += v[i];
+  }
+  return t;
+}
+
 // Row statistics are kept as partial sums of squares, one per 1024-channel
 // chunk of the row (ss[b][chunk]); consumers finish rstd in a fixed order.
 DEV float rstd_from_parts(const float *ss, int b, int nss, int dim, float eps) {
-  float t = 0.f;
-  for (int i = 0; i < nss; ++i) t += ss[b * nss + i];
-  return rstd_of(t, dim, eps);
+  return rstd_of(sum_parts(0.f, ss + b * nss, 1, nss), dim, eps);
 }
 
 DEV void chunk_sumsq_store(float v, float *ss, int b, int nss) {
@@ -285,8 +338,7 @@ __global__ __launch_bounds__(256) void dec_resid_norm_kernel(const DecodeArgs d,
   float q = 0.f;
   if (c < d.dim) {
     const int64_t o = (int64_t)b * d.dim + c;
-    f32x4 v = *(const f32x4 *)(res + o);
-    for (int sp = 0; sp < splits; ++sp) v += *(const f32x4 *)(part + sp * stride + o);
+    const f32x4 v = sum_parts4(*(const f32x4 *)(res + o), part + o, stride, splits);
     *(f32x4 *)(out + o) = v;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -317,12 +369,9 @@ __global__ void dec_gateup_combine_kernel(const DecodeArgs d, const float *part,
   const int N = 2 * d.hidden;
   const int ng = (j >> 5) * 64 + (j & 31);
   const int64_t stride = (int64_t)d.batch * N;
-  float gt = 0.f, up = 0.f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const float *pp = part + sp * stride + (int64_t)b * N;
-    gt += pp[ng];
-    up += pp[ng + 32];
-  }
+  const float *pp = part + (int64_t)b * N + ng;
+  const float gt = sum_parts(0.f, pp, stride, splits);
+  const float up = sum_parts(0.f, pp + 32, stride, splits);
   const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
   const float u = silu(gt * r) * (up * r);
   u16 hi, lo;
@@ -345,8 +394,7 @@ __global__ void dec_head_combine_kernel(const DecodeArgs d, const float *part, i
   if (idx >= d.batch * d.vocab) return;
   const int b = idx / d.vocab;
   const int64_t stride = (int64_t)d.batch * d.vocab;
-  float v = 0.f;
-  for (int sp = 0; sp < splits; ++sp) v += part[sp * stride + idx];
+  const float v = sum_parts(0.f, part + idx, stride, splits);
   const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
   logits[idx] = pos_ok(d.pos[b], d.max_seq) ? v * r : __builtin_nanf("");
 }
@@ -364,13 +412,35 @@ hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int s
 //  1. q, k, v of the new token for this head: rstd * (sum of the projection
 //     partials in split order), RoPE on q and k at pos[b]; k and v (bf16) go to
 //     cache slot pos[b] and stay in LDS for the new key's own term;
-//  2. scores of the fp32 query against cached bf16 keys 0..pos-1 (16 lanes per
-//     key, 4 keys per wavefront instruction) plus the new key;
-//  3. softmax in fp32 (exp2, log2(e)/sqrt(hd) prescale), weighted sum of the
-//     cached values plus the new value;
-//  4. the normalised head output is written as the bf16 hi/lo pair the Wo
-//     projection consumes.
+//  2. one pass over the cached keys 0..pos-1 and their values: a lane group of
+//     HD/8 lanes owns one key per instruction (4 keys per wavefront
+//     instruction, UNR instructions per step), keeps a running max, sum and
+//     weighted value sum in fp32 (online softmax, exp2 with log2(e)/sqrt(hd)
+//     folded into q); keys and values of the next step are in flight while
+//     one step is processed;
+//  3. the 16 lane groups' partial softmax states and the new key's term are
+//     merged in a fixed order and the normalised head output is written as
+//     the bf16 hi/lo pair the Wo projection consumes.
 // An invalid position writes nothing to the cache and yields NaN outputs.
+// Sum over aligned groups of G lanes (G = 2..16), every lane getting its
+// group's total, with DPP lane moves inside each 16-lane row: swap
+// neighbours, swap pairs, mirror within 8, mirror within 16. Each step adds a
+// permutation of the partial sums, so after log2(G) steps all G lanes hold
+// the same sum.
+template <int G>
+DEV float lane_group_sum(float v) {
+  static_assert(G >= 2 && G <= 16 && (G & (G - 1)) == 0, "group of 2..16 lanes");
+#define LLAMA_DPP(x, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), ctrl, 0xf, 0xf, false))
+  v += LLAMA_DPP(v, 0xB1);                  // quad_perm [1,0,3,2]
+  if (G >= 4) v += LLAMA_DPP(v, 0x4E);      // quad_perm [2,3,0,1]
+  if (G >= 8) v += LLAMA_DPP(v, 0x141);     // row_half_mirror
+  if (G >= 16) v += LLAMA_DPP(v, 0x140);    // row_mirror
+#undef LLAMA_DPP
+  return v;
+}
+
+constexpr int kMaxSeq = 2048;   // longest decode cache (positions) the attention kernel unrolls for
+
 template <int HD>
 __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
                                                        const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
@@ -378,17 +448,18 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   constexpr int LPK = HD / 8;          // lanes per key
   constexpr int KPW = 64 / LPK;        // keys per wavefront instruction
 #ifndef DEC_ATTN_UNROLL
-#define DEC_ATTN_UNROLL 4
+#define DEC_ATTN_UNROLL 2
 #endif
-  constexpr int UNR = DEC_ATTN_UNROLL; // instructions in flight per wavefront
+  constexpr int UNR = DEC_ATTN_UNROLL; // key instructions per wavefront per step
+  constexpr int KPS = 4 * KPW * UNR;   // keys per workgroup step
+  constexpr int NG = 4 * KPW;          // lane groups per workgroup
   __shared__ float sq[HD], sknew[HD], svnew[HD];
-  __shared__ float sc[2048 + 1];
-  __shared__ float red[8];
-  __shared__ float osum[4][KPW][HD];
+  __shared__ float gm[NG], gl[NG], snew;
+  __shared__ float osum[NG][HD];
   const int h = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int p = d.pos[b];
-  const bool ok = pos_ok(p, d.max_seq) && p <= 2048;
+  const bool ok = pos_ok(p, d.max_seq);
   const int64_t cbase = ((int64_t)b * d.n_heads + h) * d.max_seq * HD;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
@@ -398,12 +469,9 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
     const int N = 3 * d.dim;
     const int64_t stride = (int64_t)d.batch * N;
     const float *pp = part + (int64_t)b * N + h * HD + e;
-    float q = 0.f, k = 0.f, v = 0.f;
-    for (int sp = 0; sp < splits; ++sp) {
-      q += pp[sp * stride];
-      k += pp[sp * stride + d.dim];
-      v += pp[sp * stride + 2 * d.dim];
-    }
+    float q = sum_parts(0.f, pp, stride, splits);
+    float k = sum_parts(0.f, pp + d.dim, stride, splits);
+    float v = sum_parts(0.f, pp + 2 * d.dim, stride, splits);
     const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
     q *= r;
     k *= r;
@@ -414,7 +482,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
     k = (e & 1) ? kp * cs.y + k * cs.x : k * cs.x - kp * cs.y;
     // the cache holds bf16: the new key/value enter attention as stored
     const u16 kb = f2bf(k), vb = f2bf(v);
-    sq[e] = q;
+    sq[e] = q * scale;
     sknew[e] = bf2f(kb);
     svnew[e] = bf2f(vb);
     if (ok) {
@@ -424,88 +492,102 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   }
   __syncthreads();
   const int nk = ok ? p : 0;    // cached keys 0..p-1; key p is the new one
+  if (w == 0) {                 // the new key's score (log2 domain)
+    float s = 0.f;
+    for (int e = lane; e < HD; e += 64) s += sq[e] * sknew[e];
+    s = wave_sum(s);
+    if (lane == 0) snew = s;
+  }
 
-  // ---- 2. scores (log2 domain) of cached keys
+  // ---- 2. one pass over the cached keys and values
   const int kg = lane / LPK, d8 = lane % LPK;
   float qv[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) qv[i] = sq[d8 * 8 + i];
-  for (int kb0 = w * KPW * UNR; kb0 < nk; kb0 += 4 * KPW * UNR) {
-    u32x4 kr[UNR];
+  float m_run = -INFINITY, l_run = 0.f;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  const int nsteps = (nk + KPS - 1) / KPS;
+  const int kbase = w * KPW * UNR + kg;          // + st * KPS + u * KPW
+  // Loads are unconditional: keys past the range read key max(nk-1, 0) (a
+  // valid row) and get probability 0.
+  auto load = [&](u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], int st) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int key = kb0 + u * KPW + kg;
-      kr[u] = key < nk ? *(const u32x4 *)(kc + cbase + (int64_t)key * HD + d8 * 8) : u32x4{0, 0, 0, 0};
+      const int key = max(min(st * KPS + kbase + u * KPW, nk - 1), 0);
+      const int64_t o = cbase + (int64_t)key * HD + d8 * 8;
+      kr[u] = *(const u32x4 *)(kc + o);
+      vr[u] = *(const u32x4 *)(vc + o);
     }
+  };
+  auto step = [&](const u32x4 (&kr)[UNR], const u32x4 (&vr)[UNR], int st) {
+    float sc[UNR];
+    float mx = m_run;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int key = kb0 + u * KPW + kg;
       float kv[8];
       unpack8(kr[u], kv);
-      float s = 0.f;
+      float sdot = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) s = fmaf(qv[i], kv[i], s);
-#pragma unroll
-      for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o, 64);
-      if (d8 == 0 && key < nk) sc[key] = s * scale;
+      for (int i = 0; i < 8; ++i) sdot = fmaf(qv[i], kv[i], sdot);
+      sdot = lane_group_sum<LPK>(sdot);
+      sc[u] = st * KPS + kbase + u * KPW < nk ? sdot : -INFINITY;
+      mx = fmaxf(mx, sc[u]);
     }
-  }
-  if (tid < 64) {   // the new key's score (one wavefront)
-    float s = 0.f;
-    for (int e = lane; e < HD; e += 64) s += sq[e] * sknew[e];
-    s = wave_sum(s);
-    if (lane == 0) sc[nk] = s * scale;
-  }
-  __syncthreads();
-
-  // ---- 3. softmax over nk + 1 scores
-  const int tot = nk + 1;
-  float mx = -INFINITY;
-  for (int i = tid; i < tot; i += 256) mx = fmaxf(mx, sc[i]);
-  mx = wave_max(mx);
-  if (lane == 0) red[w] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  float ls = 0.f;
-  for (int i = tid; i < tot; i += 256) {
-    const float e = exp2f(sc[i] - mx);
-    sc[i] = e;
-    ls += e;
-  }
-  ls = block_sum(ls, red);   // contains barriers: sc is complete afterwards
-
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = w * KPW * UNR; kb0 < nk; kb0 += 4 * KPW * UNR) {
-    u32x4 vr[UNR];
+    const float m_use = mx == -INFINITY ? 0.f : mx;
+    const float alpha = exp2f(m_run - m_use);
+    m_run = mx;
+    l_run *= alpha;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int key = kb0 + u * KPW + kg;
-      vr[u] = key < nk ? *(const u32x4 *)(vc + cbase + (int64_t)key * HD + d8 * 8) : u32x4{0, 0, 0, 0};
-    }
+      const float pr = exp2f(sc[u] - m_use);
+      l_run += pr;
+      float vv[8];
+      unpack8(vr[u], vv);
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const int key = kb0 + u * KPW + kg;
-      if (key < nk) {
-        float vv[8];
-        unpack8(vr[u], vv);
-        const float pr = sc[key];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(pr, vv[i], acc[i]);
-      }
+      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pr, vv[i], acc[i]);
     }
+  };
+  // The step loop unrolls fully (a cache holds at most kMaxSeq positions) and
+  // no load sits under a branch, so each step waits for exactly its own keys
+  // and values while the next step's are in flight; steps past the range are
+  // skipped (a uniform branch around arithmetic only) and their loads re-read
+  // one valid row. The fences keep each refill right behind the step that
+  // frees its registers.
+  constexpr int MAXSTEPS = (kMaxSeq + KPS - 1) / KPS;
+  const int last = max(nsteps - 1, 0);
+  u32x4 kb[2][UNR], vb[2][UNR];
+  load(kb[0], vb[0], 0);
+  load(kb[1], vb[1], min(1, last));
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int st = 0; st < MAXSTEPS; ++st) {
+    if (st < nsteps) step(kb[st & 1], vb[st & 1], st);
+    if (st + 2 < MAXSTEPS) load(kb[st & 1], vb[st & 1], min(st + 2, last));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (d8 == 0) {
+    gm[w * KPW + kg] = m_run;
+    gl[w * KPW + kg] = l_run;
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) osum[w][kg][d8 * 8 + i] = acc[i];
+  for (int i = 0; i < 8; ++i) osum[w * KPW + kg][d8 * 8 + i] = acc[i];
   __syncthreads();
 
-  // ---- 4. normalised output (+ the new value's term) as a bf16 pair
+  // ---- 3. merge the lane groups and the new key (fixed order), normalise
   if (tid < HD) {
     const int e = tid;
-    float o = sc[nk] * svnew[e];
-    for (int ww = 0; ww < 4; ++ww)
-      for (int g2 = 0; g2 < KPW; ++g2) o += osum[ww][g2][e];
-    const float v = ok ? o / ls : __builtin_nanf("");
+    float M = snew;
+    for (int gi = 0; gi < NG; ++gi) M = fmaxf(M, gm[gi]);
+    float pn = exp2f(snew - M);
+    float L = pn, o = pn * svnew[e];
+    for (int gi = 0; gi < NG; ++gi) {
+      const float f = exp2f(gm[gi] - M);   // 0 for a group that saw no key
+      L += f * gl[gi];
+      o += f * osum[gi][e];
+    }
+    const float v = ok ? o / L : __builtin_nanf("");
     u16 hi, lo;
     split_pair(v, hi, lo);
     const int64_t oo = (int64_t)b * d.dim + h * HD + e;
@@ -516,7 +598,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
 
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
                            uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s) {
-  if (d.max_seq > 2048 + 1) return hipErrorInvalidValue;
+  if (d.max_seq > kMaxSeq) return hipErrorInvalidValue;
   dim3 grid(d.n_heads, d.batch);
   if (d.head_dim == 128)
     hipLaunchKernelGGL(dec_attn_kernel<128>, grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo);
