@@ -103,24 +103,49 @@ def decode_bytes(w) -> dict:
     }
 
 
-def traced_kernel_ms(lib, run, stream, n_kernels: int, reps: int):
-    """Average per-kernel duration (ms) over `reps` traced runs of `run`. An
-    untraced run goes first so the GPU is busy while the traced run is
-    enqueued: the first traced kernel then starts as soon as the start event
-    completes, and its time holds no host launch latency."""
-    ev = HipEvents(n_kernels + 2)
-    tot = [0.0] * n_kernels
+def traced_kernel_ms(lib, run, stream, reps: int, capacity: int = 4096):
+    """Per-kernel durations (ms) averaged over `reps` traced runs of `run`, as
+    a list of (library step label, ms). An untraced run goes first so the GPU
+    is busy while the traced run is enqueued: the first traced kernel then
+    starts as soon as the start event completes, and its time holds no host
+    launch latency."""
+    ev = HipEvents(capacity + 1)
+    tot, labels = None, None
     for _ in range(reps):
         run()
         ev.record(0, stream)
-        lib.llama_trace_begin(ev.pointer_from(1), n_kernels + 1)   # one spare slot detects extra kernels
+        lib.llama_trace_begin(ev.pointer_from(1), capacity)
         run()
         got = lib.llama_trace_end()
-        if got != n_kernels:
-            raise RuntimeError(f"traced {got} kernels, expected {n_kernels}")
-        for i in range(n_kernels):
+        if got >= capacity:
+            raise RuntimeError("trace capacity exhausted")
+        lab = [lib.llama_trace_label(i).decode() for i in range(got)]
+        if labels is None:
+            labels, tot = lab, [0.0] * got
+        elif lab != labels:
+            raise RuntimeError("launch sequence changed between traced runs")
+        for i in range(got):
             tot[i] += ev.elapsed_ms(i, i + 1)
-    return [t / reps for t in tot]
+    return [(l, t / reps) for l, t in zip(labels, tot)]
+
+
+def merge_steps(trace, names):
+    """Sum consecutive kernels of one library step; map labels to short names."""
+    out = []
+    for label, ms in trace:
+        n = names.get(label, label)
+        if out and out[-1][0] == n:
+            out[-1] = (n, out[-1][1] + ms)
+        else:
+            out.append((n, ms))
+    return out
+
+
+PREFILL_STEP_NAMES = {
+    "attention norm": "attn_norm", "rope table": "rope_table", "qkv projection": "qkv", "attention": "attention",
+    "output projection": "o", "ffn norm": "ffn_norm", "gate/up projection": "gate_up", "down projection": "down",
+    "down residual": "down_reduce",
+}
 
 
 def bench_prefill(args, torch):
@@ -141,8 +166,9 @@ def bench_prefill(args, torch):
     ms = ev.elapsed_ms(0, 1) / args.steps
     torch.cuda.synchronize()
 
-    names = ["attn_norm", "rope_table", "qkv", "attention", "o", "ffn_norm", "gate_up", "down"]
-    kms = traced_kernel_ms(_lib.load(), lambda: bw.block(bw.x), stream, len(names), max(3, args.steps // 2))
+    steps = merge_steps(traced_kernel_ms(_lib.load(), lambda: bw.block(bw.x), stream, max(3, args.steps // 2)),
+                        PREFILL_STEP_NAMES)
+    names, kms = [n for n, _ in steps], [t for _, t in steps]
     fl = block_flops(w)
     total = sum(fl.values())
     per_kernel = {n: {"ms": round(t, 4)} for n, t in zip(names, kms)}
@@ -211,11 +237,13 @@ def bench_decode(args, torch):
     ms_eager = ev.elapsed_ms(0, 1) / max(2, args.steps // 4)
 
     L = w.n_layers
-    per_layer = ["qkv", "attention", "o", "resid1", "gate_up", "silu", "down", "resid2"]
-    names = ["rope_table", "embed"] + [n for _ in range(L) for n in per_layer] + ["head", "head_combine"]
-    kms = traced_kernel_ms(_lib.load(), run, stream, len(names), 2)
+    names = {"rope table": "rope_table", "embedding": "embed", "qkv projection": "qkv", "attention": "attention",
+             "output projection": "o", "attention residual": "resid1", "gate/up projection": "gate_up",
+             "silu": "silu", "down projection": "down", "ffn residual": "resid2", "output head": "head",
+             "head combine": "head_combine"}
     agg = {}
-    for n, t in zip(names, kms):
+    for label, t in traced_kernel_ms(_lib.load(), run, stream, 2):
+        n = names.get(label, label)
         agg[n] = agg.get(n, 0.0) + t
     by = decode_bytes(w)
     total_bytes = sum(by.values())

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -16,24 +17,30 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Optional launch trace (per thread): an event recorded after every kernel.
+// Optional launch trace (per thread): an event recorded after every kernel,
+// and the launch's label (a string literal) kept until the next trace begins.
 thread_local hipEvent_t const *g_trace_ev = nullptr;
 thread_local int g_trace_cap = 0, g_trace_n = 0;
+thread_local std::vector<const char *> g_trace_labels;
 
 int hip_fail(hipError_t e, const char *where) {
   g_last_error = std::string(where) + ": " + hipGetErrorString(e);
   return LLAMA_ERR_HIP;
 }
 
-hipError_t traced(hipError_t e, hipStream_t s) {
-  if (e == hipSuccess && g_trace_ev && g_trace_n < g_trace_cap) e = hipEventRecord(g_trace_ev[g_trace_n++], s);
+hipError_t traced(hipError_t e, hipStream_t s, const char *where) {
+  if (e == hipSuccess && g_trace_ev && g_trace_n < g_trace_cap) {
+    e = hipEventRecord(g_trace_ev[g_trace_n++], s);
+    g_trace_labels.push_back(where);
+  }
   return e;
 }
 
-// Every kernel launch goes through HIP_TRY with the launch stream named `s`.
+// Every kernel launch goes through HIP_TRY with the launch stream named `s`;
+// `where` is a string literal naming the step.
 #define HIP_TRY(expr, where)                              \
   do {                                                    \
-    hipError_t e_ = traced((expr), s);                    \
+    hipError_t e_ = traced((expr), s, where);             \
     if (e_ != hipSuccess) return hip_fail(e_, where);     \
   } while (0)
 
@@ -75,14 +82,65 @@ int cu_count() {
 
 // Tile width (256 or 128 output columns) whose tile count fills the last
 // round of workgroups best; ties go to the wider tile (less operand re-reading).
+// Tile width by estimated time: rounds of workgroups over the CUs, a 256 x 128
+// tile costing 0.5 / 0.72 of a 256 x 256 tile (it does half the work at
+// ~0.72 of the matrix-core efficiency, measured on the 7B shapes).
+constexpr double kHalfTileCost = 0.5 / 0.72;
 int choose_bn(int M, int N) {
   const int cus = cu_count();
-  auto eff = [&](int bn) {
+  auto rounds = [&](int bn) {
     const long tiles = (long)((M + 255) / 256) * ((N + bn - 1) / bn);
-    const long rounds = (tiles + cus - 1) / cus;
-    return (double)tiles / (double)(rounds * cus);
+    return (double)((tiles + cus - 1) / cus);
   };
-  return eff(128) > eff(256) + 1e-9 ? 128 : 256;
+  return rounds(128) * kHalfTileCost < rounds(256) ? 128 : 256;
+}
+
+// Column ranges and tile widths of the QKV GEMM: whole rounds of 256 x 256
+// tiles over the CUs, and when the remainder fills at most half a round, the
+// remaining columns as 256 x 128 tiles (twice as many workgroups, each half
+// the work, one round) instead of a mostly idle round of 256 x 256 tiles.
+struct ColPart {
+  int bn, n_base, n_end;
+};
+int plan_qkv(int M, int N, ColPart parts[2]) {
+  const int cus = cu_count();
+  const int tm = (M + 255) / 256, tn = (N + 255) / 256;
+  const int full_rounds = (tm * tn) / cus;
+  const int rem = tm * tn - full_rounds * cus;
+  if (N % 256 == 0 && full_rounds > 0 && rem > 0 && rem % tm == 0 && 2 * rem <= cus) {
+    const int n1 = N - (rem / tm) * 256;
+    parts[0] = {256, 0, n1};
+    parts[1] = {128, n1, N};
+    return 2;
+  }
+  parts[0] = {choose_bn(M, N), 0, N};
+  return 1;
+}
+
+// Tiling of a GEMM whose epilogue adds the residual (O and down projections):
+// 256 x 128 tiles, 256 x 256 tiles, or 256 x 256 tiles with K split in two
+// (partial products added in order by the consumer). The cost model counts
+// rounds of workgroups over the CUs in units of one full-K 256 x 256 tile;
+// a 256 x 128 tile costs kHalfTileCost; a split pays for writing and reading
+// its partials at ~5 TB/s against ~4 TFLOP/s per CU of matrix-core work
+// (twice the passes when A is a hi/lo pair).
+struct ResidCfg {
+  int bn, splits;
+};
+ResidCfg choose_resid(int M, int N, int K, bool apair) {
+  const int cus = cu_count();
+  const long tm = (M + 255) / 256;
+  auto rounds = [&](long tiles) { return (double)((tiles + cus - 1) / cus); };
+  const double c128 = rounds(tm * ((N + 127) / 128)) * kHalfTileCost;
+  const double c256 = rounds(tm * ((N + 255) / 256));
+  double c256s2 = 1e30;
+  if (K % 64 == 0) {
+    const double traffic_us = (double)M * N * 4.0 * 2.0 * 2.0 / 5e6;
+    const double round_us = 256.0 * 256.0 * K * 2.0 / 4e6 * (apair ? 2.0 : 1.0);
+    c256s2 = rounds(tm * ((N + 255) / 256) * 2) * 0.5 + traffic_us / round_us;
+  }
+  if (c256s2 < c256 && c256s2 < c128) return {256, 2};
+  return c256 <= c128 ? ResidCfg{256, 1} : ResidCfg{128, 1};
 }
 
 // ------------------------------------------------------------------ validation
@@ -131,6 +189,7 @@ struct BlockWs {
   float2 *rope_tab;
   uint16_t *xg_hi, *xg_lo, *qh, *ql, *kh, *kl, *vth, *vtl, *a_hi, *a_lo, *u_hi, *u_lo;
   float *h, *rstd1, *rstd2;
+  float *part;   // split-K partials [2][n][d] fp32: aliases qh..kl (dead after attention)
   // fp32 path
   float *z, *q, *k, *v, *att, *gate, *up;
 };
@@ -151,6 +210,7 @@ BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq) {
     b.ql = cv.take<uint16_t>(n * d);
     b.kh = cv.take<uint16_t>(n * d);
     b.kl = cv.take<uint16_t>(n * d);
+    b.part = (float *)b.qh;   // qh, ql, kh, kl are contiguous: 8 n d bytes = 2 n d floats
     const size_t vt = (size_t)batch * d * vt_stride_of(seq);
     b.vth = cv.take<uint16_t>(vt);
     b.vtl = cv.take<uint16_t>(vt);
@@ -328,7 +388,13 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.kcache = kcache;
   q.vcache = vcache;
   q.max_seq = max_seq;
-  HIP_TRY(gemm_launch(GemmKey{choose_bn(M, 3 * d), qkv_pair, EPI_QKV}, q, s), "qkv projection");
+  ColPart qp[2];
+  const int nqp = plan_qkv(M, 3 * d, qp);
+  for (int i = 0; i < nqp; ++i) {
+    q.n_base = qp[i].n_base;
+    q.n_end = qp[i].n_end;
+    HIP_TRY(gemm_launch(GemmKey{qp[i].bn, qkv_pair, EPI_QKV}, q, s), "qkv projection");
+  }
 
   AttnArgs at{};
   at.qh = b.qh;
@@ -350,6 +416,9 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   HIP_TRY(attn_prefill_launch(at, (num & LLAMA_NUM_QK_PAIR) ? 1 : 0, (num & LLAMA_NUM_V_PAIR) ? 1 : 0, s),
           "attention");
 
+  // h = x + attn Wo^T. With a split K the two partial products go to the
+  // q/k buffers (dead after attention) and the ffn norm prep forms h.
+  const ResidCfg oc = choose_resid(M, d, d, opair);
   GemmArgs o{};
   o.M = M;
   o.N = d;
@@ -363,12 +432,19 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   o.ldc = d;
   o.R = x;
   o.r_f32 = x_dtype == LLAMA_F32;
-  HIP_TRY(gemm_launch(GemmKey{128, opair, EPI_RESID}, o, s), "output projection");
+  o.k_splits = oc.splits;
+  o.part = b.part;
+  HIP_TRY(gemm_launch(GemmKey{oc.bn, opair, oc.splits > 1 ? EPI_PARTIAL : EPI_RESID}, o, s), "output projection");
 
   // z2 = RMSNorm(h; g2), operand reuses the x*g1 buffers
-  HIP_TRY(norm_prep_launch(1, b.h, (const uint16_t *)w->ffn_norm, M, d, c->norm_eps, b.rstd2, b.xg_hi,
-                           ffn_pair ? b.xg_lo : nullptr, s),
-          "ffn norm");
+  if (oc.splits > 1)
+    HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, (const uint16_t *)w->ffn_norm, M, d, c->norm_eps, b.rstd2,
+                             b.xg_hi, ffn_pair ? b.xg_lo : nullptr, s, b.part, oc.splits, b.h),
+            "ffn norm");
+  else
+    HIP_TRY(norm_prep_launch(1, b.h, (const uint16_t *)w->ffn_norm, M, d, c->norm_eps, b.rstd2, b.xg_hi,
+                             ffn_pair ? b.xg_lo : nullptr, s),
+            "ffn norm");
   GemmArgs f{};
   f.M = M;
   f.N = 2 * c->hidden;
@@ -398,7 +474,11 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   dn.ldc = d;
   dn.R = b.h;
   dn.r_f32 = 1;
-  HIP_TRY(gemm_launch(GemmKey{128, dpair, EPI_RESID}, dn, s), "down projection");
+  const ResidCfg dc = choose_resid(M, d, c->hidden, dpair);
+  dn.k_splits = dc.splits;
+  dn.part = b.part;
+  HIP_TRY(gemm_launch(GemmKey{dc.bn, dpair, dc.splits > 1 ? EPI_PARTIAL : EPI_RESID}, dn, s), "down projection");
+  if (dc.splits > 1) HIP_TRY(resid_sum_launch(b.h, b.part, dc.splits, (int64_t)M * d, y, s), "down residual");
   return LLAMA_OK;
 }
 
@@ -454,7 +534,12 @@ int llama_trace_begin(void *const *events, int capacity) {
   g_trace_ev = (hipEvent_t const *)events;
   g_trace_cap = capacity;
   g_trace_n = 0;
+  g_trace_labels.clear();
   return LLAMA_OK;
+}
+
+const char *llama_trace_label(int i) {
+  return i >= 0 && i < (int)g_trace_labels.size() ? g_trace_labels[i] : nullptr;
 }
 
 int llama_trace_end(void) {
@@ -780,7 +865,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
     HIP_TRY(gemv(d, d, BMODE_PLAIN, L.wo, nullptr, nullptr, sp), "output projection");
     HIP_TRY(dec_resid_norm_launch(da, dw.x, dw.part, sp, (const uint16_t *)L.ffn_norm, dw.h, dw.rstd, dw.ag_hi,
                                   dw.ag_lo, s),
-            "residual");
+            "attention residual");
     packed_mat = lp ? lp + pl.gu : nullptr;
     HIP_TRY(gemv(2 * c->hidden, d, BMODE_GATEUP, L.w_gate, L.w_up, nullptr, sp), "gate/up projection");
     HIP_TRY(dec_gateup_combine_launch(da, dw.part, sp, dw.rstd, dw.ag_hi, dw.ag_lo, s), "silu");
@@ -789,12 +874,12 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
     const void *gnext = l + 1 < c->n_layers ? w->layers[l + 1].attn_norm : w->final_norm;
     HIP_TRY(dec_resid_norm_launch(da, dw.h, dw.part, sp, (const uint16_t *)gnext, dw.x, dw.rstd, dw.ag_hi,
                                   dw.ag_lo, s),
-            "residual");
+            "ffn residual");
   }
   int sp;
   packed_mat = pack ? pack + pl.head_off : nullptr;
   HIP_TRY(gemv(c->vocab, d, BMODE_PLAIN, w->output, nullptr, nullptr, sp), "output head");
-  HIP_TRY(dec_head_combine_launch(da, dw.part, sp, dw.rstd, logits, s), "head");
+  HIP_TRY(dec_head_combine_launch(da, dw.part, sp, dw.rstd, logits, s), "head combine");
   return LLAMA_OK;
 }
 

@@ -59,13 +59,15 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 // rstd = 1/sqrt(mean(x^2) + eps) (sum reduced across the wavefront) and the
 // GEMM operand x * g as bf16 hi (+ lo). The product's consumer multiplies its
 // fp32 accumulator by rstd, which completes RMSNorm(x; g) W^T. dim % 8 == 0.
-template <bool IN_F32, bool PAIR>
+template <bool IN_F32, bool PAIR, bool PARTS>
 __global__ __launch_bounds__(256) void norm_prep_kernel(const void *x, const u16 *g, int64_t rows, int dim,
-                                                        float eps, float *rstd, u16 *xg_hi, u16 *xg_lo) {
+                                                        float eps, float *rstd, u16 *xg_hi, u16 *xg_lo,
+                                                        const float *part, int n_parts, float *h_out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int64_t base = row * dim;
+  const int64_t pstride = rows * dim;
   float ss = 0.f;
   for (int c = 8 * lane; c < dim; c += 512) {
     float f[8], gf[8];
@@ -79,6 +81,20 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *x, const u16
       }
     } else {
       unpack8(*(const u32x4 *)((const u16 *)x + base + c), f);
+    }
+    if (PARTS) {
+      // h = x + the split-K partial products, added in split order
+      for (int z = 0; z < n_parts; ++z) {
+        const float *pp = part + z * pstride + base + c;
+        const f32x4 p0 = *(const f32x4 *)pp, p1 = *(const f32x4 *)(pp + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] += p0[i];
+          f[4 + i] += p1[i];
+        }
+      }
+      *(f32x4 *)(h_out + base + c) = f32x4{f[0], f[1], f[2], f[3]};
+      *(f32x4 *)(h_out + base + c + 4) = f32x4{f[4], f[5], f[6], f[7]};
     }
     unpack8(*(const u32x4 *)(g + c), gf);
 #pragma unroll
@@ -100,22 +116,46 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *x, const u16
 }
 
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
-                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s) {
+                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s, const float *part,
+                            int n_parts, float *h_out) {
   if (rows == 0) return hipSuccess;
   if (dim % 8) return hipErrorInvalidValue;
+  const bool parts = part != nullptr && n_parts > 0;
+  if (parts && h_out == nullptr) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + 3) / 4));
-#define NP_CASE(F, P)                                                                                     \
-  if (!!in_f32 == F && (xg_lo != nullptr) == P) {                                                         \
-    hipLaunchKernelGGL((norm_prep_kernel<F, P>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, xg_hi, \
-                       xg_lo);                                                                            \
+#define NP_CASE(F, P, R)                                                                                    \
+  if (!!in_f32 == F && (xg_lo != nullptr) == P && parts == R) {                                            \
+    hipLaunchKernelGGL((norm_prep_kernel<F, P, R>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, xg_hi, \
+                       xg_lo, part, n_parts, h_out);                                                        \
     return hipGetLastError();                                                                             \
   }
-  NP_CASE(true, true)
-  NP_CASE(true, false)
-  NP_CASE(false, true)
-  NP_CASE(false, false)
+  NP_CASE(true, true, false)
+  NP_CASE(true, false, false)
+  NP_CASE(false, true, false)
+  NP_CASE(false, false, false)
+  NP_CASE(true, true, true)
+  NP_CASE(true, false, true)
+  NP_CASE(false, true, true)
+  NP_CASE(false, false, true)
 #undef NP_CASE
   return hipErrorInvalidValue;
+}
+
+// y = r + part[0] + ... + part[n_parts-1] (fp32, split order), 4 floats per thread.
+__global__ void resid_sum_kernel(const float *r, const float *part, int n_parts, int64_t n, float *y) {
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i >= n) return;
+  f32x4 v = *(const f32x4 *)(r + i);
+  for (int z = 0; z < n_parts; ++z) v += *(const f32x4 *)(part + z * n + i);
+  *(f32x4 *)(y + i) = v;
+}
+
+hipError_t resid_sum_launch(const float *r, const float *part, int n_parts, int64_t n, float *y, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(resid_sum_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, r, part, n_parts, n,
+                     y);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ RMSNorm

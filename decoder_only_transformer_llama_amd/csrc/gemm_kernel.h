@@ -26,6 +26,8 @@
 //  - EPI_SILU: B rows interleave W_gate and W_up in blocks of 32, so a lane
 //    holds gate and up of the same output; u = SiLU(gate) * up.
 //  - EPI_RESID: C = R + acc (the pre-norm skip connection), fp32 out.
+//  - EPI_PARTIAL: split-K partial product of range blockIdx.y, fp32, into
+//    part[blockIdx.y]; the consumer adds the ranges in order (no atomics).
 //  - EPI_STORE: plain fp32 or bf16 (hi/lo) store.
 #pragma once
 
@@ -86,10 +88,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
   const int g = lane >> 5, l32 = lane & 31;
 
   const int tiles_m = (a.M + BM - 1) / BM;
-  const int tiles_n = (a.N + BN - 1) / BN;
+  const int n_end = a.n_end > 0 ? a.n_end : a.N;
+  const int tiles_n = (n_end - a.n_base + BN - 1) / BN;
   const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
   const int tm = t % tiles_m, tn = t / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  const int m0 = tm * BM, n0 = a.n_base + tn * BN;
 
   // ---- global source of each lane's 16-byte piece, fixed over K
   // A block q of this wavefront covers tile rows 16 * (wave * A_LD + q) + lane / 4.
@@ -122,8 +125,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
     bsrc[q] = ptr + 8 * c;
   }
 
+  // K range of this workgroup: split blockIdx.y of k_splits equal ranges
+  const int nk = a.K / BK / max(a.k_splits, 1);
+  const int kb0 = blockIdx.y * nk * BK;
   auto issue = [&](int kt) {
-    const int k0 = min(kt, a.K / BK - 1) * BK;   // past the end: reload the last step (never read)
+    const int k0 = kb0 + min(kt, nk - 1) * BK;   // past the end: reload the last step (never read)
     u32x4 *st = smem + (kt % STAGES) * G::STAGE;
 #pragma unroll
     for (int q = 0; q < G::A_LD; ++q)
@@ -192,7 +198,6 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
   // The buffer refilled at step kt held stage kt-1; every wavefront drained its
   // reads of it before the previous barrier. Loads past the last step re-read
   // the last step into buffers nobody reads, so the body has no branches.
-  const int nk = a.K / BK;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
   WAIT_VMCNT((STAGES - 2) * G::LPS);
@@ -342,7 +347,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
       const int row = m0 + wm * G::WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
       if (row >= a.M) continue;
       const float sc = a.rstd ? a.rstd[row] : 1.0f;
-      if (EPI == EPI_SILU) {
+      if (EPI == EPI_PARTIAL) {
+        float *out = a.part + (int64_t)blockIdx.y * a.M * a.N + (int64_t)row * a.N;
+#pragma unroll
+        for (int j = 0; j < G::TN; ++j) {
+          const int col = n0 + wn * G::WN + j * 32 + l32;
+          if (col < a.N) out[col] = acc[i][j][r] * sc;
+        }
+      } else if (EPI == EPI_SILU) {
 #pragma unroll
         for (int j = 0; j < G::TN; j += 2) {
           const float u = silu(acc[i][j][r] * sc) * (acc[i][j + 1][r] * sc);
@@ -378,9 +390,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
 template <int BN, bool APAIR, int EPI>
 hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   using G = GemmCfg<BN, APAIR>;
-  const int nb = ((a.M + G::BM - 1) / G::BM) * ((a.N + BN - 1) / BN);
+  const int n_end = a.n_end > 0 ? a.n_end : a.N;
+  if (a.n_base < 0 || a.n_base % BN || n_end > a.N || n_end <= a.n_base) return hipErrorInvalidValue;
+  const int nb = ((a.M + G::BM - 1) / G::BM) * ((n_end - a.n_base + BN - 1) / BN);
   if (nb == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI>), dim3(nb), dim3(512), 0, s, a);
+  const int ks = a.k_splits > 1 ? a.k_splits : 1;
+  if (a.K % (G::BK * ks)) return hipErrorInvalidValue;
+  if (ks > 1 && EPI != EPI_PARTIAL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI>), dim3(nb, ks), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 

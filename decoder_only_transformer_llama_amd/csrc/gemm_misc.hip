@@ -1,9 +1,13 @@
-// Instances of the bf16 GEMM with plain-store and residual-add epilogues, and
-// the dispatcher over every instance.
+// Instances of the bf16 GEMM with plain-store, residual-add and split-K
+// partial epilogues, and the dispatcher over every instance.
 #include "gemm_kernel.h"
 
 namespace llama {
 hipError_t gemm_launch_misc(const GemmKey &key, const GemmArgs &a, hipStream_t s) {
+  GEMM_CASE(256, 0, EPI_PARTIAL)
+  GEMM_CASE(256, 1, EPI_PARTIAL)
+  GEMM_CASE(256, 0, EPI_RESID)
+  GEMM_CASE(256, 1, EPI_RESID)
   GEMM_CASE(128, 0, EPI_RESID)
   GEMM_CASE(128, 1, EPI_RESID)
   GEMM_CASE(128, 0, EPI_STORE)

@@ -12,11 +12,14 @@ namespace llama {
 
 // ---------------------------------------------------------------- GEMM
 // C[M, N] = A[M, K] * B[N, K]^T on bf16 matrix cores, fp32 accumulate.
-enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_QKV = 3 };
+enum Epi { EPI_STORE = 0, EPI_RESID = 1, EPI_SILU = 2, EPI_QKV = 3, EPI_PARTIAL = 4 };
 enum BMode { BMODE_PLAIN = 0, BMODE_CONCAT3 = 1, BMODE_GATEUP = 2 };
 
 struct GemmArgs {
-  int M, N, K;                   // K % 32 == 0
+  int M, N, K;                   // K % (32 * k_splits) == 0
+  int k_splits;                  // >= 1: grid.y splits K into equal contiguous ranges
+  int n_base, n_end;             // columns [n_base, n_end) of C (n_end 0: N); n_base % BN == 0
+  float *part;                   // EPI_PARTIAL: fp32 [k_splits][M][N] partial products
   const uint16_t *A;             // [M, lda] bf16 (hi part when A_lo is set)
   const uint16_t *A_lo;          // optional lo part of a bf16 pair, same layout
   int64_t lda;
@@ -70,8 +73,14 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
                                  int max_seq, hipStream_t s);
 // Norm prep (one wavefront per row): rstd[r] = 1/sqrt(mean(x[r]^2) + eps) and the
 // product x[r] * g as bf16 (hi, and lo when xg_lo is non-null).
+// With `part` (n_parts fp32 [rows, dim] split-K partial products), the row is
+// first h = x + part[0] + ... (split order), written to h_out (fp32), and the
+// statistics and product are those of h.
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
-                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s);
+                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s,
+                            const float *part = nullptr, int n_parts = 0, float *h_out = nullptr);
+// y = r + part[0] + ... + part[n_parts-1], fp32, n elements (n % 4 == 0).
+hipError_t resid_sum_launch(const float *r, const float *part, int n_parts, int64_t n, float *y, hipStream_t s);
 hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,
                           int dim, float eps, hipStream_t s);
 // pos == nullptr: the position of token t is t % seq_mod.

@@ -239,6 +239,11 @@ const char *llama_last_error(void);
  * events recorded. Errors: NULL events with capacity > 0, capacity < 0. */
 int llama_trace_begin(void *const *events, int capacity);
 int llama_trace_end(void);
+/* Label of the i-th kernel of the last trace (a static string naming the step,
+ * e.g. "qkv projection"; one step may launch several kernels, each labelled),
+ * valid until the next llama_trace_begin on this thread; NULL when i is out
+ * of range. */
+const char *llama_trace_label(int i);
 
 #ifdef __cplusplus
 }
