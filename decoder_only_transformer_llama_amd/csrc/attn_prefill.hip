@@ -172,20 +172,24 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2f((m_run - m_use) * c);
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);   // v_exp_f32; m_run = -inf gives 0
     m_run = m_new;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const float pr = exp2f((sc[r] - m_use) * c);   // exp2(-inf) = 0 for masked keys
+      const float pr = __builtin_amdgcn_exp2f((sc[r] - m_use) * c);   // exp2(-inf) = 0 for masked keys
       sc[r] = pr;
       psum += pr;
     }
     l_run = l_run * alpha + psum;
+    // once the running maxima settle, alpha is exactly 1 on every lane: skip
+    // the rescale (a wavefront-uniform branch)
+    if (!__all(alpha == 1.0f)) {
 #pragma unroll
-    for (int e = 0; e < NEB; ++e)
+      for (int e = 0; e < NEB; ++e)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc_o[e][r] *= alpha;
+        for (int r = 0; r < 16; ++r) acc_o[e][r] *= alpha;
+    }
 
     // ---- O^T += V^T P^T
 #pragma unroll

@@ -85,6 +85,12 @@ DEV float rstd_of(float sumsq, int n, float eps) {
 // the quotient is then -0, never NaN.
 DEV float silu(float t) { return t / (1.0f + expf(-t)); }
 
+// Value of the neighbouring lane (lane ^ 1) by a DPP quad permutation [1,0,3,2]
+// (no LDS traffic, unlike a generic shuffle).
+DEV float lane_swap1(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+}
+
 // Round a workgroup count up and remap a linear workgroup id so that ids the
 // hardware sends to one XCD (id % 8) get a contiguous range of tiles.
 DEV int xcd_remap(int bid, int nb) {

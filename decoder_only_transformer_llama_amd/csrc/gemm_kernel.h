@@ -320,19 +320,24 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
         for (int j = 0; j < G::TN; ++j) {
           const int cd = n0 + wn * G::WN + j * 32 + l32 - seg * a.dim;
           const int e = cd & (a.head_dim - 1);
-          float v = acc[i][j][r] * sc;
-          const float partner = __shfl_xor(v, 1, 64);
-          if (!ok) continue;
+          const float v = acc[i][j][r] * sc;
+          const float partner = lane_swap1(v);   // element e ^ 1 of the same row
+          // the lane of the even element rotates the pair (e, e + 1) and stores
+          // both as one 4-byte word
+          if (!ok || (l32 & 1)) continue;
           const float2 cs = tab[e >> 1];
-          v = (e & 1) ? partner * cs.y + v * cs.x : v * cs.x - partner * cs.y;
-          u16 hi, lo;
-          split_pair(v, hi, lo);
+          const float r0 = v * cs.x - partner * cs.y;
+          const float r1 = v * cs.y + partner * cs.x;
+          u16 h0, l0, h1, l1;
+          split_pair(r0, h0, l0);
+          split_pair(r1, h1, l1);
           const int64_t o = (int64_t)row * a.dim + cd;
-          dh[o] = hi;
-          dl[o] = lo;
+          *(uint32_t *)(dh + o) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          *(uint32_t *)(dl + o) = (uint32_t)l0 | ((uint32_t)l1 << 16);
           if (seg == 1 && a.kcache) {
             const int hh = cd >> hd_shift;
-            a.kcache[(((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e] = hi;
+            *(uint32_t *)(a.kcache + (((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e) =
+                (uint32_t)h0 | ((uint32_t)h1 << 16);
           }
         }
       }
@@ -358,11 +363,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
 #pragma unroll
         for (int j = 0; j < G::TN; j += 2) {
           const float u = silu(acc[i][j][r] * sc) * (acc[i][j + 1][r] * sc);
+          const float un = lane_swap1(u);   // the next column's value (even lanes use it)
+          if (l32 & 1) continue;
           const int col = (n0 >> 1) + wn * (G::WN / 2) + (j >> 1) * 32 + l32;
-          const int64_t o = (int64_t)row * a.ldc + col;
-          const u16 hi = f2bf(u);
-          ((u16 *)a.C)[o] = hi;
-          if (a.C_lo) a.C_lo[o] = f2bf(u - bf2f(hi));
+          const int64_t o = (int64_t)row * a.ldc + col;   // even: two columns as one 4-byte word
+          u16 h0, l0, h1, l1;
+          split_pair(u, h0, l0);
+          split_pair(un, h1, l1);
+          *(uint32_t *)((u16 *)a.C + o) = (uint32_t)h0 | ((uint32_t)h1 << 16);
+          if (a.C_lo) *(uint32_t *)(a.C_lo + o) = (uint32_t)l0 | ((uint32_t)l1 << 16);
         }
       } else {
 #pragma unroll
