@@ -902,22 +902,27 @@ int llama_pack_decode_weights(const llama_config *c, const llama_model_weights *
   hipStream_t s = (hipStream_t)stream;
   const int d = c->dim, h = c->hidden;
   uint16_t *out = (uint16_t *)dst;
+  auto kc_of = [](int N, int K) {   // the K chunk the skinny GEMM runs with for this shape
+    int sp, kc;
+    gemv_split(N, K, sp, kc);
+    return kc;
+  };
   for (int l = 0; l < c->n_layers; ++l) {
     const llama_block_weights &L = w->layers[l];
     uint16_t *lp = out + (size_t)l * pl.layer;
     HIP_TRY(pack_tiles_launch(BMODE_CONCAT3, (const uint16_t *)L.wq, (const uint16_t *)L.wk, (const uint16_t *)L.wv,
-                              d, 3 * d, d, lp + pl.qkv, s),
+                              d, 3 * d, d, kc_of(3 * d, d), lp + pl.qkv, s),
             "pack qkv");
-    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.wo, nullptr, nullptr, d, d, d, lp + pl.o, s),
+    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.wo, nullptr, nullptr, d, d, d, kc_of(d, d), lp + pl.o, s),
             "pack o");
     HIP_TRY(pack_tiles_launch(BMODE_GATEUP, (const uint16_t *)L.w_gate, (const uint16_t *)L.w_up, nullptr, d, 2 * h, d,
-                              lp + pl.gu, s),
+                              kc_of(2 * h, d), lp + pl.gu, s),
             "pack gate/up");
-    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.w_down, nullptr, nullptr, d, d, h, lp + pl.down, s),
+    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.w_down, nullptr, nullptr, d, d, h, kc_of(d, h), lp + pl.down, s),
             "pack down");
   }
   HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)w->output, nullptr, nullptr, d, c->vocab, d,
-                            out + pl.head_off, s),
+                            kc_of(c->vocab, d), out + pl.head_off, s),
           "pack head");
   return LLAMA_OK;
 }

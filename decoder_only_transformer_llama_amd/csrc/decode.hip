@@ -46,6 +46,18 @@ constexpr int KC_MAX = GEMV_KC_MAX;
 #define GEMV_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 #define GEMV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+// Tile-packed weights: one 4 KB block per (32-column tile t, 64-wide K step),
+// holding the 64 lanes' 16-byte B-operand pieces in lane order. Blocks are
+// ordered chunk-major for the split-K chunks of kcs steps (the last chunk may
+// be shorter): all tiles' blocks of chunk 0, then chunk 1, ...; within a
+// chunk tile-major, step-minor. The blocks one workgroup streams (its
+// consecutive tiles over one K chunk) are then one contiguous region.
+__host__ __device__ inline int64_t pack_block(int t, int st, int n_tiles, int ksteps, int kcs) {
+  const int c = st / kcs, s = st - c * kcs;
+  const int len = ksteps - c * kcs < kcs ? ksteps - c * kcs : kcs;
+  return (int64_t)c * n_tiles * kcs + (int64_t)t * len + s;
+}
+
 template <int NTW, int DEPTH>
 __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const GemvArgs a) {
   __shared__ u32x4 sA[2][32][KC_MAX / 8];
@@ -70,7 +82,8 @@ __global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const G
       // tile t: 4 KB per 64-wide K step, this lane's 16 bytes at 16 * lane
       const int t = (nw0 >> 5) + j;
       bok[j] = t < n_tiles;   // wavefront-uniform
-      brow[j] = a.packed + ((int64_t)min(t, n_tiles - 1) * (a.K >> 6) + (ks >> 6)) * 2048 + lane * 8;
+      brow[j] = a.packed + pack_block(min(t, n_tiles - 1), ks >> 6, n_tiles, a.K >> 6, a.k_chunk >> 6) * 2048 +
+                lane * 8;
       continue;
     }
     bok[j] = n < a.N;
@@ -186,14 +199,15 @@ int gemv_ntw(int N) {
 #endif
 }
 
-// One thread per 16-byte piece of the tile-ordered copy.
+// One thread per 16-byte piece: source block (tile, step) in tile-major order,
+// written to its chunk-major position.
 __global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, const u16 *B2, int n_seg, int N,
-                                  int K, u16 *dst, int64_t pieces) {
+                                  int K, int kcs, u16 *dst, int64_t pieces) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= pieces) return;
   const int lane = (int)(idx & 63), q = (int)((idx >> 6) & 3);
   const int64_t blk = idx >> 8;               // (tile, step)
-  const int ksteps = K >> 6;
+  const int ksteps = K >> 6, n_tiles = (N + 31) >> 5;
   const int t = (int)(blk / ksteps), st = (int)(blk % ksteps);
   const int n = 32 * t + (lane & 31);
   const int k = 64 * st + 32 * (lane >> 5) + 8 * q;
@@ -211,15 +225,16 @@ __global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, cons
     }
     v = *(const u32x4 *)(row + k);
   }
-  *(u32x4 *)(dst + idx * 8) = v;
+  const int64_t o = pack_block(t, st, n_tiles, ksteps, kcs) * 2048 + q * 512 + lane * 8;
+  *(u32x4 *)(dst + o) = v;
 }
 
 hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
-                             int N, int K, uint16_t *dst, hipStream_t s) {
-  if (K % 64) return hipErrorInvalidValue;
+                             int N, int K, int k_chunk, uint16_t *dst, hipStream_t s) {
+  if (K % 64 || k_chunk % 64 || k_chunk <= 0) return hipErrorInvalidValue;
   const int64_t pieces = (int64_t)((N + 31) / 32) * (K / 64) * 256;
   hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, b_mode, B0, B1,
-                     B2, n_seg, N, K, dst, pieces);
+                     B2, n_seg, N, K, k_chunk / 64, dst, pieces);
   return hipGetLastError();
 }
 

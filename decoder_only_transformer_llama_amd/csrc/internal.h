@@ -114,8 +114,10 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
 // Copy B (row mapping b_mode as in GemvArgs) into tile order: 4 KB block per
 // (32-row tile t, 64-wide K step s), piece (q, lane g*32+j) = B[32t+j][64s+32g+8q..+7];
 // rows >= N are zero. dst holds ceil(N/32)*32 x K elements.
+// Tile-packed copy of B for the skinny GEMM, ordered for split-K chunks of
+// k_chunk (the chunk the skinny GEMM later runs with for this N and K).
 hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
-                             int N, int K, uint16_t *dst, hipStream_t s);
+                             int N, int K, int k_chunk, uint16_t *dst, hipStream_t s);
 int gemv_ntw(int N);               // 32-column tiles per wavefront used for N
 #ifndef GEMV_KC_MAX
 #define GEMV_KC_MAX 512
