@@ -25,8 +25,14 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # keep the compiler from emitting packed fp32 arithmetic on the device
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # every "#pragma unroll" loop over accumulator tiles must unroll fully: a
+    # loop left rolled indexes the accumulator array dynamically, which moves
+    # it to scratch memory; the remark below turns a refusal into a build error
+    "-mllvm", "-pragma-unroll-threshold=262144",
+    "-Rpass-missed=loop-unroll",
     "-Wno-unused-command-line-argument",
 ]
+UNROLL_REFUSED = "Unable to fully unroll loop as directed by unroll pragma"
 
 
 def _compile(src: str) -> str:
@@ -35,6 +41,8 @@ def _compile(src: str) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    if UNROLL_REFUSED in r.stderr:
+        raise RuntimeError(f"{src}: a '#pragma unroll' loop did not unroll fully:\n{r.stderr}")
     return obj
 
 

@@ -58,8 +58,12 @@ __host__ __device__ inline int64_t pack_block(int t, int st, int n_tiles, int ks
   return (int64_t)c * n_tiles * kcs + (int64_t)t * len + s;
 }
 
+#ifndef GEMV_OCC
+#define GEMV_OCC (KC_MAX > 512 ? 1 : 2)   // workgroups per CU the register budget is sized for
+#endif
+
 template <int NTW, int DEPTH>
-__global__ __launch_bounds__(256, KC_MAX > 512 ? 1 : 2) void gemv_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(256, GEMV_OCC) void gemv_kernel(const GemvArgs a) {
   __shared__ u32x4 sA[2][32][KC_MAX / 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;

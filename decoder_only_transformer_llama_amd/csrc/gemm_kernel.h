@@ -274,71 +274,100 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-          } else {
+          }
+          // element-wise stores: v^T where the fast path does not apply, and
+          // the cache copy
+          if (!fast || a.vcache) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-              const int row = mb + 8 * (r >> 2) + 4 * g + (r & 3);
+              const int off = 8 * (r >> 2) + 4 * g + (r & 3);
+              const int row = mb + off;
               if (row >= a.M) continue;
-              const int b = row / a.seq, s = row - b * a.seq;
+              // (sequence, position) of the row from those of the tile's first
+              // row, without a division per element
+              int b = bq, s = s0 + off;
+              while (s >= a.seq) {
+                s -= a.seq;
+                ++b;
+              }
               const int cd = cd0 + l32;
               const int hh = cd >> hd_shift, e = cd & (a.head_dim - 1);
               u16 hi, lo;
               split_pair(acc[i][j][r] * sc[r], hi, lo);
-              const int64_t o = (((int64_t)b * a.n_heads + hh) * a.head_dim + e) * a.vt_stride + s;
-              a.vth[o] = hi;
-              a.vtl[o] = lo;
-            }
-          }
-          if (a.vcache) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = mb + 8 * (r >> 2) + 4 * g + (r & 3);
-              if (row >= a.M) continue;
-              const int b = row / a.seq, s = row - b * a.seq;
-              const int cd = cd0 + l32;
-              const int hh = cd >> hd_shift, e = cd & (a.head_dim - 1);
-              a.vcache[(((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e] =
-                  f2bf(acc[i][j][r] * sc[r]);
+              if (!fast) {
+                const int64_t o = (((int64_t)b * a.n_heads + hh) * a.head_dim + e) * a.vt_stride + s;
+                a.vth[o] = hi;
+                a.vtl[o] = lo;
+              }
+              if (a.vcache) a.vcache[(((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e] = hi;
             }
           }
         }
       }
       return;
     }
+    // q, k: each 32 x 32 accumulator block goes through a per-wavefront LDS
+    // tile, so that a lane then owns 16 consecutive columns of one row: one
+    // rstd and position per lane, the (cos, sin) of its 8 pairs as 16-byte
+    // loads, and 16-byte stores of the rotated hi/lo parts.
     u16 *dh = seg == 0 ? a.qh : a.kh;
     u16 *dl = seg == 0 ? a.ql : a.kl;
+    __builtin_amdgcn_s_barrier();  // all waves are done with the K-loop buffers
+    constexpr int TQ = 36;         // row stride (floats) of the transpose tile, 16-byte aligned
+    float *tq = (float *)smem + wave * (32 * TQ);
+    const int rr = lane >> 1, c0 = 16 * (lane & 1);
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
+      const int row = m0 + wm * G::WM + i * 32 + rr;
+      const bool ok = row < a.M;
+      const int b = ok ? row / a.seq : 0, s = ok ? row - b * a.seq : 0;
+      const float sc = (a.rstd && ok) ? a.rstd[row] : 1.0f;
+      const float2 *tab = a.rope_tab + (int64_t)s * (a.head_dim >> 1);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * G::WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        const bool ok = row < a.M;
-        const int b = row / a.seq, s = row - b * a.seq;
-        const float sc = (a.rstd && ok) ? a.rstd[row] : 1.0f;
-        const float2 *tab = a.rope_tab + (int64_t)s * (a.head_dim >> 1);
+      for (int j = 0; j < G::TN; ++j) {
 #pragma unroll
-        for (int j = 0; j < G::TN; ++j) {
-          const int cd = n0 + wn * G::WN + j * 32 + l32 - seg * a.dim;
-          const int e = cd & (a.head_dim - 1);
-          const float v = acc[i][j][r] * sc;
-          const float partner = lane_swap1(v);   // element e ^ 1 of the same row
-          // the lane of the even element rotates the pair (e, e + 1) and stores
-          // both as one 4-byte word
-          if (!ok || (l32 & 1)) continue;
-          const float2 cs = tab[e >> 1];
-          const float r0 = v * cs.x - partner * cs.y;
-          const float r1 = v * cs.y + partner * cs.x;
-          u16 h0, l0, h1, l1;
-          split_pair(r0, h0, l0);
-          split_pair(r1, h1, l1);
-          const int64_t o = (int64_t)row * a.dim + cd;
-          *(uint32_t *)(dh + o) = (uint32_t)h0 | ((uint32_t)h1 << 16);
-          *(uint32_t *)(dl + o) = (uint32_t)l0 | ((uint32_t)l1 << 16);
-          if (seg == 1 && a.kcache) {
-            const int hh = cd >> hd_shift;
-            *(uint32_t *)(a.kcache + (((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e) =
-                (uint32_t)h0 | ((uint32_t)h1 << 16);
+        for (int r = 0; r < 16; ++r) tq[(8 * (r >> 2) + 4 * g + (r & 3)) * TQ + l32] = acc[i][j][r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 t4 = *(const f32x4 *)(tq + rr * TQ + c0 + 4 * q);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) v[4 * q + k] = t4[k] * sc;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();   // the tile is rewritten for the next block
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (!ok) continue;
+        const int cd = n0 + wn * G::WN + j * 32 + c0 - seg * a.dim;   // first of 16 columns
+        const int e0 = cd & (a.head_dim - 1);                          // even: 8 whole pairs
+        float rot[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 cs2 = *(const f32x4 *)(tab + (e0 >> 1) + 2 * q);   // (cos, sin) of 2 pairs
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const float x0 = v[4 * q + 2 * h], x1 = v[4 * q + 2 * h + 1];
+            const float cs = cs2[2 * h], sn = cs2[2 * h + 1];
+            rot[4 * q + 2 * h] = x0 * cs - x1 * sn;
+            rot[4 * q + 2 * h + 1] = x0 * sn + x1 * cs;
           }
+        }
+        u32x4 hi0, lo0, hi1, lo1;
+        pack8_pair(rot, hi0, lo0);
+        pack8_pair(rot + 8, hi1, lo1);
+        const int64_t o = (int64_t)row * a.dim + cd;
+        *(u32x4 *)(dh + o) = hi0;
+        *(u32x4 *)(dh + o + 8) = hi1;
+        *(u32x4 *)(dl + o) = lo0;
+        *(u32x4 *)(dl + o + 8) = lo1;
+        if (seg == 1 && a.kcache) {
+          const int hh = cd >> hd_shift;
+          u16 *kp = a.kcache + (((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e0;
+          *(u32x4 *)kp = hi0;
+          *(u32x4 *)(kp + 8) = hi1;
         }
       }
     }
