@@ -166,8 +166,10 @@ def bench_prefill(args, torch):
     ms = ev.elapsed_ms(0, 1) / args.steps
     torch.cuda.synchronize()
 
-    steps = merge_steps(traced_kernel_ms(_lib.load(), lambda: bw.block(bw.x), stream, max(3, args.steps // 2)),
-                        PREFILL_STEP_NAMES)
+    trace = traced_kernel_ms(_lib.load(), lambda: bw.block(bw.x), stream, max(3, args.steps // 2))
+    if args.raw_trace:
+        print("# prefill kernels: " + json.dumps([(l, round(t, 4)) for l, t in trace]), file=sys.stderr, flush=True)
+    steps = merge_steps(trace, PREFILL_STEP_NAMES)
     names, kms = [n for n, _ in steps], [t for _, t in steps]
     fl = block_flops(w)
     total = sum(fl.values())
@@ -293,6 +295,7 @@ def main() -> int:
     ap.add_argument("--prefill-only", action="store_true")
     ap.add_argument("--decode-only", action="store_true", help="skip the prefill leg (diagnostic runs)")
     ap.add_argument("--eager", action="store_true", help="decode: time eager launches, no HIP graph")
+    ap.add_argument("--raw-trace", action="store_true", help="print every traced prefill kernel's time")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM byte counters")
     args = ap.parse_args()
