@@ -252,8 +252,9 @@ def bench_decode(args, torch):
     att_bytes_launch = by["kv_read"] / L
     att_ms = agg["attention"] / L
     achieved = att_bytes_launch / (att_ms * 1e-3) / 1e9
+    model_prefill = None if args.no_model_prefill else bench_model_prefill(args, torch, wl)
     return {
-        "w": w, "ms": ms, "ms_eager": ms_eager, "graph": graph is not None,
+        "w": w, "ms": ms, "ms_eager": ms_eager, "graph": graph is not None, "model_prefill": model_prefill,
         "tokens_per_s": w.batch / (ms * 1e-3),
         "hbm_gbs": total_bytes / (ms * 1e-3) / 1e9,
         "bytes": total_bytes,
@@ -263,6 +264,35 @@ def bench_decode(args, torch):
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic("dec_attn"),
                      "bytes_per_launch": att_bytes_launch},
     }
+
+
+def bench_model_prefill(args, torch, wl, seq: int = 2048):
+    """Whole-model prefill on the decode workload's 7B-shape model: one
+    sequence of `seq` seeded tokens through 32 blocks (filling a KV cache),
+    the final norm and the 32000-wide head."""
+    from decoder_only_transformer_llama_amd import inputs as I
+    w, m = wl.w, wl.model
+    toks = I.tokens(w, (1, seq), device="cuda", stream=1)
+    kc, vc = m.new_cache(1, "cuda"), m.new_cache(1, "cuda")
+    for _ in range(max(1, args.warmup // 2)):
+        m.forward(toks, kc, vc)
+    torch.cuda.synchronize()
+    reps = max(2, args.steps // 4)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
+    ev.record(0, stream)
+    for _ in range(reps):
+        m.forward(toks, kc, vc)
+    ev.record(1, stream)
+    ms = ev.elapsed_ms(0, 1) / reps
+    torch.cuda.synchronize()
+    blk = block_flops(type("W", (), {"tokens": seq, "dim": w.dim, "hidden": w.hidden, "seq": seq, "batch": 1}))
+    flops = w.n_layers * sum(blk.values()) + 2.0 * seq * w.dim * w.vocab
+    del kc, vc
+    return {"workload": f"llama-7b-shape model prefill, 32 blocks + head, batch 1, seq {seq}, bf16",
+            "ms": round(ms, 3), "tokens_per_s": round(seq / (ms * 1e-3), 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
 def cpu_baseline(bw, torch, budget_s: float = 10.0, max_reps: int = 8):
@@ -301,6 +331,7 @@ def main() -> int:
     ap.add_argument("--decode-only", action="store_true", help="skip the prefill leg (diagnostic runs)")
     ap.add_argument("--eager", action="store_true", help="decode: time eager launches, no HIP graph")
     ap.add_argument("--raw-trace", action="store_true", help="print every traced prefill kernel's time")
+    ap.add_argument("--no-model-prefill", action="store_true", help="skip the whole-model prefill leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM byte counters")
     args = ap.parse_args()
@@ -318,6 +349,8 @@ def main() -> int:
         dec = bench_decode(args, torch)
         print(f"# decode: {dec['ms']:.3f} ms/step (eager {dec['ms_eager']:.3f}), {dec['tokens_per_s']:.0f} tok/s, "
               f"{dec['hbm_gbs']:.0f} GB/s; kernels {json.dumps(dec['per_kernel_ms'])}", file=sys.stderr, flush=True)
+        if dec["model_prefill"]:
+            print(f"# model prefill: {json.dumps(dec['model_prefill'])}", file=sys.stderr, flush=True)
         return 0
     pf = bench_prefill(args, torch)
     print(f"# prefill: {pf['ms']:.3f} ms/step, {pf['tokens_per_s']:.0f} tok/s, block {pf['block_tflops']:.1f} "
@@ -327,6 +360,8 @@ def main() -> int:
         dec = bench_decode(args, torch)
         print(f"# decode: {dec['ms']:.3f} ms/step (eager {dec['ms_eager']:.3f}), {dec['tokens_per_s']:.0f} tok/s, "
               f"{dec['hbm_gbs']:.0f} GB/s; kernels {json.dumps(dec['per_kernel_ms'])}", file=sys.stderr, flush=True)
+        if dec["model_prefill"]:
+            print(f"# model prefill: {json.dumps(dec['model_prefill'])}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pf["block"], torch)
     w = pf["w"]
     line = {
@@ -360,6 +395,8 @@ def main() -> int:
             "hbm_gbs": round(dec["hbm_gbs"], 1), "hbm_frac": round(dec["hbm_gbs"] / PEAK_HBM_GBS, 4),
             "bytes_per_step": dec["bytes"], "roofline": dec["roofline"], "kernels_ms": dec["per_kernel_ms"],
         }
+        if dec["model_prefill"] is not None:
+            line["model_prefill"] = dec["model_prefill"]
     line["wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(line), flush=True)
     return 0

@@ -28,7 +28,7 @@ EXPORTS = (
     "llama_hidden_dim", "llama_rmsnorm", "llama_rope", "llama_linear", "llama_causal_attn",
     "llama_swiglu_ffn", "llama_block_forward", "llama_model_forward", "llama_model_decode",
     "llama_workspace_size", "llama_status_string", "llama_last_error", "llama_trace_begin", "llama_trace_end",
-    "llama_trace_label", "llama_decode_pack_size", "llama_pack_decode_weights",
+    "llama_trace_label", "llama_argmax", "llama_decode_pack_size", "llama_pack_decode_weights",
 )
 
 
@@ -79,6 +79,7 @@ def load() -> ctypes.CDLL:
         "llama_trace_begin": [ctypes.POINTER(vp), i32],
         "llama_trace_end": [],
         "llama_trace_label": [i32],
+        "llama_argmax": [vp, i64, i32, vp, vp],
         "llama_decode_pack_size": [cfgp, ctypes.POINTER(sz)],
         "llama_pack_decode_weights": [cfgp, ctypes.POINTER(ModelWeights), vp, sz, vp],
     }

@@ -538,6 +538,14 @@ int llama_trace_begin(void *const *events, int capacity) {
   return LLAMA_OK;
 }
 
+int llama_argmax(const float *logits, int64_t rows, int vocab, int32_t *out, void *stream) {
+  if (!logits || !out) return LLAMA_ERR_NULL;
+  if (rows < 0 || vocab <= 0 || rows > INT32_MAX) return LLAMA_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(argmax_launch(logits, rows, vocab, out, s), "argmax");
+  return LLAMA_OK;
+}
+
 const char *llama_trace_label(int i) {
   return i >= 0 && i < (int)g_trace_labels.size() ? g_trace_labels[i] : nullptr;
 }

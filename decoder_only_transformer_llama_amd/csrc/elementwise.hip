@@ -453,4 +453,51 @@ hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ argmax
+// One workgroup per row: each thread scans a strided share of the row keeping
+// the largest value and its lowest index, then a tree over the block picks
+// (larger value, else lower index). Any NaN in the row gives -1.
+__global__ __launch_bounds__(256) void argmax_kernel(const float *logits, int vocab, int32_t *out) {
+  const int64_t row = blockIdx.x;
+  const float *p = logits + row * vocab;
+  float best = -INFINITY;
+  int idx = 0x7fffffff;
+  bool nan = false;
+  for (int i = threadIdx.x; i < vocab; i += 256) {
+    const float v = p[i];
+    nan |= v != v;
+    if (v > best || (v == best && i < idx)) {
+      best = v;
+      idx = i;
+    }
+  }
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ int sn;
+  if (threadIdx.x == 0) sn = 0;
+  __syncthreads();
+  if (nan) sn = 1;   // benign race: every writer stores 1
+  sv[threadIdx.x] = best;
+  si[threadIdx.x] = idx;
+  __syncthreads();
+  for (int h = 128; h > 0; h >>= 1) {
+    if ((int)threadIdx.x < h) {
+      const float v = sv[threadIdx.x + h];
+      const int j = si[threadIdx.x + h];
+      if (v > sv[threadIdx.x] || (v == sv[threadIdx.x] && j < si[threadIdx.x])) {
+        sv[threadIdx.x] = v;
+        si[threadIdx.x] = j;
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[row] = (sn || si[0] >= vocab) ? -1 : si[0];
+}
+
+hipError_t argmax_launch(const float *logits, int64_t rows, int vocab, int32_t *out, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)rows), dim3(256), 0, s, logits, vocab, out);
+  return hipGetLastError();
+}
+
 }  // namespace llama

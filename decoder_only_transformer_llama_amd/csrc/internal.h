@@ -79,6 +79,8 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
                             float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s,
                             const float *part = nullptr, int n_parts = 0, float *h_out = nullptr);
+// Index of the largest logit per row (lowest among equals; -1 if the row has a NaN).
+hipError_t argmax_launch(const float *logits, int64_t rows, int vocab, int32_t *out, hipStream_t s);
 // y = r + part[0] + ... + part[n_parts-1], fp32, n elements (n % 4 == 0).
 hipError_t resid_sum_launch(const float *r, const float *part, int n_parts, int64_t n, float *y, hipStream_t s);
 hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,

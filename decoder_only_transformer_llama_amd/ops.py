@@ -122,6 +122,19 @@ def swiglu_ffn(z, w_gate, w_up, w_down, out_dtype: torch.dtype = torch.float32) 
     return y
 
 
+def argmax(logits: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Greedy token per row of logits [..., vocab] (lowest index on ties, -1 for a NaN row)."""
+    _dev(logits)
+    if logits.dtype != torch.float32:
+        raise TypeError("logits must be float32")
+    vocab = logits.shape[-1]
+    rows = logits.numel() // vocab
+    if out is None:
+        out = torch.empty(logits.shape[:-1], dtype=torch.int32, device=logits.device)
+    L.check(L.load().llama_argmax(_p(logits), rows, vocab, _p(out), _stream()), "llama_argmax")
+    return out
+
+
 BLOCK_KEYS = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
 
 
@@ -203,6 +216,30 @@ class Model:
                                              _p(k_cache), _p(v_cache), _p(logits), _p(ws), ws.numel(), _stream()),
                 "llama_model_forward")
         return logits
+
+    def generate(self, prompt: torch.Tensor, n_new: int, k_cache: torch.Tensor,
+                 v_cache: torch.Tensor) -> torch.Tensor:
+        """Greedy generation: prefill prompt [B, T] (int32) from an empty
+        cache, then n_new tokens, each the argmax of the previous step's
+        logits and fed back through one decode step. Returns [B, n_new] int32.
+        Every step runs on the GPU; the host only enqueues."""
+        _dev(prompt, k_cache, v_cache)
+        B, T = prompt.shape
+        if T + n_new - 1 > self.cfg.max_seq:
+            raise ValueError("prompt plus generated tokens exceed max_seq")
+        out = torch.empty((B, n_new), dtype=torch.int32, device=prompt.device)
+        if n_new == 0:
+            return out
+        logits = self.forward(prompt, k_cache, v_cache)
+        tok = argmax(logits[:, -1].contiguous())
+        out[:, 0] = tok
+        step_logits = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=prompt.device)
+        for i in range(1, n_new):
+            pos = torch.full((B,), T + i - 1, dtype=torch.int32, device=prompt.device)
+            self.decode(tok, pos, k_cache, v_cache, step_logits)
+            tok = argmax(step_logits)
+            out[:, i] = tok
+        return out
 
     def decode(self, tokens: torch.Tensor, pos: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                logits: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -204,12 +204,23 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
                        const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits,
                        void *ws, size_t ws_bytes, void *stream);
 
+/* Greedy token choice over logits [rows, vocab] f32 (device): out[r] (int32,
+ * device) is the index of the largest logit of row r, the lowest index among
+ * equal maxima; a row holding a NaN (as decode gives for an invalid position)
+ * yields -1, which the embedding turns back into a NaN row. The logits are
+ * those of the output head ([P1] "The one formula"); choosing the most
+ * likely next token at each step is the plain reading of generation with
+ * them. Errors: NULL pointers, rows < 0, vocab <= 0 (LLAMA_ERR_SHAPE). */
+int llama_argmax(const float *logits, int64_t rows, int vocab, int32_t *out, void *stream);
+
 /* Decode weight pack: every projection of every block (Wq|Wk|Wv, Wo,
  * W_gate/W_up interleaved in blocks of 32 rows, W_down) and the output head,
  * copied into matrix-core tile order: for each 32-row tile and each 64-wide
  * K step one 4 KB block whose 16-byte piece for lane (g, j), step q is
- * W[32 t + j][64 s + 32 g + 8 q .. +7]. One decode step then reads every
- * weight byte in contiguous 1 KB runs. This is a load-time transform of the
+ * W[32 t + j][64 s + 32 g + 8 q .. +7]. The blocks are ordered for the
+ * split-K chunks the decode step uses (all tiles of one K chunk together), so
+ * one decode step reads every weight byte in contiguous runs; the order is
+ * internal to this library. This is a load-time transform of the
  * model (the pack costs the size of the weights once more in HBM); it does
  * not change any result. Rows past a matrix's height are zero.
  * llama_decode_pack_size: bytes of the pack for config c (host, *bytes).

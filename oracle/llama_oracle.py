@@ -268,3 +268,30 @@ def model_forward(tokens, emb, get_layer: LayerFn, n_layers: int, final_norm, ou
         vc[:, :, :T, :] = parts["v"].reshape(B, T, n_heads, hd).transpose(0, 2, 1, 3)
         x = y
     return head(x, final_norm, output, eps).reshape(B, T, -1)
+
+
+def greedy_generate(prompt, n_new: int, emb, get_layer: LayerFn, n_layers: int, final_norm, output,
+                    n_heads: int, eps: float, theta: float = 10000.0, forced=None):
+    """Greedy generation: prefill the prompt [B, T], then n_new tokens, each the
+    index of the largest logit of the previous step (the first index among
+    equal maxima, as numpy.argmax gives), fed back through one decode step at
+    the next position. Returns (tokens [B, n_new], logits [n_new, B, vocab]).
+
+    `forced` [B, n_new], when given, is fed back instead of the chosen tokens
+    (to follow another implementation's choices and compare logits step by
+    step). The caches of `get_layer` start empty and are filled in place."""
+    prompt = np.asarray(prompt, dtype=np.int64)
+    B, T = prompt.shape
+    logits = model_forward(prompt, emb, get_layer, n_layers, final_norm, output, n_heads, eps, theta)[:, -1]
+    toks, steps = [], []
+    for i in range(n_new):
+        steps.append(logits)
+        tok = np.argmax(logits, axis=-1)
+        toks.append(tok)
+        if i + 1 == n_new:
+            break
+        feed = tok if forced is None else np.asarray(forced, dtype=np.int64)[:, i]
+        pos = np.full(B, T + i, dtype=np.int64)
+        logits = model_decode(feed, pos, emb, get_layer, n_layers, final_norm, output, n_heads, eps, theta)
+    return np.stack(toks, axis=1), np.stack(steps)
+

@@ -301,3 +301,64 @@ def test_model_decode_7b_sampled_sequences():
     err = rel_err(logits[rows], want)
     print(f"7b decode logits (rows {rows}): max|d|/rms = {err:.3e}")
     assert err < TOL_BF16
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,vocab", [(1, 7), (5, 1000), (33, 32000)])
+def test_argmax(rows, vocab):
+    """Integer result: bit-exact against the first-index argmax of the same
+    fp32 logits, with planted ties and a NaN row."""
+    g = torch.Generator().manual_seed(rows * 7 + vocab)
+    x = torch.randn(rows, vocab, generator=g)
+    want = []
+    for r in range(rows):
+        j = int(torch.argmax(x[r]))
+        if r % 3 == 1 and vocab > 3:   # tie: an earlier index gets the same maximum
+            k = max(0, j - 2)
+            x[r, k] = x[r, j]
+            j = min(j, k)
+        want.append(j)
+    if rows > 2:
+        x[2, vocab // 2] = float("nan")
+        want[2] = -1
+    got = ops().argmax(x.cuda()).cpu()
+    assert got.tolist() == want
+
+
+@pytest.mark.gpu
+def test_greedy_generation():
+    """Greedy generation on the GPU: every token is the exact first-index
+    argmax of the GPU's own logits for that step; those logits match the
+    oracle fed the same tokens within the bf16 bound; and each chosen token
+    is a maximum of the oracle's logits up to that bound (several tokens can
+    be correct when their logits are within rounding of each other)."""
+    w, m, layers, gl = small_model()
+    B, T, n_new = w.batch, 8, 6
+    prompt = I.tokens(w, (B, T), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    toks = m.generate(prompt, n_new, kc, vc)
+    # the GPU's per-step logits along its own choices (fresh cache, same kernels)
+    kc2, vc2 = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    steps = [m.forward(prompt, kc2, vc2)[:, -1]]
+    for i in range(1, n_new):
+        pos = torch.full((B,), T + i - 1, dtype=torch.int32, device="cuda")
+        steps.append(m.decode(toks[:, i - 1].contiguous(), pos, kc2, vc2))
+    torch.cuda.synchronize()
+    gpu_logits = torch.stack(steps).cpu()                        # [n_new, B, vocab]
+    assert torch.equal(toks.cpu().T.long(), torch.argmax(gpu_logits, dim=-1))
+
+    hd = w.head_dim
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    caches = [(np.zeros((B, w.n_heads, w.max_seq, hd)), np.zeros((B, w.n_heads, w.max_seq, hd)))
+              for _ in range(w.n_layers)]
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    forced = toks.cpu().numpy()
+    _, want = O.greedy_generate(prompt.cpu().numpy(), n_new, emb, lambda l: (lw[l], *caches[l]), w.n_layers, fn,
+                                out, w.n_heads, w.eps, forced=forced)
+    e = rel_err(gpu_logits, want)
+    print(f"greedy generation logits max|d|/rms = {e:.3e}")
+    assert e < TOL_BF16
+    rms = np.sqrt(np.mean(want ** 2))
+    for i in range(n_new):
+        for b in range(B):
+            assert want[i, b, forced[b, i]] >= want[i, b].max() - TOL_BF16 * rms

@@ -281,3 +281,24 @@ def test_model_forward_is_block_stack_then_head():
     xn = np.array(BF.rmsnorm_rows(x.tolist(), fn.tolist(), 1e-6))
     np.testing.assert_allclose(logits[0], np.array(BF.matvec_rows(xn.tolist(), out.tolist())),
                                rtol=1e-10, atol=1e-11)
+
+
+def test_greedy_generate_matches_prefill_argmax():
+    """Each greedily generated token is the first-index argmax of a plain
+    prefill of the prompt plus the tokens generated before it (decode with a
+    cache computes the same logits as a prefill, pinned above)."""
+    L, d, H, hd, V, max_seq, B, T, n_new = 2, 16, 2, 8, 50, 12, 2, 3, 5
+    layers, emb, fn, out = _tiny_model(50, L, d, H, 48, V, max_seq)
+    prompt = np.random.default_rng(51).integers(0, V, (B, T))
+    caches = [(np.zeros((B, H, max_seq, hd)), np.zeros((B, H, max_seq, hd))) for _ in range(L)]
+    toks, step_logits = O.greedy_generate(prompt, n_new, emb, lambda l: (layers[l], *caches[l]), L, fn, out, H,
+                                          1e-6)
+    assert toks.shape == (B, n_new) and step_logits.shape == (n_new, B, V)
+    seq = prompt
+    for i in range(n_new):
+        fresh = [(np.zeros((B, H, max_seq, hd)), np.zeros((B, H, max_seq, hd))) for _ in range(L)]
+        full = O.model_forward(seq, emb, lambda l: (layers[l], *fresh[l]), L, fn, out, H, 1e-6)[:, -1]
+        np.testing.assert_allclose(step_logits[i], full, rtol=1e-10, atol=1e-11)
+        want = [min(np.flatnonzero(r == r.max())) for r in full]   # first index among equal maxima
+        assert list(toks[:, i]) == want
+        seq = np.concatenate([seq, toks[:, i:i + 1]], axis=1)
