@@ -191,6 +191,35 @@ def bench_prefill(args, torch):
     }
 
 
+def bench_other_blocks(args, torch):
+    """Throughput of the 13B-shape (4 x 2048 tokens) and 65B-shape (2 x 2048)
+    block prefill workloads, reported beside the headline (fraction of the
+    bf16 matrix-core peak)."""
+    from decoder_only_transformer_llama_amd.workloads import block_workload
+    out = {}
+    for wid in (2, 3):
+        bw = block_workload(wid, "cuda")
+        w = bw.w
+        for _ in range(max(1, args.warmup // 2)):
+            bw.block(bw.x)
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream().cuda_stream
+        reps = max(2, args.steps // 2)
+        ev = HipEvents(2)
+        ev.record(0, stream)
+        for _ in range(reps):
+            bw.block(bw.x)
+        ev.record(1, stream)
+        ms = ev.elapsed_ms(0, 1) / reps
+        torch.cuda.synchronize()
+        tf = sum(block_flops(w).values()) / (ms * 1e-3) / 1e12
+        out[w.name] = {"ms": round(ms, 3), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1), "tflops": round(tf, 1),
+                       "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+        del bw
+        torch.cuda.empty_cache()
+    return out
+
+
 def bench_decode(args, torch):
     from decoder_only_transformer_llama_amd import _lib
     from decoder_only_transformer_llama_amd.workloads import decode_workload
@@ -332,6 +361,7 @@ def main() -> int:
     ap.add_argument("--eager", action="store_true", help="decode: time eager launches, no HIP graph")
     ap.add_argument("--raw-trace", action="store_true", help="print every traced prefill kernel's time")
     ap.add_argument("--no-model-prefill", action="store_true", help="skip the whole-model prefill leg")
+    ap.add_argument("--no-other-blocks", action="store_true", help="skip the 13B/65B-shape block legs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM byte counters")
     args = ap.parse_args()
@@ -355,6 +385,10 @@ def main() -> int:
     pf = bench_prefill(args, torch)
     print(f"# prefill: {pf['ms']:.3f} ms/step, {pf['tokens_per_s']:.0f} tok/s, block {pf['block_tflops']:.1f} "
           f"TFLOP/s; kernels {json.dumps(pf['per_kernel'])}", file=sys.stderr, flush=True)
+    others = None
+    if not args.prefill_only and not args.no_other_blocks:
+        others = bench_other_blocks(args, torch)
+        print(f"# other blocks: {json.dumps(others)}", file=sys.stderr, flush=True)
     dec = None
     if not args.prefill_only:
         dec = bench_decode(args, torch)
@@ -384,6 +418,7 @@ def main() -> int:
         "block_tflops": round(pf["block_tflops"], 1),
         "roofline": pf["roofline"],
         "prefill_kernels": pf["per_kernel"],
+        "other_blocks": others,
         "cpu_baseline": cpu,
     }
     if dec is not None:
