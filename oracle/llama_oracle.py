@@ -128,37 +128,47 @@ def causal_attention(q, k, v, batch: int, seq: int, n_heads: int) -> np.ndarray:
     (diagonal included) and masked keys get exactly zero weight; head h owns
     columns [h*hd, (h+1)*hd) and heads are concatenated back in that order
     ([P1] "LLaMA is a pull request ...": the 2017 attention with a causal mask,
-    untouched)."""
+    untouched).
+
+    k and v may hold fewer heads than q (grouped-query attention, [P4] "GQA
+    Was Not an Original LLaMA Feature": a group of query heads shares one
+    key-value head). Reading: the groups are consecutive, query head h uses
+    key-value head h // (n_heads / n_kv_heads); equal head counts are plain
+    multi-head attention."""
     q, k, v = f64(q), f64(k), f64(v)
     d = q.shape[1]
     hd = d // n_heads
+    group = n_heads // (k.shape[1] // hd)
     out = np.empty_like(q)
     mask = np.triu(np.ones((seq, seq), dtype=bool), 1)        # True above the diagonal
     for b in range(batch):
         rows = slice(b * seq, (b + 1) * seq)
         for h in range(n_heads):
             cols = slice(h * hd, (h + 1) * hd)
-            s = q[rows, cols] @ k[rows, cols].T / math.sqrt(hd)
+            kv = slice((h // group) * hd, (h // group + 1) * hd)
+            s = q[rows, cols] @ k[rows, kv].T / math.sqrt(hd)
             s[mask] = -np.inf
             s = s - s.max(axis=1, keepdims=True)
             p = np.exp(s)
             p /= p.sum(axis=1, keepdims=True)
-            out[rows, cols] = p @ v[rows, cols]
+            out[rows, cols] = p @ v[rows, kv]
     return out
 
 
 def attention_over_cache(q, k_cache, v_cache, q_pos, n_heads: int) -> np.ndarray:
     """Attention of one query row per sequence over that sequence's cached keys
-    0..q_pos[b] (inclusive). q [B, dim]; caches [B, H, max_seq, hd]."""
+    0..q_pos[b] (inclusive). q [B, dim]; caches [B, n_kv_heads, max_seq, hd]
+    (query head h reads key-value head h // (n_heads / n_kv_heads))."""
     q = f64(q)
     B, d = q.shape
     hd = d // n_heads
+    group = n_heads // k_cache.shape[1]
     out = np.empty_like(q)
     for b in range(B):
         p_end = int(q_pos[b]) + 1
         for h in range(n_heads):
-            kk = f64(k_cache[b, h, :p_end])
-            vv = f64(v_cache[b, h, :p_end])
+            kk = f64(k_cache[b, h // group, :p_end])
+            vv = f64(v_cache[b, h // group, :p_end])
             s = kk @ q[b, h * hd:(h + 1) * hd] / math.sqrt(hd)
             s = s - s.max()
             p = np.exp(s)
@@ -208,7 +218,8 @@ def block_step_with_cache(x, w, pos, k_cache, v_cache, n_heads: int, eps: float,
     fp64 [B, H, max_seq, hd] and are modified in place), then the token attends
     over slots 0..pos[b] ([P4] "GQA Was Not an Original LLaMA Feature": the
     cache keeps keys and values of every previous token; LLaMA-1 is plain
-    multi-head attention, one KV head per query head)."""
+    multi-head attention, one KV head per query head; with fewer key-value
+    heads (Wk, Wv of n_kv_heads * hd rows) the caches hold n_kv_heads heads)."""
     x = f64(x)
     B, d = x.shape
     hd = d // n_heads
@@ -216,10 +227,11 @@ def block_step_with_cache(x, w, pos, k_cache, v_cache, n_heads: int, eps: float,
     q = rope(linear(z, w["wq"]), pos, hd, theta)
     k = rope(linear(z, w["wk"]), pos, hd, theta)
     v = linear(z, w["wv"])
+    n_kv = k.shape[1] // hd
     for b in range(B):
         p = int(pos[b])
-        k_cache[b, :, p, :] = k[b].reshape(n_heads, hd)
-        v_cache[b, :, p, :] = v[b].reshape(n_heads, hd)
+        k_cache[b, :, p, :] = k[b].reshape(n_kv, hd)
+        v_cache[b, :, p, :] = v[b].reshape(n_kv, hd)
     a = attention_over_cache(q, k_cache, v_cache, pos, n_heads)
     h = x + linear(a, w["wo"])
     z2 = rmsnorm(h, w["ffn_norm"], eps)
@@ -264,8 +276,9 @@ def model_forward(tokens, emb, get_layer: LayerFn, n_layers: int, final_norm, ou
     for l in range(n_layers):
         w, kc, vc = get_layer(l)
         y, parts = block_forward(x, w, B, T, n_heads, eps, theta, return_parts=True)
-        kc[:, :, :T, :] = parts["k"].reshape(B, T, n_heads, hd).transpose(0, 2, 1, 3)
-        vc[:, :, :T, :] = parts["v"].reshape(B, T, n_heads, hd).transpose(0, 2, 1, 3)
+        n_kv = parts["k"].shape[1] // hd
+        kc[:, :, :T, :] = parts["k"].reshape(B, T, n_kv, hd).transpose(0, 2, 1, 3)
+        vc[:, :, :T, :] = parts["v"].reshape(B, T, n_kv, hd).transpose(0, 2, 1, 3)
         x = y
     return head(x, final_norm, output, eps).reshape(B, T, -1)
 

@@ -55,29 +55,33 @@ def silu(v):
     return v / (1.0 + math.exp(-v)) if v > -700 else 0.0 * v
 
 
-def attention(q, k, v, batch, seq, n_heads):
+def attention(q, k, v, batch, seq, n_heads, n_kv_heads=None):
+    """Explicit loops; with n_kv_heads < n_heads, query head h reads key/value
+    head h * n_kv_heads // n_heads (consecutive groups)."""
     d = len(q[0])
     hd = d // n_heads
+    n_kv = n_kv_heads or n_heads
     out = [[0.0] * d for _ in range(batch * seq)]
     for b in range(batch):
         for h in range(n_heads):
+            kvh = h * n_kv // n_heads
             for i in range(seq):
                 qi = q[b * seq + i]
                 scores = []
                 for j in range(i + 1):            # keys 0..i, diagonal included
                     kj = k[b * seq + j]
                     acc = 0.0
-                    for e in range(h * hd, (h + 1) * hd):
-                        acc += qi[e] * kj[e]
+                    for e in range(hd):
+                        acc += qi[h * hd + e] * kj[kvh * hd + e]
                     scores.append(acc / math.sqrt(hd))
                 m = max(scores)
                 ex = [math.exp(s - m) for s in scores]
                 tot = sum(ex)
-                for e in range(h * hd, (h + 1) * hd):
+                for e in range(hd):
                     acc = 0.0
                     for j in range(i + 1):
-                        acc += ex[j] / tot * v[b * seq + j][e]
-                    out[b * seq + i][e] = acc
+                        acc += ex[j] / tot * v[b * seq + j][kvh * hd + e]
+                    out[b * seq + i][h * hd + e] = acc
     return out
 
 

@@ -302,3 +302,58 @@ def test_greedy_generate_matches_prefill_argmax():
         want = [min(np.flatnonzero(r == r.max())) for r in full]   # first index among equal maxima
         assert list(toks[:, i]) == want
         seq = np.concatenate([seq, toks[:, i:i + 1]], axis=1)
+
+
+def _gqa_block(seed, d=16, H=4, n_kv=2, hidden=48):
+    w = _tiny_block(seed, d, H, hidden)
+    hd = d // H
+    r = np.random.default_rng(seed + 1000)
+    w["wk"] = 0.3 * r.standard_normal((n_kv * hd, d))
+    w["wv"] = 0.3 * r.standard_normal((n_kv * hd, d))
+    return w
+
+
+def _repeat_kv(w, H, n_kv, hd):
+    """MHA weights equivalent to grouped K/V heads: each key-value head's rows
+    copied for every query head of its group."""
+    g = H // n_kv
+    m = dict(w)
+    for key in ("wk", "wv"):
+        m[key] = np.concatenate([w[key][(h // g) * hd:(h // g + 1) * hd] for h in range(H)], axis=0)
+    return m
+
+
+def test_gqa_attention_brute_force():
+    B, S, H, n_kv, hd = 2, 5, 4, 2, 4
+    q = _rand((B * S, H * hd), 60)
+    k, v = _rand((B * S, n_kv * hd), 61), _rand((B * S, n_kv * hd), 62)
+    got = O.causal_attention(q, k, v, B, S, H)
+    want = BF.attention(q.tolist(), k.tolist(), v.tolist(), B, S, H, n_kv)
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-11, atol=1e-12)
+
+
+@pytest.mark.parametrize("n_kv", [1, 2, 4])
+def test_gqa_block_equals_mha_with_repeated_kv(n_kv):
+    """Grouped K/V heads compute the same block as multi-head attention whose
+    K/V projections repeat each group's rows (MQA at n_kv = 1, MHA at n_kv = H)."""
+    B, S, d, H = 2, 6, 16, 4
+    w = _gqa_block(70 + n_kv, d, H, n_kv)
+    x = _rand((B * S, d), 71)
+    got = O.block_forward(x, w, B, S, H, 1e-6, 1e4)
+    want = O.block_forward(x, _repeat_kv(w, H, n_kv, d // H), B, S, H, 1e-6, 1e4)
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_gqa_decode_equals_prefill_last_row():
+    L, d, H, n_kv, V, max_seq, B = 2, 16, 4, 2, 50, 12, 2
+    hd = d // H
+    r = np.random.default_rng(80)
+    layers = [_gqa_block(81 + l, d, H, n_kv) for l in range(L)]
+    emb, fn, out = r.standard_normal((V, d)), 1 + 0.1 * r.standard_normal(d), 0.3 * r.standard_normal((V, d))
+    toks = r.integers(0, V, (B, 7))
+    c1 = [(np.zeros((B, n_kv, max_seq, hd)), np.zeros((B, n_kv, max_seq, hd))) for _ in range(L)]
+    full = O.model_forward(toks, emb, lambda l: (layers[l], *c1[l]), L, fn, out, H, 1e-6)
+    c2 = [(np.zeros((B, n_kv, max_seq, hd)), np.zeros((B, n_kv, max_seq, hd))) for _ in range(L)]
+    O.model_forward(toks[:, :6], emb, lambda l: (layers[l], *c2[l]), L, fn, out, H, 1e-6)
+    dec = O.model_decode(toks[:, 6], np.full(B, 6), emb, lambda l: (layers[l], *c2[l]), L, fn, out, H, 1e-6)
+    np.testing.assert_allclose(dec, full[:, 6], rtol=1e-10, atol=1e-11)
