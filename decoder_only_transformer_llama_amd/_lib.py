@@ -36,7 +36,7 @@ class LlamaConfig(ctypes.Structure):
     _fields_ = [("dim", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("numerics", ctypes.c_uint32)]
+                ("numerics", ctypes.c_uint32), ("n_kv_heads", ctypes.c_int32)]
 
 
 class BlockWeights(ctypes.Structure):

@@ -102,7 +102,13 @@ int choose_bn(int M, int N) {
 struct ColPart {
   int bn, n_base, n_end;
 };
-int plan_qkv(int M, int N, ColPart parts[2]) {
+int plan_qkv(int M, int d, int kvd, ColPart parts[2]) {
+  const int N = d + 2 * kvd;
+  if (kvd != d) {   // grouped K/V heads: q in 256-wide tiles, k and v (multiples of 128) in 128-wide tiles
+    parts[0] = {256, 0, d};
+    parts[1] = {128, d, N};
+    return 2;
+  }
   const int cus = cu_count();
   const int tm = (M + 255) / 256, tn = (N + 255) / 256;
   const int full_rounds = (tm * tn) / cus;
@@ -156,8 +162,20 @@ int check_block_cfg(const llama_config *c, int batch, int seq) {
   if (c->dtype == LLAMA_BF16) {
     if (c->dim % 256 || c->hidden % 128) return LLAMA_ERR_UNSUPPORTED;
   }
+  // grouped K/V heads: a divisor of n_heads, groups of 1, 2, 4 or 8, K/V
+  // width a multiple of the 128-column GEMM tile; bf16 path only
+  const int nkv = c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads;
+  if (c->n_kv_heads < 0 || nkv > c->n_heads || c->n_heads % nkv) return LLAMA_ERR_SHAPE;
+  const int group = c->n_heads / nkv;
+  if (group > 1) {
+    if (c->dtype != LLAMA_BF16) return LLAMA_ERR_UNSUPPORTED;
+    if ((group & (group - 1)) || group > 8 || (nkv * hd) % 128) return LLAMA_ERR_UNSUPPORTED;
+  }
   return LLAMA_OK;
 }
+
+int kv_heads(const llama_config *c) { return c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads; }
+int kv_dim(const llama_config *c) { return kv_heads(c) * (c->dim / c->n_heads); }
 
 int check_block_w(const llama_block_weights *w) {
   if (!w) return LLAMA_ERR_NULL;
@@ -211,7 +229,7 @@ BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq) {
     b.kh = cv.take<uint16_t>(n * d);
     b.kl = cv.take<uint16_t>(n * d);
     b.part = (float *)b.qh;   // qh, ql, kh, kl are contiguous: 8 n d bytes = 2 n d floats
-    const size_t vt = (size_t)batch * d * vt_stride_of(seq);
+    const size_t vt = (size_t)batch * kv_dim(c) * vt_stride_of(seq);
     b.vth = cv.take<uint16_t>(vt);
     b.vtl = cv.take<uint16_t>(vt);
     b.a_hi = cv.take<uint16_t>(n * d);
@@ -255,7 +273,7 @@ void gemv_split(int N, int K, int &splits, int &k_chunk) {
 
 size_t dec_part_floats(const llama_config *c, int batch) {
   const int d = c->dim, h = c->hidden;
-  const int NK[5][2] = {{3 * d, d}, {d, d}, {2 * h, d}, {d, h}, {c->vocab, d}};
+  const int NK[5][2] = {{d + 2 * kv_dim(c), d}, {d, d}, {2 * h, d}, {d, h}, {c->vocab, d}};
   size_t mx = 0;
   for (int i = 0; i < 5; ++i) {
     int sp, kc;
@@ -335,7 +353,7 @@ PackLayout pack_layout(const llama_config *c) {
   PackLayout p{};
   const int d = c->dim, h = c->hidden;
   p.qkv = 0;
-  p.o = tile_elems(3 * d, d);
+  p.o = tile_elems(d + 2 * kv_dim(c), d);
   p.gu = p.o + tile_elems(d, d);
   p.down = p.gu + tile_elems(2 * h, d);
   p.layer = p.down + tile_elems(d, h);
@@ -362,7 +380,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
 
   GemmArgs q{};
   q.M = M;
-  q.N = 3 * d;
+  const int kvd = kv_dim(c), nkv = kv_heads(c);
+  q.N = d + 2 * kvd;
   q.K = d;
   q.A = b.xg_hi;
   q.A_lo = qkv_pair ? b.xg_lo : nullptr;
@@ -384,12 +403,15 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.n_heads = H;
   q.head_dim = hd;
   q.dim = d;
+  q.n_seg_kv = kvd;
+  q.kv_dim = kvd;
+  q.n_kv_heads = nkv;
   q.vt_stride = vts;
   q.kcache = kcache;
   q.vcache = vcache;
   q.max_seq = max_seq;
   ColPart qp[2];
-  const int nqp = plan_qkv(M, 3 * d, qp);
+  const int nqp = plan_qkv(M, d, kvd, qp);
   for (int i = 0; i < nqp; ++i) {
     q.n_base = qp[i].n_base;
     q.n_end = qp[i].n_end;
@@ -411,6 +433,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   at.n_heads = H;
   at.head_dim = hd;
   at.dim = d;
+  at.kv_dim = kvd;
+  at.n_kv_heads = nkv;
   at.vt_stride = vts;
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
   HIP_TRY(attn_prefill_launch(at, (num & LLAMA_NUM_QK_PAIR) ? 1 : 0, (num & LLAMA_NUM_V_PAIR) ? 1 : 0, s),
@@ -684,6 +708,8 @@ int llama_causal_attn(int in_dtype, int out_dtype, const void *q, const void *k,
   at.n_heads = n_heads;
   at.head_dim = head_dim;
   at.dim = d;
+  at.kv_dim = d;
+  at.n_kv_heads = n_heads;
   at.vt_stride = vts;
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
   // bf16 inputs are exact, so their lo parts are zero: one pass each.
@@ -780,7 +806,7 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
   float *xa = cv.take<float>(n * d), *xb = cv.take<float>(n * d);
   const BlockWs b = carve_block(cv, c, batch, seq);
   HIP_TRY(embed_launch(0, w->tok_embeddings, tokens, n, d, c->vocab, xa, s), "embedding");
-  const size_t layer_elems = (size_t)batch * c->n_heads * c->max_seq * hd;
+  const size_t layer_elems = (size_t)batch * kv_heads(c) * c->max_seq * hd;
   for (int l = 0; l < c->n_layers; ++l) {
     st = block_bf16(c, &w->layers[l], LLAMA_F32, xa, xb, batch, seq, b,
                     (uint16_t *)k_cache + l * layer_elems, (uint16_t *)v_cache + l * layer_elems, c->max_seq, s);
@@ -825,6 +851,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   da.batch = batch;
   da.dim = d;
   da.n_heads = c->n_heads;
+  da.n_kv_heads = kv_heads(c);
   da.head_dim = hd;
   da.hidden = c->hidden;
   da.max_seq = c->max_seq;
@@ -832,7 +859,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   da.eps = c->norm_eps;
   da.pos = pos;
   da.rope_tab = dw.rope_tab;
-  const size_t layer_elems = (size_t)batch * c->n_heads * c->max_seq * hd;
+  const size_t layer_elems = (size_t)batch * kv_heads(c) * c->max_seq * hd;
 
   HIP_TRY(rope_table_pos_launch(dw.rope_tab, pos, batch, hd, c->rope_theta, c->max_seq, s), "rope table");
   HIP_TRY(dec_embed_norm_launch(da, (const uint16_t *)w->tok_embeddings, tokens,
@@ -858,6 +885,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
     g.B1 = (const uint16_t *)b1;
     g.B2 = (const uint16_t *)b2;
     g.n_seg = d;
+    g.n_seg_kv = kv_dim(c);
     g.part = dw.part;
     return gemv_launch(g, s);
   };
@@ -867,7 +895,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
     int sp;
     const uint16_t *lp = pack ? pack + (size_t)l * pl.layer : nullptr;
     packed_mat = lp ? lp + pl.qkv : nullptr;
-    HIP_TRY(gemv(3 * d, d, BMODE_CONCAT3, L.wq, L.wk, L.wv, sp), "qkv projection");
+    HIP_TRY(gemv(d + 2 * kv_dim(c), d, BMODE_CONCAT3, L.wq, L.wk, L.wv, sp), "qkv projection");
     HIP_TRY(dec_attn_launch(da, dw.part, sp, dw.rstd, kc, vc, dw.ag_hi, dw.ag_lo, s), "attention");
     packed_mat = lp ? lp + pl.o : nullptr;
     HIP_TRY(gemv(d, d, BMODE_PLAIN, L.wo, nullptr, nullptr, sp), "output projection");
@@ -915,21 +943,24 @@ int llama_pack_decode_weights(const llama_config *c, const llama_model_weights *
     gemv_split(N, K, sp, kc);
     return kc;
   };
+  const int kvd = kv_dim(c), nqkv = d + 2 * kvd;
   for (int l = 0; l < c->n_layers; ++l) {
     const llama_block_weights &L = w->layers[l];
     uint16_t *lp = out + (size_t)l * pl.layer;
     HIP_TRY(pack_tiles_launch(BMODE_CONCAT3, (const uint16_t *)L.wq, (const uint16_t *)L.wk, (const uint16_t *)L.wv,
-                              d, 3 * d, d, kc_of(3 * d, d), lp + pl.qkv, s),
+                              d, kvd, nqkv, d, kc_of(nqkv, d), lp + pl.qkv, s),
             "pack qkv");
-    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.wo, nullptr, nullptr, d, d, d, kc_of(d, d), lp + pl.o, s),
+    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.wo, nullptr, nullptr, d, 0, d, d, kc_of(d, d),
+                              lp + pl.o, s),
             "pack o");
-    HIP_TRY(pack_tiles_launch(BMODE_GATEUP, (const uint16_t *)L.w_gate, (const uint16_t *)L.w_up, nullptr, d, 2 * h, d,
-                              kc_of(2 * h, d), lp + pl.gu, s),
+    HIP_TRY(pack_tiles_launch(BMODE_GATEUP, (const uint16_t *)L.w_gate, (const uint16_t *)L.w_up, nullptr, d, 0,
+                              2 * h, d, kc_of(2 * h, d), lp + pl.gu, s),
             "pack gate/up");
-    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.w_down, nullptr, nullptr, d, d, h, kc_of(d, h), lp + pl.down, s),
+    HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)L.w_down, nullptr, nullptr, d, 0, d, h, kc_of(d, h),
+                              lp + pl.down, s),
             "pack down");
   }
-  HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)w->output, nullptr, nullptr, d, c->vocab, d,
+  HIP_TRY(pack_tiles_launch(BMODE_PLAIN, (const uint16_t *)w->output, nullptr, nullptr, d, 0, c->vocab, d,
                             kc_of(c->vocab, d), out + pl.head_off, s),
           "pack head");
   return LLAMA_OK;

@@ -81,7 +81,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   const int qi = q0 + 32 * w + l32;          // this lane's query
   const int qwave_max = q0 + 32 * w + 31;
   const int64_t tok0 = (int64_t)b * S;
-  const int64_t vbase = ((int64_t)b * a.n_heads + h) * HD * a.vt_stride;
+  // key/value head of this query head: consecutive groups of n_heads / n_kv_heads
+  const int n_kv = a.n_kv_heads > 0 ? a.n_kv_heads : a.n_heads;
+  const int kvd = a.kv_dim > 0 ? a.kv_dim : a.dim;
+  const int hk = h / (a.n_heads / n_kv);
+  const int64_t vbase = ((int64_t)b * n_kv + hk) * HD * a.vt_stride;
 
   // ---- direct-to-LDS tile loads: block q of this wavefront, lane i -> LDS slot i
   auto issue = [&](int kt) {
@@ -96,7 +100,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
         const int row = kb * (64 / KCH) + lane / KCH;
         const int c = (lane % KCH) ^ rswz<KCH>(row);
         const int key = min(kt * KT + row, S - 1);   // rows past S load a valid key; masked later
-        src = (part ? a.kl : a.kh) + (tok0 + key) * a.dim + h * HD + 8 * c;
+        src = (part ? a.kl : a.kh) + (tok0 + key) * kvd + hk * HD + 8 * c;
         dst = st + part * KTILE + kb * 64;
       } else {
         const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
@@ -258,7 +262,7 @@ static hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, hipStream_t s) {
   if (a.batch * a.seq == 0) return hipSuccess;
   if (a.seq % 32) {
-    const int64_t rows = (int64_t)a.batch * a.n_heads * a.head_dim;
+    const int64_t rows = (int64_t)a.batch * (a.n_kv_heads > 0 ? a.n_kv_heads : a.n_heads) * a.head_dim;
     const int64_t n = rows * (a.vt_stride - a.seq);
     hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        (u16 *)a.vth, v_pair ? (u16 *)a.vtl : (u16 *)nullptr, rows, a.seq, a.vt_stride);

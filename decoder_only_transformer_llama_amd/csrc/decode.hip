@@ -97,8 +97,7 @@ __global__ __launch_bounds__(256, GEMV_OCC) void gemv_kernel(const GemvArgs a) {
       const int blk = nn >> 5;
       p = ((blk & 1) ? a.B1 : a.B0) + (int64_t)((blk >> 1) * 32 + (nn & 31)) * a.K;
     } else if (a.b_mode == BMODE_CONCAT3) {
-      const int seg = nn / a.n_seg;
-      p = (seg == 0 ? a.B0 : (seg == 1 ? a.B1 : a.B2)) + (int64_t)(nn - seg * a.n_seg) * a.K;
+      p = concat3_row(a.B0, a.B1, a.B2, a.n_seg, a.n_seg_kv > 0 ? a.n_seg_kv : a.n_seg, nn, a.K);
     } else {
       p = a.B0 + (int64_t)nn * a.K;
     }
@@ -205,8 +204,8 @@ int gemv_ntw(int N) {
 
 // One thread per 16-byte piece: source block (tile, step) in tile-major order,
 // written to its chunk-major position.
-__global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, const u16 *B2, int n_seg, int N,
-                                  int K, int kcs, u16 *dst, int64_t pieces) {
+__global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, const u16 *B2, int n_seg, int n_seg_kv,
+                                  int N, int K, int kcs, u16 *dst, int64_t pieces) {
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= pieces) return;
   const int lane = (int)(idx & 63), q = (int)((idx >> 6) & 3);
@@ -222,8 +221,7 @@ __global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, cons
       const int b32 = n >> 5;
       row = ((b32 & 1) ? B1 : B0) + (int64_t)((b32 >> 1) * 32 + (n & 31)) * K;
     } else if (b_mode == BMODE_CONCAT3) {
-      const int seg = n / n_seg;
-      row = (seg == 0 ? B0 : (seg == 1 ? B1 : B2)) + (int64_t)(n - seg * n_seg) * K;
+      row = concat3_row(B0, B1, B2, n_seg, n_seg_kv > 0 ? n_seg_kv : n_seg, n, K);
     } else {
       row = B0 + (int64_t)n * K;
     }
@@ -234,11 +232,11 @@ __global__ void pack_tiles_kernel(int b_mode, const u16 *B0, const u16 *B1, cons
 }
 
 hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
-                             int N, int K, int k_chunk, uint16_t *dst, hipStream_t s) {
+                             int n_seg_kv, int N, int K, int k_chunk, uint16_t *dst, hipStream_t s) {
   if (K % 64 || k_chunk % 64 || k_chunk <= 0) return hipErrorInvalidValue;
   const int64_t pieces = (int64_t)((N + 31) / 32) * (K / 64) * 256;
   hipLaunchKernelGGL(pack_tiles_kernel, dim3((unsigned)((pieces + 255) / 256)), dim3(256), 0, s, b_mode, B0, B1,
-                     B2, n_seg, N, K, k_chunk / 64, dst, pieces);
+                     B2, n_seg, n_seg_kv, N, K, k_chunk / 64, dst, pieces);
   return hipGetLastError();
 }
 
@@ -460,7 +458,7 @@ DEV float lane_group_sum(float v) {
 
 constexpr int kMaxSeq = 2048;   // longest decode cache (positions) the attention kernel unrolls for
 
-template <int HD>
+template <int HD, int G>
 __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
                                                        const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
                                                        u16 *a_lo) {
@@ -472,59 +470,70 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   constexpr int UNR = DEC_ATTN_UNROLL; // key instructions per wavefront per step
   constexpr int KPS = 4 * KPW * UNR;   // keys per workgroup step
   constexpr int NG = 4 * KPW;          // lane groups per workgroup
-  __shared__ float sq[HD], sknew[HD], svnew[HD];
-  __shared__ float gm[NG], gl[NG], snew;
-  __shared__ float osum[NG][HD];
-  const int h = blockIdx.x, b = blockIdx.y;
+  // One workgroup per (key/value head hk, sequence b): the G query heads
+  // hk*G .. hk*G+G-1 share its cached keys and values, which are read once.
+  __shared__ float sq[G][HD], sknew[HD], svnew[HD];
+  __shared__ float gm[NG][G], gl[NG][G], snew[G];
+  __shared__ float osum[NG][G][HD];
+  const int hk = blockIdx.x, b = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int p = d.pos[b];
   const bool ok = pos_ok(p, d.max_seq);
-  const int64_t cbase = ((int64_t)b * d.n_heads + h) * d.max_seq * HD;
+  const int kvd = d.n_kv_heads * HD;
+  const int64_t cbase = ((int64_t)b * d.n_kv_heads + hk) * d.max_seq * HD;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
 
-  // ---- 1. q, k, v of the new token (threads 0..HD-1: channel e)
-  if (tid < HD) {
-    const int e = tid;
-    const int N = 3 * d.dim;
+  // ---- 1. q (G heads), k, v of the new token: channel c of [q_0 .. q_{G-1}, k, v]
+  {
+    const int N = d.dim + 2 * kvd;
     const int64_t stride = (int64_t)d.batch * N;
-    const float *pp = part + (int64_t)b * N + h * HD + e;
-    float q = sum_parts(0.f, pp, stride, splits);
-    float k = sum_parts(0.f, pp + d.dim, stride, splits);
-    float v = sum_parts(0.f, pp + 2 * d.dim, stride, splits);
     const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
-    q *= r;
-    k *= r;
-    v *= r;
-    const float qp = __shfl_xor(q, 1, 64), kp = __shfl_xor(k, 1, 64);
-    const float2 cs = d.rope_tab[b * (HD / 2) + (e >> 1)];
-    q = (e & 1) ? qp * cs.y + q * cs.x : q * cs.x - qp * cs.y;
-    k = (e & 1) ? kp * cs.y + k * cs.x : k * cs.x - kp * cs.y;
-    // the cache holds bf16: the new key/value enter attention as stored
-    const u16 kb = f2bf(k), vb = f2bf(v);
-    sq[e] = q * scale;
-    sknew[e] = bf2f(kb);
-    svnew[e] = bf2f(vb);
-    if (ok) {
-      kc[cbase + (int64_t)p * HD + e] = kb;
-      vc[cbase + (int64_t)p * HD + e] = vb;
+    for (int c = tid; c < (G + 2) * HD; c += 256) {   // stride 256: pairs (e, e^1) stay in one pass
+      const int gq = c / HD, e = c % HD;
+      const int col = gq < G ? (hk * G + gq) * HD + e : d.dim + (gq - G) * kvd + hk * HD + e;
+      float x = sum_parts(0.f, part + (int64_t)b * N + col, stride, splits) * r;
+      const float xp = __shfl_xor(x, 1, 64);   // RoPE partner (channel e ^ 1)
+      if (gq <= G) {                           // q heads and k are rotated, v is not
+        const float2 cs = d.rope_tab[b * (HD / 2) + (e >> 1)];
+        x = (e & 1) ? xp * cs.y + x * cs.x : x * cs.x - xp * cs.y;
+      }
+      if (gq < G) {
+        sq[gq][e] = x * scale;
+      } else {
+        // the cache holds bf16: the new key/value enter attention as stored
+        const u16 xb = f2bf(x);
+        (gq == G ? sknew : svnew)[e] = bf2f(xb);
+        if (ok) (gq == G ? kc : vc)[cbase + (int64_t)p * HD + e] = xb;
+      }
     }
   }
   __syncthreads();
   const int nk = ok ? p : 0;    // cached keys 0..p-1; key p is the new one
-  if (w == 0) {                 // the new key's score (log2 domain)
-    float s = 0.f;
-    for (int e = lane; e < HD; e += 64) s += sq[e] * sknew[e];
-    s = wave_sum(s);
-    if (lane == 0) snew = s;
+  if (w == 0) {                 // the new key's scores (log2 domain)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float s = 0.f;
+      for (int e = lane; e < HD; e += 64) s += sq[g][e] * sknew[e];
+      s = wave_sum(s);
+      if (lane == 0) snew[g] = s;
+    }
   }
 
   // ---- 2. one pass over the cached keys and values
   const int kg = lane / LPK, d8 = lane % LPK;
-  float qv[8];
+  float qv[G][8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) qv[i] = sq[d8 * 8 + i];
-  float m_run = -INFINITY, l_run = 0.f;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[g][i] = sq[g][d8 * 8 + i];
+  float m_run[G], l_run[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m_run[g] = -INFINITY;
+    l_run[g] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[g][i] = 0.f;
+  }
   const int nsteps = (nk + KPS - 1) / KPS;
   const int kbase = w * KPW * UNR + kg;          // + st * KPS + u * KPW
   // Loads are unconditional: keys past the range read key max(nk-1, 0) (a
@@ -539,33 +548,40 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
     }
   };
   auto step = [&](const u32x4 (&kr)[UNR], const u32x4 (&vr)[UNR], int st) {
-    float sc[UNR];
-    float mx = m_run;
+    float kv[UNR][8], vv[UNR][8];
+    bool live[UNR];
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      float kv[8];
-      unpack8(kr[u], kv);
-      float sdot = 0.f;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sdot = fmaf(qv[i], kv[i], sdot);
-      sdot = lane_group_sum<LPK>(sdot);
-      sc[u] = st * KPS + kbase + u * KPW < nk ? sdot : -INFINITY;
-      mx = fmaxf(mx, sc[u]);
+      unpack8(kr[u], kv[u]);
+      unpack8(vr[u], vv[u]);
+      live[u] = st * KPS + kbase + u * KPW < nk;
     }
-    const float m_use = mx == -INFINITY ? 0.f : mx;
-    const float alpha = exp2f(m_run - m_use);
-    m_run = mx;
-    l_run *= alpha;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] *= alpha;
+    for (int g = 0; g < G; ++g) {
+      float sc[UNR];
+      float mx = m_run[g];
 #pragma unroll
-    for (int u = 0; u < UNR; ++u) {
-      const float pr = exp2f(sc[u] - m_use);
-      l_run += pr;
-      float vv[8];
-      unpack8(vr[u], vv);
+      for (int u = 0; u < UNR; ++u) {
+        float sdot = 0.f;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(pr, vv[i], acc[i]);
+        for (int i = 0; i < 8; ++i) sdot = fmaf(qv[g][i], kv[u][i], sdot);
+        sdot = lane_group_sum<LPK>(sdot);
+        sc[u] = live[u] ? sdot : -INFINITY;
+        mx = fmaxf(mx, sc[u]);
+      }
+      const float m_use = mx == -INFINITY ? 0.f : mx;
+      const float alpha = exp2f(m_run[g] - m_use);
+      m_run[g] = mx;
+      l_run[g] *= alpha;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
+#pragma unroll
+      for (int u = 0; u < UNR; ++u) {
+        const float pr = exp2f(sc[u] - m_use);
+        l_run[g] += pr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(pr, vv[u][i], acc[g][i]);
+      }
     }
   };
   // The step loop unrolls fully (a cache holds at most kMaxSeq positions) and
@@ -587,29 +603,35 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
     __builtin_amdgcn_sched_barrier(0);
   }
   if (d8 == 0) {
-    gm[w * KPW + kg] = m_run;
-    gl[w * KPW + kg] = l_run;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      gm[w * KPW + kg][g] = m_run[g];
+      gl[w * KPW + kg][g] = l_run[g];
+    }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) osum[w * KPW + kg][d8 * 8 + i] = acc[i];
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) osum[w * KPW + kg][g][d8 * 8 + i] = acc[g][i];
   __syncthreads();
 
-  // ---- 3. merge the lane groups and the new key (fixed order), normalise
-  if (tid < HD) {
-    const int e = tid;
-    float M = snew;
-    for (int gi = 0; gi < NG; ++gi) M = fmaxf(M, gm[gi]);
-    float pn = exp2f(snew - M);
+  // ---- 3. per query head: merge the lane groups and the new key (fixed
+  // order), normalise, write the bf16 hi/lo pair the Wo projection consumes
+  for (int c = tid; c < G * HD; c += 256) {
+    const int g = c / HD, e = c % HD;
+    float M = snew[g];
+    for (int gi = 0; gi < NG; ++gi) M = fmaxf(M, gm[gi][g]);
+    const float pn = exp2f(snew[g] - M);
     float L = pn, o = pn * svnew[e];
     for (int gi = 0; gi < NG; ++gi) {
-      const float f = exp2f(gm[gi] - M);   // 0 for a group that saw no key
-      L += f * gl[gi];
-      o += f * osum[gi][e];
+      const float f = exp2f(gm[gi][g] - M);   // 0 for a group that saw no key
+      L += f * gl[gi][g];
+      o += f * osum[gi][g][e];
     }
     const float v = ok ? o / L : __builtin_nanf("");
     u16 hi, lo;
     split_pair(v, hi, lo);
-    const int64_t oo = (int64_t)b * d.dim + h * HD + e;
+    const int64_t oo = (int64_t)b * d.dim + (hk * G + g) * HD + e;
     a_hi[oo] = hi;
     a_lo[oo] = lo;
   }
@@ -618,14 +640,25 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
                            uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s) {
   if (d.max_seq > kMaxSeq) return hipErrorInvalidValue;
-  dim3 grid(d.n_heads, d.batch);
-  if (d.head_dim == 128)
-    hipLaunchKernelGGL(dec_attn_kernel<128>, grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo);
-  else if (d.head_dim == 64)
-    hipLaunchKernelGGL(dec_attn_kernel<64>, grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  if (d.n_kv_heads <= 0 || d.n_heads % d.n_kv_heads) return hipErrorInvalidValue;
+  const int group = d.n_heads / d.n_kv_heads;
+  dim3 grid(d.n_kv_heads, d.batch);
+#define DEC_ATTN_CASE(HD_, G_)                                                                              \
+  if (d.head_dim == HD_ && group == G_) {                                                                  \
+    hipLaunchKernelGGL((dec_attn_kernel<HD_, G_>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi, \
+                       a_lo);                                                                              \
+    return hipGetLastError();                                                                              \
+  }
+  DEC_ATTN_CASE(128, 1)
+  DEC_ATTN_CASE(128, 2)
+  DEC_ATTN_CASE(128, 4)
+  DEC_ATTN_CASE(128, 8)
+  DEC_ATTN_CASE(64, 1)
+  DEC_ATTN_CASE(64, 2)
+  DEC_ATTN_CASE(64, 4)
+  DEC_ATTN_CASE(64, 8)
+#undef DEC_ATTN_CASE
+  return hipErrorInvalidValue;
 }
 
 }  // namespace llama

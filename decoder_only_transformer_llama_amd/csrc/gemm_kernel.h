@@ -116,9 +116,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
       const int row = (n0 >> 1) + (blk >> 1) * 32 + (r & 31);
       ptr = ((blk & 1) ? a.B1 : a.B0) + (int64_t)row * a.K;
     } else if (a.b_mode == BMODE_CONCAT3) {
-      const int n = n0 + r, seg = n / a.n_seg;
-      const u16 *base = seg == 0 ? a.B0 : (seg == 1 ? a.B1 : a.B2);
-      ptr = base + (int64_t)(n - seg * a.n_seg) * a.K;
+      ptr = concat3_row(a.B0, a.B1, a.B2, a.n_seg, a.n_seg_kv > 0 ? a.n_seg_kv : a.n_seg, min(n0 + r, a.N - 1),
+                        a.K);
     } else {
       ptr = a.B0 + (int64_t)min(n0 + r, a.N - 1) * a.K;
     }
@@ -225,7 +224,12 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
 
   // ---------------------------------------------------------------- epilogue
   if (EPI == EPI_QKV) {
-    const int seg = n0 / a.dim;  // uniform per workgroup (dim % BN == 0)
+    // segment of this workgroup's columns: q [0, dim), k [dim, dim + kvd),
+    // v [dim + kvd, dim + 2 kvd) (uniform: dim and kvd are multiples of BN)
+    const int kvd = a.kv_dim > 0 ? a.kv_dim : a.dim;
+    const int n_kv = a.n_kv_heads > 0 ? a.n_kv_heads : a.n_heads;
+    const int seg = n0 < a.dim ? 0 : (n0 < a.dim + kvd ? 1 : 2);
+    const int seg_base = seg == 0 ? 0 : (seg == 1 ? a.dim : a.dim + kvd);
     const int hd_shift = a.head_dim == 128 ? 7 : 6;
     if (seg == 2) {
       // v: transpose each 32x32 accumulator tile through LDS, store rows of v^T
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
         }
 #pragma unroll
         for (int j = 0; j < G::TN; ++j) {
-          const int cd0 = n0 + wn * G::WN + j * 32 - 2 * a.dim;
+          const int cd0 = n0 + wn * G::WN + j * 32 - seg_base;
           if (fast) {
 #pragma unroll
             for (int rq = 0; rq < 4; ++rq) {
@@ -263,7 +267,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
             const int ce = lane >> 1, half = lane & 1;
             const int cd = cd0 + ce;
             const int hh = cd >> hd_shift, e = cd & (a.head_dim - 1);
-            const int64_t o = (((int64_t)bq * a.n_heads + hh) * a.head_dim + e) * a.vt_stride + s0 + 16 * half;
+            const int64_t o = (((int64_t)bq * n_kv + hh) * a.head_dim + e) * a.vt_stride + s0 + 16 * half;
             const u32x4 *srch = (const u32x4 *)(tr + ce * TS + 16 * half);
             const u32x4 *srcl = (const u32x4 *)(tr + 32 * TS + ce * TS + 16 * half);
             const u32x4 h0 = srch[0], h1 = srch[1], q0 = srcl[0], q1 = srcl[1];
@@ -295,11 +299,11 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
               u16 hi, lo;
               split_pair(acc[i][j][r] * sc[r], hi, lo);
               if (!fast) {
-                const int64_t o = (((int64_t)b * a.n_heads + hh) * a.head_dim + e) * a.vt_stride + s;
+                const int64_t o = (((int64_t)b * n_kv + hh) * a.head_dim + e) * a.vt_stride + s;
                 a.vth[o] = hi;
                 a.vtl[o] = lo;
               }
-              if (a.vcache) a.vcache[(((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e] = hi;
+              if (a.vcache) a.vcache[(((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e] = hi;
             }
           }
         }
@@ -341,8 +345,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
         __builtin_amdgcn_wave_barrier();   // the tile is rewritten for the next block
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         if (!ok) continue;
-        const int cd = n0 + wn * G::WN + j * 32 + c0 - seg * a.dim;   // first of 16 columns
-        const int e0 = cd & (a.head_dim - 1);                          // even: 8 whole pairs
+        const int cd = n0 + wn * G::WN + j * 32 + c0 - seg_base;   // first of 16 columns
+        const int e0 = cd & (a.head_dim - 1);                        // even: 8 whole pairs
         float rot[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -358,14 +362,14 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
         u32x4 hi0, lo0, hi1, lo1;
         pack8_pair(rot, hi0, lo0);
         pack8_pair(rot + 8, hi1, lo1);
-        const int64_t o = (int64_t)row * a.dim + cd;
+        const int64_t o = (int64_t)row * (seg == 0 ? a.dim : kvd) + cd;
         *(u32x4 *)(dh + o) = hi0;
         *(u32x4 *)(dh + o + 8) = hi1;
         *(u32x4 *)(dl + o) = lo0;
         *(u32x4 *)(dl + o + 8) = lo1;
         if (seg == 1 && a.kcache) {
           const int hh = cd >> hd_shift;
-          u16 *kp = a.kcache + (((int64_t)b * a.n_heads + hh) * a.max_seq + s) * a.head_dim + e0;
+          u16 *kp = a.kcache + (((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e0;
           *(u32x4 *)kp = hi0;
           *(u32x4 *)(kp + 8) = hi1;
         }

@@ -26,7 +26,8 @@ struct GemmArgs {
   const float *rstd;             // optional per-row scale applied to the accumulator
   int b_mode;
   const uint16_t *B0, *B1, *B2;  // weights [rows, K] bf16
-  int n_seg;                     // BMODE_CONCAT3: rows per segment
+  int n_seg;                     // BMODE_CONCAT3: rows of B0 (the query projection)
+  int n_seg_kv;                  // BMODE_CONCAT3: rows of B1 and of B2 (0: n_seg)
   // EPI_STORE / EPI_RESID / EPI_SILU outputs
   void *C;            // f32 or bf16 (EPI_SILU: bf16 hi)
   uint16_t *C_lo;     // EPI_SILU / EPI_STORE bf16: optional lo part
@@ -39,10 +40,21 @@ struct GemmArgs {
   uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, vt_stride] hi/lo of v (transposed)
   const float2 *rope_tab;        // [seq, head_dim/2] (cos, sin)
   int seq, n_heads, head_dim, dim;
+  int kv_dim, n_kv_heads;        // width and heads of k and v (0: dim, n_heads)
   int vt_stride;                 // row stride of the transposed v (>= seq, multiple of 64)
   uint16_t *kcache, *vcache;     // optional: [batch, n_heads, max_seq, head_dim] of this layer
   int max_seq;
 };
+
+// Row n of the BMODE_CONCAT3 operand [B0 (n_q rows); B1 (n_kv rows); B2 (n_kv rows)]:
+// the query, key and value projections stacked (fewer key/value rows under
+// grouped-query attention).
+__host__ __device__ inline const uint16_t *concat3_row(const uint16_t *B0, const uint16_t *B1, const uint16_t *B2,
+                                                       int n_q, int n_kv, int n, int64_t K) {
+  if (n < n_q) return B0 + (int64_t)n * K;
+  if (n < n_q + n_kv) return B1 + (int64_t)(n - n_q) * K;
+  return B2 + (int64_t)(n - n_q - n_kv) * K;
+}
 
 struct GemmKey {
   int bn, apair, epi;
@@ -62,6 +74,7 @@ struct AttnArgs {
   uint16_t *o_lo;                      // optional lo part (bf16 output only)
   int o_f32;
   int batch, seq, n_heads, head_dim, dim;
+  int kv_dim, n_kv_heads;              // k rows [batch*seq, kv_dim]; v^T [batch, n_kv_heads, head_dim, vt_stride]
   int vt_stride;                       // row stride of v^T (>= seq, multiple of 64)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
 };
@@ -108,7 +121,7 @@ struct GemvArgs {
   const uint16_t *A_hi, *A_lo;   // [M, K] bf16 pair
   int b_mode;
   const uint16_t *B0, *B1, *B2;
-  int n_seg;
+  int n_seg, n_seg_kv;           // BMODE_CONCAT3 row counts (n_seg_kv 0: n_seg)
   const uint16_t *packed;        // optional: the same matrix in 32-row tile order (see pack_tiles_launch)
   float *part;                   // [splits, M, N]
 };
@@ -119,7 +132,7 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
 // Tile-packed copy of B for the skinny GEMM, ordered for split-K chunks of
 // k_chunk (the chunk the skinny GEMM later runs with for this N and K).
 hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
-                             int N, int K, int k_chunk, uint16_t *dst, hipStream_t s);
+                             int n_seg_kv, int N, int K, int k_chunk, uint16_t *dst, hipStream_t s);
 int gemv_ntw(int N);               // 32-column tiles per wavefront used for N
 #ifndef GEMV_KC_MAX
 #define GEMV_KC_MAX 512
@@ -128,6 +141,7 @@ constexpr int kGemvMaxChunk = GEMV_KC_MAX; // largest K range of one workgroup
 
 struct DecodeArgs {
   int batch, dim, n_heads, head_dim, hidden, max_seq, vocab;
+  int n_kv_heads;                // key/value heads (query heads per group: n_heads / n_kv_heads)
   float eps;
   const int32_t *pos;            // [batch]
   const float2 *rope_tab;        // [batch, head_dim/2] for pos[b]

@@ -51,10 +51,19 @@ class Workload:
     vocab: int = 0
     max_seq: int = 0
     decode_pos: int = -1       # >= 0: a decode step at this position (cache holds 0..pos-1)
+    n_kv_heads: int = 0        # key/value heads (0: n_heads; fewer: grouped-query attention)
 
     @property
     def head_dim(self) -> int:
         return self.dim // self.n_heads
+
+    @property
+    def kv_heads(self) -> int:
+        return self.n_kv_heads or self.n_heads
+
+    @property
+    def kv_dim(self) -> int:
+        return self.kv_heads * self.head_dim
 
     @property
     def tokens(self) -> int:
@@ -93,6 +102,15 @@ TEST_WORKLOADS: Dict[int, Workload] = {
                   n_layers=2, vocab=300, max_seq=32),
     103: Workload(103, "test-block-bf16-hd64", dim=256, n_heads=4, hidden=768, batch=1, seq=129,
                   dtype="bf16"),
+    # grouped-query attention: 8 query heads on 2 key/value heads (head_dim 64), ragged seq
+    104: Workload(104, "test-block-bf16-gqa", dim=512, n_heads=8, hidden=1536, batch=2, seq=200, dtype="bf16",
+                  gain_std=0.1, n_kv_heads=2),
+    # grouped-query model, head_dim 128, groups of 4
+    105: Workload(105, "test-model-bf16-gqa", dim=1024, n_heads=8, hidden=2816, batch=3, seq=40, dtype="bf16",
+                  n_layers=2, vocab=1000, max_seq=64, gain_std=0.1, n_kv_heads=2),
+    # multi-query model (one key/value head), head_dim 128, groups of 4
+    106: Workload(106, "test-model-bf16-mqa", dim=512, n_heads=4, hidden=1536, batch=2, seq=24, dtype="bf16",
+                  n_layers=2, vocab=500, max_seq=48, n_kv_heads=1),
 }
 
 
@@ -144,8 +162,8 @@ def block_weights(w: Workload, layer: int = 0, device="cpu") -> Dict[str, torch.
     return {
         "attn_norm": gain(w, layer, T_ATTN_NORM, device),
         "wq": normal((d, d), wid, layer, T_WQ, std=WEIGHT_STD, dtype=dt, device=device),
-        "wk": normal((d, d), wid, layer, T_WK, std=WEIGHT_STD, dtype=dt, device=device),
-        "wv": normal((d, d), wid, layer, T_WV, std=WEIGHT_STD, dtype=dt, device=device),
+        "wk": normal((w.kv_dim, d), wid, layer, T_WK, std=WEIGHT_STD, dtype=dt, device=device),
+        "wv": normal((w.kv_dim, d), wid, layer, T_WV, std=WEIGHT_STD, dtype=dt, device=device),
         "wo": normal((d, d), wid, layer, T_WO, std=WEIGHT_STD, dtype=dt, device=device),
         "ffn_norm": gain(w, layer, T_FFN_NORM, device),
         "w_gate": normal((h, d), wid, layer, T_W_GATE, std=WEIGHT_STD, dtype=dt, device=device),
@@ -189,13 +207,13 @@ def kv_cache_layer(w: Workload, layer: int, filled: int, device="cpu",
     Positions [0, filled) hold N(0, 1) values (taken as already-rotated keys);
     the rest are zero. `batch_slice` returns only those sequences (the draw is
     still the full batch, so the bits match the full cache)."""
-    shape = (w.batch, w.n_heads, filled, w.head_dim)
+    shape = (w.batch, w.kv_heads, filled, w.head_dim)
     res = []
     for t in (T_K_CACHE, T_V_CACHE):
         full = normal(shape, w.wid, layer, t, dtype=w.torch_dtype, device=device)
         if batch_slice is not None:
             full = full[batch_slice]
-        c = torch.zeros((full.shape[0], w.n_heads, w.max_seq, w.head_dim), dtype=w.torch_dtype,
+        c = torch.zeros((full.shape[0], w.kv_heads, w.max_seq, w.head_dim), dtype=w.torch_dtype,
                         device=device)
         c[:, :, :filled] = full
         res.append(c)

@@ -46,8 +46,9 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 def config(dim: int, n_heads: int, hidden: int, *, dtype: torch.dtype = torch.bfloat16, n_layers: int = 1,
            vocab: int = 0, max_seq: int = 0, eps: float = 1e-6, theta: float = 10000.0,
-           numerics: int = L.NUM_DEFAULT) -> L.LlamaConfig:
-    return L.LlamaConfig(dim, n_heads, hidden, n_layers, vocab, max_seq, eps, theta, _DT[dtype], numerics)
+           numerics: int = L.NUM_DEFAULT, n_kv_heads: int = 0) -> L.LlamaConfig:
+    return L.LlamaConfig(dim, n_heads, hidden, n_layers, vocab, max_seq, eps, theta, _DT[dtype], numerics,
+                         n_kv_heads)
 
 
 def workspace_bytes(cfg: L.LlamaConfig, op: int, batch: int, seq: int) -> int:
@@ -205,7 +206,8 @@ class Model:
     def new_cache(self, batch: int, device) -> torch.Tensor:
         c = self.cfg
         hd = c.dim // c.n_heads
-        return torch.zeros((c.n_layers, batch, c.n_heads, c.max_seq, hd), dtype=_TORCH[c.dtype], device=device)
+        kv = c.n_kv_heads or c.n_heads
+        return torch.zeros((c.n_layers, batch, kv, c.max_seq, hd), dtype=_TORCH[c.dtype], device=device)
 
     def forward(self, tokens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor) -> torch.Tensor:
         _dev(tokens, k_cache, v_cache)

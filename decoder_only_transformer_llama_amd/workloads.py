@@ -25,7 +25,7 @@ def block_workload(wid: int, device="cuda", numerics: int = 0) -> BlockWorkload:
     wt = I.block_weights(w, device=device)
     x = I.block_input(w, device=device)
     cfg = ops.config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
-                     numerics=numerics)
+                     numerics=numerics, n_kv_heads=w.n_kv_heads)
     return BlockWorkload(w, wt, x, ops.Block(cfg, wt, w.batch, w.seq))
 
 
@@ -50,9 +50,9 @@ def decode_workload(wid: int, device="cuda", pack: bool = True) -> DecodeWorkloa
     layers = [I.block_weights(w, l, device=device) for l in range(w.n_layers)]
     gl = I.model_globals(w, device=device)
     cfg = ops.config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, n_layers=w.n_layers, vocab=w.vocab,
-                     max_seq=w.max_seq, eps=w.eps, theta=w.theta)
+                     max_seq=w.max_seq, eps=w.eps, theta=w.theta, n_kv_heads=w.n_kv_heads)
     m = ops.Model(cfg, layers, gl["tok_embeddings"], gl["final_norm"], gl["output"])
-    shape = (w.n_layers, w.batch, w.n_heads, w.max_seq, w.head_dim)
+    shape = (w.n_layers, w.batch, w.kv_heads, w.max_seq, w.head_dim)
     kc = torch.empty(shape, dtype=w.torch_dtype, device=device)
     vc = torch.empty(shape, dtype=w.torch_dtype, device=device)
     for l in range(w.n_layers):

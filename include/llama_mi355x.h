@@ -84,7 +84,7 @@ typedef enum {
 /* Model / block configuration. head_dim = dim / n_heads. */
 typedef struct llama_config {
   int32_t dim;        /* model width d */
-  int32_t n_heads;    /* attention heads (one K/V head per query head) */
+  int32_t n_heads;    /* query heads */
   int32_t hidden;     /* SwiGLU hidden width (llama_hidden_dim(dim, 256) for LLaMA) */
   int32_t n_layers;   /* blocks in the model (model entry points only) */
   int32_t vocab;      /* embedding rows / output-head width (model entry points only) */
@@ -93,11 +93,18 @@ typedef struct llama_config {
   float rope_theta;   /* RoPE base (10000 for LLaMA) */
   int32_t dtype;      /* llama_dtype of weights, gains, inputs and KV cache */
   uint32_t numerics;  /* LLAMA_NUM_* (bf16 path only; ignored for LLAMA_F32) */
+  int32_t n_kv_heads; /* key/value heads; 0 means n_heads (LLaMA-1: one K/V head per
+                       * query head). Fewer divide n_heads: grouped-query attention,
+                       * consecutive groups of n_heads / n_kv_heads query heads
+                       * sharing one K/V head ([P4] "GQA Was Not an Original LLaMA
+                       * Feature"). bf16 block/model entry points only; group size
+                       * 1, 2, 4 or 8; n_kv_heads * head_dim a multiple of 128. */
 } llama_config;
 
 /* Weights of one block, device pointers in config dtype ([P1] "The one
  * formula"; parameter set of [P1] "6.7B parameters ..."): two norm gains
- * [dim], wq/wk/wv/wo [dim, dim], w_gate/w_up [hidden, dim], w_down [dim, hidden]. */
+ * [dim], wq/wo [dim, dim], wk/wv [n_kv_heads * head_dim, dim] (= [dim, dim]
+ * for LLaMA), w_gate/w_up [hidden, dim], w_down [dim, hidden]. */
 typedef struct llama_block_weights {
   const void *attn_norm, *wq, *wk, *wv, *wo;
   const void *ffn_norm, *w_gate, *w_up, *w_down;

@@ -42,7 +42,7 @@ def test_header_compiles(lang, compiler, tmp_path):
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(L.LlamaConfig) == 40
+    assert ctypes.sizeof(L.LlamaConfig) == 44
     assert ctypes.sizeof(L.BlockWeights) == 9 * 8
     assert ctypes.sizeof(L.ModelWeights) == 5 * 8
 
@@ -59,7 +59,7 @@ def test_hidden_dim_and_status_strings():
 
 def _cfg(**kw):
     base = dict(dim=4096, n_heads=32, hidden=11008, n_layers=32, vocab=32000, max_seq=2048, norm_eps=1e-6,
-                rope_theta=1e4, dtype=L.LLAMA_BF16, numerics=0)
+                rope_theta=1e4, dtype=L.LLAMA_BF16, numerics=0, n_kv_heads=0)
     base.update(kw)
     return L.LlamaConfig(*[base[k] for k, _ in L.LlamaConfig._fields_])
 
@@ -133,3 +133,28 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.llama_pack_decode_weights(ctypes.byref(c), ctypes.byref(mw), FAKE, 16, None) == L.LLAMA_ERR_WORKSPACE
     assert lib.llama_pack_decode_weights(ctypes.byref(cf), ctypes.byref(mw), FAKE, 1 << 40, None) == \
         L.LLAMA_ERR_UNSUPPORTED
+
+
+def test_grouped_kv_heads_validation_and_sizes():
+    """n_kv_heads: 0 means n_heads; otherwise a divisor of n_heads with groups
+    of 1, 2, 4 or 8 query heads per key/value head (bf16 only), and a key/value
+    width that is a multiple of 128 columns."""
+    lib = L.load()
+    n = ctypes.c_size_t()
+
+    def ws(**kw):
+        return lib.llama_workspace_size(ctypes.byref(_cfg(**kw)), L.OP_BLOCK_FORWARD, 1, 64, ctypes.byref(n))
+
+    assert ws(n_kv_heads=8) == 0 and ws(n_kv_heads=32) == 0 and ws(n_kv_heads=16) == 0
+    assert ws(n_kv_heads=-1) == L.LLAMA_ERR_SHAPE
+    assert ws(n_kv_heads=5) == L.LLAMA_ERR_SHAPE            # not a divisor of 32
+    assert ws(n_kv_heads=64) == L.LLAMA_ERR_SHAPE           # more key/value heads than query heads
+    assert ws(n_kv_heads=2) == L.LLAMA_ERR_UNSUPPORTED      # groups of 16
+    assert ws(n_kv_heads=8, dtype=L.LLAMA_F32) == L.LLAMA_ERR_UNSUPPORTED
+    assert ws(dim=512, n_heads=8, hidden=1536, n_kv_heads=1) == L.LLAMA_ERR_UNSUPPORTED   # width 64
+    assert ws(dim=512, n_heads=8, hidden=1536, n_kv_heads=2) == 0                         # width 128
+    # fewer key/value heads shrink the packed decode weights by exactly the Wk, Wv rows
+    for nkv in (32, 8):
+        assert lib.llama_decode_pack_size(ctypes.byref(_cfg(n_kv_heads=nkv)), ctypes.byref(n)) == 0
+        kvd = nkv * 128
+        assert n.value == (32 * ((2 * 4096 + 2 * kvd) * 4096 + 3 * 4096 * 11008) + 32000 * 4096) * 2

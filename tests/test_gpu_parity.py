@@ -20,6 +20,11 @@ pytestmark = pytest.mark.gpu
 
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
+# Every GEMM operand carried as a bf16 hi/lo pair; the attention
+# probabilities stay single bf16 values, so the statistic shrinks (2-3x on a
+# block, 2-3x on two-layer logits) but does not vanish.
+ALL_PAIRS = (L.NUM_EXPLICIT | L.NUM_QKV_A_PAIR | L.NUM_QK_PAIR | L.NUM_V_PAIR | L.NUM_O_A_PAIR
+             | L.NUM_FFN_A_PAIR | L.NUM_DOWN_A_PAIR)
 
 
 def ops():
@@ -162,7 +167,7 @@ def run_block(wid, numerics=L.NUM_DEFAULT, seq_slice=None):
     wt = I.block_weights(w, device="cuda")
     x = I.block_input(w, device="cuda")
     cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
-                       numerics=numerics)
+                       numerics=numerics, n_kv_heads=w.n_kv_heads)
     blk = ops().Block(cfg, wt, w.batch, w.seq)
     y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
     blk(x, y)
@@ -178,12 +183,23 @@ def run_block(wid, numerics=L.NUM_DEFAULT, seq_slice=None):
     return y[rows], want, w
 
 
-@pytest.mark.parametrize("wid", [0, 100, 103])
+@pytest.mark.parametrize("wid", [0, 100, 103, 104])
 def test_block_small(wid):
     y, want, w = run_block(wid)
     err = rel_err(y, want)
     print(f"block {w.name}: max|d|/rms = {err:.3e}")
     assert err < tol_of(w)
+
+
+@pytest.mark.parametrize("wid", [100, 103, 104])
+def test_block_all_pairs(wid):
+    """Within the bound, and closer than the default operand set: an operand
+    whose low half were dropped would leave the two errors equal."""
+    y, want, w = run_block(wid, numerics=ALL_PAIRS)
+    err = rel_err(y, want)
+    err_def = rel_err(*run_block(wid)[:2])
+    print(f"block {w.name}: max|d|/rms = {err:.3e} all operands as pairs, {err_def:.3e} default")
+    assert err < TOL_BF16 and err < 0.8 * err_def
 
 
 def test_block_deterministic():
@@ -215,18 +231,31 @@ def test_block_13b_65b_sampled_sequence(wid, b):
 
 
 # ---------------------------------------------------------------- model prefill + decode
-def small_model(wid=101):
+def small_model(wid=101, numerics=L.NUM_DEFAULT, n_kv_heads=None, layers=None):
     w = I.workload(wid)
-    layers = [I.block_weights(w, l, device="cuda") for l in range(w.n_layers)]
+    layers = layers or [I.block_weights(w, l, device="cuda") for l in range(w.n_layers)]
     gl = I.model_globals(w, device="cuda")
     cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, n_layers=w.n_layers, vocab=w.vocab,
-                       max_seq=w.max_seq, eps=w.eps, theta=w.theta)
+                       max_seq=w.max_seq, eps=w.eps, theta=w.theta, numerics=numerics,
+                       n_kv_heads=w.n_kv_heads if n_kv_heads is None else n_kv_heads)
     m = ops().Model(cfg, layers, gl["tok_embeddings"], gl["final_norm"], gl["output"])
     return w, m, layers, gl
 
 
-def test_model_prefill_then_decode():
-    w, m, layers, gl = small_model()
+def oracle_caches(w, B):
+    """Zeroed fp64 caches [B, key/value heads, max_seq, head_dim] per layer."""
+    shape = (B, w.kv_heads, w.max_seq, w.head_dim)
+    return [(np.zeros(shape), np.zeros(shape)) for _ in range(w.n_layers)]
+
+
+# 101: multi-head; 105: grouped-query (4 query heads per key/value head); 106:
+# multi-query. 105 (width 1024) runs with every GEMM operand as a pair: at the
+# default operand set its two-layer logits reach 2.1e-2, all of it from the
+# bf16 rounding points (its grouped path is bitwise the multi-head path, see
+# test_grouped_kv_equals_multi_head_with_repeated_kv).
+@pytest.mark.parametrize("wid,numerics", [(101, L.NUM_DEFAULT), (105, ALL_PAIRS), (106, L.NUM_DEFAULT)])
+def test_model_prefill_then_decode(wid, numerics):
+    w, m, layers, gl = small_model(wid, numerics=numerics)
     B, T = w.batch, w.seq
     toks = I.tokens(w, (B, T + 1), device="cuda")
     kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
@@ -235,10 +264,8 @@ def test_model_prefill_then_decode():
     dec = m.decode(toks[:, T].contiguous(), pos, kc, vc)
     torch.cuda.synchronize()
 
-    hd = w.head_dim
     lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
-    caches = [(np.zeros((B, w.n_heads, w.max_seq, hd)), np.zeros((B, w.n_heads, w.max_seq, hd)))
-              for _ in range(w.n_layers)]
+    caches = oracle_caches(w, B)
     get = lambda l: (lw[l], caches[l][0], caches[l][1])
     emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
     want = O.model_forward(toks[:, :T].cpu().numpy(), emb, get, w.n_layers, fn, out, w.n_heads, w.eps)
@@ -252,14 +279,72 @@ def test_model_prefill_then_decode():
     want_dec = O.model_decode(toks[:, T].cpu().numpy(), np.full(B, T), emb, get, w.n_layers, fn, out, w.n_heads,
                               w.eps)
     e2 = rel_err(dec, want_dec)
-    print(f"prefill logits {e1:.3e}, decode logits {e2:.3e}")
+    print(f"{w.name}: prefill logits {e1:.3e}, decode logits {e2:.3e}")
     assert e1 < TOL_BF16 and e2 < TOL_BF16
 
 
-def test_decode_packed_weights_bitwise_equal():
+@pytest.mark.parametrize("wid", [101, 105, 106])
+def test_model_prefill_all_pairs(wid):
+    w, m, layers, gl = small_model(wid, numerics=ALL_PAIRS)
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    logits = m.forward(toks[:, :T].contiguous(), kc, vc)
+    torch.cuda.synchronize()
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    caches = oracle_caches(w, B)
+    want = O.model_forward(toks[:, :T].cpu().numpy(), host(gl["tok_embeddings"]),
+                           lambda l: (lw[l], caches[l][0], caches[l][1]), w.n_layers, host(gl["final_norm"]),
+                           host(gl["output"]), w.n_heads, w.eps)
+    err = rel_err(logits, want)
+    _, md, _, _ = small_model(wid, layers=layers)
+    err_def = rel_err(md.forward(toks[:, :T].contiguous(), m.new_cache(B, "cuda"), m.new_cache(B, "cuda")), want)
+    print(f"{w.name}: prefill logits {err:.3e} all operands as pairs, {err_def:.3e} default")
+    assert err < TOL_BF16 and err < 0.8 * err_def
+
+
+@pytest.mark.parametrize("wid", [105, 106])
+def test_grouped_kv_equals_multi_head_with_repeated_kv(wid):
+    """Grouped key/value heads compute exactly multi-head attention whose K/V
+    projections repeat each shared head's rows for its group of query heads.
+    The per-column products of the Q/K/V projection and the per-head
+    attention do not depend on the number of key/value heads, so prefill
+    logits and the shared cache entries are bitwise equal. Decode's split-K
+    reduction order depends on the projection width: its fp32 differences can
+    flip a bf16 rounding (cache entries, operands), one 2^-9 step on one
+    element, hence the 1e-3 bound."""
+    w = I.workload(wid)
+    G, hd = w.n_heads // w.kv_heads, w.head_dim
+    layers = [I.block_weights(w, l, device="cuda") for l in range(w.n_layers)]
+    rep = lambda t: t.reshape(w.kv_heads, 1, hd, w.dim).expand(-1, G, -1, -1).reshape(w.dim, w.dim).contiguous()
+    mha_layers = [dict(lay, wk=rep(lay["wk"]), wv=rep(lay["wv"])) for lay in layers]
+    _, mg, _, _ = small_model(wid, layers=layers)
+    _, mm, _, _ = small_model(wid, n_kv_heads=0, layers=mha_layers)
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kg, vg = mg.new_cache(B, "cuda"), mg.new_cache(B, "cuda")
+    km, vm = mm.new_cache(B, "cuda"), mm.new_cache(B, "cuda")
+    lg = mg.forward(toks[:, :T].contiguous(), kg, vg).clone()
+    lm = mm.forward(toks[:, :T].contiguous(), km, vm).clone()
+    pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    dg = mg.decode(toks[:, T].contiguous(), pos, kg, vg).clone()
+    dm = mm.decode(toks[:, T].contiguous(), pos, km, vm).clone()
+    torch.cuda.synchronize()
+    assert kg.shape[2] == w.kv_heads and km.shape[2] == w.n_heads
+    assert torch.equal(lg, lm)
+    # query head h*G+j of the multi-head cache holds shared head h
+    for j in range(G):
+        assert torch.equal(km[:, :, j::G, :T], kg[:, :, :, :T]) and torch.equal(vm[:, :, j::G, :T], vg[:, :, :, :T])
+    e = rel_err(dg, O.f64(dm.cpu()))
+    print(f"{w.name}: prefill bitwise equal, decode max|d|/rms = {e:.2e}")
+    assert e < 1e-3
+
+
+@pytest.mark.parametrize("wid", [101, 105])
+def test_decode_packed_weights_bitwise_equal(wid):
     """The tile-ordered weight pack feeds the same products in the same order:
     decode logits and cache writes are bitwise identical with and without it."""
-    w, m, layers, gl = small_model()
+    w, m, layers, gl = small_model(wid)
     B = w.batch
     toks = I.tokens(w, (B,), device="cuda")
     pos = torch.tensor([5, 17, 0][:B], dtype=torch.int32, device="cuda")
@@ -326,13 +411,14 @@ def test_argmax(rows, vocab):
 
 
 @pytest.mark.gpu
-def test_greedy_generation():
+@pytest.mark.parametrize("wid", [101, 105])
+def test_greedy_generation(wid):
     """Greedy generation on the GPU: every token is the exact first-index
     argmax of the GPU's own logits for that step; those logits match the
     oracle fed the same tokens within the bf16 bound; and each chosen token
     is a maximum of the oracle's logits up to that bound (several tokens can
     be correct when their logits are within rounding of each other)."""
-    w, m, layers, gl = small_model()
+    w, m, layers, gl = small_model(wid)
     B, T, n_new = w.batch, 8, 6
     prompt = I.tokens(w, (B, T), device="cuda")
     kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
@@ -347,10 +433,8 @@ def test_greedy_generation():
     gpu_logits = torch.stack(steps).cpu()                        # [n_new, B, vocab]
     assert torch.equal(toks.cpu().T.long(), torch.argmax(gpu_logits, dim=-1))
 
-    hd = w.head_dim
     lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
-    caches = [(np.zeros((B, w.n_heads, w.max_seq, hd)), np.zeros((B, w.n_heads, w.max_seq, hd)))
-              for _ in range(w.n_layers)]
+    caches = oracle_caches(w, B)
     emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
     forced = toks.cpu().numpy()
     _, want = O.greedy_generate(prompt.cpu().numpy(), n_new, emb, lambda l: (lw[l], *caches[l]), w.n_layers, fn,
