@@ -94,11 +94,11 @@ def block_flops(w) -> dict:
 
 
 def decode_bytes(w) -> dict:
-    d, h, L, B, V, P = w.dim, w.hidden, w.n_layers, w.batch, w.vocab, w.decode_pos
+    d, h, L, B, V, P, kvd = w.dim, w.hidden, w.n_layers, w.batch, w.vocab, w.decode_pos, w.kv_dim
     return {
-        "weights": L * (4 * d * d + 3 * d * h) * 2 + V * d * 2,
-        "kv_read": L * B * P * d * 2 * 2,
-        "kv_write": L * B * d * 2 * 2,
+        "weights": L * ((2 * d + 2 * kvd) * d + 3 * d * h) * 2 + V * d * 2,
+        "kv_read": L * B * P * kvd * 2 * 2,
+        "kv_write": L * B * kvd * 2 * 2,
         "embed_logits": B * d * 2 + B * V * 4,
     }
 
@@ -220,11 +220,11 @@ def bench_other_blocks(args, torch):
     return out
 
 
-def bench_decode(args, torch):
+def bench_decode(args, torch, wid: int = 4, with_model_prefill: bool = True):
     from decoder_only_transformer_llama_amd import _lib
     from decoder_only_transformer_llama_amd.workloads import decode_workload
 
-    wl = decode_workload(4, "cuda")
+    wl = decode_workload(wid, "cuda")
     w = wl.w
     m = wl.model
     logits = torch.empty((w.batch, w.vocab), dtype=torch.float32, device="cuda")
@@ -281,7 +281,7 @@ def bench_decode(args, torch):
     att_bytes_launch = by["kv_read"] / L
     att_ms = agg["attention"] / L
     achieved = att_bytes_launch / (att_ms * 1e-3) / 1e9
-    model_prefill = None if args.no_model_prefill else bench_model_prefill(args, torch, wl)
+    model_prefill = None if (args.no_model_prefill or not with_model_prefill) else bench_model_prefill(args, torch, wl)
     return {
         "w": w, "ms": ms, "ms_eager": ms_eager, "graph": graph is not None, "model_prefill": model_prefill,
         "tokens_per_s": w.batch / (ms * 1e-3),
@@ -362,6 +362,7 @@ def main() -> int:
     ap.add_argument("--raw-trace", action="store_true", help="print every traced prefill kernel's time")
     ap.add_argument("--no-model-prefill", action="store_true", help="skip the whole-model prefill leg")
     ap.add_argument("--no-other-blocks", action="store_true", help="skip the 13B/65B-shape block legs")
+    ap.add_argument("--no-gqa-decode", action="store_true", help="skip the grouped-query decode leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM byte counters")
     args = ap.parse_args()
@@ -381,6 +382,11 @@ def main() -> int:
               f"{dec['hbm_gbs']:.0f} GB/s; kernels {json.dumps(dec['per_kernel_ms'])}", file=sys.stderr, flush=True)
         if dec["model_prefill"]:
             print(f"# model prefill: {json.dumps(dec['model_prefill'])}", file=sys.stderr, flush=True)
+        if not args.no_gqa_decode:
+            torch.cuda.empty_cache()
+            g = bench_decode(args, torch, wid=5, with_model_prefill=False)
+            print(f"# gqa decode: {g['ms']:.3f} ms/step, {g['tokens_per_s']:.0f} tok/s, {g['hbm_gbs']:.0f} GB/s; "
+                  f"kernels {json.dumps(g['per_kernel_ms'])}", file=sys.stderr, flush=True)
         return 0
     pf = bench_prefill(args, torch)
     print(f"# prefill: {pf['ms']:.3f} ms/step, {pf['tokens_per_s']:.0f} tok/s, block {pf['block_tflops']:.1f} "
@@ -396,6 +402,17 @@ def main() -> int:
               f"{dec['hbm_gbs']:.0f} GB/s; kernels {json.dumps(dec['per_kernel_ms'])}", file=sys.stderr, flush=True)
         if dec["model_prefill"]:
             print(f"# model prefill: {json.dumps(dec['model_prefill'])}", file=sys.stderr, flush=True)
+        torch.cuda.empty_cache()
+    gqa = None
+    if not args.prefill_only and not args.no_gqa_decode:
+        g = bench_decode(args, torch, wid=5, with_model_prefill=False)
+        gqa = {"workload": "llama-7b-shape model decode step with 8 key/value heads (groups of 4), batch 32, "
+                           "KV cache 2047 positions, bf16",
+               "tokens_per_s": round(g["tokens_per_s"], 1), "ms_per_step": round(g["ms"], 4),
+               "hbm_gbs": round(g["hbm_gbs"], 1), "hbm_frac": round(g["hbm_gbs"] / PEAK_HBM_GBS, 4),
+               "bytes_per_step": g["bytes"], "attention_gbs": g["roofline"]["achieved"],
+               "kernels_ms": g["per_kernel_ms"]}
+        print(f"# gqa decode: {json.dumps(gqa)}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pf["block"], torch)
     w = pf["w"]
     line = {
@@ -432,6 +449,8 @@ def main() -> int:
         }
         if dec["model_prefill"] is not None:
             line["model_prefill"] = dec["model_prefill"]
+    if gqa is not None:
+        line["decode_gqa"] = gqa
     line["wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(line), flush=True)
     return 0

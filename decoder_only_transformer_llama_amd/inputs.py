@@ -89,6 +89,9 @@ WORKLOADS: Dict[int, Workload] = {
     # LLaMA-7B-shape full-model decode step, batch 32, cache of 2047 positions
     4: Workload(4, "7b-model-decode-b32-kv2047", dim=4096, n_heads=32, hidden=11008, batch=32, seq=1,
                 dtype="bf16", n_layers=32, vocab=32000, max_seq=2048, decode_pos=2047),
+    # the same model with grouped-query attention: 8 key/value heads (groups of 4)
+    5: Workload(5, "7b-gqa8-model-decode-b32-kv2047", dim=4096, n_heads=32, hidden=11008, batch=32, seq=1,
+                dtype="bf16", n_layers=32, vocab=32000, max_seq=2048, decode_pos=2047, n_kv_heads=8),
 }
 
 # Small workloads used only by tests (same recipes, shapes that run in seconds

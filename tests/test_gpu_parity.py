@@ -373,18 +373,22 @@ def test_decode_invalid_position_gives_nan_row():
 
 
 @pytest.mark.slow
-def test_model_decode_7b_sampled_sequences():
-    """Full 7B-shape decode step (batch 32, cache of 2047 positions); the oracle
-    recomputes two of the 32 sequences layer by layer."""
+@pytest.mark.parametrize("wid", [4, 5])
+def test_model_decode_7b_sampled_sequences(wid):
+    """Full 7B-shape decode step (batch 32, cache of 2047 positions; 5: eight
+    key/value heads); the oracle recomputes two of the 32 sequences layer by
+    layer."""
     from decoder_only_transformer_llama_amd.workloads import decode_workload
     from tests.oracle_runs import oracle_decode_rows
-    wl = decode_workload(4, "cuda")
+    wl = decode_workload(wid, "cuda")
     logits = wl.model.decode(wl.tokens, wl.pos, wl.k_cache, wl.v_cache)
     torch.cuda.synchronize()
     rows = [0, 17]
     want = oracle_decode_rows(wl, rows)
     err = rel_err(logits[rows], want)
-    print(f"7b decode logits (rows {rows}): max|d|/rms = {err:.3e}")
+    print(f"{wl.w.name} decode logits (rows {rows}): max|d|/rms = {err:.3e}")
+    del wl
+    torch.cuda.empty_cache()
     assert err < TOL_BF16
 
 
