@@ -254,6 +254,7 @@ struct DecodeWs {
   float *x, *h, *rstd, *part;
   uint16_t *ag_hi, *ag_lo;
   float2 *rope_tab;
+  float *attn_part;   // key-range softmax states of the decode attention
 };
 
 constexpr int kDecMaxSeq = 2048;   // longest cache the decode path is validated for
@@ -294,6 +295,7 @@ DecodeWs carve_decode(Carve &cv, const llama_config *c, int batch) {
   w.ag_hi = cv.take<uint16_t>((size_t)batch * wmax);
   w.ag_lo = cv.take<uint16_t>((size_t)batch * wmax);
   w.rope_tab = cv.take<float2>((size_t)batch * hd / 2);
+  w.attn_part = cv.take<float>((size_t)batch * c->n_heads * kDecAttnMaxRanges * (hd + 2));
   return w;
 }
 
@@ -896,7 +898,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
     const uint16_t *lp = pack ? pack + (size_t)l * pl.layer : nullptr;
     packed_mat = lp ? lp + pl.qkv : nullptr;
     HIP_TRY(gemv(d + 2 * kv_dim(c), d, BMODE_CONCAT3, L.wq, L.wk, L.wv, sp), "qkv projection");
-    HIP_TRY(dec_attn_launch(da, dw.part, sp, dw.rstd, kc, vc, dw.ag_hi, dw.ag_lo, s), "attention");
+    HIP_TRY(dec_attn_launch(da, dw.part, sp, dw.rstd, kc, vc, dw.ag_hi, dw.ag_lo, dw.attn_part, s), "attention");
     packed_mat = lp ? lp + pl.o : nullptr;
     HIP_TRY(gemv(d, d, BMODE_PLAIN, L.wo, nullptr, nullptr, sp), "output projection");
     HIP_TRY(dec_resid_norm_launch(da, dw.x, dw.part, sp, (const uint16_t *)L.ffn_norm, dw.h, dw.rstd, dw.ag_hi,

@@ -425,19 +425,27 @@ hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int s
 }
 
 // ------------------------------------------------------------------ cache attention
-// One workgroup per (head, sequence), fused with the Q/K/V split-K finish:
+// One workgroup per (key/value head, sequence, key range), fused with the
+// Q/K/V split-K finish:
 //  1. q, k, v of the new token for this head: rstd * (sum of the projection
 //     partials in split order), RoPE on q and k at pos[b]; k and v (bf16) go to
-//     cache slot pos[b] and stay in LDS for the new key's own term;
-//  2. one pass over the cached keys 0..pos-1 and their values: a lane group of
+//     cache slot pos[b] (written by the first key range only) and stay in LDS
+//     for the new key's own term;
+//  2. one pass over the range's share of the cached keys 0..pos-1 (NS equal
+//     ranges, multiples of one step) and their values: a lane group of
 //     HD/8 lanes owns one key per instruction (4 keys per wavefront
 //     instruction, UNR instructions per step), keeps a running max, sum and
 //     weighted value sum in fp32 (online softmax, exp2 with log2(e)/sqrt(hd)
 //     folded into q); keys and values of the next step are in flight while
 //     one step is processed;
-//  3. the 16 lane groups' partial softmax states and the new key's term are
-//     merged in a fixed order and the normalised head output is written as
-//     the bf16 hi/lo pair the Wo projection consumes.
+//  3. the lane groups' partial softmax states and (first range only) the new
+//     key's term are merged in a fixed order. With one range the normalised
+//     head output is written as the bf16 hi/lo pair the Wo projection
+//     consumes; with NS ranges each writes (max, sum, unnormalised output) and
+//     dec_attn_combine_kernel merges the NS states in range order.
+// Splitting the keys gives NS times more workgroups: grouped heads leave only
+// n_kv_heads * batch (key/value head, sequence) pairs, too few to keep enough
+// loads in flight on 256 compute units.
 // An invalid position writes nothing to the cache and yields NaN outputs.
 // Sum over aligned groups of G lanes (G = 2..16), every lane getting its
 // group's total, with DPP lane moves inside each 16-lane row: swap
@@ -458,10 +466,10 @@ DEV float lane_group_sum(float v) {
 
 constexpr int kMaxSeq = 2048;   // longest decode cache (positions) the attention kernel unrolls for
 
-template <int HD, int G>
+template <int HD, int G, int NS>
 __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
                                                        const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
-                                                       u16 *a_lo) {
+                                                       u16 *a_lo, float *opart) {
   constexpr int LPK = HD / 8;          // lanes per key
   constexpr int KPW = 64 / LPK;        // keys per wavefront instruction
 #ifndef DEC_ATTN_UNROLL
@@ -475,7 +483,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   __shared__ float sq[G][HD], sknew[HD], svnew[HD];
   __shared__ float gm[NG][G], gl[NG][G], snew[G];
   __shared__ float osum[NG][G][HD];
-  const int hk = blockIdx.x, b = blockIdx.y;
+  const int hk = blockIdx.x, b = blockIdx.y, rs = NS > 1 ? (int)blockIdx.z : 0;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int p = d.pos[b];
   const bool ok = pos_ok(p, d.max_seq);
@@ -503,12 +511,17 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
         // the cache holds bf16: the new key/value enter attention as stored
         const u16 xb = f2bf(x);
         (gq == G ? sknew : svnew)[e] = bf2f(xb);
-        if (ok) (gq == G ? kc : vc)[cbase + (int64_t)p * HD + e] = xb;
+        if (ok && rs == 0) (gq == G ? kc : vc)[cbase + (int64_t)p * HD + e] = xb;
       }
     }
   }
   __syncthreads();
-  const int nk = ok ? p : 0;    // cached keys 0..p-1; key p is the new one
+  // cached keys 0..p-1 (key p is the new one); this range covers keys
+  // k0 .. k0+nk-1, a multiple of KPS long except at the end
+  const int nk_all = ok ? p : 0;
+  const int chunk = NS == 1 ? nk_all : ((nk_all + NS - 1) / NS + KPS - 1) / KPS * KPS;
+  const int k0 = min(rs * chunk, nk_all);
+  const int nk = min(k0 + chunk, nk_all) - k0;
   if (w == 0) {                 // the new key's scores (log2 domain)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -541,7 +554,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   auto load = [&](u32x4 (&kr)[UNR], u32x4 (&vr)[UNR], int st) {
 #pragma unroll
     for (int u = 0; u < UNR; ++u) {
-      const int key = max(min(st * KPS + kbase + u * KPW, nk - 1), 0);
+      const int key = k0 + max(min(st * KPS + kbase + u * KPW, nk - 1), 0);
       const int64_t o = cbase + (int64_t)key * HD + d8 * 8;
       kr[u] = *(const u32x4 *)(kc + o);
       vr[u] = *(const u32x4 *)(vc + o);
@@ -590,7 +603,8 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   // skipped (a uniform branch around arithmetic only) and their loads re-read
   // one valid row. The fences keep each refill right behind the step that
   // frees its registers.
-  constexpr int MAXSTEPS = (kMaxSeq + KPS - 1) / KPS;
+  // a range holds at most ceil(kMaxSeq / NS) keys rounded up to a step
+  constexpr int MAXSTEPS = ((kMaxSeq + NS - 1) / NS + KPS - 1) / KPS;
   const int last = max(nsteps - 1, 0);
   u32x4 kb[2][UNR], vb[2][UNR];
   load(kb[0], vb[0], 0);
@@ -616,39 +630,117 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   __syncthreads();
 
   // ---- 3. per query head: merge the lane groups and the new key (fixed
-  // order), normalise, write the bf16 hi/lo pair the Wo projection consumes
+  // order); one range: normalise and write the bf16 hi/lo pair the Wo
+  // projection consumes; several: store this range's softmax state
   for (int c = tid; c < G * HD; c += 256) {
     const int g = c / HD, e = c % HD;
-    float M = snew[g];
+    const float sn = rs == 0 ? snew[g] : -INFINITY;   // the new key belongs to the first range
+    float M = sn;
     for (int gi = 0; gi < NG; ++gi) M = fmaxf(M, gm[gi][g]);
-    const float pn = exp2f(snew[g] - M);
+    const float Mu = M == -INFINITY ? 0.f : M;        // a later range may see no key at all
+    const float pn = exp2f(sn - Mu);
     float L = pn, o = pn * svnew[e];
     for (int gi = 0; gi < NG; ++gi) {
-      const float f = exp2f(gm[gi][g] - M);   // 0 for a group that saw no key
+      const float f = exp2f(gm[gi][g] - Mu);   // 0 for a group that saw no key
       L += f * gl[gi][g];
       o += f * osum[gi][g][e];
     }
-    const float v = ok ? o / L : __builtin_nanf("");
-    u16 hi, lo;
-    split_pair(v, hi, lo);
-    const int64_t oo = (int64_t)b * d.dim + (hk * G + g) * HD + e;
-    a_hi[oo] = hi;
-    a_lo[oo] = lo;
+    if (NS == 1) {
+      const float v = ok ? o / L : __builtin_nanf("");
+      u16 hi, lo;
+      split_pair(v, hi, lo);
+      const int64_t oo = (int64_t)b * d.dim + (hk * G + g) * HD + e;
+      a_hi[oo] = hi;
+      a_lo[oo] = lo;
+    } else {
+      float *st = opart + (((int64_t)b * d.n_heads + hk * G + g) * NS + rs) * (HD + 2);
+      st[2 + e] = o;
+      if (e == 0) {
+        st[0] = M;
+        st[1] = L;
+      }
+    }
   }
 }
 
+// Merge the NS key-range states of each (sequence, query head) in range
+// order; one thread per output channel.
+__global__ void dec_attn_combine_kernel(const DecodeArgs d, const float *opart, int ns, u16 *a_hi, u16 *a_lo) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= d.batch * d.dim) return;
+  const int HD = d.head_dim, b = idx / d.dim, c = idx - b * d.dim, h = c / HD, e = c - h * HD;
+  const float *st = opart + ((int64_t)b * d.n_heads + h) * ns * (HD + 2);
+  float M = -INFINITY;
+  for (int r = 0; r < ns; ++r) M = fmaxf(M, st[r * (HD + 2)]);
+  float L = 0.f, o = 0.f;
+  for (int r = 0; r < ns; ++r) {
+    const float f = exp2f(st[r * (HD + 2)] - M);   // 0 for a range that saw no key
+    L += f * st[r * (HD + 2) + 1];
+    o += f * st[r * (HD + 2) + 2 + e];
+  }
+  const float v = pos_ok(d.pos[b], d.max_seq) ? o / L : __builtin_nanf("");
+  u16 hi, lo;
+  split_pair(v, hi, lo);
+  a_hi[idx] = hi;
+  a_lo[idx] = lo;
+}
+
+// Key ranges per (key/value head, sequence): at least 512 workgroups (two per
+// compute unit). Measured on the 7B-shape decode step (batch 32, 2047 cached
+// positions): 8 key/value heads (256 pairs) take 2.79 / 2.22 / 2.39 / 2.48 ms
+// per step of attention with 1 / 2 / 4 / 8 ranges; 32 heads (1024 pairs) are
+// fastest unsplit (5.94 ms against 6.15 with 2 ranges).
+int dec_attn_ranges(const DecodeArgs &d) {
+#ifdef DEC_ATTN_SPLITS
+  return DEC_ATTN_SPLITS;
+#else
+  int ns = 1;
+  while (ns < kDecAttnMaxRanges && d.n_kv_heads * d.batch * ns < 512) ns *= 2;
+  return ns;
+#endif
+}
+
+template <int HD, int G>
+hipError_t dec_attn_launch_g(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
+                             uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, int ns, hipStream_t s) {
+  dim3 grid(d.n_kv_heads, d.batch, ns);
+  switch (ns) {
+    case 1:
+      hipLaunchKernelGGL((dec_attn_kernel<HD, G, 1>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi,
+                         a_lo, opart);
+      return hipGetLastError();
+    case 2:
+      hipLaunchKernelGGL((dec_attn_kernel<HD, G, 2>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi,
+                         a_lo, opart);
+      break;
+    case 4:
+      hipLaunchKernelGGL((dec_attn_kernel<HD, G, 4>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi,
+                         a_lo, opart);
+      break;
+    case 8:
+      hipLaunchKernelGGL((dec_attn_kernel<HD, G, 8>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi,
+                         a_lo, opart);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = d.batch * d.dim;
+  hipLaunchKernelGGL(dec_attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d, opart, ns, a_hi, a_lo);
+  return hipGetLastError();
+}
+
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
-                           uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s) {
+                           uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, hipStream_t s) {
   if (d.max_seq > kMaxSeq) return hipErrorInvalidValue;
   if (d.n_kv_heads <= 0 || d.n_heads % d.n_kv_heads) return hipErrorInvalidValue;
   const int group = d.n_heads / d.n_kv_heads;
-  dim3 grid(d.n_kv_heads, d.batch);
-#define DEC_ATTN_CASE(HD_, G_)                                                                              \
-  if (d.head_dim == HD_ && group == G_) {                                                                  \
-    hipLaunchKernelGGL((dec_attn_kernel<HD_, G_>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi, \
-                       a_lo);                                                                              \
-    return hipGetLastError();                                                                              \
-  }
+  const int ns = dec_attn_ranges(d);
+  if (ns > 1 && !opart) return hipErrorInvalidValue;
+#define DEC_ATTN_CASE(HD_, G_)                                                                         \
+  if (d.head_dim == HD_ && group == G_)                                                               \
+    return dec_attn_launch_g<HD_, G_>(d, part, splits, ss, kc, vc, a_hi, a_lo, opart, ns, s);
   DEC_ATTN_CASE(128, 1)
   DEC_ATTN_CASE(128, 2)
   DEC_ATTN_CASE(128, 4)

@@ -154,8 +154,12 @@ hipError_t dec_embed_norm_launch(const DecodeArgs &d, const uint16_t *emb, const
 // Attention of one new token per sequence over the KV cache, fused with the
 // finish of the Q/K/V split-K partials (rstd, RoPE, cache append at pos[b]);
 // writes the head outputs as a bf16 pair [batch, dim]. max_seq <= 2048.
+// opart: [batch, n_heads, kDecAttnMaxRanges, head_dim + 2] fp32 states of the
+// key ranges (dec_attn_ranges(d) of them; unused with one range).
+constexpr int kDecAttnMaxRanges = 8;
+int dec_attn_ranges(const DecodeArgs &d);
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
-                           uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, hipStream_t s);
+                           uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, hipStream_t s);
 // out = res + sum(part); ss of out; out*g as pair
 hipError_t dec_resid_norm_launch(const DecodeArgs &d, const float *res, const float *part, int splits,
                                  const uint16_t *g, float *out, float *ss, uint16_t *og_hi,
