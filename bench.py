@@ -152,7 +152,7 @@ def bench_prefill(args, torch):
     from decoder_only_transformer_llama_amd import _lib, inputs as I
     from decoder_only_transformer_llama_amd.workloads import block_workload
 
-    bw = block_workload(1, "cuda")
+    bw = block_workload(1, "cuda", numerics=args.numerics)
     w = bw.w
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(args.warmup):
@@ -363,6 +363,8 @@ def main() -> int:
     ap.add_argument("--no-model-prefill", action="store_true", help="skip the whole-model prefill leg")
     ap.add_argument("--no-other-blocks", action="store_true", help="skip the 13B/65B-shape block legs")
     ap.add_argument("--no-gqa-decode", action="store_true", help="skip the grouped-query decode leg")
+    ap.add_argument("--numerics", type=lambda v: int(v, 0), default=0,
+                    help="prefill operand-precision bits (llama_config.numerics; 0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run the plain copy used to scale HBM byte counters")
     args = ap.parse_args()

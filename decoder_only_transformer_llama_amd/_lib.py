@@ -23,6 +23,7 @@ NUM_DEFAULT = 0
 NUM_EXPLICIT = 1 << 31
 NUM_QKV_A_PAIR, NUM_QK_PAIR, NUM_V_PAIR = 1 << 0, 1 << 1, 1 << 2
 NUM_O_A_PAIR, NUM_FFN_A_PAIR, NUM_DOWN_A_PAIR = 1 << 3, 1 << 4, 1 << 5
+NUM_ATTN_F16 = 1 << 6
 
 EXPORTS = (
     "llama_hidden_dim", "llama_rmsnorm", "llama_rope", "llama_linear", "llama_causal_attn",

@@ -63,7 +63,7 @@ struct Carve {
 
 uint32_t numerics_of(const llama_config *c) {
   if (c->numerics & LLAMA_NUM_EXPLICIT) return c->numerics;
-  return LLAMA_NUM_QK_PAIR | LLAMA_NUM_V_PAIR | LLAMA_NUM_O_A_PAIR;
+  return LLAMA_NUM_ATTN_F16 | LLAMA_NUM_O_A_PAIR;
 }
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
@@ -162,6 +162,9 @@ int check_block_cfg(const llama_config *c, int batch, int seq) {
   if (c->dtype == LLAMA_BF16) {
     if (c->dim % 256 || c->hidden % 128) return LLAMA_ERR_UNSUPPORTED;
   }
+  // fp16 attention operands are single values: no q/k or v pairs with them
+  const uint32_t num = numerics_of(c);
+  if ((num & LLAMA_NUM_ATTN_F16) && (num & (LLAMA_NUM_QK_PAIR | LLAMA_NUM_V_PAIR))) return LLAMA_ERR_UNSUPPORTED;
   // grouped K/V heads: a divisor of n_heads, groups of 1, 2, 4 or 8, K/V
   // width a multiple of the 128-column GEMM tile; bf16 path only
   const int nkv = c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads;
@@ -372,6 +375,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   const uint32_t num = numerics_of(c);
   const bool qkv_pair = num & LLAMA_NUM_QKV_A_PAIR, ffn_pair = num & LLAMA_NUM_FFN_A_PAIR;
   const bool opair = num & LLAMA_NUM_O_A_PAIR, dpair = num & LLAMA_NUM_DOWN_A_PAIR;
+  const bool af16 = num & LLAMA_NUM_ATTN_F16;
   const int vts = vt_stride_of(seq);
 
   // z = RMSNorm(x; g1): statistic + gained operand; the rstd multiply happens in the QKV epilogue
@@ -401,6 +405,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.vth = b.vth;
   q.vtl = b.vtl;
   q.rope_tab = b.rope_tab;
+  q.attn_f16 = af16;
   q.seq = seq;
   q.n_heads = H;
   q.head_dim = hd;
@@ -439,7 +444,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   at.n_kv_heads = nkv;
   at.vt_stride = vts;
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-  HIP_TRY(attn_prefill_launch(at, (num & LLAMA_NUM_QK_PAIR) ? 1 : 0, (num & LLAMA_NUM_V_PAIR) ? 1 : 0, s),
+  HIP_TRY(attn_prefill_launch(at, (num & LLAMA_NUM_QK_PAIR) ? 1 : 0, (num & LLAMA_NUM_V_PAIR) ? 1 : 0, af16, s),
           "attention");
 
   // h = x + attn Wo^T. With a split K the two partial products go to the
@@ -715,7 +720,7 @@ int llama_causal_attn(int in_dtype, int out_dtype, const void *q, const void *k,
   at.vt_stride = vts;
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)head_dim));
   // bf16 inputs are exact, so their lo parts are zero: one pass each.
-  HIP_TRY(attn_prefill_launch(at, 0, 0, s), "llama_causal_attn");
+  HIP_TRY(attn_prefill_launch(at, 0, 0, 0, s), "llama_causal_attn");
   return LLAMA_OK;
 }
 

@@ -1,7 +1,7 @@
 // Causal flash-style attention for prefill on gfx950 matrix cores.
 //
 // Per (sequence, head, 128-query tile) one workgroup of 4 wavefronts; each
-// wavefront owns 32 queries. Keys/values stream through LDS in tiles of 64.
+// wavefront owns 32 queries. Keys/values stream through LDS in tiles of 32.
 // The product is formed transposed — S^T = K Q^T and O^T = V^T P^T — so that in
 // the 32x32 accumulator layout every lane holds values of ONE query (its lane
 // index mod 32): the running max, the running sum and the rescaling of O stay
@@ -13,8 +13,10 @@
 //
 // Softmax is online in fp32 with exp2 and a log2(e)/sqrt(hd) prescale; masked
 // keys get exactly zero weight; tiles entirely above the diagonal are never
-// loaded and fully masked 32-key halves are skipped per wavefront. q/k and v
-// can be carried as bf16 hi/lo pairs (3 and 2 matrix-core passes).
+// loaded and fully masked 32-key halves are skipped per wavefront. Operands are
+// either bf16 (q/k and v optionally as hi/lo pairs: 3 and 2 matrix-core
+// passes) or IEEE fp16 (F16: q, k, v and the probabilities, one pass each;
+// 11 significant bits instead of 8, range up to 65504).
 //
 // Attention itself is the 2017 scaled-dot-product attention with a causal mask
 // (paperfordummies.in LLaMA page, "LLaMA is a pull request against the 2017
@@ -55,8 +57,9 @@ DEV void attn_tile_of(int k, int nqt, int bh_count, int &bh, int &qt) {
   }
 }
 
-template <int HD, bool QKPAIR, bool VPAIR>
+template <int HD, bool QKPAIR, bool VPAIR, bool F16>
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) {
+  static_assert(!F16 || (!QKPAIR && !VPAIR), "fp16 operands are single");
   constexpr int KT = 32;                         // keys per tile
   constexpr int KCH = HD / 8;                    // 16-byte chunks per K row
   constexpr int NKK = HD / 16;                   // k-steps of the score product
@@ -119,13 +122,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   issue(0);
 
   // q fragments (B operand of S^T = K Q^T): q[qi][16kk + 8g .. +7]
-  bf16x8 qh[NKK], ql[QKPAIR ? NKK : 1];
+  u32x4 qh[NKK], ql[QKPAIR ? NKK : 1];
   {
     const int64_t base = (tok0 + min(qi, S - 1)) * a.dim + h * HD + 8 * g;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      qh[kk] = as_bf16x8(*(const u32x4 *)(a.qh + base + 16 * kk));
-      if (QKPAIR) ql[kk] = as_bf16x8(*(const u32x4 *)(a.ql + base + 16 * kk));
+      qh[kk] = *(const u32x4 *)(a.qh + base + 16 * kk);
+      if (QKPAIR) ql[kk] = *(const u32x4 *)(a.ql + base + 16 * kk);
     }
   }
 
@@ -156,11 +159,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
-      const bf16x8 kf = as_bf16x8(sk[so]);
-      sc = mfma32(kf, qh[kk], sc);
-      if (QKPAIR) {
-        sc = mfma32(as_bf16x8(skl[so]), qh[kk], sc);
-        sc = mfma32(kf, ql[kk], sc);
+      if (F16) {
+        sc = mfma32h(as_f16x8(sk[so]), as_f16x8(qh[kk]), sc);
+      } else {
+        const bf16x8 kf = as_bf16x8(sk[so]);
+        sc = mfma32(kf, as_bf16x8(qh[kk]), sc);
+        if (QKPAIR) {
+          sc = mfma32(as_bf16x8(skl[so]), as_bf16x8(qh[kk]), sc);
+          sc = mfma32(kf, as_bf16x8(ql[kk]), sc);
+        }
       }
     }
 
@@ -201,14 +208,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       float pv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) pv[i] = sc[8 * s2 + i];
-      const bf16x8 pf = as_bf16x8(pack8(pv));
+      const u32x4 pf = F16 ? pack8h(pv) : pack8(pv);
       const int ch = 2 * s2 + g;
 #pragma unroll
       for (int e = 0; e < NEB; ++e) {
         const int row = 32 * e + l32;
         const int so = row * 4 + (ch ^ vswz(row));
-        acc_o[e] = mfma32(as_bf16x8(sv[so]), pf, acc_o[e]);
-        if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), pf, acc_o[e]);
+        if (F16) {
+          acc_o[e] = mfma32h(as_f16x8(sv[so]), as_f16x8(pf), acc_o[e]);
+        } else {
+          acc_o[e] = mfma32(as_bf16x8(sv[so]), as_bf16x8(pf), acc_o[e]);
+          if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), as_bf16x8(pf), acc_o[e]);
+        }
       }
     }
   }
@@ -252,22 +263,30 @@ __global__ void vt_pad_zero_kernel(u16 *vth, u16 *vtl, int64_t rows, int seq, in
   if (vtl) vtl[o] = 0;
 }
 
-template <int HD, bool QKPAIR, bool VPAIR>
+template <int HD, bool QKPAIR, bool VPAIR, bool F16 = false>
 static hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   const int nqt = (a.seq + 127) / 128;
-  hipLaunchKernelGGL((attn_prefill_kernel<HD, QKPAIR, VPAIR>), dim3(nqt * a.batch * a.n_heads), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((attn_prefill_kernel<HD, QKPAIR, VPAIR, F16>), dim3(nqt * a.batch * a.n_heads), dim3(256), 0,
+                     s, a);
   return hipGetLastError();
 }
 
-hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, hipStream_t s) {
+hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, int f16, hipStream_t s) {
+  if (f16 && (qk_pair || v_pair)) return hipErrorInvalidValue;
   if (a.batch * a.seq == 0) return hipSuccess;
   if (a.seq % 32) {
     const int64_t rows = (int64_t)a.batch * (a.n_kv_heads > 0 ? a.n_kv_heads : a.n_heads) * a.head_dim;
     const int64_t n = rows * (a.vt_stride - a.seq);
+    // all-zero bits are +0 in bf16 and in fp16
     hipLaunchKernelGGL(vt_pad_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
                        (u16 *)a.vth, v_pair ? (u16 *)a.vtl : (u16 *)nullptr, rows, a.seq, a.vt_stride);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (f16) {
+    if (a.head_dim == 128) return launch_t<128, false, false, true>(a, s);
+    if (a.head_dim == 64) return launch_t<64, false, false, true>(a, s);
+    return hipErrorInvalidValue;
   }
 #define ATTN_CASE(HD_, QK_, V_) \
   if (a.head_dim == HD_ && !!qk_pair == QK_ && !!v_pair == V_) return launch_t<HD_, QK_, V_>(a, s);

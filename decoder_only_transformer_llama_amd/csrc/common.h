@@ -8,6 +8,7 @@
 
 typedef uint16_t u16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -59,9 +60,22 @@ DEV void pack8_pair(const float *f, u32x4 &hi, u32x4 &lo) {
 }
 
 DEV bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+DEV f16x8 as_f16x8(const u32x4 &v) { return __builtin_bit_cast(f16x8, v); }
 
 DEV f32x16 mfma32(const bf16x8 &a, const bf16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+DEV f32x16 mfma32h(const f16x8 &a, const f16x8 &b, const f32x16 &c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// fp32 -> IEEE fp16, round to nearest even (overflow gives +-inf).
+DEV u16 f2h(float f) { return __builtin_bit_cast(u16, (_Float16)f); }
+DEV u32x4 pack8h(const float *f) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = (uint32_t)f2h(f[2 * i]) | ((uint32_t)f2h(f[2 * i + 1]) << 16);
+  return r;
 }
 
 DEV float wave_sum(float v) {

@@ -46,8 +46,11 @@ template <int BN, bool APAIR>
 struct GemmCfg {
   static constexpr int BM = 256, BK = 32;
   static constexpr int CH = 4;                     // 16-byte chunks per LDS row (64 bytes)
-  static constexpr int NW = 8;                     // wavefronts: 2 (M) x 4 (N)
-  static constexpr int WM = BM / 2, WN = BN / 4;
+#ifndef GEMM_NW
+#define GEMM_NW 8
+#endif
+  static constexpr int NW = GEMM_NW;               // wavefronts: 2 (M) x NW/2 (N)
+  static constexpr int WM = BM / 2, WN = BN / (NW / 2);
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_TILE = BM * CH;           // u32x4 per A tile
   static constexpr int B_TILE = BN * CH;
@@ -78,13 +81,13 @@ DEV void interleave() {
 }
 
 template <int BN, bool APAIR, int EPI>
-__global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmArgs a) {
   using G = GemmCfg<BN, APAIR>;
   constexpr int BM = G::BM, BK = G::BK, CH = G::CH, STAGES = G::STAGES;
   __shared__ u32x4 smem[STAGES * G::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / (G::NW / 2), wn = wave % (G::NW / 2);
   const int g = lane >> 5, l32 = lane & 31;
 
   const int tiles_m = (a.M + BM - 1) / BM;
@@ -255,7 +258,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
             for (int rq = 0; rq < 4; ++rq) {
               u16 hi[4], lo[4];
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) split_pair(acc[i][j][4 * rq + rr] * sc[4 * rq + rr], hi[rr], lo[rr]);
+              for (int rr = 0; rr < 4; ++rr) {
+                const float x = acc[i][j][4 * rq + rr] * sc[4 * rq + rr];
+                if (a.attn_f16) {
+                  hi[rr] = f2h(x);
+                  lo[rr] = 0;
+                } else {
+                  split_pair(x, hi[rr], lo[rr]);
+                }
+              }
               const int o = l32 * TS + 8 * rq + 4 * g;
               *(u32x2 *)(tr + o) = u32x2{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
               *(u32x2 *)(tr + 32 * TS + o) = u32x2{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
@@ -273,8 +284,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
             const u32x4 h0 = srch[0], h1 = srch[1], q0 = srcl[0], q1 = srcl[1];
             *(u32x4 *)(a.vth + o) = h0;
             *(u32x4 *)(a.vth + o + 8) = h1;
-            *(u32x4 *)(a.vtl + o) = q0;
-            *(u32x4 *)(a.vtl + o + 8) = q1;
+            if (!a.attn_f16) {
+              *(u32x4 *)(a.vtl + o) = q0;
+              *(u32x4 *)(a.vtl + o + 8) = q1;
+            }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -296,14 +309,19 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
               }
               const int cd = cd0 + l32;
               const int hh = cd >> hd_shift, e = cd & (a.head_dim - 1);
-              u16 hi, lo;
-              split_pair(acc[i][j][r] * sc[r], hi, lo);
+              const float x = acc[i][j][r] * sc[r];
               if (!fast) {
                 const int64_t o = (((int64_t)b * n_kv + hh) * a.head_dim + e) * a.vt_stride + s;
-                a.vth[o] = hi;
-                a.vtl[o] = lo;
+                if (a.attn_f16) {
+                  a.vth[o] = f2h(x);
+                } else {
+                  u16 hi, lo;
+                  split_pair(x, hi, lo);
+                  a.vth[o] = hi;
+                  a.vtl[o] = lo;
+                }
               }
-              if (a.vcache) a.vcache[(((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e] = hi;
+              if (a.vcache) a.vcache[(((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e] = f2bf(x);
             }
           }
         }
@@ -360,13 +378,20 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_kernel(const GemmArgs a) {
           }
         }
         u32x4 hi0, lo0, hi1, lo1;
-        pack8_pair(rot, hi0, lo0);
-        pack8_pair(rot + 8, hi1, lo1);
         const int64_t o = (int64_t)row * (seg == 0 ? a.dim : kvd) + cd;
-        *(u32x4 *)(dh + o) = hi0;
-        *(u32x4 *)(dh + o + 8) = hi1;
-        *(u32x4 *)(dl + o) = lo0;
-        *(u32x4 *)(dl + o + 8) = lo1;
+        if (a.attn_f16) {
+          *(u32x4 *)(dh + o) = pack8h(rot);
+          *(u32x4 *)(dh + o + 8) = pack8h(rot + 8);
+          hi0 = pack8(rot);   // the cache holds bf16
+          hi1 = pack8(rot + 8);
+        } else {
+          pack8_pair(rot, hi0, lo0);
+          pack8_pair(rot + 8, hi1, lo1);
+          *(u32x4 *)(dh + o) = hi0;
+          *(u32x4 *)(dh + o + 8) = hi1;
+          *(u32x4 *)(dl + o) = lo0;
+          *(u32x4 *)(dl + o + 8) = lo1;
+        }
         if (seg == 1 && a.kcache) {
           const int hh = cd >> hd_shift;
           u16 *kp = a.kcache + (((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e0;
@@ -439,7 +464,7 @@ hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   const int ks = a.k_splits > 1 ? a.k_splits : 1;
   if (a.K % (G::BK * ks)) return hipErrorInvalidValue;
   if (ks > 1 && EPI != EPI_PARTIAL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI>), dim3(nb, ks), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI>), dim3(nb, ks), dim3(G::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 

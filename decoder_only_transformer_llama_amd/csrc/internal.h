@@ -38,11 +38,12 @@ struct GemmArgs {
   // EPI_QKV
   uint16_t *qh, *ql, *kh, *kl;   // [M, dim] hi/lo of rotated q and k
   uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, vt_stride] hi/lo of v (transposed)
+  int attn_f16;                  // 1: qh, kh, vth hold fp16 (no lo parts written)
   const float2 *rope_tab;        // [seq, head_dim/2] (cos, sin)
   int seq, n_heads, head_dim, dim;
   int kv_dim, n_kv_heads;        // width and heads of k and v (0: dim, n_heads)
   int vt_stride;                 // row stride of the transposed v (>= seq, multiple of 64)
-  uint16_t *kcache, *vcache;     // optional: [batch, n_heads, max_seq, head_dim] of this layer
+  uint16_t *kcache, *vcache;     // optional bf16: [batch, n_kv_heads, max_seq, head_dim] of this layer
   int max_seq;
 };
 
@@ -78,7 +79,9 @@ struct AttnArgs {
   int vt_stride;                       // row stride of v^T (>= seq, multiple of 64)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
 };
-hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, hipStream_t s);
+// f16: q, k, v^T hold IEEE fp16 (single, no lo parts) and the probabilities
+// are rounded to fp16; otherwise bf16 with optional hi/lo pairs.
+hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, int f16, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
 hipError_t rope_table_launch(float2 *tab, int positions, int head_dim, float theta, hipStream_t s);

@@ -69,9 +69,13 @@ typedef enum {
 /* Numerics options of the bf16 path (llama_config.numerics). Weights are
  * exact bf16 inputs; an activation operand of a bf16 matrix-core product is
  * either rounded to bf16 or carried as an exact-to-2^-16 pair hi + lo of two
- * bf16 values (two products, same fp32 accumulator). LLAMA_NUM_DEFAULT (0)
- * selects the library's default set; LLAMA_NUM_EXPLICIT plus any of the bits
- * selects exactly those pairs. */
+ * bf16 values (two products, same fp32 accumulator). Inside attention, q, k,
+ * v and the probabilities may instead be IEEE fp16 (LLAMA_NUM_ATTN_F16: 11
+ * significant bits, one matrix-core pass per product; |q|, |k|, |v| must stay
+ * below 65504). LLAMA_NUM_DEFAULT (0) selects the library's default set,
+ * LLAMA_NUM_ATTN_F16 | LLAMA_NUM_O_A_PAIR; LLAMA_NUM_EXPLICIT plus any of the
+ * bits selects exactly those (ATTN_F16 excludes QK_PAIR and V_PAIR). The KV
+ * cache is bf16 in every mode. */
 #define LLAMA_NUM_DEFAULT 0u
 #define LLAMA_NUM_EXPLICIT (1u << 31)
 #define LLAMA_NUM_QKV_A_PAIR (1u << 0)  /* x*g1 operand of the Q/K/V projection */
@@ -80,6 +84,7 @@ typedef enum {
 #define LLAMA_NUM_O_A_PAIR (1u << 3)    /* attention output into the Wo projection */
 #define LLAMA_NUM_FFN_A_PAIR (1u << 4)  /* h*g2 operand of the gate/up projection */
 #define LLAMA_NUM_DOWN_A_PAIR (1u << 5) /* SiLU(gate)*up operand of the down projection */
+#define LLAMA_NUM_ATTN_F16 (1u << 6)    /* q, k, v and probabilities as fp16 in prefill attention */
 
 /* Model / block configuration. head_dim = dim / n_heads. */
 typedef struct llama_config {

@@ -153,6 +153,10 @@ def test_grouped_kv_heads_validation_and_sizes():
     assert ws(n_kv_heads=8, dtype=L.LLAMA_F32) == L.LLAMA_ERR_UNSUPPORTED
     assert ws(dim=512, n_heads=8, hidden=1536, n_kv_heads=1) == L.LLAMA_ERR_UNSUPPORTED   # width 64
     assert ws(dim=512, n_heads=8, hidden=1536, n_kv_heads=2) == 0                         # width 128
+    # fp16 attention operands are single values: no q/k or v pairs alongside
+    assert ws(numerics=L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_O_A_PAIR) == 0
+    assert ws(numerics=L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_QK_PAIR) == L.LLAMA_ERR_UNSUPPORTED
+    assert ws(numerics=L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_V_PAIR) == L.LLAMA_ERR_UNSUPPORTED
     # fewer key/value heads shrink the packed decode weights by exactly the Wk, Wv rows
     for nkv in (32, 8):
         assert lib.llama_decode_pack_size(ctypes.byref(_cfg(n_kv_heads=nkv)), ctypes.byref(n)) == 0
