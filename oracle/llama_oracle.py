@@ -209,6 +209,80 @@ def block_forward(x, w: Dict[str, np.ndarray], batch: int, seq: int, n_heads: in
     return y
 
 
+# --------------------------------------------------------------------------- norm placement
+def attn_sublayer(z, w: Dict[str, np.ndarray], batch: int, seq: int, n_heads: int,
+                  theta: float = 10000.0) -> np.ndarray:
+    """Wo . CausalAttn(RoPE(Wq z), RoPE(Wk z), Wv z): the attention branch of a
+    block applied to whatever the placement feeds it."""
+    z = f64(z)
+    hd = z.shape[1] // n_heads
+    pos = np.tile(np.arange(seq, dtype=np.float64), batch)
+    q = rope(linear(z, w["wq"]), pos, hd, theta)
+    k = rope(linear(z, w["wk"]), pos, hd, theta)
+    return linear(causal_attention(q, k, linear(z, w["wv"]), batch, seq, n_heads), w["wo"])
+
+
+def post_norm_block_forward(x, w: Dict[str, np.ndarray], batch: int, seq: int, n_heads: int,
+                            eps: float, theta: float = 10000.0) -> np.ndarray:
+    """The 2017 ordering, norm on the trunk after each residual add ([P1]
+    "Pre-norm: the norm goes on the branch, not the trunk"):
+
+        h = RMSNorm(x + Attn(x); g1),   y = RMSNorm(h + FFN(h); g2)
+
+    with the same attention and SwiGLU branches as the LLaMA block. Reading:
+    the block's two gains (attn_norm, ffn_norm) scale the two trunk norms; with
+    g = 1 and eps = 0 every output row has norm sqrt(dim) exactly, the page's
+    "pins the trunk at sqrt(d)"."""
+    x = f64(x)
+    h = rmsnorm(x + attn_sublayer(x, w, batch, seq, n_heads, theta), w["attn_norm"], eps)
+    return rmsnorm(h + swiglu_ffn(h, w["w_gate"], w["w_up"], w["w_down"]), w["ffn_norm"], eps)
+
+
+def no_norm_block_forward(x, w: Dict[str, np.ndarray], batch: int, seq: int, n_heads: int,
+                          eps: float = 0.0, theta: float = 10000.0) -> np.ndarray:
+    """The pre-norm block with both RMSNorm calls deleted ([P1] "Now break it":
+    the no-norm block): h = x + Attn(x), y = h + FFN(h). The gains and eps are
+    unused."""
+    x = f64(x)
+    h = x + attn_sublayer(x, w, batch, seq, n_heads, theta)
+    return h + swiglu_ffn(h, w["w_gate"], w["w_up"], w["w_down"])
+
+
+PLACEMENTS = {"pre": block_forward, "post": post_norm_block_forward, "none": no_norm_block_forward}
+
+
+def stack_forward(x, blocks, batch: int, seq: int, n_heads: int, eps: float, placement: str = "pre",
+                  theta: float = 10000.0):
+    """Blocks applied one after another (a model without embedding and head).
+    Returns the output and the trunk norm after every block: the mean over
+    tokens of each token's L2 norm ([P1] "Pre-norm ...": "residual-stream norm
+    per token"). Overflow is left to IEEE arithmetic (inf, then NaN), as in the
+    page's no-norm run."""
+    f = PLACEMENTS[placement]
+    x = f64(x)
+    norms = []
+    with np.errstate(over="ignore", invalid="ignore"):
+        for w in blocks:
+            x = f(x, w, batch, seq, n_heads, eps, theta)
+            norms.append(float(np.mean(np.sqrt(np.sum(x * x, axis=1)))))
+    return x, norms
+
+
+def amplification(x, direction, delta: float, blocks, batch: int, seq: int, n_heads: int, eps: float,
+                  placement: str = "pre", theta: float = 10000.0) -> float:
+    """Finite-difference probe of [P1] "Pre-norm ...": bump the stack's input
+    by delta along `direction`, run both inputs through the blocks, and divide
+    how far the output moved by how far the input moved:
+        ||F(x + delta u) - F(x)|| / ||delta u||   (Frobenius norms).
+    Reading: the page does not print the bump's shape; here it is one
+    direction over all tokens and channels, and the ratio is the directional
+    derivative's gain for small delta."""
+    x, u = f64(x), f64(direction)
+    y0, _ = stack_forward(x, blocks, batch, seq, n_heads, eps, placement, theta)
+    y1, _ = stack_forward(x + delta * u, blocks, batch, seq, n_heads, eps, placement, theta)
+    return float(np.linalg.norm(y1 - y0) / np.linalg.norm(delta * u))
+
+
 def block_step_with_cache(x, w, pos, k_cache, v_cache, n_heads: int, eps: float,
                           theta: float = 10000.0) -> np.ndarray:
     """One block applied to a single new token per sequence (decode).

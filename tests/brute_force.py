@@ -102,3 +102,33 @@ def block(x, w, batch, seq, n_heads, eps, theta):
     u = [[silu(gate[t][j]) * up[t][j] for j in range(len(gate[t]))] for t in range(len(gate))]
     dn = matvec_rows(u, w["w_down"])
     return [[h[t][c] + dn[t][c] for c in range(d)] for t in range(len(x))]
+
+
+def add_rows(a, b):
+    return [[a[t][c] + b[t][c] for c in range(len(a[t]))] for t in range(len(a))]
+
+
+def attn_branch(z, w, batch, seq, n_heads, theta):
+    hd = len(z[0]) // n_heads
+    pos = [float(s) for _ in range(batch) for s in range(seq)]
+    q = rope_rows(matvec_rows(z, w["wq"]), pos, hd, theta)
+    k = rope_rows(matvec_rows(z, w["wk"]), pos, hd, theta)
+    return matvec_rows(attention(q, k, matvec_rows(z, w["wv"]), batch, seq, n_heads), w["wo"])
+
+
+def ffn_branch(z, w):
+    gate, up = matvec_rows(z, w["w_gate"]), matvec_rows(z, w["w_up"])
+    u = [[silu(gate[t][j]) * up[t][j] for j in range(len(gate[t]))] for t in range(len(gate))]
+    return matvec_rows(u, w["w_down"])
+
+
+def post_norm_block(x, w, batch, seq, n_heads, eps, theta):
+    """Norm on the trunk after each residual add (2017 ordering)."""
+    h = rmsnorm_rows(add_rows(x, attn_branch(x, w, batch, seq, n_heads, theta)), w["attn_norm"], eps)
+    return rmsnorm_rows(add_rows(h, ffn_branch(h, w)), w["ffn_norm"], eps)
+
+
+def no_norm_block(x, w, batch, seq, n_heads, theta):
+    """Pre-norm block with both norms removed."""
+    h = add_rows(x, attn_branch(x, w, batch, seq, n_heads, theta))
+    return add_rows(h, ffn_branch(h, w))

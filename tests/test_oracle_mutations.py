@@ -91,3 +91,28 @@ def test_planted_ffn_norm_on_trunk_input_is_caught(monkeypatch):
     monkeypatch.setattr(O, "rmsnorm", first_arg_memory)
     got = O.block_forward(x, w, B, S, H, 1e-2, 1e4)
     assert np.max(np.abs(got - want)) > 1e-6
+
+
+def _post_norm_norm_before_add(x, w, batch, seq, n_heads, eps, theta=10000.0):
+    # 2017 ordering read wrongly: normalise the branch output, then add
+    h = x + O.rmsnorm(O.attn_sublayer(x, w, batch, seq, n_heads, theta), w["attn_norm"], eps)
+    return h + O.rmsnorm(O.swiglu_ffn(h, w["w_gate"], w["w_up"], w["w_down"]), w["ffn_norm"], eps)
+
+
+def _no_norm_keeps_ffn_norm(x, w, batch, seq, n_heads, eps=0.0, theta=10000.0):
+    # only the first norm deleted
+    h = x + O.attn_sublayer(x, w, batch, seq, n_heads, theta)
+    return h + O.swiglu_ffn(O.rmsnorm(h, w["ffn_norm"], 1e-6), w["w_gate"], w["w_up"], w["w_down"])
+
+
+@pytest.mark.parametrize("which,patch", [("post", _post_norm_norm_before_add), ("none", _no_norm_keeps_ffn_norm)])
+def test_planted_norm_placement_mistake_is_caught(which, patch):
+    B, S, d, H = 2, 4, 16, 2
+    w = _tiny_block(52, d, H)
+    x = _rand((B * S, d), 53)
+    wl = {k: v.tolist() for k, v in w.items()}
+    if which == "post":
+        want = np.array(BF.post_norm_block(x.tolist(), wl, B, S, H, 1e-6, 1e4))
+    else:
+        want = np.array(BF.no_norm_block(x.tolist(), wl, B, S, H, 1e4))
+    assert np.max(np.abs(patch(x, w, B, S, H, 1e-6, 1e4) - want)) > 1e-6

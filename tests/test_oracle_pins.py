@@ -357,3 +357,81 @@ def test_gqa_decode_equals_prefill_last_row():
     O.model_forward(toks[:, :6], emb, lambda l: (layers[l], *c2[l]), L, fn, out, H, 1e-6)
     dec = O.model_decode(toks[:, 6], np.full(B, 6), emb, lambda l: (layers[l], *c2[l]), L, fn, out, H, 1e-6)
     np.testing.assert_allclose(dec, full[:, 6], rtol=1e-10, atol=1e-11)
+
+
+# ---------------------------------------------------------------- norm placement ([P1] "Pre-norm ...")
+def test_post_and_no_norm_blocks_brute_force():
+    B, S, d, H = 2, 5, 16, 2
+    w = _tiny_block(30, d, H)
+    x = _rand((B * S, d), 31)
+    wl = {k: v.tolist() for k, v in w.items()}
+    got = O.post_norm_block_forward(x, w, B, S, H, 1e-6, 10000.0)
+    want = BF.post_norm_block(x.tolist(), wl, B, S, H, 1e-6, 10000.0)
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-11, atol=1e-12)
+    got = O.no_norm_block_forward(x, w, B, S, H, 1e-6, 10000.0)
+    want = BF.no_norm_block(x.tolist(), wl, B, S, H, 10000.0)
+    np.testing.assert_allclose(got, np.array(want), rtol=1e-11, atol=1e-12)
+
+
+def test_post_norm_rows_have_norm_sqrt_d():
+    """With unit gains and eps = 0 the post-norm trunk is pinned: every output
+    row has L2 norm sqrt(d) exactly (the page's sqrt(64) = 8)."""
+    B, S, d, H = 1, 7, 16, 2
+    w = _tiny_block(32, d, H, gain_std=0.0)
+    y = O.post_norm_block_forward(4.0 * _rand((B * S, d), 33), w, B, S, H, 0.0, 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=1), np.sqrt(d), rtol=1e-14)
+
+
+def test_placements_with_silent_branches():
+    """Wo = 0 and W_down = 0 silence both branches: pre-norm and no-norm blocks
+    are then the identity, the post-norm block is RMSNorm(RMSNorm(x; g1); g2)."""
+    B, S, d, H = 1, 6, 16, 2
+    w = _tiny_block(34, d, H)
+    w["wo"] = np.zeros_like(w["wo"])
+    w["w_down"] = np.zeros_like(w["w_down"])
+    x = _rand((B * S, d), 35)
+    np.testing.assert_array_equal(O.block_forward(x, w, B, S, H, 1e-6), x)
+    np.testing.assert_array_equal(O.no_norm_block_forward(x, w, B, S, H), x)
+    r1 = x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + 1e-6) * w["attn_norm"]
+    r2 = r1 / np.sqrt(np.mean(r1 * r1, axis=1, keepdims=True) + 1e-6) * w["ffn_norm"]
+    np.testing.assert_allclose(O.post_norm_block_forward(x, w, B, S, H, 1e-6), r2, rtol=1e-13)
+
+
+def test_amplification_closed_forms():
+    """Silenced branches: a pre-norm stack is the identity, so any bump comes
+    out unchanged (ratio 1); a post-norm stack with unit gains and eps = 0 maps
+    each row to its direction, so a bump along x itself does not move the
+    output (ratio 0)."""
+    B, S, d, H = 1, 5, 16, 2
+    blocks = []
+    for i in range(3):
+        w = _tiny_block(40 + i, d, H, gain_std=0.0)
+        w["wo"] = np.zeros_like(w["wo"])
+        w["w_down"] = np.zeros_like(w["w_down"])
+        blocks.append(w)
+    x = _rand((B * S, d), 45)
+    u = _rand((B * S, d), 46)
+    u /= np.linalg.norm(u)
+    assert O.amplification(x, u, 1e-3, blocks, B, S, H, 1e-6, "pre") == pytest.approx(1.0, rel=1e-12)
+    assert O.amplification(x, x / np.linalg.norm(x), 1e-3, blocks, B, S, H, 0.0, "post") < 1e-10
+
+
+def test_norm_placement_trunk_behaviour():
+    """The trunk under the three placements on the 32-block d = 64 study
+    workload (weights N(0, 1/fan_in); the page's own init is not printed, so
+    its numbers are not pinned, only these properties it states): post-norm
+    holds every token at norm sqrt(d) (eps = 1e-5 shaves a relative 1e-5 at
+    most), pre-norm lets it grow, and without norms it overflows to inf and
+    then NaN before layer 10."""
+    from decoder_only_transformer_llama_amd import inputs as I
+    w = I.workload(7)
+    blocks = [{k: O.f64(v) for k, v in I.block_weights(w, l).items()} for l in range(20)]
+    x = O.f64(I.block_input(w))
+    d = w.dim
+    _, post = O.stack_forward(x, blocks, 1, w.seq, w.n_heads, w.eps, "post")
+    assert all(np.sqrt(d) * (1 - 1e-5) <= n <= np.sqrt(d) for n in post)
+    _, pre = O.stack_forward(x, blocks, 1, w.seq, w.n_heads, w.eps, "pre")
+    assert all(np.isfinite(pre)) and pre[19] > 2 * pre[0] and all(b > a for a, b in zip(pre, pre[1:]))
+    _, none = O.stack_forward(x, blocks, 1, w.seq, w.n_heads, w.eps, "none")
+    assert np.isfinite(none[0]) and none[4] > 1e6 * none[0]
+    assert not np.isfinite(none[9]) and np.isnan(none[19])
