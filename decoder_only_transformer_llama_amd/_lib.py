@@ -24,6 +24,7 @@ NUM_EXPLICIT = 1 << 31
 NUM_QKV_A_PAIR, NUM_QK_PAIR, NUM_V_PAIR = 1 << 0, 1 << 1, 1 << 2
 NUM_O_A_PAIR, NUM_FFN_A_PAIR, NUM_DOWN_A_PAIR = 1 << 3, 1 << 4, 1 << 5
 NUM_ATTN_F16 = 1 << 6
+NORM_PRE, NORM_POST, NORM_NONE = 0, 1, 2
 
 EXPORTS = (
     "llama_hidden_dim", "llama_rmsnorm", "llama_rope", "llama_linear", "llama_causal_attn",
@@ -37,7 +38,7 @@ class LlamaConfig(ctypes.Structure):
     _fields_ = [("dim", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("hidden", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("vocab", ctypes.c_int32), ("max_seq", ctypes.c_int32),
                 ("norm_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("numerics", ctypes.c_uint32), ("n_kv_heads", ctypes.c_int32)]
+                ("numerics", ctypes.c_uint32), ("n_kv_heads", ctypes.c_int32), ("norm_placement", ctypes.c_int32)]
 
 
 class BlockWeights(ctypes.Structure):

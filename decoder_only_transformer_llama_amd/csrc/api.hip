@@ -162,6 +162,7 @@ int check_block_cfg(const llama_config *c, int batch, int seq) {
   if (c->dtype == LLAMA_BF16) {
     if (c->dim % 256 || c->hidden % 128) return LLAMA_ERR_UNSUPPORTED;
   }
+  if (c->norm_placement < LLAMA_NORM_PRE || c->norm_placement > LLAMA_NORM_NONE) return LLAMA_ERR_UNSUPPORTED;
   // fp16 attention operands are single values: no q/k or v pairs with them
   const uint32_t num = numerics_of(c);
   if ((num & LLAMA_NUM_ATTN_F16) && (num & (LLAMA_NUM_QK_PAIR | LLAMA_NUM_V_PAIR))) return LLAMA_ERR_UNSUPPORTED;
@@ -192,7 +193,7 @@ int check_model_cfg(const llama_config *c, int batch, int seq) {
   int st = check_block_cfg(c, batch, seq);
   if (st) return st;
   if (c->n_layers <= 0 || c->vocab <= 0 || c->max_seq <= 0) return LLAMA_ERR_SHAPE;
-  if (c->dtype != LLAMA_BF16) return LLAMA_ERR_UNSUPPORTED;
+  if (c->dtype != LLAMA_BF16 || c->norm_placement != LLAMA_NORM_PRE) return LLAMA_ERR_UNSUPPORTED;
   return LLAMA_OK;
 }
 
@@ -377,10 +378,13 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   const bool opair = num & LLAMA_NUM_O_A_PAIR, dpair = num & LLAMA_NUM_DOWN_A_PAIR;
   const bool af16 = num & LLAMA_NUM_ATTN_F16;
   const int vts = vt_stride_of(seq);
+  // Pre-norm (LLaMA) folds RMSNorm into the next projection; post-norm and
+  // no-norm feed the branches the trunk itself (operand x, no rstd scale).
+  const bool pre = c->norm_placement == LLAMA_NORM_PRE, post = c->norm_placement == LLAMA_NORM_POST;
 
   // z = RMSNorm(x; g1): statistic + gained operand; the rstd multiply happens in the QKV epilogue
-  HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, (const uint16_t *)w->attn_norm, M, d, c->norm_eps, b.rstd1,
-                           b.xg_hi, qkv_pair ? b.xg_lo : nullptr, s),
+  HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, pre ? (const uint16_t *)w->attn_norm : nullptr, M, d,
+                           c->norm_eps, b.rstd1, b.xg_hi, qkv_pair ? b.xg_lo : nullptr, s),
           "attention norm");
   HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");
 
@@ -392,7 +396,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.A = b.xg_hi;
   q.A_lo = qkv_pair ? b.xg_lo : nullptr;
   q.lda = d;
-  q.rstd = b.rstd1;
+  q.rstd = pre ? b.rstd1 : nullptr;
   q.b_mode = BMODE_CONCAT3;
   q.B0 = (const uint16_t *)w->wq;
   q.B1 = (const uint16_t *)w->wk;
@@ -449,7 +453,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
 
   // h = x + attn Wo^T. With a split K the two partial products go to the
   // q/k buffers (dead after attention) and the ffn norm prep forms h.
-  const ResidCfg oc = choose_resid(M, d, d, opair);
+  ResidCfg oc = choose_resid(M, d, d, opair);
+  if (post) oc.splits = 1;   // the trunk norm below reads x + attn Wo^T whole
   GemmArgs o{};
   o.M = M;
   o.N = d;
@@ -467,14 +472,16 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   o.part = b.part;
   HIP_TRY(gemm_launch(GemmKey{oc.bn, opair, oc.splits > 1 ? EPI_PARTIAL : EPI_RESID}, o, s), "output projection");
 
+  // post-norm: h = RMSNorm(x + attn Wo^T; g1) in place, fp32
+  if (post) HIP_TRY(rmsnorm_launch(1, 1, b.h, w->attn_norm, b.h, M, d, c->norm_eps, s, 0), "attention norm");
   // z2 = RMSNorm(h; g2), operand reuses the x*g1 buffers
+  const uint16_t *g2 = pre ? (const uint16_t *)w->ffn_norm : nullptr;
   if (oc.splits > 1)
-    HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, (const uint16_t *)w->ffn_norm, M, d, c->norm_eps, b.rstd2,
-                             b.xg_hi, ffn_pair ? b.xg_lo : nullptr, s, b.part, oc.splits, b.h),
+    HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, g2, M, d, c->norm_eps, b.rstd2, b.xg_hi,
+                             ffn_pair ? b.xg_lo : nullptr, s, b.part, oc.splits, b.h),
             "ffn norm");
   else
-    HIP_TRY(norm_prep_launch(1, b.h, (const uint16_t *)w->ffn_norm, M, d, c->norm_eps, b.rstd2, b.xg_hi,
-                             ffn_pair ? b.xg_lo : nullptr, s),
+    HIP_TRY(norm_prep_launch(1, b.h, g2, M, d, c->norm_eps, b.rstd2, b.xg_hi, ffn_pair ? b.xg_lo : nullptr, s),
             "ffn norm");
   GemmArgs f{};
   f.M = M;
@@ -483,7 +490,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   f.A = b.xg_hi;
   f.A_lo = ffn_pair ? b.xg_lo : nullptr;
   f.lda = d;
-  f.rstd = b.rstd2;
+  f.rstd = pre ? b.rstd2 : nullptr;
   f.b_mode = BMODE_GATEUP;
   f.B0 = (const uint16_t *)w->w_gate;
   f.B1 = (const uint16_t *)w->w_up;
@@ -510,25 +517,39 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   dn.part = b.part;
   HIP_TRY(gemm_launch(GemmKey{dc.bn, dpair, dc.splits > 1 ? EPI_PARTIAL : EPI_RESID}, dn, s), "down projection");
   if (dc.splits > 1) HIP_TRY(resid_sum_launch(b.h, b.part, dc.splits, (int64_t)M * d, y, s), "down residual");
+  if (post) HIP_TRY(rmsnorm_launch(1, 1, y, w->ffn_norm, y, M, d, c->norm_eps, s, 0), "ffn norm");
   return LLAMA_OK;
 }
 
 int block_f32(const llama_config *c, const llama_block_weights *w, const float *x, float *y, int batch,
               int seq, const BlockWs &b, hipStream_t s) {
   const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq, hid = c->hidden;
-  HIP_TRY(rmsnorm_launch(1, 1, x, w->attn_norm, b.z, M, d, c->norm_eps, s), "rmsnorm");
-  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->wq, b.q, nullptr, M, d, d, s), "q projection");
-  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->wk, b.k, nullptr, M, d, d, s), "k projection");
-  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->wv, b.v, nullptr, M, d, d, s), "v projection");
+  const int np = c->norm_placement;
+  // attention branch input: RMSNorm(x; g1) before it (pre-norm) or x itself
+  const float *za = x;
+  if (np == LLAMA_NORM_PRE) {
+    HIP_TRY(rmsnorm_launch(1, 1, x, w->attn_norm, b.z, M, d, c->norm_eps, s), "rmsnorm");
+    za = b.z;
+  }
+  HIP_TRY(gemm_f32_launch(za, (const float *)w->wq, b.q, nullptr, M, d, d, s), "q projection");
+  HIP_TRY(gemm_f32_launch(za, (const float *)w->wk, b.k, nullptr, M, d, d, s), "k projection");
+  HIP_TRY(gemm_f32_launch(za, (const float *)w->wv, b.v, nullptr, M, d, d, s), "v projection");
   HIP_TRY(rope_launch(1, b.q, b.q, nullptr, M, H, hd, c->rope_theta, seq, s), "rope q");
   HIP_TRY(rope_launch(1, b.k, b.k, nullptr, M, H, hd, c->rope_theta, seq, s), "rope k");
   HIP_TRY(attn_f32_launch(b.q, b.k, b.v, b.att, batch, seq, H, hd, s), "attention");
   HIP_TRY(gemm_f32_launch(b.att, (const float *)w->wo, b.h, x, M, d, d, s), "output projection");
-  HIP_TRY(rmsnorm_launch(1, 1, b.h, w->ffn_norm, b.z, M, d, c->norm_eps, s), "rmsnorm");
-  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->w_gate, b.gate, nullptr, M, hid, d, s), "gate");
-  HIP_TRY(gemm_f32_launch(b.z, (const float *)w->w_up, b.up, nullptr, M, hid, d, s), "up");
+  // post-norm: the trunk itself is normalised, h = RMSNorm(x + attn; g1)
+  if (np == LLAMA_NORM_POST) HIP_TRY(rmsnorm_launch(1, 1, b.h, w->attn_norm, b.h, M, d, c->norm_eps, s), "rmsnorm");
+  const float *zf = b.h;
+  if (np == LLAMA_NORM_PRE) {
+    HIP_TRY(rmsnorm_launch(1, 1, b.h, w->ffn_norm, b.z, M, d, c->norm_eps, s), "rmsnorm");
+    zf = b.z;
+  }
+  HIP_TRY(gemm_f32_launch(zf, (const float *)w->w_gate, b.gate, nullptr, M, hid, d, s), "gate");
+  HIP_TRY(gemm_f32_launch(zf, (const float *)w->w_up, b.up, nullptr, M, hid, d, s), "up");
   HIP_TRY(silu_mul_f32_launch(b.gate, b.up, b.gate, (int64_t)M * hid, s), "silu");
   HIP_TRY(gemm_f32_launch(b.gate, (const float *)w->w_down, y, b.h, M, d, hid, s), "down projection");
+  if (np == LLAMA_NORM_POST) HIP_TRY(rmsnorm_launch(1, 1, y, w->ffn_norm, y, M, d, c->norm_eps, s), "rmsnorm");
   return LLAMA_OK;
 }
 

@@ -59,6 +59,8 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 // rstd = 1/sqrt(mean(x^2) + eps) (sum reduced across the wavefront) and the
 // GEMM operand x * g as bf16 hi (+ lo). The product's consumer multiplies its
 // fp32 accumulator by rstd, which completes RMSNorm(x; g) W^T. dim % 8 == 0.
+// g == nullptr: the operand is x itself (a block without a norm before the
+// projection; rstd is then written but not used).
 template <bool IN_F32, bool PAIR, bool PARTS>
 __global__ __launch_bounds__(256) void norm_prep_kernel(const void *x, const u16 *g, int64_t rows, int dim,
                                                         float eps, float *rstd, u16 *xg_hi, u16 *xg_lo,
@@ -96,7 +98,12 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *x, const u16
       *(f32x4 *)(h_out + base + c) = f32x4{f[0], f[1], f[2], f[3]};
       *(f32x4 *)(h_out + base + c + 4) = f32x4{f[4], f[5], f[6], f[7]};
     }
-    unpack8(*(const u32x4 *)(g + c), gf);
+    if (g) {
+      unpack8(*(const u32x4 *)(g + c), gf);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) gf[i] = 1.0f;
+    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       ss += f[i] * f[i];
@@ -160,7 +167,8 @@ hipError_t resid_sum_launch(const float *r, const float *part, int n_parts, int6
 
 // ------------------------------------------------------------------ RMSNorm
 // One 64-lane wavefront per row; the sum of squares is reduced across lanes.
-template <bool IN_F32, bool OUT_F32>
+// In place (y == x) is allowed: each lane rereads only the elements it writes.
+template <bool IN_F32, bool OUT_F32, bool G_F32>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, const void *g, void *y, int64_t rows,
                                                       int dim, float eps) {
   const int lane = threadIdx.x & 63;
@@ -179,7 +187,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, const void 
   const float r = rstd_of(ss, dim, eps);
   for (int c = lane; c < dim; c += 64) {
     float v = ld(x, base + c) * r;
-    if (g) v *= ld(g, c);
+    if (g) v *= G_F32 ? ((const float *)g)[c] : bf2f(((const u16 *)g)[c]);
     if (OUT_F32)
       ((float *)y)[base + c] = v;
     else
@@ -188,18 +196,20 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const void *x, const void 
 }
 
 hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,
-                          int dim, float eps, hipStream_t s) {
+                          int dim, float eps, hipStream_t s, int g_f32) {
   if (rows == 0) return hipSuccess;
+  if (g_f32 < 0) g_f32 = in_f32;
   dim3 grid((unsigned)((rows + 3) / 4));
-#define RMS_CASE(I, O)                                                                       \
-  if (!!in_f32 == I && !!out_f32 == O) {                                                     \
-    hipLaunchKernelGGL((rmsnorm_kernel<I, O>), grid, dim3(256), 0, s, x, g, y, rows, dim, eps); \
-    return hipGetLastError();                                                                \
+#define RMS_CASE(I, O, G)                                                                       \
+  if (!!in_f32 == I && !!out_f32 == O && !!g_f32 == G) {                                        \
+    hipLaunchKernelGGL((rmsnorm_kernel<I, O, G>), grid, dim3(256), 0, s, x, g, y, rows, dim, eps); \
+    return hipGetLastError();                                                                   \
   }
-  RMS_CASE(true, true)
-  RMS_CASE(true, false)
-  RMS_CASE(false, true)
-  RMS_CASE(false, false)
+  RMS_CASE(true, true, true)
+  RMS_CASE(true, false, true)
+  RMS_CASE(false, true, false)
+  RMS_CASE(false, false, false)
+  RMS_CASE(true, true, false)
 #undef RMS_CASE
   return hipErrorInvalidValue;
 }

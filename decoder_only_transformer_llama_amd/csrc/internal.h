@@ -88,7 +88,8 @@ hipError_t rope_table_launch(float2 *tab, int positions, int head_dim, float the
 hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int head_dim, float theta,
                                  int max_seq, hipStream_t s);
 // Norm prep (one wavefront per row): rstd[r] = 1/sqrt(mean(x[r]^2) + eps) and the
-// product x[r] * g as bf16 (hi, and lo when xg_lo is non-null).
+// product x[r] * g as bf16 (hi, and lo when xg_lo is non-null); g == nullptr
+// gives x[r] itself.
 // With `part` (n_parts fp32 [rows, dim] split-K partial products), the row is
 // first h = x + part[0] + ... (split order), written to h_out (fp32), and the
 // statistics and product are those of h.
@@ -99,8 +100,10 @@ hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_
 hipError_t argmax_launch(const float *logits, int64_t rows, int vocab, int32_t *out, hipStream_t s);
 // y = r + part[0] + ... + part[n_parts-1], fp32, n elements (n % 4 == 0).
 hipError_t resid_sum_launch(const float *r, const float *part, int n_parts, int64_t n, float *y, hipStream_t s);
+// y = x / sqrt(mean(x^2) + eps) * g per row; g in fp32 when g_f32 (default:
+// the dtype of x); y may alias x.
 hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,
-                          int dim, float eps, hipStream_t s);
+                          int dim, float eps, hipStream_t s, int g_f32 = -1);
 // pos == nullptr: the position of token t is t % seq_mod.
 hipError_t rope_launch(int f32, const void *x, void *y, const int32_t *pos, int64_t tokens, int n_heads,
                        int head_dim, float theta, int seq_mod, hipStream_t s);

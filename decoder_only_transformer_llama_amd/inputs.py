@@ -29,6 +29,7 @@ T_X, T_ATTN_NORM, T_WQ, T_WK, T_WV, T_WO = 0, 1, 2, 3, 4, 5
 T_FFN_NORM, T_W_GATE, T_W_UP, T_W_DOWN = 6, 7, 8, 9
 T_TOK_EMB, T_FINAL_NORM, T_OUTPUT, T_K_CACHE, T_V_CACHE, T_TOKENS = 10, 11, 12, 13, 14, 15
 T_Q, T_K, T_V, T_POS = 16, 17, 18, 19
+T_BUMP = 20
 
 WEIGHT_STD = 0.02
 
@@ -52,6 +53,7 @@ class Workload:
     max_seq: int = 0
     decode_pos: int = -1       # >= 0: a decode step at this position (cache holds 0..pos-1)
     n_kv_heads: int = 0        # key/value heads (0: n_heads; fewer: grouped-query attention)
+    fan_in_init: bool = False  # weights N(0, 1/fan_in) instead of N(0, WEIGHT_STD^2)
 
     @property
     def head_dim(self) -> int:
@@ -89,6 +91,10 @@ WORKLOADS: Dict[int, Workload] = {
     # LLaMA-7B-shape full-model decode step, batch 32, cache of 2047 positions
     4: Workload(4, "7b-model-decode-b32-kv2047", dim=4096, n_heads=32, hidden=11008, batch=32, seq=1,
                 dtype="bf16", n_layers=32, vocab=32000, max_seq=2048, decode_pos=2047),
+    # norm placement study: a stack of 32 small blocks (d 64, one head, SwiGLU
+    # hidden 256), one sequence of 16 tokens, fp32, weights N(0, 1/fan_in), gains 1
+    7: Workload(7, "norm-placement-d64-l32-s16", dim=64, n_heads=1, hidden=256, batch=1, seq=16, dtype="f32",
+                eps=1e-5, n_layers=32, fan_in_init=True),
     # the same model with grouped-query attention: 8 key/value heads (groups of 4)
     5: Workload(5, "7b-gqa8-model-decode-b32-kv2047", dim=4096, n_heads=32, hidden=11008, batch=32, seq=1,
                 dtype="bf16", n_layers=32, vocab=32000, max_seq=2048, decode_pos=2047, n_kv_heads=8),
@@ -159,20 +165,29 @@ def gain(w: Workload, layer: int, tensor: int, device="cpu") -> torch.Tensor:
 
 
 def block_weights(w: Workload, layer: int = 0, device="cpu") -> Dict[str, torch.Tensor]:
-    """Weights of one block, [out, in] row-major (y = x W^T)."""
+    """Weights of one block, [out, in] row-major (y = x W^T): N(0, 0.02^2), or
+    N(0, 1/in) with `fan_in_init`."""
     d, h, dt = w.dim, w.hidden, w.torch_dtype
     wid = w.wid
+    sd = (lambda fan_in: fan_in ** -0.5) if w.fan_in_init else (lambda fan_in: WEIGHT_STD)
     return {
         "attn_norm": gain(w, layer, T_ATTN_NORM, device),
-        "wq": normal((d, d), wid, layer, T_WQ, std=WEIGHT_STD, dtype=dt, device=device),
-        "wk": normal((w.kv_dim, d), wid, layer, T_WK, std=WEIGHT_STD, dtype=dt, device=device),
-        "wv": normal((w.kv_dim, d), wid, layer, T_WV, std=WEIGHT_STD, dtype=dt, device=device),
-        "wo": normal((d, d), wid, layer, T_WO, std=WEIGHT_STD, dtype=dt, device=device),
+        "wq": normal((d, d), wid, layer, T_WQ, std=sd(d), dtype=dt, device=device),
+        "wk": normal((w.kv_dim, d), wid, layer, T_WK, std=sd(d), dtype=dt, device=device),
+        "wv": normal((w.kv_dim, d), wid, layer, T_WV, std=sd(d), dtype=dt, device=device),
+        "wo": normal((d, d), wid, layer, T_WO, std=sd(d), dtype=dt, device=device),
         "ffn_norm": gain(w, layer, T_FFN_NORM, device),
-        "w_gate": normal((h, d), wid, layer, T_W_GATE, std=WEIGHT_STD, dtype=dt, device=device),
-        "w_up": normal((h, d), wid, layer, T_W_UP, std=WEIGHT_STD, dtype=dt, device=device),
-        "w_down": normal((d, h), wid, layer, T_W_DOWN, std=WEIGHT_STD, dtype=dt, device=device),
+        "w_gate": normal((h, d), wid, layer, T_W_GATE, std=sd(d), dtype=dt, device=device),
+        "w_up": normal((h, d), wid, layer, T_W_UP, std=sd(d), dtype=dt, device=device),
+        "w_down": normal((d, h), wid, layer, T_W_DOWN, std=sd(h), dtype=dt, device=device),
     }
+
+
+def bump_direction(w: Workload, device="cpu") -> torch.Tensor:
+    """Unit-Frobenius-norm direction [tokens, dim] (fp32) for the
+    finite-difference probe of a block stack."""
+    u = normal((w.tokens, w.dim), w.wid, 0, T_BUMP, device=device)
+    return u / torch.linalg.vector_norm(u)
 
 
 def block_input(w: Workload, device="cpu") -> torch.Tensor:

@@ -46,9 +46,10 @@ def _ws(nbytes: int, device) -> torch.Tensor:
 
 def config(dim: int, n_heads: int, hidden: int, *, dtype: torch.dtype = torch.bfloat16, n_layers: int = 1,
            vocab: int = 0, max_seq: int = 0, eps: float = 1e-6, theta: float = 10000.0,
-           numerics: int = L.NUM_DEFAULT, n_kv_heads: int = 0) -> L.LlamaConfig:
+           numerics: int = L.NUM_DEFAULT, n_kv_heads: int = 0,
+           norm_placement: int = L.NORM_PRE) -> L.LlamaConfig:
     return L.LlamaConfig(dim, n_heads, hidden, n_layers, vocab, max_seq, eps, theta, _DT[dtype], numerics,
-                         n_kv_heads)
+                         n_kv_heads, norm_placement)
 
 
 def workspace_bytes(cfg: L.LlamaConfig, op: int, batch: int, seq: int) -> int:

@@ -86,6 +86,14 @@ typedef enum {
 #define LLAMA_NUM_DOWN_A_PAIR (1u << 5) /* SiLU(gate)*up operand of the down projection */
 #define LLAMA_NUM_ATTN_F16 (1u << 6)    /* q, k, v and probabilities as fp16 in prefill attention */
 
+/* Where a block's two RMSNorms sit ([P1] "Pre-norm: the norm goes on the
+ * branch, not the trunk" and "Now break it"). With Attn and FFN the two
+ * branches of the block:
+ *   PRE  (LLaMA): h = x + Attn(RMSNorm(x; g1)),  y = h + FFN(RMSNorm(h; g2))
+ *   POST (2017):  h = RMSNorm(x + Attn(x); g1),  y = RMSNorm(h + FFN(h); g2)
+ *   NONE:         h = x + Attn(x),               y = h + FFN(h)  (gains unused) */
+typedef enum { LLAMA_NORM_PRE = 0, LLAMA_NORM_POST = 1, LLAMA_NORM_NONE = 2 } llama_norm_placement;
+
 /* Model / block configuration. head_dim = dim / n_heads. */
 typedef struct llama_config {
   int32_t dim;        /* model width d */
@@ -104,6 +112,8 @@ typedef struct llama_config {
                        * sharing one K/V head ([P4] "GQA Was Not an Original LLaMA
                        * Feature"). bf16 block/model entry points only; group size
                        * 1, 2, 4 or 8; n_kv_heads * head_dim a multiple of 128. */
+  int32_t norm_placement; /* llama_norm_placement; llama_block_forward only, the model
+                           * entry points take LLAMA_NORM_PRE */
 } llama_config;
 
 /* Weights of one block, device pointers in config dtype ([P1] "The one

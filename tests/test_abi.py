@@ -42,7 +42,7 @@ def test_header_compiles(lang, compiler, tmp_path):
 
 
 def test_struct_layout_matches_header():
-    assert ctypes.sizeof(L.LlamaConfig) == 44
+    assert ctypes.sizeof(L.LlamaConfig) == 48
     assert ctypes.sizeof(L.BlockWeights) == 9 * 8
     assert ctypes.sizeof(L.ModelWeights) == 5 * 8
 
@@ -59,7 +59,7 @@ def test_hidden_dim_and_status_strings():
 
 def _cfg(**kw):
     base = dict(dim=4096, n_heads=32, hidden=11008, n_layers=32, vocab=32000, max_seq=2048, norm_eps=1e-6,
-                rope_theta=1e4, dtype=L.LLAMA_BF16, numerics=0, n_kv_heads=0)
+                rope_theta=1e4, dtype=L.LLAMA_BF16, numerics=0, n_kv_heads=0, norm_placement=0)
     base.update(kw)
     return L.LlamaConfig(*[base[k] for k, _ in L.LlamaConfig._fields_])
 
@@ -162,3 +162,19 @@ def test_grouped_kv_heads_validation_and_sizes():
         assert lib.llama_decode_pack_size(ctypes.byref(_cfg(n_kv_heads=nkv)), ctypes.byref(n)) == 0
         kvd = nkv * 128
         assert n.value == (32 * ((2 * 4096 + 2 * kvd) * 4096 + 3 * 4096 * 11008) + 32000 * 4096) * 2
+
+
+def test_norm_placement_validation():
+    """Blocks take pre-, post- or no-norm; the model entry points only pre-norm."""
+    lib = L.load()
+    n = ctypes.c_size_t()
+    for placement, st in ((L.NORM_PRE, 0), (L.NORM_POST, 0), (L.NORM_NONE, 0), (3, L.LLAMA_ERR_UNSUPPORTED),
+                          (-1, L.LLAMA_ERR_UNSUPPORTED)):
+        c = _cfg(norm_placement=placement)
+        assert lib.llama_workspace_size(ctypes.byref(c), L.OP_BLOCK_FORWARD, 1, 64, ctypes.byref(n)) == st
+    for placement in (L.NORM_POST, L.NORM_NONE):
+        c = _cfg(norm_placement=placement)
+        assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_FORWARD, 1, 64, ctypes.byref(n)) == \
+            L.LLAMA_ERR_UNSUPPORTED
+        assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 4, 1, ctypes.byref(n)) == \
+            L.LLAMA_ERR_UNSUPPORTED

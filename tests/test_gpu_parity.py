@@ -6,6 +6,7 @@ workloads and 2e-2 for bf16 workloads (fp32 accumulation). Standalone
 attention normalises by RMS(v) instead (its output is a convex combination of
 v rows, whose own RMS shrinks with averaging). Outputs are pre-filled with NaN
 so a tile the kernels forget to write fails the comparison."""
+import ctypes
 import math
 
 import numpy as np
@@ -450,3 +451,80 @@ def test_greedy_generation(wid):
     for i in range(n_new):
         for b in range(B):
             assert want[i, b, forced[b, i]] >= want[i, b].max() - TOL_BF16 * rms
+
+
+# ---------------------------------------------------------------- norm placement
+PLACEMENT = {"post": (L.NORM_POST, O.post_norm_block_forward), "none": (L.NORM_NONE, O.no_norm_block_forward)}
+
+
+@pytest.mark.parametrize("wid", [0, 7, 100])
+@pytest.mark.parametrize("placement", ["post", "none"])
+def test_block_norm_placement(wid, placement):
+    """Post-norm (2017 ordering) and no-norm blocks through llama_block_forward,
+    fp32 (0: d256, 7: d64) and bf16 (100: d512, ragged sequences)."""
+    code, ref = PLACEMENT[placement]
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
+                       norm_placement=code)
+    y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
+    ops().Block(cfg, wt, w.batch, w.seq)(x, y)
+    torch.cuda.synchronize()
+    want = ref(host(x), {k: host(v) for k, v in wt.items()}, w.batch, w.seq, w.n_heads, w.eps, w.theta)
+    err = rel_err(y, want)
+    print(f"{placement}-norm block {w.name}: max|d|/rms = {err:.3e}")
+    assert err < tol_of(w)
+
+
+def test_norm_placement_stack_probe():
+    """The 32-block d64 study stack run block by block on the GPU (fp32): the
+    trunk norm after every block, and the finite-difference amplification of
+    a bump of the input (||F(x + delta u) - F(x)|| / delta) at depths 5, 10,
+    20 and 32, against the oracle on the same weights, input, direction and
+    delta. delta = 1e-3 ||x|| keeps the output difference well above fp32
+    rounding, but the stack amplifies the rounding of both runs as it does the
+    bump (ratios up to ~60 at this delta): ratios agree to 1e-2, norms to
+    1e-4. Without norms the trunk
+    overflows: norms are compared while the oracle's stay below 1e30, and the
+    GPU's must be non-finite wherever the oracle's exceed the fp32 range."""
+    w = I.workload(7)
+    layers = [I.block_weights(w, l, device="cuda") for l in range(w.n_layers)]
+    x = I.block_input(w, device="cuda")
+    u = I.bump_direction(w, device="cuda")
+    delta = 1e-3 * float(torch.linalg.vector_norm(x))
+    hl = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    for placement, code in (("pre", L.NORM_PRE), ("post", L.NORM_POST), ("none", L.NORM_NONE)):
+        cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=torch.float32, eps=w.eps, theta=w.theta,
+                           norm_placement=code)
+        blocks = [ops().Block(cfg, lay, w.batch, w.seq) for lay in layers]
+
+        def run(inp, depth):
+            h, norms = inp, []
+            for blk in blocks[:depth]:
+                h = blk(h).clone()
+                norms.append(float(torch.linalg.vector_norm(h, dim=1).mean()))
+            return h, norms
+
+        y, norms = run(x, w.n_layers)
+        _, want = O.stack_forward(host(x), hl, w.batch, w.seq, w.n_heads, w.eps, placement, w.theta)
+        for l, (g, r) in enumerate(zip(norms, want)):
+            if np.isfinite(r) and r < 1e30:
+                assert abs(g - r) <= 1e-4 * r, (placement, l, g, r)
+            elif not np.isfinite(r) or r > 3.4e38:
+                assert not np.isfinite(g), (placement, l, g, r)
+        if placement == "none":
+            print(f"none: trunk norms {['%.3g' % v for v in norms[:10]]}")
+            continue
+        ratios = []
+        for depth in (5, 10, 20, 32):
+            y0, _ = run(x, depth)
+            y1, _ = run(x + delta * u, depth)
+            torch.cuda.synchronize()
+            got = float(torch.linalg.vector_norm(y1 - y0)) / delta
+            ref = O.amplification(host(x), host(u), delta, hl[:depth], w.batch, w.seq, w.n_heads, w.eps, placement,
+                                  w.theta)
+            assert abs(got - ref) <= 1e-2 * ref, (placement, depth, got, ref)
+            ratios.append(got)
+        print(f"{placement}: trunk norms {['%.3g' % v for v in norms[:20]]}, amplification at depth 5/10/20/32 "
+              f"{['%.3g' % v for v in ratios]}")
