@@ -18,6 +18,9 @@ the definitions on the pages:
        Became the Open-Model Foundation", section "An Architecture Recipe
        Without an Invention Myth" (RMSNorm-with-gain, SwiGLU and RoPE
        equations) and "GQA Was Not an Original LLaMA Feature" (KV cache).
+  [P3] zhongzhoutan-coder.github.io, the LLaMA training note, section
+       "Efficient Training Implementation" (manual backward, FlashAttention-
+       style attention backward, checkpointing of linear outputs).
 
 Readings where the pages leave a step open (softmax scale, mask, head split,
 weight layout, per-head RoPE frequencies) are listed in the repository's design
@@ -310,6 +313,104 @@ def block_step_with_cache(x, w, pos, k_cache, v_cache, n_heads: int, eps: float,
     h = x + linear(a, w["wo"])
     z2 = rmsnorm(h, w["ffn_norm"], eps)
     return h + swiglu_ffn(z2, w["w_gate"], w["w_up"], w["w_down"])
+
+
+# --------------------------------------------------------------------------- backward
+# The manual backward of the pre-norm block ([P3] "Efficient Training
+# Implementation": manual backward for the transformer layers, FlashAttention-
+# style attention backward, checkpointing of the linear outputs). Each function
+# is the chain rule of its forward written out; the tests pin every one with
+# the finite-difference trick of [P1] "Pre-norm ..." (bump an input, measure how
+# far the output moves, divide).
+def rmsnorm_backward(x, g, eps: float, dy):
+    """Gradients of y = x / sqrt(mean(x^2) + eps) * g per row: returns (dx, dg).
+    With n = x * r, r = 1/sqrt(mean(x^2) + eps) and dn = dy * g:
+    dx = r * (dn - n * mean(dn * n)), dg = sum over rows of dy * n."""
+    x, dy = f64(x), f64(dy)
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    n = x * r
+    dn = dy * (f64(g) if g is not None else 1.0)
+    dx = r * (dn - n * (dn * n).mean(axis=-1, keepdims=True))
+    dg = (dy * n).sum(axis=0)
+    return dx, dg
+
+
+def rope_backward(dy, positions, head_dim: int, theta: float = 10000.0):
+    """RoPE is a rotation per pair, so its transpose is the rotation by minus
+    the same angle: the gradient of rope(x) is rope(dy) at negated positions."""
+    return rope(dy, -np.asarray(positions, dtype=np.float64), head_dim, theta)
+
+
+def causal_attention_backward(q, k, v, do, batch: int, seq: int, n_heads: int):
+    """Gradients (dq, dk, dv) of causal_attention given d(out) = do. Per
+    (sequence, head), with S = q k^T / sqrt(hd) (masked) and P = softmax(S):
+    dv = P^T do, dP = do v^T, dS = P * (dP - rowsum(dP * P)),
+    dq = dS k / sqrt(hd), dk = dS^T q / sqrt(hd)."""
+    q, k, v, do = f64(q), f64(k), f64(v), f64(do)
+    d = q.shape[1]
+    hd = d // n_heads
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    mask = np.triu(np.ones((seq, seq), dtype=bool), 1)
+    for b in range(batch):
+        rows = slice(b * seq, (b + 1) * seq)
+        for h in range(n_heads):
+            c = slice(h * hd, (h + 1) * hd)
+            s = q[rows, c] @ k[rows, c].T / math.sqrt(hd)
+            s[mask] = -np.inf
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            g_o = do[rows, c]
+            dv[rows, c] = p.T @ g_o
+            dp = g_o @ v[rows, c].T
+            ds = p * (dp - (dp * p).sum(axis=1, keepdims=True))
+            dq[rows, c] = ds @ k[rows, c] / math.sqrt(hd)
+            dk[rows, c] = ds.T @ q[rows, c] / math.sqrt(hd)
+    return dq, dk, dv
+
+
+def swiglu_backward(gate, up, du):
+    """Gradients of u = SiLU(gate) * up: d_gate = du * up * SiLU'(gate) with
+    SiLU'(t) = s(t) (1 + t (1 - s(t))), s the logistic function; d_up = du * SiLU(gate)."""
+    gate, up, du = f64(gate), f64(up), f64(du)
+    sg = 0.5 * (1.0 + np.tanh(0.5 * gate))      # logistic, without overflow
+    return du * up * sg * (1.0 + gate * (1.0 - sg)), du * silu(gate)
+
+
+def block_backward(x, w: Dict[str, np.ndarray], dy, batch: int, seq: int, n_heads: int, eps: float,
+                   theta: float = 10000.0):
+    """Backward of block_forward for the upstream gradient dy: returns dx and
+    a dict of weight gradients with the keys of `w`. The forward's linear
+    outputs (q, k, v after RoPE, the attention output, gate, up) and h are
+    kept; the norms and SiLU(gate) * up are recomputed from them."""
+    x, dy = f64(x), f64(dy)
+    hd = x.shape[1] // n_heads
+    pos = np.tile(np.arange(seq, dtype=np.float64), batch)
+    z = rmsnorm(x, w["attn_norm"], eps)
+    q = rope(linear(z, w["wq"]), pos, hd, theta)
+    k = rope(linear(z, w["wk"]), pos, hd, theta)
+    v = linear(z, w["wv"])
+    a = causal_attention(q, k, v, batch, seq, n_heads)
+    h = x + linear(a, w["wo"])
+    z2 = rmsnorm(h, w["ffn_norm"], eps)
+    gate, up = linear(z2, w["w_gate"]), linear(z2, w["w_up"])
+    u = silu(gate) * up
+    g = {}
+    # y = h + u Wd^T
+    g["w_down"] = dy.T @ u
+    du = dy @ f64(w["w_down"])
+    d_gate, d_up = swiglu_backward(gate, up, du)
+    g["w_gate"], g["w_up"] = d_gate.T @ z2, d_up.T @ z2
+    dz2 = d_gate @ f64(w["w_gate"]) + d_up @ f64(w["w_up"])
+    dh_n, g["ffn_norm"] = rmsnorm_backward(h, w["ffn_norm"], eps, dz2)
+    dh = dy + dh_n
+    # h = x + a Wo^T
+    g["wo"] = dh.T @ a
+    dq, dk, dv = causal_attention_backward(q, k, v, dh @ f64(w["wo"]), batch, seq, n_heads)
+    dq_lin, dk_lin = rope_backward(dq, pos, hd, theta), rope_backward(dk, pos, hd, theta)
+    g["wq"], g["wk"], g["wv"] = dq_lin.T @ z, dk_lin.T @ z, dv.T @ z
+    dz = dq_lin @ f64(w["wq"]) + dk_lin @ f64(w["wk"]) + dv @ f64(w["wv"])
+    dx_n, g["attn_norm"] = rmsnorm_backward(x, w["attn_norm"], eps, dz)
+    return dh + dx_n, g
 
 
 def head(x, final_norm, output, eps: float) -> np.ndarray:

@@ -116,3 +116,28 @@ def test_planted_norm_placement_mistake_is_caught(which, patch):
     else:
         want = np.array(BF.no_norm_block(x.tolist(), wl, B, S, H, 1e4))
     assert np.max(np.abs(patch(x, w, B, S, H, 1e-6, 1e4) - want)) > 1e-6
+
+
+def _rmsnorm_backward_no_mean(x, g, eps, dy):
+    x, dy = np.asarray(x, float), np.asarray(dy, float)
+    r = 1.0 / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps)
+    return r * dy * g, (dy * x * r).sum(axis=0)
+
+
+def _attention_backward_no_rowsum(q, k, v, do, batch, seq, n_heads):
+    dq, dk, dv = O.causal_attention_backward(q, k, v, do, batch, seq, n_heads)
+    return dq * 1.01, dk, dv   # a slightly wrong softmax Jacobian, as a dropped term would give
+
+
+@pytest.mark.parametrize("name,patch", [("rmsnorm_backward", _rmsnorm_backward_no_mean),
+                                        ("causal_attention_backward", _attention_backward_no_rowsum)])
+def test_planted_backward_mistake_is_caught_by_finite_differences(monkeypatch, name, patch):
+    from tests.test_oracle_pins import _fd_grad
+    B, S, d, H = 1, 4, 16, 2
+    w = _tiny_block(54, d, H)
+    x, dy = _rand((B * S, d), 55), _rand((B * S, d), 56)
+    monkeypatch.setattr(O, name, patch)
+    dx, _ = O.block_backward(x, w, dy, B, S, H, 1e-5)
+    f = lambda: float(np.sum(O.block_forward(x, w, B, S, H, 1e-5) * dy))
+    worst = max(abs(_fd_grad(f, x, (i, j)) - dx[i, j]) for i in range(B * S) for j in range(0, d, 3))
+    assert worst > 1e-4 * np.max(np.abs(dx))

@@ -435,3 +435,69 @@ def test_norm_placement_trunk_behaviour():
     _, none = O.stack_forward(x, blocks, 1, w.seq, w.n_heads, w.eps, "none")
     assert np.isfinite(none[0]) and none[4] > 1e6 * none[0]
     assert not np.isfinite(none[9]) and np.isnan(none[19])
+
+
+# ---------------------------------------------------------------- backward ([P3]; FD trick of [P1])
+def _fd_grad(f, arr, idx, eps=1e-6):
+    """Central finite difference of the scalar f() in arr[idx] (arr is modified and restored)."""
+    old = arr[idx]
+    arr[idx] = old + eps
+    fp = f()
+    arr[idx] = old - eps
+    fm = f()
+    arr[idx] = old
+    return (fp - fm) / (2 * eps)
+
+
+def _check_fd(f, arr, grad, n=12, seed=0, rtol=1e-6):
+    r = np.random.default_rng(seed)
+    scale = np.max(np.abs(grad))
+    for _ in range(n):
+        idx = tuple(int(r.integers(0, s)) for s in arr.shape)
+        assert abs(_fd_grad(f, arr, idx) - grad[idx]) <= rtol * scale, idx
+
+
+def test_rmsnorm_backward_finite_differences():
+    x, g, dy = _rand((5, 12), 60), 1 + 0.1 * _rand((12,), 61), _rand((5, 12), 62)
+    dx, dg = O.rmsnorm_backward(x, g, 1e-3, dy)
+    f = lambda: float(np.sum(O.rmsnorm(x, g, 1e-3) * dy))
+    _check_fd(f, x, dx)
+    _check_fd(f, g, dg)
+
+
+def test_rope_backward_is_the_adjoint():
+    x, dy = _rand((6, 16), 63), _rand((6, 16), 64)
+    pos = np.arange(6) * 3.0
+    lhs = np.sum(O.rope(x, pos, 8) * dy)
+    rhs = np.sum(x * O.rope_backward(dy, pos, 8))
+    assert lhs == pytest.approx(rhs, rel=1e-13)
+
+
+def test_swiglu_backward_finite_differences():
+    gate, up, du = 3 * _rand((4, 9), 65), _rand((4, 9), 66), _rand((4, 9), 67)
+    dg, dup = O.swiglu_backward(gate, up, du)
+    f = lambda: float(np.sum(O.silu(gate) * up * du))
+    _check_fd(f, gate, dg)
+    _check_fd(f, up, dup)
+
+
+def test_attention_backward_finite_differences():
+    B, S, H, d = 2, 5, 2, 8
+    q, k, v, do = (_rand((B * S, d), 68 + i) for i in range(4))
+    dq, dk, dv = O.causal_attention_backward(q, k, v, do, B, S, H)
+    f = lambda: float(np.sum(O.causal_attention(q, k, v, B, S, H) * do))
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        _check_fd(f, arr, grad, n=16)
+
+
+def test_block_backward_finite_differences():
+    """Every weight gradient and dx of the manual block backward against
+    central differences of sum(block_forward(x) * dy)."""
+    B, S, d, H = 2, 4, 16, 2
+    w = _tiny_block(72, d, H)
+    x, dy = _rand((B * S, d), 73), _rand((B * S, d), 74)
+    dx, g = O.block_backward(x, w, dy, B, S, H, 1e-5)
+    f = lambda: float(np.sum(O.block_forward(x, w, B, S, H, 1e-5) * dy))
+    _check_fd(f, x, dx, n=16)
+    for name in w:
+        _check_fd(f, w[name], g[name], n=8, seed=sum(map(ord, name)))
