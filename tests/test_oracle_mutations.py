@@ -9,7 +9,7 @@ from oracle import llama_oracle as O
 from tests import brute_force as BF
 from tests.test_oracle_pins import _rand, _tiny_block
 
-_rope, _attn = O.rope, O.causal_attention
+_rope, _attn, _attn_bwd = O.rope, O.causal_attention, O.causal_attention_backward
 
 
 def rope_wrong_sign(x, positions, head_dim, theta=10000.0):
@@ -125,7 +125,7 @@ def _rmsnorm_backward_no_mean(x, g, eps, dy):
 
 
 def _attention_backward_no_rowsum(q, k, v, do, batch, seq, n_heads):
-    dq, dk, dv = O.causal_attention_backward(q, k, v, do, batch, seq, n_heads)
+    dq, dk, dv = _attn_bwd(q, k, v, do, batch, seq, n_heads)
     return dq * 1.01, dk, dv   # a slightly wrong softmax Jacobian, as a dropped term would give
 
 
