@@ -18,6 +18,7 @@ LLAMA_OK = 0
 LLAMA_ERR_NULL, LLAMA_ERR_SHAPE, LLAMA_ERR_DTYPE, LLAMA_ERR_WORKSPACE = -1, -2, -3, -4
 LLAMA_ERR_POSITION, LLAMA_ERR_UNSUPPORTED, LLAMA_ERR_HIP = -5, -6, -7
 OP_CAUSAL_ATTN, OP_SWIGLU_FFN, OP_BLOCK_FORWARD, OP_MODEL_FORWARD, OP_MODEL_DECODE = 1, 2, 3, 4, 5
+OP_CAUSAL_ATTN_BACKWARD, OP_BLOCK_BACKWARD = 6, 7
 
 NUM_DEFAULT = 0
 NUM_EXPLICIT = 1 << 31
@@ -31,6 +32,8 @@ EXPORTS = (
     "llama_swiglu_ffn", "llama_block_forward", "llama_model_forward", "llama_model_decode",
     "llama_workspace_size", "llama_status_string", "llama_last_error", "llama_trace_begin", "llama_trace_end",
     "llama_trace_label", "llama_argmax", "llama_decode_pack_size", "llama_pack_decode_weights",
+    "llama_causal_attn_backward", "llama_block_train_saved_size", "llama_block_train_forward",
+    "llama_block_backward", "llama_axpby",
 )
 
 
@@ -84,6 +87,12 @@ def load() -> ctypes.CDLL:
         "llama_argmax": [vp, i64, i32, vp, vp],
         "llama_decode_pack_size": [cfgp, ctypes.POINTER(sz)],
         "llama_pack_decode_weights": [cfgp, ctypes.POINTER(ModelWeights), vp, sz, vp],
+        "llama_causal_attn_backward": [i32, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp],
+        "llama_block_train_saved_size": [cfgp, i32, i32, ctypes.POINTER(sz)],
+        "llama_block_train_forward": [cfgp, ctypes.POINTER(BlockWeights), vp, vp, vp, sz, i32, i32, vp, sz, vp],
+        "llama_block_backward": [cfgp, ctypes.POINTER(BlockWeights), vp, vp, sz, vp, vp, ctypes.POINTER(BlockWeights),
+                                 i32, i32, vp, sz, vp],
+        "llama_axpby": [vp, vp, vp, f32, f32, i64, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -303,6 +303,57 @@ DecodeWs carve_decode(Carve &cv, const llama_config *c, int batch) {
   return w;
 }
 
+// ------------------------------------------------------------------ training layouts
+// Activations kept by the training forward (fp32): the linear outputs and h.
+struct TrainSaved {
+  float *q, *k, *v, *a, *h, *gate, *up, *lse;
+};
+TrainSaved carve_saved(Carve &cv, const llama_config *c, int batch, int seq) {
+  const size_t n = (size_t)batch * seq, d = c->dim, hid = c->hidden;
+  TrainSaved t{};
+  t.q = cv.take<float>(n * d);
+  t.k = cv.take<float>(n * d);
+  t.v = cv.take<float>(n * d);
+  t.a = cv.take<float>(n * d);
+  t.h = cv.take<float>(n * d);
+  t.gate = cv.take<float>(n * hid);
+  t.up = cv.take<float>(n * hid);
+  t.lse = cv.take<float>((size_t)batch * c->n_heads * seq);
+  return t;
+}
+
+// Backward workspace: recomputed norms and SiLU(gate)*up, gradient buffers.
+struct BwdWs {
+  float *z1, *z2, *u, *du, *dup, *dz, *dh, *da, *dq, *dk, *dv, *delta, *rstd;
+};
+BwdWs carve_backward(Carve &cv, const llama_config *c, int batch, int seq) {
+  const size_t n = (size_t)batch * seq, d = c->dim, hid = c->hidden;
+  BwdWs w{};
+  w.z1 = cv.take<float>(n * d);
+  w.z2 = cv.take<float>(n * d);
+  w.u = cv.take<float>(n * hid);
+  w.du = cv.take<float>(n * hid);
+  w.dup = cv.take<float>(n * hid);
+  w.dz = cv.take<float>(n * d);
+  w.dh = cv.take<float>(n * d);
+  w.da = cv.take<float>(n * d);
+  w.dq = cv.take<float>(n * d);
+  w.dk = cv.take<float>(n * d);
+  w.dv = cv.take<float>(n * d);
+  w.delta = cv.take<float>((size_t)batch * c->n_heads * seq);
+  w.rstd = cv.take<float>(n);
+  return w;
+}
+
+// fp32 pre-norm blocks with one K/V head per query head.
+int check_train_cfg(const llama_config *c, int batch, int seq) {
+  const int st = check_block_cfg(c, batch, seq);
+  if (st) return st;
+  if (c->dtype != LLAMA_F32 || c->norm_placement != LLAMA_NORM_PRE || kv_heads(c) != c->n_heads)
+    return LLAMA_ERR_UNSUPPORTED;
+  return LLAMA_OK;
+}
+
 size_t ws_bytes_of(const llama_config *c, int op, int batch, int seq) {
   Carve cv(nullptr);
   const int64_t n = (int64_t)batch * seq;
@@ -338,6 +389,14 @@ size_t ws_bytes_of(const llama_config *c, int op, int batch, int seq) {
       break;
     case LLAMA_OP_MODEL_DECODE:
       carve_decode(cv, c, batch);
+      break;
+    case LLAMA_OP_CAUSAL_ATTN_BACKWARD:
+      cv.take<float>(n * c->dim);                                 // recomputed output
+      cv.take<float>((size_t)batch * c->n_heads * seq);           // log-sum-exp
+      cv.take<float>((size_t)batch * c->n_heads * seq);           // rowsum(dout * out)
+      break;
+    case LLAMA_OP_BLOCK_BACKWARD:
+      carve_backward(cv, c, batch, seq);
       break;
     default:
       return 0;
@@ -580,6 +639,143 @@ const char *llama_status_string(int st) {
 
 const char *llama_last_error(void) { return g_last_error.c_str(); }
 
+int llama_causal_attn_backward(int dtype, const void *q, const void *k, const void *v, const void *dout,
+                               void *dq, void *dk, void *dv, int batch, int seq, int n_heads, int head_dim,
+                               void *ws, size_t ws_bytes, void *stream) {
+  if (!q || !k || !v || !dout || !dq || !dk || !dv) return LLAMA_ERR_NULL;
+  if (!dtype_ok(dtype)) return LLAMA_ERR_DTYPE;
+  if (batch <= 0 || seq <= 0 || n_heads <= 0 || head_dim <= 0) return LLAMA_ERR_SHAPE;
+  if (dtype != LLAMA_F32 || (head_dim != 64 && head_dim != 128)) return LLAMA_ERR_UNSUPPORTED;
+  if ((int64_t)batch * seq > (1 << 24)) return LLAMA_ERR_SHAPE;
+  llama_config c{};
+  c.dim = n_heads * head_dim;
+  c.n_heads = n_heads;
+  c.dtype = dtype;
+  if (!ws || ws_bytes < ws_bytes_of(&c, LLAMA_OP_CAUSAL_ATTN_BACKWARD, batch, seq)) return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  Carve cv(ws);
+  const int64_t n = (int64_t)batch * seq;
+  float *o = cv.take<float>(n * c.dim);
+  float *lse = cv.take<float>((size_t)batch * n_heads * seq);
+  float *delta = cv.take<float>((size_t)batch * n_heads * seq);
+  const float *qf = (const float *)q, *kf = (const float *)k, *vf = (const float *)v;
+  HIP_TRY(attn_f32_launch(qf, kf, vf, o, batch, seq, n_heads, head_dim, s, lse), "attention (recomputed)");
+  HIP_TRY(attn_bwd_launch(qf, kf, vf, o, (const float *)dout, lse, delta, (float *)dq, (float *)dk, (float *)dv,
+                          batch, seq, n_heads, head_dim, s),
+          "attention backward");
+  return LLAMA_OK;
+}
+
+int llama_block_train_saved_size(const llama_config *c, int batch, int seq, size_t *bytes) {
+  if (!c || !bytes) return LLAMA_ERR_NULL;
+  const int st = check_train_cfg(c, batch, seq);
+  if (st) return st;
+  Carve cv(nullptr);
+  carve_saved(cv, c, batch, seq);
+  *bytes = cv.off + 256;
+  return LLAMA_OK;
+}
+
+int llama_block_train_forward(const llama_config *c, const llama_block_weights *w, const float *x, float *y,
+                              void *saved, size_t saved_bytes, int batch, int seq, void *ws, size_t ws_bytes,
+                              void *stream) {
+  int st = check_train_cfg(c, batch, seq);
+  if (st) return st;
+  if ((st = check_block_w(w))) return st;
+  if (!x || !y || !saved) return LLAMA_ERR_NULL;
+  size_t need_saved = 0;
+  llama_block_train_saved_size(c, batch, seq, &need_saved);
+  if (saved_bytes < need_saved || !ws || ws_bytes < ws_bytes_of(c, LLAMA_OP_BLOCK_BACKWARD, batch, seq))
+    return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq, hid = c->hidden;
+  Carve cs(saved), cw(ws);
+  const TrainSaved t = carve_saved(cs, c, batch, seq);
+  const BwdWs b = carve_backward(cw, c, batch, seq);
+  HIP_TRY(rmsnorm_launch(1, 1, x, w->attn_norm, b.z1, M, d, c->norm_eps, s), "rmsnorm");
+  HIP_TRY(gemm_f32_launch(b.z1, (const float *)w->wq, t.q, nullptr, M, d, d, s), "q projection");
+  HIP_TRY(gemm_f32_launch(b.z1, (const float *)w->wk, t.k, nullptr, M, d, d, s), "k projection");
+  HIP_TRY(gemm_f32_launch(b.z1, (const float *)w->wv, t.v, nullptr, M, d, d, s), "v projection");
+  HIP_TRY(rope_launch(1, t.q, t.q, nullptr, M, H, hd, c->rope_theta, seq, s), "rope q");
+  HIP_TRY(rope_launch(1, t.k, t.k, nullptr, M, H, hd, c->rope_theta, seq, s), "rope k");
+  HIP_TRY(attn_f32_launch(t.q, t.k, t.v, t.a, batch, seq, H, hd, s, t.lse), "attention");
+  HIP_TRY(gemm_f32_launch(t.a, (const float *)w->wo, t.h, x, M, d, d, s), "output projection");
+  HIP_TRY(rmsnorm_launch(1, 1, t.h, w->ffn_norm, b.z2, M, d, c->norm_eps, s), "rmsnorm");
+  HIP_TRY(gemm_f32_launch(b.z2, (const float *)w->w_gate, t.gate, nullptr, M, hid, d, s), "gate");
+  HIP_TRY(gemm_f32_launch(b.z2, (const float *)w->w_up, t.up, nullptr, M, hid, d, s), "up");
+  HIP_TRY(silu_mul_f32_launch(t.gate, t.up, b.u, (int64_t)M * hid, s), "silu");
+  HIP_TRY(gemm_f32_launch(b.u, (const float *)w->w_down, y, t.h, M, d, hid, s), "down projection");
+  return LLAMA_OK;
+}
+
+int llama_block_backward(const llama_config *c, const llama_block_weights *w, const float *x, const void *saved,
+                         size_t saved_bytes, const float *dy, float *dx, const llama_block_weights *grads,
+                         int batch, int seq, void *ws, size_t ws_bytes, void *stream) {
+  int st = check_train_cfg(c, batch, seq);
+  if (st) return st;
+  if ((st = check_block_w(w)) || (st = check_block_w(grads))) return st;
+  if (!x || !saved || !dy || !dx) return LLAMA_ERR_NULL;
+  size_t need_saved = 0;
+  llama_block_train_saved_size(c, batch, seq, &need_saved);
+  if (saved_bytes < need_saved || !ws || ws_bytes < ws_bytes_of(c, LLAMA_OP_BLOCK_BACKWARD, batch, seq))
+    return LLAMA_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq, hid = c->hidden;
+  Carve cs((void *)saved), cw(ws);
+  const TrainSaved t = carve_saved(cs, c, batch, seq);
+  const BwdWs b = carve_backward(cw, c, batch, seq);
+  auto W = [](const void *p) { return (const float *)p; };
+  auto G = [](const void *p) { return (float *)p; };
+  // C = A B with A [m, k] and B [k, n] row-major
+  auto nn = [&](const float *A, const float *B, float *C, int m, int n, int k, int acc) {
+    return gemm_f32_strided_launch(A, k, 1, B, n, 1, C, m, n, k, acc, s);
+  };
+  // C [n_out, k_in] = X^T Y with X [tokens, n_out], Y [tokens, k_in] row-major (a weight gradient)
+  auto tn = [&](const float *X, const float *Y, float *C, int n_out, int k_in) {
+    return gemm_f32_strided_launch(X, 1, n_out, Y, k_in, 1, C, n_out, k_in, M, 0, s);
+  };
+  // recomputed: the two norm outputs and SiLU(gate) * up
+  HIP_TRY(rmsnorm_launch(1, 1, x, w->attn_norm, b.z1, M, d, c->norm_eps, s), "rmsnorm");
+  HIP_TRY(rmsnorm_launch(1, 1, t.h, w->ffn_norm, b.z2, M, d, c->norm_eps, s), "rmsnorm");
+  HIP_TRY(silu_mul_f32_launch(t.gate, t.up, b.u, (int64_t)M * hid, s), "silu");
+  // y = h + u Wd^T
+  HIP_TRY(tn(dy, b.u, G(grads->w_down), d, hid), "down weight gradient");
+  HIP_TRY(nn(dy, W(w->w_down), b.du, M, hid, d, 0), "down input gradient");
+  HIP_TRY(swiglu_bwd_launch(t.gate, t.up, b.du, b.du, b.dup, (int64_t)M * hid, s), "silu backward");
+  HIP_TRY(tn(b.du, b.z2, G(grads->w_gate), hid, d), "gate weight gradient");
+  HIP_TRY(tn(b.dup, b.z2, G(grads->w_up), hid, d), "up weight gradient");
+  HIP_TRY(nn(b.du, W(w->w_gate), b.dz, M, d, hid, 0), "gate input gradient");
+  HIP_TRY(nn(b.dup, W(w->w_up), b.dz, M, d, hid, 1), "up input gradient");
+  // z2 = RMSNorm(h; g2); dh = dy + its gradient
+  HIP_TRY(rmsnorm_bwd_launch(t.h, W(w->ffn_norm), b.dz, dy, b.dh, G(grads->ffn_norm), b.rstd, M, d, c->norm_eps, s),
+          "ffn norm backward");
+  // h = x + a Wo^T
+  HIP_TRY(tn(b.dh, t.a, G(grads->wo), d, d), "output weight gradient");
+  HIP_TRY(nn(b.dh, W(w->wo), b.da, M, d, d, 0), "output input gradient");
+  HIP_TRY(attn_bwd_launch(t.q, t.k, t.v, t.a, b.da, t.lse, b.delta, b.dq, b.dk, b.dv, batch, seq, H, hd, s),
+          "attention backward");
+  HIP_TRY(rope_launch(1, b.dq, b.dq, nullptr, M, H, hd, c->rope_theta, seq, s, 1), "rope backward");
+  HIP_TRY(rope_launch(1, b.dk, b.dk, nullptr, M, H, hd, c->rope_theta, seq, s, 1), "rope backward");
+  HIP_TRY(tn(b.dq, b.z1, G(grads->wq), d, d), "q weight gradient");
+  HIP_TRY(tn(b.dk, b.z1, G(grads->wk), d, d), "k weight gradient");
+  HIP_TRY(tn(b.dv, b.z1, G(grads->wv), d, d), "v weight gradient");
+  HIP_TRY(nn(b.dq, W(w->wq), b.dz, M, d, d, 0), "q input gradient");
+  HIP_TRY(nn(b.dk, W(w->wk), b.dz, M, d, d, 1), "k input gradient");
+  HIP_TRY(nn(b.dv, W(w->wv), b.dz, M, d, d, 1), "v input gradient");
+  // z1 = RMSNorm(x; g1); dx = dh + its gradient
+  HIP_TRY(rmsnorm_bwd_launch(x, W(w->attn_norm), b.dz, b.dh, dx, G(grads->attn_norm), b.rstd, M, d, c->norm_eps, s),
+          "attention norm backward");
+  return LLAMA_OK;
+}
+
+int llama_axpby(float *z, const float *x, const float *y, float a, float b, int64_t n, void *stream) {
+  if (!z || !x || !y) return LLAMA_ERR_NULL;
+  if (n < 0) return LLAMA_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(axpby_launch(z, x, y, a, b, n, s), "axpby");
+  return LLAMA_OK;
+}
+
 int llama_trace_begin(void *const *events, int capacity) {
   if (!events && capacity > 0) return LLAMA_ERR_NULL;
   if (capacity < 0) return LLAMA_ERR_SHAPE;
@@ -630,6 +826,14 @@ int llama_workspace_size(const llama_config *c, int op, int batch, int seq, size
     case LLAMA_OP_MODEL_DECODE:
       st = check_model_cfg(c, batch, 1);
       if (!st && (batch > 32 || c->max_seq > kDecMaxSeq)) st = LLAMA_ERR_UNSUPPORTED;
+      break;
+    case LLAMA_OP_CAUSAL_ATTN_BACKWARD:
+      if (!dtype_ok(c->dtype)) return LLAMA_ERR_DTYPE;
+      if (c->dim <= 0 || c->n_heads <= 0 || c->dim % c->n_heads || batch <= 0 || seq <= 0) return LLAMA_ERR_SHAPE;
+      if (c->dtype != LLAMA_F32) return LLAMA_ERR_UNSUPPORTED;
+      break;
+    case LLAMA_OP_BLOCK_BACKWARD:
+      st = check_train_cfg(c, batch, seq);
       break;
     default:
       return LLAMA_ERR_UNSUPPORTED;

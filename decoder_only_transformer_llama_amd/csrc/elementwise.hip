@@ -217,7 +217,7 @@ hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g,
 // ------------------------------------------------------------------ RoPE
 template <bool F32>
 __global__ void rope_kernel(const void *x, void *y, const int32_t *pos, int64_t tokens, int n_heads,
-                            int hd, double theta, int seq_mod) {
+                            int hd, double theta, int seq_mod, double sign) {
   const int half = hd >> 1;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t per_tok = (int64_t)n_heads * half;
@@ -226,7 +226,7 @@ __global__ void rope_kernel(const void *x, void *y, const int32_t *pos, int64_t 
   const int rem = (int)(idx % per_tok);
   const int h = rem / half, i = rem % half;
   const int p = pos ? pos[t] : (int)(t % seq_mod);
-  const double ang = (double)p * pow(theta, -(2.0 * i) / hd);
+  const double ang = sign * (double)p * pow(theta, -(2.0 * i) / hd);   // sign -1: the inverse rotation
   double sn, cs;
   sincos(ang, &sn, &cs);
   const float c = (float)cs, sv = (float)sn;
@@ -250,16 +250,17 @@ __global__ void rope_kernel(const void *x, void *y, const int32_t *pos, int64_t 
 }
 
 hipError_t rope_launch(int f32, const void *x, void *y, const int32_t *pos, int64_t tokens, int n_heads,
-                       int head_dim, float theta, int seq_mod, hipStream_t s) {
+                       int head_dim, float theta, int seq_mod, hipStream_t s, int inverse) {
+  const double sign = inverse ? -1.0 : 1.0;
   const int64_t n = tokens * n_heads * (head_dim / 2);
   if (n == 0) return hipSuccess;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (f32)
     hipLaunchKernelGGL(rope_kernel<true>, grid, dim3(256), 0, s, x, y, pos, tokens, n_heads, head_dim,
-                       (double)theta, seq_mod);
+                       (double)theta, seq_mod, sign);
   else
     hipLaunchKernelGGL(rope_kernel<false>, grid, dim3(256), 0, s, x, y, pos, tokens, n_heads, head_dim,
-                       (double)theta, seq_mod);
+                       (double)theta, seq_mod, sign);
   return hipGetLastError();
 }
 
@@ -416,7 +417,7 @@ hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64
 // Causal attention in fp32, one thread per (sequence, head, query), online softmax.
 template <int HD>
 __global__ __launch_bounds__(64) void attn_f32_kernel(const float *q, const float *k, const float *v,
-                                                      float *o, int batch, int seq, int n_heads) {
+                                                      float *o, float *lse, int batch, int seq, int n_heads) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= batch * n_heads * seq) return;
   const int i = idx % seq, h = (idx / seq) % n_heads, b = idx / (seq * n_heads);
@@ -447,17 +448,18 @@ __global__ __launch_bounds__(64) void attn_f32_kernel(const float *q, const floa
   float *oi = o + ((int64_t)b * seq + i) * d + h * HD;
 #pragma unroll
   for (int e = 0; e < HD; ++e) oi[e] = acc[e] / l;
+  if (lse) lse[idx] = m + logf(l);   // [batch][n_heads][seq]: the backward's softmax statistic
 }
 
 hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float *o, int batch, int seq,
-                           int n_heads, int head_dim, hipStream_t s) {
+                           int n_heads, int head_dim, hipStream_t s, float *lse) {
   const int n = batch * n_heads * seq;
   if (n == 0) return hipSuccess;
   const dim3 grid((n + 63) / 64);
   if (head_dim == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, o, batch, seq, n_heads);
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, o, lse, batch, seq, n_heads);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, o, batch, seq, n_heads);
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, o, lse, batch, seq, n_heads);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

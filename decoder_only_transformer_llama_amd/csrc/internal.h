@@ -105,8 +105,9 @@ hipError_t resid_sum_launch(const float *r, const float *part, int n_parts, int6
 hipError_t rmsnorm_launch(int in_f32, int out_f32, const void *x, const void *g, void *y, int64_t rows,
                           int dim, float eps, hipStream_t s, int g_f32 = -1);
 // pos == nullptr: the position of token t is t % seq_mod.
+// inverse: rotate by minus the angle (the transpose of RoPE, for its gradient).
 hipError_t rope_launch(int f32, const void *x, void *y, const int32_t *pos, int64_t tokens, int n_heads,
-                       int head_dim, float theta, int seq_mod, hipStream_t s);
+                       int head_dim, float theta, int seq_mod, hipStream_t s, int inverse = 0);
 hipError_t attn_pack_launch(int in_f32, const void *q, const void *k, const void *v, uint16_t *qh,
                             uint16_t *ql, uint16_t *kh, uint16_t *kl, uint16_t *vth, uint16_t *vtl,
                             int batch, int seq, int n_heads, int head_dim, int vt_stride, hipStream_t s);
@@ -117,8 +118,9 @@ hipError_t embed_launch(int w_f32, const void *emb, const int32_t *tokens, int64
 hipError_t gemm_f32_launch(const float *A, const float *B, float *C, const float *R, int M, int N, int K,
                            hipStream_t s);
 hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64_t n, hipStream_t s);
+// lse (optional): [batch][n_heads][seq] log-sum-exp of each query's scaled scores.
 hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float *o, int batch, int seq,
-                           int n_heads, int head_dim, hipStream_t s);
+                           int n_heads, int head_dim, hipStream_t s, float *lse = nullptr);
 hipError_t convert_launch(int in_f32, int out_f32, const void *x, void *y, int64_t n, hipStream_t s);
 
 // ---------------------------------------------------------------- decode
@@ -174,6 +176,22 @@ hipError_t dec_gateup_combine_launch(const DecodeArgs &d, const float *part, int
                                      const float *ss, uint16_t *u_hi, uint16_t *u_lo, hipStream_t s);
 hipError_t dec_head_combine_launch(const DecodeArgs &d, const float *part, int splits, const float *ss,
                                    float *logits, hipStream_t s);
+
+// ------------------------------------------------------------------ backward (fp32)
+// C[m, n] = (accumulate ? C : 0) + sum_k A[m*sam + k*sak] B[k*sbk + n*sbn]
+hipError_t gemm_f32_strided_launch(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk,
+                                   int64_t sbn, float *C, int M, int N, int K, int accumulate, hipStream_t s);
+// dq, dk, dv of causal attention from q, k, v, the forward output o, its
+// log-sum-exp lse [batch][n_heads][seq] and dout; delta: scratch of the lse's size.
+hipError_t attn_bwd_launch(const float *q, const float *k, const float *v, const float *o, const float *dout,
+                           const float *lse, float *delta, float *dq, float *dk, float *dv, int batch, int seq,
+                           int n_heads, int head_dim, hipStream_t s);
+// dx = add + gradient of RMSNorm(x; g) for dy; dg = its gain gradient; rstd: [rows] scratch.
+hipError_t rmsnorm_bwd_launch(const float *x, const float *g, const float *dy, const float *add, float *dx,
+                              float *dg, float *rstd, int64_t rows, int dim, float eps, hipStream_t s);
+hipError_t swiglu_bwd_launch(const float *gate, const float *up, const float *du, float *d_gate, float *d_up,
+                             int64_t n, hipStream_t s);
+hipError_t axpby_launch(float *z, const float *x, const float *y, float a, float b, int64_t n, hipStream_t s);
 
 
 }  // namespace llama

@@ -117,6 +117,9 @@ TEST_WORKLOADS: Dict[int, Workload] = {
     # grouped-query model, head_dim 128, groups of 4
     105: Workload(105, "test-model-bf16-gqa", dim=1024, n_heads=8, hidden=2816, batch=3, seq=40, dtype="bf16",
                   n_layers=2, vocab=1000, max_seq=64, gain_std=0.1, n_kv_heads=2),
+    # fp32 training block: head_dim 128, two sequences of a ragged length
+    107: Workload(107, "test-train-block-f32", dim=256, n_heads=2, hidden=768, batch=2, seq=37, dtype="f32",
+                  gain_std=0.1),
     # multi-query model (one key/value head), head_dim 128, groups of 4
     106: Workload(106, "test-model-bf16-mqa", dim=512, n_heads=4, hidden=1536, batch=2, seq=24, dtype="bf16",
                   n_layers=2, vocab=500, max_seq=48, n_kv_heads=1),

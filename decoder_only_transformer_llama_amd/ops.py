@@ -112,6 +112,19 @@ def causal_attn(q, k, v, batch: int, seq: int, n_heads: int,
     return o
 
 
+def causal_attn_backward(q, k, v, dout, batch: int, seq: int, n_heads: int):
+    """(dq, dk, dv) of causal_attn for the output gradient dout (fp32)."""
+    _dev(q, k, v, dout)
+    d = q.shape[-1]
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    cfg = config(d, n_heads, 1, dtype=q.dtype)
+    ws = _ws(workspace_bytes(cfg, L.OP_CAUSAL_ATTN_BACKWARD, batch, seq), q.device)
+    L.check(L.load().llama_causal_attn_backward(_dt(q), _p(q), _p(k), _p(v), _p(dout), _p(dq), _p(dk), _p(dv), batch,
+                                                seq, n_heads, d // n_heads, _p(ws), ws.numel(), _stream()),
+            "llama_causal_attn_backward")
+    return dq, dk, dv
+
+
 def swiglu_ffn(z, w_gate, w_up, w_down, out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     _dev(z, w_gate, w_up, w_down)
     tokens, dim = z.shape
@@ -161,6 +174,61 @@ class Block:
         L.check(L.load().llama_block_forward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _dt(x), _p(x),
                                              _p(y), self.batch, self.seq, _p(self.ws), self.ws.numel(), _stream()),
                 "llama_block_forward")
+        return y
+
+
+def axpby(z: torch.Tensor, x: torch.Tensor, y: torch.Tensor, a: float, b: float) -> torch.Tensor:
+    """z = a x + b y over fp32 tensors of one size (z may be x or y)."""
+    _dev(z, x, y)
+    L.check(L.load().llama_axpby(_p(z), _p(x), _p(y), a, b, z.numel(), _stream()), "llama_axpby")
+    return z
+
+
+class TrainBlock:
+    """An fp32 block for training: forward keeping the linear outputs,
+    manual backward into gradient buffers, and an SGD step, all in the
+    library's kernels. Weights are updated in place."""
+
+    def __init__(self, cfg: L.LlamaConfig, weights: Dict[str, torch.Tensor], batch: int, seq: int):
+        self.cfg, self.weights, self.batch, self.seq = cfg, weights, batch, seq
+        dev = weights["wq"].device
+        self.wstruct = block_weights_struct(weights)
+        self.grads = {k: torch.zeros_like(weights[k]) for k in BLOCK_KEYS}
+        self.gstruct = block_weights_struct(self.grads)
+        n = ctypes.c_size_t(0)
+        L.check(L.load().llama_block_train_saved_size(ctypes.byref(cfg), batch, seq, ctypes.byref(n)),
+                "llama_block_train_saved_size")
+        self.saved = _ws(n.value, dev)
+        self.ws = _ws(workspace_bytes(cfg, L.OP_BLOCK_BACKWARD, batch, seq), dev)
+        self.y = torch.empty((batch * seq, cfg.dim), dtype=torch.float32, device=dev)
+        self.dx = torch.empty_like(self.y)
+        self.dy = torch.empty_like(self.y)
+
+    def forward(self, x: torch.Tensor) -> torch.Tensor:
+        _dev(x)
+        L.check(L.load().llama_block_train_forward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(x), _p(self.y),
+                                                   _p(self.saved), self.saved.numel(), self.batch, self.seq,
+                                                   _p(self.ws), self.ws.numel(), _stream()),
+                "llama_block_train_forward")
+        return self.y
+
+    def backward(self, x: torch.Tensor, dy: torch.Tensor) -> torch.Tensor:
+        """dx for the upstream gradient dy; weight gradients land in self.grads."""
+        _dev(x, dy)
+        L.check(L.load().llama_block_backward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(x), _p(self.saved),
+                                              self.saved.numel(), _p(dy), _p(self.dx), ctypes.byref(self.gstruct),
+                                              self.batch, self.seq, _p(self.ws), self.ws.numel(), _stream()),
+                "llama_block_backward")
+        return self.dx
+
+    def train_step(self, x: torch.Tensor, target: torch.Tensor, lr: float) -> torch.Tensor:
+        """One SGD step on the loss 0.5 * ||y - target||^2: forward, dL/dy = y -
+        target, backward, w <- w - lr * dL/dw. Returns y before the update."""
+        y = self.forward(x)
+        axpby(self.dy, y, target, 1.0, -1.0)
+        self.backward(x, self.dy)
+        for k in BLOCK_KEYS:
+            axpby(self.weights[k], self.weights[k], self.grads[k], 1.0, -lr)
         return y
 
 

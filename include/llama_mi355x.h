@@ -63,7 +63,9 @@ typedef enum {
   LLAMA_OP_SWIGLU_FFN = 2,
   LLAMA_OP_BLOCK_FORWARD = 3,
   LLAMA_OP_MODEL_FORWARD = 4,
-  LLAMA_OP_MODEL_DECODE = 5
+  LLAMA_OP_MODEL_DECODE = 5,
+  LLAMA_OP_CAUSAL_ATTN_BACKWARD = 6,
+  LLAMA_OP_BLOCK_BACKWARD = 7 /* also the workspace of llama_block_train_forward */
 } llama_op;
 
 /* Numerics options of the bf16 path (llama_config.numerics). Weights are
@@ -262,6 +264,54 @@ const char *llama_status_string(int status);
 
 /* Text of the last LLAMA_ERR_HIP on the calling thread ("" if none). */
 const char *llama_last_error(void);
+
+/* ---------------------------------------------------------------- training (fp32)
+ * The backward of the pre-norm block written out by hand, with the forward's
+ * linear outputs kept and the rest recomputed ([P3] "Efficient Training
+ * Implementation": manual backward of the transformer layers, FlashAttention-
+ * inspired attention backward, selective activation checkpointing). Gradients
+ * follow the chain rule of the forward defined above; the attention backward
+ * recomputes the probabilities tile by tile from q, k and the forward's
+ * per-row log-sum-exp and never stores an S x S matrix. All three calls take
+ * LLAMA_F32 only (bf16 configs: LLAMA_ERR_UNSUPPORTED), pre-norm blocks with
+ * one K/V head per query head, head_dim 64 or 128. Results are deterministic
+ * (no atomics). */
+
+/* Gradients of llama_causal_attn (fp32 q, k, v, dout [batch*seq, n_heads*head_dim],
+ * same layout as the forward) into dq, dk, dv. The forward's output and
+ * log-sum-exp are recomputed into the workspace (llama_workspace_size with
+ * LLAMA_OP_CAUSAL_ATTN_BACKWARD and a config of dim = n_heads*head_dim,
+ * n_heads, dtype). Errors as llama_causal_attn. */
+int llama_causal_attn_backward(int dtype, const void *q, const void *k, const void *v, const void *dout,
+                               void *dq, void *dk, void *dv, int batch, int seq, int n_heads, int head_dim,
+                               void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of the activation buffer llama_block_train_forward fills: the rotated
+ * q and k, v, the attention output, h = x + attention (each [tokens, dim]),
+ * the gate and up projections ([tokens, hidden]) and the attention's
+ * log-sum-exp ([batch, n_heads, seq]), fp32, 256-byte aligned pieces. */
+int llama_block_train_saved_size(const llama_config *cfg, int batch, int seq, size_t *bytes);
+
+/* y = llama_block_forward(x) (fp32), keeping the linear outputs listed above
+ * in `saved` for llama_block_backward; RMSNorm outputs and SiLU(gate)*up are
+ * not kept. ws: llama_workspace_size(LLAMA_OP_BLOCK_BACKWARD). */
+int llama_block_train_forward(const llama_config *cfg, const llama_block_weights *w, const float *x, float *y,
+                              void *saved, size_t saved_bytes, int batch, int seq, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* Backward of the block for the upstream gradient dy = dL/dy [tokens, dim]:
+ * dx = dL/dx and the gradient of every weight, written through the device
+ * pointers of `grads` (same shapes as the weights, fp32; the struct's pointers
+ * are outputs here). x and `saved` must be those of the llama_block_train_forward
+ * call. The norms and SiLU(gate)*up are recomputed from x, h, gate and up. */
+int llama_block_backward(const llama_config *cfg, const llama_block_weights *w, const float *x,
+                         const void *saved, size_t saved_bytes, const float *dy, float *dx,
+                         const llama_block_weights *grads, int batch, int seq, void *ws, size_t ws_bytes,
+                         void *stream);
+
+/* z = a*x + b*y elementwise over n fp32 values (z may alias x or y): the loss
+ * gradient y - target and the SGD update w - lr*g of a training step. */
+int llama_axpby(float *z, const float *x, const float *y, float a, float b, int64_t n, void *stream);
 
 /* Launch trace for profiling, per calling thread, off by default.
  * llama_trace_begin(events, capacity): after every kernel the library then

@@ -178,3 +178,39 @@ def test_norm_placement_validation():
             L.LLAMA_ERR_UNSUPPORTED
         assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 4, 1, ctypes.byref(n)) == \
             L.LLAMA_ERR_UNSUPPORTED
+
+
+def test_training_entry_points_validate_before_any_launch():
+    lib = L.load()
+    n = ctypes.c_size_t()
+    f32 = dict(dim=256, n_heads=2, hidden=768, dtype=L.LLAMA_F32)
+    c = _cfg(**f32)
+    assert lib.llama_block_train_saved_size(ctypes.byref(c), 2, 37, ctypes.byref(n)) == 0
+    # q, k, v, a, h [74, 256] + gate, up [74, 768] + lse [2, 2, 37], 256-byte aligned pieces (+256)
+    pieces = [74 * 256 * 4] * 5 + [74 * 768 * 4] * 2 + [2 * 2 * 37 * 4]
+    assert n.value == sum((p + 255) // 256 * 256 for p in pieces[:-1]) + pieces[-1] + 256
+    assert lib.llama_workspace_size(ctypes.byref(c), L.OP_BLOCK_BACKWARD, 2, 37, ctypes.byref(n)) == 0
+    for bad, st in ((dict(dtype=L.LLAMA_BF16), L.LLAMA_ERR_UNSUPPORTED),
+                    (dict(norm_placement=L.NORM_POST), L.LLAMA_ERR_UNSUPPORTED),
+                    (dict(n_kv_heads=1), L.LLAMA_ERR_UNSUPPORTED)):
+        cb = _cfg(**{**f32, **bad})
+        assert lib.llama_block_train_saved_size(ctypes.byref(cb), 2, 37, ctypes.byref(n)) == st
+        assert lib.llama_workspace_size(ctypes.byref(cb), L.OP_BLOCK_BACKWARD, 2, 37, ctypes.byref(n)) == st
+    w = L.BlockWeights(*([0x1000] * 9))
+    assert lib.llama_block_train_forward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, FAKE, 16, 2, 37, FAKE, 1 << 40,
+                                         None) == L.LLAMA_ERR_WORKSPACE
+    assert lib.llama_block_train_forward(ctypes.byref(c), ctypes.byref(w), None, FAKE, FAKE, 1 << 40, 2, 37, FAKE,
+                                         1 << 40, None) == L.LLAMA_ERR_NULL
+    gn = L.BlockWeights(*([0x1000] * 8 + [0]))
+    assert lib.llama_block_backward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 1 << 40, FAKE, FAKE, ctypes.byref(gn),
+                                    2, 37, FAKE, 1 << 40, None) == L.LLAMA_ERR_NULL
+    assert lib.llama_block_backward(ctypes.byref(c), ctypes.byref(w), FAKE, FAKE, 1 << 40, FAKE, FAKE, ctypes.byref(w),
+                                    2, 37, FAKE, 16, None) == L.LLAMA_ERR_WORKSPACE
+    assert lib.llama_causal_attn_backward(L.LLAMA_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, FAKE,
+                                          1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_causal_attn_backward(L.LLAMA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 96, FAKE,
+                                          1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_causal_attn_backward(L.LLAMA_F32, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 8, 2, 64, FAKE,
+                                          16, None) == L.LLAMA_ERR_WORKSPACE
+    assert lib.llama_axpby(None, FAKE, FAKE, 1.0, 1.0, 4, None) == L.LLAMA_ERR_NULL
+    assert lib.llama_axpby(FAKE, FAKE, FAKE, 1.0, 1.0, -1, None) == L.LLAMA_ERR_SHAPE

@@ -528,3 +528,80 @@ def test_norm_placement_stack_probe():
             ratios.append(got)
         print(f"{placement}: trunk norms {['%.3g' % v for v in norms[:20]]}, amplification at depth 5/10/20/32 "
               f"{['%.3g' % v for v in ratios]}")
+
+
+# ---------------------------------------------------------------- backward and training (fp32)
+def rel_err_each(got: dict, want: dict) -> dict:
+    return {k: rel_err(got[k], want[k]) for k in want}
+
+
+@pytest.mark.parametrize("B,S,H,hd", [(2, 100, 2, 64), (1, 130, 3, 128), (1, 1, 2, 64), (3, 64, 1, 128)])
+def test_causal_attn_backward(B, S, H, hd):
+    """FlashAttention-style backward against the oracle's chain rule, fp32,
+    each gradient's max error relative to its own RMS."""
+    w = I.Workload(906, "attn-bwd", dim=H * hd, n_heads=H, hidden=0, batch=B, seq=S, dtype="f32")
+    q, k, v = I.qkv_inputs(w, device="cuda")
+    do = I.normal((w.tokens, w.dim), 906, 0, I.T_POS, device="cuda")
+    dq, dk, dv = ops().causal_attn_backward(q, k, v, do, B, S, H)
+    torch.cuda.synchronize()
+    want = O.causal_attention_backward(host(q), host(k), host(v), host(do), B, S, H)
+    if S == 1:
+        # one key: the softmax is constant, dq = dk = 0 exactly in the oracle; the
+        # GPU's dP - D is a difference of two equal fp32 dot products
+        assert np.max(np.abs(host(dq))) + np.max(np.abs(host(dk))) < 1e-5 * np.sqrt(np.mean(want[2] ** 2))
+        assert rel_err(dv, want[2]) < TOL_F32
+        return
+    errs = [rel_err(g, r) for g, r in zip((dq, dk, dv), want)]
+    print(f"attention backward B{B} S{S} H{H} hd{hd}: dq {errs[0]:.2e} dk {errs[1]:.2e} dv {errs[2]:.2e}")
+    assert max(errs) < TOL_F32
+
+
+@pytest.mark.parametrize("wid", [0, 107])
+def test_block_backward(wid):
+    """Manual block backward (forward keeping the linear outputs, norms and
+    SiLU recomputed) against the oracle: dx and all nine weight gradients."""
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    dy = I.normal((w.tokens, w.dim), w.wid, 0, I.T_POS, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=torch.float32, eps=w.eps, theta=w.theta)
+    tb = ops().TrainBlock(cfg, wt, w.batch, w.seq)
+    y = tb.forward(x).clone()
+    dx = tb.backward(x, dy).clone()
+    torch.cuda.synchronize()
+    hw = {k: host(v) for k, v in wt.items()}
+    assert rel_err(y, O.block_forward(host(x), hw, w.batch, w.seq, w.n_heads, w.eps, w.theta)) < TOL_F32
+    want_dx, want_g = O.block_backward(host(x), hw, host(dy), w.batch, w.seq, w.n_heads, w.eps, w.theta)
+    errs = rel_err_each({k: v for k, v in tb.grads.items()}, want_g)
+    errs["dx"] = rel_err(dx, want_dx)
+    print(f"block backward {w.name}: " + ", ".join(f"{k} {v:.1e}" for k, v in errs.items()))
+    assert max(errs.values()) < TOL_F32
+
+
+def test_training_step_sgd():
+    """One SGD step on 0.5 ||y - t||^2: the gradients match the oracle's for
+    dL/dy = y - t, and every weight becomes w - lr * g to fp32 rounding; five
+    more steps lower the loss each time."""
+    w = I.workload(107)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    t = I.normal((w.tokens, w.dim), w.wid, 0, I.T_BUMP, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=torch.float32, eps=w.eps, theta=w.theta)
+    hw = {k: host(v) for k, v in wt.items()}
+    tb = ops().TrainBlock(cfg, wt, w.batch, w.seq)
+    lr = 1e-4
+    y0 = tb.train_step(x, t, lr).clone()
+    torch.cuda.synchronize()
+    y_ref = O.block_forward(host(x), hw, w.batch, w.seq, w.n_heads, w.eps, w.theta)
+    _, g_ref = O.block_backward(host(x), hw, y_ref - host(t), w.batch, w.seq, w.n_heads, w.eps, w.theta)
+    for k in hw:
+        g = host(tb.grads[k])
+        assert rel_err(g, g_ref[k]) < TOL_F32, k
+        # w_new = fl(w - fl(lr g)): within two fp32 roundings of the exact update
+        assert np.all(np.abs(host(wt[k]) - (hw[k] - lr * g)) <= 2.0 ** -23 * (np.abs(hw[k]) + lr * np.abs(g))), k
+    losses = [0.5 * float(torch.sum((y0 - t) ** 2))]
+    for _ in range(5):
+        y = tb.train_step(x, t, lr)
+        losses.append(0.5 * float(torch.sum((y - t) ** 2)))
+    print(f"training losses {['%.6g' % v for v in losses]}")
+    assert all(b < a for a, b in zip(losses, losses[1:]))
