@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E peak
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 vector peak
 COPY_CALIBRATION_BYTES = 1 << 30   # bytes read and written by each calibration copy
 
 # HBM bytes per launch of the roofline kernels, from rocprofv3 FETCH_SIZE and
@@ -220,6 +221,35 @@ def bench_other_blocks(args, torch):
     return out
 
 
+def bench_train_step(args, torch, wid: int = 0):
+    """fp32 training step of a block (forward keeping the linear outputs,
+    manual backward, SGD update of all nine weights) on the tiny fp32 block
+    workload. Work is counted as three times the forward's matrix products
+    (the backward's input and weight gradients are two more of each)."""
+    from decoder_only_transformer_llama_amd import inputs as I, ops
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    t = I.normal((w.tokens, w.dim), w.wid, 0, I.T_BUMP, device="cuda")
+    cfg = ops.config(w.dim, w.n_heads, w.hidden, dtype=torch.float32, eps=w.eps, theta=w.theta)
+    tb = ops.TrainBlock(cfg, wt, w.batch, w.seq)
+    for _ in range(args.warmup):
+        tb.train_step(x, t, 1e-6)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
+    ev.record(0, stream)
+    for _ in range(args.steps):
+        tb.train_step(x, t, 1e-6)
+    ev.record(1, stream)
+    ms = ev.elapsed_ms(0, 1) / args.steps
+    torch.cuda.synchronize()
+    fl = 3 * sum(block_flops(w).values())
+    return {"workload": f"{w.name}: fp32 block training step (forward, backward, SGD), batch {w.batch}, seq {w.seq}",
+            "ms": round(ms, 4), "tokens_per_s": round(w.tokens / (ms * 1e-3), 1),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "fp32_frac": round(fl / (ms * 1e-3) / 1e12 / PEAK_FP32_TFLOPS, 4)}
+
+
 def bench_decode(args, torch, wid: int = 4, with_model_prefill: bool = True):
     from decoder_only_transformer_llama_amd import _lib
     from decoder_only_transformer_llama_amd.workloads import decode_workload
@@ -363,6 +393,7 @@ def main() -> int:
     ap.add_argument("--no-model-prefill", action="store_true", help="skip the whole-model prefill leg")
     ap.add_argument("--no-other-blocks", action="store_true", help="skip the 13B/65B-shape block legs")
     ap.add_argument("--no-gqa-decode", action="store_true", help="skip the grouped-query decode leg")
+    ap.add_argument("--no-train", action="store_true", help="skip the fp32 training-step leg")
     ap.add_argument("--numerics", type=lambda v: int(v, 0), default=0,
                     help="prefill operand-precision bits (llama_config.numerics; 0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -415,6 +446,10 @@ def main() -> int:
                "bytes_per_step": g["bytes"], "attention_gbs": g["roofline"]["achieved"],
                "kernels_ms": g["per_kernel_ms"]}
         print(f"# gqa decode: {json.dumps(gqa)}", file=sys.stderr, flush=True)
+    train = None
+    if not args.prefill_only and not args.no_train:
+        train = bench_train_step(args, torch)
+        print(f"# train step: {json.dumps(train)}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pf["block"], torch)
     w = pf["w"]
     line = {
@@ -453,6 +488,8 @@ def main() -> int:
             line["model_prefill"] = dec["model_prefill"]
     if gqa is not None:
         line["decode_gqa"] = gqa
+    if train is not None:
+        line["train_step"] = train
     line["wall_s"] = round(time.time() - t_start, 1)
     print(json.dumps(line), flush=True)
     return 0
