@@ -67,7 +67,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   constexpr int KTILE = KT * KCH;                // u32x4 per K tile
   constexpr int VTILE = HD * 4;                  // u32x4 per v^T tile (4 chunks of 8 keys)
   constexpr int STAGE = KTILE * (QKPAIR ? 2 : 1) + VTILE * (VPAIR ? 2 : 1);
-  constexpr int NST = 2;
+#ifndef ATTN_NST
+#define ATTN_NST 3
+#endif
+  // LDS ring depth: single fp16 operands (16 KB per stage at hd 128) keep
+  // ATTN_NST - 1 tiles in flight; bf16 pairs (32 KB per stage) stay at 2 so
+  // that two workgroups still fit a compute unit.
+  constexpr int NST = F16 ? ATTN_NST : 2;
+  constexpr float kLazyRescale = 8.0f;   // log2 units a running maximum may lag the true one
   constexpr int KBLK = KTILE / 64, VBLK = VTILE / 64;       // 1 KB blocks per tile
   constexpr int NBLK = KBLK * (QKPAIR ? 2 : 1) + VBLK * (VPAIR ? 2 : 1);
   static_assert(NBLK % 4 == 0, "blocks split evenly over 4 wavefronts");
@@ -90,9 +97,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   const int hk = h / (a.n_heads / n_kv);
   const int64_t vbase = ((int64_t)b * n_kv + hk) * HD * a.vt_stride;
 
-  // ---- direct-to-LDS tile loads: block q of this wavefront, lane i -> LDS slot i
-  auto issue = [&](int kt) {
-    u32x4 *st = smem + (kt % NST) * STAGE;
+  const int kend = min(S, q0 + 128);
+  const int n_kt = (kend + KT - 1) / KT;
+
+  // ---- direct-to-LDS tile loads: block q of this wavefront, lane i -> LDS slot i.
+  // Ring slot kt % NST; slots past the last tile reload the last tile (never
+  // read) so that every step waits on the same number of loads.
+  auto issue = [&](int kt_slot) {
+    u32x4 *st = smem + (kt_slot % NST) * STAGE;
+    const int kt = min(kt_slot, n_kt - 1);
 #pragma unroll
     for (int qb = 0; qb < NBLK / 4; ++qb) {
       const int blk = w * (NBLK / 4) + qb;
@@ -117,8 +130,6 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     }
   };
 
-  const int kend = min(S, q0 + 128);
-  const int n_kt = (kend + KT - 1) / KT;
   issue(0);
 
   // q fragments (B operand of S^T = K Q^T): q[qi][16kk + 8g .. +7]
@@ -140,11 +151,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   float m_run = -INFINITY, l_run = 0.f;
   const float c = a.scale_log2;
   const int krow = perm23(l32);   // key (within the tile) this lane supplies as A-operand row
+  for (int st = 1; st < NST - 1; ++st) issue(st);   // after the q fragments: they complete first
 
   for (int kt = 0; kt < n_kt; ++kt) {
-    ATT_WAIT_VMCNT(0);                 // this wavefront's loads of tile kt (and the q fragments)
-    __builtin_amdgcn_s_barrier();      // everyone's; everyone is done with tile kt-1
-    if (kt + 1 < n_kt) issue(kt + 1);  // overwrites the buffer of tile kt-1
+    ATT_WAIT_VMCNT((NST - 2) * (NBLK / 4));   // this wavefront's loads of tile kt (and the q fragments)
+    __builtin_amdgcn_s_barrier();             // everyone's; everyone is done with tile kt-1
+    if (NST == 2) {
+      if (kt + 1 < n_kt) issue(kt + 1);       // overwrites the buffer of tile kt-1
+    } else {
+      issue(kt + NST - 1);
+    }
     const int kt0 = kt * KT;
     if (kt0 > qwave_max) continue;     // whole tile above this wavefront's diagonal
     const u32x4 *sk = smem + (kt % NST) * STAGE;
@@ -152,39 +168,62 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     const u32x4 *sv = sk + KTILE * (QKPAIR ? 2 : 1);
     const u32x4 *svl = sv + VTILE;
 
-    // ---- scores S^T (32 keys x 32 queries)
-    f32x16 sc;
+    // ---- scores S^T (32 keys x 32 queries), in two accumulators (even and
+    // odd k-steps) so that two dependent matrix-core chains of half the
+    // length run interleaved
+    f32x16 sc2[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+    for (int r = 0; r < 16; ++r) sc2[0][r] = sc2[1][r] = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
+      f32x16 &acc = sc2[kk & 1];
       if (F16) {
-        sc = mfma32h(as_f16x8(sk[so]), as_f16x8(qh[kk]), sc);
+        acc = mfma32h(as_f16x8(sk[so]), as_f16x8(qh[kk]), acc);
       } else {
         const bf16x8 kf = as_bf16x8(sk[so]);
-        sc = mfma32(kf, as_bf16x8(qh[kk]), sc);
+        acc = mfma32(kf, as_bf16x8(qh[kk]), acc);
         if (QKPAIR) {
-          sc = mfma32(as_bf16x8(skl[so]), as_bf16x8(qh[kk]), sc);
-          sc = mfma32(kf, as_bf16x8(ql[kk]), sc);
+          acc = mfma32(as_bf16x8(skl[so]), as_bf16x8(qh[kk]), acc);
+          acc = mfma32(kf, as_bf16x8(ql[kk]), acc);
         }
       }
     }
+    f32x16 sc = sc2[0] + sc2[1];
 
-    // ---- online softmax (fp32); lane holds 16 keys of query qi
+    // ---- online softmax (fp32); lane holds 16 keys of query qi. Only tiles
+    // crossing this wavefront's diagonal or the sequence end need the mask
+    // (a wavefront-uniform test).
     float mx = -INFINITY;
+    if (kt0 + KT - 1 > q0 + 32 * w || kt0 + KT > S) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = kt0 + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
-      const bool ok = key <= qi && key < S;
-      sc[r] = ok ? sc[r] : -INFINITY;
-      mx = fmaxf(mx, sc[r]);
+      for (int r = 0; r < 16; ++r) {
+        const int key = kt0 + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
+        const bool ok = key <= qi && key < S;
+        sc[r] = ok ? sc[r] : -INFINITY;
+        mx = fmaxf(mx, sc[r]);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c);   // v_exp_f32; m_run = -inf gives 0
-    m_run = m_new;
+    // Lazy rescaling: the reference maximum m_run moves (and O, l are
+    // rescaled) only when some lane's new maximum exceeds it by more than
+    // kLazyRescale in log2 units; otherwise probabilities up to 2^kLazyRescale
+    // enter P (exact in fp32, within fp16 range) and the final 1/l cancels the
+    // common factor. m_run = -inf (no visible key yet) always takes the update.
+    if (!__all((mx - m_run) * c <= kLazyRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);   // -inf -> 0
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < NEB; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[e][r] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -192,15 +231,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       sc[r] = pr;
       psum += pr;
     }
-    l_run = l_run * alpha + psum;
-    // once the running maxima settle, alpha is exactly 1 on every lane: skip
-    // the rescale (a wavefront-uniform branch)
-    if (!__all(alpha == 1.0f)) {
-#pragma unroll
-      for (int e = 0; e < NEB; ++e)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[e][r] *= alpha;
-    }
+    l_run += psum;
 
     // ---- O^T += V^T P^T
 #pragma unroll

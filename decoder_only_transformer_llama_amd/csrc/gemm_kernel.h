@@ -6,10 +6,12 @@
 // HBM -> LDS with global_load_lds_dwordx4 (no register staging): every
 // wavefront instruction drops 64 lanes x 16 bytes into one contiguous 1 KB
 // block of LDS, and the row/chunk each lane fetches is chosen so the block
-// lands already XOR-swizzled. K is consumed in steps of 32 with a ring of
-// STAGES LDS buffers (STAGES-1 steps of loads in flight); operand reads of the
-// next substep are interleaved with the current substep's MFMAs; one barrier
-// per step with explicit vmcnt/lgkmcnt waits.
+// lands already XOR-swizzled. K is consumed in steps of 64 (32 when A is a
+// hi/lo pair) with a ring of STAGES LDS buffers (STAGES-1 steps of loads in
+// flight); operand reads of the next 16-deep substep are interleaved with the
+// current substep's MFMAs; one barrier per step with explicit vmcnt/lgkmcnt
+// waits. The 64-deep step halves the barriers per MFMA: on the 7B block the
+// QKV, gate/up and down GEMMs run 2.5-5% faster than with 32-deep steps.
 //
 // A may be a bf16 hi/lo pair (A_lo non-null): both parts are multiplied into
 // the same accumulator, which carries an fp32 activation at ~2^-16 relative
@@ -42,10 +44,16 @@ namespace llama {
 // lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
+#ifndef GEMM_BK
+#define GEMM_BK 64
+#endif
 template <int BN, bool APAIR>
 struct GemmCfg {
-  static constexpr int BM = 256, BK = 32;
-  static constexpr int CH = 4;                     // 16-byte chunks per LDS row (64 bytes)
+  // K step: GEMM_BK (32 or 64) for single operands; hi/lo pairs keep 32 (a
+  // 64-deep stage with A_lo would not fit two stages in LDS)
+  static constexpr int BM = 256, BK = APAIR ? 32 : GEMM_BK;
+  static constexpr int CH = BK / 8;                // 16-byte chunks per LDS row
+  static constexpr int RPL = 64 / CH;              // rows per 1 KB wavefront load
 #ifndef GEMM_NW
 #define GEMM_NW 8
 #endif
@@ -55,17 +63,33 @@ struct GemmCfg {
   static constexpr int A_TILE = BM * CH;           // u32x4 per A tile
   static constexpr int B_TILE = BN * CH;
   static constexpr int STAGE = A_TILE * (APAIR ? 2 : 1) + B_TILE;
-  static constexpr int STAGES = (STAGE * 16 * 5 <= 160 * 1024) ? 5 : ((STAGE * 16 * 4 <= 160 * 1024) ? 4 : 3);
-  static constexpr int A_LD = BM / 16 / NW;        // 1 KB loads per wavefront per A tile
-  static constexpr int B_LD = BN / 16 / NW;
+  static constexpr int STAGE_BYTES = STAGE * 16;
+  static constexpr int STAGES = STAGE_BYTES * 5 <= 160 * 1024   ? 5
+                                : STAGE_BYTES * 4 <= 160 * 1024 ? 4
+                                : STAGE_BYTES * 3 <= 160 * 1024 ? 3
+                                                                : 2;
+  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
+  static constexpr int A_LD = BM / RPL / NW;       // 1 KB loads per wavefront per A tile
+  static constexpr int B_LD = BN / RPL / NW;
   static constexpr int LPS = A_LD * (APAIR ? 2 : 1) + B_LD;  // loads per stage per wavefront
 };
 
-// Swizzle of the 4 chunks of a 64-byte LDS row. gfx950 LDS serves a 16-byte
-// read 16 lanes per pass across 64 four-byte banks (256 bytes): the 16 rows
-// read together (same logical chunk) must land on 16 distinct 16-byte slots
-// of the 256-byte bank window, i.e. distinct (row mod 4, chunk) pairs.
-DEV int swz4(int row) { return (row >> 2) & 3; }
+// Swizzle of the CH chunks of an LDS row (CH * 16 bytes). gfx950 LDS serves a
+// 16-byte read 16 lanes per pass across 64 four-byte banks (256 bytes): the 16
+// rows read together (same logical chunk) must land on 16 distinct 16-byte
+// slots of the 256-byte bank window: distinct (row mod 4, chunk) pairs for
+// 64-byte rows, distinct (row mod 2, chunk) pairs for 128-byte rows.
+template <int CH>
+DEV int swz(int row) { return CH == 4 ? (row >> 2) & 3 : (row >> 1) & 7; }
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices).
+template <int I, int N, class F>
+DEV void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 // Scheduling hint: alternate one MFMA with one LDS read, then the remainder.
 template <int NMF, int NRD, int ID>
@@ -98,12 +122,12 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   const int m0 = tm * BM, n0 = a.n_base + tn * BN;
 
   // ---- global source of each lane's 16-byte piece, fixed over K
-  // A block q of this wavefront covers tile rows 16 * (wave * A_LD + q) + lane / 4.
+  // A block q of this wavefront covers tile rows RPL * (wave * A_LD + q) + lane / CH.
   const u16 *asrc[G::A_LD], *alsrc[APAIR ? G::A_LD : 1];
 #pragma unroll
   for (int q = 0; q < G::A_LD; ++q) {
-    const int r = 16 * (wave * G::A_LD + q) + (lane >> 2);
-    const int c = (lane & 3) ^ swz4(r);
+    const int r = G::RPL * (wave * G::A_LD + q) + lane / G::CH;
+    const int c = (lane % G::CH) ^ swz<G::CH>(r);
     const int row = min(m0 + r, a.M - 1);  // rows past M load a valid row; never stored
     asrc[q] = (const u16 *)a.A + (int64_t)row * a.lda + 8 * c;
     if (APAIR) alsrc[q] = a.A_lo + (int64_t)row * a.lda + 8 * c;
@@ -111,8 +135,8 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   const u16 *bsrc[G::B_LD];
 #pragma unroll
   for (int q = 0; q < G::B_LD; ++q) {
-    const int r = 16 * (wave * G::B_LD + q) + (lane >> 2);
-    const int c = (lane & 3) ^ swz4(r);
+    const int r = G::RPL * (wave * G::B_LD + q) + lane / G::CH;
+    const int c = (lane % G::CH) ^ swz<G::CH>(r);
     const u16 *ptr;
     if (a.b_mode == BMODE_GATEUP) {
       const int blk = r >> 5;
@@ -171,12 +195,12 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
 #pragma unroll
     for (int j = 0; j < G::TN; ++j) {
       const int r = wn * G::WN + j * 32 + l32;
-      f.b[j] = as_bf16x8(sb[r * CH + (c ^ swz4(r))]);
+      f.b[j] = as_bf16x8(sb[r * CH + (c ^ swz<CH>(r))]);
     }
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
       const int r = wm * G::WM + i * 32 + l32;
-      const int off = r * CH + (c ^ swz4(r));
+      const int off = r * CH + (c ^ swz<CH>(r));
       f.a[i] = as_bf16x8(sa[off]);
       if (APAIR) f.al[i] = as_bf16x8(sal[off]);
     }
@@ -193,36 +217,45 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
     }
   };
 
-  // Pipeline per K step kt (two 16-deep substeps, fragments F0/F1), one barrier:
-  //   issue loads of stage kt+S-1 | [mma F0(kt) interleaved with reads of F1(kt)]
+  // Pipeline per K step kt (NS = BK/16 substeps, fragments alternating in
+  // f[0] / f[1]), one barrier:
+  //   issue loads of stage kt+S-1 | for each substep but the last:
+  //   [mma f(ss) interleaved with reads of f(ss+1)]
   //   wait own stage-(kt+1) loads, drain own LDS reads, barrier
-  //   [mma F1(kt) interleaved with reads of F0(kt+1)]
+  //   [mma of the last substep interleaved with reads of f[0] of step kt+1]
   // The buffer refilled at step kt held stage kt-1; every wavefront drained its
   // reads of it before the previous barrier. Loads past the last step re-read
   // the last step into buffers nobody reads, so the body has no branches.
+  constexpr int NS = BK / 16;
+  static_assert(NS % 2 == 0, "the last substep's fragments are f[1]");
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
   WAIT_VMCNT((STAGES - 2) * G::LPS);
   __builtin_amdgcn_s_barrier();
-  Frag f0, f1;
-  read_frag(f0, 0, 0);
+  Frag f[2];
+  read_frag(f[0], 0, 0);
   constexpr int NMF = G::TM * G::TN * (APAIR ? 2 : 1);     // MFMAs per substep
   constexpr int NRD = G::TM * (APAIR ? 2 : 1) + G::TN;      // LDS reads per substep
+  auto inner = [&](int kt) {   // substeps 0 .. NS-2 of step kt
+    static_for<0, NS - 1>([&](auto ic) {
+      constexpr int ss = decltype(ic)::value;
+      read_frag(f[(ss + 1) & 1], kt, ss + 1);
+      mma(f[ss & 1]);
+      interleave<NMF, NRD, ss>();
+    });
+  };
   for (int kt = 0; kt < nk - 1; ++kt) {
     issue(kt + STAGES - 1);
-    read_frag(f1, kt, 1);
-    mma(f0);
-    interleave<NMF, NRD, 0>();
+    inner(kt);
     WAIT_VMCNT((STAGES - 2) * G::LPS);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    read_frag(f0, kt + 1, 0);
-    mma(f1);
-    interleave<NMF, NRD, 1>();
+    read_frag(f[0], kt + 1, 0);
+    mma(f[1]);
+    interleave<NMF, NRD, NS - 1>();
   }
-  read_frag(f1, nk - 1, 1);
-  mma(f0);
-  mma(f1);
+  inner(nk - 1);
+  mma(f[1]);
   WAIT_VMCNT(0);   // drain the reloads past the end before LDS is reused
 
   // ---------------------------------------------------------------- epilogue
