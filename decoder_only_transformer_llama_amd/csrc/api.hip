@@ -139,8 +139,13 @@ ResidCfg choose_resid(int M, int N, int K, bool apair) {
   auto rounds = [&](long tiles) { return (double)((tiles + cus - 1) / cus); };
   const double c128 = rounds(tm * ((N + 127) / 128)) * kHalfTileCost;
   const double c256 = rounds(tm * ((N + 255) / 256));
+#ifdef RESID_FORCE   // tiling experiments: 1 = 256 x 128, 2 = 256 x 256, 3 = 256 x 256 with K split in two
+  if (RESID_FORCE == 1) return {128, 1};
+  if (RESID_FORCE == 2) return {256, 1};
+  if (RESID_FORCE == 3 && K % 128 == 0) return {256, 2};
+#endif
   double c256s2 = 1e30;
-  if (K % 64 == 0) {
+  if (K % 128 == 0) {   // each half a whole number of 64-deep steps
     const double traffic_us = (double)M * N * 4.0 * 2.0 * 2.0 / 5e6;
     const double round_us = 256.0 * 256.0 * K * 2.0 / 4e6 * (apair ? 2.0 : 1.0);
     c256s2 = rounds(tm * ((N + 255) / 256) * 2) * 0.5 + traffic_us / round_us;

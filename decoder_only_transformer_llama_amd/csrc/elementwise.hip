@@ -61,61 +61,76 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 // fp32 accumulator by rstd, which completes RMSNorm(x; g) W^T. dim % 8 == 0.
 // g == nullptr: the operand is x itself (a block without a norm before the
 // projection; rstd is then written but not used).
-template <bool IN_F32, bool PAIR, bool PARTS>
-__global__ __launch_bounds__(256) void norm_prep_kernel(const void *x, const u16 *g, int64_t rows, int dim,
-                                                        float eps, float *rstd, u16 *xg_hi, u16 *xg_lo,
-                                                        const float *part, int n_parts, float *h_out) {
+// U consecutive 512-channel chunks per step (dim a multiple of 512 * U when
+// U > 1): all their loads issue before any is used, and __restrict__ lets the
+// compiler move the next step's loads above this step's stores.
+template <bool IN_F32, bool PAIR, bool PARTS, int U>
+__global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__ x, const u16 *__restrict__ g,
+                                                        int64_t rows, int dim, float eps, float *__restrict__ rstd,
+                                                        u16 *__restrict__ xg_hi, u16 *__restrict__ xg_lo,
+                                                        const float *__restrict__ part, int n_parts,
+                                                        float *__restrict__ h_out) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
   const int64_t base = row * dim;
   const int64_t pstride = rows * dim;
   float ss = 0.f;
-  for (int c = 8 * lane; c < dim; c += 512) {
-    float f[8], gf[8];
-    if (IN_F32) {
-      const f32x4 a0 = *(const f32x4 *)((const float *)x + base + c);
-      const f32x4 a1 = *(const f32x4 *)((const float *)x + base + c + 4);
+  for (int c0 = 8 * lane; c0 < dim; c0 += 512 * U) {
+    float f[U][8], gf[U][8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f[i] = a0[i];
-        f[4 + i] = a1[i];
-      }
-    } else {
-      unpack8(*(const u32x4 *)((const u16 *)x + base + c), f);
-    }
-    if (PARTS) {
-      // h = x + the split-K partial products, added in split order
-      for (int z = 0; z < n_parts; ++z) {
-        const float *pp = part + z * pstride + base + c;
-        const f32x4 p0 = *(const f32x4 *)pp, p1 = *(const f32x4 *)(pp + 4);
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 512 * u;
+      if (IN_F32) {
+        const f32x4 a0 = *(const f32x4 *)((const float *)x + base + c);
+        const f32x4 a1 = *(const f32x4 *)((const float *)x + base + c + 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f[i] += p0[i];
-          f[4 + i] += p1[i];
+          f[u][i] = a0[i];
+          f[u][4 + i] = a1[i];
+        }
+      } else {
+        unpack8(*(const u32x4 *)((const u16 *)x + base + c), f[u]);
+      }
+      if (PARTS) {
+        // h = x + the split-K partial products, added in split order
+        for (int z = 0; z < n_parts; ++z) {
+          const float *pp = part + z * pstride + base + c;
+          const f32x4 p0 = *(const f32x4 *)pp, p1 = *(const f32x4 *)(pp + 4);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            f[u][i] += p0[i];
+            f[u][4 + i] += p1[i];
+          }
         }
       }
-      *(f32x4 *)(h_out + base + c) = f32x4{f[0], f[1], f[2], f[3]};
-      *(f32x4 *)(h_out + base + c + 4) = f32x4{f[4], f[5], f[6], f[7]};
-    }
-    if (g) {
-      unpack8(*(const u32x4 *)(g + c), gf);
-    } else {
+      if (g) {
+        unpack8(*(const u32x4 *)(g + c), gf[u]);
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) gf[i] = 1.0f;
+        for (int i = 0; i < 8; ++i) gf[u][i] = 1.0f;
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      ss += f[i] * f[i];
-      f[i] *= gf[i];
-    }
-    if (PAIR) {
-      u32x4 hi, lo;
-      pack8_pair(f, hi, lo);
-      *(u32x4 *)(xg_hi + base + c) = hi;
-      *(u32x4 *)(xg_lo + base + c) = lo;
-    } else {
-      *(u32x4 *)(xg_hi + base + c) = pack8(f);
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + 512 * u;
+      if (PARTS) {
+        *(f32x4 *)(h_out + base + c) = f32x4{f[u][0], f[u][1], f[u][2], f[u][3]};
+        *(f32x4 *)(h_out + base + c + 4) = f32x4{f[u][4], f[u][5], f[u][6], f[u][7]};
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ss += f[u][i] * f[u][i];
+        f[u][i] *= gf[u][i];
+      }
+      if (PAIR) {
+        u32x4 hi, lo;
+        pack8_pair(f[u], hi, lo);
+        *(u32x4 *)(xg_hi + base + c) = hi;
+        *(u32x4 *)(xg_lo + base + c) = lo;
+      } else {
+        *(u32x4 *)(xg_hi + base + c) = pack8(f[u]);
+      }
     }
   }
   ss = wave_sum(ss);
@@ -130,20 +145,26 @@ hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_
   const bool parts = part != nullptr && n_parts > 0;
   if (parts && h_out == nullptr) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + 3) / 4));
-#define NP_CASE(F, P, R)                                                                                    \
-  if (!!in_f32 == F && (xg_lo != nullptr) == P && parts == R) {                                            \
-    hipLaunchKernelGGL((norm_prep_kernel<F, P, R>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, xg_hi, \
-                       xg_lo, part, n_parts, h_out);                                                        \
-    return hipGetLastError();                                                                             \
+  const int u = dim % 2048 == 0 ? 4 : (dim % 1024 == 0 ? 2 : 1);
+#define NP_CASE(F, P, R, U_)                                                                                     \
+  if (!!in_f32 == F && (xg_lo != nullptr) == P && parts == R && u == U_) {                                      \
+    hipLaunchKernelGGL((norm_prep_kernel<F, P, R, U_>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, xg_hi, \
+                       xg_lo, part, n_parts, h_out);                                                             \
+    return hipGetLastError();                                                                                  \
   }
-  NP_CASE(true, true, false)
-  NP_CASE(true, false, false)
-  NP_CASE(false, true, false)
-  NP_CASE(false, false, false)
-  NP_CASE(true, true, true)
-  NP_CASE(true, false, true)
-  NP_CASE(false, true, true)
-  NP_CASE(false, false, true)
+#define NP_CASES(U_)              \
+  NP_CASE(true, true, false, U_)  \
+  NP_CASE(true, false, false, U_) \
+  NP_CASE(false, true, false, U_) \
+  NP_CASE(false, false, false, U_) \
+  NP_CASE(true, true, true, U_)   \
+  NP_CASE(true, false, true, U_)  \
+  NP_CASE(false, true, true, U_)  \
+  NP_CASE(false, false, true, U_)
+  NP_CASES(4)
+  NP_CASES(2)
+  NP_CASES(1)
+#undef NP_CASES
 #undef NP_CASE
   return hipErrorInvalidValue;
 }
