@@ -66,14 +66,23 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   constexpr int NEB = HD / 32;                   // 32-wide blocks of the head dimension
   constexpr int KTILE = KT * KCH;                // u32x4 per K tile
   constexpr int VTILE = HD * 4;                  // u32x4 per v^T tile (4 chunks of 8 keys)
-  constexpr int STAGE = KTILE * (QKPAIR ? 2 : 1) + VTILE * (VPAIR ? 2 : 1);
+  constexpr int STAGE1 = KTILE * (QKPAIR ? 2 : 1) + VTILE * (VPAIR ? 2 : 1);   // one 32-key tile
 #ifndef ATTN_NST
 #define ATTN_NST 3
 #endif
-  // LDS ring depth: single fp16 operands (16 KB per stage at hd 128) keep
-  // ATTN_NST - 1 tiles in flight; bf16 pairs (32 KB per stage) stay at 2 so
-  // that two workgroups still fit a compute unit.
-  constexpr int NST = F16 ? ATTN_NST : 2;
+#ifndef ATTN_SUB
+#define ATTN_SUB 2
+#endif
+  // Tiles per step (SUB): with fp16 operands two 32-key tiles share one
+  // barrier and one softmax update, so each step carries two independent
+  // score chains; the longest workgroups (the last query tiles, 2048 keys)
+  // then take half as many dependent steps.
+  constexpr int SUB = F16 ? ATTN_SUB : 1;
+  constexpr int STAGE = SUB * STAGE1;
+  // LDS ring depth: single fp16 operands (16 KB per tile at hd 128) keep
+  // ATTN_NST - 1 steps in flight with one tile per step, one with two; bf16
+  // pairs (32 KB per tile) stay at 2, so that two workgroups fit a compute unit.
+  constexpr int NST = (F16 && SUB == 1) ? ATTN_NST : 2;
   constexpr float kLazyRescale = 8.0f;   // log2 units a running maximum may lag the true one
   constexpr int KBLK = KTILE / 64, VBLK = VTILE / 64;       // 1 KB blocks per tile
   constexpr int NBLK = KBLK * (QKPAIR ? 2 : 1) + VBLK * (VPAIR ? 2 : 1);
@@ -98,35 +107,40 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   const int64_t vbase = ((int64_t)b * n_kv + hk) * HD * a.vt_stride;
 
   const int kend = min(S, q0 + 128);
-  const int n_kt = (kend + KT - 1) / KT;
+  const int n_kt = (kend + KT - 1) / KT;        // 32-key tiles
+  const int n_st = (n_kt + SUB - 1) / SUB;      // steps of SUB tiles
 
   // ---- direct-to-LDS tile loads: block q of this wavefront, lane i -> LDS slot i.
-  // Ring slot kt % NST; slots past the last tile reload the last tile (never
+  // Ring slot st % NST holds tiles SUB*st .. SUB*st + SUB-1; tiles past the
+  // last reload the last tile (their keys are masked, or the slot is never
   // read) so that every step waits on the same number of loads.
-  auto issue = [&](int kt_slot) {
-    u32x4 *st = smem + (kt_slot % NST) * STAGE;
-    const int kt = min(kt_slot, n_kt - 1);
+  auto issue = [&](int st_slot) {
 #pragma unroll
-    for (int qb = 0; qb < NBLK / 4; ++qb) {
-      const int blk = w * (NBLK / 4) + qb;
-      const u16 *src;
-      u32x4 *dst;
-      if (blk < KBLK * (QKPAIR ? 2 : 1)) {
-        const int part = blk / KBLK, kb = blk % KBLK;
-        const int row = kb * (64 / KCH) + lane / KCH;
-        const int c = (lane % KCH) ^ rswz<KCH>(row);
-        const int key = min(kt * KT + row, S - 1);   // rows past S load a valid key; masked later
-        src = (part ? a.kl : a.kh) + (tok0 + key) * kvd + hk * HD + 8 * c;
-        dst = st + part * KTILE + kb * 64;
-      } else {
-        const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
-        const int part = vblk / VBLK, vb = vblk % VBLK;
-        const int e = vb * 16 + (lane >> 2);
-        const int c = (lane & 3) ^ vswz(e);
-        src = (part ? a.vtl : a.vth) + vbase + (int64_t)e * a.vt_stride + kt * KT + 8 * c;
-        dst = st + KTILE * (QKPAIR ? 2 : 1) + part * VTILE + vb * 64;
+    for (int u = 0; u < SUB; ++u) {
+      u32x4 *st = smem + (st_slot % NST) * STAGE + u * STAGE1;
+      const int kt = min(st_slot * SUB + u, n_kt - 1);
+#pragma unroll
+      for (int qb = 0; qb < NBLK / 4; ++qb) {
+        const int blk = w * (NBLK / 4) + qb;
+        const u16 *src;
+        u32x4 *dst;
+        if (blk < KBLK * (QKPAIR ? 2 : 1)) {
+          const int part = blk / KBLK, kb = blk % KBLK;
+          const int row = kb * (64 / KCH) + lane / KCH;
+          const int c = (lane % KCH) ^ rswz<KCH>(row);
+          const int key = min(kt * KT + row, S - 1);   // rows past S load a valid key; masked later
+          src = (part ? a.kl : a.kh) + (tok0 + key) * kvd + hk * HD + 8 * c;
+          dst = st + part * KTILE + kb * 64;
+        } else {
+          const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
+          const int part = vblk / VBLK, vb = vblk % VBLK;
+          const int e = vb * 16 + (lane >> 2);
+          const int c = (lane & 3) ^ vswz(e);
+          src = (part ? a.vtl : a.vth) + vbase + (int64_t)e * a.vt_stride + kt * KT + 8 * c;
+          dst = st + KTILE * (QKPAIR ? 2 : 1) + part * VTILE + vb * 64;
+        }
+        __builtin_amdgcn_global_load_lds((const void *)src, ATT_LDS(dst), 16, 0, 0);
       }
-      __builtin_amdgcn_global_load_lds((const void *)src, ATT_LDS(dst), 16, 0, 0);
     }
   };
 
@@ -153,59 +167,68 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   const int krow = perm23(l32);   // key (within the tile) this lane supplies as A-operand row
   for (int st = 1; st < NST - 1; ++st) issue(st);   // after the q fragments: they complete first
 
-  for (int kt = 0; kt < n_kt; ++kt) {
-    ATT_WAIT_VMCNT((NST - 2) * (NBLK / 4));   // this wavefront's loads of tile kt (and the q fragments)
-    __builtin_amdgcn_s_barrier();             // everyone's; everyone is done with tile kt-1
+  for (int step = 0; step < n_st; ++step) {
+    ATT_WAIT_VMCNT((NST - 2) * SUB * (NBLK / 4));   // this wavefront's loads of this step (and the q fragments)
+    __builtin_amdgcn_s_barrier();                   // everyone's; everyone is done with the previous step
     if (NST == 2) {
-      if (kt + 1 < n_kt) issue(kt + 1);       // overwrites the buffer of tile kt-1
+      if (step + 1 < n_st) issue(step + 1);         // overwrites the buffer of the previous step
     } else {
-      issue(kt + NST - 1);
+      issue(step + NST - 1);
     }
-    const int kt0 = kt * KT;
-    if (kt0 > qwave_max) continue;     // whole tile above this wavefront's diagonal
-    const u32x4 *sk = smem + (kt % NST) * STAGE;
-    const u32x4 *skl = sk + KTILE;
-    const u32x4 *sv = sk + KTILE * (QKPAIR ? 2 : 1);
-    const u32x4 *svl = sv + VTILE;
+    const int s0 = step * SUB * KT;
+    if (s0 > qwave_max) continue;     // whole step above this wavefront's diagonal
 
-    // ---- scores S^T (32 keys x 32 queries), in two accumulators (even and
-    // odd k-steps) so that two dependent matrix-core chains of half the
-    // length run interleaved
-    f32x16 sc2[2];
+    // ---- scores S^T (32 keys x 32 queries per tile). One tile per step: two
+    // accumulators (even and odd k-steps) so that two dependent matrix-core
+    // chains of half the length run interleaved; two tiles: one chain each.
+    constexpr int NACC = SUB == 1 ? 2 : 1;
+    f32x16 sc[SUB];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) sc2[0][r] = sc2[1][r] = 0.f;
+    for (int u = 0; u < SUB; ++u) {
+      const u32x4 *sk = smem + (step % NST) * STAGE + u * STAGE1;
+      const u32x4 *skl = sk + KTILE;
+      f32x16 sacc[NACC];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
-      f32x16 &acc = sc2[kk & 1];
-      if (F16) {
-        acc = mfma32h(as_f16x8(sk[so]), as_f16x8(qh[kk]), acc);
-      } else {
-        const bf16x8 kf = as_bf16x8(sk[so]);
-        acc = mfma32(kf, as_bf16x8(qh[kk]), acc);
-        if (QKPAIR) {
-          acc = mfma32(as_bf16x8(skl[so]), as_bf16x8(qh[kk]), acc);
-          acc = mfma32(kf, as_bf16x8(ql[kk]), acc);
+      for (int j = 0; j < NACC; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[j][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
+        f32x16 &acc = sacc[kk % NACC];
+        if (F16) {
+          acc = mfma32h(as_f16x8(sk[so]), as_f16x8(qh[kk]), acc);
+        } else {
+          const bf16x8 kf = as_bf16x8(sk[so]);
+          acc = mfma32(kf, as_bf16x8(qh[kk]), acc);
+          if (QKPAIR) {
+            acc = mfma32(as_bf16x8(skl[so]), as_bf16x8(qh[kk]), acc);
+            acc = mfma32(kf, as_bf16x8(ql[kk]), acc);
+          }
         }
       }
+      sc[u] = NACC == 2 ? sacc[0] + sacc[NACC - 1] : sacc[0];
     }
-    f32x16 sc = sc2[0] + sc2[1];
 
-    // ---- online softmax (fp32); lane holds 16 keys of query qi. Only tiles
-    // crossing this wavefront's diagonal or the sequence end need the mask
-    // (a wavefront-uniform test).
+    // ---- online softmax (fp32); lane holds 16 keys of query qi per tile.
+    // Only tiles crossing this wavefront's diagonal or the sequence end need
+    // the mask (a wavefront-uniform test).
     float mx = -INFINITY;
-    if (kt0 + KT - 1 > q0 + 32 * w || kt0 + KT > S) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt0 + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
-        const bool ok = key <= qi && key < S;
-        sc[r] = ok ? sc[r] : -INFINITY;
-        mx = fmaxf(mx, sc[r]);
+    for (int u = 0; u < SUB; ++u) {
+      const int kt0 = s0 + u * KT;
+      if (kt0 + KT - 1 > q0 + 32 * w || kt0 + KT > S) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
+          const bool ok = key <= qi && key < S;
+          sc[u][r] = ok ? sc[u][r] : -INFINITY;
+          mx = fmaxf(mx, sc[u][r]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[u][r]);
       }
-    } else {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     // Lazy rescaling: the reference maximum m_run moves (and O, l are
@@ -226,30 +249,37 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
     float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pr = __builtin_amdgcn_exp2f((sc[r] - m_use) * c);   // exp2(-inf) = 0 for masked keys
-      sc[r] = pr;
-      psum += pr;
-    }
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = __builtin_amdgcn_exp2f((sc[u][r] - m_use) * c);   // exp2(-inf) = 0 for masked keys
+        sc[u][r] = pr;
+        psum += pr;
+      }
     l_run += psum;
 
     // ---- O^T += V^T P^T
 #pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      float pv[8];
+    for (int u = 0; u < SUB; ++u) {
+      const u32x4 *sv = smem + (step % NST) * STAGE + u * STAGE1 + KTILE * (QKPAIR ? 2 : 1);
+      const u32x4 *svl = sv + VTILE;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = sc[8 * s2 + i];
-      const u32x4 pf = F16 ? pack8h(pv) : pack8(pv);
-      const int ch = 2 * s2 + g;
+      for (int s2 = 0; s2 < 2; ++s2) {
+        float pv[8];
 #pragma unroll
-      for (int e = 0; e < NEB; ++e) {
-        const int row = 32 * e + l32;
-        const int so = row * 4 + (ch ^ vswz(row));
-        if (F16) {
-          acc_o[e] = mfma32h(as_f16x8(sv[so]), as_f16x8(pf), acc_o[e]);
-        } else {
-          acc_o[e] = mfma32(as_bf16x8(sv[so]), as_bf16x8(pf), acc_o[e]);
-          if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), as_bf16x8(pf), acc_o[e]);
+        for (int i = 0; i < 8; ++i) pv[i] = sc[u][8 * s2 + i];
+        const u32x4 pf = F16 ? pack8h(pv) : pack8(pv);
+        const int ch = 2 * s2 + g;
+#pragma unroll
+        for (int e = 0; e < NEB; ++e) {
+          const int row = 32 * e + l32;
+          const int so = row * 4 + (ch ^ vswz(row));
+          if (F16) {
+            acc_o[e] = mfma32h(as_f16x8(sv[so]), as_f16x8(pf), acc_o[e]);
+          } else {
+            acc_o[e] = mfma32(as_bf16x8(sv[so]), as_bf16x8(pf), acc_o[e]);
+            if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), as_bf16x8(pf), acc_o[e]);
+          }
         }
       }
     }
