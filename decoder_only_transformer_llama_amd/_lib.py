@@ -25,6 +25,8 @@ NUM_EXPLICIT = 1 << 31
 NUM_QKV_A_PAIR, NUM_QK_PAIR, NUM_V_PAIR = 1 << 0, 1 << 1, 1 << 2
 NUM_O_A_PAIR, NUM_FFN_A_PAIR, NUM_DOWN_A_PAIR = 1 << 3, 1 << 4, 1 << 5
 NUM_ATTN_F16 = 1 << 6
+NUM_QKV_A_F16, NUM_O_A_F16, NUM_FFN_A_F16, NUM_DOWN_A_F16 = 1 << 7, 1 << 8, 1 << 9, 1 << 10
+NUM_GEMM_F16 = NUM_QKV_A_F16 | NUM_O_A_F16 | NUM_FFN_A_F16 | NUM_DOWN_A_F16
 NORM_PRE, NORM_POST, NORM_NONE = 0, 1, 2
 
 EXPORTS = (

@@ -63,7 +63,7 @@ struct Carve {
 
 uint32_t numerics_of(const llama_config *c) {
   if (c->numerics & LLAMA_NUM_EXPLICIT) return c->numerics;
-  return LLAMA_NUM_ATTN_F16 | LLAMA_NUM_O_A_PAIR;
+  return LLAMA_NUM_ATTN_F16 | LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 | LLAMA_NUM_FFN_A_F16;
 }
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
@@ -171,6 +171,12 @@ int check_block_cfg(const llama_config *c, int batch, int seq) {
   // fp16 attention operands are single values: no q/k or v pairs with them
   const uint32_t num = numerics_of(c);
   if ((num & LLAMA_NUM_ATTN_F16) && (num & (LLAMA_NUM_QK_PAIR | LLAMA_NUM_V_PAIR))) return LLAMA_ERR_UNSUPPORTED;
+  // fp16 projection operands are single values too
+  if (((num & LLAMA_NUM_QKV_A_F16) && (num & LLAMA_NUM_QKV_A_PAIR)) ||
+      ((num & LLAMA_NUM_O_A_F16) && (num & LLAMA_NUM_O_A_PAIR)) ||
+      ((num & LLAMA_NUM_FFN_A_F16) && (num & LLAMA_NUM_FFN_A_PAIR)) ||
+      ((num & LLAMA_NUM_DOWN_A_F16) && (num & LLAMA_NUM_DOWN_A_PAIR)))
+    return LLAMA_ERR_UNSUPPORTED;
   // grouped K/V heads: a divisor of n_heads, groups of 1, 2, 4 or 8, K/V
   // width a multiple of the 128-column GEMM tile; bf16 path only
   const int nkv = c->n_kv_heads > 0 ? c->n_kv_heads : c->n_heads;
@@ -441,6 +447,9 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   const bool qkv_pair = num & LLAMA_NUM_QKV_A_PAIR, ffn_pair = num & LLAMA_NUM_FFN_A_PAIR;
   const bool opair = num & LLAMA_NUM_O_A_PAIR, dpair = num & LLAMA_NUM_DOWN_A_PAIR;
   const bool af16 = num & LLAMA_NUM_ATTN_F16;
+  // fp16 activation operands, per projection
+  const int qf16 = (num & LLAMA_NUM_QKV_A_F16) ? 1 : 0, of16 = (num & LLAMA_NUM_O_A_F16) ? 1 : 0;
+  const int ff16 = (num & LLAMA_NUM_FFN_A_F16) ? 1 : 0, df16 = (num & LLAMA_NUM_DOWN_A_F16) ? 1 : 0;
   const int vts = vt_stride_of(seq);
   // Pre-norm (LLaMA) folds RMSNorm into the next projection; post-norm and
   // no-norm feed the branches the trunk itself (operand x, no rstd scale).
@@ -448,7 +457,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
 
   // z = RMSNorm(x; g1): statistic + gained operand; the rstd multiply happens in the QKV epilogue
   HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, pre ? (const uint16_t *)w->attn_norm : nullptr, M, d,
-                           c->norm_eps, b.rstd1, b.xg_hi, qkv_pair ? b.xg_lo : nullptr, s),
+                           c->norm_eps, b.rstd1, b.xg_hi, qkv_pair ? b.xg_lo : nullptr, s, nullptr, 0, nullptr,
+                           qf16),
           "attention norm");
   HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");
 
@@ -490,7 +500,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   for (int i = 0; i < nqp; ++i) {
     q.n_base = qp[i].n_base;
     q.n_end = qp[i].n_end;
-    HIP_TRY(gemm_launch(GemmKey{qp[i].bn, qkv_pair, EPI_QKV}, q, s), "qkv projection");
+    HIP_TRY(gemm_launch(GemmKey{qp[i].bn, qkv_pair, EPI_QKV, qf16}, q, s), "qkv projection");
   }
 
   AttnArgs at{};
@@ -503,6 +513,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   at.o = b.a_hi;
   at.o_lo = opair ? b.a_lo : nullptr;
   at.o_f32 = 0;
+  at.o_f16 = of16;
   at.batch = batch;
   at.seq = seq;
   at.n_heads = H;
@@ -534,7 +545,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   o.r_f32 = x_dtype == LLAMA_F32;
   o.k_splits = oc.splits;
   o.part = b.part;
-  HIP_TRY(gemm_launch(GemmKey{oc.bn, opair, oc.splits > 1 ? EPI_PARTIAL : EPI_RESID}, o, s), "output projection");
+  HIP_TRY(gemm_launch(GemmKey{oc.bn, opair, oc.splits > 1 ? EPI_PARTIAL : EPI_RESID, of16}, o, s),
+          "output projection");
 
   // post-norm: h = RMSNorm(x + attn Wo^T; g1) in place, fp32
   if (post) HIP_TRY(rmsnorm_launch(1, 1, b.h, w->attn_norm, b.h, M, d, c->norm_eps, s, 0), "attention norm");
@@ -542,10 +554,11 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   const uint16_t *g2 = pre ? (const uint16_t *)w->ffn_norm : nullptr;
   if (oc.splits > 1)
     HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, g2, M, d, c->norm_eps, b.rstd2, b.xg_hi,
-                             ffn_pair ? b.xg_lo : nullptr, s, b.part, oc.splits, b.h),
+                             ffn_pair ? b.xg_lo : nullptr, s, b.part, oc.splits, b.h, ff16),
             "ffn norm");
   else
-    HIP_TRY(norm_prep_launch(1, b.h, g2, M, d, c->norm_eps, b.rstd2, b.xg_hi, ffn_pair ? b.xg_lo : nullptr, s),
+    HIP_TRY(norm_prep_launch(1, b.h, g2, M, d, c->norm_eps, b.rstd2, b.xg_hi, ffn_pair ? b.xg_lo : nullptr, s,
+                             nullptr, 0, nullptr, ff16),
             "ffn norm");
   GemmArgs f{};
   f.M = M;
@@ -560,8 +573,9 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   f.B1 = (const uint16_t *)w->w_up;
   f.C = b.u_hi;
   f.C_lo = dpair ? b.u_lo : nullptr;
+  f.c_f16 = df16;   // u in the format the down projection takes
   f.ldc = c->hidden;
-  HIP_TRY(gemm_launch(GemmKey{256, ffn_pair, EPI_SILU}, f, s), "gate/up projection");
+  HIP_TRY(gemm_launch(GemmKey{256, ffn_pair, EPI_SILU, ff16}, f, s), "gate/up projection");
 
   GemmArgs dn{};
   dn.M = M;
@@ -579,7 +593,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   const ResidCfg dc = choose_resid(M, d, c->hidden, dpair);
   dn.k_splits = dc.splits;
   dn.part = b.part;
-  HIP_TRY(gemm_launch(GemmKey{dc.bn, dpair, dc.splits > 1 ? EPI_PARTIAL : EPI_RESID}, dn, s), "down projection");
+  HIP_TRY(gemm_launch(GemmKey{dc.bn, dpair, dc.splits > 1 ? EPI_PARTIAL : EPI_RESID, df16}, dn, s),
+          "down projection");
   if (dc.splits > 1) HIP_TRY(resid_sum_launch(b.h, b.part, dc.splits, (int64_t)M * d, y, s), "down residual");
   if (post) HIP_TRY(rmsnorm_launch(1, 1, y, w->ffn_norm, y, M, d, c->norm_eps, s, 0), "ffn norm");
   return LLAMA_OK;

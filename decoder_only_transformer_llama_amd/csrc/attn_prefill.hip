@@ -300,6 +300,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       for (int i = 0; i < 4; ++i) v[i] = acc_o[e][4 * rq + i] * inv;
       if (a.o_f32) {
         *(f32x4 *)((float *)a.o + obase + e0) = f32x4{v[0], v[1], v[2], v[3]};
+      } else if (a.o_f16) {   // the fp16 operand of an fp16 output projection
+        *(u32x2 *)((u16 *)a.o + obase + e0) = u32x2{(uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16),
+                                                    (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16)};
       } else {
         u16 hi[4], lo[4];
 #pragma unroll

@@ -69,6 +69,21 @@ DEV f32x16 mfma32h(const f16x8 &a, const f16x8 &b, const f32x16 &c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Eight bf16 values (16 bytes) as eight IEEE fp16 values. Exact for zero and
+// for magnitudes in [2^-14, 65504] (fp16 has 3 more significand bits and the
+// exponent fits); smaller magnitudes become fp16 subnormals cut to a
+// multiple of 2^-24, larger ones +-inf. The conversion truncates, which is
+// exact wherever the value is representable.
+DEV u32x4 bf16x8_to_f16x8(const u32x4 &v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = __uint_as_float(v[i] << 16), hi = __uint_as_float(v[i] & 0xffff0000u);
+    r[i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+  }
+  return r;
+}
+
 // fp32 -> IEEE fp16, round to nearest even (overflow gives +-inf).
 DEV u16 f2h(float f) { return __builtin_bit_cast(u16, (_Float16)f); }
 DEV u32x4 pack8h(const float *f) {

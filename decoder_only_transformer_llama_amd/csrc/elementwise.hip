@@ -64,7 +64,7 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 // U consecutive 512-channel chunks per step (dim a multiple of 512 * U when
 // U > 1): all their loads issue before any is used, and __restrict__ lets the
 // compiler move the next step's loads above this step's stores.
-template <bool IN_F32, bool PAIR, bool PARTS, int U>
+template <bool IN_F32, bool PAIR, bool PARTS, int U, bool H = false>
 __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__ x, const u16 *__restrict__ g,
                                                         int64_t rows, int dim, float eps, float *__restrict__ rstd,
                                                         u16 *__restrict__ xg_hi, u16 *__restrict__ xg_lo,
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__
         *(u32x4 *)(xg_hi + base + c) = hi;
         *(u32x4 *)(xg_lo + base + c) = lo;
       } else {
-        *(u32x4 *)(xg_hi + base + c) = pack8(f[u]);
+        *(u32x4 *)(xg_hi + base + c) = H ? pack8h(f[u]) : pack8(f[u]);   // H: IEEE fp16 operand
       }
     }
   }
@@ -139,13 +139,27 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__
 
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
                             float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s, const float *part,
-                            int n_parts, float *h_out) {
+                            int n_parts, float *h_out, int out_f16) {
   if (rows == 0) return hipSuccess;
   if (dim % 8) return hipErrorInvalidValue;
   const bool parts = part != nullptr && n_parts > 0;
   if (parts && h_out == nullptr) return hipErrorInvalidValue;
+  if (out_f16 && xg_lo) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + 3) / 4));
   const int u = dim % 2048 == 0 ? 4 : (dim % 1024 == 0 ? 2 : 1);
+  if (out_f16) {
+#define NPH_CASE(F, R, U_)                                                                                      \
+  if (!!in_f32 == F && parts == R && u == U_) {                                                                 \
+    hipLaunchKernelGGL((norm_prep_kernel<F, false, R, U_, true>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, \
+                       xg_hi, xg_lo, part, n_parts, h_out);                                                     \
+    return hipGetLastError();                                                                                   \
+  }
+    NPH_CASE(true, false, 4) NPH_CASE(true, true, 4) NPH_CASE(false, false, 4) NPH_CASE(false, true, 4)
+    NPH_CASE(true, false, 2) NPH_CASE(true, true, 2) NPH_CASE(false, false, 2) NPH_CASE(false, true, 2)
+    NPH_CASE(true, false, 1) NPH_CASE(true, true, 1) NPH_CASE(false, false, 1) NPH_CASE(false, true, 1)
+#undef NPH_CASE
+    return hipErrorInvalidValue;
+  }
 #define NP_CASE(F, P, R, U_)                                                                                     \
   if (!!in_f32 == F && (xg_lo != nullptr) == P && parts == R && u == U_) {                                      \
     hipLaunchKernelGGL((norm_prep_kernel<F, P, R, U_>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, xg_hi, \

@@ -104,8 +104,12 @@ DEV void interleave() {
   if (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, ID);
 }
 
-template <int BN, bool APAIR, int EPI>
+// F16: the A operand holds IEEE fp16 and the bf16 B fragments are converted
+// to fp16 in registers (exactly, for weights in fp16's normal range) before
+// fp16 matrix-core products: 11-bit activations at the bf16 rate.
+template <int BN, bool APAIR, int EPI, bool F16 = false>
 __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmArgs a) {
+  static_assert(!(F16 && APAIR), "fp16 operands are single");
   using G = GemmCfg<BN, APAIR>;
   constexpr int BM = G::BM, BK = G::BK, CH = G::CH, STAGES = G::STAGES;
   __shared__ u32x4 smem[STAGES * G::STAGE];
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   // Operand fragments of one 16-deep k-substep: A (and its lo part) for the
   // wavefront's 4 row tiles, B for its TN column tiles.
   struct Frag {
-    bf16x8 a[G::TM], al[APAIR ? G::TM : 1], b[G::TN];
+    u32x4 a[G::TM], al[APAIR ? G::TM : 1], b[G::TN];   // raw bits: bf16 (or fp16 when F16)
   };
   auto read_frag = [&](Frag &f, int kt, int ks) {
     const u32x4 *sa = smem + (kt % STAGES) * G::STAGE;
@@ -195,24 +199,30 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
 #pragma unroll
     for (int j = 0; j < G::TN; ++j) {
       const int r = wn * G::WN + j * 32 + l32;
-      f.b[j] = as_bf16x8(sb[r * CH + (c ^ swz<CH>(r))]);
+      f.b[j] = sb[r * CH + (c ^ swz<CH>(r))];   // converted at use (F16), not here: the
+                                                  // LDS wait then stays next to the MFMAs
     }
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
       const int r = wm * G::WM + i * 32 + l32;
       const int off = r * CH + (c ^ swz<CH>(r));
-      f.a[i] = as_bf16x8(sa[off]);
-      if (APAIR) f.al[i] = as_bf16x8(sal[off]);
+      f.a[i] = sa[off];
+      if (APAIR) f.al[i] = sal[off];
     }
   };
   auto mma = [&](const Frag &f) {
+    u32x4 bh[G::TN];
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j) bh[j] = F16 ? bf16x8_to_f16x8(f.b[j]) : f.b[j];
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
 #pragma unroll
-      for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+      for (int j = 0; j < G::TN; ++j)
+        acc[i][j] = F16 ? mfma32h(as_f16x8(f.a[i]), as_f16x8(bh[j]), acc[i][j])
+                        : mfma32(as_bf16x8(f.a[i]), as_bf16x8(bh[j]), acc[i][j]);
       if (APAIR) {
 #pragma unroll
-        for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma32(f.al[i], f.b[j], acc[i][j]);
+        for (int j = 0; j < G::TN; ++j) acc[i][j] = mfma32(as_bf16x8(f.al[i]), as_bf16x8(f.b[j]), acc[i][j]);
       }
     }
   };
@@ -458,6 +468,10 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
           if (l32 & 1) continue;
           const int col = (n0 >> 1) + wn * (G::WN / 2) + (j >> 1) * 32 + l32;
           const int64_t o = (int64_t)row * a.ldc + col;   // even: two columns as one 4-byte word
+          if (a.c_f16) {
+            *(uint32_t *)((u16 *)a.C + o) = (uint32_t)f2h(u) | ((uint32_t)f2h(un) << 16);
+            continue;
+          }
           u16 h0, l0, h1, l1;
           split_pair(u, h0, l0);
           split_pair(un, h1, l1);
@@ -487,7 +501,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   }
 }
 
-template <int BN, bool APAIR, int EPI>
+template <int BN, bool APAIR, int EPI, bool F16 = false>
 hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   using G = GemmCfg<BN, APAIR>;
   const int n_end = a.n_end > 0 ? a.n_end : a.N;
@@ -497,11 +511,15 @@ hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   const int ks = a.k_splits > 1 ? a.k_splits : 1;
   if (a.K % (G::BK * ks)) return hipErrorInvalidValue;
   if (ks > 1 && EPI != EPI_PARTIAL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI>), dim3(nb, ks), dim3(G::NW * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI, F16>), dim3(nb, ks), dim3(G::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace llama
 
-#define GEMM_CASE(BN_, APAIR_, EPI_) \
-  if (key.bn == BN_ && key.apair == APAIR_ && key.epi == EPI_) return gemm_launch_t<BN_, APAIR_, EPI_>(a, s);
+#define GEMM_CASE(BN_, APAIR_, EPI_)                                                       \
+  if (key.bn == BN_ && key.apair == APAIR_ && key.epi == EPI_ && !key.f16)                  \
+    return gemm_launch_t<BN_, APAIR_, EPI_>(a, s);
+#define GEMM_CASE_F16(BN_, EPI_)                                                           \
+  if (key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16)                            \
+    return gemm_launch_t<BN_, false, EPI_, true>(a, s);

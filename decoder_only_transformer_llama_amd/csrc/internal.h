@@ -29,8 +29,9 @@ struct GemmArgs {
   int n_seg;                     // BMODE_CONCAT3: rows of B0 (the query projection)
   int n_seg_kv;                  // BMODE_CONCAT3: rows of B1 and of B2 (0: n_seg)
   // EPI_STORE / EPI_RESID / EPI_SILU outputs
-  void *C;            // f32 or bf16 (EPI_SILU: bf16 hi)
+  void *C;            // f32 or bf16 (EPI_SILU: bf16 hi, or fp16 when c_f16)
   uint16_t *C_lo;     // EPI_SILU / EPI_STORE bf16: optional lo part
+  int c_f16;          // EPI_SILU: u as IEEE fp16 (the operand of an fp16 down projection)
   int c_f32;          // EPI_STORE: 1 -> f32 output, 0 -> bf16
   int64_t ldc;
   const void *R;      // EPI_RESID residual [M, ldc]
@@ -59,6 +60,7 @@ __host__ __device__ inline const uint16_t *concat3_row(const uint16_t *B0, const
 
 struct GemmKey {
   int bn, apair, epi;
+  int f16 = 0;   // A operand fp16, B (bf16 weights) converted to fp16 in registers
 };
 
 // Returns a hipError_t; hipErrorInvalidValue when no instance matches `key`.
@@ -71,9 +73,10 @@ hipError_t gemm_launch_misc(const GemmKey &key, const GemmArgs &a, hipStream_t s
 struct AttnArgs {
   const uint16_t *qh, *ql, *kh, *kl;   // [batch*seq, dim]
   const uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, seq]
-  void *o;                             // [batch*seq, dim] f32 or bf16 (hi)
+  void *o;                             // [batch*seq, dim] f32, bf16 (hi) or fp16
   uint16_t *o_lo;                      // optional lo part (bf16 output only)
   int o_f32;
+  int o_f16;                           // output as IEEE fp16 (no lo part)
   int batch, seq, n_heads, head_dim, dim;
   int kv_dim, n_kv_heads;              // k rows [batch*seq, kv_dim]; v^T [batch, n_kv_heads, head_dim, vt_stride]
   int vt_stride;                       // row stride of v^T (>= seq, multiple of 64)
@@ -93,9 +96,11 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 // With `part` (n_parts fp32 [rows, dim] split-K partial products), the row is
 // first h = x + part[0] + ... (split order), written to h_out (fp32), and the
 // statistics and product are those of h.
+// out_f16: the product as IEEE fp16 (single; xg_lo must be null).
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
                             float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s,
-                            const float *part = nullptr, int n_parts = 0, float *h_out = nullptr);
+                            const float *part = nullptr, int n_parts = 0, float *h_out = nullptr,
+                            int out_f16 = 0);
 // Index of the largest logit per row (lowest among equals; -1 if the row has a NaN).
 hipError_t argmax_launch(const float *logits, int64_t rows, int vocab, int32_t *out, hipStream_t s);
 // y = r + part[0] + ... + part[n_parts-1], fp32, n elements (n % 4 == 0).

@@ -71,13 +71,21 @@ typedef enum {
 /* Numerics options of the bf16 path (llama_config.numerics). Weights are
  * exact bf16 inputs; an activation operand of a bf16 matrix-core product is
  * either rounded to bf16 or carried as an exact-to-2^-16 pair hi + lo of two
- * bf16 values (two products, same fp32 accumulator). Inside attention, q, k,
- * v and the probabilities may instead be IEEE fp16 (LLAMA_NUM_ATTN_F16: 11
- * significant bits, one matrix-core pass per product; |q|, |k|, |v| must stay
- * below 65504). LLAMA_NUM_DEFAULT (0) selects the library's default set,
- * LLAMA_NUM_ATTN_F16 | LLAMA_NUM_O_A_PAIR; LLAMA_NUM_EXPLICIT plus any of the
- * bits selects exactly those (ATTN_F16 excludes QK_PAIR and V_PAIR). The KV
- * cache is bf16 in every mode. */
+ * bf16 values (two products, same fp32 accumulator). Other bits use IEEE fp16
+ * operands instead (11 significant bits against bf16's 8, one pass per
+ * product, values below 65504 in magnitude):
+ *  - LLAMA_NUM_ATTN_F16: q, k, v and the probabilities inside attention;
+ *  - LLAMA_NUM_{QKV,O,FFN,DOWN}_A_F16: the activation operand of that block
+ *    projection (x*g1, the attention output, h*g2, SiLU(gate)*up); the bf16
+ *    weights are converted to fp16 in registers, exactly for magnitudes in
+ *    [2^-14, 65504] (smaller ones become fp16 subnormals, within 2^-24).
+ *    LLAMA_NUM_GEMM_F16 is all four.
+ * LLAMA_NUM_DEFAULT (0) selects the library's default set,
+ * LLAMA_NUM_ATTN_F16 | LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 |
+ * LLAMA_NUM_FFN_A_F16 (SiLU(gate)*up stays a single bf16 value);
+ * LLAMA_NUM_EXPLICIT plus any of the
+ * bits selects exactly those (ATTN_F16 excludes QK_PAIR and V_PAIR; an
+ * operand is either a pair or fp16). The KV cache is bf16 in every mode. */
 #define LLAMA_NUM_DEFAULT 0u
 #define LLAMA_NUM_EXPLICIT (1u << 31)
 #define LLAMA_NUM_QKV_A_PAIR (1u << 0)  /* x*g1 operand of the Q/K/V projection */
@@ -87,6 +95,11 @@ typedef enum {
 #define LLAMA_NUM_FFN_A_PAIR (1u << 4)  /* h*g2 operand of the gate/up projection */
 #define LLAMA_NUM_DOWN_A_PAIR (1u << 5) /* SiLU(gate)*up operand of the down projection */
 #define LLAMA_NUM_ATTN_F16 (1u << 6)    /* q, k, v and probabilities as fp16 in prefill attention */
+#define LLAMA_NUM_QKV_A_F16 (1u << 7)   /* x*g1 operand of the Q/K/V projection as fp16 */
+#define LLAMA_NUM_O_A_F16 (1u << 8)     /* attention output into the Wo projection as fp16 */
+#define LLAMA_NUM_FFN_A_F16 (1u << 9)   /* h*g2 operand of the gate/up projection as fp16 */
+#define LLAMA_NUM_DOWN_A_F16 (1u << 10) /* SiLU(gate)*up operand of the down projection as fp16 */
+#define LLAMA_NUM_GEMM_F16 (LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 | LLAMA_NUM_FFN_A_F16 | LLAMA_NUM_DOWN_A_F16)
 
 /* Where a block's two RMSNorms sit ([P1] "Pre-norm: the norm goes on the
  * branch, not the trunk" and "Now break it"). With Attn and FFN the two

@@ -157,6 +157,10 @@ def test_grouped_kv_heads_validation_and_sizes():
     assert ws(numerics=L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_O_A_PAIR) == 0
     assert ws(numerics=L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_QK_PAIR) == L.LLAMA_ERR_UNSUPPORTED
     assert ws(numerics=L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_V_PAIR) == L.LLAMA_ERR_UNSUPPORTED
+    # fp16 projection operands are single values as well
+    assert ws(numerics=L.NUM_EXPLICIT | L.NUM_GEMM_F16) == 0
+    for pair in (L.NUM_QKV_A_PAIR, L.NUM_O_A_PAIR, L.NUM_FFN_A_PAIR, L.NUM_DOWN_A_PAIR):
+        assert ws(numerics=L.NUM_EXPLICIT | L.NUM_GEMM_F16 | pair) == L.LLAMA_ERR_UNSUPPORTED
     # fewer key/value heads shrink the packed decode weights by exactly the Wk, Wv rows
     for nkv in (32, 8):
         assert lib.llama_decode_pack_size(ctypes.byref(_cfg(n_kv_heads=nkv)), ctypes.byref(n)) == 0

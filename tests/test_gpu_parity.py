@@ -22,10 +22,12 @@ pytestmark = pytest.mark.gpu
 TOL_F32 = 1e-4
 TOL_BF16 = 2e-2
 # Every GEMM operand carried as a bf16 hi/lo pair; the attention
-# probabilities stay single bf16 values, so the statistic shrinks (2-3x on a
-# block, 2-3x on two-layer logits) but does not vanish.
+# probabilities stay single bf16 values, so the statistic shrinks against
+# single bf16 operands (2-3x on a block, 2-3x on two-layer logits) but does
+# not vanish.
 ALL_PAIRS = (L.NUM_EXPLICIT | L.NUM_QKV_A_PAIR | L.NUM_QK_PAIR | L.NUM_V_PAIR | L.NUM_O_A_PAIR
              | L.NUM_FFN_A_PAIR | L.NUM_DOWN_A_PAIR)
+ALL_SINGLE_BF16 = L.NUM_EXPLICIT   # every operand one bf16 value, attention included
 
 
 def ops():
@@ -194,13 +196,28 @@ def test_block_small(wid):
 
 @pytest.mark.parametrize("wid", [100, 103, 104])
 def test_block_all_pairs(wid):
-    """Within the bound, and closer than the default operand set: an operand
-    whose low half were dropped would leave the two errors equal."""
+    """Within the bound, and closer than with every operand a single bf16
+    value: an operand whose low half were dropped would leave the two equal."""
     y, want, w = run_block(wid, numerics=ALL_PAIRS)
     err = rel_err(y, want)
-    err_def = rel_err(*run_block(wid)[:2])
-    print(f"block {w.name}: max|d|/rms = {err:.3e} all operands as pairs, {err_def:.3e} default")
-    assert err < TOL_BF16 and err < 0.8 * err_def
+    err_single = rel_err(*run_block(wid, numerics=ALL_SINGLE_BF16)[:2])
+    print(f"block {w.name}: max|d|/rms = {err:.3e} all operands as pairs, {err_single:.3e} all single bf16")
+    assert err < TOL_BF16 and err < 0.8 * err_single
+
+
+# Other operand sets of the four projections: all bf16 (attention output as a
+# pair), and all fp16 (weights converted in registers).
+BF16_OPERANDS = L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_O_A_PAIR
+F16_OPERANDS = L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_GEMM_F16
+
+
+@pytest.mark.parametrize("wid", [100, 103, 104])
+@pytest.mark.parametrize("numerics", [BF16_OPERANDS, F16_OPERANDS])
+def test_block_operand_sets(wid, numerics):
+    y, want, w = run_block(wid, numerics=numerics)
+    err = rel_err(y, want)
+    print(f"block {w.name} (numerics {numerics:#x}): max|d|/rms = {err:.3e}")
+    assert err < TOL_BF16
 
 
 def test_block_deterministic():
@@ -215,10 +232,11 @@ def test_block_deterministic():
 
 
 @pytest.mark.slow
-def test_block_7b_full():
-    y, want, w = run_block(1)
+@pytest.mark.parametrize("numerics", [L.NUM_DEFAULT, BF16_OPERANDS, F16_OPERANDS])
+def test_block_7b_full(numerics):
+    y, want, w = run_block(1, numerics=numerics)
     err = rel_err(y, want)
-    print(f"block {w.name}: max|d|/rms = {err:.3e}")
+    print(f"block {w.name} (numerics {numerics:#x}): max|d|/rms = {err:.3e}")
     assert err < TOL_BF16
 
 
@@ -250,11 +268,12 @@ def oracle_caches(w, B):
 
 
 # 101: multi-head; 105: grouped-query (4 query heads per key/value head); 106:
-# multi-query. 105 (width 1024) runs with every GEMM operand as a pair: at the
-# default operand set its two-layer logits reach 2.1e-2, all of it from the
-# bf16 rounding points (its grouped path is bitwise the multi-head path, see
-# test_grouped_kv_equals_multi_head_with_repeated_kv).
-@pytest.mark.parametrize("wid,numerics", [(101, L.NUM_DEFAULT), (105, ALL_PAIRS), (106, L.NUM_DEFAULT)])
+# multi-query; each with the default operands and with every GEMM operand a
+# bf16 pair. (With single bf16 projection operands instead of the fp16
+# default, 105's two-layer logits reach 2.1e-2, all of it from the bf16
+# rounding points.)
+@pytest.mark.parametrize("wid,numerics", [(101, L.NUM_DEFAULT), (105, L.NUM_DEFAULT), (106, L.NUM_DEFAULT),
+                                          (105, ALL_PAIRS)])
 def test_model_prefill_then_decode(wid, numerics):
     w, m, layers, gl = small_model(wid, numerics=numerics)
     B, T = w.batch, w.seq
@@ -298,10 +317,10 @@ def test_model_prefill_all_pairs(wid):
                            lambda l: (lw[l], caches[l][0], caches[l][1]), w.n_layers, host(gl["final_norm"]),
                            host(gl["output"]), w.n_heads, w.eps)
     err = rel_err(logits, want)
-    _, md, _, _ = small_model(wid, layers=layers)
-    err_def = rel_err(md.forward(toks[:, :T].contiguous(), m.new_cache(B, "cuda"), m.new_cache(B, "cuda")), want)
-    print(f"{w.name}: prefill logits {err:.3e} all operands as pairs, {err_def:.3e} default")
-    assert err < TOL_BF16 and err < 0.8 * err_def
+    _, ms, _, _ = small_model(wid, numerics=ALL_SINGLE_BF16, layers=layers)
+    err_single = rel_err(ms.forward(toks[:, :T].contiguous(), m.new_cache(B, "cuda"), m.new_cache(B, "cuda")), want)
+    print(f"{w.name}: prefill logits {err:.3e} all operands as pairs, {err_single:.3e} all single bf16")
+    assert err < TOL_BF16 and err < 0.8 * err_single
 
 
 @pytest.mark.parametrize("wid", [105, 106])
