@@ -446,6 +446,71 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
     return;
   }
 
+  // Row-contiguous stores (RESID, PARTIAL, STORE): each 32 x 32 accumulator
+  // block goes through a per-wavefront LDS tile and comes back as 8 rows per
+  // instruction, 8 lanes per row, 4 consecutive columns per lane: every
+  // residual load and output store then covers whole 128-byte row segments
+  // with 16-byte (fp32) or 8-byte (bf16) vectors, instead of one column per
+  // lane.
+  const uintptr_t base_bits = (uintptr_t)a.C | (uintptr_t)a.C_lo | (uintptr_t)a.R | (uintptr_t)a.part;
+  if (EPI != EPI_SILU && a.N % 32 == 0 && a.ldc % 16 == 0 && base_bits % 16 == 0) {
+    __builtin_amdgcn_s_barrier();  // all waves are done with the K-loop buffers
+    constexpr int TQ = 40;         // row stride (floats): the two half-waves write disjoint banks
+    float *tq = (float *)smem + wave * (32 * TQ);
+    const int r8 = lane >> 3, c4 = 4 * (lane & 7);
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int rb = m0 + wm * G::WM + i * 32;   // first row of the block
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tq[(8 * (r >> 2) + 4 * g + (r & 3)) * TQ + l32] = acc[i][j][r];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = *(const f32x4 *)(tq + (8 * q + r8) * TQ + c4);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();   // the tile is rewritten for the next block
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int col = n0 + wn * G::WN + j * 32 + c4;   // N % 32 == 0: the block is inside or outside
+        if (col >= a.N) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = rb + 8 * q + r8;
+          if (row >= a.M) continue;
+          f32x4 x = v[q];
+          if (a.rstd) x *= a.rstd[row];
+          if (EPI == EPI_PARTIAL) {
+            *(f32x4 *)(a.part + (int64_t)blockIdx.y * a.M * a.N + (int64_t)row * a.N + col) = x;
+            continue;
+          }
+          const int64_t o = (int64_t)row * a.ldc + col;
+          if (EPI == EPI_RESID) {
+            if (a.r_f32) {
+              x += *(const f32x4 *)((const float *)a.R + o);
+            } else {
+              const u32x2 r2 = *(const u32x2 *)((const u16 *)a.R + o);
+              x += f32x4{__uint_as_float(r2[0] << 16), __uint_as_float(r2[0] & 0xffff0000u),
+                         __uint_as_float(r2[1] << 16), __uint_as_float(r2[1] & 0xffff0000u)};
+            }
+          }
+          if (EPI == EPI_RESID || a.c_f32) {
+            *(f32x4 *)((float *)a.C + o) = x;
+          } else {
+            u16 h[4], l[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) split_pair(x[k], h[k], l[k]);
+            *(u32x2 *)((u16 *)a.C + o) = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+            if (a.C_lo) *(u32x2 *)(a.C_lo + o) = u32x2{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
+          }
+        }
+      }
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < G::TM; ++i) {
 #pragma unroll
