@@ -256,7 +256,12 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   };
   for (int kt = 0; kt < nk - 1; ++kt) {
     issue(kt + STAGES - 1);
+    // the substeps before the barrier at raised wave priority: when both
+    // wavefronts of a SIMD are ready, the one in its MFMA stretch issues
+    // first (~1.5% on the 7B block)
+    __builtin_amdgcn_s_setprio(1);
     inner(kt);
+    __builtin_amdgcn_s_setprio(0);
     WAIT_VMCNT((STAGES - 2) * G::LPS);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
