@@ -87,13 +87,33 @@ def counter_per_dispatch(d: str, counter: str, kernel: str) -> Tuple[float, int]
     return sum(vals.values()) / len(vals), len(vals)
 
 
+def trace_medians(d: str) -> Dict[str, float]:
+    """Median duration (ns) per kernel name from the run's kernel trace."""
+    durs: Dict[str, List[int]] = {}
+    for f in _find(d, "kernel_trace.csv"):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                durs.setdefault(r["Kernel_Name"], []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    out = {}
+    for k, v in durs.items():
+        v.sort()
+        n = len(v)
+        out[k] = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return out
+
+
 def write_stats(d: str, out: str, command: str, top: int) -> None:
     rows = stats_table(d)
+    med = trace_medians(d)
     total = sum(r[2] for r in rows)
     lines = ["# rocprofv3 kernel statistics", "", "command:", "  " + command, "",
-             f"{'avg us':>10} {'calls':>6} {'total ms':>9} {'%':>6}  kernel"]
+             "avg: rocprofv3's mean over every dispatch; median: from the kernel trace of the same run",
+             "(calls right after an idle gap, while the clock ramps up, pull the mean above the median)", "",
+             f"{'avg us':>10} {'median us':>10} {'calls':>6} {'total ms':>9} {'%':>6}  kernel"]
     for name, calls, tot, avg, pct in rows[:top]:
-        lines.append(f"{avg / 1e3:10.2f} {calls:6d} {tot / 1e6:9.3f} {pct:6.2f}  {short_name(name)}")
+        m = med.get(name)
+        ms = f"{m / 1e3:10.2f}" if m is not None else f"{'-':>10}"
+        lines.append(f"{avg / 1e3:10.2f} {ms} {calls:6d} {tot / 1e6:9.3f} {pct:6.2f}  {short_name(name)}")
     lines += ["", f"all kernels: {total / 1e6:.3f} ms over {sum(r[1] for r in rows)} dispatches"]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
