@@ -247,12 +247,13 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
         for (int r = 0; r < 16; ++r) acc_o[e][r] *= alpha;
     }
     const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    const float mc = -m_use * c;   // exponent (s - m) c as one fma: s c - m c
     float psum = 0.f;
 #pragma unroll
     for (int u = 0; u < SUB; ++u)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float pr = __builtin_amdgcn_exp2f((sc[u][r] - m_use) * c);   // exp2(-inf) = 0 for masked keys
+        const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][r], c, mc));   // exp2(-inf) = 0 for masked keys
         sc[u][r] = pr;
         psum += pr;
       }
@@ -301,8 +302,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       if (a.o_f32) {
         *(f32x4 *)((float *)a.o + obase + e0) = f32x4{v[0], v[1], v[2], v[3]};
       } else if (a.o_f16) {   // the fp16 operand of an fp16 output projection
-        *(u32x2 *)((u16 *)a.o + obase + e0) = u32x2{(uint32_t)f2h(v[0]) | ((uint32_t)f2h(v[1]) << 16),
-                                                    (uint32_t)f2h(v[2]) | ((uint32_t)f2h(v[3]) << 16)};
+        *(u32x2 *)((u16 *)a.o + obase + e0) = u32x2{pack2h(v[0], v[1]), pack2h(v[2], v[3])};
       } else {
         u16 hi[4], lo[4];
 #pragma unroll

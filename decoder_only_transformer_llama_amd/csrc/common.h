@@ -86,10 +86,17 @@ DEV u32x4 bf16x8_to_f16x8(const u32x4 &v) {
 
 // fp32 -> IEEE fp16, round to nearest even (overflow gives +-inf).
 DEV u16 f2h(float f) { return __builtin_bit_cast(u16, (_Float16)f); }
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+// Two floats as two packed fp16 (low half = first), the same rounding as
+// f2h; one v_cvt_pk_f16_f32 on gfx950.
+DEV uint32_t pack2h(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, f16x2));
+}
 DEV u32x4 pack8h(const float *f) {
   u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = (uint32_t)f2h(f[2 * i]) | ((uint32_t)f2h(f[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) r[i] = pack2h(f[2 * i], f[2 * i + 1]);
   return r;
 }
 

@@ -539,7 +539,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
           const int col = (n0 >> 1) + wn * (G::WN / 2) + (j >> 1) * 32 + l32;
           const int64_t o = (int64_t)row * a.ldc + col;   // even: two columns as one 4-byte word
           if (a.c_f16) {
-            *(uint32_t *)((u16 *)a.C + o) = (uint32_t)f2h(u) | ((uint32_t)f2h(un) << 16);
+            *(uint32_t *)((u16 *)a.C + o) = pack2h(u, un);
             continue;
           }
           u16 h0, l0, h1, l1;
