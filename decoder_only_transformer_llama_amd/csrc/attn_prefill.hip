@@ -94,7 +94,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   int bh, qt;
   attn_tile_of(blockIdx.x, nqt, a.batch * a.n_heads, bh, qt);
   const int b = bh / a.n_heads, h = bh % a.n_heads;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wavefront index as a scalar: the block each wavefront loads and its
+  // diagonal tests then branch on scalars, without per-lane masks
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int q0 = qt * 128;
   const int qi = q0 + 32 * w + l32;          // this lane's query
@@ -114,32 +116,43 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   // Ring slot st % NST holds tiles SUB*st .. SUB*st + SUB-1; tiles past the
   // last reload the last tile (their keys are masked, or the slot is never
   // read) so that every step waits on the same number of loads.
+  // Per block this wavefront loads: K or v^T (wavefront-uniform), the lane's
+  // fixed part of the source address, and the block's place in a stage.
+  constexpr int NQB = NBLK / 4;
+  bool isk[NQB];
+  const u16 *lsrc[NQB];
+  int lrow[NQB], ldst[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    const int blk = w * NQB + qb;
+    isk[qb] = blk < KBLK * (QKPAIR ? 2 : 1);
+    if (isk[qb]) {
+      const int part = blk / KBLK, kb = blk % KBLK;
+      const int row = kb * (64 / KCH) + lane / KCH;
+      const int c = (lane % KCH) ^ rswz<KCH>(row);
+      lrow[qb] = row;
+      lsrc[qb] = (part ? a.kl : a.kh) + tok0 * kvd + hk * HD + 8 * c;
+      ldst[qb] = part * KTILE + kb * 64;
+    } else {
+      const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
+      const int part = vblk / VBLK, vb = vblk % VBLK;
+      const int e = vb * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ vswz(e);
+      lrow[qb] = 0;
+      lsrc[qb] = (part ? a.vtl : a.vth) + vbase + (int64_t)e * a.vt_stride + 8 * c;
+      ldst[qb] = KTILE * (QKPAIR ? 2 : 1) + part * VTILE + vb * 64;
+    }
+  }
   auto issue = [&](int st_slot) {
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       u32x4 *st = smem + (st_slot % NST) * STAGE + u * STAGE1;
       const int kt = min(st_slot * SUB + u, n_kt - 1);
 #pragma unroll
-      for (int qb = 0; qb < NBLK / 4; ++qb) {
-        const int blk = w * (NBLK / 4) + qb;
-        const u16 *src;
-        u32x4 *dst;
-        if (blk < KBLK * (QKPAIR ? 2 : 1)) {
-          const int part = blk / KBLK, kb = blk % KBLK;
-          const int row = kb * (64 / KCH) + lane / KCH;
-          const int c = (lane % KCH) ^ rswz<KCH>(row);
-          const int key = min(kt * KT + row, S - 1);   // rows past S load a valid key; masked later
-          src = (part ? a.kl : a.kh) + (tok0 + key) * kvd + hk * HD + 8 * c;
-          dst = st + part * KTILE + kb * 64;
-        } else {
-          const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
-          const int part = vblk / VBLK, vb = vblk % VBLK;
-          const int e = vb * 16 + (lane >> 2);
-          const int c = (lane & 3) ^ vswz(e);
-          src = (part ? a.vtl : a.vth) + vbase + (int64_t)e * a.vt_stride + kt * KT + 8 * c;
-          dst = st + KTILE * (QKPAIR ? 2 : 1) + part * VTILE + vb * 64;
-        }
-        __builtin_amdgcn_global_load_lds((const void *)src, ATT_LDS(dst), 16, 0, 0);
+      for (int qb = 0; qb < NQB; ++qb) {
+        // K row: rows past S load a valid key (masked later); v^T: key columns
+        const u16 *src = isk[qb] ? lsrc[qb] + (int64_t)min(kt * KT + lrow[qb], S - 1) * kvd : lsrc[qb] + kt * KT;
+        __builtin_amdgcn_global_load_lds((const void *)src, ATT_LDS(st + ldst[qb]), 16, 0, 0);
       }
     }
   };
