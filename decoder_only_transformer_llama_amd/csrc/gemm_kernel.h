@@ -114,7 +114,8 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   constexpr int BM = G::BM, BK = G::BK, CH = G::CH, STAGES = G::STAGES;
   __shared__ u32x4 smem[STAGES * G::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wavefront index as a scalar: LDS destinations of the direct loads are then scalar sums
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / (G::NW / 2), wn = wave % (G::NW / 2);
   const int g = lane >> 5, l32 = lane & 31;
 
