@@ -439,9 +439,11 @@ PackLayout pack_layout(const llama_config *c) {
 }
 
 // ------------------------------------------------------------------ block launch sequences
+// make_rope: build the (cos, sin) table in b.rope_tab first (a stack of blocks
+// over the same positions builds it once).
 int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype, const void *x, float *y,
                int batch, int seq, const BlockWs &b, uint16_t *kcache, uint16_t *vcache, int max_seq,
-               hipStream_t s) {
+               hipStream_t s, bool make_rope = true) {
   const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq;
   const uint32_t num = numerics_of(c);
   const bool qkv_pair = num & LLAMA_NUM_QKV_A_PAIR, ffn_pair = num & LLAMA_NUM_FFN_A_PAIR;
@@ -460,7 +462,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
                            c->norm_eps, b.rstd1, b.xg_hi, qkv_pair ? b.xg_lo : nullptr, s, nullptr, 0, nullptr,
                            qf16),
           "attention norm");
-  HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");
+  if (make_rope) HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");
 
   GemmArgs q{};
   q.M = M;
@@ -1059,9 +1061,11 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
   const BlockWs b = carve_block(cv, c, batch, seq);
   HIP_TRY(embed_launch(0, w->tok_embeddings, tokens, n, d, c->vocab, xa, s), "embedding");
   const size_t layer_elems = (size_t)batch * kv_heads(c) * c->max_seq * hd;
+  HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");   // shared by every layer
   for (int l = 0; l < c->n_layers; ++l) {
     st = block_bf16(c, &w->layers[l], LLAMA_F32, xa, xb, batch, seq, b,
-                    (uint16_t *)k_cache + l * layer_elems, (uint16_t *)v_cache + l * layer_elems, c->max_seq, s);
+                    (uint16_t *)k_cache + l * layer_elems, (uint16_t *)v_cache + l * layer_elems, c->max_seq, s,
+                    false);
     if (st) return st;
     std::swap(xa, xb);
   }

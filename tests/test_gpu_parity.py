@@ -115,6 +115,22 @@ def test_linear_bf16(rows, n, k):
     assert_bf16_rounded(yb, want) if rows * n < 10 ** 6 else None
 
 
+def test_linear_unaligned_output():
+    """An output 4 bytes off 16-byte alignment takes the column-per-lane
+    epilogue (the row-segment vector stores need 16-byte aligned rows)."""
+    rows, n, k = 70, 256, 128
+    x = I.normal((rows, k), 903, 0, 0, dtype=torch.bfloat16, device="cuda")
+    w = I.normal((n, k), 903, 0, 1, std=0.02, dtype=torch.bfloat16, device="cuda")
+    buf = torch.full((rows * n + 4,), float("nan"), dtype=torch.float32, device="cuda")
+    y = buf[1:1 + rows * n].view(rows, n)
+    assert y.data_ptr() % 16 == 4
+    L.check(L.load().llama_linear(L.LLAMA_BF16, L.LLAMA_BF16, L.LLAMA_F32, x.data_ptr(), w.data_ptr(), y.data_ptr(),
+                                  rows, n, k, torch.cuda.current_stream().cuda_stream), "llama_linear")
+    torch.cuda.synchronize()
+    assert torch.equal(y, ops().linear(x, w))           # same products, other store path
+    assert torch.isnan(buf[0]) and torch.isnan(buf[1 + rows * n:]).all()   # nothing written outside
+
+
 def test_linear_mixed_dtypes_rejected():
     x = torch.zeros((4, 64), device="cuda")
     w = torch.zeros((8, 64), dtype=torch.bfloat16, device="cuda")
