@@ -61,6 +61,8 @@ struct Carve {
   }
 };
 
+constexpr uint32_t kNumOptionBits = (LLAMA_NUM_DOWN_A_F16 << 1) - 1;   // bits 0 .. 10 of the numerics field
+
 uint32_t numerics_of(const llama_config *c) {
   if (c->numerics & LLAMA_NUM_EXPLICIT) return c->numerics;
   return LLAMA_NUM_ATTN_F16 | LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 | LLAMA_NUM_FFN_A_F16;
@@ -168,6 +170,10 @@ int check_block_cfg(const llama_config *c, int batch, int seq) {
     if (c->dim % 256 || c->hidden % 128) return LLAMA_ERR_UNSUPPORTED;
   }
   if (c->norm_placement < LLAMA_NORM_PRE || c->norm_placement > LLAMA_NORM_NONE) return LLAMA_ERR_UNSUPPORTED;
+  // numerics: 0, or LLAMA_NUM_EXPLICIT with known option bits
+  if (c->numerics != LLAMA_NUM_DEFAULT &&
+      (!(c->numerics & LLAMA_NUM_EXPLICIT) || (c->numerics & ~(LLAMA_NUM_EXPLICIT | kNumOptionBits))))
+    return LLAMA_ERR_UNSUPPORTED;
   // fp16 attention operands are single values: no q/k or v pairs with them
   const uint32_t num = numerics_of(c);
   if ((num & LLAMA_NUM_ATTN_F16) && (num & (LLAMA_NUM_QK_PAIR | LLAMA_NUM_V_PAIR))) return LLAMA_ERR_UNSUPPORTED;

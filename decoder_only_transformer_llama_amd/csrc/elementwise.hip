@@ -57,7 +57,8 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 // ------------------------------------------------------------------ norm prep
 // One 64-lane wavefront per row, 8 consecutive channels per lane and step:
 // rstd = 1/sqrt(mean(x^2) + eps) (sum reduced across the wavefront) and the
-// GEMM operand x * g as bf16 hi (+ lo). The product's consumer multiplies its
+// GEMM operand x * g as bf16 hi (+ lo), or as IEEE fp16 (H). The product's
+// consumer multiplies its
 // fp32 accumulator by rstd, which completes RMSNorm(x; g) W^T. dim % 8 == 0.
 // g == nullptr: the operand is x itself (a block without a norm before the
 // projection; rstd is then written but not used).

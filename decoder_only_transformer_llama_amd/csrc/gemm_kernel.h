@@ -1,8 +1,9 @@
-// bf16 matrix-core GEMM for gfx950: C[M, N] = A[M, K] * B[N, K]^T, fp32 accumulate.
+// Matrix-core GEMM for gfx950 over bf16 weights: C[M, N] = A[M, K] * B[N, K]^T,
+// fp32 accumulate.
 //
 // One workgroup = 8 wavefronts (2 x 4, two per SIMD so one wavefront's LDS and
 // barrier waits overlap the other's matrix-core work) computing a 256 x BN tile
-// with v_mfma_f32_32x32x16_bf16 (each wavefront 128 x BN/4). A and B move
+// with v_mfma_f32_32x32x16_{bf16,f16} (each wavefront 128 x BN/4). A and B move
 // HBM -> LDS with global_load_lds_dwordx4 (no register staging): every
 // wavefront instruction drops 64 lanes x 16 bytes into one contiguous 1 KB
 // block of LDS, and the row/chunk each lane fetches is chosen so the block
@@ -13,24 +14,30 @@
 // waits. The 64-deep step halves the barriers per MFMA: on the 7B block the
 // QKV, gate/up and down GEMMs run 2.5-5% faster than with 32-deep steps.
 //
-// A may be a bf16 hi/lo pair (A_lo non-null): both parts are multiplied into
+// A is bf16, a bf16 hi/lo pair (A_lo non-null: both parts are multiplied into
 // the same accumulator, which carries an fp32 activation at ~2^-16 relative
-// accuracy through bf16 matrix cores.
+// accuracy through bf16 matrix cores), or IEEE fp16 (F16: the bf16 weights
+// are converted to fp16 in registers, exactly in fp16's normal range, and the
+// fp16 matrix cores run at the bf16 rate with 11-bit activations).
 //
 // Epilogues (elementwise work of the block fused into the producing GEMM):
 //  - every epilogue first scales row r by rstd[r] when rstd is given: the
 //    RMSNorm statistic, so the product is RMSNorm(x; g) W^T with the operand
 //    x * g prepared by the norm-prep kernel (diag(rstd) commutes with the
 //    product; RMSNorm with gain as on the chenyuan1125.github.io LLaMA page).
-//  - EPI_QKV: RoPE of q and k in registers (pair partner in the neighbouring
-//    lane), hi/lo split; v is written transposed per head ([b][h][e][s]) via an
-//    LDS transpose so the stores stay 16-byte vectors; optional KV-cache copy.
+//  - EPI_QKV: RoPE of q and k after a per-wavefront LDS transpose (a lane
+//    owns 16 consecutive columns of one row), stored as fp16 or a bf16 hi/lo
+//    pair; v is written transposed per head ([b][h][e][s]) via an LDS
+//    transpose so the stores stay 16-byte vectors; optional bf16 KV-cache copy.
 //  - EPI_SILU: B rows interleave W_gate and W_up in blocks of 32, so a lane
-//    holds gate and up of the same output; u = SiLU(gate) * up.
+//    holds gate and up of the same output; u = SiLU(gate) * up (bf16, hi/lo
+//    pair or fp16).
 //  - EPI_RESID: C = R + acc (the pre-norm skip connection), fp32 out.
 //  - EPI_PARTIAL: split-K partial product of range blockIdx.y, fp32, into
 //    part[blockIdx.y]; the consumer adds the ranges in order (no atomics).
 //  - EPI_STORE: plain fp32 or bf16 (hi/lo) store.
+//  RESID, PARTIAL and STORE leave through an LDS transpose as whole 128-byte
+//  row segments when the output allows (N % 32 == 0, 16-byte aligned rows).
 #pragma once
 
 #include "common.h"

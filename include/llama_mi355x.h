@@ -85,7 +85,9 @@ typedef enum {
  * LLAMA_NUM_FFN_A_F16 (SiLU(gate)*up stays a single bf16 value);
  * LLAMA_NUM_EXPLICIT plus any of the
  * bits selects exactly those (ATTN_F16 excludes QK_PAIR and V_PAIR; an
- * operand is either a pair or fp16). The KV cache is bf16 in every mode. */
+ * operand is either a pair or fp16). Any other value (option bits without
+ * LLAMA_NUM_EXPLICIT, unknown bits) is LLAMA_ERR_UNSUPPORTED. The KV cache is
+ * bf16 in every mode. */
 #define LLAMA_NUM_DEFAULT 0u
 #define LLAMA_NUM_EXPLICIT (1u << 31)
 #define LLAMA_NUM_QKV_A_PAIR (1u << 0)  /* x*g1 operand of the Q/K/V projection */

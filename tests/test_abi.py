@@ -159,6 +159,8 @@ def test_grouped_kv_heads_validation_and_sizes():
     assert ws(numerics=L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_V_PAIR) == L.LLAMA_ERR_UNSUPPORTED
     # fp16 projection operands are single values as well
     assert ws(numerics=L.NUM_EXPLICIT | L.NUM_GEMM_F16) == 0
+    assert ws(numerics=L.NUM_QK_PAIR) == L.LLAMA_ERR_UNSUPPORTED             # option bits need EXPLICIT
+    assert ws(numerics=L.NUM_EXPLICIT | (1 << 11)) == L.LLAMA_ERR_UNSUPPORTED  # unknown bit
     for pair in (L.NUM_QKV_A_PAIR, L.NUM_O_A_PAIR, L.NUM_FFN_A_PAIR, L.NUM_DOWN_A_PAIR):
         assert ws(numerics=L.NUM_EXPLICIT | L.NUM_GEMM_F16 | pair) == L.LLAMA_ERR_UNSUPPORTED
     # fewer key/value heads shrink the packed decode weights by exactly the Wk, Wv rows
