@@ -85,6 +85,21 @@ def test_rmsnorm_page_example_and_zero_row():
     assert torch.all(torch.isnan(y0[1]))
 
 
+def test_empty_inputs_are_no_ops():
+    """rows == 0 (rmsnorm, argmax) and tokens == 0 (rope) return OK and write
+    nothing; sizes that must be positive are rejected before any launch."""
+    lib, st = L.load(), torch.cuda.current_stream().cuda_stream
+    guard = torch.full((64,), 7.0, device="cuda")
+    gi = torch.full((8,), 7, dtype=torch.int32, device="cuda")
+    p = guard.data_ptr()
+    assert lib.llama_rmsnorm(L.LLAMA_F32, L.LLAMA_F32, p, None, p, 0, 64, 1e-6, st) == L.LLAMA_OK
+    assert lib.llama_rope(L.LLAMA_F32, p, p, gi.data_ptr(), 0, 1, 64, 1e4, st) == L.LLAMA_OK
+    assert lib.llama_argmax(p, 0, 64, gi.data_ptr(), st) == L.LLAMA_OK
+    assert lib.llama_linear(L.LLAMA_F32, L.LLAMA_F32, L.LLAMA_F32, p, p, p, 0, 8, 8, st) == L.LLAMA_ERR_SHAPE
+    torch.cuda.synchronize()
+    assert torch.all(guard == 7.0) and torch.all(gi == 7)
+
+
 # ---------------------------------------------------------------- RoPE
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_rope(dtype):
@@ -146,7 +161,8 @@ def test_linear_f32():
 
 
 # ---------------------------------------------------------------- attention
-@pytest.mark.parametrize("B,S,H,hd", [(1, 1, 1, 64), (2, 200, 3, 64), (1, 130, 2, 128), (1, 2048, 4, 128)])
+@pytest.mark.parametrize("B,S,H,hd", [(1, 1, 1, 64), (2, 200, 3, 64), (1, 130, 2, 128), (1, 2048, 4, 128),
+                                     (1, 8192, 1, 128)])
 def test_causal_attn_bf16(B, S, H, hd):
     w = I.Workload(904, "attn", dim=H * hd, n_heads=H, hidden=0, batch=B, seq=S, dtype="bf16")
     q, k, v = I.qkv_inputs(w, device="cuda")
