@@ -254,9 +254,10 @@ def bench_other_blocks(args, torch):
 
 def bench_train_step(args, torch, wid: int = 0):
     """fp32 training step of a block (forward keeping the linear outputs,
-    manual backward, SGD update of all nine weights) on the tiny fp32 block
-    workload. Work is counted as three times the forward's matrix products
-    (the backward's input and weight gradients are two more of each)."""
+    manual backward, SGD update of all nine weights) on an fp32 block workload
+    (the tiny block, or the d1024 seq-1024 block). Work is counted as three
+    times the forward's matrix products (the backward's input and weight
+    gradients are two more of each)."""
     from decoder_only_transformer_llama_amd import inputs as I, ops
     w = I.workload(wid)
     wt = I.block_weights(w, device="cuda")
@@ -425,6 +426,7 @@ def main() -> int:
     ap.add_argument("--no-other-blocks", action="store_true", help="skip the 13B/65B-shape block legs")
     ap.add_argument("--no-gqa-decode", action="store_true", help="skip the grouped-query decode leg")
     ap.add_argument("--no-train", action="store_true", help="skip the fp32 training-step leg")
+    ap.add_argument("--train-only", action="store_true", help="only the fp32 training-step legs (diagnostic runs)")
     ap.add_argument("--numerics", type=lambda v: int(v, 0), default=0,
                     help="prefill operand-precision bits (llama_config.numerics; 0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -439,6 +441,10 @@ def main() -> int:
     t_start = time.time()
     if args.copy_calibration:
         copy_calibration(torch)
+        return 0
+    if args.train_only:
+        for wid in (0, 8):
+            print(f"# train step: {json.dumps(bench_train_step(args, torch, wid))}", file=sys.stderr, flush=True)
         return 0
     if args.decode_only:
         dec = bench_decode(args, torch)
@@ -479,8 +485,9 @@ def main() -> int:
         print(f"# gqa decode: {json.dumps(gqa)}", file=sys.stderr, flush=True)
     train = None
     if not args.prefill_only and not args.no_train:
-        train = bench_train_step(args, torch)
-        print(f"# train step: {json.dumps(train)}", file=sys.stderr, flush=True)
+        train = [bench_train_step(args, torch, wid) for wid in (0, 8)]
+        for tr in train:
+            print(f"# train step: {json.dumps(tr)}", file=sys.stderr, flush=True)
     cpu = None if args.no_cpu_baseline else cpu_baseline(pf["block"], torch)
     w = pf["w"]
     line = {

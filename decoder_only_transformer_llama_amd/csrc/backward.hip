@@ -78,9 +78,121 @@ __global__ __launch_bounds__(256) void gemm_f32_strided_kernel(const float *A, i
     }
 }
 
+// fp32 GEMM on the matrix cores (v_mfma_f32_32x32x2_f32: fp32 products,
+// fp32 accumulation): C[m][n] = sum_k A(m, k) B(k, n) (+ R[m][n]) (+ C[m][n]
+// when accumulating), with A(m, k) = A[m sam + k sak] and B(k, n) =
+// B[k sbk + n sbn]. A_KC / B_KC: the operand is contiguous along K (sak == 1 /
+// sbk == 1), else along M / N (sam == 1 / sbn == 1); tiles arrive as 16-byte
+// vectors along the contiguous direction. One workgroup = 4 wavefronts
+// computing a 64 x 64 tile (32 x 32 each); K in steps of 16 through a 2-stage
+// LDS ring whose rows [k][m] are padded to 96 floats, so the two half-waves of
+// an operand read (rows k and k + 1) fall on disjoint banks.
+constexpr int kMfT = 64, kMfK = 16, kMfLd = 96;
+template <bool KC>
+DEV void mf_load(const float *P, int64_t s_row, int64_t s_k, int r0, int rows, int k0, int K, f32x4 &v) {
+  const int t = threadIdx.x;
+  if (KC) {   // row r = t / 4 holds k0 + 4 (t % 4) .. +3 contiguously
+    const int r = r0 + t / 4, k = k0 + 4 * (t % 4);
+    if (r < rows && k + 3 < K) {
+      v = *(const f32x4 *)(P + (int64_t)r * s_row + k);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (r < rows && k + e < K) ? P[(int64_t)r * s_row + k + e] : 0.f;
+    }
+  } else {    // k row t / 16 holds rows r0 + 4 (t % 16) .. +3 contiguously
+    const int k = k0 + t / 16, r = r0 + 4 * (t % 16);
+    if (k < K && r + 3 < rows) {
+      v = *(const f32x4 *)(P + (int64_t)k * s_k + r);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = (k < K && r + e < rows) ? P[(int64_t)k * s_k + r + e] : 0.f;
+    }
+  }
+}
+template <bool KC>
+DEV void mf_store(float (*S)[kMfLd], const f32x4 &v) {
+  const int t = threadIdx.x;
+  if (KC) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) S[4 * (t % 4) + e][t / 4] = v[e];
+  } else {
+    *(f32x4 *)&S[t / 16][4 * (t % 16)] = v;
+  }
+}
+
+template <bool A_KC, bool B_KC>
+__global__ __launch_bounds__(256) void gemm_f32_mfma_kernel(const float *A, int64_t sam, int64_t sak, const float *B,
+                                                            int64_t sbk, int64_t sbn, float *C, const float *R, int M,
+                                                            int N, int K, int accumulate) {
+  __shared__ float As[2][kMfK][kMfLd], Bs[2][kMfK][kMfLd];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int m0 = blockIdx.y * kMfT, n0 = blockIdx.x * kMfT;
+  const int mw = 32 * (w >> 1), nw = 32 * (w & 1);   // this wavefront's 32 x 32 block of the tile
+  const int nk = (K + kMfK - 1) / kMfK;
+  f32x4 va, vb;
+  mf_load<A_KC>(A, sam, sak, m0, M, 0, K, va);
+  mf_load<B_KC>(B, sbn, sbk, n0, N, 0, K, vb);
+  mf_store<A_KC>(As[0], va);
+  mf_store<B_KC>(Bs[0], vb);
+  __syncthreads();
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int st = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) {   // next tile: global -> registers while this one is multiplied
+      mf_load<A_KC>(A, sam, sak, m0, M, (kt + 1) * kMfK, K, va);
+      mf_load<B_KC>(B, sbn, sbk, n0, N, (kt + 1) * kMfK, K, vb);
+    }
+#pragma unroll
+    for (int kk = 0; kk < kMfK / 2; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(As[st][2 * kk + g][mw + l32], Bs[st][2 * kk + g][nw + l32], acc, 0,
+                                                 0, 0);
+    if (more) {   // the other stage was last read before the previous barrier
+      mf_store<A_KC>(As[st ^ 1], va);
+      mf_store<B_KC>(Bs[st ^ 1], vb);
+    }
+    __syncthreads();
+  }
+  const int n = n0 + nw + l32;
+  if (n >= N) return;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int m = m0 + mw + 8 * (r >> 2) + 4 * g + (r & 3);
+    if (m >= M) continue;
+    const int64_t o = (int64_t)m * N + n;
+    C[o] = acc[r] + (R ? R[o] : 0.f) + (accumulate ? C[o] : 0.f);
+  }
+}
+
+// The matrix-core path when the contiguous strides allow 16-byte vectors;
+// hipErrorNotSupported otherwise (the caller then uses the VALU kernel).
+hipError_t gemm_f32_mfma_launch(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
+                                float *C, const float *R, int M, int N, int K, int accumulate, hipStream_t s) {
+  const bool a_kc = sak == 1, b_kc = sbk == 1;
+  const int64_t sa = a_kc ? sam : sak, sb = b_kc ? sbn : sbk;   // strides between the 16-byte runs
+  if ((!a_kc && sam != 1) || (!b_kc && sbn != 1) || sa % 4 || sb % 4 || ((uintptr_t)A | (uintptr_t)B) % 16)
+    return hipErrorNotSupported;
+  if (M == 0 || N == 0) return hipSuccess;
+  const dim3 grid((N + kMfT - 1) / kMfT, (M + kMfT - 1) / kMfT);
+#define MF_CASE(AK, BK)                                                                                          \
+  if (a_kc == AK && b_kc == BK) {                                                                                \
+    hipLaunchKernelGGL((gemm_f32_mfma_kernel<AK, BK>), grid, dim3(256), 0, s, A, sam, sak, B, sbk, sbn, C, R, M, \
+                       N, K, accumulate);                                                                        \
+    return hipGetLastError();                                                                                    \
+  }
+  MF_CASE(true, true) MF_CASE(true, false) MF_CASE(false, true) MF_CASE(false, false)
+#undef MF_CASE
+  return hipErrorNotSupported;
+}
+
 hipError_t gemm_f32_strided_launch(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk,
                                    int64_t sbn, float *C, int M, int N, int K, int accumulate, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  const hipError_t e = gemm_f32_mfma_launch(A, sam, sak, B, sbk, sbn, C, nullptr, M, N, K, accumulate, s);
+  if (e != hipErrorNotSupported) return e;
   hipLaunchKernelGGL(gemm_f32_strided_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, A, sam, sak, B,
                      sbk, sbn, C, M, N, K, accumulate);
   return hipGetLastError();
@@ -314,13 +426,27 @@ __global__ __launch_bounds__(256) void rmsnorm_bwd_kernel(const float *x, const 
 }
 
 // dg[c] = sum over rows of dy[row, c] x[row, c] rstd[row] (one thread per column, rows in order).
-__global__ void rmsnorm_bwd_gain_kernel(const float *x, const float *dy, const float *rstd, float *dg, int64_t rows,
-                                        int dim) {
-  const int c = blockIdx.x * blockDim.x + threadIdx.x;
-  if (c >= dim) return;
+// dg[c] = sum_r dy[r][c] x[r][c] rstd[r]: one workgroup per 64 columns,
+// 16 row phases (rows p, p + 16, ...) summed per thread, then the phases
+// added in a fixed order through LDS (deterministic, no atomics).
+constexpr int kGainCols = 64, kGainPhases = 16;
+__global__ __launch_bounds__(kGainCols * kGainPhases) void rmsnorm_bwd_gain_kernel(
+    const float *x, const float *dy, const float *rstd, float *dg, int64_t rows, int dim) {
+  __shared__ float part[kGainPhases][kGainCols];
+  const int cl = threadIdx.x % kGainCols, ph = threadIdx.x / kGainCols;
+  const int c = blockIdx.x * kGainCols + cl;
   float acc = 0.f;
-  for (int64_t r = 0; r < rows; ++r) acc = fmaf(dy[r * dim + c], x[r * dim + c] * rstd[r], acc);
-  dg[c] = acc;
+  if (c < dim) {
+#pragma unroll 8
+    for (int64_t r = ph; r < rows; r += kGainPhases) acc = fmaf(dy[r * dim + c], x[r * dim + c] * rstd[r], acc);
+  }
+  part[ph][cl] = acc;
+  __syncthreads();
+  if (ph == 0 && c < dim) {
+    float t = 0.f;
+    for (int p = 0; p < kGainPhases; ++p) t += part[p][cl];
+    dg[c] = t;
+  }
 }
 
 hipError_t rmsnorm_bwd_launch(const float *x, const float *g, const float *dy, const float *add, float *dx,
@@ -330,7 +456,8 @@ hipError_t rmsnorm_bwd_launch(const float *x, const float *g, const float *dy, c
                      rows, dim, eps);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(rmsnorm_bwd_gain_kernel, dim3((dim + 255) / 256), dim3(256), 0, s, x, dy, rstd, dg, rows, dim);
+  hipLaunchKernelGGL(rmsnorm_bwd_gain_kernel, dim3((dim + kGainCols - 1) / kGainCols), dim3(kGainCols * kGainPhases),
+                     0, s, x, dy, rstd, dg, rows, dim);
   return hipGetLastError();
 }
 

@@ -434,6 +434,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(const float *A, const flo
 hipError_t gemm_f32_launch(const float *A, const float *B, float *C, const float *R, int M, int N, int K,
                            hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
+  // C = A B^T: A(m, k) = A[m K + k], B(k, n) = B[n K + k]
+  const hipError_t e = gemm_f32_mfma_launch(A, K, 1, B, 1, K, C, R, M, N, K, 0, s);
+  if (e != hipErrorNotSupported) return e;
   hipLaunchKernelGGL(gemm_f32_kernel, dim3((N + 63) / 64, (M + 63) / 64), dim3(256), 0, s, A, B, C, R, M,
                      N, K);
   return hipGetLastError();

@@ -122,6 +122,10 @@ hipError_t embed_launch(int w_f32, const void *emb, const int32_t *tokens, int64
 // fp32 path (small workloads, plain VALU kernels)
 hipError_t gemm_f32_launch(const float *A, const float *B, float *C, const float *R, int M, int N, int K,
                            hipStream_t s);
+// fp32 GEMM on the matrix cores for operands with a unit stride along K or
+// along M / N (16-byte aligned runs); hipErrorNotSupported for other layouts.
+hipError_t gemm_f32_mfma_launch(const float *A, int64_t sam, int64_t sak, const float *B, int64_t sbk, int64_t sbn,
+                                float *C, const float *R, int M, int N, int K, int accumulate, hipStream_t s);
 hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64_t n, hipStream_t s);
 // lse (optional): [batch][n_heads][seq] log-sum-exp of each query's scaled scores.
 hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float *o, int batch, int seq,

@@ -95,6 +95,10 @@ WORKLOADS: Dict[int, Workload] = {
     # hidden 256), one sequence of 16 tokens, fp32, weights N(0, 1/fan_in), gains 1
     7: Workload(7, "norm-placement-d64-l32-s16", dim=64, n_heads=1, hidden=256, batch=1, seq=16, dtype="f32",
                 eps=1e-5, n_layers=32, fan_in_init=True),
+    # fp32 training step at a size where the kernels, not the launches, set the
+    # time: d 1024 (8 heads of 128), SwiGLU hidden 2816, one sequence of 1024
+    8: Workload(8, "train-block-f32-d1024-s1024", dim=1024, n_heads=8, hidden=2816, batch=1, seq=1024,
+                dtype="f32", gain_std=0.1),
     # the same model with grouped-query attention: 8 key/value heads (groups of 4)
     5: Workload(5, "7b-gqa8-model-decode-b32-kv2047", dim=4096, n_heads=32, hidden=11008, batch=32, seq=1,
                 dtype="bf16", n_layers=32, vocab=32000, max_seq=2048, decode_pos=2047, n_kv_heads=8),
