@@ -453,52 +453,100 @@ hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64
   return hipGetLastError();
 }
 
-// Causal attention in fp32, one thread per (sequence, head, query), online softmax.
+// Causal attention in fp32 with online softmax. One workgroup per (query
+// tile of 64, sequence, head): 4 wavefronts, all on the same 64 queries (one
+// per lane), wavefront g taking the keys j = g mod 4 of every 64-key tile of K
+// and V staged in LDS (a wavefront's lanes read the same key row: broadcast).
+// Each lane keeps the running (max, sum, output) of its keys; the four
+// partial states of a query are merged in group order at the end, so the
+// result does not depend on timing. lse (optional) gets max + log(sum).
+constexpr int kAttnQ = 64, kAttnK = 64, kAttnG = 4;
 template <int HD>
-__global__ __launch_bounds__(64) void attn_f32_kernel(const float *q, const float *k, const float *v,
-                                                      float *o, float *lse, int batch, int seq, int n_heads) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= batch * n_heads * seq) return;
-  const int i = idx % seq, h = (idx / seq) % n_heads, b = idx / (seq * n_heads);
+__global__ __launch_bounds__(kAttnQ * kAttnG) void attn_f32_kernel(const float *q, const float *k, const float *v,
+                                                                   float *o, float *lse, int batch, int seq,
+                                                                   int n_heads) {
+  __shared__ float kv[2][kAttnK][HD];   // K and V tiles; after the loop, the merge buffer
+  const int lq = threadIdx.x % kAttnQ, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / kAttnQ);
+  const int bh = blockIdx.y, b = bh / n_heads, h = bh % n_heads;
+  const int q0 = blockIdx.x * kAttnQ, qi = q0 + lq;
   const int d = n_heads * HD;
-  const float *qi = q + ((int64_t)b * seq + i) * d + h * HD;
   float qr[HD], acc[HD];
+  {
+    const float *qp = q + ((int64_t)b * seq + min(qi, seq - 1)) * d + h * HD;
 #pragma unroll
-  for (int e = 0; e < HD; ++e) {
-    qr[e] = qi[e];
-    acc[e] = 0.f;
+    for (int e = 0; e < HD; ++e) {
+      qr[e] = qp[e];
+      acc[e] = 0.f;
+    }
   }
   const float sc = 1.0f / sqrtf((float)HD);
   float m = -INFINITY, l = 0.f;
-  for (int j = 0; j <= i; ++j) {
-    const float *kj = k + ((int64_t)b * seq + j) * d + h * HD;
-    float s = 0.f;
+  const int kend = min(seq, q0 + kAttnQ);   // keys any query of the tile sees
+  for (int j0 = 0; j0 < kend; j0 += kAttnK) {
+    __syncthreads();   // everyone is done with the previous tile
+    for (int i = threadIdx.x; i < kAttnK * HD; i += kAttnQ * kAttnG) {   // rows past seq: zeros
+      const int r = i / HD, c = i % HD;
+      const int j = j0 + r;
+      const int64_t src = ((int64_t)b * seq + j) * d + h * HD + c;
+      kv[0][r][c] = j < seq ? k[src] : 0.f;
+      kv[1][r][c] = j < seq ? v[src] : 0.f;
+    }
+    __syncthreads();
+    for (int u = 0; u < kAttnK / kAttnG; ++u) {
+      const int jl = grp + kAttnG * u, j = j0 + jl;
+      if (j > qi || j >= seq) break;   // keys ascend: past the diagonal (or the end) for this lane
+      float sdot = 0.f;
 #pragma unroll
-    for (int e = 0; e < HD; ++e) s = fmaf(qr[e], kj[e], s);
-    s *= sc;
-    const float mn = fmaxf(m, s);
-    const float al = expf(m - mn), p = expf(s - mn);
-    l = l * al + p;
-    const float *vj = v + ((int64_t)b * seq + j) * d + h * HD;
+      for (int e = 0; e < HD; ++e) sdot = fmaf(qr[e], kv[0][jl][e], sdot);
+      const float s = sdot * sc;
+      const float mn = fmaxf(m, s);
+      const float al = expf(m - mn), p = expf(s - mn);
+      l = l * al + p;
 #pragma unroll
-    for (int e = 0; e < HD; ++e) acc[e] = acc[e] * al + p * vj[e];
-    m = mn;
+      for (int e = 0; e < HD; ++e) acc[e] = acc[e] * al + p * kv[1][jl][e];
+      m = mn;
+    }
   }
-  float *oi = o + ((int64_t)b * seq + i) * d + h * HD;
+  // merge group g = 1, 2, 3 into group 0, in that order
+  float *xb = &kv[0][0][0];   // [64 queries][HD + 2]
+  for (int gsrc = 1; gsrc < kAttnG; ++gsrc) {
+    __syncthreads();
+    if (grp == gsrc) {
+      float *row = xb + lq * (HD + 2);
 #pragma unroll
-  for (int e = 0; e < HD; ++e) oi[e] = acc[e] / l;
-  if (lse) lse[idx] = m + logf(l);   // [batch][n_heads][seq]: the backward's softmax statistic
+      for (int e = 0; e < HD; ++e) row[e] = acc[e];
+      row[HD] = m;
+      row[HD + 1] = l;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float *row = xb + lq * (HD + 2);
+      const float m1 = row[HD], l1 = row[HD + 1];
+      const float mn = fmaxf(m, m1);
+      const float a0 = expf(m - mn), a1 = expf(m1 - mn);   // m1 = -inf (no keys): a1 = 0
+      l = l * a0 + l1 * a1;
+#pragma unroll
+      for (int e = 0; e < HD; ++e) acc[e] = acc[e] * a0 + row[e] * a1;
+      m = mn;
+    }
+  }
+  if (grp != 0 || qi >= seq) return;
+  float *op = o + ((int64_t)b * seq + qi) * d + h * HD;
+  const float inv = 1.0f / l;
+#pragma unroll
+  for (int e = 0; e < HD; ++e) op[e] = acc[e] * inv;
+  if (lse) lse[((int64_t)b * n_heads + h) * seq + qi] = m + logf(l);   // [batch][n_heads][seq]: the backward's statistic
 }
 
 hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float *o, int batch, int seq,
                            int n_heads, int head_dim, hipStream_t s, float *lse) {
-  const int n = batch * n_heads * seq;
-  if (n == 0) return hipSuccess;
-  const dim3 grid((n + 63) / 64);
+  if (batch * n_heads * seq == 0) return hipSuccess;
+  const dim3 grid((seq + kAttnQ - 1) / kAttnQ, batch * n_heads);
   if (head_dim == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(64), 0, s, q, k, v, o, lse, batch, seq, n_heads);
+    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(kAttnQ * kAttnG), 0, s, q, k, v, o, lse, batch, seq, n_heads);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(64), 0, s, q, k, v, o, lse, batch, seq, n_heads);
+    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(kAttnQ * kAttnG), 0, s, q, k, v, o, lse, batch, seq,
+                       n_heads);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

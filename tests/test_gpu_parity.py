@@ -649,7 +649,9 @@ def test_training_step_sgd():
         g = host(tb.grads[k])
         assert rel_err(g, g_ref[k]) < TOL_F32, k
         # w_new = fl(w - fl(lr g)): within two fp32 roundings of the exact update
-        assert np.all(np.abs(host(wt[k]) - (hw[k] - lr * g)) <= 2.0 ** -23 * (np.abs(hw[k]) + lr * np.abs(g))), k
+        # with the learning rate the kernel receives (an fp32 argument)
+        lr32 = float(np.float32(lr))
+        assert np.all(np.abs(host(wt[k]) - (hw[k] - lr32 * g)) <= 2.0 ** -23 * (np.abs(hw[k]) + lr32 * np.abs(g))), k
     losses = [0.5 * float(torch.sum((y0 - t) ** 2))]
     for _ in range(5):
         y = tb.train_step(x, t, lr)
