@@ -454,19 +454,20 @@ hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64
 }
 
 // Causal attention in fp32 with online softmax. One workgroup per (query
-// tile of 64, sequence, head): 4 wavefronts, all on the same 64 queries (one
-// per lane), wavefront g taking the keys j = g mod 4 of every 64-key tile of K
-// and V staged in LDS (a wavefront's lanes read the same key row: broadcast).
-// Each lane keeps the running (max, sum, output) of its keys; the four
-// partial states of a query are merged in group order at the end, so the
-// result does not depend on timing. lse (optional) gets max + log(sum).
-constexpr int kAttnQ = 64, kAttnK = 64, kAttnG = 4;
+// tile of 32, sequence, head): 8 key groups of 32 lanes (two per wavefront),
+// all on the same 32 queries (one per lane), group g taking the keys
+// j = g mod 8 of every 64-key tile of K and V staged in LDS (the lanes of a
+// group read the same key row: broadcast). Each lane keeps the running (max,
+// sum, output) of its keys; the eight partial states of a query are merged in
+// group order at the end, so the result does not depend on timing. lse
+// (optional) gets max + log(sum).
+constexpr int kAttnQ = 32, kAttnK = 64, kAttnG = 8;
 template <int HD>
 __global__ __launch_bounds__(kAttnQ * kAttnG) void attn_f32_kernel(const float *q, const float *k, const float *v,
                                                                    float *o, float *lse, int batch, int seq,
                                                                    int n_heads) {
   __shared__ float kv[2][kAttnK][HD];   // K and V tiles; after the loop, the merge buffer
-  const int lq = threadIdx.x % kAttnQ, grp = __builtin_amdgcn_readfirstlane(threadIdx.x / kAttnQ);
+  const int lq = threadIdx.x % kAttnQ, grp = threadIdx.x / kAttnQ;
   const int bh = blockIdx.y, b = bh / n_heads, h = bh % n_heads;
   const int q0 = blockIdx.x * kAttnQ, qi = q0 + lq;
   const int d = n_heads * HD;
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(kAttnQ * kAttnG) void attn_f32_kernel(const float *
     }
   }
   // merge group g = 1, 2, 3 into group 0, in that order
-  float *xb = &kv[0][0][0];   // [64 queries][HD + 2]
+  float *xb = &kv[0][0][0];   // [32 queries][HD + 2]
   for (int gsrc = 1; gsrc < kAttnG; ++gsrc) {
     __syncthreads();
     if (grp == gsrc) {
