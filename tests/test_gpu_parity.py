@@ -684,3 +684,39 @@ def test_block_hip_graph_replays_match_eager():
         other = bw.block(bw.x * 0.5).clone()   # eager work between replays
         torch.cuda.synchronize()
         assert not torch.equal(other, eager)
+
+
+def test_decode_hip_graph_replays_match_eager():
+    """A decode step captured in a HIP graph: three replays, each rewriting the
+    same cache slot, with an eager decode on other caches (same workspace)
+    between them; every replay's logits are bitwise the eager step's."""
+    w, m, _, _ = small_model(101)
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    m.forward(toks[:, :T].contiguous(), kc, vc)
+    kc2, vc2 = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    tok = toks[:, T].contiguous()
+    logits = torch.empty((B, w.vocab), dtype=torch.float32, device="cuda")
+    m.decode(tok, pos, kc, vc, logits)
+    torch.cuda.synchronize()
+    eager = logits.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        m.decode(tok, pos, kc, vc, logits)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.decode(tok, pos, kc, vc, logits)
+    other = torch.empty_like(logits)
+    for i in range(3):
+        logits.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(logits, eager), i
+        m.decode(tok, pos, kc2, vc2, other)   # eager work between replays
+        torch.cuda.synchronize()
+        assert not torch.equal(other, eager)
