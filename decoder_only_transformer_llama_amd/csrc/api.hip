@@ -341,7 +341,7 @@ TrainSaved carve_saved(Carve &cv, const llama_config *c, int batch, int seq) {
 
 // Backward workspace: recomputed norms and SiLU(gate)*up, gradient buffers.
 struct BwdWs {
-  float *z1, *z2, *u, *du, *dup, *dz, *dh, *da, *dq, *dk, *dv, *delta, *rstd;
+  float *z1, *z2, *u, *du, *dup, *dz, *dh, *da, *dq, *dk, *dv, *delta, *rstd, *kv_part;
 };
 BwdWs carve_backward(Carve &cv, const llama_config *c, int batch, int seq) {
   const size_t n = (size_t)batch * seq, d = c->dim, hid = c->hidden;
@@ -359,6 +359,7 @@ BwdWs carve_backward(Carve &cv, const llama_config *c, int batch, int seq) {
   w.dv = cv.take<float>(n * d);
   w.delta = cv.take<float>((size_t)batch * c->n_heads * seq);
   w.rstd = cv.take<float>(n);
+  w.kv_part = cv.take<float>((size_t)kAttnBwdKvRanges * 2 * n * d);
   return w;
 }
 
@@ -411,6 +412,7 @@ size_t ws_bytes_of(const llama_config *c, int op, int batch, int seq) {
       cv.take<float>(n * c->dim);                                 // recomputed output
       cv.take<float>((size_t)batch * c->n_heads * seq);           // log-sum-exp
       cv.take<float>((size_t)batch * c->n_heads * seq);           // rowsum(dout * out)
+      cv.take<float>((size_t)kAttnBwdKvRanges * 2 * n * c->dim);  // split key/value-gradient sums
       break;
     case LLAMA_OP_BLOCK_BACKWARD:
       carve_backward(cv, c, batch, seq);
@@ -686,10 +688,11 @@ int llama_causal_attn_backward(int dtype, const void *q, const void *k, const vo
   float *o = cv.take<float>(n * c.dim);
   float *lse = cv.take<float>((size_t)batch * n_heads * seq);
   float *delta = cv.take<float>((size_t)batch * n_heads * seq);
+  float *kv_part = cv.take<float>((size_t)kAttnBwdKvRanges * 2 * n * c.dim);
   const float *qf = (const float *)q, *kf = (const float *)k, *vf = (const float *)v;
   HIP_TRY(attn_f32_launch(qf, kf, vf, o, batch, seq, n_heads, head_dim, s, lse), "attention (recomputed)");
   HIP_TRY(attn_bwd_launch(qf, kf, vf, o, (const float *)dout, lse, delta, (float *)dq, (float *)dk, (float *)dv,
-                          batch, seq, n_heads, head_dim, s),
+                          batch, seq, n_heads, head_dim, s, kv_part),
           "attention backward");
   return LLAMA_OK;
 }
@@ -780,7 +783,8 @@ int llama_block_backward(const llama_config *c, const llama_block_weights *w, co
   // h = x + a Wo^T
   HIP_TRY(tn(b.dh, t.a, G(grads->wo), d, d), "output weight gradient");
   HIP_TRY(nn(b.dh, W(w->wo), b.da, M, d, d, 0), "output input gradient");
-  HIP_TRY(attn_bwd_launch(t.q, t.k, t.v, t.a, b.da, t.lse, b.delta, b.dq, b.dk, b.dv, batch, seq, H, hd, s),
+  HIP_TRY(attn_bwd_launch(t.q, t.k, t.v, t.a, b.da, t.lse, b.delta, b.dq, b.dk, b.dv, batch, seq, H, hd, s,
+                          b.kv_part),
           "attention backward");
   HIP_TRY(rope_launch(1, b.dq, b.dq, nullptr, M, H, hd, c->rope_theta, seq, s, 1), "rope backward");
   HIP_TRY(rope_launch(1, b.dk, b.dk, nullptr, M, H, hd, c->rope_theta, seq, s, 1), "rope backward");

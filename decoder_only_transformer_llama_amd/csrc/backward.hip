@@ -261,11 +261,16 @@ DEV void bwd_scores(const float (*sQ)[HD + 1], const float (*sdO)[HD + 1], const
   }
 }
 
+// Key/value gradients of one 64-key tile. The causal loop over query tiles
+// (those at or after the key tile) is split into gridDim.z contiguous ranges,
+// one per workgroup: with one range the tile's dk (scaled) and dv are stored;
+// with several, range z stores its unscaled sums to part[z] ([2][rows][d]:
+// dk then dv) and attn_bwd_kv_sum_kernel adds the ranges in order.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const float *q, const float *k, const float *v,
                                                             const float *dout, const float *lse,
                                                             const float *delta, float *dk, float *dv, int seq,
-                                                            int n_heads, float scale) {
+                                                            int n_heads, float scale, float *part) {
   constexpr int CW = HD / 16;
   __shared__ float sK[kBwdBK][HD + 1], sV[kBwdBK][HD + 1];
   __shared__ float sQ[kBwdBQ][HD + 1], sdO[kBwdBQ][HD + 1];
@@ -278,7 +283,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const float *q, cons
   const int kq = threadIdx.x / 16, ce = threadIdx.x % 16;   // keys 4*kq.., channels ce*CW..
   float accK[4][CW] = {}, accV[4][CW] = {};
   const int nqt = (seq + kBwdBQ - 1) / kBwdBQ;
-  for (int it = k0 / kBwdBQ; it < nqt; ++it) {   // causal: queries at or after the key tile
+  const int it0 = k0 / kBwdBQ, nit = nqt - it0, nz = gridDim.z, z = blockIdx.z;
+  const int ib = it0 + (int)((int64_t)nit * z / nz), ie = it0 + (int)((int64_t)nit * (z + 1) / nz);
+  for (int it = ib; it < ie; ++it) {   // causal: queries at or after the key tile, this range
     const int q0 = it * kBwdBQ;
     __syncthreads();   // the previous tile's readers are done (and sK/sV are loaded)
     bwd_load_rows<HD>(sQ, q, b, h, q0, kBwdBQ, seq, n_heads);
@@ -310,6 +317,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const float *q, cons
     }
   }
   const int d = n_heads * HD;
+  const int64_t rd = (int64_t)gridDim.y / n_heads * seq * d;   // rows x d of one gradient
+  float *pk = part + (int64_t)z * 2 * rd, *pv = pk + rd;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int kj = k0 + 4 * kq + j;
@@ -317,10 +326,28 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const float *q, cons
     const int64_t o = ((int64_t)b * seq + kj) * d + (int64_t)h * HD + ce * CW;
 #pragma unroll
     for (int c = 0; c < CW; ++c) {
-      dk[o + c] = accK[j][c] * scale;
-      dv[o + c] = accV[j][c];
+      if (nz == 1) {
+        dk[o + c] = accK[j][c] * scale;
+        dv[o + c] = accV[j][c];
+      } else {
+        pk[o + c] = accK[j][c];
+        pv[o + c] = accV[j][c];
+      }
     }
   }
+}
+
+// dk = scale * (part[0].k + part[1].k + ...), dv = part[0].v + ..., ranges in order.
+__global__ void attn_bwd_kv_sum_kernel(const float *part, int nz, int64_t rd, float scale, float *dk, float *dv) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rd) return;
+  float sk = 0.f, sv = 0.f;
+  for (int z = 0; z < nz; ++z) {
+    sk += part[(int64_t)z * 2 * rd + i];
+    sv += part[(int64_t)z * 2 * rd + rd + i];
+  }
+  dk[i] = sk * scale;
+  dv[i] = sv;
 }
 
 template <int HD>
@@ -376,7 +403,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const float *q, const 
 
 hipError_t attn_bwd_launch(const float *q, const float *k, const float *v, const float *o, const float *dout,
                            const float *lse, float *delta, float *dq, float *dk, float *dv, int batch, int seq,
-                           int n_heads, int head_dim, hipStream_t s) {
+                           int n_heads, int head_dim, hipStream_t s, float *kv_part) {
   const int64_t rows = (int64_t)batch * n_heads * seq;
   if (rows == 0) return hipSuccess;
   if (head_dim != 64 && head_dim != 128) return hipErrorInvalidValue;
@@ -385,20 +412,25 @@ hipError_t attn_bwd_launch(const float *q, const float *k, const float *v, const
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale = 1.0f / sqrtf((float)head_dim);
-  const dim3 gkv((seq + kBwdBK - 1) / kBwdBK, batch * n_heads), gq((seq + kBwdBQ - 1) / kBwdBQ, batch * n_heads);
+  const int nz = kv_part ? kAttnBwdKvRanges : 1;
+  const dim3 gkv((seq + kBwdBK - 1) / kBwdBK, batch * n_heads, nz), gq((seq + kBwdBQ - 1) / kBwdBQ, batch * n_heads);
   if (head_dim == 128) {
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gkv, dim3(256), 0, s, q, k, v, dout, lse, delta, dk, dv, seq,
-                       n_heads, scale);
+                       n_heads, scale, kv_part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(attn_bwd_dq_kernel<128>, gq, dim3(256), 0, s, q, k, v, dout, lse, delta, dq, seq, n_heads,
                        scale);
   } else {
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<64>, gkv, dim3(256), 0, s, q, k, v, dout, lse, delta, dk, dv, seq,
-                       n_heads, scale);
+                       n_heads, scale, kv_part);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(attn_bwd_dq_kernel<64>, gq, dim3(256), 0, s, q, k, v, dout, lse, delta, dq, seq, n_heads,
                        scale);
   }
+  if ((e = hipGetLastError()) != hipSuccess || nz == 1) return e;
+  const int64_t rd = rows * head_dim;
+  hipLaunchKernelGGL(attn_bwd_kv_sum_kernel, dim3((unsigned)((rd + 255) / 256)), dim3(256), 0, s, kv_part, nz, rd,
+                     scale, dk, dv);
   return hipGetLastError();
 }
 

@@ -192,9 +192,13 @@ hipError_t gemm_f32_strided_launch(const float *A, int64_t sam, int64_t sak, con
                                    int64_t sbn, float *C, int M, int N, int K, int accumulate, hipStream_t s);
 // dq, dk, dv of causal attention from q, k, v, the forward output o, its
 // log-sum-exp lse [batch][n_heads][seq] and dout; delta: scratch of the lse's size.
+// kv_part: nullptr, or kAttnBwdKvRanges * 2 * batch * seq * n_heads * head_dim
+// floats of scratch, with which the key/value-gradient loop runs split over
+// that many workgroups per key tile.
+constexpr int kAttnBwdKvRanges = 4;
 hipError_t attn_bwd_launch(const float *q, const float *k, const float *v, const float *o, const float *dout,
                            const float *lse, float *delta, float *dq, float *dk, float *dv, int batch, int seq,
-                           int n_heads, int head_dim, hipStream_t s);
+                           int n_heads, int head_dim, hipStream_t s, float *kv_part = nullptr);
 // dx = add + gradient of RMSNorm(x; g) for dy; dg = its gain gradient; rstd: [rows] scratch.
 hipError_t rmsnorm_bwd_launch(const float *x, const float *g, const float *dy, const float *add, float *dx,
                               float *dg, float *rstd, int64_t rows, int dim, float eps, hipStream_t s);
