@@ -1079,15 +1079,20 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
     if (st) return st;
     std::swap(xa, xb);
   }
-  HIP_TRY(norm_prep_launch(1, xa, (const uint16_t *)w->final_norm, n, d, c->norm_eps, b.rstd1, b.xg_hi, b.xg_lo,
-                           s),
+  // the head's operand RMSNorm(x)*g_f is carried like the QKV projection's
+  // (fp16, a bf16 pair or bf16, by the numerics bits of that projection)
+  const uint32_t num = numerics_of(c);
+  const bool hpair = num & LLAMA_NUM_QKV_A_PAIR;
+  const int hf16 = (num & LLAMA_NUM_QKV_A_F16) ? 1 : 0;
+  HIP_TRY(norm_prep_launch(1, xa, (const uint16_t *)w->final_norm, n, d, c->norm_eps, b.rstd1, b.xg_hi,
+                           hpair ? b.xg_lo : nullptr, s, nullptr, 0, nullptr, hf16),
           "final norm");
   GemmArgs hd_{};
   hd_.M = (int)n;
   hd_.N = c->vocab;
   hd_.K = d;
   hd_.A = b.xg_hi;
-  hd_.A_lo = b.xg_lo;
+  hd_.A_lo = hpair ? b.xg_lo : nullptr;
   hd_.lda = d;
   hd_.rstd = b.rstd1;
   hd_.b_mode = BMODE_PLAIN;
@@ -1095,7 +1100,7 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
   hd_.C = logits;
   hd_.c_f32 = 1;
   hd_.ldc = c->vocab;
-  HIP_TRY(gemm_launch(GemmKey{256, 1, EPI_STORE}, hd_, s), "output head");
+  HIP_TRY(gemm_launch(GemmKey{256, hpair, EPI_STORE, hf16}, hd_, s), "output head");
   return LLAMA_OK;
 }
 

@@ -7,6 +7,7 @@ hipError_t gemm_launch_misc(const GemmKey &key, const GemmArgs &a, hipStream_t s
   GEMM_CASE_F16(256, EPI_PARTIAL)
   GEMM_CASE_F16(256, EPI_RESID)
   GEMM_CASE_F16(128, EPI_RESID)
+  GEMM_CASE_F16(256, EPI_STORE)
   GEMM_CASE(256, 0, EPI_PARTIAL)
   GEMM_CASE(256, 1, EPI_PARTIAL)
   GEMM_CASE(256, 0, EPI_RESID)

@@ -223,7 +223,9 @@ int llama_block_forward(const llama_config *c, const llama_block_weights *w, int
  * RMSNorm and output head ([P1] "The one formula": one final RMSNorm, then the
  * output head). Each layer's rotated keys and values are written to cache
  * slots 0..seq-1. k_cache, v_cache: [n_layers][batch][n_heads][max_seq][head_dim]
- * in config dtype. logits [batch, seq, vocab] f32.
+ * in config dtype. logits [batch, seq, vocab] f32. The head's operand
+ * RMSNorm(x; final_norm) is carried as the Q/K/V projection's operand is
+ * (numerics bits QKV_A_F16 / QKV_A_PAIR).
  * bf16 configs only (LLAMA_ERR_UNSUPPORTED for f32). seq <= max_seq. */
 int llama_model_forward(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
                         int batch, int seq, void *k_cache, void *v_cache, float *logits, void *ws,
