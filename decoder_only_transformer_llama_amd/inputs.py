@@ -124,6 +124,10 @@ TEST_WORKLOADS: Dict[int, Workload] = {
     # fp32 training block: head_dim 128, two sequences of a ragged length
     107: Workload(107, "test-train-block-f32", dim=256, n_heads=2, hidden=768, batch=2, seq=37, dtype="f32",
                   gain_std=0.1),
+    # one layer at the LLaMA-7B widths with the 32000-wide head: the model
+    # path (embedding, split-K down projection, fp16 head) at full width
+    108: Workload(108, "test-model-7b-dims-1layer", dim=4096, n_heads=32, hidden=11008, batch=1, seq=256,
+                  dtype="bf16", n_layers=1, vocab=32000, max_seq=512, gain_std=0.1),
     # multi-query model (one key/value head), head_dim 128, groups of 4
     106: Workload(106, "test-model-bf16-mqa", dim=512, n_heads=4, hidden=1536, batch=2, seq=24, dtype="bf16",
                   n_layers=2, vocab=500, max_seq=48, n_kv_heads=1),

@@ -304,8 +304,16 @@ def oracle_caches(w, B):
 # bf16 pair. (With single bf16 projection operands instead of the fp16
 # default, 105's two-layer logits reach 2.1e-2, all of it from the bf16
 # rounding points.)
+# The decode step on a given cache: activations are bf16 hi/lo pairs (about
+# 16 significant bits); what remains is the new key/value entering the cache
+# as bf16 and fp32 arithmetic. Measured 3.7e-4 to 1.4e-3 of the logits' RMS on
+# the test models (the grouped-query ones highest); the bound is a quarter of
+# the end-to-end one.
+TOL_DECODE_STEP = 5e-3
+
+
 @pytest.mark.parametrize("wid,numerics", [(101, L.NUM_DEFAULT), (105, L.NUM_DEFAULT), (106, L.NUM_DEFAULT),
-                                          (105, ALL_PAIRS)])
+                                          (105, ALL_PAIRS), (108, L.NUM_DEFAULT)])
 def test_model_prefill_then_decode(wid, numerics):
     w, m, layers, gl = small_model(wid, numerics=numerics)
     B, T = w.batch, w.seq
@@ -331,8 +339,20 @@ def test_model_prefill_then_decode(wid, numerics):
     want_dec = O.model_decode(toks[:, T].cpu().numpy(), np.full(B, T), emb, get, w.n_layers, fn, out, w.n_heads,
                               w.eps)
     e2 = rel_err(dec, want_dec)
-    print(f"{w.name}: prefill logits {e1:.3e}, decode logits {e2:.3e}")
+    # the decode step alone: the oracle continuing from the GPU's own bf16
+    # cache (slots 0..T-1; it appends slot T itself). Decode carries its
+    # activations as pairs, so this is much tighter than the end-to-end
+    # figure, whose remainder is the prefill's rounding stored in the cache.
+    gc = [tuple(O.f64(c[l].cpu()).copy() for c in (kc, vc)) for l in range(w.n_layers)]
+    for kg, vg in gc:
+        kg[:, :, T:] = 0
+        vg[:, :, T:] = 0
+    want_dec_gc = O.model_decode(toks[:, T].cpu().numpy(), np.full(B, T), emb, lambda l: (lw[l], *gc[l]),
+                                 w.n_layers, fn, out, w.n_heads, w.eps)
+    e3 = rel_err(dec, want_dec_gc)
+    print(f"{w.name}: prefill logits {e1:.3e}, decode logits {e2:.3e} ({e3:.3e} from the GPU's cache)")
     assert e1 < TOL_BF16 and e2 < TOL_BF16
+    assert e3 < TOL_DECODE_STEP
 
 
 @pytest.mark.parametrize("wid", [101, 105, 106])
