@@ -153,7 +153,7 @@ def bench_prefill(args, torch):
     from decoder_only_transformer_llama_amd import _lib, inputs as I
     from decoder_only_transformer_llama_amd.workloads import block_workload
 
-    bw = block_workload(1, "cuda", numerics=args.numerics)
+    bw = block_workload(1, "cuda", numerics=args.numerics, weights_f16=not args.bf16_weights)
     w = bw.w
     stream = torch.cuda.current_stream().cuda_stream
     run = lambda: bw.block(bw.x)
@@ -215,7 +215,9 @@ def bench_prefill(args, torch):
         "w": w, "ms": ms, "ms_graph": ms_graph, "tokens_per_s": w.tokens / (ms * 1e-3),
         "block_tflops": total / (ms * 1e-3) / 1e12,
         "per_kernel": per_kernel,
-        "roofline": {"bound": "mfma", "kernel": "gate/up GEMM (fp16 h*g2 x bf16 weights on the fp16 matrix cores; rstd row scale + SiLU*up epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "gate/up GEMM (fp16 h*g2 x fp16 weights on the fp16 matrix cores; "
+                                                "rstd row scale + SiLU*up epilogue)" if not args.bf16_weights else
+                     "gate/up GEMM (fp16 h*g2 x bf16 weights converted in registers; rstd row scale + SiLU*up epilogue)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic("gate_up"),
                      "flops_per_launch": fl[dom]},
@@ -230,7 +232,7 @@ def bench_other_blocks(args, torch):
     from decoder_only_transformer_llama_amd.workloads import block_workload
     out = {}
     for wid in (2, 3):
-        bw = block_workload(wid, "cuda")
+        bw = block_workload(wid, "cuda", weights_f16=not args.bf16_weights)
         w = bw.w
         for _ in range(max(1, args.warmup // 2)):
             bw.block(bw.x)
@@ -362,7 +364,20 @@ def bench_model_prefill(args, torch, wl, seq: int = 2048):
     sequence of `seq` seeded tokens through 32 blocks (filling a KV cache),
     the final norm and the 32000-wide head."""
     from decoder_only_transformer_llama_amd import inputs as I
+    from decoder_only_transformer_llama_amd import ops
     w, m = wl.w, wl.model
+    if not args.bf16_weights:
+        # the same model with its projections and head as fp16 (converted once;
+        # the decode pack and the bf16 weights stay for the decode legs)
+        num, layers = args.numerics, []
+        for lw in m.layers:
+            num_l, l16 = ops.with_f16_weights(args.numerics, lw)
+            layers.append(l16)
+            num = num_l
+        cfg = ops.config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, n_layers=w.n_layers, vocab=w.vocab,
+                         max_seq=w.max_seq, eps=w.eps, theta=w.theta, numerics=num, n_kv_heads=w.n_kv_heads)
+        tok_emb, final_norm, head = m.tensors
+        m = ops.Model(cfg, layers, tok_emb, final_norm, ops.convert_weights_f16(head))
     toks = I.tokens(w, (1, seq), device="cuda", stream=1)
     kc, vc = m.new_cache(1, "cuda"), m.new_cache(1, "cuda")
     for _ in range(max(1, args.warmup // 2)):
@@ -379,7 +394,7 @@ def bench_model_prefill(args, torch, wl, seq: int = 2048):
     torch.cuda.synchronize()
     blk = block_flops(type("W", (), {"tokens": seq, "dim": w.dim, "hidden": w.hidden, "seq": seq, "batch": 1}))
     flops = w.n_layers * sum(blk.values()) + 2.0 * seq * w.dim * w.vocab
-    del kc, vc
+    del kc, vc, m
     return {"workload": f"llama-7b-shape model prefill, 32 blocks + head, batch 1, seq {seq}, bf16",
             "ms": round(ms, 3), "tokens_per_s": round(seq / (ms * 1e-3), 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
@@ -427,6 +442,9 @@ def main() -> int:
     ap.add_argument("--no-gqa-decode", action="store_true", help="skip the grouped-query decode leg")
     ap.add_argument("--no-train", action="store_true", help="skip the fp32 training-step leg")
     ap.add_argument("--train-only", action="store_true", help="only the fp32 training-step legs (diagnostic runs)")
+    ap.add_argument("--bf16-weights", action="store_true",
+                    help="prefill: keep the projections' weights bf16 and convert them in registers at every "
+                         "product, instead of fp16 copies made once (same output bits)")
     ap.add_argument("--numerics", type=lambda v: int(v, 0), default=0,
                     help="prefill operand-precision bits (llama_config.numerics; 0 = library default)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -506,6 +524,9 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": "llama-7b-shape block prefill, batch 1, seq 2048, bf16 (fp32 accumulate)",
                    "dim": w.dim, "n_heads": w.n_heads, "hidden": w.hidden, "batch": w.batch, "seq": w.seq,
+                   "weights": ("bf16, converted to fp16 in registers at each product" if args.bf16_weights else
+                               "bf16 model; projections stored as fp16 copies made once before timing "
+                               "(output bit-identical to converting in registers)"),
                    "parallelism": "single GPU"},
         "block_mfma_frac": round(pf["block_tflops"] / PEAK_BF16_TFLOPS, 4),
         "block_tflops": round(pf["block_tflops"], 1),

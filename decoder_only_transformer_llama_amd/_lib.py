@@ -27,6 +27,7 @@ NUM_O_A_PAIR, NUM_FFN_A_PAIR, NUM_DOWN_A_PAIR = 1 << 3, 1 << 4, 1 << 5
 NUM_ATTN_F16 = 1 << 6
 NUM_QKV_A_F16, NUM_O_A_F16, NUM_FFN_A_F16, NUM_DOWN_A_F16 = 1 << 7, 1 << 8, 1 << 9, 1 << 10
 NUM_GEMM_F16 = NUM_QKV_A_F16 | NUM_O_A_F16 | NUM_FFN_A_F16 | NUM_DOWN_A_F16
+NUM_W_F16 = 1 << 11
 NORM_PRE, NORM_POST, NORM_NONE = 0, 1, 2
 
 EXPORTS = (
@@ -35,7 +36,7 @@ EXPORTS = (
     "llama_workspace_size", "llama_status_string", "llama_last_error", "llama_trace_begin", "llama_trace_end",
     "llama_trace_label", "llama_argmax", "llama_decode_pack_size", "llama_pack_decode_weights",
     "llama_causal_attn_backward", "llama_block_train_saved_size", "llama_block_train_forward",
-    "llama_block_backward", "llama_axpby",
+    "llama_block_backward", "llama_axpby", "llama_convert_weights_f16",
 )
 
 
@@ -95,6 +96,7 @@ def load() -> ctypes.CDLL:
         "llama_block_backward": [cfgp, ctypes.POINTER(BlockWeights), vp, vp, sz, vp, vp, ctypes.POINTER(BlockWeights),
                                  i32, i32, vp, sz, vp],
         "llama_axpby": [vp, vp, vp, f32, f32, i64, vp],
+        "llama_convert_weights_f16": [vp, vp, i64, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -61,11 +61,12 @@ struct Carve {
   }
 };
 
-constexpr uint32_t kNumOptionBits = (LLAMA_NUM_DOWN_A_F16 << 1) - 1;   // bits 0 .. 10 of the numerics field
+constexpr uint32_t kNumOptionBits = (LLAMA_NUM_W_F16 << 1) - 1;   // bits 0 .. 11 of the numerics field
 
 uint32_t numerics_of(const llama_config *c) {
   if (c->numerics & LLAMA_NUM_EXPLICIT) return c->numerics;
-  return LLAMA_NUM_ATTN_F16 | LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 | LLAMA_NUM_FFN_A_F16;
+  return LLAMA_NUM_ATTN_F16 | LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 | LLAMA_NUM_FFN_A_F16 |
+         (c->numerics & LLAMA_NUM_W_F16);
 }
 
 int round_up(int v, int m) { return (v + m - 1) / m * m; }
@@ -170,8 +171,8 @@ int check_block_cfg(const llama_config *c, int batch, int seq) {
     if (c->dim % 256 || c->hidden % 128) return LLAMA_ERR_UNSUPPORTED;
   }
   if (c->norm_placement < LLAMA_NORM_PRE || c->norm_placement > LLAMA_NORM_NONE) return LLAMA_ERR_UNSUPPORTED;
-  // numerics: 0, or LLAMA_NUM_EXPLICIT with known option bits
-  if (c->numerics != LLAMA_NUM_DEFAULT &&
+  // numerics: 0 or LLAMA_NUM_W_F16 (default operands), or LLAMA_NUM_EXPLICIT with known option bits
+  if (c->numerics != LLAMA_NUM_DEFAULT && c->numerics != LLAMA_NUM_W_F16 &&
       (!(c->numerics & LLAMA_NUM_EXPLICIT) || (c->numerics & ~(LLAMA_NUM_EXPLICIT | kNumOptionBits))))
     return LLAMA_ERR_UNSUPPORTED;
   // fp16 attention operands are single values: no q/k or v pairs with them
@@ -460,6 +461,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   // fp16 activation operands, per projection
   const int qf16 = (num & LLAMA_NUM_QKV_A_F16) ? 1 : 0, of16 = (num & LLAMA_NUM_O_A_F16) ? 1 : 0;
   const int ff16 = (num & LLAMA_NUM_FFN_A_F16) ? 1 : 0, df16 = (num & LLAMA_NUM_DOWN_A_F16) ? 1 : 0;
+  // GEMM mode of an fp16 operand: weights converted in registers (1) or supplied as fp16 (2)
+  const int wf = (num & LLAMA_NUM_W_F16) ? 2 : 1;
   const int vts = vt_stride_of(seq);
   // Pre-norm (LLaMA) folds RMSNorm into the next projection; post-norm and
   // no-norm feed the branches the trunk itself (operand x, no rstd scale).
@@ -510,7 +513,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   for (int i = 0; i < nqp; ++i) {
     q.n_base = qp[i].n_base;
     q.n_end = qp[i].n_end;
-    HIP_TRY(gemm_launch(GemmKey{qp[i].bn, qkv_pair, EPI_QKV, qf16}, q, s), "qkv projection");
+    HIP_TRY(gemm_launch(GemmKey{qp[i].bn, qkv_pair, EPI_QKV, qf16 * wf}, q, s), "qkv projection");
   }
 
   AttnArgs at{};
@@ -555,7 +558,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   o.r_f32 = x_dtype == LLAMA_F32;
   o.k_splits = oc.splits;
   o.part = b.part;
-  HIP_TRY(gemm_launch(GemmKey{oc.bn, opair, oc.splits > 1 ? EPI_PARTIAL : EPI_RESID, of16}, o, s),
+  HIP_TRY(gemm_launch(GemmKey{oc.bn, opair, oc.splits > 1 ? EPI_PARTIAL : EPI_RESID, of16 * wf}, o, s),
           "output projection");
 
   // post-norm: h = RMSNorm(x + attn Wo^T; g1) in place, fp32
@@ -585,7 +588,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   f.C_lo = dpair ? b.u_lo : nullptr;
   f.c_f16 = df16;   // u in the format the down projection takes
   f.ldc = c->hidden;
-  HIP_TRY(gemm_launch(GemmKey{256, ffn_pair, EPI_SILU, ff16}, f, s), "gate/up projection");
+  HIP_TRY(gemm_launch(GemmKey{256, ffn_pair, EPI_SILU, ff16 * wf}, f, s), "gate/up projection");
 
   GemmArgs dn{};
   dn.M = M;
@@ -603,7 +606,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   const ResidCfg dc = choose_resid(M, d, c->hidden, dpair);
   dn.k_splits = dc.splits;
   dn.part = b.part;
-  HIP_TRY(gemm_launch(GemmKey{dc.bn, dpair, dc.splits > 1 ? EPI_PARTIAL : EPI_RESID, df16}, dn, s),
+  HIP_TRY(gemm_launch(GemmKey{dc.bn, dpair, dc.splits > 1 ? EPI_PARTIAL : EPI_RESID, df16 * wf}, dn, s),
           "down projection");
   if (dc.splits > 1) HIP_TRY(resid_sum_launch(b.h, b.part, dc.splits, (int64_t)M * d, y, s), "down residual");
   if (post) HIP_TRY(rmsnorm_launch(1, 1, y, w->ffn_norm, y, M, d, c->norm_eps, s, 0), "ffn norm");
@@ -805,6 +808,18 @@ int llama_axpby(float *z, const float *x, const float *y, float a, float b, int6
   if (n < 0) return LLAMA_ERR_SHAPE;
   hipStream_t s = (hipStream_t)stream;
   HIP_TRY(axpby_launch(z, x, y, a, b, n, s), "axpby");
+  return LLAMA_OK;
+}
+
+int llama_convert_weights_f16(const void *src, void *dst, int64_t n, void *stream) {
+  if (n < 0) return LLAMA_ERR_SHAPE;
+  if (n == 0) return LLAMA_OK;
+  if (!src || !dst) return LLAMA_ERR_NULL;
+  const char *a = (const char *)src, *b = (const char *)dst;
+  const int64_t bytes = n * (int64_t)sizeof(uint16_t);
+  if (a != b && a < b + bytes && b < a + bytes) return LLAMA_ERR_SHAPE;   // partial overlap
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(bf16_to_f16_launch((const uint16_t *)src, (uint16_t *)dst, n, s), "convert weights");
   return LLAMA_OK;
 }
 
@@ -1100,7 +1115,7 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
   hd_.C = logits;
   hd_.c_f32 = 1;
   hd_.ldc = c->vocab;
-  HIP_TRY(gemm_launch(GemmKey{256, hpair, EPI_STORE, hf16}, hd_, s), "output head");
+  HIP_TRY(gemm_launch(GemmKey{256, hpair, EPI_STORE, hf16 * ((num & LLAMA_NUM_W_F16) ? 2 : 1)}, hd_, s), "output head");
   return LLAMA_OK;
 }
 
@@ -1111,6 +1126,8 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   if (st) return st;
   if (batch > 32 || c->max_seq > kDecMaxSeq) return LLAMA_ERR_UNSUPPORTED;
   if ((st = check_model_w(c, w))) return st;
+  // without a pack the skinny GEMMs read the projections themselves, as bf16
+  if (c->dtype == LLAMA_BF16 && (numerics_of(c) & LLAMA_NUM_W_F16) && !w->decode_pack) return LLAMA_ERR_UNSUPPORTED;
   if (!tokens || !pos || !k_cache || !v_cache || !logits) return LLAMA_ERR_NULL;
   const size_t need = ws_bytes_of(c, LLAMA_OP_MODEL_DECODE, batch, 1);
   if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
@@ -1203,6 +1220,7 @@ int llama_pack_decode_weights(const llama_config *c, const llama_model_weights *
   int st = check_model_cfg(c, 1, 1);
   if (st) return st;
   if ((st = check_model_w(c, w))) return st;
+  if (numerics_of(c) & LLAMA_NUM_W_F16) return LLAMA_ERR_UNSUPPORTED;   // the pack is built from bf16 weights
   if (!dst) return LLAMA_ERR_NULL;
   const PackLayout pl = pack_layout(c);
   if (dst_bytes < pl.total * sizeof(uint16_t)) return LLAMA_ERR_WORKSPACE;

@@ -600,4 +600,43 @@ hipError_t argmax_launch(const float *logits, int64_t rows, int vocab, int32_t *
   return hipGetLastError();
 }
 
+// Weights bf16 -> IEEE fp16 ahead of time, by the conversion the GEMM applies
+// to bf16 B fragments in registers (bf16x8_to_f16x8: the value widened to fp32,
+// then rounded toward zero to fp16), so that a product over converted weights
+// sees the same bits. Eight values per lane when both pointers are 16-byte
+// aligned (VEC), else one. In place (src == dst) is safe: a lane reads its
+// values before it writes them and no lane touches another's.
+template <bool VEC>
+__global__ void bf16_to_f16_kernel(const uint16_t *src, uint16_t *dst, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (VEC) {
+    const int64_t i = t * 8;
+    if (i + 8 <= n) {
+      const u32x4 v = *(const u32x4 *)(src + i);
+      *(u32x4 *)(dst + i) = bf16x8_to_f16x8(v);
+      return;
+    }
+    for (int64_t j = i; j < n; ++j) {   // the last lane: fewer than 8 left
+      const float f = __uint_as_float((uint32_t)src[j] << 16);
+      dst[j] = (uint16_t)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f, 0.f));
+    }
+  } else if (t < n) {
+    const float f = __uint_as_float((uint32_t)src[t] << 16);
+    dst[t] = (uint16_t)__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f, 0.f));
+  }
+}
+
+hipError_t bf16_to_f16_launch(const uint16_t *src, uint16_t *dst, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const bool vec = (((uintptr_t)src | (uintptr_t)dst) & 15) == 0;
+  const int64_t lanes = vec ? (n + 7) / 8 : n;
+  const int64_t blocks = (lanes + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if (vec)
+    hipLaunchKernelGGL(bf16_to_f16_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  else
+    hipLaunchKernelGGL(bf16_to_f16_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n);
+  return hipGetLastError();
+}
+
 }  // namespace llama

@@ -16,9 +16,11 @@
 //
 // A is bf16, a bf16 hi/lo pair (A_lo non-null: both parts are multiplied into
 // the same accumulator, which carries an fp32 activation at ~2^-16 relative
-// accuracy through bf16 matrix cores), or IEEE fp16 (F16: the bf16 weights
+// accuracy through bf16 matrix cores), or IEEE fp16 (F16 1: the bf16 weights
 // are converted to fp16 in registers, exactly in fp16's normal range, and the
-// fp16 matrix cores run at the bf16 rate with 11-bit activations).
+// fp16 matrix cores run at the bf16 rate with 11-bit activations; F16 2: the
+// weights arrive already converted, by the same conversion, and go to the
+// matrix cores as loaded).
 //
 // Epilogues (elementwise work of the block fused into the producing GEMM):
 //  - every epilogue first scales row r by rstd[r] when rstd is given: the
@@ -111,10 +113,13 @@ DEV void interleave() {
   if (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, ID);
 }
 
-// F16: the A operand holds IEEE fp16 and the bf16 B fragments are converted
-// to fp16 in registers (exactly, for weights in fp16's normal range) before
-// fp16 matrix-core products: 11-bit activations at the bf16 rate.
-template <int BN, bool APAIR, int EPI, bool F16 = false>
+// F16 0: bf16 A (or pair) and bf16 B. F16 1: the A operand holds IEEE fp16
+// and the bf16 B fragments are converted to fp16 in registers (exactly, for
+// weights in fp16's normal range) before fp16 matrix-core products: 11-bit
+// activations at the bf16 rate. F16 2: A and B both hold fp16 (B converted
+// once, ahead of time, by the same rule), so the products see the same bits
+// as with F16 1 without the 3 VALU instructions per two weights.
+template <int BN, bool APAIR, int EPI, int F16 = 0>
 __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmArgs a) {
   static_assert(!(F16 && APAIR), "fp16 operands are single");
   using G = GemmCfg<BN, APAIR>;
@@ -197,7 +202,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   // Operand fragments of one 16-deep k-substep: A (and its lo part) for the
   // wavefront's 4 row tiles, B for its TN column tiles.
   struct Frag {
-    u32x4 a[G::TM], al[APAIR ? G::TM : 1], b[G::TN];   // raw bits: bf16 (or fp16 when F16)
+    u32x4 a[G::TM], al[APAIR ? G::TM : 1], b[G::TN];   // raw bits: bf16, or fp16 per F16
   };
   auto read_frag = [&](Frag &f, int kt, int ks) {
     const u32x4 *sa = smem + (kt % STAGES) * G::STAGE;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
 #pragma unroll
     for (int j = 0; j < G::TN; ++j) {
       const int r = wn * G::WN + j * 32 + l32;
-      f.b[j] = sb[r * CH + (c ^ swz<CH>(r))];   // converted at use (F16), not here: the
+      f.b[j] = sb[r * CH + (c ^ swz<CH>(r))];   // converted at use (F16 1), not here: the
                                                   // LDS wait then stays next to the MFMAs
     }
 #pragma unroll
@@ -221,7 +226,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   auto mma = [&](const Frag &f) {
     u32x4 bh[G::TN];
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) bh[j] = F16 ? bf16x8_to_f16x8(f.b[j]) : f.b[j];
+    for (int j = 0; j < G::TN; ++j) bh[j] = F16 == 1 ? bf16x8_to_f16x8(f.b[j]) : f.b[j];
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
 #pragma unroll
@@ -579,7 +584,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   }
 }
 
-template <int BN, bool APAIR, int EPI, bool F16 = false>
+template <int BN, bool APAIR, int EPI, int F16 = 0>
 hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   using G = GemmCfg<BN, APAIR>;
   const int n_end = a.n_end > 0 ? a.n_end : a.N;
@@ -599,5 +604,7 @@ hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   if (key.bn == BN_ && key.apair == APAIR_ && key.epi == EPI_ && !key.f16)                  \
     return gemm_launch_t<BN_, APAIR_, EPI_>(a, s);
 #define GEMM_CASE_F16(BN_, EPI_)                                                           \
-  if (key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16)                            \
-    return gemm_launch_t<BN_, false, EPI_, true>(a, s);
+  if (key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16 == 1)                       \
+    return gemm_launch_t<BN_, false, EPI_, 1>(a, s);                                       \
+  if (key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16 == 2)                       \
+    return gemm_launch_t<BN_, false, EPI_, 2>(a, s);

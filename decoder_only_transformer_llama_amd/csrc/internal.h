@@ -25,7 +25,7 @@ struct GemmArgs {
   int64_t lda;
   const float *rstd;             // optional per-row scale applied to the accumulator
   int b_mode;
-  const uint16_t *B0, *B1, *B2;  // weights [rows, K] bf16
+  const uint16_t *B0, *B1, *B2;  // weights [rows, K] bf16 (fp16 with key f16 == 2)
   int n_seg;                     // BMODE_CONCAT3: rows of B0 (the query projection)
   int n_seg_kv;                  // BMODE_CONCAT3: rows of B1 and of B2 (0: n_seg)
   // EPI_STORE / EPI_RESID / EPI_SILU outputs
@@ -60,7 +60,8 @@ __host__ __device__ inline const uint16_t *concat3_row(const uint16_t *B0, const
 
 struct GemmKey {
   int bn, apair, epi;
-  int f16 = 0;   // A operand fp16, B (bf16 weights) converted to fp16 in registers
+  int f16 = 0;   // 1: A operand fp16, B (bf16 weights) converted to fp16 in registers;
+                 // 2: A and B (weights converted ahead of time) both fp16
 };
 
 // Returns a hipError_t; hipErrorInvalidValue when no instance matches `key`.
@@ -205,6 +206,9 @@ hipError_t rmsnorm_bwd_launch(const float *x, const float *g, const float *dy, c
 hipError_t swiglu_bwd_launch(const float *gate, const float *up, const float *du, float *d_gate, float *d_up,
                              int64_t n, hipStream_t s);
 hipError_t axpby_launch(float *z, const float *x, const float *y, float a, float b, int64_t n, hipStream_t s);
+// dst[i] = IEEE fp16 of the bf16 value src[i], by the GEMM's in-register
+// weight conversion (round toward zero). src == dst allowed.
+hipError_t bf16_to_f16_launch(const uint16_t *src, uint16_t *dst, int64_t n, hipStream_t s);
 
 
 }  // namespace llama

@@ -177,6 +177,41 @@ class Block:
         return y
 
 
+def convert_weights_f16(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """IEEE fp16 copy of a bf16 weight tensor (out may be w itself, viewed as
+    fp16 afterwards), by the library's load-time conversion: the one its fp16
+    matrix-core products otherwise apply to bf16 weights in registers."""
+    _dev(w)
+    if w.dtype != torch.bfloat16:
+        raise TypeError("convert_weights_f16 takes a bf16 tensor")
+    if out is None:
+        out = torch.empty(w.shape, dtype=torch.float16, device=w.device)
+    _dev(out)
+    if out.numel() != w.numel() or out.element_size() != 2:
+        raise ValueError("out must hold as many 16-bit values as w")
+    L.check(L.load().llama_convert_weights_f16(_p(w), _p(out), w.numel(), _stream()), "llama_convert_weights_f16")
+    return out
+
+
+# Projections whose weights LLAMA_NUM_W_F16 supplies as fp16, by the operand bit that selects each.
+_W_F16_OF = ((L.NUM_QKV_A_F16, ("wq", "wk", "wv")), (L.NUM_O_A_F16, ("wo",)),
+             (L.NUM_FFN_A_F16, ("w_gate", "w_up")), (L.NUM_DOWN_A_F16, ("w_down",)))
+_NUM_DEFAULT_SET = L.NUM_ATTN_F16 | L.NUM_QKV_A_F16 | L.NUM_O_A_F16 | L.NUM_FFN_A_F16
+
+
+def with_f16_weights(numerics: int, weights: Dict[str, torch.Tensor]):
+    """(numerics | NUM_W_F16, weights) for a bf16 block: the projections whose
+    activation operand `numerics` makes fp16 are replaced by fp16 copies; the
+    rest (gains, bf16-operand projections) are the same tensors."""
+    num = numerics if numerics & L.NUM_EXPLICIT else _NUM_DEFAULT_SET
+    out = dict(weights)
+    for bit, keys in _W_F16_OF:
+        if num & bit:
+            for k in keys:
+                out[k] = convert_weights_f16(weights[k])
+    return numerics | L.NUM_W_F16, out
+
+
 def axpby(z: torch.Tensor, x: torch.Tensor, y: torch.Tensor, a: float, b: float) -> torch.Tensor:
     """z = a x + b y over fp32 tensors of one size (z may be x or y)."""
     _dev(z, x, y)

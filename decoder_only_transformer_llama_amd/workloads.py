@@ -20,10 +20,15 @@ class BlockWorkload:
     block: "ops.Block"
 
 
-def block_workload(wid: int, device="cuda", numerics: int = 0) -> BlockWorkload:
+def block_workload(wid: int, device="cuda", numerics: int = 0, weights_f16: bool = False) -> BlockWorkload:
+    """A block's seeded weights, input and callable. With `weights_f16`, the
+    projections with fp16 operands get their weights converted to fp16 once,
+    here (LLAMA_NUM_W_F16: the same bits the in-register conversion gives)."""
     w = I.workload(wid)
     wt = I.block_weights(w, device=device)
     x = I.block_input(w, device=device)
+    if weights_f16:
+        numerics, wt = ops.with_f16_weights(numerics, wt)
     cfg = ops.config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
                      numerics=numerics, n_kv_heads=w.n_kv_heads)
     return BlockWorkload(w, wt, x, ops.Block(cfg, wt, w.batch, w.seq))

@@ -80,9 +80,20 @@ typedef enum {
  *    weights are converted to fp16 in registers, exactly for magnitudes in
  *    [2^-14, 65504] (smaller ones become fp16 subnormals, within 2^-24).
  *    LLAMA_NUM_GEMM_F16 is all four.
+ *  - LLAMA_NUM_W_F16: the weights of every projection whose activation
+ *    operand is fp16 arrive as IEEE fp16 instead of bf16, made once by
+ *    llama_convert_weights_f16 (wq, wk, wv with QKV_A_F16, and the output head
+ *    of llama_model_forward with it; wo with O_A_F16; w_gate, w_up with
+ *    FFN_A_F16; w_down with DOWN_A_F16). That is the conversion the matrix
+ *    cores' operand otherwise gets in registers, so results are bit-identical
+ *    to the same set without this bit; it only moves the conversion out of the
+ *    GEMM loop. Gains, embeddings and the other projections stay bf16.
+ *    llama_pack_decode_weights rejects it (the pack is built from bf16
+ *    weights), and llama_model_decode accepts it only with a decode pack.
  * LLAMA_NUM_DEFAULT (0) selects the library's default set,
  * LLAMA_NUM_ATTN_F16 | LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 |
- * LLAMA_NUM_FFN_A_F16 (SiLU(gate)*up stays a single bf16 value);
+ * LLAMA_NUM_FFN_A_F16 (SiLU(gate)*up stays a single bf16 value), and
+ * LLAMA_NUM_W_F16 alone that set with fp16 weights;
  * LLAMA_NUM_EXPLICIT plus any of the
  * bits selects exactly those (ATTN_F16 excludes QK_PAIR and V_PAIR; an
  * operand is either a pair or fp16). Any other value (option bits without
@@ -102,6 +113,7 @@ typedef enum {
 #define LLAMA_NUM_FFN_A_F16 (1u << 9)   /* h*g2 operand of the gate/up projection as fp16 */
 #define LLAMA_NUM_DOWN_A_F16 (1u << 10) /* SiLU(gate)*up operand of the down projection as fp16 */
 #define LLAMA_NUM_GEMM_F16 (LLAMA_NUM_QKV_A_F16 | LLAMA_NUM_O_A_F16 | LLAMA_NUM_FFN_A_F16 | LLAMA_NUM_DOWN_A_F16)
+#define LLAMA_NUM_W_F16 (1u << 11)      /* weights of the fp16-operand projections supplied as fp16 */
 
 /* Where a block's two RMSNorms sit ([P1] "Pre-norm: the norm goes on the
  * branch, not the trunk" and "Now break it"). With Attn and FFN the two
@@ -270,6 +282,18 @@ int llama_argmax(const float *logits, int64_t rows, int vocab, int32_t *out, voi
 int llama_decode_pack_size(const llama_config *c, size_t *bytes);
 int llama_pack_decode_weights(const llama_config *c, const llama_model_weights *w, void *dst,
                               size_t dst_bytes, void *stream);
+
+/* Prefill weights as IEEE fp16 (for LLAMA_NUM_W_F16), a load-time transform
+ * like the decode pack, not an operation of the pages: dst[i] = the bf16
+ * value src[i] widened to fp32 and rounded toward zero to fp16, exactly the
+ * conversion the fp16 matrix-core products apply to bf16 weights in
+ * registers. Exact for magnitudes in [2^-14, 65504]; smaller ones become fp16
+ * subnormals (an absolute change below 2^-24); larger ones are outside the
+ * fp16 operand's range. src and dst are device buffers of n 16-bit values,
+ * either the same buffer (in place) or disjoint; any alignment. Runs on
+ * `stream`. Errors: n < 0 or a partial overlap (LLAMA_ERR_SHAPE), NULL
+ * pointers with n > 0. n == 0 is a no-op. */
+int llama_convert_weights_f16(const void *src, void *dst, int64_t n, void *stream);
 
 /* Workspace bytes for `op` at the given batch and seq (seq ignored for decode).
  * Writes *bytes (host pointer). Errors as the matching entry point would report

@@ -133,6 +133,17 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
     assert lib.llama_pack_decode_weights(ctypes.byref(c), ctypes.byref(mw), FAKE, 16, None) == L.LLAMA_ERR_WORKSPACE
     assert lib.llama_pack_decode_weights(ctypes.byref(cf), ctypes.byref(mw), FAKE, 1 << 40, None) == \
         L.LLAMA_ERR_UNSUPPORTED
+    # fp16 prefill weights: the decode pack is built from bf16 weights, and a
+    # decode step without a pack would read the projections as bf16
+    cw = _cfg(numerics=L.NUM_W_F16)
+    assert lib.llama_pack_decode_weights(ctypes.byref(cw), ctypes.byref(mw), FAKE, 1 << 40, None) == \
+        L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_model_decode(ctypes.byref(cw), ctypes.byref(mw), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE,
+                                  1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_convert_weights_f16(FAKE, FAKE, -1, None) == L.LLAMA_ERR_SHAPE
+    assert lib.llama_convert_weights_f16(None, FAKE, 8, None) == L.LLAMA_ERR_NULL
+    assert lib.llama_convert_weights_f16(None, None, 0, None) == 0                    # nothing to do
+    assert lib.llama_convert_weights_f16(0x1000, 0x1008, 8, None) == L.LLAMA_ERR_SHAPE  # partial overlap
 
 
 def test_grouped_kv_heads_validation_and_sizes():
@@ -160,7 +171,11 @@ def test_grouped_kv_heads_validation_and_sizes():
     # fp16 projection operands are single values as well
     assert ws(numerics=L.NUM_EXPLICIT | L.NUM_GEMM_F16) == 0
     assert ws(numerics=L.NUM_QK_PAIR) == L.LLAMA_ERR_UNSUPPORTED             # option bits need EXPLICIT
-    assert ws(numerics=L.NUM_EXPLICIT | (1 << 11)) == L.LLAMA_ERR_UNSUPPORTED  # unknown bit
+    assert ws(numerics=L.NUM_EXPLICIT | (1 << 12)) == L.LLAMA_ERR_UNSUPPORTED  # unknown bit
+    # fp16 weights: alone (the default operand set) or among explicit bits
+    assert ws(numerics=L.NUM_W_F16) == 0
+    assert ws(numerics=L.NUM_EXPLICIT | L.NUM_GEMM_F16 | L.NUM_W_F16) == 0
+    assert ws(numerics=L.NUM_W_F16 | L.NUM_ATTN_F16) == L.LLAMA_ERR_UNSUPPORTED
     for pair in (L.NUM_QKV_A_PAIR, L.NUM_O_A_PAIR, L.NUM_FFN_A_PAIR, L.NUM_DOWN_A_PAIR):
         assert ws(numerics=L.NUM_EXPLICIT | L.NUM_GEMM_F16 | pair) == L.LLAMA_ERR_UNSUPPORTED
     # fewer key/value heads shrink the packed decode weights by exactly the Wk, Wv rows

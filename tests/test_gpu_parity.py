@@ -252,6 +252,71 @@ def test_block_operand_sets(wid, numerics):
     assert err < TOL_BF16
 
 
+# ---------------------------------------------------------------- fp16 weights (LLAMA_NUM_W_F16)
+def f16_rtz_bits_of_bf16(bits: np.ndarray) -> np.ndarray:
+    """The load-time weight conversion written out on the host: the bf16 value
+    (bits << 16 as fp32), rounded toward zero to IEEE fp16. From 2^-14 up to
+    65504 fp16 holds every bf16 value exactly; below, the result is the fp16
+    subnormal k * 2^-24 with k = floor(|v| / 2^-24), sign kept."""
+    v = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    a = np.abs(v)
+    assert a.max() <= 65504.0
+    mag = np.where(a < 2.0 ** -14, np.floor(a / 2.0 ** -24) * 2.0 ** -24, a)
+    out = np.where(np.signbit(v), -mag, mag).astype(np.float16)   # exact: each value is an fp16
+    return out.view(np.uint16)
+
+
+def test_convert_weights_f16_definition():
+    """Aligned (eight values per lane) and unaligned (one per lane) paths,
+    ragged lengths, in place, and values at and below fp16's normal range."""
+    g = np.random.default_rng(11)
+    vals = np.concatenate([g.normal(0.0, 0.02, 4093), g.normal(0.0, 3.0, 1000),
+                           [2.0 ** -14, -2.0 ** -14, 1.5 * 2.0 ** -20, -3.7e-6, 6e-8, -6e-8, 1e-9, -1e-9, 0.0, -0.0,
+                            60000.0, -1.0, 2.0 ** -14 * 0.999]])
+    bits = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # bf16 by truncation: any bf16 will do
+    want = f16_rtz_bits_of_bf16(bits)
+    src = torch.from_numpy(bits.view(np.int16).copy()).cuda().view(torch.bfloat16)
+    for off in (0, 1, 3, 8):
+        got = ops().convert_weights_f16(src[off:])
+        torch.cuda.synchronize()
+        assert got.dtype == torch.float16
+        assert np.array_equal(got.cpu().view(torch.int16).numpy().view(np.uint16), want[off:]), off
+    t = src.clone()
+    ops().convert_weights_f16(t, out=t.view(torch.float16))
+    torch.cuda.synchronize()
+    assert np.array_equal(t.cpu().view(torch.int16).numpy().view(np.uint16), want)
+
+
+def run_block_pair(wid, numerics):
+    """(y over bf16 weights, y over the fp16 weight copies) for one block workload."""
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    cfg = lambda num: ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
+                                   numerics=num, n_kv_heads=w.n_kv_heads)
+    y0 = ops().Block(cfg(numerics), wt, w.batch, w.seq)(x).clone()
+    num16, wt16 = ops().with_f16_weights(numerics, wt)
+    y1 = ops().Block(cfg(num16), wt16, w.batch, w.seq)(x).clone()
+    torch.cuda.synchronize()
+    return y0, y1, wt16, w
+
+
+@pytest.mark.parametrize("wid,numerics", [(100, L.NUM_DEFAULT), (103, L.NUM_DEFAULT), (104, L.NUM_DEFAULT),
+                                          (100, F16_OPERANDS), (104, F16_OPERANDS), (1, L.NUM_DEFAULT)])
+def test_block_f16_weights_bitwise_equal(wid, numerics):
+    """Weights converted once feed the matrix cores the bits that the
+    in-register conversion gives them, through the same tiles in the same
+    order: the block output is bitwise that of the same operand set over the
+    bf16 weights (whose parity with the oracle the tests above check)."""
+    y0, y1, wt16, w = run_block_pair(wid, numerics)
+    assert torch.isfinite(y0).all()
+    assert torch.equal(y0, y1)
+    f16 = [k for k, v in wt16.items() if v.dtype == torch.float16]
+    down16 = ["w_down"] if numerics & L.NUM_EXPLICIT and numerics & L.NUM_DOWN_A_F16 else []
+    assert sorted(f16) == sorted(["wq", "wk", "wv", "wo", "w_gate", "w_up"] + down16)
+    print(f"block {w.name} (numerics {numerics:#x}): fp16 weights bitwise equal ({len(f16)} matrices)")
+
+
 def test_block_deterministic():
     w = I.workload(100)
     wt = I.block_weights(w, device="cuda")
@@ -430,6 +495,45 @@ def test_decode_packed_weights_bitwise_equal(wid):
     torch.cuda.synchronize()
     assert torch.equal(ref, got)
     assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+
+
+@pytest.mark.parametrize("wid", [101, 105, 108])
+def test_model_f16_weights_bitwise_equal(wid):
+    """Prefill with the projections and the head as fp16 copies gives the
+    logits and cache bits of prefill over the bf16 weights; a decode step of
+    that model, streaming the pack built from the bf16 weights, gives the
+    decode logits of the bf16 model."""
+    w, m, layers, gl = small_model(wid)
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    ref = m.forward(toks, kc, vc).clone()
+    m.pack_for_decode()
+    conv = [ops().with_f16_weights(L.NUM_DEFAULT, lw) for lw in layers]
+    c = m.cfg
+    cfg16 = ops().config(c.dim, c.n_heads, c.hidden, dtype=w.torch_dtype, n_layers=c.n_layers, vocab=c.vocab,
+                         max_seq=c.max_seq, eps=w.eps, theta=w.theta, numerics=conv[0][0], n_kv_heads=c.n_kv_heads)
+    m16 = ops().Model(cfg16, [l16 for _, l16 in conv], gl["tok_embeddings"], gl["final_norm"],
+                      ops().convert_weights_f16(gl["output"]))
+    kc2, vc2 = m16.new_cache(B, "cuda"), m16.new_cache(B, "cuda")
+    got = m16.forward(toks, kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref).all()
+    assert torch.equal(ref, got)
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+    # decode: without a pack the fp16-weight model is refused; with the bf16-built pack it matches
+    tok = I.tokens(w, (B,), device="cuda")
+    pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    with pytest.raises(L.LlamaError):
+        m16.decode(tok, pos, kc2, vc2)
+    m16.decode_pack = m.decode_pack
+    m16.wstruct.decode_pack = m.decode_pack.data_ptr()
+    d0 = m.decode(tok, pos, kc, vc).clone()
+    d1 = m16.decode(tok, pos, kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.equal(d0, d1)
+    assert torch.equal(kc, kc2) and torch.equal(vc, vc2)
+    print(f"{w.name}: fp16-weight prefill and decode bitwise equal")
 
 
 def test_decode_invalid_position_gives_nan_row():
