@@ -134,8 +134,15 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   const int tiles_m = (a.M + BM - 1) / BM;
   const int n_end = a.n_end > 0 ? a.n_end : a.N;
   const int tiles_n = (n_end - a.n_base + BN - 1) / BN;
+  // Tiles in groups of up to 8 row tiles, column-major inside a group, so
+  // that the 32 workgroups one XCD runs at a time cover 8 row tiles x 4
+  // column tiles of C (12 operand strips through that XCD's L2) whatever M
+  // is, instead of one column of up to M/256 row tiles.
   const int t = xcd_remap(blockIdx.x, tiles_m * tiles_n);
-  const int tm = t % tiles_m, tn = t / tiles_m;
+  constexpr int GM = 8;
+  const int grp = t / (GM * tiles_n), first = grp * GM;
+  const int gm = min(tiles_m - first, GM), r_in = t - first * tiles_n;
+  const int tm = first + r_in % gm, tn = r_in / gm;
   const int m0 = tm * BM, n0 = a.n_base + tn * BN;
 
   // ---- global source of each lane's 16-byte piece, fixed over K
