@@ -48,10 +48,14 @@ def f64(a) -> np.ndarray:
 
 # --------------------------------------------------------------------------- sizes
 def llama_hidden(dim: int, multiple_of: int = 256) -> int:
-    """SwiGLU hidden width: two thirds of 4*dim, truncated, then rounded up to a
-    multiple of `multiple_of` ([P1] "SwiGLU ..." and `llama_hidden` in "The code")."""
-    hidden = (2 * 4 * dim) // 3
-    return multiple_of * ((hidden + multiple_of - 1) // multiple_of)
+    """SwiGLU hidden width ([P1] "SwiGLU: a gate in the FFN"): the vanilla
+    FFN's 4*dim cut to two thirds, then rounded up to a multiple of
+    `multiple_of` (256), the smallest such multiple at or above 8*dim/3,
+    found here in exact integer arithmetic. For multiples of 8 this agrees
+    with truncating 8*dim/3 first: 8*dim is then never one or two above a
+    multiple of 3*multiple_of."""
+    units = -(-(8 * dim) // (3 * multiple_of))   # ceil(8 dim / (3 multiple_of))
+    return units * multiple_of
 
 
 def count_params(dim: int, n_layers: int, hidden: int, vocab: int = 32000, bias: bool = False) -> int:
@@ -104,24 +108,24 @@ def linear(x: np.ndarray, w: np.ndarray) -> np.ndarray:
 
 
 def rope(x: np.ndarray, positions: np.ndarray, head_dim: int, theta: float = 10000.0) -> np.ndarray:
-    """Rotary position embedding, applied per head ([P1] `rope`; [P4] RoPE).
+    """Rotary position embedding, applied per head ([P4] RoPE equation; [P1]
+    "RoPE: rotate Q and K, leave V alone").
 
-    Pair i of each head (channels 2i, 2i+1, interleaved as in [P1]'s
-    x[..., 0::2] / x[..., 1::2]) is rotated by the angle pos * theta^(-2i/hd),
-    with hd the head dimension (reading: [P1]'s `d = x.shape[-1]` is the head
-    width when x is laid out per head)."""
+    Channels (2i, 2i+1) of a head are one point of the plane, read as the
+    complex number x[2i] + j x[2i+1]; RoPE turns it by the angle
+    pos * theta^(-2i/hd), i.e. multiplies it by exp(j pos theta^(-2i/hd)),
+    with hd the head dimension (reading: the frequencies run over one head's
+    pairs). The pairs are adjacent channels, the interleaved layout of [P1]."""
     x = f64(x)
     t, width = x.shape
     assert width % head_dim == 0 and head_dim % 2 == 0
-    xh = x.reshape(t, width // head_dim, head_dim)
-    inv = theta ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)   # (hd/2,)
-    ang = np.asarray(positions, dtype=np.float64)[:, None] * inv[None, :]     # (t, hd/2)
-    cos, sin = np.cos(ang)[:, None, :], np.sin(ang)[:, None, :]
-    a, b = xh[..., 0::2], xh[..., 1::2]
-    out = np.empty_like(xh)
-    out[..., 0::2] = a * cos - b * sin
-    out[..., 1::2] = a * sin + b * cos
-    return out.reshape(t, width)
+    pairs = x.reshape(t, width // head_dim, head_dim // 2, 2)
+    z = pairs[..., 0] + 1j * pairs[..., 1]                                    # (t, heads, hd/2)
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    freq = np.power(float(theta), -2.0 * i / head_dim)                        # per-pair frequency
+    turn = np.exp(1j * np.asarray(positions, dtype=np.float64)[:, None, None] * freq[None, None, :])
+    w = z * turn
+    return np.stack([w.real, w.imag], axis=-1).reshape(t, width)
 
 
 def causal_attention(q, k, v, batch: int, seq: int, n_heads: int) -> np.ndarray:

@@ -111,21 +111,24 @@ def _rand(shape, seed):
     return np.random.default_rng(seed).standard_normal(shape)
 
 
-def test_rope_complex_closed_form():
-    """Pair i of a head is the complex number x[2i] + i x[2i+1] multiplied by
-    exp(i * pos * theta^(-2i/hd))."""
+def test_rope_rotation_matrix_closed_form():
+    """RoPE as the block-diagonal rotation matrix of the RoPE equation: per
+    head, R = diag(R_0, ..., R_(hd/2-1)) with R_i the 2x2 rotation by
+    pos * theta^(-2i/hd) acting on channels (2i, 2i+1); y = R x, built here as
+    a full hd x hd matrix per position."""
     hd, H, T = 16, 3, 7
     x = _rand((T, H * hd), 1)
     pos = np.array([0, 1, 2, 5, 100, 1000, 2047], dtype=float)
     y = O.rope(x, pos, hd, 10000.0)
-    z = x.reshape(T, H, hd // 2, 2)
-    zc = z[..., 0] + 1j * z[..., 1]
-    freq = np.array([10000.0 ** (-(2.0 * i) / hd) for i in range(hd // 2)])
-    rot = np.exp(1j * pos[:, None, None] * freq[None, None, :])
-    want = zc * rot
-    yc = y.reshape(T, H, hd // 2, 2)
-    np.testing.assert_allclose(yc[..., 0], want.real, atol=1e-12)
-    np.testing.assert_allclose(yc[..., 1], want.imag, atol=1e-12)
+    want = np.empty_like(x)
+    for t in range(T):
+        R = np.zeros((hd, hd))
+        for i in range(hd // 2):
+            a = pos[t] * 10000.0 ** (-(2.0 * i) / hd)
+            R[2 * i:2 * i + 2, 2 * i:2 * i + 2] = [[math.cos(a), -math.sin(a)], [math.sin(a), math.cos(a)]]
+        for h in range(H):
+            want[t, h * hd:(h + 1) * hd] = R @ x[t, h * hd:(h + 1) * hd]
+    np.testing.assert_allclose(y, want, atol=1e-12)
 
 
 def test_rope_invariants():
