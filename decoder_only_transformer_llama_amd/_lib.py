@@ -79,7 +79,7 @@ def load() -> ctypes.CDLL:
         "llama_causal_attn": [i32, i32, vp, vp, vp, vp, i32, i32, i32, i32, vp, sz, vp],
         "llama_swiglu_ffn": [i32, i32, vp, vp, vp, vp, vp, i64, i32, i32, vp, sz, vp],
         "llama_block_forward": [cfgp, ctypes.POINTER(BlockWeights), i32, vp, vp, i32, i32, vp, sz, vp],
-        "llama_model_forward": [cfgp, ctypes.POINTER(ModelWeights), vp, i32, i32, vp, vp, vp, vp, sz, vp],
+        "llama_model_forward": [cfgp, ctypes.POINTER(ModelWeights), vp, vp, i32, i32, vp, vp, vp, vp, sz, vp],
         "llama_model_decode": [cfgp, ctypes.POINTER(ModelWeights), vp, vp, i32, vp, vp, vp, vp, sz, vp],
         "llama_workspace_size": [cfgp, i32, i32, i32, ctypes.POINTER(sz)],
         "llama_status_string": [i32],

@@ -236,22 +236,26 @@ struct BlockWs {
 
 int vt_stride_of(int seq) { return round_up(seq, 64); }
 
-BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq) {
+// kv_rows: key rows held per sequence (seq, or max_seq for a prefill that may
+// continue a cached prefix); the rope table covers as many positions.
+BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq, int kv_rows = 0) {
   BlockWs b{};
   const int64_t n = (int64_t)batch * seq;
   const int d = c->dim, hd = d / c->n_heads;
+  kv_rows = std::max(kv_rows, seq);
+  const int64_t nk = (int64_t)batch * kv_rows;
   if (c->dtype == LLAMA_BF16) {
-    b.rope_tab = cv.take<float2>((size_t)seq * hd / 2);
+    b.rope_tab = cv.take<float2>((size_t)kv_rows * hd / 2);
     b.rstd1 = cv.take<float>(n);
     b.rstd2 = cv.take<float>(n);
     b.xg_hi = cv.take<uint16_t>(n * d);
     b.xg_lo = cv.take<uint16_t>(n * d);
     b.qh = cv.take<uint16_t>(n * d);
     b.ql = cv.take<uint16_t>(n * d);
-    b.kh = cv.take<uint16_t>(n * d);
-    b.kl = cv.take<uint16_t>(n * d);
-    b.part = (float *)b.qh;   // qh, ql, kh, kl are contiguous: 8 n d bytes = 2 n d floats
-    const size_t vt = (size_t)batch * kv_dim(c) * vt_stride_of(seq);
+    b.kh = cv.take<uint16_t>(nk * d);
+    b.kl = cv.take<uint16_t>(nk * d);
+    b.part = (float *)b.qh;   // qh, ql, kh, kl are contiguous: at least 8 n d bytes = 2 n d floats
+    const size_t vt = (size_t)batch * kv_dim(c) * vt_stride_of(kv_rows);
     b.vth = cv.take<uint16_t>(vt);
     b.vtl = cv.take<uint16_t>(vt);
     b.a_hi = cv.take<uint16_t>(n * d);
@@ -404,7 +408,7 @@ size_t ws_bytes_of(const llama_config *c, int op, int batch, int seq) {
     case LLAMA_OP_MODEL_FORWARD:
       cv.take<float>(n * c->dim);
       cv.take<float>(n * c->dim);
-      carve_block(cv, c, batch, seq);
+      carve_block(cv, c, batch, seq, c->max_seq);
       break;
     case LLAMA_OP_MODEL_DECODE:
       carve_decode(cv, c, batch);
@@ -450,9 +454,11 @@ PackLayout pack_layout(const llama_config *c) {
 // ------------------------------------------------------------------ block launch sequences
 // make_rope: build the (cos, sin) table in b.rope_tab first (a stack of blocks
 // over the same positions builds it once).
+// start_pos (device [batch], or nullptr): the sequences continue a cached
+// prefix (model prefill); k and v^T then hold kv_rows positions per sequence.
 int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype, const void *x, float *y,
                int batch, int seq, const BlockWs &b, uint16_t *kcache, uint16_t *vcache, int max_seq,
-               hipStream_t s, bool make_rope = true) {
+               hipStream_t s, bool make_rope = true, const int32_t *start_pos = nullptr, int kv_rows = 0) {
   const int d = c->dim, H = c->n_heads, hd = d / H, M = batch * seq;
   const uint32_t num = numerics_of(c);
   const bool qkv_pair = num & LLAMA_NUM_QKV_A_PAIR, ffn_pair = num & LLAMA_NUM_FFN_A_PAIR;
@@ -463,9 +469,11 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   const int ff16 = (num & LLAMA_NUM_FFN_A_F16) ? 1 : 0, df16 = (num & LLAMA_NUM_DOWN_A_F16) ? 1 : 0;
   // GEMM mode of an fp16 operand: weights converted in registers (1) or supplied as fp16 (2)
   const int wf = (num & LLAMA_NUM_W_F16) ? 2 : 1;
-  const int vts = vt_stride_of(seq);
+  if (!start_pos) kv_rows = seq;
+  const int vts = vt_stride_of(kv_rows);
   // Pre-norm (LLaMA) folds RMSNorm into the next projection; post-norm and
-  // no-norm feed the branches the trunk itself (operand x, no rstd scale).
+  // no-norm feed the branches the trunk itself (operand x; the row multiplier
+  // then only undoes the fp16 operand's power-of-two scale).
   const bool pre = c->norm_placement == LLAMA_NORM_PRE, post = c->norm_placement == LLAMA_NORM_POST;
 
   // z = RMSNorm(x; g1): statistic + gained operand; the rstd multiply happens in the QKV epilogue
@@ -483,7 +491,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.A = b.xg_hi;
   q.A_lo = qkv_pair ? b.xg_lo : nullptr;
   q.lda = d;
-  q.rstd = pre ? b.rstd1 : nullptr;
+  q.rstd = b.rstd1;
   q.b_mode = BMODE_CONCAT3;
   q.B0 = (const uint16_t *)w->wq;
   q.B1 = (const uint16_t *)w->wk;
@@ -508,6 +516,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.kcache = kcache;
   q.vcache = vcache;
   q.max_seq = max_seq;
+  q.start_pos = start_pos;
+  q.kv_rows = kv_rows;
   ColPart qp[2];
   const int nqp = plan_qkv(M, d, kvd, qp);
   for (int i = 0; i < nqp; ++i) {
@@ -515,6 +525,12 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
     q.n_end = qp[i].n_end;
     HIP_TRY(gemm_launch(GemmKey{qp[i].bn, qkv_pair, EPI_QKV, qf16 * wf}, q, s), "qkv projection");
   }
+  // earlier positions of every sequence come from the cache
+  if (start_pos)
+    HIP_TRY(kv_prefix_launch(kcache, vcache, start_pos, batch, nkv, hd, max_seq, seq, b.kh,
+                             (num & LLAMA_NUM_QK_PAIR) ? b.kl : nullptr, b.vth, (num & LLAMA_NUM_V_PAIR) ? b.vtl : nullptr,
+                             kv_rows, vts, af16, s),
+            "cached prefix");
 
   AttnArgs at{};
   at.qh = b.qh;
@@ -536,6 +552,9 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   at.n_kv_heads = nkv;
   at.vt_stride = vts;
   at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  at.start_pos = start_pos;
+  at.kv_rows = kv_rows;
+  at.max_seq = max_seq;
   HIP_TRY(attn_prefill_launch(at, (num & LLAMA_NUM_QK_PAIR) ? 1 : 0, (num & LLAMA_NUM_V_PAIR) ? 1 : 0, af16, s),
           "attention");
 
@@ -580,7 +599,7 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   f.A = b.xg_hi;
   f.A_lo = ffn_pair ? b.xg_lo : nullptr;
   f.lda = d;
-  f.rstd = pre ? b.rstd2 : nullptr;
+  f.rstd = b.rstd2;
   f.b_mode = BMODE_GATEUP;
   f.B0 = (const uint16_t *)w->w_gate;
   f.B1 = (const uint16_t *)w->w_up;
@@ -1068,9 +1087,9 @@ int llama_block_forward(const llama_config *c, const llama_block_weights *w, int
   return block_bf16(c, w, x_dtype, x, y, batch, seq, b, nullptr, nullptr, 0, s);
 }
 
-int llama_model_forward(const llama_config *c, const llama_model_weights *w, const int32_t *tokens, int batch,
-                        int seq, void *k_cache, void *v_cache, float *logits, void *ws, size_t ws_bytes,
-                        void *stream) {
+int llama_model_forward(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                        const int32_t *start_pos, int batch, int seq, void *k_cache, void *v_cache, float *logits,
+                        void *ws, size_t ws_bytes, void *stream) {
   int st = check_model_cfg(c, batch, seq);
   if (st) return st;
   if ((st = check_model_w(c, w))) return st;
@@ -1083,14 +1102,15 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
   const int d = c->dim, hd = d / c->n_heads;
   Carve cv(ws);
   float *xa = cv.take<float>(n * d), *xb = cv.take<float>(n * d);
-  const BlockWs b = carve_block(cv, c, batch, seq);
+  const BlockWs b = carve_block(cv, c, batch, seq, c->max_seq);
   HIP_TRY(embed_launch(0, w->tok_embeddings, tokens, n, d, c->vocab, xa, s), "embedding");
   const size_t layer_elems = (size_t)batch * kv_heads(c) * c->max_seq * hd;
-  HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");   // shared by every layer
+  // shared by every layer; positions up to max_seq when continuing a prefix
+  HIP_TRY(rope_table_launch(b.rope_tab, start_pos ? c->max_seq : seq, hd, c->rope_theta, s), "rope table");
   for (int l = 0; l < c->n_layers; ++l) {
     st = block_bf16(c, &w->layers[l], LLAMA_F32, xa, xb, batch, seq, b,
                     (uint16_t *)k_cache + l * layer_elems, (uint16_t *)v_cache + l * layer_elems, c->max_seq, s,
-                    false);
+                    false, start_pos, c->max_seq);
     if (st) return st;
     std::swap(xa, xb);
   }
@@ -1116,6 +1136,8 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
   hd_.c_f32 = 1;
   hd_.ldc = c->vocab;
   HIP_TRY(gemm_launch(GemmKey{256, hpair, EPI_STORE, hf16 * ((num & LLAMA_NUM_W_F16) ? 2 : 1)}, hd_, s), "output head");
+  if (start_pos)
+    HIP_TRY(nan_unplaced_rows_launch(start_pos, batch, seq, c->max_seq, logits, c->vocab, s), "unplaced sequences");
   return LLAMA_OK;
 }
 

@@ -102,13 +102,18 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   const int qi = q0 + 32 * w + l32;          // this lane's query
   const int qwave_max = q0 + 32 * w + 31;
   const int64_t tok0 = (int64_t)b * S;
+  // Continuing a cached prefix: queries are positions p0 .. p0+S-1 and the
+  // keys positions 0 .. p0+S-1 (k rows by position, kv_rows per sequence).
+  const int p0 = max(chunk_start(a.start_pos, b, S, a.max_seq), 0);
+  const int nkeys = p0 + S;
+  const int64_t ktok0 = a.start_pos ? (int64_t)b * a.kv_rows : tok0;
   // key/value head of this query head: consecutive groups of n_heads / n_kv_heads
   const int n_kv = a.n_kv_heads > 0 ? a.n_kv_heads : a.n_heads;
   const int kvd = a.kv_dim > 0 ? a.kv_dim : a.dim;
   const int hk = h / (a.n_heads / n_kv);
   const int64_t vbase = ((int64_t)b * n_kv + hk) * HD * a.vt_stride;
 
-  const int kend = min(S, q0 + 128);
+  const int kend = min(nkeys, p0 + q0 + 128);
   const int n_kt = (kend + KT - 1) / KT;        // 32-key tiles
   const int n_st = (n_kt + SUB - 1) / SUB;      // steps of SUB tiles
 
@@ -131,7 +136,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       const int row = kb * (64 / KCH) + lane / KCH;
       const int c = (lane % KCH) ^ rswz<KCH>(row);
       lrow[qb] = row;
-      lsrc[qb] = (part ? a.kl : a.kh) + tok0 * kvd + hk * HD + 8 * c;
+      lsrc[qb] = (part ? a.kl : a.kh) + ktok0 * kvd + hk * HD + 8 * c;
       ldst[qb] = part * KTILE + kb * 64;
     } else {
       const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
@@ -150,8 +155,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       const int kt = min(st_slot * SUB + u, n_kt - 1);
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
-        // K row: rows past S load a valid key (masked later); v^T: key columns
-        const u16 *src = isk[qb] ? lsrc[qb] + (int64_t)min(kt * KT + lrow[qb], S - 1) * kvd : lsrc[qb] + kt * KT;
+        // K row: rows past the last key load a valid key (masked later); v^T: key columns
+        const u16 *src = isk[qb] ? lsrc[qb] + (int64_t)min(kt * KT + lrow[qb], nkeys - 1) * kvd : lsrc[qb] + kt * KT;
         __builtin_amdgcn_global_load_lds((const void *)src, ATT_LDS(st + ldst[qb]), 16, 0, 0);
       }
     }
@@ -189,7 +194,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       issue(step + NST - 1);
     }
     const int s0 = step * SUB * KT;
-    if (s0 > qwave_max) continue;     // whole step above this wavefront's diagonal
+    if (s0 > p0 + qwave_max) continue;   // whole step above this wavefront's diagonal
 
     // ---- scores S^T (32 keys x 32 queries per tile). One tile per step: two
     // accumulators (even and odd k-steps) so that two dependent matrix-core
@@ -230,11 +235,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       const int kt0 = s0 + u * KT;
-      if (kt0 + KT - 1 > q0 + 32 * w || kt0 + KT > S) {
+      if (kt0 + KT - 1 > p0 + q0 + 32 * w || kt0 + KT > nkeys) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt0 + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
-          const bool ok = key <= qi && key < S;
+          const bool ok = key <= p0 + qi && key < nkeys;
           sc[u][r] = ok ? sc[u][r] : -INFINITY;
           mx = fmaxf(mx, sc[u][r]);
         }
@@ -340,6 +345,88 @@ __global__ void vt_pad_zero_kernel(u16 *vth, u16 *vtl, int64_t rows, int seq, in
   if (vtl) vtl[o] = 0;
 }
 
+// Cached prefix of a prefill chunk into the attention operands. One thread
+// per (sequence, key/value head, 8 positions, 8 channels): an 8 x 8 block of
+// the bf16 cache goes to 8 k rows (16-byte stores) and to 8 v^T rows (16-byte
+// stores when all 8 positions are prefix, else element by element).
+template <bool F16>
+__global__ void kv_prefix_kernel(const u16 *__restrict__ kc, const u16 *__restrict__ vc, const int32_t *start_pos,
+                                 int batch, int n_kv, int hd, int max_seq, int seq, u16 *kh, u16 *kl, u16 *vth,
+                                 u16 *vtl, int kv_rows, int vt_stride) {
+  const int npos8 = (max_seq + 7) / 8, nch8 = hd / 8;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (int64_t)batch * n_kv * npos8 * nch8) return;
+  const int e0 = 8 * (int)(idx % nch8);
+  const int64_t r = idx / nch8;
+  const int j0 = 8 * (int)(r % npos8);
+  const int bh = (int)(r / npos8), b = bh / n_kv, hk = bh % n_kv;
+  const int p0 = max(chunk_start(start_pos, b, seq, max_seq), 0);
+  const int pad_end = min((p0 + seq + 31) / 32 * 32, vt_stride);
+  if (j0 >= p0 && (j0 + 8 <= p0 + seq || j0 >= pad_end)) return;   // nothing of this block to write
+  auto cvt = [](u16 v) -> u16 { return F16 ? f2h(bf2f(v)) : v; };   // bf16 -> fp16 is exact in fp16's range
+  const int kvd = n_kv * hd;
+  u16 vt[8][8];   // [channel][position]
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const int j = j0 + jj;
+    u16 vals[8];
+    if (j < p0) {
+      const int64_t src = (((int64_t)b * n_kv + hk) * max_seq + j) * hd + e0;
+      const u32x4 kq = *(const u32x4 *)(kc + src), vq = *(const u32x4 *)(vc + src);
+      const u16 *kk = (const u16 *)&kq, *vv = (const u16 *)&vq;
+      u32x4 ko;
+      u16 *ko16 = (u16 *)&ko;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ko16[i] = cvt(kk[i]);
+        vals[i] = cvt(vv[i]);
+      }
+      const int64_t dst = ((int64_t)b * kv_rows + j) * kvd + hk * hd + e0;
+      *(u32x4 *)(kh + dst) = ko;
+      if (kl) *(u32x4 *)(kl + dst) = u32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) vals[i] = 0;   // +0 in bf16 and fp16
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vt[i][jj] = vals[i];
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t o = (((int64_t)b * n_kv + hk) * hd + e0 + i) * vt_stride + j0;
+    if (j0 + 8 <= p0) {
+      *(u32x4 *)(vth + o) = *(const u32x4 *)vt[i];
+      if (vtl) *(u32x4 *)(vtl + o) = u32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        if (j < p0 || (j >= p0 + seq && j < pad_end)) {
+          vth[o + jj] = vt[i][jj];
+          if (vtl) vtl[o + jj] = 0;
+        }
+      }
+    }
+  }
+}
+
+hipError_t kv_prefix_launch(const uint16_t *kcache, const uint16_t *vcache, const int32_t *start_pos, int batch,
+                            int n_kv, int head_dim, int max_seq, int seq, uint16_t *kh, uint16_t *kl, uint16_t *vth,
+                            uint16_t *vtl, int kv_rows, int vt_stride, int f16, hipStream_t s) {
+  if (batch == 0 || seq == 0) return hipSuccess;
+  if (head_dim % 8 || kv_rows < max_seq || vt_stride < kv_rows || vt_stride % 8) return hipErrorInvalidValue;
+  if (f16 && (kl || vtl)) return hipErrorInvalidValue;
+  const int64_t n = (int64_t)batch * n_kv * ((max_seq + 7) / 8) * (head_dim / 8);
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (f16)
+    hipLaunchKernelGGL(kv_prefix_kernel<true>, grid, dim3(256), 0, s, kcache, vcache, start_pos, batch, n_kv, head_dim,
+                       max_seq, seq, kh, kl, vth, vtl, kv_rows, vt_stride);
+  else
+    hipLaunchKernelGGL(kv_prefix_kernel<false>, grid, dim3(256), 0, s, kcache, vcache, start_pos, batch, n_kv,
+                       head_dim, max_seq, seq, kh, kl, vth, vtl, kv_rows, vt_stride);
+  return hipGetLastError();
+}
+
 template <int HD, bool QKPAIR, bool VPAIR, bool F16 = false>
 static hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
   const int nqt = (a.seq + 127) / 128;
@@ -351,7 +438,9 @@ static hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, int f16, hipStream_t s) {
   if (f16 && (qk_pair || v_pair)) return hipErrorInvalidValue;
   if (a.batch * a.seq == 0) return hipSuccess;
-  if (a.seq % 32) {
+  if (a.start_pos && (a.kv_rows < a.seq || a.max_seq > a.kv_rows || a.vt_stride < a.kv_rows))
+    return hipErrorInvalidValue;
+  if (a.seq % 32 && !a.start_pos) {   // with start_pos the prefix copy zeroes the pad
     const int64_t rows = (int64_t)a.batch * (a.n_kv_heads > 0 ? a.n_kv_heads : a.n_heads) * a.head_dim;
     const int64_t n = rows * (a.vt_stride - a.seq);
     // all-zero bits are +0 in bf16 and in fp16

@@ -55,19 +55,34 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 }
 
 // ------------------------------------------------------------------ norm prep
-// One 64-lane wavefront per row, 8 consecutive channels per lane and step:
-// rstd = 1/sqrt(mean(x^2) + eps) (sum reduced across the wavefront) and the
-// GEMM operand x * g as bf16 hi (+ lo), or as IEEE fp16 (H). The product's
-// consumer multiplies its
-// fp32 accumulator by rstd, which completes RMSNorm(x; g) W^T. dim % 8 == 0.
-// g == nullptr: the operand is x itself (a block without a norm before the
-// projection; rstd is then written but not used).
-// U consecutive 512-channel chunks per step (dim a multiple of 512 * U when
-// U > 1): all their loads issue before any is used, and __restrict__ lets the
-// compiler move the next step's loads above this step's stores.
-template <bool IN_F32, bool PAIR, bool PARTS, int U, bool H = false>
+// One 64-lane wavefront per row, 8 consecutive channels per lane and 512-wide
+// chunk. It writes the GEMM operand x * g (bf16, a bf16 hi/lo pair, or IEEE
+// fp16 by OUT) and the row multiplier rmul that the consumer applies to its
+// fp32 accumulator; x * g times rmul is RMSNorm(x; g) (RMSNorm with gain, as
+// in the chenyuan1125.github.io page's equation), so the product
+// (x * g) W^T * rmul completes RMSNorm(x; g) W^T. With g == nullptr the
+// operand is x itself (a block without a norm before the projection) and
+// rmul only undoes the operand's scale below.
+//
+// RMSNorm puts every row on the same scale ("RMSNorm: LayerNorm minus the
+// mean" on the paperfordummies.in page), so the operand must not depend on
+// the row's own scale. fp16 holds magnitudes from 2^-14 to 65504 only: the
+// fp16 operand is x * g * 2^k with 2^k the largest power of two at most
+// 4 rstd, which puts the row's RMS in (2, 4] and every element below
+// 4 sqrt(dim) |g|, and rmul = rstd * 2^-k. Scaling by 2^k is exact, so inside
+// fp16's range the products and the accumulator are exactly 2^k times those
+// of the unscaled operand and the result bits do not change. bf16 and bf16
+// pairs have fp32's range and stay unscaled (rmul = rstd). The statistics are
+// fp32: a row whose sum of squares overflows fp32 is out of range.
+//
+// NC > 0: the row stays in registers between the statistics and the operand
+// (NC chunks per lane, dim <= 512 NC; every load issues before the first
+// use); NC == 0: two passes over memory.
+// PARTS: the row is h = x + part[0] + ... (split-K partial products, added in
+// split order), written to h_out in fp32.
+template <bool IN_F32, int OUT, bool PARTS, int NC>
 __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__ x, const u16 *__restrict__ g,
-                                                        int64_t rows, int dim, float eps, float *__restrict__ rstd,
+                                                        int64_t rows, int dim, float eps, float *__restrict__ rmul,
                                                         u16 *__restrict__ xg_hi, u16 *__restrict__ xg_lo,
                                                         const float *__restrict__ part, int n_parts,
                                                         float *__restrict__ h_out) {
@@ -76,70 +91,124 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__
   if (row >= rows) return;
   const int64_t base = row * dim;
   const int64_t pstride = rows * dim;
-  float ss = 0.f;
-  for (int c0 = 8 * lane; c0 < dim; c0 += 512 * U) {
-    float f[U][8], gf[U][8];
+  // channels c .. c+7 of the row (c is a multiple of 8 below dim)
+  auto load = [&](int c, float *f) {
+    if (IN_F32) {
+      const f32x4 a0 = *(const f32x4 *)((const float *)x + base + c);
+      const f32x4 a1 = *(const f32x4 *)((const float *)x + base + c + 4);
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 512 * u;
-      if (IN_F32) {
-        const f32x4 a0 = *(const f32x4 *)((const float *)x + base + c);
-        const f32x4 a1 = *(const f32x4 *)((const float *)x + base + c + 4);
+      for (int i = 0; i < 4; ++i) {
+        f[i] = a0[i];
+        f[4 + i] = a1[i];
+      }
+    } else {
+      unpack8(*(const u32x4 *)((const u16 *)x + base + c), f);
+    }
+    if (PARTS) {
+      for (int z = 0; z < n_parts; ++z) {
+        const float *pp = part + z * pstride + base + c;
+        const f32x4 p0 = *(const f32x4 *)pp, p1 = *(const f32x4 *)(pp + 4);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f[u][i] = a0[i];
-          f[u][4 + i] = a1[i];
+          f[i] += p0[i];
+          f[4 + i] += p1[i];
         }
-      } else {
-        unpack8(*(const u32x4 *)((const u16 *)x + base + c), f[u]);
-      }
-      if (PARTS) {
-        // h = x + the split-K partial products, added in split order
-        for (int z = 0; z < n_parts; ++z) {
-          const float *pp = part + z * pstride + base + c;
-          const f32x4 p0 = *(const f32x4 *)pp, p1 = *(const f32x4 *)(pp + 4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            f[u][i] += p0[i];
-            f[u][4 + i] += p1[i];
-          }
-        }
-      }
-      if (g) {
-        unpack8(*(const u32x4 *)(g + c), gf[u]);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) gf[u][i] = 1.0f;
       }
     }
+  };
+  auto put_h = [&](int c, const float *f) {
+    *(f32x4 *)(h_out + base + c) = f32x4{f[0], f[1], f[2], f[3]};
+    *(f32x4 *)(h_out + base + c + 4) = f32x4{f[4], f[5], f[6], f[7]};
+  };
+  auto put_operand = [&](int c, const float *f, float scale) {
+    float v[8], gf[8];
+    if (g) {
+      unpack8(*(const u32x4 *)(g + c), gf);
+    } else {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = c0 + 512 * u;
-      if (PARTS) {
-        *(f32x4 *)(h_out + base + c) = f32x4{f[u][0], f[u][1], f[u][2], f[u][3]};
-        *(f32x4 *)(h_out + base + c + 4) = f32x4{f[u][4], f[u][5], f[u][6], f[u][7]};
-      }
+      for (int i = 0; i < 8; ++i) gf[i] = 1.0f;
+    }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ss += f[u][i] * f[u][i];
-        f[u][i] *= gf[u][i];
-      }
-      if (PAIR) {
-        u32x4 hi, lo;
-        pack8_pair(f[u], hi, lo);
-        *(u32x4 *)(xg_hi + base + c) = hi;
-        *(u32x4 *)(xg_lo + base + c) = lo;
+    for (int i = 0; i < 8; ++i) v[i] = f[i] * gf[i] * scale;
+    if (OUT == 1) {
+      u32x4 hi, lo;
+      pack8_pair(v, hi, lo);
+      *(u32x4 *)(xg_hi + base + c) = hi;
+      *(u32x4 *)(xg_lo + base + c) = lo;
+    } else {
+      *(u32x4 *)(xg_hi + base + c) = OUT == 2 ? pack8h(v) : pack8(v);
+    }
+  };
+  // operand scale 2^k and row multiplier from the statistics
+  auto scales = [&](float ss, float &scale, float &mul) {
+    const float r = rstd_of(ss, dim, eps);
+    const float keep = g ? r : 1.0f;   // no norm: the multiplier only undoes the scale
+    scale = 1.0f;
+    mul = keep;
+    const int e = (int)((__float_as_uint(r) >> 23) & 0xff);
+    if (OUT == 2 && e != 0 && e != 0xff) {   // finite nonzero rstd; otherwise unscaled (0 * inf stays NaN)
+      const int k = min(max(e - 127 + 2, -126), 126);
+      scale = __uint_as_float((uint32_t)(k + 127) << 23);
+      mul = keep * __uint_as_float((uint32_t)(127 - k) << 23);
+    }
+  };
+
+  float ss = 0.f, scale, mul;
+  if (NC > 0) {
+    float f[NC > 0 ? NC : 1][8];
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int c = 8 * lane + 512 * u;
+      const bool in = c < dim;     // chunks past dim (and the tail of a dim not a multiple of 512)
+      float t[8];
+      load(in ? c : dim - 8, t);   // every load issues before the first use
+#pragma unroll
+      for (int i = 0; i < 8; ++i) f[u][i] = in ? t[i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int c = 8 * lane + 512 * u;
+      if (PARTS && c < dim) put_h(c, f[u]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += f[u][i] * f[u][i];
+    }
+    ss = wave_sum(ss);
+    scales(ss, scale, mul);
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      const int c = 8 * lane + 512 * u;
+      if (c < dim) put_operand(c, f[u], scale);
+    }
+  } else {
+    for (int c = 8 * lane; c < dim; c += 512) {
+      float f[8];
+      load(c, f);
+      if (PARTS) put_h(c, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ss += f[i] * f[i];
+    }
+    ss = wave_sum(ss);
+    scales(ss, scale, mul);
+    for (int c = 8 * lane; c < dim; c += 512) {
+      float f[8];
+      if (PARTS) {   // h as this lane wrote it
+        const f32x4 a0 = *(const f32x4 *)(h_out + base + c), a1 = *(const f32x4 *)(h_out + base + c + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f[i] = a0[i];
+          f[4 + i] = a1[i];
+        }
       } else {
-        *(u32x4 *)(xg_hi + base + c) = H ? pack8h(f[u]) : pack8(f[u]);   // H: IEEE fp16 operand
+        load(c, f);
       }
+      put_operand(c, f, scale);
     }
   }
-  ss = wave_sum(ss);
-  if (lane == 0) rstd[row] = rstd_of(ss, dim, eps);
+  if (lane == 0) rmul[row] = mul;
 }
 
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
-                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s, const float *part,
+                            float *rmul, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s, const float *part,
                             int n_parts, float *h_out, int out_f16) {
   if (rows == 0) return hipSuccess;
   if (dim % 8) return hipErrorInvalidValue;
@@ -147,41 +216,44 @@ hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_
   if (parts && h_out == nullptr) return hipErrorInvalidValue;
   if (out_f16 && xg_lo) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + 3) / 4));
-  const int u = dim % 2048 == 0 ? 4 : (dim % 1024 == 0 ? 2 : 1);
-  if (out_f16) {
-#define NPH_CASE(F, R, U_)                                                                                      \
-  if (!!in_f32 == F && parts == R && u == U_) {                                                                 \
-    hipLaunchKernelGGL((norm_prep_kernel<F, false, R, U_, true>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, \
-                       xg_hi, xg_lo, part, n_parts, h_out);                                                     \
+  const int out = out_f16 ? 2 : (xg_lo ? 1 : 0);
+  const int nc = dim <= 2048 ? 4 : (dim <= 4096 ? 8 : (dim <= 8192 ? 16 : 0));
+#define NP_CASE(F, O_, R, NC_)                                                                                    \
+  if (!!in_f32 == F && out == O_ && parts == R && nc == NC_) {                                                   \
+    hipLaunchKernelGGL((norm_prep_kernel<F, O_, R, NC_>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rmul, xg_hi, \
+                       xg_lo, part, n_parts, h_out);                                                              \
     return hipGetLastError();                                                                                   \
   }
-    NPH_CASE(true, false, 4) NPH_CASE(true, true, 4) NPH_CASE(false, false, 4) NPH_CASE(false, true, 4)
-    NPH_CASE(true, false, 2) NPH_CASE(true, true, 2) NPH_CASE(false, false, 2) NPH_CASE(false, true, 2)
-    NPH_CASE(true, false, 1) NPH_CASE(true, true, 1) NPH_CASE(false, false, 1) NPH_CASE(false, true, 1)
-#undef NPH_CASE
-    return hipErrorInvalidValue;
-  }
-#define NP_CASE(F, P, R, U_)                                                                                     \
-  if (!!in_f32 == F && (xg_lo != nullptr) == P && parts == R && u == U_) {                                      \
-    hipLaunchKernelGGL((norm_prep_kernel<F, P, R, U_>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rstd, xg_hi, \
-                       xg_lo, part, n_parts, h_out);                                                             \
-    return hipGetLastError();                                                                                  \
-  }
-#define NP_CASES(U_)              \
-  NP_CASE(true, true, false, U_)  \
-  NP_CASE(true, false, false, U_) \
-  NP_CASE(false, true, false, U_) \
-  NP_CASE(false, false, false, U_) \
-  NP_CASE(true, true, true, U_)   \
-  NP_CASE(true, false, true, U_)  \
-  NP_CASE(false, true, true, U_)  \
-  NP_CASE(false, false, true, U_)
+#define NP_CASES(NC_)                                                                                   \
+  NP_CASE(true, 0, false, NC_) NP_CASE(true, 1, false, NC_) NP_CASE(true, 2, false, NC_)                \
+  NP_CASE(false, 0, false, NC_) NP_CASE(false, 1, false, NC_) NP_CASE(false, 2, false, NC_)             \
+  NP_CASE(true, 0, true, NC_) NP_CASE(true, 1, true, NC_) NP_CASE(true, 2, true, NC_)                   \
+  NP_CASE(false, 0, true, NC_) NP_CASE(false, 1, true, NC_) NP_CASE(false, 2, true, NC_)
   NP_CASES(4)
-  NP_CASES(2)
-  NP_CASES(1)
+  NP_CASES(8)
+  NP_CASES(16)
+  NP_CASES(0)
 #undef NP_CASES
 #undef NP_CASE
   return hipErrorInvalidValue;
+}
+
+// NaN logits rows of the sequences whose prefill chunk does not fit the cache.
+__global__ void nan_unplaced_rows_kernel(const int32_t *start_pos, int seq, int max_seq, float *logits,
+                                         int64_t per_seq) {
+  const int b = blockIdx.y;
+  if (chunk_start(start_pos, b, seq, max_seq) >= 0) return;
+  float *row = logits + (int64_t)b * per_seq;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < per_seq; i += (int64_t)gridDim.x * blockDim.x)
+    row[i] = __builtin_nanf("");
+}
+
+hipError_t nan_unplaced_rows_launch(const int32_t *start_pos, int batch, int seq, int max_seq, float *logits,
+                                    int vocab, hipStream_t s) {
+  if (batch == 0 || seq == 0 || !start_pos) return hipSuccess;
+  hipLaunchKernelGGL(nan_unplaced_rows_kernel, dim3(64, batch), dim3(256), 0, s, start_pos, seq, max_seq, logits,
+                     (int64_t)seq * vocab);
+  return hipGetLastError();
 }
 
 // y = r + part[0] + ... + part[n_parts-1] (fp32, split order), 4 floats per thread.

@@ -311,7 +311,9 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
       for (int i = 0; i < G::TM; ++i) {
         const int mb = m0 + wm * G::WM + i * 32;  // first row of the tile
         const int bq = mb / a.seq, s0 = mb - bq * a.seq;
-        const bool fast = mb + 32 <= a.M && s0 + 32 <= a.seq && (s0 & 7) == 0;
+        const int cs0 = mb < a.M ? chunk_start(a.start_pos, bq, a.seq, a.max_seq) : 0;
+        const int p0 = max(cs0, 0);              // position of the sequence's first row
+        const bool fast = mb + 32 <= a.M && s0 + 32 <= a.seq && ((p0 + s0) & 7) == 0;
         float sc[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -346,7 +348,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
             const int ce = lane >> 1, half = lane & 1;
             const int cd = cd0 + ce;
             const int hh = cd >> hd_shift, e = cd & (a.head_dim - 1);
-            const int64_t o = (((int64_t)bq * n_kv + hh) * a.head_dim + e) * a.vt_stride + s0 + 16 * half;
+            const int64_t o = (((int64_t)bq * n_kv + hh) * a.head_dim + e) * a.vt_stride + p0 + s0 + 16 * half;
             const u32x4 *srch = (const u32x4 *)(tr + ce * TS + 16 * half);
             const u32x4 *srcl = (const u32x4 *)(tr + 32 * TS + ce * TS + 16 * half);
             const u32x4 h0 = srch[0], h1 = srch[1], q0 = srcl[0], q1 = srcl[1];
@@ -378,6 +380,8 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
               const int cd = cd0 + l32;
               const int hh = cd >> hd_shift, e = cd & (a.head_dim - 1);
               const float x = acc[i][j][r] * sc[r];
+              const int cs = b == bq ? cs0 : chunk_start(a.start_pos, b, a.seq, a.max_seq);
+              s += max(cs, 0);   // the row's position
               if (!fast) {
                 const int64_t o = (((int64_t)b * n_kv + hh) * a.head_dim + e) * a.vt_stride + s;
                 if (a.attn_f16) {
@@ -389,7 +393,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
                   a.vtl[o] = lo;
                 }
               }
-              if (a.vcache) a.vcache[(((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e] = f2bf(x);
+              if (a.vcache && cs >= 0) a.vcache[(((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e] = f2bf(x);
             }
           }
         }
@@ -410,9 +414,13 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
     for (int i = 0; i < G::TM; ++i) {
       const int row = m0 + wm * G::WM + i * 32 + rr;
       const bool ok = row < a.M;
-      const int b = ok ? row / a.seq : 0, s = ok ? row - b * a.seq : 0;
+      const int b = ok ? row / a.seq : 0;
+      const int cs = ok ? chunk_start(a.start_pos, b, a.seq, a.max_seq) : 0;
+      const int s = ok ? row - b * a.seq + max(cs, 0) : 0;   // the row's position
       const float sc = (a.rstd && ok) ? a.rstd[row] : 1.0f;
       const float2 *tab = a.rope_tab + (int64_t)s * (a.head_dim >> 1);
+      // k row: by position within the sequence's kv_rows when continuing a prefix
+      const int64_t krow = a.start_pos ? (int64_t)b * a.kv_rows + s : row;
 #pragma unroll
       for (int j = 0; j < G::TN; ++j) {
 #pragma unroll
@@ -446,7 +454,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
           }
         }
         u32x4 hi0, lo0, hi1, lo1;
-        const int64_t o = (int64_t)row * (seg == 0 ? a.dim : kvd) + cd;
+        const int64_t o = seg == 0 ? (int64_t)row * a.dim + cd : krow * kvd + cd;
         if (a.attn_f16) {
           *(u32x4 *)(dh + o) = pack8h(rot);
           *(u32x4 *)(dh + o + 8) = pack8h(rot + 8);
@@ -460,7 +468,7 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
           *(u32x4 *)(dl + o) = lo0;
           *(u32x4 *)(dl + o + 8) = lo1;
         }
-        if (seg == 1 && a.kcache) {
+        if (seg == 1 && a.kcache && cs >= 0) {
           const int hh = cd >> hd_shift;
           u16 *kp = a.kcache + (((int64_t)b * n_kv + hh) * a.max_seq + s) * a.head_dim + e0;
           *(u32x4 *)kp = hi0;

@@ -46,7 +46,23 @@ struct GemmArgs {
   int vt_stride;                 // row stride of the transposed v (>= seq, multiple of 64)
   uint16_t *kcache, *vcache;     // optional bf16: [batch, n_kv_heads, max_seq, head_dim] of this layer
   int max_seq;
+  // Prefill that continues a cached prefix: sequence b's rows take positions
+  // start_pos[b] + s (RoPE angle, cache slot), and k and v^T are stored by
+  // position, k at row b * kv_rows + position. nullptr: positions 0..seq-1,
+  // k at the token's own row. A sequence whose chunk does not fit the cache
+  // (chunk_start < 0) is computed as if it started at 0 and writes no cache.
+  const int32_t *start_pos;
+  int kv_rows;                   // rows per sequence of k (0: seq)
 };
+
+// Position of the first token of sequence b's chunk of `seq` tokens:
+// start_pos[b] when 0 <= start_pos[b] and start_pos[b] + seq <= max_seq, -1
+// otherwise; 0 without start_pos.
+__host__ __device__ inline int chunk_start(const int32_t *start_pos, int b, int seq, int max_seq) {
+  if (!start_pos) return 0;
+  const int p = start_pos[b];
+  return (p >= 0 && p <= max_seq - seq) ? p : -1;
+}
 
 // Row n of the BMODE_CONCAT3 operand [B0 (n_q rows); B1 (n_kv rows); B2 (n_kv rows)]:
 // the query, key and value projections stacked (fewer key/value rows under
@@ -80,26 +96,48 @@ struct AttnArgs {
   int o_f16;                           // output as IEEE fp16 (no lo part)
   int batch, seq, n_heads, head_dim, dim;
   int kv_dim, n_kv_heads;              // k rows [batch*seq, kv_dim]; v^T [batch, n_kv_heads, head_dim, vt_stride]
-  int vt_stride;                       // row stride of v^T (>= seq, multiple of 64)
+  int vt_stride;                       // row stride of v^T (>= keys per sequence, multiple of 64)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
+  // With start_pos, sequence b's queries are positions p0 .. p0+seq-1
+  // (p0 = chunk_start(start_pos, b, seq, max_seq), 0 when negative) and its
+  // keys are positions 0 .. p0+seq-1: k rows b * kv_rows + position, v^T
+  // columns by position; query s sees keys up to p0 + s.
+  const int32_t *start_pos;
+  int kv_rows;                         // rows per sequence of k (0: seq)
+  int max_seq;
 };
 // f16: q, k, v^T hold IEEE fp16 (single, no lo parts) and the probabilities
 // are rounded to fp16; otherwise bf16 with optional hi/lo pairs.
 hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, int f16, hipStream_t s);
+// The cached prefix of a prefill chunk in the attention's operand layout: for
+// every sequence b with p0 = chunk_start(...) > 0, cache positions 0..p0-1 of
+// this layer (bf16 [batch, n_kv, max_seq, hd]) go to k rows b * kv_rows + j
+// and to v^T columns j (IEEE fp16 when f16, else bf16 with zero lo parts when
+// kl / vtl are given); v^T columns p0+seq .. up to the next multiple of 32 are
+// zeroed (the attention's last key tile multiplies them by zero weights).
+hipError_t kv_prefix_launch(const uint16_t *kcache, const uint16_t *vcache, const int32_t *start_pos, int batch,
+                            int n_kv, int head_dim, int max_seq, int seq, uint16_t *kh, uint16_t *kl, uint16_t *vth,
+                            uint16_t *vtl, int kv_rows, int vt_stride, int f16, hipStream_t s);
+// logits rows [b*seq, (b+1)*seq) set to NaN for every sequence whose chunk
+// does not fit the cache (chunk_start < 0).
+hipError_t nan_unplaced_rows_launch(const int32_t *start_pos, int batch, int seq, int max_seq, float *logits,
+                                    int vocab, hipStream_t s);
 
 // ---------------------------------------------------------------- small kernels
 hipError_t rope_table_launch(float2 *tab, int positions, int head_dim, float theta, hipStream_t s);
 hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int head_dim, float theta,
                                  int max_seq, hipStream_t s);
-// Norm prep (one wavefront per row): rstd[r] = 1/sqrt(mean(x[r]^2) + eps) and the
-// product x[r] * g as bf16 (hi, and lo when xg_lo is non-null); g == nullptr
-// gives x[r] itself.
+// Norm prep (one wavefront per row): the GEMM operand x[r] * g (bf16 hi, and
+// lo when xg_lo is non-null; IEEE fp16 with out_f16, carrying an exact
+// power-of-two row scale that keeps it inside fp16's range) and rmul[r], the
+// multiplier the consumer applies to its fp32 accumulator: rstd[r] =
+// 1/sqrt(mean(x[r]^2) + eps) times the inverse of that scale. g == nullptr
+// gives x[r] itself (no norm: rmul only undoes the scale).
 // With `part` (n_parts fp32 [rows, dim] split-K partial products), the row is
 // first h = x + part[0] + ... (split order), written to h_out (fp32), and the
 // statistics and product are those of h.
-// out_f16: the product as IEEE fp16 (single; xg_lo must be null).
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
-                            float *rstd, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s,
+                            float *rmul, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s,
                             const float *part = nullptr, int n_parts = 0, float *h_out = nullptr,
                             int out_f16 = 0);
 // Index of the largest logit per row (lowest among equals; -1 if the row has a NaN).

@@ -32,6 +32,15 @@ def _dev(*ts):
             raise ValueError("tensors must be contiguous")
 
 
+def _need(t: torch.Tensor, name: str, shape, dtype) -> None:
+    """Shape and dtype check before any launch: a wrong size would make the
+    kernels read or write outside the tensor, a wrong dtype reinterpret it."""
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _p(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -169,8 +178,13 @@ class Block:
         self.y = torch.empty((batch * seq, cfg.dim), dtype=torch.float32, device=dev)
 
     def __call__(self, x: torch.Tensor, y: Optional[torch.Tensor] = None) -> torch.Tensor:
-        _dev(x)
         y = self.y if y is None else y
+        _dev(x, y)
+        n, dim = self.batch * self.seq, self.cfg.dim
+        if x.dtype not in (torch.float32, _TORCH[self.cfg.dtype]):
+            raise TypeError(f"x must be float32 or {_TORCH[self.cfg.dtype]}, got {x.dtype}")
+        _need(x, "x", (n, dim), x.dtype)
+        _need(y, "y", (n, dim), torch.float32)
         L.check(L.load().llama_block_forward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _dt(x), _p(x),
                                              _p(y), self.batch, self.seq, _p(self.ws), self.ws.numel(), _stream()),
                 "llama_block_forward")
@@ -308,18 +322,37 @@ class Model:
         return self._ws[key]
 
     def new_cache(self, batch: int, device) -> torch.Tensor:
-        c = self.cfg
-        hd = c.dim // c.n_heads
-        kv = c.n_kv_heads or c.n_heads
-        return torch.zeros((c.n_layers, batch, kv, c.max_seq, hd), dtype=_TORCH[c.dtype], device=device)
+        return torch.zeros(self.cache_shape(batch), dtype=_TORCH[self.cfg.dtype], device=device)
 
-    def forward(self, tokens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor) -> torch.Tensor:
-        _dev(tokens, k_cache, v_cache)
+    def cache_shape(self, batch: int):
+        c = self.cfg
+        return (c.n_layers, batch, c.n_kv_heads or c.n_heads, c.max_seq, c.dim // c.n_heads)
+
+    def _check_caches(self, batch: int, k_cache: torch.Tensor, v_cache: torch.Tensor) -> None:
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            _need(t, name, self.cache_shape(batch), _TORCH[self.cfg.dtype])
+
+    def forward(self, tokens: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                start_pos: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Prefill tokens [B, T] (int32). start_pos (int32 [B]): the sequences
+        continue cached prefixes of those lengths (None: all start at 0)."""
+        _dev(tokens, k_cache, v_cache, start_pos, logits)
+        if tokens.dim() != 2:
+            raise ValueError("tokens must be [batch, seq]")
         B, T = tokens.shape
-        logits = torch.empty((B, T, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _need(tokens, "tokens", (B, T), torch.int32)
+        if T > self.cfg.max_seq:
+            raise ValueError(f"seq {T} exceeds max_seq {self.cfg.max_seq}")
+        if start_pos is not None:
+            _need(start_pos, "start_pos", (B,), torch.int32)
+        self._check_caches(B, k_cache, v_cache)
+        if logits is None:
+            logits = torch.empty((B, T, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _need(logits, "logits", (B, T, self.cfg.vocab), torch.float32)
         ws = self.workspace(L.OP_MODEL_FORWARD, B, T, tokens.device)
-        L.check(L.load().llama_model_forward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(tokens), B, T,
-                                             _p(k_cache), _p(v_cache), _p(logits), _p(ws), ws.numel(), _stream()),
+        L.check(L.load().llama_model_forward(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(tokens),
+                                             _p(start_pos), B, T, _p(k_cache), _p(v_cache), _p(logits), _p(ws),
+                                             ws.numel(), _stream()),
                 "llama_model_forward")
         return logits
 
@@ -349,10 +382,16 @@ class Model:
 
     def decode(self, tokens: torch.Tensor, pos: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                logits: Optional[torch.Tensor] = None) -> torch.Tensor:
-        _dev(tokens, pos, k_cache, v_cache)
+        _dev(tokens, pos, k_cache, v_cache, logits)
+        if tokens.dim() != 1:
+            raise ValueError("tokens must be [batch]")
         B = tokens.shape[0]
+        _need(tokens, "tokens", (B,), torch.int32)
+        _need(pos, "pos", (B,), torch.int32)
+        self._check_caches(B, k_cache, v_cache)
         if logits is None:
             logits = torch.empty((B, self.cfg.vocab), dtype=torch.float32, device=tokens.device)
+        _need(logits, "logits", (B, self.cfg.vocab), torch.float32)
         ws = self.workspace(L.OP_MODEL_DECODE, B, 1, tokens.device)
         L.check(L.load().llama_model_decode(ctypes.byref(self.cfg), ctypes.byref(self.wstruct), _p(tokens), _p(pos),
                                             B, _p(k_cache), _p(v_cache), _p(logits), _p(ws), ws.numel(), _stream()),

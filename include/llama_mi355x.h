@@ -230,18 +230,30 @@ int llama_block_forward(const llama_config *c, const llama_block_weights *w, int
                         const void *x, float *y, int batch, int seq, void *ws, size_t ws_bytes,
                         void *stream);
 
-/* Whole-model prefill from an empty cache: embedding rows of tokens
- * [batch, seq] (int32, device), n_layers blocks at positions 0..seq-1, final
- * RMSNorm and output head ([P1] "The one formula": one final RMSNorm, then the
- * output head). Each layer's rotated keys and values are written to cache
- * slots 0..seq-1. k_cache, v_cache: [n_layers][batch][n_heads][max_seq][head_dim]
+/* Whole-model prefill ([P1] "The one formula": embedding, the blocks, one
+ * final RMSNorm, then the output head) of tokens [batch, seq] (int32, device).
+ * start_pos (int32 [batch], device, or NULL for all zeros): sequence b's
+ * tokens take positions start_pos[b] .. start_pos[b]+seq-1 (their RoPE angles
+ * and cache slots), and each attends over cache slots 0 .. its own position:
+ * the cache keeps the keys and values of every earlier token ([P4] "GQA Was
+ * Not an Original LLaMA Feature"), so slots below start_pos[b] must hold the
+ * entries an earlier llama_model_forward or llama_model_decode wrote. That
+ * allows a prompt to be prefilled in chunks or extended after decoding. Each
+ * layer's rotated keys and values of the new tokens are written to their
+ * slots. k_cache, v_cache: [n_layers][batch][n_kv_heads][max_seq][head_dim]
  * in config dtype. logits [batch, seq, vocab] f32. The head's operand
  * RMSNorm(x; final_norm) is carried as the Q/K/V projection's operand is
  * (numerics bits QKV_A_F16 / QKV_A_PAIR).
- * bf16 configs only (LLAMA_ERR_UNSUPPORTED for f32). seq <= max_seq. */
+ * The host cannot see start_pos: a sequence with start_pos[b] < 0 or
+ * start_pos[b] + seq > max_seq gets NaN logits rows and no cache write; the
+ * other sequences are unaffected.
+ * bf16 configs only (LLAMA_ERR_UNSUPPORTED for f32). seq <= max_seq
+ * (LLAMA_ERR_POSITION otherwise).
+ * ws: llama_workspace_size(c, LLAMA_OP_MODEL_FORWARD, batch, seq), which
+ * holds keys for max_seq positions per sequence. */
 int llama_model_forward(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
-                        int batch, int seq, void *k_cache, void *v_cache, float *logits, void *ws,
-                        size_t ws_bytes, void *stream);
+                        const int32_t *start_pos, int batch, int seq, void *k_cache, void *v_cache,
+                        float *logits, void *ws, size_t ws_bytes, void *stream);
 
 /* One decode step ([P4] "GQA Was Not an Original LLaMA Feature": keys and
  * values of earlier tokens are cached; LLaMA-1 has one K/V head per query

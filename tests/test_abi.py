@@ -116,10 +116,14 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                                    1 << 40, None) == L.LLAMA_ERR_DTYPE
     layers = (L.BlockWeights * 32)(*([w] * 32))
     mw = L.ModelWeights(0x1000, ctypes.cast(layers, ctypes.POINTER(L.BlockWeights)), 0x1000, 0x1000)
-    assert lib.llama_model_forward(ctypes.byref(c), ctypes.byref(mw), FAKE, 1, 4096, FAKE, FAKE, FAKE, FAKE,
+    assert lib.llama_model_forward(ctypes.byref(c), ctypes.byref(mw), FAKE, None, 1, 4096, FAKE, FAKE, FAKE, FAKE,
                                    1 << 40, None) == L.LLAMA_ERR_POSITION
-    assert lib.llama_model_forward(ctypes.byref(cf), ctypes.byref(mw), FAKE, 1, 16, FAKE, FAKE, FAKE, FAKE,
+    assert lib.llama_model_forward(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 1, 4096, FAKE, FAKE, FAKE, FAKE,
+                                   1 << 40, None) == L.LLAMA_ERR_POSITION
+    assert lib.llama_model_forward(ctypes.byref(cf), ctypes.byref(mw), FAKE, None, 1, 16, FAKE, FAKE, FAKE, FAKE,
                                    1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+    assert lib.llama_model_forward(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 1, 16, FAKE, FAKE, FAKE, FAKE,
+                                   16, None) == L.LLAMA_ERR_WORKSPACE
     assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 33, FAKE, FAKE, FAKE, FAKE,
                                   1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
     assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, None, 4, FAKE, FAKE, FAKE, FAKE,

@@ -338,12 +338,64 @@ def test_block_7b_full(numerics):
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("wid,b", [(2, 3), (3, 1)])
-def test_block_13b_65b_sampled_sequence(wid, b):
-    y, want, w = run_block(wid, seq_slice=b)
-    err = rel_err(y, want)
-    print(f"block {w.name} (sequence {b}): max|d|/rms = {err:.3e}")
-    assert err < TOL_BF16
+@pytest.mark.parametrize("wid", [2, 3])
+def test_block_13b_65b_every_sequence(wid):
+    """13B (4 sequences) and 65B (2 sequences) blocks: one GPU call, every
+    sequence against its own oracle run (sequences are independent), the
+    statistic per sequence."""
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    x = I.block_input(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta)
+    y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
+    ops().Block(cfg, wt, w.batch, w.seq)(x, y)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all()
+    hw = {k: host(v) for k, v in wt.items()}
+    errs = []
+    for b in range(w.batch):
+        rows = slice(b * w.seq, (b + 1) * w.seq)
+        want = O.block_forward(host(x[rows]), hw, 1, w.seq, w.n_heads, w.eps, w.theta)
+        errs.append(rel_err(y[rows], want))
+    print(f"block {w.name}: max|d|/rms per sequence {['%.3e' % e for e in errs]}")
+    assert max(errs) < TOL_BF16
+
+
+# ---------------------------------------------------------------- range of the fp16 operands
+# RMSNorm puts every row on the same scale, so the block's branches must not
+# depend on the scale of x. Rows scaled by 2^16 would put x*g past fp16's
+# largest value (65504) and rows scaled by 2^-16 into its subnormals if the
+# operand were stored unscaled.
+ROW_SCALES = (2.0 ** 16, 2.0 ** -16, 1.0, 2.0 ** 8, 2.0 ** -12)
+
+
+@pytest.mark.parametrize("wid", [100, 104])
+@pytest.mark.parametrize("numerics", [L.NUM_DEFAULT, F16_OPERANDS])
+def test_block_row_scales(wid, numerics):
+    """Rows of x scaled by powers of two from 2^-16 to 2^16 (exact in bf16).
+    Each output row against its own RMS; and the branch sum y - x on the rows
+    whose fp32 residual still resolves it (scale <= 2^8) against the RMS of the
+    oracle's branch sum."""
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    sc = torch.tensor([ROW_SCALES[i % len(ROW_SCALES)] for i in range(w.tokens)], dtype=torch.float64)
+    x = (I.block_input(w, device="cuda").double() * sc.cuda()[:, None]).to(w.torch_dtype)
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
+                       numerics=numerics, n_kv_heads=w.n_kv_heads)
+    y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
+    ops().Block(cfg, wt, w.batch, w.seq)(x, y)
+    torch.cuda.synchronize()
+    xh = host(x)
+    want = O.block_forward(xh, {k: host(v) for k, v in wt.items()}, w.batch, w.seq, w.n_heads, w.eps, w.theta)
+    got = y.cpu().double().numpy()
+    assert np.all(np.isfinite(got))
+    row_err = float(np.max(np.max(np.abs(got - want), axis=1) / np.sqrt(np.mean(want ** 2, axis=1))))
+    small = (sc <= 2.0 ** 8).numpy()
+    dw = (want - xh)[small]
+    br_err = float(np.max(np.abs((got - xh)[small] - dw)) / np.sqrt(np.mean(dw ** 2)))
+    print(f"block {w.name} (numerics {numerics:#x}) rows scaled 2^-16..2^16: per-row {row_err:.3e}, "
+          f"branches {br_err:.3e}")
+    assert row_err < TOL_BF16 and br_err < TOL_BF16
 
 
 # ---------------------------------------------------------------- model prefill + decode
@@ -418,6 +470,32 @@ def test_model_prefill_then_decode(wid, numerics):
     print(f"{w.name}: prefill logits {e1:.3e}, decode logits {e2:.3e} ({e3:.3e} from the GPU's cache)")
     assert e1 < TOL_BF16 and e2 < TOL_BF16
     assert e3 < TOL_DECODE_STEP
+
+
+def test_model_residual_beyond_fp16_range():
+    """A two-layer model whose embedding rows (and so its residual stream)
+    reach 4e5, beyond fp16's 65504: prefill and decode logits against the
+    oracle on the same scaled table (scaling by 2^22 is exact in bf16)."""
+    w, m, layers, gl = small_model(101)
+    gl["tok_embeddings"].mul_(2.0 ** 22)
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    assert float(gl["tok_embeddings"][toks.long()].abs().max()) > 65504.0
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    logits = m.forward(toks[:, :T].contiguous(), kc, vc)
+    pos = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    dec = m.decode(toks[:, T].contiguous(), pos, kc, vc)
+    torch.cuda.synchronize()
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    caches = oracle_caches(w, B)
+    get = lambda l: (lw[l], caches[l][0], caches[l][1])
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    want = O.model_forward(toks[:, :T].cpu().numpy(), emb, get, w.n_layers, fn, out, w.n_heads, w.eps)
+    want_dec = O.model_decode(toks[:, T].cpu().numpy(), np.full(B, T), emb, get, w.n_layers, fn, out, w.n_heads,
+                              w.eps)
+    e1, e2 = rel_err(logits, want), rel_err(dec, want_dec)
+    print(f"{w.name} with embeddings x 2^22: prefill logits {e1:.3e}, decode logits {e2:.3e}")
+    assert e1 < TOL_BF16 and e2 < TOL_BF16
 
 
 @pytest.mark.parametrize("wid", [101, 105, 106])
@@ -536,6 +614,142 @@ def test_model_f16_weights_bitwise_equal(wid):
     print(f"{w.name}: fp16-weight prefill and decode bitwise equal")
 
 
+# ---------------------------------------------------------------- prefill continuing a cached prefix
+@pytest.mark.parametrize("wid", [101, 105, 106])
+def test_model_prefill_continues_cached_prefix(wid):
+    """start_pos: a first prefill of T1 tokens, then a second of T2 tokens
+    with start_pos[b] <= T1 per sequence (the sequence keeps its first
+    start_pos[b] tokens; later slots are overwritten). Each sequence's second
+    logits and its cache must match one oracle prefill of its whole history
+    toks1[b, :start_pos[b]] + toks2[b]."""
+    w, m, layers, gl = small_model(wid)
+    B = w.batch
+    T1, T2 = 16, w.seq - 16
+    toks1 = I.tokens(w, (B, T1), device="cuda")
+    toks2 = I.tokens(w, (B, T2), device="cuda", stream=1)
+    starts = [T1, T1 - 5, T1 - 16][:B]
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    m.forward(toks1, kc, vc)
+    logits = m.forward(toks2, kc, vc, start_pos=torch.tensor(starts, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    errs = []
+    for b in range(B):
+        hist = np.concatenate([toks1[b, :starts[b]].cpu().numpy(), toks2[b].cpu().numpy()])[None]
+        L_ = hist.shape[1]
+        caches = oracle_caches(w, 1)
+        want = O.model_forward(hist, emb, lambda l: (lw[l], caches[l][0], caches[l][1]), w.n_layers, fn, out,
+                               w.n_heads, w.eps)
+        errs.append(rel_err(logits[b], want[0, starts[b]:]))
+        for l in range(w.n_layers):
+            for got, ref in ((kc[l, b], caches[l][0][0]), (vc[l, b], caches[l][1][0])):
+                g = O.f64(got.cpu())
+                assert np.max(np.abs(g[:, :L_] - ref[:, :L_])) < 0.02 * np.abs(ref[:, :L_]).max()
+    print(f"{w.name}: prefill from start_pos {starts}: logits max|d|/rms {['%.3e' % e for e in errs]}")
+    assert max(errs) < TOL_BF16
+
+
+def test_model_start_pos_zero_equals_no_start_pos():
+    """start_pos all zero takes the prefix path (keys by position, the prefix
+    copy) with an empty prefix: logits and cache are bitwise those of the
+    plain prefill."""
+    w, m, layers, gl = small_model(105)
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    ref = m.forward(toks, kc, vc).clone()
+    kc2, vc2 = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    got = m.forward(toks, kc2, vc2, start_pos=torch.zeros(B, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.isfinite(ref).all()
+    assert torch.equal(ref, got) and torch.equal(kc, kc2) and torch.equal(vc, vc2)
+
+
+def test_model_start_pos_outside_cache_gives_nan_rows():
+    """A sequence whose chunk would run past max_seq (or starts below 0) gets
+    NaN logits and no cache write; the others are bitwise unaffected."""
+    w, m, layers, gl = small_model(101)
+    B, T = w.batch, 20
+    toks = I.tokens(w, (B, T), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    kc.normal_(generator=torch.Generator("cuda").manual_seed(5))
+    vc.normal_(generator=torch.Generator("cuda").manual_seed(6))
+    k0, v0 = kc.clone(), vc.clone()
+    ok = m.forward(toks, kc.clone(), vc.clone(), start_pos=torch.full((B,), 3, dtype=torch.int32, device="cuda"))
+    sp = torch.tensor([w.max_seq - T + 1, -1, 3][:B], dtype=torch.int32, device="cuda")
+    got = m.forward(toks, kc, vc, start_pos=sp)
+    torch.cuda.synchronize()
+    assert torch.isnan(got[0]).all() and torch.isnan(got[1]).all()
+    assert torch.equal(kc[:, :2], k0[:, :2]) and torch.equal(vc[:, :2], v0[:, :2])
+    assert torch.isfinite(got[2]).all() and torch.equal(got[2], ok[2])
+
+
+@pytest.mark.parametrize("wid", [101, 105])
+def test_decode_ragged_positions(wid):
+    """A decode step with a different position per sequence (the new token at
+    pos[b] overwrites slot pos[b]; attention covers slots 0..pos[b]) against
+    the oracle continuing from the GPU's own cache."""
+    w, m, layers, gl = small_model(wid)
+    B, T = w.batch, w.seq
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    m.forward(toks[:, :T].contiguous(), kc, vc)
+    pos = np.array([T - 3, T, T - 1][:B])
+    dec = m.decode(toks[:, T].contiguous(), torch.tensor(pos, dtype=torch.int32, device="cuda"), kc, vc)
+    torch.cuda.synchronize()
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    gc = [tuple(O.f64(c[l].cpu()).copy() for c in (kc, vc)) for l in range(w.n_layers)]
+    for kg, vg in gc:
+        for b in range(B):
+            kg[b, :, pos[b]:] = 0
+            vg[b, :, pos[b]:] = 0
+    want = O.model_decode(toks[:, T].cpu().numpy(), pos, emb, lambda l: (lw[l], *gc[l]), w.n_layers, fn, out,
+                          w.n_heads, w.eps)
+    e = rel_err(dec, want)
+    print(f"{w.name}: decode at positions {pos.tolist()}: max|d|/rms = {e:.3e}")
+    assert e < TOL_DECODE_STEP
+
+
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks dtypes and shapes before any launch: an int64
+    position array, a cache for another batch or max_seq, a wrong logits or
+    block output size, or too long a prompt raise instead of reaching the
+    kernels."""
+    w, m, layers, gl = small_model(101)
+    B, T = w.batch, 8
+    toks = I.tokens(w, (B, T), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    with pytest.raises(TypeError):
+        m.decode(toks[:, 0].contiguous(), torch.full((B,), 3, device="cuda", dtype=torch.int64), kc, vc)
+    with pytest.raises(TypeError):
+        m.forward(toks.long(), kc, vc)
+    with pytest.raises(ValueError):
+        m.forward(toks, m.new_cache(B - 1, "cuda"), m.new_cache(B - 1, "cuda"))
+    with pytest.raises(ValueError):
+        m.forward(toks, kc[:, :, :, : w.max_seq // 2].contiguous(), vc)
+    with pytest.raises(TypeError):
+        m.forward(toks, kc.float(), vc)
+    with pytest.raises(ValueError):
+        m.forward(toks, kc, vc, logits=torch.empty((B, T, w.vocab - 1), device="cuda"))
+    with pytest.raises(ValueError):
+        m.forward(I.tokens(w, (B, w.max_seq + 1), device="cuda"), kc, vc)
+    with pytest.raises(ValueError):
+        m.forward(toks, kc, vc, start_pos=torch.zeros(B + 1, dtype=torch.int32, device="cuda"))
+    bw = I.workload(100)
+    cfg = ops().config(bw.dim, bw.n_heads, bw.hidden, eps=bw.eps)
+    blk = ops().Block(cfg, I.block_weights(bw, device="cuda"), bw.batch, bw.seq)
+    x = I.block_input(bw, device="cuda")
+    with pytest.raises(ValueError):
+        blk(x[1:].contiguous())
+    with pytest.raises(ValueError):
+        blk(x, torch.empty((bw.tokens, bw.dim + 1), device="cuda"))
+    with pytest.raises(TypeError):
+        blk(x.half())
+    assert torch.all(kc == 0)   # nothing ran
+
+
 def test_decode_invalid_position_gives_nan_row():
     w, m, layers, gl = small_model()
     B = w.batch
@@ -552,17 +766,20 @@ def test_decode_invalid_position_gives_nan_row():
 @pytest.mark.parametrize("wid", [4, 5])
 def test_model_decode_7b_sampled_sequences(wid):
     """Full 7B-shape decode step (batch 32, cache of 2047 positions; 5: eight
-    key/value heads); the oracle recomputes two of the 32 sequences layer by
-    layer."""
+    key/value heads): every logit finite, and the oracle recomputes five of
+    the 32 sequences (first, last and three between) layer by layer."""
     from decoder_only_transformer_llama_amd.workloads import decode_workload
     from tests.oracle_runs import oracle_decode_rows
     wl = decode_workload(wid, "cuda")
     logits = wl.model.decode(wl.tokens, wl.pos, wl.k_cache, wl.v_cache)
     torch.cuda.synchronize()
-    rows = [0, 17]
+    assert torch.isfinite(logits).all()
+    rows = [0, 7, 15, 23, 31]
     want = oracle_decode_rows(wl, rows)
     err = rel_err(logits[rows], want)
-    print(f"{wl.w.name} decode logits (rows {rows}): max|d|/rms = {err:.3e}")
+    per_row = [rel_err(logits[r], want[i]) for i, r in enumerate(rows)]
+    print(f"{wl.w.name} decode logits (rows {rows}): max|d|/rms = {err:.3e}; per row "
+          f"{['%.3e' % e for e in per_row]}")
     del wl
     torch.cuda.empty_cache()
     assert err < TOL_BF16
