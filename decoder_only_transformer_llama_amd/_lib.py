@@ -36,7 +36,7 @@ EXPORTS = (
     "llama_workspace_size", "llama_status_string", "llama_last_error", "llama_trace_begin", "llama_trace_end",
     "llama_trace_label", "llama_argmax", "llama_decode_pack_size", "llama_pack_decode_weights",
     "llama_causal_attn_backward", "llama_block_train_saved_size", "llama_block_train_forward",
-    "llama_block_backward", "llama_axpby", "llama_convert_weights_f16",
+    "llama_block_backward", "llama_axpby", "llama_convert_weights_f16", "llama_model_decode_static",
 )
 
 
@@ -97,6 +97,7 @@ def load() -> ctypes.CDLL:
                                  i32, i32, vp, sz, vp],
         "llama_axpby": [vp, vp, vp, f32, f32, i64, vp],
         "llama_convert_weights_f16": [vp, vp, i64, vp],
+        "llama_model_decode_static": [cfgp, ctypes.POINTER(ModelWeights), vp, vp, i32, vp, vp, vp, vp],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -1,15 +1,24 @@
 // C-ABI entry points: host-side validation, workspace carving and the launch
 // sequence of each operation on the caller's stream. No allocation, no
 // synchronisation, no global mutable state except the per-thread text of the
-// last HIP error.
+// last HIP error and the per-device address of the static decode scratch
+// (looked up once per device, under a lock).
 #include <math.h>
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "internal.h"
+
+// Scratch of llama_model_decode_static: library-owned device memory, one copy
+// per GPU the library runs on, held until the process ends. In host code this
+// name is only a stand-in: the memory is reached through the address that
+// hipGetSymbolAddress returns on each device.
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 using namespace llama;
 
@@ -43,6 +52,31 @@ hipError_t traced(hipError_t e, hipStream_t s, const char *where) {
     hipError_t e_ = traced((expr), s, where);             \
     if (e_ != hipSuccess) return hip_fail(e_, where);     \
   } while (0)
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+std::mutex g_scratch_mu;
+constexpr int kMaxDevices = 64;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch_of_current_device(void **ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) {
+    g_last_error = "static scratch: device index out of range";
+    return LLAMA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return LLAMA_OK;
+}
 
 bool dtype_ok(int d) { return d == LLAMA_F32 || d == LLAMA_BF16; }
 size_t dsize(int d) { return d == LLAMA_F32 ? 4 : 2; }
@@ -1227,6 +1261,23 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   HIP_TRY(gemv(c->vocab, d, BMODE_PLAIN, w->output, nullptr, nullptr, sp), "output head");
   HIP_TRY(dec_head_combine_launch(da, dw.part, sp, dw.rstd, logits, s), "head combine");
   return LLAMA_OK;
+}
+
+int llama_model_decode_static(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                              const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits,
+                              void *stream) {
+  const int st = check_model_cfg(c, batch, 1);
+  if (st) return st;
+  const size_t need = ws_bytes_of(c, LLAMA_OP_MODEL_DECODE, batch, 1);
+  if (need > kStaticScratchBytes) {
+    g_last_error = "llama_model_decode_static: the step needs " + std::to_string(need) +
+                   " bytes of scratch; the library's static scratch holds " + std::to_string(kStaticScratchBytes);
+    return LLAMA_ERR_WORKSPACE;
+  }
+  void *ws = nullptr;
+  const int sst = static_scratch_of_current_device(&ws);
+  if (sst) return sst;
+  return llama_model_decode(c, w, tokens, pos, batch, k_cache, v_cache, logits, ws, kStaticScratchBytes, stream);
 }
 
 int llama_decode_pack_size(const llama_config *c, size_t *bytes) {

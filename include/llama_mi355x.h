@@ -17,7 +17,9 @@
  *  - Pointers named in the argument list are DEVICE pointers (memory the
  *    caller allocated on the current HIP device) unless marked "host".
  *    The library never allocates, frees or synchronises: scratch memory comes
- *    from a caller-provided workspace whose size llama_workspace_size reports.
+ *    from a caller-provided workspace whose size llama_workspace_size reports
+ *    (llama_model_decode_static instead uses a device array the library
+ *    owns).
  *  - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *    null stream). Buffers must stay valid until the stream passes the call.
  *  - Activations are [tokens, dim] row-major with token = b*seq + s. Head h
@@ -268,6 +270,24 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
 int llama_model_decode(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
                        const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits,
                        void *ws, size_t ws_bytes, void *stream);
+
+/* llama_model_decode without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation). Its scratch is a device array owned by
+ * the library, LLAMA_DECODE_STATIC_SCRATCH_BYTES (64 MiB) on each GPU it runs
+ * on, held until the process ends; the call itself allocates nothing.
+ * Arguments, layouts, results and errors are those of llama_model_decode; a
+ * step that needs more scratch than the array holds (llama_workspace_size
+ * reports the need; 38 MiB for the LLaMA-7B shape at batch 32) returns
+ * LLAMA_ERR_WORKSPACE before any launch, with the sizes in llama_last_error.
+ * Every call on one GPU uses that GPU's array: calls that overlap on one GPU
+ * (streams not ordered against each other, or several host threads) race.
+ * The step writes every scratch word before reading it, so nothing carries
+ * over from an earlier call. */
+#define LLAMA_DECODE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int llama_model_decode_static(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                              const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits,
+                              void *stream);
 
 /* Greedy token choice over logits [rows, vocab] f32 (device): out[r] (int32,
  * device) is the index of the largest logit of row r, the lowest index among
