@@ -4,7 +4,7 @@
 // One workgroup = 8 wavefronts (2 x 4, two per SIMD so one wavefront's LDS and
 // barrier waits overlap the other's matrix-core work) computing a 256 x BN tile
 // with v_mfma_f32_32x32x16_{bf16,f16} (each wavefront 128 x BN/4). A and B move
-// HBM -> LDS with global_load_lds_dwordx4 (no register staging): every
+// HBM -> LDS with buffer_load_dwordx4 ... lds (no register staging): every
 // wavefront instruction drops 64 lanes x 16 bytes into one contiguous 1 KB
 // block of LDS, and the row/chunk each lane fetches is chosen so the block
 // lands already XOR-swizzled. K is consumed in steps of 64 (32 when A is a
@@ -91,6 +91,14 @@ struct GemmCfg {
 template <int CH>
 DEV int swz(int row) { return CH == 4 ? (row >> 2) & 3 : (row >> 1) & 7; }
 
+// 16 bytes per lane from base + voff + soff (bytes) into LDS at lds + 16 * lane:
+// buffer_load_dwordx4 ... lds (the LDS address comes from M0, the lane slot
+// from the lane index). Offsets are 32-bit: callers keep them below one tile.
+DEV void buf_load_lds16(const void *base, uint32_t voff, uint32_t soff, void *lds) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 16, voff, soff, 0, 0);
+}
+
 // Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices).
 template <int I, int N, class F>
 DEV void static_for(F &&f) {
@@ -145,57 +153,73 @@ __global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmAr
   const int tm = first + r_in % gm, tn = r_in / gm;
   const int m0 = tm * BM, n0 = a.n_base + tn * BN;
 
-  // ---- global source of each lane's 16-byte piece, fixed over K
-  // A block q of this wavefront covers tile rows RPL * (wave * A_LD + q) + lane / CH.
-  const u16 *asrc[G::A_LD], *alsrc[APAIR ? G::A_LD : 1];
+  // ---- global source of each lane's 16-byte piece, fixed over K. Load q of
+  // this wavefront covers 8 consecutive tile rows, RPL * (wave * LD + q) +
+  // lane / CH; its base address is that load's first row (uniform, so it
+  // stays in scalar registers), and each lane adds a byte offset of its own
+  // below 8 rows. Rows past the matrix load a valid row (never stored).
+  int64_t afirst[G::A_LD];   // element offset of the load's first row (in A and A_lo alike)
+  uint32_t aoff[G::A_LD];
 #pragma unroll
   for (int q = 0; q < G::A_LD; ++q) {
-    const int r = G::RPL * (wave * G::A_LD + q) + lane / G::CH;
+    const int r0 = G::RPL * (wave * G::A_LD + q), r = r0 + lane / G::CH;
     const int c = (lane % G::CH) ^ swz<G::CH>(r);
-    const int row = min(m0 + r, a.M - 1);  // rows past M load a valid row; never stored
-    asrc[q] = (const u16 *)a.A + (int64_t)row * a.lda + 8 * c;
-    if (APAIR) alsrc[q] = a.A_lo + (int64_t)row * a.lda + 8 * c;
+    const int first = min(m0 + r0, a.M - 1), row = min(m0 + r, a.M - 1);
+    afirst[q] = (int64_t)first * a.lda;
+    aoff[q] = (uint32_t)(((row - first) * a.lda + 8 * c) * 2);
   }
-  const u16 *bsrc[G::B_LD];
+  const u16 *bbase[G::B_LD];
+  uint32_t boff[G::B_LD];
 #pragma unroll
   for (int q = 0; q < G::B_LD; ++q) {
-    const int r = G::RPL * (wave * G::B_LD + q) + lane / G::CH;
+    const int r0 = G::RPL * (wave * G::B_LD + q), r = r0 + lane / G::CH;
     const int c = (lane % G::CH) ^ swz<G::CH>(r);
-    const u16 *ptr;
-    if (a.b_mode == BMODE_GATEUP) {
-      const int blk = r >> 5;
-      const int row = (n0 >> 1) + (blk >> 1) * 32 + (r & 31);
-      ptr = ((blk & 1) ? a.B1 : a.B0) + (int64_t)row * a.K;
-    } else if (a.b_mode == BMODE_CONCAT3) {
-      ptr = concat3_row(a.B0, a.B1, a.B2, a.n_seg, a.n_seg_kv > 0 ? a.n_seg_kv : a.n_seg, min(n0 + r, a.N - 1),
-                        a.K);
-    } else {
-      ptr = a.B0 + (int64_t)min(n0 + r, a.N - 1) * a.K;
-    }
-    bsrc[q] = ptr + 8 * c;
+    // matrix and row index in it of tile row t (the 8 rows of one load never
+    // straddle a matrix: gate/up blocks are 32 rows, the Q/K/V boundaries
+    // multiples of the tile width)
+    auto locate = [&](int t, const u16 *&m, int &row) {
+      if (a.b_mode == BMODE_GATEUP) {
+        m = ((t >> 5) & 1) ? a.B1 : a.B0;
+        row = (n0 >> 1) + (t >> 6) * 32 + (t & 31);
+      } else if (a.b_mode == BMODE_CONCAT3) {
+        const int n = min(n0 + t, a.N - 1), nq = a.n_seg, nkv = a.n_seg_kv > 0 ? a.n_seg_kv : a.n_seg;
+        m = n < nq ? a.B0 : (n < nq + nkv ? a.B1 : a.B2);
+        row = n < nq ? n : (n < nq + nkv ? n - nq : n - nq - nkv);
+      } else {
+        m = a.B0;
+        row = min(n0 + t, a.N - 1);
+      }
+    };
+    const u16 *m;
+    int first, row;
+    locate(r0, m, first);
+    locate(r, m, row);
+    bbase[q] = m + (int64_t)first * a.K;
+    boff[q] = (uint32_t)(((row - first) * a.K + 8 * c) * 2);
   }
 
   // K range of this workgroup: split blockIdx.y of k_splits equal ranges
   const int nk = a.K / BK / max(a.k_splits, 1);
   const int kb0 = blockIdx.y * nk * BK;
+  // Loads go global -> LDS as buffer_load_dwordx4 ... lds: each counts only
+  // against vmcnt, so waits for LDS operand reads (lgkmcnt) stay exact; with
+  // the global form of the same load the compiler also counts it as an
+  // outstanding LDS access and drains every in-flight load before each
+  // operand read (7B block 2.5% slower).
   auto issue = [&](int kt) {
     const int k0 = kb0 + min(kt, nk - 1) * BK;   // past the end: reload the last step (never read)
     u32x4 *st = smem + (kt % STAGES) * G::STAGE;
 #pragma unroll
     for (int q = 0; q < G::A_LD; ++q)
-      __builtin_amdgcn_global_load_lds((const void *)(asrc[q] + k0), LDS_PTR(st + (wave * G::A_LD + q) * 64), 16,
-                                       0, 0);
+      buf_load_lds16((const u16 *)a.A + afirst[q], aoff[q], k0 * 2, st + (wave * G::A_LD + q) * 64);
     if (APAIR) {
 #pragma unroll
       for (int q = 0; q < G::A_LD; ++q)
-        __builtin_amdgcn_global_load_lds((const void *)(alsrc[q] + k0),
-                                         LDS_PTR(st + G::A_TILE + (wave * G::A_LD + q) * 64), 16, 0, 0);
+        buf_load_lds16(a.A_lo + afirst[q], aoff[q], k0 * 2, st + G::A_TILE + (wave * G::A_LD + q) * 64);
     }
     u32x4 *sb = st + G::A_TILE * (APAIR ? 2 : 1);
 #pragma unroll
-    for (int q = 0; q < G::B_LD; ++q)
-      __builtin_amdgcn_global_load_lds((const void *)(bsrc[q] + k0), LDS_PTR(sb + (wave * G::B_LD + q) * 64), 16,
-                                       0, 0);
+    for (int q = 0; q < G::B_LD; ++q) buf_load_lds16(bbase[q], boff[q], k0 * 2, sb + (wave * G::B_LD + q) * 64);
   };
 
   f32x16 acc[G::TM][G::TN];
