@@ -123,9 +123,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   // read) so that every step waits on the same number of loads.
   // Per block this wavefront loads: K or v^T (wavefront-uniform), the lane's
   // fixed part of the source address, and the block's place in a stage.
+  // Loads go out as buffer loads to LDS: a uniform base per block (this
+  // sequence and head's K rows, or v^T row block) and per-lane byte offsets.
   constexpr int NQB = NBLK / 4;
   bool isk[NQB];
-  const u16 *lsrc[NQB];
+  const u16 *lbase[NQB];
+  uint32_t loff[NQB];
   int lrow[NQB], ldst[NQB];
 #pragma unroll
   for (int qb = 0; qb < NQB; ++qb) {
@@ -136,7 +139,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       const int row = kb * (64 / KCH) + lane / KCH;
       const int c = (lane % KCH) ^ rswz<KCH>(row);
       lrow[qb] = row;
-      lsrc[qb] = (part ? a.kl : a.kh) + ktok0 * kvd + hk * HD + 8 * c;
+      lbase[qb] = (part ? a.kl : a.kh) + ktok0 * kvd + hk * HD;
+      loff[qb] = (uint32_t)(8 * c * 2);
       ldst[qb] = part * KTILE + kb * 64;
     } else {
       const int vblk = blk - KBLK * (QKPAIR ? 2 : 1);
@@ -144,7 +148,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       const int e = vb * 16 + (lane >> 2);
       const int c = (lane & 3) ^ vswz(e);
       lrow[qb] = 0;
-      lsrc[qb] = (part ? a.vtl : a.vth) + vbase + (int64_t)e * a.vt_stride + 8 * c;
+      lbase[qb] = (part ? a.vtl : a.vth) + vbase;
+      loff[qb] = (uint32_t)((e * a.vt_stride + 8 * c) * 2);
       ldst[qb] = KTILE * (QKPAIR ? 2 : 1) + part * VTILE + vb * 64;
     }
   }
@@ -156,8 +161,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
 #pragma unroll
       for (int qb = 0; qb < NQB; ++qb) {
         // K row: rows past the last key load a valid key (masked later); v^T: key columns
-        const u16 *src = isk[qb] ? lsrc[qb] + (int64_t)min(kt * KT + lrow[qb], nkeys - 1) * kvd : lsrc[qb] + kt * KT;
-        __builtin_amdgcn_global_load_lds((const void *)src, ATT_LDS(st + ldst[qb]), 16, 0, 0);
+        if (isk[qb])
+          buf_load_lds16(lbase[qb], loff[qb] + (uint32_t)(min(kt * KT + lrow[qb], nkeys - 1) * kvd * 2), 0,
+                         st + ldst[qb]);
+        else
+          buf_load_lds16(lbase[qb], loff[qb], (uint32_t)(kt * KT * 2), st + ldst[qb]);
       }
     }
   };

@@ -134,3 +134,14 @@ DEV int xcd_remap(int bid, int nb) {
   const int x = bid % 8, i = bid / 8;
   return x < rem ? x * (per + 1) + i : rem * (per + 1) + (x - rem) * per + i;
 }
+
+// 16 bytes per lane from base + voff + soff (bytes) into LDS at lds + 16 * lane:
+// buffer_load_dwordx4 ... lds (the LDS address comes from M0, the lane slot
+// from the lane index). Offsets are 32-bit: callers keep them small (below a
+// tile or one sequence's rows). Used instead of the global form of the same
+// load, which the compiler also counts as an outstanding LDS access: every
+// LDS operand read would then wait for all loads in flight (lgkmcnt(0)).
+DEV void buf_load_lds16(const void *base, uint32_t voff, uint32_t soff, void *lds) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
+}

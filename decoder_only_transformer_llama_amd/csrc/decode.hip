@@ -115,10 +115,11 @@ __global__ __launch_bounds__(256, GEMV_OCC) void gemv_kernel(const GemvArgs a) {
     const int seg = q / 16;
     const int part = rr >> 5, m = rr & 31;
     const int c = (seg * 64 + lane) ^ (m & 15);
-    const int k = ks + min(8 * c, (ke - ks) - 8);
     const int mm = m < a.M ? m : 0;
-    const u16 *src = (part ? a.A_lo : a.A_hi) + (int64_t)mm * a.K + k;
-    __builtin_amdgcn_global_load_lds((const void *)src, GEMV_LDS(&sA[part][m][seg * 64]), 16, 0, 0);
+    // buffer form of the load: the global form would make the compiler wait
+    // for every load in flight (the weight ring too) before the first LDS read
+    buf_load_lds16((part ? a.A_lo : a.A_hi) + (int64_t)mm * a.K + ks, (uint32_t)(min(8 * c, (ke - ks) - 8) * 2), 0,
+                   &sA[part][m][seg * 64]);
   }
 
   f32x16 acc[NTW];

@@ -91,14 +91,6 @@ struct GemmCfg {
 template <int CH>
 DEV int swz(int row) { return CH == 4 ? (row >> 2) & 3 : (row >> 1) & 7; }
 
-// 16 bytes per lane from base + voff + soff (bytes) into LDS at lds + 16 * lane:
-// buffer_load_dwordx4 ... lds (the LDS address comes from M0, the lane slot
-// from the lane index). Offsets are 32-bit: callers keep them below one tile.
-DEV void buf_load_lds16(const void *base, uint32_t voff, uint32_t soff, void *lds) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, LDS_PTR(lds), 16, voff, soff, 0, 0);
-}
-
 // Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (compile-time indices).
 template <int I, int N, class F>
 DEV void static_for(F &&f) {
