@@ -254,6 +254,47 @@ def bench_other_blocks(args, torch):
     return out
 
 
+def time_block(torch, bw, reps: int, warmup: int) -> float:
+    """Mean ms of bw.block(bw.x) over `reps` calls (HIP events on the library's stream)."""
+    for _ in range(warmup):
+        bw.block(bw.x)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    ev = HipEvents(2)
+    ev.record(0, stream)
+    for _ in range(reps):
+        bw.block(bw.x)
+    ev.record(1, stream)
+    ms = ev.elapsed_ms(0, 1) / reps
+    torch.cuda.synchronize()
+    return ms
+
+
+def bench_extra_blocks(args, torch):
+    """The 7B-shape block with bf16 matrix-core projections (bf16 operands and
+    weights, no fp16 copies) beside the default, and the tiny fp32 block
+    (d 256, 128 tokens: launch-bound, no roofline target)."""
+    from decoder_only_transformer_llama_amd import _lib as L
+    from decoder_only_transformer_llama_amd.workloads import block_workload
+    # every projection operand one bf16 value on the bf16 matrix cores, the
+    # attention output into Wo as a bf16 hi/lo pair, fp16 attention
+    bf16_operands = L.NUM_EXPLICIT | L.NUM_ATTN_F16 | L.NUM_O_A_PAIR
+    out = {}
+    bw = block_workload(1, "cuda", numerics=bf16_operands)
+    ms = time_block(torch, bw, args.steps, args.warmup)
+    tf = sum(block_flops(bw.w).values()) / (ms * 1e-3) / 1e12
+    out["7b-block-bf16-operands"] = {"ms": round(ms, 4), "tokens_per_s": round(bw.w.tokens / (ms * 1e-3), 1),
+                                     "tflops": round(tf, 1), "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                                     "numerics": hex(bf16_operands)}
+    del bw
+    torch.cuda.empty_cache()
+    bw = block_workload(0, "cuda")
+    ms = time_block(torch, bw, args.steps, args.warmup)
+    out[bw.w.name] = {"ms": round(ms, 4), "tokens_per_s": round(bw.w.tokens / (ms * 1e-3), 1),
+                      "tflops": round(sum(block_flops(bw.w).values()) / (ms * 1e-3) / 1e12, 3)}
+    return out
+
+
 def bench_train_step(args, torch, wid: int = 0):
     """fp32 training step of a block (forward keeping the linear outputs,
     manual backward, SGD update of all nine weights) on an fp32 block workload
@@ -407,11 +448,24 @@ def cpu_baseline(bw, torch, budget_s: float = 10.0, max_reps: int = 8):
     `max_reps` passes), reported as tokens/s over all passes."""
     import numpy as np
     from oracle import llama_oracle as O
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        info = threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in info] or [1])
+        blas = ", ".join(f"{p.get('internal_api')} {p.get('version')}" for p in info if p.get("user_api") == "blas") \
+            or blas
     except Exception:
         cores = os.cpu_count() or 1
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     w = bw.w
     x = O.f64(bw.x.cpu())
     wt = {k: O.f64(v.cpu()) for k, v in bw.weights.items()}
@@ -424,7 +478,8 @@ def cpu_baseline(bw, torch, budget_s: float = 10.0, max_reps: int = 8):
             break
     return {"value": round(reps * w.tokens / dt, 1), "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"7B-shape block forward (fp64 NumPy oracle), batch {w.batch} x seq {w.seq}, "
-                      f"{reps} pass(es) in {dt:.2f} s"}
+                      f"{reps} pass(es) in {dt:.2f} s",
+            "cpu_model": cpu_model, "blas": blas}
 
 
 def main() -> int:
@@ -483,6 +538,8 @@ def main() -> int:
     if not args.prefill_only and not args.no_other_blocks:
         others = bench_other_blocks(args, torch)
         print(f"# other blocks: {json.dumps(others)}", file=sys.stderr, flush=True)
+        others.update(bench_extra_blocks(args, torch))
+        print(f"# extra blocks: {json.dumps(others)}", file=sys.stderr, flush=True)
     dec = None
     if not args.prefill_only:
         dec = bench_decode(args, torch)

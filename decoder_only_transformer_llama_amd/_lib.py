@@ -37,6 +37,7 @@ EXPORTS = (
     "llama_trace_label", "llama_argmax", "llama_decode_pack_size", "llama_pack_decode_weights",
     "llama_causal_attn_backward", "llama_block_train_saved_size", "llama_block_train_forward",
     "llama_block_backward", "llama_axpby", "llama_convert_weights_f16", "llama_model_decode_static",
+    "llama_decode_pack_max_read",
 )
 
 
@@ -98,6 +99,7 @@ def load() -> ctypes.CDLL:
         "llama_axpby": [vp, vp, vp, f32, f32, i64, vp],
         "llama_convert_weights_f16": [vp, vp, i64, vp],
         "llama_model_decode_static": [cfgp, ctypes.POINTER(ModelWeights), vp, vp, i32, vp, vp, vp, vp],
+        "llama_decode_pack_max_read": [cfgp, ctypes.POINTER(sz)],
     }
     for name, args in sig.items():
         fn = getattr(lib, name)

@@ -176,11 +176,6 @@ ResidCfg choose_resid(int M, int N, int K, bool apair) {
   auto rounds = [&](long tiles) { return (double)((tiles + cus - 1) / cus); };
   const double c128 = rounds(tm * ((N + 127) / 128)) * kHalfTileCost;
   const double c256 = rounds(tm * ((N + 255) / 256));
-#ifdef RESID_FORCE   // tiling experiments: 1 = 256 x 128, 2 = 256 x 256, 3 = 256 x 256 with K split in two
-  if (RESID_FORCE == 1) return {128, 1};
-  if (RESID_FORCE == 2) return {256, 1};
-  if (RESID_FORCE == 3 && K % 128 == 0) return {256, 2};
-#endif
   double c256s2 = 1e30;
   if (K % 128 == 0) {   // each half a whole number of 64-deep steps
     const double traffic_us = (double)M * N * 4.0 * 2.0 * 2.0 / 5e6;
@@ -323,10 +318,8 @@ void gemv_split(int N, int K, int &splits, int &k_chunk) {
   const int per_wg = 128 * gemv_ntw(N);
   const int n_wg = (N + per_wg - 1) / per_wg;
   const int ksteps = K / 64;
-#ifndef GEMV_TARGET_WGS
-#define GEMV_TARGET_WGS 256
-#endif
-  const int s = std::max(1, std::min(ksteps, (GEMV_TARGET_WGS + n_wg - 1) / n_wg));
+  constexpr int kTargetWgs = 256;   // workgroups a skinny GEMM aims for (one per compute unit)
+  const int s = std::max(1, std::min(ksteps, (kTargetWgs + n_wg - 1) / n_wg));
   const int per = std::min((ksteps + s - 1) / s, kGemvMaxChunk / 64);
   k_chunk = per * 64;
   splits = (K + k_chunk - 1) / k_chunk;
@@ -1278,6 +1271,43 @@ int llama_model_decode_static(const llama_config *c, const llama_model_weights *
   const int sst = static_scratch_of_current_device(&ws);
   if (sst) return sst;
   return llama_model_decode(c, w, tokens, pos, batch, k_cache, v_cache, logits, ws, kStaticScratchBytes, stream);
+}
+
+int llama_decode_pack_max_read(const llama_config *c, size_t *bytes) {
+  if (!c || !bytes) return LLAMA_ERR_NULL;
+  const int st = check_model_cfg(c, 1, 1);
+  if (st) return st;
+  // every skinny GEMM launch of a decode step, with the block addressing of
+  // gemv_kernel: workgroup x, wavefront w, tile j of NTW; split y streams
+  // steps it < nit of its K chunk, pieces q < 4, lanes < 64 (16 bytes each)
+  const PackLayout pl = pack_layout(c);
+  const int d = c->dim, h = c->hidden;
+  struct Mat { size_t off; int N, K; };
+  const Mat mats[5] = {{pl.qkv, d + 2 * kv_dim(c), d}, {pl.o, d, d}, {pl.gu, 2 * h, d}, {pl.down, d, h},
+                       {pl.head_off, c->vocab, d}};
+  size_t end = 0;
+  for (int m = 0; m < 5; ++m) {
+    const Mat &mt = mats[m];
+    // every layer's matrices share the first layer's offsets plus whole layers
+    const size_t layer_base = m < 4 ? (size_t)(c->n_layers - 1) * pl.layer : 0;
+    int splits, kc;
+    gemv_split(mt.N, mt.K, splits, kc);
+    const int ntw = gemv_ntw(mt.N), n_tiles = (mt.N + 31) / 32, per_wg = 128 * ntw;
+    const int n_wg = (mt.N + per_wg - 1) / per_wg;
+    for (int y = 0; y < splits; ++y) {
+      const int ks = y * kc, ke = std::min(mt.K, ks + kc), nit = (ke - ks) / 64;
+      for (int x = 0; x < n_wg; ++x)
+        for (int w = 0; w < 4; ++w)
+          for (int j = 0; j < ntw; ++j) {
+            const int t = std::min((x * 4 + w) * ntw + j, n_tiles - 1);
+            const size_t last = (size_t)pack_block(t, ks / 64, n_tiles, mt.K / 64, kc / 64) * 2048 +
+                                63 * 8 + 2048 * (size_t)(nit - 1) + 512 * 3 + 8;   // one past the last element
+            end = std::max(end, mt.off + layer_base + last);
+          }
+    }
+  }
+  *bytes = end * sizeof(uint16_t);
+  return LLAMA_OK;
 }
 
 int llama_decode_pack_size(const llama_config *c, size_t *bytes) {

@@ -67,22 +67,16 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   constexpr int KTILE = KT * KCH;                // u32x4 per K tile
   constexpr int VTILE = HD * 4;                  // u32x4 per v^T tile (4 chunks of 8 keys)
   constexpr int STAGE1 = KTILE * (QKPAIR ? 2 : 1) + VTILE * (VPAIR ? 2 : 1);   // one 32-key tile
-#ifndef ATTN_NST
-#define ATTN_NST 3
-#endif
-#ifndef ATTN_SUB
-#define ATTN_SUB 2
-#endif
   // Tiles per step (SUB): with fp16 operands two 32-key tiles share one
   // barrier and one softmax update, so each step carries two independent
   // score chains; the longest workgroups (the last query tiles, 2048 keys)
   // then take half as many dependent steps.
-  constexpr int SUB = F16 ? ATTN_SUB : 1;
+  constexpr int SUB = F16 ? 2 : 1;
   constexpr int STAGE = SUB * STAGE1;
   // LDS ring depth: single fp16 operands (16 KB per tile at hd 128) keep
-  // ATTN_NST - 1 steps in flight with one tile per step, one with two; bf16
+  // two steps in flight with one tile per step, one with two; bf16
   // pairs (32 KB per tile) stay at 2, so that two workgroups fit a compute unit.
-  constexpr int NST = (F16 && SUB == 1) ? ATTN_NST : 2;
+  constexpr int NST = (F16 && SUB == 1) ? 3 : 2;
   constexpr float kLazyRescale = 8.0f;   // log2 units a running maximum may lag the true one
   constexpr int KBLK = KTILE / 64, VBLK = VTILE / 64;       // 1 KB blocks per tile
   constexpr int NBLK = KBLK * (QKPAIR ? 2 : 1) + VBLK * (VPAIR ? 2 : 1);

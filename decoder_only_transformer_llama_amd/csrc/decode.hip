@@ -38,32 +38,15 @@ DEV bool pos_ok(int p, int max_seq) { return p >= 0 && p < max_seq; }
 // weights are already streaming from HBM into a ring of B-operand registers,
 // so the two latencies overlap; afterwards DEPTH steps of 64 K stay in flight
 // per wavefront.
-#ifndef GEMV_KC_MAX
-#define GEMV_KC_MAX 512
-#endif
-constexpr int KC_MAX = GEMV_KC_MAX;
+constexpr int KC_MAX = kGemvMaxChunk;
 
 #define GEMV_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 #define GEMV_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-// Tile-packed weights: one 4 KB block per (32-column tile t, 64-wide K step),
-// holding the 64 lanes' 16-byte B-operand pieces in lane order. Blocks are
-// ordered chunk-major for the split-K chunks of kcs steps (the last chunk may
-// be shorter): all tiles' blocks of chunk 0, then chunk 1, ...; within a
-// chunk tile-major, step-minor. The blocks one workgroup streams (its
-// consecutive tiles over one K chunk) are then one contiguous region.
-__host__ __device__ inline int64_t pack_block(int t, int st, int n_tiles, int ksteps, int kcs) {
-  const int c = st / kcs, s = st - c * kcs;
-  const int len = ksteps - c * kcs < kcs ? ksteps - c * kcs : kcs;
-  return (int64_t)c * n_tiles * kcs + (int64_t)t * len + s;
-}
-
-#ifndef GEMV_OCC
-#define GEMV_OCC (KC_MAX > 512 ? 1 : 2)   // workgroups per CU the register budget is sized for
-#endif
+constexpr int kGemvOcc = 2;   // workgroups per CU the register budget is sized for
 
 template <int NTW, int DEPTH>
-__global__ __launch_bounds__(256, GEMV_OCC) void gemv_kernel(const GemvArgs a) {
+__global__ __launch_bounds__(256, kGemvOcc) void gemv_kernel(const GemvArgs a) {
   __shared__ u32x4 sA[2][32][KC_MAX / 8];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g = lane >> 5, l32 = lane & 31;
@@ -191,16 +174,10 @@ __global__ __launch_bounds__(256, GEMV_OCC) void gemv_kernel(const GemvArgs a) {
   }
 }
 
-#ifndef GEMV_DEPTH
-#define GEMV_DEPTH 4
-#endif
+constexpr int kGemvDepth = 4;   // 64-deep weight steps in flight per wavefront
 
 int gemv_ntw(int N) {
-#ifdef GEMV_NTW_FORCE
-  return GEMV_NTW_FORCE;
-#else
   return N > 8192 ? 2 : 1;
-#endif
 }
 
 // One thread per 16-byte piece: source block (tile, step) in tile-major order,
@@ -247,9 +224,9 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s) {
   const int per_wg = 4 * 32 * ntw;
   dim3 grid((a.N + per_wg - 1) / per_wg, a.splits);
   if (ntw == 2)
-    hipLaunchKernelGGL((gemv_kernel<2, GEMV_DEPTH>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<2, kGemvDepth>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemv_kernel<1, GEMV_DEPTH>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((gemv_kernel<1, kGemvDepth>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -473,10 +450,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
                                                        u16 *a_lo, float *opart) {
   constexpr int LPK = HD / 8;          // lanes per key
   constexpr int KPW = 64 / LPK;        // keys per wavefront instruction
-#ifndef DEC_ATTN_UNROLL
-#define DEC_ATTN_UNROLL 2
-#endif
-  constexpr int UNR = DEC_ATTN_UNROLL; // key instructions per wavefront per step
+  constexpr int UNR = 2;               // key instructions per wavefront per step
   constexpr int KPS = 4 * KPW * UNR;   // keys per workgroup step
   constexpr int NG = 4 * KPW;          // lane groups per workgroup
   // One workgroup per (key/value head hk, sequence b): the G query heads
@@ -695,13 +669,9 @@ __global__ void dec_attn_combine_kernel(const DecodeArgs d, const float *opart, 
 // per step of attention with 1 / 2 / 4 / 8 ranges; 32 heads (1024 pairs) are
 // fastest unsplit (5.94 ms against 6.15 with 2 ranges).
 int dec_attn_ranges(const DecodeArgs &d) {
-#ifdef DEC_ATTN_SPLITS
-  return DEC_ATTN_SPLITS;
-#else
   int ns = 1;
   while (ns < kDecAttnMaxRanges && d.n_kv_heads * d.batch * ns < 512) ns *= 2;
   return ns;
-#endif
 }
 
 template <int HD, int G>

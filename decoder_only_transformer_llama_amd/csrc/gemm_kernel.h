@@ -53,20 +53,16 @@ namespace llama {
 // lgkmcnt[11:8], vmcnt[5:4] in [15:14]).
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 
-#ifndef GEMM_BK
-#define GEMM_BK 64
-#endif
+constexpr int kGemmWaves = 8;   // wavefronts per workgroup, two per SIMD
+
 template <int BN, bool APAIR>
 struct GemmCfg {
-  // K step: GEMM_BK (32 or 64) for single operands; hi/lo pairs keep 32 (a
-  // 64-deep stage with A_lo would not fit two stages in LDS)
-  static constexpr int BM = 256, BK = APAIR ? 32 : GEMM_BK;
+  // K step: 64 for single operands; hi/lo pairs keep 32 (a 64-deep stage
+  // with A_lo would not fit two stages in LDS)
+  static constexpr int BM = 256, BK = APAIR ? 32 : 64;
   static constexpr int CH = BK / 8;                // 16-byte chunks per LDS row
   static constexpr int RPL = 64 / CH;              // rows per 1 KB wavefront load
-#ifndef GEMM_NW
-#define GEMM_NW 8
-#endif
-  static constexpr int NW = GEMM_NW;               // wavefronts: 2 (M) x NW/2 (N)
+  static constexpr int NW = kGemmWaves;            // wavefronts: 2 (M) x NW/2 (N)
   static constexpr int WM = BM / 2, WN = BN / (NW / 2);
   static constexpr int TM = WM / 32, TN = WN / 32;
   static constexpr int A_TILE = BM * CH;           // u32x4 per A tile
@@ -120,7 +116,7 @@ DEV void interleave() {
 // once, ahead of time, by the same rule), so the products see the same bits
 // as with F16 1 without the 3 VALU instructions per two weights.
 template <int BN, bool APAIR, int EPI, int F16 = 0>
-__global__ __launch_bounds__(GEMM_NW * 64, 1) void gemm_bf16_kernel(const GemmArgs a) {
+__global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const GemmArgs a) {
   static_assert(!(F16 && APAIR), "fp16 operands are single");
   using G = GemmCfg<BN, APAIR>;
   constexpr int BM = G::BM, BK = G::BK, CH = G::CH, STAGES = G::STAGES;

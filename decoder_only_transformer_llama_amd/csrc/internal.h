@@ -181,6 +181,18 @@ struct GemvArgs {
   const uint16_t *packed;        // optional: the same matrix in 32-row tile order (see pack_tiles_launch)
   float *part;                   // [splits, M, N]
 };
+// Tile-packed weights: one 4 KB block per (32-column tile t, 64-wide K step),
+// holding the 64 lanes' 16-byte B-operand pieces in lane order. Blocks are
+// ordered chunk-major for the split-K chunks of kcs steps (the last chunk may
+// be shorter): all tiles' blocks of chunk 0, then chunk 1, ...; within a
+// chunk tile-major, step-minor. The blocks one workgroup streams (its
+// consecutive tiles over one K chunk) are then one contiguous region.
+__host__ __device__ inline int64_t pack_block(int t, int st, int n_tiles, int ksteps, int kcs) {
+  const int c = st / kcs, s = st - c * kcs;
+  const int len = ksteps - c * kcs < kcs ? ksteps - c * kcs : kcs;
+  return (int64_t)c * n_tiles * kcs + (int64_t)t * len + s;
+}
+
 hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
 // Copy B (row mapping b_mode as in GemvArgs) into tile order: 4 KB block per
 // (32-row tile t, 64-wide K step s), piece (q, lane g*32+j) = B[32t+j][64s+32g+8q..+7];
@@ -190,10 +202,7 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
 hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
                              int n_seg_kv, int N, int K, int k_chunk, uint16_t *dst, hipStream_t s);
 int gemv_ntw(int N);               // 32-column tiles per wavefront used for N
-#ifndef GEMV_KC_MAX
-#define GEMV_KC_MAX 512
-#endif
-constexpr int kGemvMaxChunk = GEMV_KC_MAX; // largest K range of one workgroup
+constexpr int kGemvMaxChunk = 512;  // largest K range of one workgroup
 
 struct DecodeArgs {
   int batch, dim, n_heads, head_dim, hidden, max_seq, vocab;

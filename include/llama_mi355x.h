@@ -312,6 +312,11 @@ int llama_argmax(const float *logits, int64_t rows, int vocab, int32_t *out, voi
  * llama_pack_decode_weights: fill dst (device, dst_bytes >= that size) from
  * w on `stream`. bf16 configs only. Errors as llama_model_decode validates. */
 int llama_decode_pack_size(const llama_config *c, size_t *bytes);
+/* One past the last byte of the pack that the decode step's skinny GEMMs
+ * read (host, *bytes), computed with the launches' own tile, split and block
+ * addressing; a pack of llama_decode_pack_size bytes holds it. For checking
+ * the layout without a GPU. Errors as llama_decode_pack_size. */
+int llama_decode_pack_max_read(const llama_config *c, size_t *bytes);
 int llama_pack_decode_weights(const llama_config *c, const llama_model_weights *w, void *dst,
                               size_t dst_bytes, void *stream);
 

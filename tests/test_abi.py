@@ -239,3 +239,22 @@ def test_training_entry_points_validate_before_any_launch():
                                           16, None) == L.LLAMA_ERR_WORKSPACE
     assert lib.llama_axpby(None, FAKE, FAKE, 1.0, 1.0, 4, None) == L.LLAMA_ERR_NULL
     assert lib.llama_axpby(FAKE, FAKE, FAKE, 1.0, 1.0, -1, None) == L.LLAMA_ERR_SHAPE
+
+
+@pytest.mark.parametrize("wid", [4, 5, 101, 105, 106, 108])
+def test_decode_pack_reads_stay_inside_the_pack(wid):
+    """Every skinny-GEMM launch of a decode step reads the weight pack through
+    its tile, split-K and block addressing; the furthest byte any launch reads
+    (computed by the library from the launches' own addressing, host only)
+    must be the pack's last byte: not past it (an out-of-bounds read), and
+    not short of it (a part of the pack never streamed)."""
+    import torch
+    from decoder_only_transformer_llama_amd import inputs as I, ops
+    w = I.workload(wid)
+    cfg = ops.config(w.dim, w.n_heads, w.hidden, dtype=torch.bfloat16, n_layers=w.n_layers, vocab=w.vocab,
+                     max_seq=w.max_seq, eps=w.eps, n_kv_heads=w.n_kv_heads)
+    lib = L.load()
+    size, end = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.llama_decode_pack_size(ctypes.byref(cfg), ctypes.byref(size)) == L.LLAMA_OK
+    assert lib.llama_decode_pack_max_read(ctypes.byref(cfg), ctypes.byref(end)) == L.LLAMA_OK
+    assert end.value == size.value, (end.value, size.value)
