@@ -145,3 +145,20 @@ DEV void buf_load_lds16(const void *base, uint32_t voff, uint32_t soff, void *ld
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16, voff, soff, 0, 0);
 }
+
+// v, which must already be the same in every lane of the wavefront, as a
+// value the compiler knows to be uniform (it is read from the first active
+// lane). A buffer load whose base the compiler cannot prove uniform is
+// wrapped in a loop over the distinct lane values.
+// (The builtin returns a signed int: each half goes back through uint32_t so
+// that the low half is zero-extended, not sign-extended, into 64 bits.)
+DEV int64_t wave_uniform(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+  return (int64_t)(((uint64_t)hi << 32) | (uint64_t)lo);
+}
+template <typename T>
+DEV T *wave_uniform(T *p) {
+  return (T *)wave_uniform((int64_t)p);
+}

@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
     const int r0 = G::RPL * (wave * G::A_LD + q), r = r0 + lane / G::CH;
     const int c = (lane % G::CH) ^ swz<G::CH>(r);
     const int first = min(m0 + r0, a.M - 1), row = min(m0 + r, a.M - 1);
-    afirst[q] = (int64_t)first * a.lda;
+    afirst[q] = wave_uniform((int64_t)first * a.lda);
     aoff[q] = (uint32_t)(((row - first) * a.lda + 8 * c) * 2);
   }
   const u16 *bbase[G::B_LD];
@@ -178,11 +178,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
         row = min(n0 + t, a.N - 1);
       }
     };
-    const u16 *m;
+    const u16 *m, *mr;
     int first, row;
-    locate(r0, m, first);
-    locate(r, m, row);
-    bbase[q] = m + (int64_t)first * a.K;
+    locate(r0, m, first);   // the load's base: the same in every lane
+    locate(r, mr, row);     // mr == m
+    bbase[q] = wave_uniform(m + (int64_t)first * a.K);
     boff[q] = (uint32_t)(((row - first) * a.K + 8 * c) * 2);
   }
 
