@@ -315,14 +315,9 @@ struct DecodeWs {
 constexpr int kDecMaxSeq = 2048;   // longest cache the decode path is validated for
 
 void gemv_split(int N, int K, int &splits, int &k_chunk) {
-  const int per_wg = 128 * gemv_ntw(N);
-  const int n_wg = (N + per_wg - 1) / per_wg;
-  const int ksteps = K / 64;
-  constexpr int kTargetWgs = 256;   // workgroups a skinny GEMM aims for (one per compute unit)
-  const int s = std::max(1, std::min(ksteps, (kTargetWgs + n_wg - 1) / n_wg));
-  const int per = std::min((ksteps + s - 1) / s, kGemvMaxChunk / 64);
-  k_chunk = per * 64;
-  splits = (K + k_chunk - 1) / k_chunk;
+  const GemvShape g = gemv_shape(N, K);
+  splits = g.splits;
+  k_chunk = g.k_chunk;
 }
 
 size_t dec_part_floats(const llama_config *c, int batch) {
@@ -1292,7 +1287,7 @@ int llama_decode_pack_max_read(const llama_config *c, size_t *bytes) {
     const size_t layer_base = m < 4 ? (size_t)(c->n_layers - 1) * pl.layer : 0;
     int splits, kc;
     gemv_split(mt.N, mt.K, splits, kc);
-    const int ntw = gemv_ntw(mt.N), n_tiles = (mt.N + 31) / 32, per_wg = 128 * ntw;
+    const int ntw = gemv_shape(mt.N, mt.K).ntw, n_tiles = (mt.N + 31) / 32, per_wg = 128 * ntw;
     const int n_wg = (mt.N + per_wg - 1) / per_wg;
     for (int y = 0; y < splits; ++y) {
       const int ks = y * kc, ke = std::min(mt.K, ks + kc), nit = (ke - ks) / 64;

@@ -201,7 +201,12 @@ hipError_t gemv_launch(const GemvArgs &a, hipStream_t s);
 // k_chunk (the chunk the skinny GEMM later runs with for this N and K).
 hipError_t pack_tiles_launch(int b_mode, const uint16_t *B0, const uint16_t *B1, const uint16_t *B2, int n_seg,
                              int n_seg_kv, int N, int K, int k_chunk, uint16_t *dst, hipStream_t s);
-int gemv_ntw(int N);               // 32-column tiles per wavefront used for N
+// Shape of the skinny product of N columns over K: 32-column tiles per
+// wavefront (ntw), K range per workgroup (k_chunk) and number of ranges.
+struct GemvShape {
+  int ntw, k_chunk, splits;
+};
+GemvShape gemv_shape(int N, int K);
 constexpr int kGemvMaxChunk = 512;  // largest K range of one workgroup
 
 struct DecodeArgs {

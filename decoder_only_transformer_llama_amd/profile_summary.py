@@ -11,8 +11,18 @@ Two summaries:
   The summary records the SHA-256 of the kernel's source files; bench.py
   reports the figure only while those sources are unchanged.
 
+* ``counters``: per kernel, the SQ/GRBM counters of one or more ``--pmc``
+  runs with what follows from them: the fraction of SIMD cycles the matrix
+  cores were busy (SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE per XCD times
+  the SIMD count), the clock the kernel ran at (GUI-active cycles per XCD over
+  the dispatch's duration), non-matrix VALU instructions per MFMA, LDS bank
+  conflict cycles per LDS instruction; and, with ``--bytes`` runs
+  (FETCH_SIZE / WRITE_SIZE), HBM GB/s per kernel.
+
 Usage:
   python -m decoder_only_transformer_llama_amd.profile_summary stats DIR OUT.txt --command "..."
+  python -m decoder_only_transformer_llama_amd.profile_summary counters OUT.txt --pmc DIR [DIR ...] \
+      [--fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N] --command "..."
   python -m decoder_only_transformer_llama_amd.profile_summary traffic --kernel SUBSTR \\
       --fetch DIR --write DIR --copy-fetch DIR --copy-write DIR --copy-bytes N \\
       --sources a.hip b.h --command "..." OUT.txt
@@ -148,6 +158,98 @@ def write_traffic(a) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+def _agent(d: str) -> Dict[str, float]:
+    """Num_Xcc, Simd_Count and Max_Engine_Clk_Fcompute of the GPU agent of a run."""
+    for f in _find(d, "agent_info.csv"):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Agent_Type") == "GPU":
+                    return {k: float(r[k]) for k in ("Num_Xcc", "Simd_Count", "Max_Engine_Clk_Fcompute")}
+    raise SystemExit(f"no GPU agent_info.csv under {d}")
+
+
+def per_kernel_counters(dirs: List[str]) -> Dict[str, Dict[str, float]]:
+    """{kernel: {counter: mean per dispatch, '_n': dispatches, '_dur_ns': median duration}}"""
+    out: Dict[str, Dict[str, float]] = {}
+    for d in dirs:
+        per: Dict[Tuple[str, str], Dict[str, float]] = {}
+        durs: Dict[Tuple[str, str], int] = {}
+        for f in _find(d, "counter_collection.csv"):
+            with open(f, newline="") as fh:
+                for r in csv.DictReader(fh):
+                    key = (r["Kernel_Name"], f + ":" + r["Dispatch_Id"])
+                    c = per.setdefault(key, {})
+                    c[r["Counter_Name"]] = c.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+                    durs[key] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        by_k: Dict[str, List[Tuple[Dict[str, float], int]]] = {}
+        for (k, disp), c in per.items():
+            by_k.setdefault(k, []).append((c, durs[(k, disp)]))
+        for k, lst in by_k.items():
+            o = out.setdefault(k, {})
+            for name in lst[0][0]:
+                o[name] = sum(c.get(name, 0.0) for c, _ in lst) / len(lst)
+            o["_n"] = len(lst)
+            ds = sorted(t for _, t in lst)
+            o.setdefault("_dur_ns", float(ds[len(ds) // 2]))
+    return out
+
+
+def write_counters(a) -> None:
+    ag = _agent(a.pmc[0])
+    xcc, simds, mhz = ag["Num_Xcc"], ag["Simd_Count"], ag["Max_Engine_Clk_Fcompute"]
+    kc = per_kernel_counters(a.pmc)
+    f_fetch = f_write = None
+    if a.fetch:
+        cf, _ = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
+        cw, _ = counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
+        f_fetch, f_write = cf * 1024.0 / a.copy_bytes, cw * 1024.0 / a.copy_bytes
+        for k, v in per_kernel_counters([a.fetch, a.write]).items():
+            o = kc.setdefault(k, {"_n": v["_n"], "_dur_ns": v["_dur_ns"]})
+            for name in ("FETCH_SIZE", "WRITE_SIZE"):
+                if name in v:
+                    o[name] = v[name]
+            o["_bytes_dur_ns"] = v["_dur_ns"]
+    rows = []
+    for k, c in kc.items():
+        if not any(s in k for s in a.kernel) and a.kernel:
+            continue
+        rows.append((k, c))
+    rows.sort(key=lambda kv: -kv[1].get("SQ_VALU_MFMA_BUSY_CYCLES", kv[1].get("FETCH_SIZE", 0.0)))
+    lines = ["# rocprofv3 counters per kernel (means per dispatch)", "", "commands:"] + ["  " + c for c in a.command]
+    lines += ["", f"GPU: {int(xcc)} XCDs, {int(simds)} SIMDs, peak engine clock {mhz:.0f} MHz", "",
+              "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs), at the clock the kernel ran",
+              "clock: GRBM_GUI_ACTIVE / XCDs / dispatch duration under counters; peak_frac = mfma_busy * clock / peak clock",
+              "valu/mfma: (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (SQ_INSTS_VALU counts MFMAs too)",
+              "lds_conf: SQ_LDS_BANK_CONFLICT cycles per SQ_INSTS_LDS instruction"]
+    if f_fetch:
+        lines += [f"HBM bytes: FETCH_SIZE / {f_fetch:.4f} + WRITE_SIZE / {f_write:.4f} (factors from a {a.copy_kernel} "
+                  f"copy of {a.copy_bytes} bytes); GB/s over the dispatch's duration in the byte-counter runs"]
+    lines += ["", f"{'n':>4} {'dur us':>9} {'mfma':>10} {'busy':>6} {'clk GHz':>7} {'peak_fr':>7} {'valu/mfma':>9} "
+              f"{'lds_conf':>8} {'MB':>9} {'GB/s':>7}  kernel"]
+    for k, c in rows:
+        n = int(c["_n"])
+        dur = c["_dur_ns"]
+        gui = c.get("GRBM_GUI_ACTIVE")
+        mf = c.get("SQ_INSTS_MFMA")
+        busy = c.get("SQ_VALU_MFMA_BUSY_CYCLES")
+        cyc = gui / xcc if gui else None
+        fb = busy / (cyc * simds) if busy is not None and cyc else None
+        clk = cyc / dur if cyc and dur else None
+        pf = fb * clk / (mhz / 1e3) if fb is not None and clk else None
+        vpm = (c["SQ_INSTS_VALU"] - mf) / mf if mf and "SQ_INSTS_VALU" in c else None
+        lc = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"] if c.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in c else None
+        mb = gbs = None
+        if f_fetch and "FETCH_SIZE" in c and "WRITE_SIZE" in c:
+            byt = c["FETCH_SIZE"] * 1024.0 / f_fetch + c["WRITE_SIZE"] * 1024.0 / f_write
+            mb = byt / 1e6
+            gbs = byt / c.get("_bytes_dur_ns", dur)
+        fmt = lambda v, w, p: f"{v:{w}.{p}f}" if v is not None else f"{'-':>{w}}"
+        lines.append(f"{n:4d} {dur / 1e3:9.2f} {fmt(mf, 10, 0)} {fmt(fb, 6, 3)} {fmt(clk, 7, 3)} {fmt(pf, 7, 3)} "
+                     f"{fmt(vpm, 9, 2)} {fmt(lc, 8, 3)} {fmt(mb, 9, 2)} {fmt(gbs, 7, 0)}  {short_name(k)}")
+    with open(a.out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def stored_traffic(path: str) -> Optional[float]:
     """traffic_bytes_per_launch from a summary written by `traffic`, or None
     when the file is missing or the kernel's sources changed since."""
@@ -187,9 +289,22 @@ def main() -> None:
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--sources", nargs="+", required=True)
     t.add_argument("--command", action="append", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("out")
+    c.add_argument("--pmc", nargs="+", required=True)
+    c.add_argument("--kernel", action="append", default=[], help="keep kernels whose name contains this")
+    c.add_argument("--fetch")
+    c.add_argument("--write")
+    c.add_argument("--copy-fetch")
+    c.add_argument("--copy-write")
+    c.add_argument("--copy-kernel", default="copy")
+    c.add_argument("--copy-bytes", type=int)
+    c.add_argument("--command", action="append", required=True)
     a = ap.parse_args()
     if a.cmd == "stats":
         write_stats(a.dir, a.out, a.command, a.top)
+    elif a.cmd == "counters":
+        write_counters(a)
     else:
         write_traffic(a)
 
