@@ -43,6 +43,16 @@ def stored_traffic(key: str):
     return None if v is None else round(v)
 
 
+def decode_summary(dec: dict) -> dict:
+    return {
+        "workload": "llama-7b-shape model decode step, batch 32, KV cache 2047 positions, bf16",
+        "tokens_per_s": round(dec["tokens_per_s"], 1), "ms_per_step": round(dec["ms"], 4),
+        "ms_per_step_eager": round(dec["ms_eager"], 4), "hip_graph": dec["graph"],
+        "hbm_gbs": round(dec["hbm_gbs"], 1), "hbm_frac": round(dec["hbm_gbs"] / PEAK_HBM_GBS, 4),
+        "bytes_per_step": dec["bytes"], "roofline": dec["roofline"], "kernels_ms": dec["per_kernel_ms"],
+    }
+
+
 def copy_calibration(torch) -> None:
     """A plain device copy of known size (read and write COPY_CALIBRATION_BYTES
     each) for scaling the HBM byte counters; run under rocprofv3 --pmc."""
@@ -523,6 +533,8 @@ def main() -> int:
         dec = bench_decode(args, torch)
         print(f"# decode: {dec['ms']:.3f} ms/step (eager {dec['ms_eager']:.3f}), {dec['tokens_per_s']:.0f} tok/s, "
               f"{dec['hbm_gbs']:.0f} GB/s; kernels {json.dumps(dec['per_kernel_ms'])}", file=sys.stderr, flush=True)
+        # the decode object of the full line on its own (diagnostic runs: profiles read its roofline)
+        print(json.dumps({"decode": decode_summary(dec)}), flush=True)
         if dec["model_prefill"]:
             print(f"# model prefill: {json.dumps(dec['model_prefill'])}", file=sys.stderr, flush=True)
         if not args.no_gqa_decode:
@@ -594,13 +606,7 @@ def main() -> int:
     }
     if dec is not None:
         dw = dec["w"]
-        line["decode"] = {
-            "workload": "llama-7b-shape model decode step, batch 32, KV cache 2047 positions, bf16",
-            "tokens_per_s": round(dec["tokens_per_s"], 1), "ms_per_step": round(dec["ms"], 4),
-            "ms_per_step_eager": round(dec["ms_eager"], 4), "hip_graph": dec["graph"],
-            "hbm_gbs": round(dec["hbm_gbs"], 1), "hbm_frac": round(dec["hbm_gbs"] / PEAK_HBM_GBS, 4),
-            "bytes_per_step": dec["bytes"], "roofline": dec["roofline"], "kernels_ms": dec["per_kernel_ms"],
-        }
+        line["decode"] = decode_summary(dec)
         if dec["model_prefill"] is not None:
             line["model_prefill"] = dec["model_prefill"]
     if gqa is not None:

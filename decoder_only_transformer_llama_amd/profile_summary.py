@@ -112,7 +112,23 @@ def trace_medians(d: str) -> Dict[str, float]:
     return out
 
 
-def write_stats(d: str, out: str, command: str, top: int) -> None:
+def _bench_line(path: str) -> Optional[dict]:
+    """The JSON line bench.py printed (the last line of the log that parses as an object)."""
+    import json
+    found = None
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("{"):
+                try:
+                    found = json.loads(line)
+                except ValueError:
+                    pass
+    return found
+
+
+def write_stats(d: str, out: str, command: str, top: int, bench_log: Optional[str] = None,
+                roofline: Optional[List[str]] = None) -> None:
     rows = stats_table(d)
     med = trace_medians(d)
     total = sum(r[2] for r in rows)
@@ -125,6 +141,27 @@ def write_stats(d: str, out: str, command: str, top: int) -> None:
         ms = f"{m / 1e3:10.2f}" if m is not None else f"{'-':>10}"
         lines.append(f"{avg / 1e3:10.2f} {ms} {calls:6d} {tot / 1e6:9.3f} {pct:6.2f}  {short_name(name)}")
     lines += ["", f"all kernels: {total / 1e6:.3f} ms over {sum(r[1] for r in rows)} dispatches"]
+    # roofline objects of the bench line printed by this same run, recomputed
+    # from the trace median of the kernel they name: (path in the line, kernel)
+    line = _bench_line(bench_log) if bench_log else None
+    if line is not None:
+        lines += ["", "bench.py line of this run (ms_per_step %s):" % line.get("ms_per_step")]
+        for spec in roofline or []:
+            path, kern = spec.split("=", 1)
+            obj = line
+            for key in path.split("."):
+                obj = obj.get(key, {}) if isinstance(obj, dict) else {}
+            m = [v for k, v in med.items() if kern in k]
+            if not obj or not m:
+                continue
+            per = obj.get("flops_per_launch") or obj.get("bytes_per_launch")
+            scale = 1e-3 if obj.get("unit") == "TFLOP/s" else 1.0   # per ns -> TFLOP/s (1e-3) or GB/s (1)
+            rec = per / m[0] * scale
+            lines += [f"  {path}: {obj.get('kernel')}",
+                      f"    line: achieved {obj.get('achieved')} {obj.get('unit')}, frac {obj.get('frac')}, "
+                      f"traffic {obj.get('traffic')}",
+                      f"    trace median of {kern!r}: {m[0] / 1e3:.2f} us -> {rec:.1f} {obj.get('unit')}, "
+                      f"frac {rec / obj.get('peak'):.4f}"]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
@@ -218,7 +255,9 @@ def write_counters(a) -> None:
     lines = ["# rocprofv3 counters per kernel (means per dispatch)", "", "commands:"] + ["  " + c for c in a.command]
     lines += ["", f"GPU: {int(xcc)} XCDs, {int(simds)} SIMDs, peak engine clock {mhz:.0f} MHz", "",
               "mfma_busy: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / XCDs * SIMDs), at the clock the kernel ran",
-              "clock: GRBM_GUI_ACTIVE / XCDs / dispatch duration under counters; peak_frac = mfma_busy * clock / peak clock",
+              "clock: GRBM_GUI_ACTIVE / XCDs / dispatch duration under counters ('-' where that exceeds the peak",
+              "  clock: for short kernels the GUI-active count includes time outside the dispatch)",
+              "peak_frac = mfma_busy * clock / peak clock: the fraction of the 2.5 PFLOP/s dense fp16/bf16 peak",
               "valu/mfma: (SQ_INSTS_VALU - SQ_INSTS_MFMA) / SQ_INSTS_MFMA (SQ_INSTS_VALU counts MFMAs too)",
               "lds_conf: SQ_LDS_BANK_CONFLICT cycles per SQ_INSTS_LDS instruction"]
     if f_fetch:
@@ -235,6 +274,8 @@ def write_counters(a) -> None:
         cyc = gui / xcc if gui else None
         fb = busy / (cyc * simds) if busy is not None and cyc else None
         clk = cyc / dur if cyc and dur else None
+        if clk is not None and clk > 1.05 * mhz / 1e3:
+            clk = None   # GUI-active cycles outside the dispatch dominate a short kernel: no clock estimate
         pf = fb * clk / (mhz / 1e3) if fb is not None and clk else None
         vpm = (c["SQ_INSTS_VALU"] - mf) / mf if mf and "SQ_INSTS_VALU" in c else None
         lc = c["SQ_LDS_BANK_CONFLICT"] / c["SQ_INSTS_LDS"] if c.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in c else None
@@ -278,6 +319,10 @@ def main() -> None:
     s.add_argument("out")
     s.add_argument("--command", required=True)
     s.add_argument("--top", type=int, default=25)
+    s.add_argument("--bench-log", help="output of the profiled bench.py run (its JSON line)")
+    s.add_argument("--roofline", action="append", default=[],
+                   help="PATH=KERNEL: a roofline object of the line (e.g. roofline or decode.roofline) and a "
+                        "substring of the kernel it times")
     t = sub.add_parser("traffic")
     t.add_argument("out")
     t.add_argument("--kernel", required=True)
@@ -302,7 +347,7 @@ def main() -> None:
     c.add_argument("--command", action="append", required=True)
     a = ap.parse_args()
     if a.cmd == "stats":
-        write_stats(a.dir, a.out, a.command, a.top)
+        write_stats(a.dir, a.out, a.command, a.top, a.bench_log, a.roofline)
     elif a.cmd == "counters":
         write_counters(a)
     else:
