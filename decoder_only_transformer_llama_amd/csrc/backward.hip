@@ -211,130 +211,203 @@ __global__ void attn_bwd_delta_kernel(const float *o, const float *dout, float *
   delta[idx] = acc;
 }
 
-constexpr int kBwdBK = 64;   // keys per tile
-constexpr int kBwdBQ = 32;   // queries per tile
+// Both gradient kernels run on the matrix cores (v_mfma_f32_32x32x2_f32)
+// over 32 x 32 tiles. A workgroup owns one 32-query tile (dQ) or one 32-key
+// tile (dK, dV); its four wavefronts take the other side's tiles in turn and
+// their sums are added in wavefront order at the end (deterministic). Each
+// wavefront stages its tiles in a private LDS region, rows padded by 4
+// floats so that the row-wise 16-byte operand reads of the 32 lanes of a
+// half-wave fall on distinct banks. The score-side products contract the head
+// dimension with half-wave g taking entries g*HD/2 .. g*HD/2 + HD/2 - 1; the
+// gradient products contract keys (or queries) in the order the accumulators
+// hold them (8*(kk/4) + 4g + kk%4 at step kk), so P and dS enter them straight
+// from the lane's registers.
+constexpr int kBwdT = 32;   // keys or queries per tile
 
-// Rows [r0, r0 + n) of head h of sequence b into an LDS tile [n][HD + 1];
-// rows past seq are zero.
-template <int HD>
-DEV void bwd_load_rows(float (*dst)[HD + 1], const float *src, int b, int h, int r0, int n, int seq,
-                       int n_heads) {
-  const int d = n_heads * HD;
-  for (int i = threadIdx.x; i < n * HD; i += 256) {
-    const int r = i / HD, e = i % HD;
-    const int row = r0 + r;
-    dst[r][e] = row < seq ? src[((int64_t)b * seq + row) * d + (int64_t)h * HD + e] : 0.f;
-  }
+DEV void bwd_wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Scores, probabilities and dS of 2 queries (rows 2*tq, 2*tq+1 of the query
-// tile) x 4 keys (rows 4*tk .. 4*tk+3 of the key tile), written to sP / sdS.
+// 16-byte piece it of rows [r0, r0 + 32) of head h (row past seq: the last row).
 template <int HD>
-DEV void bwd_scores(const float (*sQ)[HD + 1], const float (*sdO)[HD + 1], const float (*sK)[HD + 1],
-                    const float (*sV)[HD + 1], const float *sL, const float *sD, int q0, int k0, int seq,
-                    float scale, float (*sP)[kBwdBK + 1], float (*sdS)[kBwdBK + 1]) {
-  const int tq = threadIdx.x / 16, tk = threadIdx.x % 16;
-  float s[2][4] = {}, dp[2][4] = {};
-  for (int e = 0; e < HD; ++e) {
-    const float q0v = sQ[2 * tq][e], q1v = sQ[2 * tq + 1][e];
-    const float o0v = sdO[2 * tq][e], o1v = sdO[2 * tq + 1][e];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float kv = sK[4 * tk + j][e], vv = sV[4 * tk + j][e];
-      s[0][j] = fmaf(q0v, kv, s[0][j]);
-      s[1][j] = fmaf(q1v, kv, s[1][j]);
-      dp[0][j] = fmaf(o0v, vv, dp[0][j]);
-      dp[1][j] = fmaf(o1v, vv, dp[1][j]);
-    }
-  }
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int r = 2 * tq + a, qi = q0 + r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = 4 * tk + j, kj = k0 + c;
-      const bool ok = qi < seq && kj <= qi;   // kj < seq follows
-      const float p = ok ? expf(s[a][j] * scale - sL[r]) : 0.f;
-      if (sP) sP[r][c] = p;
-      sdS[r][c] = p * (dp[a][j] - sD[r]);
-    }
-  }
+DEV f32x4 bwd_piece(const float *src, int b, int h, int r0, int seq, int n_heads, int it) {
+  const int i = (threadIdx.x & 63) + 64 * it, row = i / (HD / 4), c = 4 * (i % (HD / 4));
+  return *(const f32x4 *)(src + ((int64_t)b * seq + min(r0 + row, seq - 1)) * n_heads * HD + (int64_t)h * HD + c);
+}
+template <int HD>
+DEV void bwd_put(float *dst, const f32x4 &v, int it) {
+  const int i = (threadIdx.x & 63) + 64 * it, row = i / (HD / 4), c = 4 * (i % (HD / 4));
+  *(f32x4 *)&dst[row * (HD + 4) + c] = v;
 }
 
-// Key/value gradients of one 64-key tile. The causal loop over query tiles
-// (those at or after the key tile) is split into gridDim.z contiguous ranges,
-// one per workgroup: with one range the tile's dk (scaled) and dv are stored;
-// with several, range z stores its unscaled sums to part[z] ([2][rows][d]:
-// dk then dv) and attn_bwd_kv_sum_kernel adds the ranges in order.
+// Score-side product of one 32 x 32 tile: C[m][n] = sum_e A[m][e] B[n][e], A
+// rows m from the LDS tile (row l32), B as the lane's own HD/2 entries.
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_kernel(const float *q, const float *k, const float *v,
-                                                            const float *dout, const float *lse,
-                                                            const float *delta, float *dk, float *dv, int seq,
-                                                            int n_heads, float scale, float *part) {
-  constexpr int CW = HD / 16;
-  __shared__ float sK[kBwdBK][HD + 1], sV[kBwdBK][HD + 1];
-  __shared__ float sQ[kBwdBQ][HD + 1], sdO[kBwdBQ][HD + 1];
-  __shared__ float sP[kBwdBQ][kBwdBK + 1], sdS[kBwdBQ][kBwdBK + 1];
-  __shared__ float sL[kBwdBQ], sD[kBwdBQ];
+DEV f32x16 bwd_rows_product(const float *tile, const float *breg) {
+  constexpr int HH = HD / 2;
+  const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
+  f32x16 c0, c1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c0[r] = c1[r] = 0.f;
+#pragma unroll
+  for (int j = 0; j < HH / 4; ++j) {
+    const f32x4 a = *(const f32x4 *)&tile[l32 * (HD + 4) + g * HH + 4 * j];
+    c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[0], breg[4 * j], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[1], breg[4 * j + 1], c1, 0, 0, 0);
+    c0 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[2], breg[4 * j + 2], c0, 0, 0, 0);
+    c1 = __builtin_amdgcn_mfma_f32_32x32x2f32(a[3], breg[4 * j + 3], c1, 0, 0, 0);
+  }
+  return c0 + c1;
+}
+
+// Gradient-side product: acc[e-block][...] += tile^T[e][row] * w[row][col],
+// contracting the 32 rows of the LDS tile in accumulator order, w[kk] from
+// the lane's registers.
+template <int HD, int NA, int OFF>
+DEV void bwd_cols_product(f32x16 (&acc)[NA], const float *tile, const float (&wv)[16]) {
+  const int lane = threadIdx.x & 63, g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int e = 0; e < HD / 32; ++e)
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const int row = 8 * (kk >> 2) + 4 * g + (kk & 3);
+      acc[OFF + e] =
+          __builtin_amdgcn_mfma_f32_32x32x2f32(tile[row * (HD + 4) + 32 * e + l32], wv[kk], acc[OFF + e], 0, 0, 0);
+    }
+}
+
+// Adds wavefronts 1..3's accumulators (NA of them, 16 floats per lane each)
+// into wavefront 0's, in order; returns false on wavefronts 1..3.
+template <int NA>
+DEV bool bwd_merge(f32x16 (&acc)[NA], float *lds, int stride) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (w > 0) {
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lds[w * stride + (a * 16 + r) * 64 + lane] = acc[a][r];
+  }
+  __syncthreads();
+  if (w > 0) return false;
+  for (int src = 1; src < 4; ++src)
+#pragma unroll
+    for (int a = 0; a < NA; ++a)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][r] += lds[src * stride + (a * 16 + r) * 64 + lane];
+  return true;
+}
+
+// Key/value gradients of one 32-key tile: dV^T = dO^T P and dK^T = Q^T dS over
+// the query tiles at or after it (causal). The query tiles are split into
+// gridDim.z contiguous ranges, one per workgroup: with one range the tile's
+// dk (scaled) and dv are stored; with several, range z stores its unscaled
+// sums to part[z] ([2][rows][d]: dk then dv) and attn_bwd_kv_sum_kernel adds
+// the ranges in order. Per query tile: S = Q K^T and dP = dO V^T (query rows,
+// a lane holds 16 queries of one key), P = exp(S scale - lse), dS = P (dP - D).
+template <int HD>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(const float *q, const float *k, const float *v,
+                                                               const float *dout, const float *lse,
+                                                               const float *delta, float *dk, float *dv, int seq,
+                                                               int n_heads, float scale, float *part) {
+  constexpr int HH = HD / 2, NEB = HD / 32, NV4 = kBwdT * HD / 4 / 64;
+  constexpr int TS = kBwdT * (HD + 4);   // floats of one staged tile
+  constexpr int WS = 2 * TS + 2 * kBwdT;  // per wavefront: Q, dO, lse, D
+  static_assert(2 * NEB * 16 * 64 <= WS, "merge buffer fits a wavefront's region");
+  __shared__ float lds[4 * WS];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y, b = bh / n_heads, h = bh % n_heads;
-  const int k0 = blockIdx.x * kBwdBK;
-  bwd_load_rows<HD>(sK, k, b, h, k0, kBwdBK, seq, n_heads);
-  bwd_load_rows<HD>(sV, v, b, h, k0, kBwdBK, seq, n_heads);
-  const int kq = threadIdx.x / 16, ce = threadIdx.x % 16;   // keys 4*kq.., channels ce*CW..
-  float accK[4][CW] = {}, accV[4][CW] = {};
-  const int nqt = (seq + kBwdBQ - 1) / kBwdBQ;
-  const int it0 = k0 / kBwdBQ, nit = nqt - it0, nz = gridDim.z, z = blockIdx.z;
-  const int ib = it0 + (int)((int64_t)nit * z / nz), ie = it0 + (int)((int64_t)nit * (z + 1) / nz);
-  for (int it = ib; it < ie; ++it) {   // causal: queries at or after the key tile, this range
-    const int q0 = it * kBwdBQ;
-    __syncthreads();   // the previous tile's readers are done (and sK/sV are loaded)
-    bwd_load_rows<HD>(sQ, q, b, h, q0, kBwdBQ, seq, n_heads);
-    bwd_load_rows<HD>(sdO, dout, b, h, q0, kBwdBQ, seq, n_heads);
-    if (threadIdx.x < kBwdBQ) {
-      const int qi = q0 + threadIdx.x;
-      sL[threadIdx.x] = qi < seq ? lse[(int64_t)bh * seq + qi] : 0.f;
-      sD[threadIdx.x] = qi < seq ? delta[(int64_t)bh * seq + qi] : 0.f;
-    }
-    __syncthreads();
-    bwd_scores<HD>(sQ, sdO, sK, sV, sL, sD, q0, k0, seq, scale, sP, sdS);
-    __syncthreads();
-    for (int r = 0; r < kBwdBQ; ++r) {
-      float pr[4], dsr[4];
+  const int k0 = blockIdx.x * kBwdT, kj = k0 + l32;
+  const int d = n_heads * HD;
+  float *sq = lds + w * WS, *so = sq + TS, *sl = so + TS, *sd = sl + kBwdT;
+  // this lane's key and value rows, entries g*HH .. (B operands of S and dP)
+  float kr[HH], vr[HH];
+  {
+    const int64_t base = ((int64_t)b * seq + min(kj, seq - 1)) * d + (int64_t)h * HD + g * HH;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        pr[j] = sP[r][4 * kq + j];
-        dsr[j] = sdS[r][4 * kq + j];
-      }
-#pragma unroll
-      for (int c = 0; c < CW; ++c) {
-        const float ov = sdO[r][ce * CW + c], qv = sQ[r][ce * CW + c];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          accV[j][c] = fmaf(pr[j], ov, accV[j][c]);
-          accK[j][c] = fmaf(dsr[j], qv, accK[j][c]);
-        }
-      }
+    for (int i = 0; i < HH; i += 4) {
+      *(f32x4 *)&kr[i] = *(const f32x4 *)(k + base + i);
+      *(f32x4 *)&vr[i] = *(const f32x4 *)(v + base + i);
     }
   }
-  const int d = n_heads * HD;
+  f32x16 acc[2 * NEB];   // dK^T blocks, then dV^T blocks
+#pragma unroll
+  for (int a = 0; a < 2 * NEB; ++a)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[a][r] = 0.f;
+  const int nqt = (seq + kBwdT - 1) / kBwdT;
+  const int it0 = k0 / kBwdT, nit = nqt - it0, nz = gridDim.z, z = blockIdx.z;
+  const int ib = it0 + (int)((int64_t)nit * z / nz), ie = it0 + (int)((int64_t)nit * (z + 1) / nz);
+  f32x4 qn[NV4], on[NV4];
+  float ln = 0.f, dn = 0.f;
+  auto load = [&](int it) {
+    const int q0 = it * kBwdT;
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      qn[i] = bwd_piece<HD>(q, b, h, q0, seq, n_heads, i);
+      on[i] = bwd_piece<HD>(dout, b, h, q0, seq, n_heads, i);
+    }
+    const int qi = min(q0 + l32, seq - 1);
+    ln = lse[(int64_t)bh * seq + qi];
+    dn = delta[(int64_t)bh * seq + qi];
+  };
+  // hd 128 keeps 2 x 64 key/value entries and 2 x 64 accumulators per lane:
+  // the next tile is then loaded after the current one is multiplied, not
+  // during (prefetching it as well spills)
+  constexpr bool kPrefetch = HD <= 64;
+  if (kPrefetch && ib + w < ie) load(ib + w);
+  for (int it = ib + w; it < ie; it += 4) {
+    const int q0 = it * kBwdT;
+    if (!kPrefetch) load(it);
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      bwd_put<HD>(sq, qn[i], i);
+      bwd_put<HD>(so, on[i], i);
+    }
+    if (g == 0) {
+      sl[l32] = ln;
+      sd[l32] = dn;
+    }
+    bwd_wave_sync();
+    if (kPrefetch) load(min(it + 4, ie - 1));
+    const f32x16 st = bwd_rows_product<HD>(sq, kr);   // S[query][key]
+    const f32x16 dp = bwd_rows_product<HD>(so, vr);   // dP[query][key]
+    float pw[16], dsw[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ql = 8 * (r >> 2) + 4 * g + (r & 3), qi = q0 + ql;
+      const bool ok = qi < seq && kj <= qi;
+      pw[r] = ok ? expf(st[r] * scale - sl[ql]) : 0.f;
+      dsw[r] = pw[r] * (dp[r] - sd[ql]);
+    }
+    bwd_cols_product<HD, 2 * NEB, NEB>(acc, so, pw);   // dV^T[e][key] += dO^T P
+    bwd_cols_product<HD, 2 * NEB, 0>(acc, sq, dsw);    // dK^T[e][key] += Q^T dS
+    bwd_wave_sync();
+  }
+  if (!bwd_merge<2 * NEB>(acc, lds, WS)) return;
+  if (kj >= seq) return;
   const int64_t rd = (int64_t)gridDim.y / n_heads * seq * d;   // rows x d of one gradient
   float *pk = part + (int64_t)z * 2 * rd, *pv = pk + rd;
+  const int64_t o = ((int64_t)b * seq + kj) * d + (int64_t)h * HD;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int kj = k0 + 4 * kq + j;
-    if (kj >= seq) continue;
-    const int64_t o = ((int64_t)b * seq + kj) * d + (int64_t)h * HD + ce * CW;
+  for (int e = 0; e < NEB; ++e)
 #pragma unroll
-    for (int c = 0; c < CW; ++c) {
+    for (int rq = 0; rq < 4; ++rq) {
+      const int e0 = 32 * e + 8 * rq + 4 * g;
+      const f32x4 vk = {acc[e][4 * rq], acc[e][4 * rq + 1], acc[e][4 * rq + 2], acc[e][4 * rq + 3]};
+      const f32x4 vv = {acc[NEB + e][4 * rq], acc[NEB + e][4 * rq + 1], acc[NEB + e][4 * rq + 2],
+                        acc[NEB + e][4 * rq + 3]};
       if (nz == 1) {
-        dk[o + c] = accK[j][c] * scale;
-        dv[o + c] = accV[j][c];
+        *(f32x4 *)(dk + o + e0) = vk * scale;
+        *(f32x4 *)(dv + o + e0) = vv;
       } else {
-        pk[o + c] = accK[j][c];
-        pv[o + c] = accV[j][c];
+        *(f32x4 *)(pk + o + e0) = vk;
+        *(f32x4 *)(pv + o + e0) = vv;
       }
     }
-  }
 }
 
 // dk = scale * (part[0].k + part[1].k + ...), dv = part[0].v + ..., ranges in order.
@@ -350,55 +423,80 @@ __global__ void attn_bwd_kv_sum_kernel(const float *part, int nz, int64_t rd, fl
   dv[i] = sv;
 }
 
+// Query gradients of one 32-query tile: dQ^T = K^T dS^T over the key tiles at
+// or before it. Per key tile: S^T = K Q^T and dP^T = V dO^T (key rows, a lane
+// holds 16 keys of one query), P^T = exp(S^T scale - lse), dS^T = P^T (dP^T - D).
 template <int HD>
-__global__ __launch_bounds__(256) void attn_bwd_dq_kernel(const float *q, const float *k, const float *v,
-                                                          const float *dout, const float *lse, const float *delta,
-                                                          float *dq, int seq, int n_heads, float scale) {
-  constexpr int CW = HD / 16;
-  __shared__ float sK[kBwdBK][HD + 1], sV[kBwdBK][HD + 1];
-  __shared__ float sQ[kBwdBQ][HD + 1], sdO[kBwdBQ][HD + 1];
-  __shared__ float sdS[kBwdBQ][kBwdBK + 1];
-  __shared__ float sL[kBwdBQ], sD[kBwdBQ];
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(const float *q, const float *k, const float *v,
+                                                             const float *dout, const float *lse, const float *delta,
+                                                             float *dq, int seq, int n_heads, float scale) {
+  constexpr int HH = HD / 2, NEB = HD / 32, NV4 = kBwdT * HD / 4 / 64;
+  constexpr int TS = kBwdT * (HD + 4);
+  constexpr int WS = 2 * TS;   // per wavefront: K, V
+  static_assert(NEB * 16 * 64 <= WS, "merge buffer fits a wavefront's region");
+  __shared__ float lds[4 * WS];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y, b = bh / n_heads, h = bh % n_heads;
-  const int q0 = blockIdx.x * kBwdBQ;
-  bwd_load_rows<HD>(sQ, q, b, h, q0, kBwdBQ, seq, n_heads);
-  bwd_load_rows<HD>(sdO, dout, b, h, q0, kBwdBQ, seq, n_heads);
-  if (threadIdx.x < kBwdBQ) {
-    const int qi = q0 + threadIdx.x;
-    sL[threadIdx.x] = qi < seq ? lse[(int64_t)bh * seq + qi] : 0.f;
-    sD[threadIdx.x] = qi < seq ? delta[(int64_t)bh * seq + qi] : 0.f;
-  }
-  const int tq = threadIdx.x / 16, tk = threadIdx.x % 16;   // queries 2*tq.., channels tk*CW..
-  float acc[2][CW] = {};
-  const int last = min(q0 + kBwdBQ, seq) - 1;                // causal: keys up to the last query
-  const int nkt = last / kBwdBK + 1;
-  for (int jt = 0; jt < nkt; ++jt) {
-    const int k0 = jt * kBwdBK;
-    __syncthreads();   // the previous tile's readers are done (and sQ/sdO/sL/sD are loaded)
-    bwd_load_rows<HD>(sK, k, b, h, k0, kBwdBK, seq, n_heads);
-    bwd_load_rows<HD>(sV, v, b, h, k0, kBwdBK, seq, n_heads);
-    __syncthreads();
-    bwd_scores<HD>(sQ, sdO, sK, sV, sL, sD, q0, k0, seq, scale, nullptr, sdS);
-    __syncthreads();
-    for (int kk = 0; kk < kBwdBK; ++kk) {
-      const float d0 = sdS[2 * tq][kk], d1 = sdS[2 * tq + 1][kk];
+  const int q0 = blockIdx.x * kBwdT, qi = q0 + l32;
+  const int d = n_heads * HD;
+  float *sk = lds + w * WS, *sv = sk + TS;
+  float qr[HH], dor[HH];
+  {
+    const int64_t base = ((int64_t)b * seq + min(qi, seq - 1)) * d + (int64_t)h * HD + g * HH;
 #pragma unroll
-      for (int c = 0; c < CW; ++c) {
-        const float kv = sK[kk][tk * CW + c];
-        acc[0][c] = fmaf(d0, kv, acc[0][c]);
-        acc[1][c] = fmaf(d1, kv, acc[1][c]);
-      }
+    for (int i = 0; i < HH; i += 4) {
+      *(f32x4 *)&qr[i] = *(const f32x4 *)(q + base + i);
+      *(f32x4 *)&dor[i] = *(const f32x4 *)(dout + base + i);
     }
   }
-  const int d = n_heads * HD;
+  const float lq = lse[(int64_t)bh * seq + min(qi, seq - 1)], dq_d = delta[(int64_t)bh * seq + min(qi, seq - 1)];
+  f32x16 acc[NEB];
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int qi = q0 + 2 * tq + a;
-    if (qi >= seq) continue;
-    const int64_t o = ((int64_t)b * seq + qi) * d + (int64_t)h * HD + tk * CW;
+  for (int e = 0; e < NEB; ++e)
 #pragma unroll
-    for (int c = 0; c < CW; ++c) dq[o + c] = acc[a][c] * scale;
+    for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
+  const int nkt = (min(q0 + kBwdT, seq) - 1) / kBwdT + 1;   // key tiles up to the tile's last query
+  f32x4 kn[NV4], vn[NV4];
+  auto load = [&](int kt) {
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      kn[i] = bwd_piece<HD>(k, b, h, kt * kBwdT, seq, n_heads, i);
+      vn[i] = bwd_piece<HD>(v, b, h, kt * kBwdT, seq, n_heads, i);
+    }
+  };
+  if (w < nkt) load(w);
+  for (int kt = w; kt < nkt; kt += 4) {
+#pragma unroll
+    for (int i = 0; i < NV4; ++i) {
+      bwd_put<HD>(sk, kn[i], i);
+      bwd_put<HD>(sv, vn[i], i);
+    }
+    bwd_wave_sync();
+    load(min(kt + 4, nkt - 1));
+    const f32x16 st = bwd_rows_product<HD>(sk, qr);    // S^T[key][query]
+    const f32x16 dp = bwd_rows_product<HD>(sv, dor);   // dP^T[key][query]
+    float dsw[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * kBwdT + 8 * (r >> 2) + 4 * g + (r & 3);
+      const bool ok = qi < seq && key <= qi;
+      const float p = ok ? expf(st[r] * scale - lq) : 0.f;
+      dsw[r] = p * (dp[r] - dq_d);
+    }
+    bwd_cols_product<HD, NEB, 0>(acc, sk, dsw);   // dQ^T[e][query] += K^T dS^T
+    bwd_wave_sync();
   }
+  if (!bwd_merge<NEB>(acc, lds, WS)) return;
+  if (qi >= seq) return;
+  float *op = dq + ((int64_t)b * seq + qi) * d + (int64_t)h * HD;
+#pragma unroll
+  for (int e = 0; e < NEB; ++e)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int e0 = 32 * e + 8 * rq + 4 * g;
+      *(f32x4 *)(op + e0) = f32x4{acc[e][4 * rq], acc[e][4 * rq + 1], acc[e][4 * rq + 2], acc[e][4 * rq + 3]} * scale;
+    }
 }
 
 hipError_t attn_bwd_launch(const float *q, const float *k, const float *v, const float *o, const float *dout,
@@ -412,8 +510,13 @@ hipError_t attn_bwd_launch(const float *q, const float *k, const float *v, const
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const float scale = 1.0f / sqrtf((float)head_dim);
-  const int nz = kv_part ? kAttnBwdKvRanges : 1;
-  const dim3 gkv((seq + kBwdBK - 1) / kBwdBK, batch * n_heads, nz), gq((seq + kBwdBQ - 1) / kBwdBQ, batch * n_heads);
+  // key-tile workgroups; split their query loops into ranges (when a partial
+  // buffer is given) only while there are fewer than one per compute unit
+  const int tiles = (seq + kBwdT - 1) / kBwdT;
+  int nz = 1;
+  if (kv_part)
+    while (nz < kAttnBwdKvRanges && (int64_t)tiles * batch * n_heads * nz < 256) nz *= 2;
+  const dim3 gkv(tiles, batch * n_heads, nz), gq(tiles, batch * n_heads);
   if (head_dim == 128) {
     hipLaunchKernelGGL(attn_bwd_dkdv_kernel<128>, gkv, dim3(256), 0, s, q, k, v, dout, lse, delta, dk, dv, seq,
                        n_heads, scale, kv_part);

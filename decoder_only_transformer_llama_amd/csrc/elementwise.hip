@@ -525,101 +525,174 @@ hipError_t silu_mul_f32_launch(const float *g, const float *u, float *out, int64
   return hipGetLastError();
 }
 
-// Causal attention in fp32 with online softmax. One workgroup per (query
-// tile of 32, sequence, head): 8 key groups of 32 lanes (two per wavefront),
-// all on the same 32 queries (one per lane), group g taking the keys
-// j = g mod 8 of every 64-key tile of K and V staged in LDS (the lanes of a
-// group read the same key row: broadcast). Each lane keeps the running (max,
-// sum, output) of its keys; the eight partial states of a query are merged in
-// group order at the end, so the result does not depend on timing. lse
+// Causal attention in fp32 on the matrix cores (v_mfma_f32_32x32x2_f32:
+// fp32 products and sums). One workgroup per (32-query tile, sequence, head);
+// its four wavefronts take the 32-key tiles at or before the diagonal in turn
+// (wavefront w: tiles w, w + 4, ...), each keeping the running (max, sum,
+// output) of its keys, and the four states of a query are merged in
+// wavefront order at the end, so the result does not depend on timing. lse
 // (optional) gets max + log(sum).
-constexpr int kAttnQ = 32, kAttnK = 64, kAttnG = 8;
+// Per key tile a wavefront computes S^T = K Q^T (32 keys x 32 queries): a lane
+// holds 16 keys of one query, so the softmax of a query reduces over the
+// lane and its partner half-wave. O^T += V^T P^T then contracts over the keys
+// in the order the accumulator holds them, so P enters the product straight
+// from the lane's registers. K and V tiles go through a wavefront-private LDS
+// region (rows padded so the half-waves' reads fall on distinct banks); the
+// next tile is loaded into registers while the current one is multiplied.
 template <int HD>
-__global__ __launch_bounds__(kAttnQ * kAttnG) void attn_f32_kernel(const float *q, const float *k, const float *v,
-                                                                   float *o, float *lse, int batch, int seq,
-                                                                   int n_heads) {
-  __shared__ float kv[2][kAttnK][HD];   // K and V tiles; after the loop, the merge buffer
-  const int lq = threadIdx.x % kAttnQ, grp = threadIdx.x / kAttnQ;
+__global__ __launch_bounds__(256, 1) void attn_f32_mfma_kernel(const float *q, const float *k, const float *v,
+                                                               float *o, float *lse, int batch, int seq,
+                                                               int n_heads) {
+  constexpr int KS = HD + 4, VS = HD + 8;   // LDS row strides (floats) of the K and V tiles
+  constexpr int TILE = 32 * KS + 32 * VS;   // floats per wavefront
+  constexpr int NEB = HD / 32;              // 32-wide blocks of the head dimension
+  constexpr int HH = HD / 2;                // head-dimension entries each half-wave contracts
+  constexpr int NV4 = 32 * HD / 4 / 64;     // 16-byte pieces per lane of one K (or V) tile
+  __shared__ float lds[4 * TILE];
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.y, b = bh / n_heads, h = bh % n_heads;
-  const int q0 = blockIdx.x * kAttnQ, qi = q0 + lq;
+  const int q0 = blockIdx.x * 32, qi = q0 + l32;
   const int d = n_heads * HD;
-  float qr[HD], acc[HD];
-  {
-    const float *qp = q + ((int64_t)b * seq + min(qi, seq - 1)) * d + h * HD;
-#pragma unroll
-    for (int e = 0; e < HD; ++e) {
-      qr[e] = qp[e];
-      acc[e] = 0.f;
-    }
-  }
+  float *sk = lds + w * TILE, *sv = sk + 32 * KS;
   const float sc = 1.0f / sqrtf((float)HD);
+
+  // this lane's query, head-dimension entries g*HH .. g*HH+HH-1 (the B operand of S^T)
+  float qr[HH];
+  {
+    const float *qp = q + ((int64_t)b * seq + min(qi, seq - 1)) * d + h * HD + g * HH;
+#pragma unroll
+    for (int i = 0; i < HH; i += 4) *(f32x4 *)&qr[i] = *(const f32x4 *)(qp + i);
+  }
+  f32x16 acc[NEB];
+#pragma unroll
+  for (int e = 0; e < NEB; ++e)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[e][r] = 0.f;
   float m = -INFINITY, l = 0.f;
-  const int kend = min(seq, q0 + kAttnQ);   // keys any query of the tile sees
-  for (int j0 = 0; j0 < kend; j0 += kAttnK) {
-    __syncthreads();   // everyone is done with the previous tile
-    for (int i = threadIdx.x; i < kAttnK * HD; i += kAttnQ * kAttnG) {   // rows past seq: zeros
-      const int r = i / HD, c = i % HD;
-      const int j = j0 + r;
-      const int64_t src = ((int64_t)b * seq + j) * d + h * HD + c;
-      kv[0][r][c] = j < seq ? k[src] : 0.f;
-      kv[1][r][c] = j < seq ? v[src] : 0.f;
-    }
-    __syncthreads();
-    for (int u = 0; u < kAttnK / kAttnG; ++u) {
-      const int jl = grp + kAttnG * u, j = j0 + jl;
-      if (j > qi || j >= seq) break;   // keys ascend: past the diagonal (or the end) for this lane
-      float sdot = 0.f;
+
+  const int nkt = min(q0 + 31, seq - 1) / 32 + 1;   // key tiles a query of the tile sees
+  // piece i of a tile: row i / (HD/4), 4 columns at 4 (i % (HD/4)); rows past seq load the last key
+  f32x4 kr[NV4], vr[NV4];
+  auto load = [&](int kt) {
 #pragma unroll
-      for (int e = 0; e < HD; ++e) sdot = fmaf(qr[e], kv[0][jl][e], sdot);
-      const float s = sdot * sc;
-      const float mn = fmaxf(m, s);
-      const float al = expf(m - mn), p = expf(s - mn);
-      l = l * al + p;
-#pragma unroll
-      for (int e = 0; e < HD; ++e) acc[e] = acc[e] * al + p * kv[1][jl][e];
-      m = mn;
+    for (int it = 0; it < NV4; ++it) {
+      const int i = lane + 64 * it, row = i / (HD / 4), c = 4 * (i % (HD / 4));
+      const int64_t src = ((int64_t)b * seq + min(kt * 32 + row, seq - 1)) * d + h * HD + c;
+      kr[it] = *(const f32x4 *)(k + src);
+      vr[it] = *(const f32x4 *)(v + src);
     }
+  };
+  auto wave_sync = [] {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if (w < nkt) load(w);
+  for (int kt = w; kt < nkt; kt += 4) {
+#pragma unroll
+    for (int it = 0; it < NV4; ++it) {
+      const int i = lane + 64 * it, row = i / (HD / 4), c = 4 * (i % (HD / 4));
+      *(f32x4 *)&sk[row * KS + c] = kr[it];
+      *(f32x4 *)&sv[row * VS + c] = vr[it];
+    }
+    wave_sync();
+    load(min(kt + 4, nkt - 1));   // the next tile (past the end: the last one again, unused)
+
+    // S^T[key][query]: A = K[key l32][g*HH + kk], B = Q[query l32][g*HH + kk]
+    f32x16 st[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st[0][r] = st[1][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < HH / 4; ++j) {
+      const f32x4 ka = *(const f32x4 *)&sk[l32 * KS + g * HH + 4 * j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)   // two independent chains
+        st[u & 1] = __builtin_amdgcn_mfma_f32_32x32x2f32(ka[u], qr[4 * j + u], st[u & 1], 0, 0, 0);
+    }
+    // online softmax of query qi over the tile's keys 8*(r/4) + 4g + r%4
+    float p[16];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = kt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+      p[r] = key <= qi && key < seq ? (st[0][r] + st[1][r]) * sc : -INFINITY;
+      mx = fmaxf(mx, p[r]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float mn = fmaxf(m, mx);   // finite: key kt*32 <= q0 <= qi is always seen
+    const float al = expf(m - mn);   // m = -inf before the first tile: 0
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      p[r] = expf(p[r] - mn);        // masked keys: exp(-inf) = 0
+      ps += p[r];
+    }
+    ps += __shfl_xor(ps, 32, 64);
+    l = l * al + ps;
+    m = mn;
+    // O^T[e][query] += V^T P^T: step kk contracts keys 8*(kk/4) + 4g + kk%4
+#pragma unroll
+    for (int e = 0; e < NEB; ++e) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[e][r] *= al;
+#pragma unroll
+      for (int kk = 0; kk < 16; ++kk) {
+        const int key = 8 * (kk >> 2) + 4 * g + (kk & 3);
+        acc[e] = __builtin_amdgcn_mfma_f32_32x32x2f32(sv[key * VS + 32 * e + l32], p[kk], acc[e], 0, 0, 0);
+      }
+    }
+    wave_sync();   // this tile's LDS reads are done before the next store
   }
-  // merge group g = 1, 2, 3 into group 0, in that order
-  float *xb = &kv[0][0][0];   // [32 queries][HD + 2]
-  for (int gsrc = 1; gsrc < kAttnG; ++gsrc) {
-    __syncthreads();
-    if (grp == gsrc) {
-      float *row = xb + lq * (HD + 2);
+
+  // merge wavefronts 1, 2, 3 into wavefront 0, in that order (same layout:
+  // element (e-block, r) of lane `lane`)
+  __syncthreads();
+  if (w > 0) {
+    float *buf = lds + w * TILE;
 #pragma unroll
-      for (int e = 0; e < HD; ++e) row[e] = acc[e];
-      row[HD] = m;
-      row[HD + 1] = l;
-    }
-    __syncthreads();
-    if (grp == 0) {
-      const float *row = xb + lq * (HD + 2);
-      const float m1 = row[HD], l1 = row[HD + 1];
-      const float mn = fmaxf(m, m1);
-      const float a0 = expf(m - mn), a1 = expf(m1 - mn);   // m1 = -inf (no keys): a1 = 0
-      l = l * a0 + l1 * a1;
+    for (int e = 0; e < NEB; ++e)
 #pragma unroll
-      for (int e = 0; e < HD; ++e) acc[e] = acc[e] * a0 + row[e] * a1;
-      m = mn;
-    }
+      for (int r = 0; r < 16; ++r) buf[(e * 16 + r) * 64 + lane] = acc[e][r];
+    buf[NEB * 16 * 64 + lane] = m;
+    buf[(NEB * 16 + 1) * 64 + lane] = l;
   }
-  if (grp != 0 || qi >= seq) return;
+  __syncthreads();
+  if (w != 0) return;
+  for (int src = 1; src < 4; ++src) {
+    const float *buf = lds + src * TILE;
+    const float m1 = buf[NEB * 16 * 64 + lane], l1 = buf[(NEB * 16 + 1) * 64 + lane];
+    const float mn = fmaxf(m, m1);
+    const float a0 = expf(m - mn), a1 = expf(m1 - mn);   // m1 = -inf (no tiles): a1 = 0
+    l = l * a0 + l1 * a1;
+#pragma unroll
+    for (int e = 0; e < NEB; ++e)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[e][r] = acc[e][r] * a0 + buf[(e * 16 + r) * 64 + lane] * a1;
+    m = mn;
+  }
+  if (qi >= seq) return;
   float *op = o + ((int64_t)b * seq + qi) * d + h * HD;
   const float inv = 1.0f / l;
 #pragma unroll
-  for (int e = 0; e < HD; ++e) op[e] = acc[e] * inv;
-  if (lse) lse[((int64_t)b * n_heads + h) * seq + qi] = m + logf(l);   // [batch][n_heads][seq]: the backward's statistic
+  for (int e = 0; e < NEB; ++e)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      const int e0 = 32 * e + 8 * rq + 4 * g;
+      *(f32x4 *)(op + e0) = f32x4{acc[e][4 * rq] * inv, acc[e][4 * rq + 1] * inv, acc[e][4 * rq + 2] * inv,
+                                  acc[e][4 * rq + 3] * inv};
+    }
+  if (lse && g == 0) lse[((int64_t)b * n_heads + h) * seq + qi] = m + logf(l);   // [batch][n_heads][seq]
 }
 
 hipError_t attn_f32_launch(const float *q, const float *k, const float *v, float *o, int batch, int seq,
                            int n_heads, int head_dim, hipStream_t s, float *lse) {
   if (batch * n_heads * seq == 0) return hipSuccess;
-  const dim3 grid((seq + kAttnQ - 1) / kAttnQ, batch * n_heads);
+  const dim3 grid((seq + 31) / 32, batch * n_heads);
   if (head_dim == 64)
-    hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(kAttnQ * kAttnG), 0, s, q, k, v, o, lse, batch, seq, n_heads);
+    hipLaunchKernelGGL(attn_f32_mfma_kernel<64>, grid, dim3(256), 0, s, q, k, v, o, lse, batch, seq, n_heads);
   else if (head_dim == 128)
-    hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(kAttnQ * kAttnG), 0, s, q, k, v, o, lse, batch, seq,
-                       n_heads);
+    hipLaunchKernelGGL(attn_f32_mfma_kernel<128>, grid, dim3(256), 0, s, q, k, v, o, lse, batch, seq, n_heads);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

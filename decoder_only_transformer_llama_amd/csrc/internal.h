@@ -247,7 +247,8 @@ hipError_t gemm_f32_strided_launch(const float *A, int64_t sam, int64_t sak, con
 // log-sum-exp lse [batch][n_heads][seq] and dout; delta: scratch of the lse's size.
 // kv_part: nullptr, or kAttnBwdKvRanges * 2 * batch * seq * n_heads * head_dim
 // floats of scratch, with which the key/value-gradient loop runs split over
-// that many workgroups per key tile.
+// up to that many workgroups per key tile while the key tiles alone make
+// fewer than 256 workgroups.
 constexpr int kAttnBwdKvRanges = 4;
 hipError_t attn_bwd_launch(const float *q, const float *k, const float *v, const float *o, const float *dout,
                            const float *lse, float *delta, float *dq, float *dk, float *dv, int batch, int seq,

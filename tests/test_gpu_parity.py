@@ -175,8 +175,12 @@ def test_causal_attn_bf16(B, S, H, hd):
         np.testing.assert_allclose(o[b * S].numpy(), host(v)[b * S], rtol=0, atol=2e-2)
 
 
-def test_causal_attn_f32():
-    B, S, H, hd = 2, 70, 2, 64
+@pytest.mark.parametrize("B,S,H,hd", [(2, 70, 2, 64), (1, 300, 2, 128), (1, 1, 1, 128), (3, 33, 1, 64),
+                                     (1, 257, 1, 128)])
+def test_causal_attn_f32(B, S, H, hd):
+    """fp32 causal attention (matrix-core tiles of 32 keys x 32 queries; four
+    wavefronts take the key tiles in turn): one query tile, ragged tails, more
+    key tiles than wavefronts, a single key."""
     w = I.Workload(905, "attn32", dim=H * hd, n_heads=H, hidden=0, batch=B, seq=S, dtype="f32")
     q, k, v = I.qkv_inputs(w, device="cuda")
     o = ops().causal_attn(q, k, v, B, S, H)
