@@ -68,15 +68,15 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   constexpr int VTILE = HD * 4;                  // u32x4 per v^T tile (4 chunks of 8 keys)
   constexpr int STAGE1 = KTILE * (QKPAIR ? 2 : 1) + VTILE * (VPAIR ? 2 : 1);   // one 32-key tile
   // Tiles per step (SUB): with fp16 operands two 32-key tiles share one
-  // barrier and one softmax update, so each step carries two independent
-  // score chains; the longest workgroups (the last query tiles, 2048 keys)
-  // then take half as many dependent steps.
+  // barrier and one softmax update (f16_step below), so each step carries two
+  // independent score chains; the longest workgroups (the last query tiles,
+  // 2048 keys) then take half as many dependent steps.
   constexpr int SUB = F16 ? 2 : 1;
   constexpr int STAGE = SUB * STAGE1;
-  // LDS ring depth: single fp16 operands (16 KB per tile at hd 128) keep
-  // two steps in flight with one tile per step, one with two; bf16
-  // pairs (32 KB per tile) stay at 2, so that two workgroups fit a compute unit.
-  constexpr int NST = (F16 && SUB == 1) ? 3 : 2;
+  // LDS ring depth 2 (64 KB at hd 128), so that two workgroups share a
+  // compute unit. (A third slot measured slower: loads are not what the
+  // steps wait on.)
+  constexpr int NST = 2;
   constexpr float kLazyRescale = 8.0f;   // log2 units a running maximum may lag the true one
   constexpr int KBLK = KTILE / 64, VBLK = VTILE / 64;       // 1 KB blocks per tile
   constexpr int NBLK = KBLK * (QKPAIR ? 2 : 1) + VBLK * (VPAIR ? 2 : 1);
@@ -187,6 +187,102 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   const int krow = perm23(l32);   // key (within the tile) this lane supplies as A-operand row
   for (int st = 1; st < NST - 1; ++st) issue(st);   // after the q fragments: they complete first
 
+  // One step of the fp16 path: SUB = 2 tiles of 32 keys in ring slot `stg`,
+  // keys s0 .. s0 + 63. Ordered so that latencies overlap inside the
+  // wavefront: every K fragment read is issued before the first product, the
+  // two tiles' score chains alternate on the matrix cores, the v^T fragments
+  // are read while the softmax runs, and the second tile's exponentials are
+  // computed while the first tile's P^T products run.
+  auto f16_step = [&](const u32x4 *stg, int s0) {
+    u32x4 kf[SUB][NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) kf[u][kk] = stg[u * STAGE1 + so];
+    }
+    f32x16 sc[SUB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[u][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) sc[u] = mfma32h(as_f16x8(kf[u][kk]), as_f16x8(qh[kk]), sc[u]);
+    // every K fragment read ahead of the first product (left alone, the
+    // compiler reuses two register quads and waits on each read in turn)
+    __builtin_amdgcn_sched_group_barrier(0x100, SUB * NKK, 0);   // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, SUB * NKK, 0);   // matrix-core products
+    u32x4 vf[SUB][2][NEB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int e = 0; e < NEB; ++e) {
+          const int row = 32 * e + l32;
+          vf[u][s2][e] = stg[u * STAGE1 + KTILE + row * 4 + ((2 * s2 + g) ^ vswz(row))];
+        }
+    // masked maximum of each tile (independent chains), then over both
+    // 32-lane halves of the wavefront (lanes l and l ^ 32 hold the same query)
+    float mxu[SUB];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const int kt0 = s0 + u * KT;
+      float m = -INFINITY;
+      if (kt0 + KT - 1 > p0 + q0 + 32 * w || kt0 + KT > nkeys) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt0 + 16 * ((r >> 2) >> 1) + 8 * g + 4 * ((r >> 2) & 1) + (r & 3);
+          const bool ok = key <= p0 + qi && key < nkeys;
+          sc[u][r] = ok ? sc[u][r] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, sc[u][r]);
+      mxu[u] = m;
+    }
+    float mx = mxu[0];
+#pragma unroll
+    for (int u = 1; u < SUB; ++u) mx = fmaxf(mx, mxu[u]);
+    {
+      // v_permlane32_swap: lanes l and l ^ 32 exchange values, no LDS round trip
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+      mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    // lazy rescaling, as below for bf16 operands
+    if (!__all((mx - m_run) * c <= kLazyRescale)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);   // -inf -> 0
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < NEB; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[e][r] *= alpha;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    const float mc = -m_use * c;   // exponent (s - m) c as one fma: s c - m c
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      float pr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][r], c, mc));   // exp2(-inf) = 0 for masked keys
+        ps[r & 3] += pr[r];
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const u32x4 pf = pack8h(pr + 8 * s2);
+#pragma unroll
+        for (int e = 0; e < NEB; ++e) acc_o[e] = mfma32h(as_f16x8(vf[u][s2][e]), as_f16x8(pf), acc_o[e]);
+      }
+    }
+    l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+  };
+
   for (int step = 0; step < n_st; ++step) {
     ATT_WAIT_VMCNT((NST - 2) * SUB * (NBLK / 4));   // this wavefront's loads of this step (and the q fragments)
     __builtin_amdgcn_s_barrier();                   // everyone's; everyone is done with the previous step
@@ -198,10 +294,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     const int s0 = step * SUB * KT;
     if (s0 > p0 + qwave_max) continue;   // whole step above this wavefront's diagonal
 
-    // ---- scores S^T (32 keys x 32 queries per tile). One tile per step: two
-    // accumulators (even and odd k-steps) so that two dependent matrix-core
-    // chains of half the length run interleaved; two tiles: one chain each.
-    constexpr int NACC = SUB == 1 ? 2 : 1;
+    if constexpr (F16) {
+      f16_step(smem + (step % NST) * STAGE, s0);
+      continue;
+    }
+    // ---- bf16 operands, one tile per step. Scores S^T (32 keys x 32
+    // queries): two accumulators (even and odd k-steps) so that two dependent
+    // matrix-core chains of half the length run interleaved.
+    constexpr int NACC = 2;
     f32x16 sc[SUB];
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
@@ -216,18 +316,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       for (int kk = 0; kk < NKK; ++kk) {
         const int so = krow * KCH + ((2 * kk + g) ^ rswz<KCH>(krow));
         f32x16 &acc = sacc[kk % NACC];
-        if (F16) {
-          acc = mfma32h(as_f16x8(sk[so]), as_f16x8(qh[kk]), acc);
-        } else {
-          const bf16x8 kf = as_bf16x8(sk[so]);
-          acc = mfma32(kf, as_bf16x8(qh[kk]), acc);
-          if (QKPAIR) {
-            acc = mfma32(as_bf16x8(skl[so]), as_bf16x8(qh[kk]), acc);
-            acc = mfma32(kf, as_bf16x8(ql[kk]), acc);
-          }
+        const bf16x8 kf = as_bf16x8(sk[so]);
+        acc = mfma32(kf, as_bf16x8(qh[kk]), acc);
+        if (QKPAIR) {
+          acc = mfma32(as_bf16x8(skl[so]), as_bf16x8(qh[kk]), acc);
+          acc = mfma32(kf, as_bf16x8(ql[kk]), acc);
         }
       }
-      sc[u] = NACC == 2 ? sacc[0] + sacc[NACC - 1] : sacc[0];
+      sc[u] = sacc[0] + sacc[1];
     }
 
     // ---- online softmax (fp32); lane holds 16 keys of query qi per tile.
@@ -289,18 +385,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
         float pv[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) pv[i] = sc[u][8 * s2 + i];
-        const u32x4 pf = F16 ? pack8h(pv) : pack8(pv);
+        const u32x4 pf = pack8(pv);
         const int ch = 2 * s2 + g;
 #pragma unroll
         for (int e = 0; e < NEB; ++e) {
           const int row = 32 * e + l32;
           const int so = row * 4 + (ch ^ vswz(row));
-          if (F16) {
-            acc_o[e] = mfma32h(as_f16x8(sv[so]), as_f16x8(pf), acc_o[e]);
-          } else {
-            acc_o[e] = mfma32(as_bf16x8(sv[so]), as_bf16x8(pf), acc_o[e]);
-            if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), as_bf16x8(pf), acc_o[e]);
-          }
+          acc_o[e] = mfma32(as_bf16x8(sv[so]), as_bf16x8(pf), acc_o[e]);
+          if (VPAIR) acc_o[e] = mfma32(as_bf16x8(svl[so]), as_bf16x8(pf), acc_o[e]);
         }
       }
     }
