@@ -466,8 +466,10 @@ DEV float lane_group_sum(float v) {
 
 constexpr int kMaxSeq = 2048;   // longest decode cache (positions) the attention kernel unrolls for
 
+// Launch bounds: four workgroups per compute unit (at most 128 registers; the
+// grouped-query instances would otherwise take 129 and fit only three).
 template <int HD, int G, int NS>
-__global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
+__global__ __launch_bounds__(256, 4) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
                                                        const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
                                                        u16 *a_lo, float *opart) {
   constexpr int LPK = HD / 8;          // lanes per key
@@ -475,6 +477,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
   constexpr int UNR = 2;               // key instructions per wavefront per step
   constexpr int KPS = 4 * KPW * UNR;   // keys per workgroup step
   constexpr int NG = 4 * KPW;          // lane groups per workgroup
+  constexpr float kLazyRescale = 8.0f;   // log2 units a running maximum may lag the true one
   // One workgroup per (key/value head hk, sequence b): the G query heads
   // hk*G .. hk*G+G-1 share its cached keys and values, which are read once.
   __shared__ float sq[G][HD], sknew[HD], svnew[HD];
@@ -572,7 +575,7 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float sc[UNR];
-      float mx = m_run[g];
+      float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
         float sdot = 0.f;
@@ -582,15 +585,23 @@ __global__ __launch_bounds__(256) void dec_attn_kernel(const DecodeArgs d, const
         sc[u] = live[u] ? sdot : -INFINITY;
         mx = fmaxf(mx, sc[u]);
       }
-      const float m_use = mx == -INFINITY ? 0.f : mx;
-      const float alpha = exp2f(m_run[g] - m_use);
-      m_run[g] = mx;
-      l_run[g] *= alpha;
+      // Lazy rescaling: the reference maximum m_run moves (and the running
+      // sum and output are rescaled) only when some lane's new maximum
+      // exceeds it by more than kLazyRescale (scores are in log2 units), so
+      // probabilities up to 2^kLazyRescale enter the sums; the merge below
+      // works from each group's reference. m_run = -inf always takes it.
+      if (!__all(mx <= m_run[g] + kLazyRescale)) {
+        const float m_new = fmaxf(m_run[g], mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[g] - (m_new == -INFINITY ? 0.f : m_new));   // -inf -> 0
+        m_run[g] = m_new;
+        l_run[g] *= alpha;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
+        for (int i = 0; i < 8; ++i) acc[g][i] *= alpha;
+      }
+      const float m_use = m_run[g] == -INFINITY ? 0.f : m_run[g];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const float pr = exp2f(sc[u] - m_use);
+        const float pr = __builtin_amdgcn_exp2f(sc[u] - m_use);   // raw v_exp_f32; exp2(-inf) = 0
         l_run[g] += pr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) acc[g][i] = fmaf(pr, vv[u][i], acc[g][i]);
@@ -685,14 +696,17 @@ __global__ void dec_attn_combine_kernel(const DecodeArgs d, const float *opart, 
   a_lo[idx] = lo;
 }
 
-// Key ranges per (key/value head, sequence): at least 512 workgroups (two per
-// compute unit). Measured on the 7B-shape decode step (batch 32, 2047 cached
-// positions): 8 key/value heads (256 pairs) take 2.79 / 2.22 / 2.39 / 2.48 ms
-// per step of attention with 1 / 2 / 4 / 8 ranges; 32 heads (1024 pairs) are
-// fastest unsplit (5.94 ms against 6.15 with 2 ranges).
+// Key ranges per (key/value head, sequence): at least 1024 workgroups (four
+// per compute unit; the kernel's launch bounds keep four resident). Measured
+// on the 7B-shape decode step (batch 32, 2047 cached positions) with 8
+// key/value heads (256 pairs): 2.79 / 2.22 / 2.39 / 2.48 ms per step of
+// attention with 1 / 2 / 4 / 8 ranges at three workgroups per compute unit;
+// with four resident, 4 ranges take 2.06-2.17 ms against 2.09-2.19 with 2.
+// 32 heads (1024 pairs) are fastest unsplit (5.94 ms against 6.15 with 2
+// ranges).
 int dec_attn_ranges(const DecodeArgs &d) {
   int ns = 1;
-  while (ns < kDecAttnMaxRanges && d.n_kv_heads * d.batch * ns < 512) ns *= 2;
+  while (ns < kDecAttnMaxRanges && d.n_kv_heads * d.batch * ns < 1024) ns *= 2;
   return ns;
 }
 
