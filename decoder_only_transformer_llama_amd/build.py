@@ -9,6 +9,7 @@ from __future__ import annotations
 import concurrent.futures as cf
 import glob
 import os
+import re
 import shutil
 import subprocess
 import sys
@@ -30,9 +31,28 @@ FLAGS = [
     # it to scratch memory; the remark below turns a refusal into a build error
     "-mllvm", "-pragma-unroll-threshold=262144",
     "-Rpass-missed=loop-unroll",
+    # per-kernel resource report: a kernel that spills registers to scratch
+    # memory fails the build (scratch loads also count against vmcnt, so one
+    # spill can make every wait on in-flight tile loads drain them all)
+    "-Rpass-analysis=kernel-resource-usage",
     "-Wno-unused-command-line-argument",
 ]
 UNROLL_REFUSED = "Unable to fully unroll loop as directed by unroll pragma"
+SCRATCH = re.compile(r"ScratchSize \[bytes/lane\]: ([0-9]+)")
+FUNC = re.compile(r"Function Name: (\S+)")
+
+
+def _scratch_kernels(log: str):
+    """Kernels whose resource report shows scratch memory per lane."""
+    bad, name = [], None
+    for line in log.splitlines():
+        m = FUNC.search(line)
+        if m:
+            name = m.group(1)
+        m = SCRATCH.search(line)
+        if m and int(m.group(1)) > 0:
+            bad.append(f"{name} ({m.group(1)} bytes/lane)")
+    return bad
 
 
 def _compile(src: str) -> str:
@@ -43,6 +63,9 @@ def _compile(src: str) -> str:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
     if UNROLL_REFUSED in r.stderr:
         raise RuntimeError(f"{src}: a '#pragma unroll' loop did not unroll fully:\n{r.stderr}")
+    bad = _scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels spill to scratch memory: " + ", ".join(bad))
     return obj
 
 

@@ -466,10 +466,11 @@ DEV float lane_group_sum(float v) {
 
 constexpr int kMaxSeq = 2048;   // longest decode cache (positions) the attention kernel unrolls for
 
-// Launch bounds: four workgroups per compute unit (at most 128 registers; the
-// grouped-query instances would otherwise take 129 and fit only three).
+// Launch bounds at head dim 128: four workgroups per compute unit (at most 128
+// registers; the grouped-query instances would otherwise take 129 and fit
+// only three). At head dim 64 that bound would spill, so two.
 template <int HD, int G, int NS>
-__global__ __launch_bounds__(256, 4) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
+__global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
                                                        const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
                                                        u16 *a_lo, float *opart) {
   constexpr int LPK = HD / 8;          // lanes per key

@@ -258,3 +258,19 @@ def test_decode_pack_reads_stay_inside_the_pack(wid):
     assert lib.llama_decode_pack_size(ctypes.byref(cfg), ctypes.byref(size)) == L.LLAMA_OK
     assert lib.llama_decode_pack_max_read(ctypes.byref(cfg), ctypes.byref(end)) == L.LLAMA_OK
     assert end.value == size.value, (end.value, size.value)
+
+
+def test_build_rejects_kernels_that_spill_to_scratch():
+    """The build parses hipcc's per-kernel resource report and names every
+    kernel with scratch memory per lane (a spill); kernels without it pass."""
+    from decoder_only_transformer_llama_amd import build as B
+    log = "\n".join([
+        "k.hip:1:1: remark: Function Name: _Z4goodv [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark: Function Name: _Z5spillv [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark:     VGPRs Spill: 1 [-Rpass-analysis=kernel-resource-usage]",
+        "k.hip:9:1: remark:     ScratchSize [bytes/lane]: 8 [-Rpass-analysis=kernel-resource-usage]",
+    ])
+    assert B._scratch_kernels(log) == ["_Z5spillv (8 bytes/lane)"]
+    assert B._scratch_kernels(log.split("\n_")[0]) == []
+    assert "-Rpass-analysis=kernel-resource-usage" in B.FLAGS
