@@ -577,7 +577,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
       } else if (EPI == EPI_SILU) {
 #pragma unroll
         for (int j = 0; j < G::TN; j += 2) {
-          const float u = silu(acc[i][j][r] * sc) * (acc[i][j + 1][r] * sc);
+          const float u = silu_fast(acc[i][j][r] * sc) * (acc[i][j + 1][r] * sc);
           const float un = lane_swap1(u);   // the next column's value (even lanes use it)
           if (l32 & 1) continue;
           const int col = (n0 >> 1) + wn * (G::WN / 2) + (j >> 1) * 32 + l32;
