@@ -73,11 +73,14 @@ struct GemmCfg {
   static constexpr int B_TILE = BN * CH;
   static constexpr int STAGE = A_TILE * (APAIR ? 2 : 1) + B_TILE;
   static constexpr int STAGE_BYTES = STAGE * 16;
-  static constexpr int STAGES = STAGE_BYTES * 5 <= 160 * 1024   ? 5
-                                : STAGE_BYTES * 4 <= 160 * 1024 ? 4
-                                : STAGE_BYTES * 3 <= 160 * 1024 ? 3
-                                                                : 2;
-  static_assert(STAGES * STAGE_BYTES <= 160 * 1024, "LDS ring exceeds 160 KB");
+  // the ring takes what the 160 KB of LDS leave beside the tile's row
+  // statistics (BM floats)
+  static constexpr int RING_MAX = 160 * 1024 - BM * 4;
+  static constexpr int STAGES = STAGE_BYTES * 5 <= RING_MAX   ? 5
+                                : STAGE_BYTES * 4 <= RING_MAX ? 4
+                                : STAGE_BYTES * 3 <= RING_MAX ? 3
+                                                              : 2;
+  static_assert(STAGES * STAGE_BYTES <= RING_MAX, "LDS ring exceeds its share of the 160 KB");
   static constexpr int A_LD = BM / RPL / NW;       // 1 KB loads per wavefront per A tile
   static constexpr int B_LD = BN / RPL / NW;
   static constexpr int LPS = A_LD * (APAIR ? 2 : 1) + B_LD;  // loads per stage per wavefront
@@ -124,7 +127,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   static_assert(!(F16 && APAIR), "fp16 operands are single");
   using G = GemmCfg<BN, APAIR>;
   constexpr int BM = G::BM, BK = G::BK, CH = G::CH, STAGES = G::STAGES;
-  __shared__ u32x4 smem[STAGES * G::STAGE];
+  // the LDS ring at offset 0, then the tile's rows' rstd (1 where there is
+  // none), staged once: read per element from global memory, each epilogue
+  // load was a dependent round trip
+  __shared__ u32x4 smem[STAGES * G::STAGE + BM / 4];
+  float *const s_rstd = (float *)(smem + STAGES * G::STAGE);
 
   // the wavefront index as a scalar: LDS destinations of the direct loads are then scalar sums
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -274,8 +281,14 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   // the last step into buffers nobody reads, so the body has no branches.
   constexpr int NS = BK / 16;
   static_assert(NS % 2 == 0, "the last substep's fragments are f[1]");
+  // row statistic of tile row tid: loaded ahead of the prologue's tile loads,
+  // so that waiting for it below overlaps them
+  float rs_tid = 1.0f;
+  if (a.rstd && tid < BM) rs_tid = a.rstd[min(m0 + tid, a.M - 1)];
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s);
+  if (tid < BM) s_rstd[tid] = rs_tid;
+  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the statistics are in LDS before the barrier
   WAIT_VMCNT((STAGES - 2) * G::LPS);
   __builtin_amdgcn_s_barrier();
   Frag f[2];
@@ -334,7 +347,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = mb + 8 * (r >> 2) + 4 * g + (r & 3);
-          sc[r] = (a.rstd && row < a.M) ? a.rstd[row] : 1.0f;
+          sc[r] = s_rstd[min(row, a.M - 1) - m0];
         }
 #pragma unroll
         for (int j = 0; j < G::TN; ++j) {
@@ -433,7 +446,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
       const int b = ok ? row / a.seq : 0;
       const int cs = ok ? chunk_start(a.start_pos, b, a.seq, a.max_seq) : 0;
       const int s = ok ? row - b * a.seq + max(cs, 0) : 0;   // the row's position
-      const float sc = (a.rstd && ok) ? a.rstd[row] : 1.0f;
+      const float sc = s_rstd[min(row, a.M - 1) - m0];
       const float2 *tab = a.rope_tab + (int64_t)s * (a.head_dim >> 1);
       // k row: by position within the sequence's kv_rows when continuing a prefix
       const int64_t krow = a.start_pos ? (int64_t)b * a.kv_rows + s : row;
@@ -530,7 +543,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
           const int row = rb + 8 * q + r8;
           if (row >= a.M) continue;
           f32x4 x = v[q];
-          if (a.rstd) x *= a.rstd[row];
+          x *= s_rstd[row - m0];
           if (EPI == EPI_PARTIAL) {
             *(f32x4 *)(a.part + (int64_t)blockIdx.y * a.M * a.N + (int64_t)row * a.N + col) = x;
             continue;
@@ -566,7 +579,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
     for (int r = 0; r < 16; ++r) {
       const int row = m0 + wm * G::WM + i * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
       if (row >= a.M) continue;
-      const float sc = a.rstd ? a.rstd[row] : 1.0f;
+      const float sc = s_rstd[row - m0];
       if (EPI == EPI_PARTIAL) {
         float *out = a.part + (int64_t)blockIdx.y * a.M * a.N + (int64_t)row * a.N;
 #pragma unroll
