@@ -508,6 +508,59 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
     return;
   }
 
+  // SiLU(gate) * up, row-contiguous: each 32-column block of u goes through
+  // the same per-wavefront LDS tile as the stores below and leaves as 8-byte
+  // (fp16) or 8 + 8-byte (bf16 hi/lo) row segments, 4 per lane and block,
+  // instead of 4-byte stores from every other lane.
+  if (EPI == EPI_SILU && a.ldc % 4 == 0 && (((uintptr_t)a.C | (uintptr_t)a.C_lo) % 8) == 0) {
+    __builtin_amdgcn_s_barrier();  // all waves are done with the K-loop buffers
+    constexpr int TQ = 40;         // row stride (floats): the two half-waves write disjoint banks
+    float *tq = (float *)smem + wave * (32 * TQ);
+    const int r8 = lane >> 3, c4 = 4 * (lane & 7);
+    const int hidden = a.N >> 1;
+#pragma unroll
+    for (int i = 0; i < G::TM; ++i) {
+      const int rb = m0 + wm * G::WM + i * 32;   // first row of the block
+      float scr[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) scr[r] = s_rstd[min(rb + 8 * (r >> 2) + 4 * g + (r & 3), a.M - 1) - m0];
+#pragma unroll
+      for (int jp = 0; jp < G::TN / 2; ++jp) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          tq[(8 * (r >> 2) + 4 * g + (r & 3)) * TQ + l32] =
+              silu_fast(acc[i][2 * jp][r] * scr[r]) * (acc[i][2 * jp + 1][r] * scr[r]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        f32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = *(const f32x4 *)(tq + (8 * q + r8) * TQ + c4);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();   // the tile is rewritten for the next block
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int col = (n0 >> 1) + wn * (G::WN / 2) + jp * 32 + c4;   // hidden % 32 == 0
+        if (col >= hidden) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = rb + 8 * q + r8;
+          if (row >= a.M) continue;
+          const int64_t o = (int64_t)row * a.ldc + col;
+          if (a.c_f16) {
+            *(u32x2 *)((u16 *)a.C + o) = u32x2{pack2h(v[q][0], v[q][1]), pack2h(v[q][2], v[q][3])};
+          } else {
+            u16 h[4], l[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) split_pair(v[q][k], h[k], l[k]);
+            *(u32x2 *)((u16 *)a.C + o) = u32x2{h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16)};
+            if (a.C_lo) *(u32x2 *)(a.C_lo + o) = u32x2{l[0] | ((uint32_t)l[1] << 16), l[2] | ((uint32_t)l[3] << 16)};
+          }
+        }
+      }
+    }
+    return;
+  }
+
   // Row-contiguous stores (RESID, PARTIAL, STORE): each 32 x 32 accumulator
   // block goes through a per-wavefront LDS tile and comes back as 8 rows per
   // instruction, 8 lanes per row, 4 consecutive columns per lane: every
