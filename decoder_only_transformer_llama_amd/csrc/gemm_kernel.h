@@ -450,6 +450,15 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
       const float2 *tab = a.rope_tab + (int64_t)s * (a.head_dim >> 1);
       // k row: by position within the sequence's kv_rows when continuing a prefix
       const int64_t krow = a.start_pos ? (int64_t)b * a.kv_rows + s : row;
+      // (cos, sin) of every block's 8 pairs, loaded ahead of the transposes
+      // (the fences around them would otherwise expose each load's latency)
+      f32x4 csv[G::TN][4];
+#pragma unroll
+      for (int j = 0; j < G::TN; ++j) {
+        const int e0 = (n0 + wn * G::WN + j * 32 + c0 - seg_base) & (a.head_dim - 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) csv[j][q] = *(const f32x4 *)(tab + (e0 >> 1) + 2 * q);
+      }
 #pragma unroll
       for (int j = 0; j < G::TN; ++j) {
 #pragma unroll
@@ -473,7 +482,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
         float rot[16];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const f32x4 cs2 = *(const f32x4 *)(tab + (e0 >> 1) + 2 * q);   // (cos, sin) of 2 pairs
+          const f32x4 cs2 = csv[j][q];   // (cos, sin) of 2 pairs
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
             const float x0 = v[4 * q + 2 * h], x1 = v[4 * q + 2 * h + 1];
@@ -578,6 +587,25 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
       const int rb = m0 + wm * G::WM + i * 32;   // first row of the block
 #pragma unroll
       for (int j = 0; j < G::TN; ++j) {
+        const int col = n0 + wn * G::WN + j * 32 + c4;   // N % 32 == 0: the block is inside or outside
+        // the residual rows of this block, loaded ahead of the transpose (the
+        // fences around it would otherwise expose each load's latency);
+        // rows and columns past the matrix read its first row instead
+        f32x4 res[4];
+        if (EPI == EPI_RESID) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = rb + 8 * q + r8;
+            const int64_t o = (row < a.M && col < a.N) ? (int64_t)row * a.ldc + col : 0;
+            if (a.r_f32) {
+              res[q] = *(const f32x4 *)((const float *)a.R + o);
+            } else {
+              const u32x2 r2 = *(const u32x2 *)((const u16 *)a.R + o);
+              res[q] = f32x4{__uint_as_float(r2[0] << 16), __uint_as_float(r2[0] & 0xffff0000u),
+                             __uint_as_float(r2[1] << 16), __uint_as_float(r2[1] & 0xffff0000u)};
+            }
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) tq[(8 * (r >> 2) + 4 * g + (r & 3)) * TQ + l32] = acc[i][j][r];
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -589,7 +617,6 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();   // the tile is rewritten for the next block
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int col = n0 + wn * G::WN + j * 32 + c4;   // N % 32 == 0: the block is inside or outside
         if (col >= a.N) continue;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -602,15 +629,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
             continue;
           }
           const int64_t o = (int64_t)row * a.ldc + col;
-          if (EPI == EPI_RESID) {
-            if (a.r_f32) {
-              x += *(const f32x4 *)((const float *)a.R + o);
-            } else {
-              const u32x2 r2 = *(const u32x2 *)((const u16 *)a.R + o);
-              x += f32x4{__uint_as_float(r2[0] << 16), __uint_as_float(r2[0] & 0xffff0000u),
-                         __uint_as_float(r2[1] << 16), __uint_as_float(r2[1] & 0xffff0000u)};
-            }
-          }
+          if (EPI == EPI_RESID) x += res[q];
           if (EPI == EPI_RESID || a.c_f32) {
             *(f32x4 *)((float *)a.C + o) = x;
           } else {
