@@ -160,6 +160,32 @@ int plan_qkv(int M, int d, int kvd, ColPart parts[2]) {
   return 1;
 }
 
+// Column ranges of the gate/up GEMM: whole rounds of 256 x 256 tiles over the
+// CUs, and when the columns left over make a partial round whose tiles still
+// fit one round as 192 x 256 tiles (three quarters of the work each), those
+// columns as 192 x 256 tiles: the last round then takes about three quarters
+// of a tile's time instead of a whole one. (7B shape: 688 tiles = 2 rounds
+// of 512 + 176; the 22 last column tiles become 11 x 22 = 242 tiles of 192.)
+struct FfnPart {
+  int bm, n_base, n_end;
+};
+int plan_ffn(int M, int N, bool apair, FfnPart parts[2]) {
+  const int cus = cu_count();
+  const int tm = (M + 255) / 256, tn = (N + 255) / 256;
+  const int total = tm * tn, full = total / cus, rem = total - full * cus;
+  if (!apair && N % 256 == 0 && full > 0 && rem > 0 && rem % tm == 0) {
+    const int rem_cols = rem / tm;
+    if ((long)((M + 191) / 192) * rem_cols <= cus) {
+      const int n1 = N - rem_cols * 256;
+      parts[0] = {256, 0, n1};
+      parts[1] = {192, n1, N};
+      return 2;
+    }
+  }
+  parts[0] = {256, 0, N};
+  return 1;
+}
+
 // Tiling of a GEMM whose epilogue adds the residual (O and down projections):
 // 256 x 128 tiles, 256 x 256 tiles, or 256 x 256 tiles with K split in two
 // (partial products added in order by the consumer). The cost model counts
@@ -629,7 +655,15 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   f.C_lo = dpair ? b.u_lo : nullptr;
   f.c_f16 = df16;   // u in the format the down projection takes
   f.ldc = c->hidden;
-  HIP_TRY(gemm_launch(GemmKey{256, ffn_pair, EPI_SILU, ff16 * wf}, f, s), "gate/up projection");
+  FfnPart fp[2];
+  const int nfp = plan_ffn(M, f.N, ffn_pair, fp);
+  for (int i = 0; i < nfp; ++i) {
+    f.n_base = fp[i].n_base;
+    f.n_end = fp[i].n_end;
+    GemmKey fk{256, ffn_pair, EPI_SILU, ff16 * wf};
+    fk.bm = fp[i].bm;
+    HIP_TRY(gemm_launch(fk, f, s), "gate/up projection");
+  }
 
   GemmArgs dn{};
   dn.M = M;
@@ -1075,7 +1109,15 @@ int llama_swiglu_ffn(int in_dtype, int out_dtype, const void *z, const void *w_g
   f.C = uh;
   f.C_lo = ul;
   f.ldc = hidden;
-  HIP_TRY(gemm_launch(GemmKey{256, 0, EPI_SILU}, f, s), "gate/up projection");
+  FfnPart fp[2];
+  const int nfp = plan_ffn(M, f.N, false, fp);
+  for (int i = 0; i < nfp; ++i) {
+    f.n_base = fp[i].n_base;
+    f.n_end = fp[i].n_end;
+    GemmKey fk{256, 0, EPI_SILU};
+    fk.bm = fp[i].bm;
+    HIP_TRY(gemm_launch(fk, f, s), "gate/up projection");
+  }
   GemmArgs dn{};
   dn.M = M;
   dn.N = dim;

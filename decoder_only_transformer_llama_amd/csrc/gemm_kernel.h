@@ -55,11 +55,14 @@ namespace llama {
 
 constexpr int kGemmWaves = 8;   // wavefronts per workgroup, two per SIMD
 
-template <int BN, bool APAIR>
+template <int BN, bool APAIR, int BMT = 256>
 struct GemmCfg {
   // K step: 64 for single operands; hi/lo pairs keep 32 (a 64-deep stage
-  // with A_lo would not fit two stages in LDS)
-  static constexpr int BM = 256, BK = APAIR ? 32 : 64;
+  // with A_lo would not fit two stages in LDS). Tiles are 256 rows, or 192
+  // (a 2 x 4 grid of 96 x 64 wavefront tiles) for the round that finishes a
+  // launch whose last round would otherwise run mostly empty.
+  static_assert(BMT == 256 || (BMT == 192 && BN == 256 && !APAIR), "tile heights 256, or 192 x 256 single");
+  static constexpr int BM = BMT, BK = APAIR ? 32 : 64;
   static constexpr int CH = BK / 8;                // 16-byte chunks per LDS row
   static constexpr int RPL = 64 / CH;              // rows per 1 KB wavefront load
   // Wavefront grid MW (M) x NW/MW (N): 128 x 64 wavefront tiles for 256-wide
@@ -122,10 +125,10 @@ DEV void interleave() {
 // activations at the bf16 rate. F16 2: A and B both hold fp16 (B converted
 // once, ahead of time, by the same rule), so the products see the same bits
 // as with F16 1 without the 3 VALU instructions per two weights.
-template <int BN, bool APAIR, int EPI, int F16 = 0>
+template <int BN, bool APAIR, int EPI, int F16 = 0, int BMT = 256>
 __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const GemmArgs a) {
   static_assert(!(F16 && APAIR), "fp16 operands are single");
-  using G = GemmCfg<BN, APAIR>;
+  using G = GemmCfg<BN, APAIR, BMT>;
   constexpr int BM = G::BM, BK = G::BK, CH = G::CH, STAGES = G::STAGES;
   // the LDS ring at offset 0, then the tile's rows' rstd (1 where there is
   // none), staged once: read per element from global memory, each epilogue
@@ -700,9 +703,9 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   }
 }
 
-template <int BN, bool APAIR, int EPI, int F16 = 0>
+template <int BN, bool APAIR, int EPI, int F16 = 0, int BMT = 256>
 hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
-  using G = GemmCfg<BN, APAIR>;
+  using G = GemmCfg<BN, APAIR, BMT>;
   const int n_end = a.n_end > 0 ? a.n_end : a.N;
   if (a.n_base < 0 || a.n_base % BN || n_end > a.N || n_end <= a.n_base) return hipErrorInvalidValue;
   const int nb = ((a.M + G::BM - 1) / G::BM) * ((n_end - a.n_base + BN - 1) / BN);
@@ -710,17 +713,24 @@ hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   const int ks = a.k_splits > 1 ? a.k_splits : 1;
   if (a.K % (G::BK * ks)) return hipErrorInvalidValue;
   if (ks > 1 && EPI != EPI_PARTIAL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI, F16>), dim3(nb, ks), dim3(G::NW * 64), 0, s, a);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI, F16, BMT>), dim3(nb, ks), dim3(G::NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
 }  // namespace llama
 
 #define GEMM_CASE(BN_, APAIR_, EPI_)                                                       \
-  if (key.bn == BN_ && key.apair == APAIR_ && key.epi == EPI_ && !key.f16)                  \
+  if (key.bm == 256 && key.bn == BN_ && key.apair == APAIR_ && key.epi == EPI_ && !key.f16) \
     return gemm_launch_t<BN_, APAIR_, EPI_>(a, s);
 #define GEMM_CASE_F16(BN_, EPI_)                                                           \
-  if (key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16 == 1)                       \
+  if (key.bm == 256 && key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16 == 1)      \
     return gemm_launch_t<BN_, false, EPI_, 1>(a, s);                                       \
-  if (key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16 == 2)                       \
+  if (key.bm == 256 && key.bn == BN_ && !key.apair && key.epi == EPI_ && key.f16 == 2)      \
     return gemm_launch_t<BN_, false, EPI_, 2>(a, s);
+// 192 x 256 tiles (single operands), every operand precision
+#define GEMM_CASE_192(EPI_)                                                                \
+  if (key.bm == 192 && key.bn == 256 && !key.apair && key.epi == EPI_) {                    \
+    if (key.f16 == 0) return gemm_launch_t<256, false, EPI_, 0, 192>(a, s);                 \
+    if (key.f16 == 1) return gemm_launch_t<256, false, EPI_, 1, 192>(a, s);                 \
+    if (key.f16 == 2) return gemm_launch_t<256, false, EPI_, 2, 192>(a, s);                 \
+  }

@@ -78,6 +78,7 @@ struct GemmKey {
   int bn, apair, epi;
   int f16 = 0;   // 1: A operand fp16, B (bf16 weights) converted to fp16 in registers;
                  // 2: A and B (weights converted ahead of time) both fp16
+  int bm = 256;  // tile rows: 256, or 192 (256-wide single-operand SiLU tiles)
 };
 
 // Returns a hipError_t; hipErrorInvalidValue when no instance matches `key`.
