@@ -225,9 +225,13 @@ def bench_prefill(args, torch):
         "w": w, "ms": ms, "ms_graph": ms_graph, "tokens_per_s": w.tokens / (ms * 1e-3),
         "block_tflops": total / (ms * 1e-3) / 1e12,
         "per_kernel": per_kernel,
+        # the gate/up GEMM runs as its launches of one step: whole rounds of
+        # 256 x 256 tiles, then (7B) the last round's columns as 192 x 256 tiles
         "roofline": {"bound": "mfma", "kernel": "gate/up GEMM (fp16 h*g2 x fp16 weights on the fp16 matrix cores; "
-                                                "rstd row scale + SiLU*up epilogue)" if not args.bf16_weights else
-                     "gate/up GEMM (fp16 h*g2 x bf16 weights converted in registers; rstd row scale + SiLU*up epilogue)",
+                                                "rstd row scale + SiLU*up epilogue; 256- and 192-row tile launches)"
+                     if not args.bf16_weights else
+                     "gate/up GEMM (fp16 h*g2 x bf16 weights converted in registers; rstd row scale + SiLU*up "
+                     "epilogue; 256- and 192-row tile launches)",
                      "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic("gate_up"),
                      "flops_per_launch": fl[dom]},

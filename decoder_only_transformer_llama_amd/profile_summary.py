@@ -151,38 +151,46 @@ def write_stats(d: str, out: str, command: str, top: int, bench_log: Optional[st
             obj = line
             for key in path.split("."):
                 obj = obj.get(key, {}) if isinstance(obj, dict) else {}
-            m = [v for k, v in med.items() if kern in k]
-            if not obj or not m:
+            # KERNEL may be several '+'-joined substrings (one launch each, all
+            # timed together by the line): their trace medians add up
+            parts = kern.split("+")
+            m = [[v for k, v in med.items() if part in k] for part in parts]
+            if not obj or not all(m):
                 continue
+            t_ns = sum(x[0] for x in m)
             per = obj.get("flops_per_launch") or obj.get("bytes_per_launch")
             scale = 1e-3 if obj.get("unit") == "TFLOP/s" else 1.0   # per ns -> TFLOP/s (1e-3) or GB/s (1)
-            rec = per / m[0] * scale
+            rec = per / t_ns * scale
             lines += [f"  {path}: {obj.get('kernel')}",
                       f"    line: achieved {obj.get('achieved')} {obj.get('unit')}, frac {obj.get('frac')}, "
                       f"traffic {obj.get('traffic')}",
-                      f"    trace median of {kern!r}: {m[0] / 1e3:.2f} us -> {rec:.1f} {obj.get('unit')}, "
-                      f"frac {rec / obj.get('peak'):.4f}"]
+                      f"    trace median of {' + '.join(repr(p) for p in parts)}: {t_ns / 1e3:.2f} us -> "
+                      f"{rec:.1f} {obj.get('unit')}, frac {rec / obj.get('peak'):.4f}"]
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
 def write_traffic(a) -> None:
-    fetch, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", a.kernel)
-    write, nw = counter_per_dispatch(a.write, "WRITE_SIZE", a.kernel)
+    # one or more kernels (--kernel repeated: the launches of one step, e.g. a
+    # GEMM split into two column ranges); their per-dispatch means add up
     cf, ncf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
     cw, ncw = counter_per_dispatch(a.copy_write, "WRITE_SIZE", a.copy_kernel)
     f_fetch = cf * 1024.0 / a.copy_bytes
     f_write = cw * 1024.0 / a.copy_bytes
-    traffic = fetch * 1024.0 / f_fetch + write * 1024.0 / f_write
+    traffic, per_kernel = 0.0, []
+    for k in a.kernel:
+        fetch, nf = counter_per_dispatch(a.fetch, "FETCH_SIZE", k)
+        write, nw = counter_per_dispatch(a.write, "WRITE_SIZE", k)
+        traffic += fetch * 1024.0 / f_fetch + write * 1024.0 / f_write
+        per_kernel += [f"{k}:",
+                       f"  FETCH_SIZE per dispatch: {fetch:.1f} KiB (mean of {nf} dispatches)",
+                       f"  WRITE_SIZE per dispatch: {write:.1f} KiB (mean of {nw} dispatches)"]
     lines = [
         "# HBM traffic per launch from rocprofv3 counters",
         "",
-        f"kernel: {a.kernel}",
+        f"kernel: {' + '.join(a.kernel)}",
         "commands:",
-    ] + ["  " + c for c in a.command] + [
-        "",
-        f"FETCH_SIZE per dispatch: {fetch:.1f} KiB (mean of {nf} dispatches)",
-        f"WRITE_SIZE per dispatch: {write:.1f} KiB (mean of {nw} dispatches)",
+    ] + ["  " + c for c in a.command] + [""] + per_kernel + [
         f"copy calibration ({a.copy_kernel}, {a.copy_bytes} bytes read and written per dispatch):",
         f"  FETCH_SIZE {cf:.1f} KiB over {ncf} dispatches -> factor {f_fetch:.4f}",
         f"  WRITE_SIZE {cw:.1f} KiB over {ncw} dispatches -> factor {f_write:.4f}",
@@ -322,10 +330,11 @@ def main() -> None:
     s.add_argument("--bench-log", help="output of the profiled bench.py run (its JSON line)")
     s.add_argument("--roofline", action="append", default=[],
                    help="PATH=KERNEL: a roofline object of the line (e.g. roofline or decode.roofline) and a "
-                        "substring of the kernel it times")
+                        "substring of the kernel it times ('+'-joined substrings: launches timed together)")
     t = sub.add_parser("traffic")
     t.add_argument("out")
-    t.add_argument("--kernel", required=True)
+    t.add_argument("--kernel", action="append", required=True,
+                   help="substring of the kernel's name; repeat for the launches of one step (summed)")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
     t.add_argument("--copy-fetch", required=True)
