@@ -466,38 +466,24 @@ DEV float lane_group_sum(float v) {
 
 constexpr int kMaxSeq = 2048;   // longest decode cache (positions) the attention kernel unrolls for
 
-// Launch bounds at head dim 128: four workgroups per compute unit (at most 128
-// registers; the grouped-query instances would otherwise take 129 and fit
-// only three). At head dim 64 that bound would spill, so two.
-template <int HD, int G, int NS>
-__global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
-                                                       const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
-                                                       u16 *a_lo, float *opart) {
-  constexpr int LPK = HD / 8;          // lanes per key
-  constexpr int KPW = 64 / LPK;        // keys per wavefront instruction
-  constexpr int UNR = 2;               // key instructions per wavefront per step
-  constexpr int KPS = 4 * KPW * UNR;   // keys per workgroup step
-  constexpr int NG = 4 * KPW;          // lane groups per workgroup
-  constexpr float kLazyRescale = 8.0f;   // log2 units a running maximum may lag the true one
-  // One workgroup per (key/value head hk, sequence b): the G query heads
-  // hk*G .. hk*G+G-1 share its cached keys and values, which are read once.
-  __shared__ float sq[G][HD], sknew[HD], svnew[HD];
-  __shared__ float gm[NG][G], gl[NG][G], snew[G];
-  __shared__ float osum[NG][G][HD];
-  const int hk = blockIdx.x, b = blockIdx.y, rs = NS > 1 ? (int)blockIdx.z : 0;
+// The new token's part of a decode attention workgroup (key/value head hk,
+// sequence b, key range rs): q of the G query heads hk*G .. hk*G+G-1, k and
+// v, each the sum of the Q/K/V split-K partials times rstd, RoPE on q and k;
+// q scaled by log2(e)/sqrt(hd) into sq, k and v (fp32) into sknew / svnew,
+// the bf16 cache copy at position p (first range only), and the new key's
+// score per query head into snew (log2 domain). Ends synchronised.
+template <int HD, int G, int NT = 256>
+DEV void dec_attn_new_token(const DecodeArgs &d, const float *part, int splits, const float *ss, u16 *kc, u16 *vc,
+                            int hk, int b, int rs, int p, bool ok, int64_t cbase, float (*sq)[HD], float *sknew,
+                            float *svnew, float *snew) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int p = d.pos[b];
-  const bool ok = pos_ok(p, d.max_seq);
   const int kvd = d.n_kv_heads * HD;
-  const int64_t cbase = ((int64_t)b * d.n_kv_heads + hk) * d.max_seq * HD;
   const float scale = 1.4426950408889634f / sqrtf((float)HD);
-
-  // ---- 1. q (G heads), k, v of the new token: channel c of [q_0 .. q_{G-1}, k, v]
   {
     const int N = d.dim + 2 * kvd;
     const int64_t stride = (int64_t)d.batch * N;
     const float r = rstd_from_parts(ss, b, (d.dim + 1023) / 1024, d.dim, d.eps);
-    for (int c = tid; c < (G + 2) * HD; c += 256) {   // stride 256: pairs (e, e^1) stay in one pass
+    for (int c = tid; c < (G + 2) * HD; c += NT) {   // an even stride: pairs (e, e^1) stay in one pass
       const int gq = c / HD, e = c % HD;
       const int col = gq < G ? (hk * G + gq) * HD + e : d.dim + (gq - G) * kvd + hk * HD + e;
       float x = sum_parts(0.f, part + (int64_t)b * N + col, stride, splits) * r;
@@ -520,12 +506,6 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
     }
   }
   __syncthreads();
-  // cached keys 0..p-1 (key p is the new one); this range covers keys
-  // k0 .. k0+nk-1, a multiple of KPS long except at the end
-  const int nk_all = ok ? p : 0;
-  const int chunk = NS == 1 ? nk_all : ((nk_all + NS - 1) / NS + KPS - 1) / KPS * KPS;
-  const int k0 = min(rs * chunk, nk_all);
-  const int nk = min(k0 + chunk, nk_all) - k0;
   if (w == 0) {                 // the new key's scores (log2 domain)
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -535,14 +515,42 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
       if (lane == 0) snew[g] = s;
     }
   }
+}
+
+// Launch bounds at head dim 128: four workgroups per compute unit (at most 128
+// registers; the grouped-query instances would otherwise take 129 and fit
+// only three). At head dim 64 that bound would spill, so two.
+template <int HD, int G, int NS>
+__global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const DecodeArgs d, const float *part, int splits,
+                                                       const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
+                                                       u16 *a_lo, float *opart) {
+  constexpr int LPK = HD / 8;          // lanes per key
+  constexpr int KPW = 64 / LPK;        // keys per wavefront instruction
+  constexpr int UNR = 2;               // key instructions per wavefront per step
+  constexpr int KPS = 4 * KPW * UNR;   // keys per workgroup step
+  constexpr int NG = 4 * KPW;          // lane groups per workgroup
+  constexpr float kLazyRescale = 8.0f;   // log2 units a running maximum may lag the true one
+  // One workgroup per (key/value head hk, sequence b): the G query heads
+  // hk*G .. hk*G+G-1 share its cached keys and values, which are read once.
+  __shared__ float sq[G][HD], sknew[HD], svnew[HD];
+  __shared__ float gm[NG][G], gl[NG][G], snew[G];
+  __shared__ float osum[NG][G][HD];
+  const int hk = blockIdx.x, b = blockIdx.y, rs = NS > 1 ? (int)blockIdx.z : 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int p = d.pos[b];
+  const bool ok = pos_ok(p, d.max_seq);
+  const int64_t cbase = ((int64_t)b * d.n_kv_heads + hk) * d.max_seq * HD;
+
+  // cached keys 0..p-1 (key p is the new one); this range covers keys
+  // k0 .. k0+nk-1, a multiple of KPS long except at the end
+  const int nk_all = ok ? p : 0;
+  const int chunk = NS == 1 ? nk_all : ((nk_all + NS - 1) / NS + KPS - 1) / KPS * KPS;
+  const int k0 = min(rs * chunk, nk_all);
+  const int nk = min(k0 + chunk, nk_all) - k0;
 
   // ---- 2. one pass over the cached keys and values
   const int kg = lane / LPK, d8 = lane % LPK;
-  float qv[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) qv[g][i] = sq[g][d8 * 8 + i];
+  float qv[G][8];   // this lane's channels of the G queries (after the new token's part below)
   float m_run[G], l_run[G], acc[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -621,6 +629,14 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
   u32x4 kb[2][UNR], vb[2][UNR];
   load(kb[0], vb[0], 0);
   load(kb[1], vb[1], min(1, last));
+
+  // ---- 1. q (G heads), k, v of the new token (its latency overlaps the
+  // first two steps' loads, which read only cached rows below p)
+  dec_attn_new_token<HD, G>(d, part, splits, ss, kc, vc, hk, b, rs, p, ok, cbase, sq, sknew, svnew, snew);
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qv[g][i] = sq[g][d8 * 8 + i];
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int st = 0; st < MAXSTEPS; ++st) {
@@ -654,6 +670,259 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
     float L = pn, o = pn * svnew[e];
     for (int gi = 0; gi < NG; ++gi) {
       const float f = exp2f(gm[gi][g] - Mu);   // 0 for a group that saw no key
+      L += f * gl[gi][g];
+      o += f * osum[gi][g][e];
+    }
+    if (NS == 1) {
+      const float v = ok ? o / L : __builtin_nanf("");
+      u16 hi, lo;
+      split_pair(v, hi, lo);
+      const int64_t oo = (int64_t)b * d.dim + (hk * G + g) * HD + e;
+      a_hi[oo] = hi;
+      a_lo[oo] = lo;
+    } else {
+      float *st = opart + (((int64_t)b * d.n_heads + hk * G + g) * NS + rs) * (HD + 2);
+      st[2 + e] = o;
+      if (e == 0) {
+        st[0] = M;
+        st[1] = L;
+      }
+    }
+  }
+}
+
+// Grouped-query decode attention on the matrix cores (head dim 128, G = 2..8
+// query heads per key/value head), for the same workgroups as dec_attn_kernel
+// (key/value head, sequence, key range). Each wavefront takes 32-key chunks
+// of the range in turn (chunk c to wavefront c mod 4):
+//  - S = K Q^T with v_mfma_f32_16x16x32_bf16, two 16-key blocks: K rows go
+//    from the cache straight into the A operand (a lane holds 8 channels of
+//    one key), q (fp32) enters as a bf16 hi/lo pair (two products, ~2^-17
+//    relative), G of the 16 columns used. The keys of block b, row r are
+//    chunk keys 8 (r / 4) + 4 b + r % 4, so that a lane's four scores of
+//    each block are the eight consecutive keys the P operand wants.
+//  - online softmax in fp32 against a per-head reference maximum that moves
+//    only when some score exceeds it by more than 2^8 (no cross-lane step in
+//    the common case); P as a bf16 hi/lo pair.
+//  - O = P V with the same instruction over the 32 keys: V (row-major in the
+//    cache) is staged in a per-wavefront LDS tile by direct loads and read
+//    with ds_read_b64_tr_b16, which hands each lane four consecutive keys of
+//    one channel. Tile rows are 256 bytes with the 16-byte chunks XOR-ed by
+//    2 f(row), f(row) = (row & 3) + 4 ((row >> 3) & 1), so the 16 rows one
+//    transposing read touches fall on distinct chunks per half-wavefront.
+// The next chunk's keys and value tile are in flight while one is processed.
+// The four wavefronts' states and the new key merge in a fixed order (as in
+// dec_attn_kernel); results are deterministic.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <int G, int NS>
+__global__ __launch_bounds__(512, 1) void dec_attn_mfma_kernel(const DecodeArgs d, const float *part, int splits,
+                                                               const float *ss, u16 *kc, u16 *vc, u16 *a_hi,
+                                                               u16 *a_lo, float *opart) {
+  static_assert(G >= 2 && G <= 8, "grouped heads, 2 to 8 per key/value head");
+  constexpr int HD = 128;
+  constexpr int CK = 32;                   // keys per chunk
+  constexpr int NB = HD / 16;              // 16-channel blocks of O
+  constexpr int VT = CK * HD / 8;          // u32x4 per value tile (8 KB)
+  constexpr float kLazyRescale = 8.0f;     // log2 units the reference maximum may lag
+  constexpr int NWV = 8;                   // wavefronts (two per SIMD)
+  __shared__ float sq[G][HD], sknew[HD], svnew[HD];
+  __shared__ float gm[NWV][G], gl[NWV][G], snew[G];
+  // two value tiles per wavefront; after the key loop the same memory holds
+  // the wavefronts' output sums for the merge
+  __shared__ u32x4 vtile[NWV * 2 * VT];
+  static_assert(NWV * G * HD * 4 <= (int)sizeof(vtile), "output sums fit the value tiles");
+  float(*osum)[G][HD] = (float(*)[G][HD])vtile;
+
+  const int hk = blockIdx.x, b = blockIdx.y, rs = NS > 1 ? (int)blockIdx.z : 0;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int j = lane & 15, g4 = lane >> 4;   // operand column / row-block of the 16 x 16 products
+  const int p = d.pos[b];
+  const bool ok = pos_ok(p, d.max_seq);
+  const int64_t cbase = ((int64_t)b * d.n_kv_heads + hk) * d.max_seq * HD;
+
+  // cached keys 0..p-1: this range covers k0 .. k0+nk-1 (a multiple of NWV
+  // chunks long except at the end), chunk c of it to wavefront c % NWV
+  const int nk_all = ok ? p : 0;
+  const int chunk = NS == 1 ? nk_all : ((nk_all + NS - 1) / NS + NWV * CK - 1) / (NWV * CK) * (NWV * CK);
+  const int k0 = min(rs * chunk, nk_all);
+  const int nk = min(k0 + chunk, nk_all) - k0;
+  const int nch = (nk + CK - 1) / CK;
+  const int my_n = nch > w ? (nch - w + NWV - 1) / NWV : 0;
+
+  const u16 *kbase = kc + cbase;
+  const u16 *vbase = wave_uniform(vc + cbase);
+  u32x4 *const myv = vtile + w * (2 * VT);
+  auto tile_f = [](int row) { return (row & 3) + 4 * ((row >> 3) & 1); };
+  // keys of chunk c into kf (past the range: the range's last key, masked;
+  // an empty range reads its first position, never used)
+  auto load_k = [&](u32x4 (&kf)[2][4], int c) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int key = k0 + max(min(c * CK + 8 * (j >> 2) + 4 * bb + (j & 3), nk - 1), 0);
+      const u16 *row = kbase + (int64_t)key * HD + 8 * g4;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kf[bb][kk] = *(const u32x4 *)(row + 32 * kk);
+    }
+  };
+  // values of chunk c into tile slot `slot` (8 direct loads of 4 rows each)
+  auto load_v = [&](int slot, int c) {
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int row = 4 * q + (lane >> 4);
+      const int lc = (lane & 15) ^ (2 * tile_f(row));
+      const int key = k0 + max(min(c * CK + row, nk - 1), 0);
+      buf_load_lds16(vbase, (uint32_t)((key * HD + 8 * lc) * 2), 0, myv + slot * VT + q * 64);
+    }
+  };
+
+  f32x4 acc[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float my_ref = -INFINITY, lpart = 0.f;   // this lane's head j: reference maximum, partial sum
+
+  // The chunk loop unrolls fully (at most MAXIT chunks per wavefront for a
+  // cache of kMaxSeq positions), so the two buffers are indexed at compile
+  // time; loads are unconditional (the next chunk's, clamped to valid rows
+  // past the range) and only the arithmetic of chunks past this
+  // wavefront's share is skipped: a load under a branch would make the
+  // compiler wait for every load in flight at the join.
+  constexpr int MAXIT = ((kMaxSeq + NS - 1) / NS + NWV * CK - 1) / (NWV * CK);
+  u32x4 kf[2][2][4];
+  load_k(kf[0], w);
+  load_v(0, w);
+
+  // ---- 1. the new token (its latency overlaps the first chunk's loads)
+  dec_attn_new_token<HD, G, NWV * 64>(d, part, splits, ss, kc, vc, hk, b, rs, p, ok, cbase, sq, sknew, svnew, snew);
+
+  // q as the B operand of S = K Q^T: column j (query head j < G), channels
+  // 32 kk + 8 g4 .. +7, as a bf16 hi/lo pair
+  u32x4 qhi[4], qlo[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    float qf[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qf[i] = j < G ? sq[j][32 * kk + 8 * g4 + i] : 0.f;
+    pack8_pair(qf, qhi[kk], qlo[kk]);
+  }
+
+  // ---- 2. the cached keys
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    const int c = w + NWV * it, cur = it & 1;
+    if (it + 1 < MAXIT) {
+      load_k(kf[cur ^ 1], c + NWV);
+      load_v(cur ^ 1, c + NWV);
+    }
+    if (it >= my_n) continue;
+    // scores of the two 16-key blocks
+    f32x4 sc[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      sc[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[cur][bb][kk]), as_bf16x8(qhi[kk]), sc[bb], 0, 0, 0);
+        sc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kf[cur][bb][kk]), as_bf16x8(qlo[kk]), sc[bb], 0, 0, 0);
+      }
+    }
+    // lane (g4, j): head j, chunk keys 8 g4 + 4 bb + u
+    float mx = -INFINITY;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool live = j < G && c * CK + 8 * g4 + 4 * bb + u < nk;
+        sc[bb][u] = live ? sc[bb][u] : -INFINITY;
+        mx = fmaxf(mx, sc[bb][u]);
+      }
+    if (__any(mx > my_ref + kLazyRescale)) {
+      // a head's maximum moved: over the four lanes of each head, the new
+      // reference, and every accumulator of that head rescaled
+      float hm = fmaxf(mx, __shfl_xor(mx, 16, 64));
+      hm = fmaxf(hm, __shfl_xor(hm, 32, 64));
+      const float m_new = fmaxf(my_ref, hm);
+      const float alpha = __builtin_amdgcn_exp2f(my_ref - (m_new == -INFINITY ? 0.f : m_new));   // -inf -> 0
+      my_ref = m_new;
+      lpart *= alpha;
+      // O rows of this lane are heads 4 g4 + u; their factors sit in lanes 4 g4 + u
+      float af[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) af[u] = __shfl(alpha, 4 * g4 + u, 64);
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[nb][u] *= af[u];
+    }
+    const float m_use = my_ref == -INFINITY ? 0.f : my_ref;
+    float pr[8];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        pr[4 * bb + u] = __builtin_amdgcn_exp2f(sc[bb][u] - m_use);   // exp2(-inf) = 0
+        lpart += pr[4 * bb + u];
+      }
+    u32x4 phi, plo;
+    pack8_pair(pr, phi, plo);   // P operand: row j (head), keys 8 g4 .. +7
+    // this chunk's value tile is in LDS once its direct loads are done (the
+    // next chunk's 16 loads may still be in flight)
+    if (it + 1 < MAXIT) {
+      GEMV_WAIT_VMCNT(16);
+    } else {
+      GEMV_WAIT_VMCNT(0);
+    }
+    const u32x4 *tile = myv + cur * VT;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      // B operand: channel 16 nb + j of keys 8 g4 .. +7, two transposing reads
+      // of four keys; lane j of a 16-lane group points at row kb + j / 4,
+      // channels 16 nb + 4 (j % 4) .. +3
+      u32x2 vv[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * g4 + 4 * h + (j >> 2);
+        const int ch = 2 * nb + ((j & 3) >> 1);            // logical 16-byte chunk
+        const int byte = (row * 16 + (ch ^ (2 * tile_f(row)))) * 16 + 8 * (j & 1);
+        const auto t = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)((char *)tile + byte));
+        vv[h] = __builtin_bit_cast(u32x2, t);
+      }
+      const u32x4 vb = u32x4{vv[0][0], vv[0][1], vv[1][0], vv[1][1]};
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(phi), as_bf16x8(vb), acc[nb], 0, 0, 0);
+      acc[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(plo), as_bf16x8(vb), acc[nb], 0, 0, 0);
+    }
+  }
+  GEMV_WAIT_VMCNT(0);   // the last prefetch (unused) is in LDS before the tiles are reused
+
+  // ---- per wavefront: head references and sums (lanes j < G of the first
+  // row block), output sums (rows 4 g4 + u < G)
+  {
+    float ls = lpart + __shfl_xor(lpart, 16, 64);
+    ls += __shfl_xor(ls, 32, 64);
+    if (g4 == 0 && j < G) {
+      gm[w][j] = my_ref;
+      gl[w][j] = ls;
+    }
+  }
+  __syncthreads();   // every wavefront is done with its value tiles
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (4 * g4 + u < G) osum[w][4 * g4 + u][16 * nb + j] = acc[nb][u];
+  __syncthreads();
+
+  // ---- 3. per query head: merge the wavefronts and the new key (fixed
+  // order), as in dec_attn_kernel
+  for (int c = tid; c < G * HD; c += NWV * 64) {
+    const int g = c / HD, e = c % HD;
+    const float sn = rs == 0 ? snew[g] : -INFINITY;   // the new key belongs to the first range
+    float M = sn;
+    for (int gi = 0; gi < NWV; ++gi) M = fmaxf(M, gm[gi][g]);
+    const float Mu = M == -INFINITY ? 0.f : M;        // a later range may see no key at all
+    const float pn = exp2f(sn - Mu);
+    float L = pn, o = pn * svnew[e];
+    for (int gi = 0; gi < NWV; ++gi) {
+      const float f = exp2f(gm[gi][g] - Mu);   // 0 for a wavefront that saw no key
       L += f * gl[gi][g];
       o += f * osum[gi][g][e];
     }
@@ -742,6 +1011,50 @@ hipError_t dec_attn_launch_g(const DecodeArgs &d, const float *part, int splits,
   return hipGetLastError();
 }
 
+// Matrix-core kernel for grouped heads at head dim 128: key ranges until there
+// are at least 256 workgroups (one per compute unit; each range repeats the
+// new token's work, so fewer, longer ranges are faster: on the 7B shape with 8
+// key/value heads, 1.84-1.92 ms per step of attention with 256 four-wavefront
+// workgroups against 1.92-1.98 with 512 and 2.02-2.14 with 1024).
+int dec_attn_mfma_ranges(const DecodeArgs &d) {
+  int ns = 1;
+  while (ns < kDecAttnMaxRanges && d.n_kv_heads * d.batch * ns < 256) ns *= 2;
+  return ns;
+}
+
+template <int G>
+hipError_t dec_attn_mfma_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
+                                uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, hipStream_t s) {
+  const int ns = dec_attn_mfma_ranges(d);
+  if (ns > 1 && !opart) return hipErrorInvalidValue;
+  dim3 grid(d.n_kv_heads, d.batch, ns);
+  switch (ns) {
+    case 1:
+      hipLaunchKernelGGL((dec_attn_mfma_kernel<G, 1>), grid, dim3(512), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo,
+                         opart);
+      return hipGetLastError();
+    case 2:
+      hipLaunchKernelGGL((dec_attn_mfma_kernel<G, 2>), grid, dim3(512), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo,
+                         opart);
+      break;
+    case 4:
+      hipLaunchKernelGGL((dec_attn_mfma_kernel<G, 4>), grid, dim3(512), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo,
+                         opart);
+      break;
+    case 8:
+      hipLaunchKernelGGL((dec_attn_mfma_kernel<G, 8>), grid, dim3(512), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo,
+                         opart);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int n = d.batch * d.dim;
+  hipLaunchKernelGGL(dec_attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d, opart, ns, a_hi, a_lo);
+  return hipGetLastError();
+}
+
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
                            uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, hipStream_t s) {
   if (d.max_seq > kMaxSeq) return hipErrorInvalidValue;
@@ -749,6 +1062,10 @@ hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, c
   const int group = d.n_heads / d.n_kv_heads;
   const int ns = dec_attn_ranges(d);
   if (ns > 1 && !opart) return hipErrorInvalidValue;
+  // grouped heads at head dim 128: the matrix-core kernel
+  if (d.head_dim == 128 && group == 2) return dec_attn_mfma_launch<2>(d, part, splits, ss, kc, vc, a_hi, a_lo, opart, s);
+  if (d.head_dim == 128 && group == 4) return dec_attn_mfma_launch<4>(d, part, splits, ss, kc, vc, a_hi, a_lo, opart, s);
+  if (d.head_dim == 128 && group == 8) return dec_attn_mfma_launch<8>(d, part, splits, ss, kc, vc, a_hi, a_lo, opart, s);
 #define DEC_ATTN_CASE(HD_, G_)                                                                         \
   if (d.head_dim == HD_ && group == G_)                                                               \
     return dec_attn_launch_g<HD_, G_>(d, part, splits, ss, kc, vc, a_hi, a_lo, opart, ns, s);
