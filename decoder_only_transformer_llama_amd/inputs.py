@@ -131,6 +131,12 @@ TEST_WORKLOADS: Dict[int, Workload] = {
     # multi-query model (one key/value head), head_dim 128, groups of 4
     106: Workload(106, "test-model-bf16-mqa", dim=512, n_heads=4, hidden=1536, batch=2, seq=24, dtype="bf16",
                   n_layers=2, vocab=500, max_seq=48, n_kv_heads=1),
+    # grouped-query models at head_dim 128 with groups of 2 and of 8 (one
+    # key/value head), prompts past one 32-key decode chunk
+    109: Workload(109, "test-model-bf16-gqa2", dim=1024, n_heads=8, hidden=2816, batch=2, seq=70, dtype="bf16",
+                  n_layers=2, vocab=500, max_seq=96, gain_std=0.1, n_kv_heads=4),
+    110: Workload(110, "test-model-bf16-gqa8", dim=1024, n_heads=8, hidden=2816, batch=3, seq=45, dtype="bf16",
+                  n_layers=2, vocab=500, max_seq=64, gain_std=0.1, n_kv_heads=1),
 }
 
 

@@ -434,6 +434,7 @@ TOL_DECODE_STEP = 5e-3
 
 
 @pytest.mark.parametrize("wid,numerics", [(101, L.NUM_DEFAULT), (105, L.NUM_DEFAULT), (106, L.NUM_DEFAULT),
+                                          (109, L.NUM_DEFAULT), (110, L.NUM_DEFAULT),
                                           (105, ALL_PAIRS), (108, L.NUM_DEFAULT)])
 def test_model_prefill_then_decode(wid, numerics):
     w, m, layers, gl = small_model(wid, numerics=numerics)
@@ -522,7 +523,7 @@ def test_model_prefill_all_pairs(wid):
     assert err < TOL_BF16 and err < 0.8 * err_single
 
 
-@pytest.mark.parametrize("wid", [105, 106])
+@pytest.mark.parametrize("wid", [105, 106, 109, 110])
 def test_grouped_kv_equals_multi_head_with_repeated_kv(wid):
     """Grouped key/value heads compute exactly multi-head attention whose K/V
     projections repeat each shared head's rows for its group of query heads.
@@ -689,7 +690,7 @@ def test_model_start_pos_outside_cache_gives_nan_rows():
     assert torch.isfinite(got[2]).all() and torch.equal(got[2], ok[2])
 
 
-@pytest.mark.parametrize("wid", [101, 105])
+@pytest.mark.parametrize("wid", [101, 105, 110])
 def test_decode_ragged_positions(wid):
     """A decode step with a different position per sequence (the new token at
     pos[b] overwrites slot pos[b]; attention covers slots 0..pos[b]) against
