@@ -119,6 +119,30 @@ DEV void interleave() {
   if (NRD > P) __builtin_amdgcn_sched_group_barrier(0x100, NRD - P, ID);
 }
 
+// Scheduling hint for a substep that also issues NLD of the K step's
+// global->LDS loads: the LDS reads two per MFMA first, then one load per MFMA
+// (the loads must follow the reads: they write LDS that the compiler cannot
+// tell apart from what the reads read). Issuing a load takes tens of cycles;
+// paired this way it overlaps the matrix core instead of stalling it.
+template <int NMF, int NRD>
+constexpr int free_mfmas() { return NMF - (NRD + 1) / 2; }
+template <int NMF, int NRD, int NLD, int ID>
+DEV void interleave_loads() {
+  constexpr int NR = (NRD + 1) / 2;   // MFMAs that carry the reads
+  static_assert(NLD <= NMF - NR, "more loads than MFMAs to pair them with");
+  static_for<0, NR>([](auto ii) {
+    constexpr int i = decltype(ii)::value;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);                      // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * i + 1 < NRD ? 2 : 1, ID);  // LDS reads
+  });
+#pragma unroll
+  for (int i = 0; i < NLD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, ID);  // one MFMA
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, ID);  // one global->LDS load
+  }
+  if (NMF > NR + NLD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR - NLD, ID);
+}
+
 // F16 0: bf16 A (or pair) and bf16 B. F16 1: the A operand holds IEEE fp16
 // and the bf16 B fragments are converted to fp16 in registers (exactly, for
 // weights in fp16's normal range) before fp16 matrix-core products: 11-bit
@@ -208,20 +232,26 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   // the global form of the same load the compiler also counts it as an
   // outstanding LDS access and drains every in-flight load before each
   // operand read (7B block 2.5% slower).
-  auto issue = [&](int kt) {
+  // Loads LO .. HI-1 of stage kt in the order A, A lo part, B (LPS per wavefront).
+  auto issue_part = [&](int kt, auto lo, auto hi) {
+    constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
     const int k0 = kb0 + min(kt, nk - 1) * BK;   // past the end: reload the last step (never read)
     u32x4 *st = smem + (kt % STAGES) * G::STAGE;
-#pragma unroll
-    for (int q = 0; q < G::A_LD; ++q)
-      buf_load_lds16((const u16 *)a.A + afirst[q], aoff[q], k0 * 2, st + (wave * G::A_LD + q) * 64);
-    if (APAIR) {
-#pragma unroll
-      for (int q = 0; q < G::A_LD; ++q)
-        buf_load_lds16(a.A_lo + afirst[q], aoff[q], k0 * 2, st + G::A_TILE + (wave * G::A_LD + q) * 64);
-    }
     u32x4 *sb = st + G::A_TILE * (APAIR ? 2 : 1);
-#pragma unroll
-    for (int q = 0; q < G::B_LD; ++q) buf_load_lds16(bbase[q], boff[q], k0 * 2, sb + (wave * G::B_LD + q) * 64);
+    static_for<LO, HI>([&](auto iq) {
+      constexpr int q = decltype(iq)::value;
+      constexpr int NA = G::A_LD * (APAIR ? 2 : 1);
+      if constexpr (q < G::A_LD)
+        buf_load_lds16((const u16 *)a.A + afirst[q], aoff[q], k0 * 2, st + (wave * G::A_LD + q) * 64);
+      else if constexpr (q < NA)
+        buf_load_lds16(a.A_lo + afirst[q - G::A_LD], aoff[q - G::A_LD], k0 * 2,
+                       st + G::A_TILE + (wave * G::A_LD + q - G::A_LD) * 64);
+      else
+        buf_load_lds16(bbase[q - NA], boff[q - NA], k0 * 2, sb + (wave * G::B_LD + q - NA) * 64);
+    });
+  };
+  auto issue = [&](int kt) {
+    issue_part(kt, std::integral_constant<int, 0>{}, std::integral_constant<int, G::LPS>{});
   };
 
   f32x16 acc[G::TM][G::TN];
@@ -298,21 +328,37 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   read_frag(f[0], 0, 0);
   constexpr int NMF = G::TM * G::TN * (APAIR ? 2 : 1);     // MFMAs per substep
   constexpr int NRD = G::TM * (APAIR ? 2 : 1) + G::TN;      // LDS reads per substep
-  auto inner = [&](int kt) {   // substeps 0 .. NS-2 of step kt
+  // With three or more stages the K step's loads are spread over the
+  // substeps before the barrier, at most as many per substep as it has MFMAs
+  // free of LDS reads (O projection 7% faster). With two stages a load has
+  // only the one K step to land in, and issuing any of them later costs more
+  // (gate/up 5% slower): all are issued at the top of the step.
+  constexpr bool SPREAD = STAGES > 2;
+  constexpr int LPSS = free_mfmas<NMF, NRD>();
+  static_assert(!SPREAD || LPSS * (NS - 1) >= G::LPS, "loads do not fit the substeps before the barrier");
+  auto inner = [&](int kt, auto with_loads) {   // substeps 0 .. NS-2 of step kt
     static_for<0, NS - 1>([&](auto ic) {
       constexpr int ss = decltype(ic)::value;
       read_frag(f[(ss + 1) & 1], kt, ss + 1);
-      mma(f[ss & 1]);
-      interleave<NMF, NRD, ss>();
+      constexpr int LO = ss * LPSS < G::LPS ? ss * LPSS : G::LPS;
+      constexpr int HI = LO + LPSS < G::LPS ? LO + LPSS : G::LPS;
+      if constexpr (SPREAD && decltype(with_loads)::value && HI > LO) {
+        issue_part(kt + STAGES - 1, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{});
+        mma(f[ss & 1]);
+        interleave_loads<NMF, NRD, HI - LO, ss>();
+      } else {
+        mma(f[ss & 1]);
+        interleave<NMF, NRD, ss>();
+      }
     });
   };
   for (int kt = 0; kt < nk - 1; ++kt) {
-    issue(kt + STAGES - 1);
+    if constexpr (!SPREAD) issue(kt + STAGES - 1);
     // the substeps before the barrier at raised wave priority: when both
     // wavefronts of a SIMD are ready, the one in its MFMA stretch issues
     // first (~1.5% on the 7B block)
     __builtin_amdgcn_s_setprio(1);
-    inner(kt);
+    inner(kt, std::true_type{});
     __builtin_amdgcn_s_setprio(0);
     WAIT_VMCNT((STAGES - 2) * G::LPS);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
@@ -321,7 +367,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
     mma(f[1]);
     interleave<NMF, NRD, NS - 1>();
   }
-  inner(nk - 1);
+  inner(nk - 1, std::false_type{});
   mma(f[1]);
   WAIT_VMCNT(0);   // drain the reloads past the end before LDS is reused
 
