@@ -524,12 +524,14 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   // then only undoes the fp16 operand's power-of-two scale).
   const bool pre = c->norm_placement == LLAMA_NORM_PRE, post = c->norm_placement == LLAMA_NORM_POST;
 
-  // z = RMSNorm(x; g1): statistic + gained operand; the rstd multiply happens in the QKV epilogue
+  // z = RMSNorm(x; g1): statistic + gained operand; the rstd multiply happens
+  // in the QKV epilogue. The same launch builds the RoPE table when asked.
+  RopeRows rope;
+  if (make_rope) rope = RopeRows{b.rope_tab, seq, hd, (double)c->rope_theta};
   HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, pre ? (const uint16_t *)w->attn_norm : nullptr, M, d,
                            c->norm_eps, b.rstd1, b.xg_hi, qkv_pair ? b.xg_lo : nullptr, s, nullptr, 0, nullptr,
-                           qf16),
+                           qf16, rope),
           "attention norm");
-  if (make_rope) HIP_TRY(rope_table_launch(b.rope_tab, seq, hd, c->rope_theta, s), "rope table");
 
   GemmArgs q{};
   q.M = M;

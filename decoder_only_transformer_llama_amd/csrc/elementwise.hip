@@ -14,15 +14,18 @@ namespace llama {
 
 // ------------------------------------------------------------------ RoPE tables
 // tab[p * hd/2 + i] = (cos, sin)(p * theta^(-2i/hd)), angles in fp64.
+DEV float2 rope_entry(int p, int i, int hd, double theta) {
+  const double ang = (double)p * pow(theta, -(2.0 * i) / hd);
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  return make_float2((float)cs, (float)sn);
+}
+
 __global__ void rope_table_kernel(float2 *tab, int positions, int hd, double theta) {
   const int half = hd >> 1;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= (int64_t)positions * half) return;
-  const int p = (int)(idx / half), i = (int)(idx % half);
-  const double ang = (double)p * pow(theta, -(2.0 * i) / hd);
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  tab[idx] = make_float2((float)cs, (float)sn);
+  tab[idx] = rope_entry((int)(idx / half), (int)(idx % half), hd, theta);
 }
 
 __global__ void rope_table_pos_kernel(float2 *tab, const int32_t *pos, int n, int hd, double theta) {
@@ -85,10 +88,14 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__
                                                         int64_t rows, int dim, float eps, float *__restrict__ rmul,
                                                         u16 *__restrict__ xg_hi, u16 *__restrict__ xg_lo,
                                                         const float *__restrict__ part, int n_parts,
-                                                        float *__restrict__ h_out) {
+                                                        float *__restrict__ h_out, const RopeRows rope) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= rows) return;
+  // table row p = row for the first rope.positions rows: the RoPE table is
+  // built by this launch instead of one of its own
+  if (row < rope.positions)
+    for (int i = lane; i < rope.hd / 2; i += 64) rope.tab[row * (rope.hd / 2) + i] = rope_entry((int)row, i, rope.hd, rope.theta);
   const int64_t base = row * dim;
   const int64_t pstride = rows * dim;
   // channels c .. c+7 of the row (c is a multiple of 8 below dim)
@@ -209,8 +216,9 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__
 
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
                             float *rmul, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s, const float *part,
-                            int n_parts, float *h_out, int out_f16) {
+                            int n_parts, float *h_out, int out_f16, RopeRows rope) {
   if (rows == 0) return hipSuccess;
+  if (rope.positions > rows || (rope.positions > 0 && (!rope.tab || rope.hd <= 0))) return hipErrorInvalidValue;
   if (dim % 8) return hipErrorInvalidValue;
   const bool parts = part != nullptr && n_parts > 0;
   if (parts && h_out == nullptr) return hipErrorInvalidValue;
@@ -221,7 +229,7 @@ hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_
 #define NP_CASE(F, O_, R, NC_)                                                                                    \
   if (!!in_f32 == F && out == O_ && parts == R && nc == NC_) {                                                   \
     hipLaunchKernelGGL((norm_prep_kernel<F, O_, R, NC_>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rmul, xg_hi, \
-                       xg_lo, part, n_parts, h_out);                                                              \
+                       xg_lo, part, n_parts, h_out, rope);                                                        \
     return hipGetLastError();                                                                                   \
   }
 #define NP_CASES(NC_)                                                                                   \

@@ -137,10 +137,18 @@ hipError_t rope_table_pos_launch(float2 *tab, const int32_t *pos, int n, int hea
 // With `part` (n_parts fp32 [rows, dim] split-K partial products), the row is
 // first h = x + part[0] + ... (split order), written to h_out (fp32), and the
 // statistics and product are those of h.
+// With rope.positions > 0 (at most rows) the same launch also writes the
+// RoPE (cos, sin) table of positions 0 .. rope.positions-1, as
+// rope_table_launch does.
+struct RopeRows {
+  float2 *tab = nullptr;
+  int positions = 0, hd = 0;
+  double theta = 0.0;
+};
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
                             float *rmul, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s,
                             const float *part = nullptr, int n_parts = 0, float *h_out = nullptr,
-                            int out_f16 = 0);
+                            int out_f16 = 0, RopeRows rope = RopeRows{});
 // Index of the largest logit per row (lowest among equals; -1 if the row has a NaN).
 hipError_t argmax_launch(const float *logits, int64_t rows, int vocab, int32_t *out, hipStream_t s);
 // y = r + part[0] + ... + part[n_parts-1], fp32, n elements (n % 4 == 0).
