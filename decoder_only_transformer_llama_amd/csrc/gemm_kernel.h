@@ -11,7 +11,8 @@
 // hi/lo pair) with a ring of STAGES LDS buffers (STAGES-1 steps of loads in
 // flight); operand reads of the next 16-deep substep are interleaved with the
 // current substep's MFMAs; one barrier per step with explicit vmcnt/lgkmcnt
-// waits. The 64-deep step halves the barriers per MFMA: on the 7B block the
+// waits (when only two whole stages fit, B gets a third buffer: see SPLIT
+// below). The 64-deep step halves the barriers per MFMA: on the 7B block the
 // QKV, gate/up and down GEMMs run 2.5-5% faster than with 32-deep steps.
 //
 // A is bf16, a bf16 hi/lo pair (A_lo non-null: both parts are multiplied into
@@ -84,6 +85,16 @@ struct GemmCfg {
                                 : STAGE_BYTES * 3 <= RING_MAX ? 3
                                                               : 2;
   static_assert(STAGES * STAGE_BYTES <= RING_MAX, "LDS ring exceeds its share of the 160 KB");
+  // Split ring: when only two whole stages fit, A keeps two buffers and B
+  // (the weights, streamed from HBM once per launch) gets three, so each
+  // weight load has two K steps to land instead of one (a 256 x 256 x 64
+  // tile then fills the 160 KB exactly; the tile's row statistics move into
+  // the ring after the last step). A is the activation, re-read by every
+  // column tile and so served from the caches.
+  static constexpr int A_STAGE = A_TILE * (APAIR ? 2 : 1);   // u32x4 per A stage
+  static constexpr bool SPLIT = STAGES == 2 && (2 * A_STAGE + 3 * B_TILE) * 16 <= 160 * 1024;
+  static constexpr int SA = SPLIT ? 2 : STAGES, SB = SPLIT ? 3 : STAGES;
+  static constexpr int LDS_U4 = SPLIT ? SA * A_STAGE + SB * B_TILE : STAGES * STAGE + BM / 4;
   static constexpr int A_LD = BM / RPL / NW;       // 1 KB loads per wavefront per A tile
   static constexpr int B_LD = BN / RPL / NW;
   static constexpr int LPS = A_LD * (APAIR ? 2 : 1) + B_LD;  // loads per stage per wavefront
@@ -157,8 +168,17 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   // the LDS ring at offset 0, then the tile's rows' rstd (1 where there is
   // none), staged once: read per element from global memory, each epilogue
   // load was a dependent round trip
-  __shared__ u32x4 smem[STAGES * G::STAGE + BM / 4];
-  float *const s_rstd = (float *)(smem + STAGES * G::STAGE);
+  __shared__ u32x4 smem[G::LDS_U4];
+  // split ring: the statistics take the ring's last BM floats once the K loop is done
+  float *const s_rstd = G::SPLIT ? (float *)(smem + G::LDS_U4) - BM : (float *)(smem + STAGES * G::STAGE);
+  // A and B buffers of K step kt
+  auto a_stage = [&](int kt) -> u32x4 * {
+    return G::SPLIT ? smem + (kt % G::SA) * G::A_STAGE : smem + (kt % STAGES) * G::STAGE;
+  };
+  auto b_stage = [&](int kt) -> u32x4 * {
+    return G::SPLIT ? smem + G::SA * G::A_STAGE + (kt % G::SB) * G::B_TILE
+                    : smem + (kt % STAGES) * G::STAGE + G::A_STAGE;
+  };
 
   // the wavefront index as a scalar: LDS destinations of the direct loads are then scalar sums
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -232,26 +252,32 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   // the global form of the same load the compiler also counts it as an
   // outstanding LDS access and drains every in-flight load before each
   // operand read (7B block 2.5% slower).
-  // Loads LO .. HI-1 of stage kt in the order A, A lo part, B (LPS per wavefront).
-  auto issue_part = [&](int kt, auto lo, auto hi) {
+  // Loads LO .. HI-1 in the order A, A lo part, B (LPS per wavefront): the A
+  // loads of K step kta and the B loads of K step ktb.
+  auto issue_part = [&](int kta, int ktb, auto lo, auto hi) {
     constexpr int LO = decltype(lo)::value, HI = decltype(hi)::value;
-    const int k0 = kb0 + min(kt, nk - 1) * BK;   // past the end: reload the last step (never read)
-    u32x4 *st = smem + (kt % STAGES) * G::STAGE;
-    u32x4 *sb = st + G::A_TILE * (APAIR ? 2 : 1);
+    const int ka = kb0 + min(kta, nk - 1) * BK;   // past the end: reload the last step (never read)
+    const int kb = kb0 + min(ktb, nk - 1) * BK;
+    u32x4 *st = a_stage(kta);
+    u32x4 *sb = b_stage(ktb);
     static_for<LO, HI>([&](auto iq) {
       constexpr int q = decltype(iq)::value;
       constexpr int NA = G::A_LD * (APAIR ? 2 : 1);
       if constexpr (q < G::A_LD)
-        buf_load_lds16((const u16 *)a.A + afirst[q], aoff[q], k0 * 2, st + (wave * G::A_LD + q) * 64);
+        buf_load_lds16((const u16 *)a.A + afirst[q], aoff[q], ka * 2, st + (wave * G::A_LD + q) * 64);
       else if constexpr (q < NA)
-        buf_load_lds16(a.A_lo + afirst[q - G::A_LD], aoff[q - G::A_LD], k0 * 2,
+        buf_load_lds16(a.A_lo + afirst[q - G::A_LD], aoff[q - G::A_LD], ka * 2,
                        st + G::A_TILE + (wave * G::A_LD + q - G::A_LD) * 64);
       else
-        buf_load_lds16(bbase[q - NA], boff[q - NA], k0 * 2, sb + (wave * G::B_LD + q - NA) * 64);
+        buf_load_lds16(bbase[q - NA], boff[q - NA], kb * 2, sb + (wave * G::B_LD + q - NA) * 64);
     });
   };
+  constexpr int NA_LD = G::A_LD * (APAIR ? 2 : 1);   // A loads per stage per wavefront
+  // the loads issued at the top of K step kt: stage kt + S - 1 (split ring:
+  // A of step kt + 1, B of step kt + 2)
   auto issue = [&](int kt) {
-    issue_part(kt, std::integral_constant<int, 0>{}, std::integral_constant<int, G::LPS>{});
+    issue_part(kt + G::SA - 1, kt + G::SB - 1, std::integral_constant<int, 0>{},
+               std::integral_constant<int, G::LPS>{});
   };
 
   f32x16 acc[G::TM][G::TN];
@@ -268,9 +294,9 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
     u32x4 a[G::TM], al[APAIR ? G::TM : 1], b[G::TN];   // raw bits: bf16, or fp16 per F16
   };
   auto read_frag = [&](Frag &f, int kt, int ks) {
-    const u32x4 *sa = smem + (kt % STAGES) * G::STAGE;
+    const u32x4 *sa = a_stage(kt);
     const u32x4 *sal = sa + G::A_TILE;
-    const u32x4 *sb = sa + G::A_TILE * (APAIR ? 2 : 1);
+    const u32x4 *sb = b_stage(kt);
     const int c = ks * 2 + g;
 #pragma unroll
     for (int j = 0; j < G::TN; ++j) {
@@ -305,7 +331,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
 
   // Pipeline per K step kt (NS = BK/16 substeps, fragments alternating in
   // f[0] / f[1]), one barrier:
-  //   issue loads of stage kt+S-1 | for each substep but the last:
+  //   issue loads of stage kt+S-1 (split ring: A kt+1, B kt+2) | for each substep but the last:
   //   [mma f(ss) interleaved with reads of f(ss+1)]
   //   wait own stage-(kt+1) loads, drain own LDS reads, barrier
   //   [mma of the last substep interleaved with reads of f[0] of step kt+1]
@@ -318,11 +344,21 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   // so that waiting for it below overlaps them
   float rs_tid = 1.0f;
   if (a.rstd && tid < BM) rs_tid = a.rstd[min(m0 + tid, a.M - 1)];
+  // loads still in flight at each step's barrier: the next stages' (split
+  // ring: the B loads of the step after next, issued last)
+  constexpr int IN_FLIGHT = G::SPLIT ? G::B_LD : (STAGES - 2) * G::LPS;
+  if constexpr (G::SPLIT) {
+    // A and B of step 0, then B of step 1
+    issue_part(0, 0, std::integral_constant<int, 0>{}, std::integral_constant<int, G::LPS>{});
+    issue_part(0, 1, std::integral_constant<int, NA_LD>{}, std::integral_constant<int, G::LPS>{});
+  } else {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s);
-  if (tid < BM) s_rstd[tid] = rs_tid;
-  __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the statistics are in LDS before the barrier
-  WAIT_VMCNT((STAGES - 2) * G::LPS);
+    for (int s = 0; s < STAGES - 1; ++s) issue_part(s, s, std::integral_constant<int, 0>{},
+                                                     std::integral_constant<int, G::LPS>{});
+    if (tid < BM) s_rstd[tid] = rs_tid;
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): the statistics are in LDS before the barrier
+  }
+  WAIT_VMCNT(IN_FLIGHT);
   __builtin_amdgcn_s_barrier();
   Frag f[2];
   read_frag(f[0], 0, 0);
@@ -343,7 +379,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
       constexpr int LO = ss * LPSS < G::LPS ? ss * LPSS : G::LPS;
       constexpr int HI = LO + LPSS < G::LPS ? LO + LPSS : G::LPS;
       if constexpr (SPREAD && decltype(with_loads)::value && HI > LO) {
-        issue_part(kt + STAGES - 1, std::integral_constant<int, LO>{}, std::integral_constant<int, HI>{});
+        issue_part(kt + STAGES - 1, kt + STAGES - 1, std::integral_constant<int, LO>{},
+                   std::integral_constant<int, HI>{});
         mma(f[ss & 1]);
         interleave_loads<NMF, NRD, HI - LO, ss>();
       } else {
@@ -353,14 +390,14 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
     });
   };
   for (int kt = 0; kt < nk - 1; ++kt) {
-    if constexpr (!SPREAD) issue(kt + STAGES - 1);
+    if constexpr (!SPREAD) issue(kt);
     // the substeps before the barrier at raised wave priority: when both
     // wavefronts of a SIMD are ready, the one in its MFMA stretch issues
     // first (~1.5% on the 7B block)
     __builtin_amdgcn_s_setprio(1);
     inner(kt, std::true_type{});
     __builtin_amdgcn_s_setprio(0);
-    WAIT_VMCNT((STAGES - 2) * G::LPS);
+    WAIT_VMCNT(IN_FLIGHT);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     read_frag(f[0], kt + 1, 0);
@@ -370,6 +407,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   inner(nk - 1, std::false_type{});
   mma(f[1]);
   WAIT_VMCNT(0);   // drain the reloads past the end before LDS is reused
+  if constexpr (G::SPLIT) {
+    __syncthreads();   // every wavefront is done with the ring
+    if (tid < BM) s_rstd[tid] = rs_tid;
+    __syncthreads();
+  }
 
   // ---------------------------------------------------------------- epilogue
   if (EPI == EPI_QKV) {
