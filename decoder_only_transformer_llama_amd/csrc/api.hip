@@ -339,6 +339,10 @@ struct DecodeWs {
 };
 
 constexpr int kDecMaxSeq = 2048;   // longest cache the decode path is validated for
+// The skinny GEMMs carry the batch in the 32 rows of one matrix-core tile: a
+// step over more sequences runs in chunks of 32 (each chunk streams the
+// weights again).
+constexpr int kDecChunk = 32;
 
 void gemv_split(int N, int K, int &splits, int &k_chunk) {
   const GemvShape g = gemv_shape(N, K);
@@ -459,7 +463,7 @@ size_t ws_bytes_of(const llama_config *c, int op, int batch, int seq) {
       carve_block(cv, c, batch, seq, c->max_seq);
       break;
     case LLAMA_OP_MODEL_DECODE:
-      carve_decode(cv, c, batch);
+      carve_decode(cv, c, std::min(batch, kDecChunk));   // chunks of kDecChunk sequences reuse it
       break;
     case LLAMA_OP_CAUSAL_ATTN_BACKWARD:
       cv.take<float>(n * c->dim);                                 // recomputed output
@@ -949,7 +953,7 @@ int llama_workspace_size(const llama_config *c, int op, int batch, int seq, size
       break;
     case LLAMA_OP_MODEL_DECODE:
       st = check_model_cfg(c, batch, 1);
-      if (!st && (batch > 32 || c->max_seq > kDecMaxSeq)) st = LLAMA_ERR_UNSUPPORTED;
+      if (!st && c->max_seq > kDecMaxSeq) st = LLAMA_ERR_UNSUPPORTED;
       break;
     case LLAMA_OP_CAUSAL_ATTN_BACKWARD:
       if (!dtype_ok(c->dtype)) return LLAMA_ERR_DTYPE;
@@ -1207,19 +1211,12 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
   return LLAMA_OK;
 }
 
-int llama_model_decode(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
-                       const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits, void *ws,
-                       size_t ws_bytes, void *stream) {
-  int st = check_model_cfg(c, batch, 1);
-  if (st) return st;
-  if (batch > 32 || c->max_seq > kDecMaxSeq) return LLAMA_ERR_UNSUPPORTED;
-  if ((st = check_model_w(c, w))) return st;
-  // without a pack the skinny GEMMs read the projections themselves, as bf16
-  if (c->dtype == LLAMA_BF16 && (numerics_of(c) & LLAMA_NUM_W_F16) && !w->decode_pack) return LLAMA_ERR_UNSUPPORTED;
-  if (!tokens || !pos || !k_cache || !v_cache || !logits) return LLAMA_ERR_NULL;
-  const size_t need = ws_bytes_of(c, LLAMA_OP_MODEL_DECODE, batch, 1);
-  if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
-  hipStream_t s = (hipStream_t)stream;
+// One decode step over `batch` <= kDecChunk sequences whose layer-0 caches
+// start at k_cache / v_cache; layer l's are layer_elems further on (the
+// stride of the caller's whole batch).
+static int model_decode_chunk(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                              const int32_t *pos, int batch, uint16_t *k_cache, uint16_t *v_cache,
+                              size_t layer_elems, float *logits, void *ws, hipStream_t s) {
   const int d = c->dim, hd = d / c->n_heads;
   Carve cv(ws);
   const DecodeWs dw = carve_decode(cv, c, batch);
@@ -1235,7 +1232,6 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   da.eps = c->norm_eps;
   da.pos = pos;
   da.rope_tab = dw.rope_tab;
-  const size_t layer_elems = (size_t)batch * kv_heads(c) * c->max_seq * hd;
 
   HIP_TRY(rope_table_pos_launch(dw.rope_tab, pos, batch, hd, c->rope_theta, c->max_seq, s), "rope table");
   HIP_TRY(dec_embed_norm_launch(da, (const uint16_t *)w->tok_embeddings, tokens,
@@ -1267,7 +1263,7 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   };
   for (int l = 0; l < c->n_layers; ++l) {
     const llama_block_weights &L = w->layers[l];
-    uint16_t *kc = (uint16_t *)k_cache + l * layer_elems, *vc = (uint16_t *)v_cache + l * layer_elems;
+    uint16_t *kc = k_cache + l * layer_elems, *vc = v_cache + l * layer_elems;
     int sp;
     const uint16_t *lp = pack ? pack + (size_t)l * pl.layer : nullptr;
     packed_mat = lp ? lp + pl.qkv : nullptr;
@@ -1292,6 +1288,30 @@ int llama_model_decode(const llama_config *c, const llama_model_weights *w, cons
   packed_mat = pack ? pack + pl.head_off : nullptr;
   HIP_TRY(gemv(c->vocab, d, BMODE_PLAIN, w->output, nullptr, nullptr, sp), "output head");
   HIP_TRY(dec_head_combine_launch(da, dw.part, sp, dw.rstd, logits, s), "head combine");
+  return LLAMA_OK;
+}
+
+int llama_model_decode(const llama_config *c, const llama_model_weights *w, const int32_t *tokens,
+                       const int32_t *pos, int batch, void *k_cache, void *v_cache, float *logits, void *ws,
+                       size_t ws_bytes, void *stream) {
+  int st = check_model_cfg(c, batch, 1);
+  if (st) return st;
+  if (c->max_seq > kDecMaxSeq) return LLAMA_ERR_UNSUPPORTED;
+  if ((st = check_model_w(c, w))) return st;
+  // without a pack the skinny GEMMs read the projections themselves, as bf16
+  if (c->dtype == LLAMA_BF16 && (numerics_of(c) & LLAMA_NUM_W_F16) && !w->decode_pack) return LLAMA_ERR_UNSUPPORTED;
+  if (!tokens || !pos || !k_cache || !v_cache || !logits) return LLAMA_ERR_NULL;
+  const size_t need = ws_bytes_of(c, LLAMA_OP_MODEL_DECODE, batch, 1);
+  if (!ws || ws_bytes < need) return LLAMA_ERR_WORKSPACE;
+  const size_t seq_elems = (size_t)kv_heads(c) * c->max_seq * (c->dim / c->n_heads);   // one sequence, one layer
+  const size_t layer_elems = (size_t)batch * seq_elems;
+  for (int b0 = 0; b0 < batch; b0 += kDecChunk) {
+    const int nb = std::min(kDecChunk, batch - b0);
+    st = model_decode_chunk(c, w, tokens + b0, pos + b0, nb, (uint16_t *)k_cache + b0 * seq_elems,
+                            (uint16_t *)v_cache + b0 * seq_elems, layer_elems, logits + (size_t)b0 * c->vocab, ws,
+                            (hipStream_t)stream);
+    if (st) return st;
+  }
   return LLAMA_OK;
 }
 

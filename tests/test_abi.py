@@ -75,8 +75,12 @@ def test_workspace_size_and_validation():
     # q,k hi/lo, v^T hi/lo, attention out hi/lo (2 B each) + h f32 + u hi/lo + rope table
     assert n.value >= 2048 * 4096 * (2 * 8 + 4) + 2048 * 11008 * 4
     assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 32, 1, ctypes.byref(n)) == 0
-    assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 33, 1, ctypes.byref(n)) == \
-        L.LLAMA_ERR_UNSUPPORTED
+    n32 = n.value
+    # more than 32 sequences run in chunks of 32 that reuse one chunk's workspace
+    assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 33, 1, ctypes.byref(n)) == 0
+    assert n.value == n32
+    assert lib.llama_workspace_size(ctypes.byref(_cfg(max_seq=4096)), L.OP_MODEL_DECODE, 4, 1,
+                                    ctypes.byref(n)) == L.LLAMA_ERR_UNSUPPORTED
     assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_FORWARD, 1, 4096, ctypes.byref(n)) == \
         L.LLAMA_ERR_POSITION
     assert lib.llama_workspace_size(ctypes.byref(_cfg(dim=4001)), L.OP_BLOCK_FORWARD, 1, 8,
@@ -124,8 +128,10 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                                    1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
     assert lib.llama_model_forward(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 1, 16, FAKE, FAKE, FAKE, FAKE,
                                    16, None) == L.LLAMA_ERR_WORKSPACE
+    assert lib.llama_model_decode(ctypes.byref(_cfg(max_seq=4096)), ctypes.byref(mw), FAKE, FAKE, 4, FAKE, FAKE,
+                                  FAKE, FAKE, 1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
     assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 33, FAKE, FAKE, FAKE, FAKE,
-                                  1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
+                                  16, None) == L.LLAMA_ERR_WORKSPACE
     assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, None, 4, FAKE, FAKE, FAKE, FAKE,
                                   1 << 40, None) == L.LLAMA_ERR_NULL
     assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE,

@@ -717,6 +717,38 @@ def test_decode_ragged_positions(wid):
     assert e < TOL_DECODE_STEP
 
 
+@pytest.mark.parametrize("wid", [101, 105])
+def test_decode_batch_above_32(wid):
+    """A decode step over 40 sequences runs as chunks of 32 and 8 (the
+    skinny GEMMs carry the batch in the 32 rows of a matrix-core tile), each
+    chunk reading and appending its own sequences' caches: every sequence's
+    logits against the oracle continuing from the GPU's own cache, at ragged
+    positions."""
+    w, m, layers, gl = small_model(wid)
+    B, T = 40, 12
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    m.forward(toks[:, :T].contiguous(), kc, vc)
+    pos = np.array([T - (b % 3) for b in range(B)])
+    dec = m.decode(toks[:, T].contiguous(), torch.tensor(pos, dtype=torch.int32, device="cuda"), kc, vc)
+    torch.cuda.synchronize()
+    assert torch.isfinite(dec).all()
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    gc = [tuple(O.f64(c[l].cpu()).copy() for c in (kc, vc)) for l in range(w.n_layers)]
+    for kg, vg in gc:
+        for b in range(B):
+            kg[b, :, pos[b]:] = 0
+            vg[b, :, pos[b]:] = 0
+    want = O.model_decode(toks[:, T].cpu().numpy(), pos, emb, lambda l: (lw[l], *gc[l]), w.n_layers, fn, out,
+                          w.n_heads, w.eps)
+    e = rel_err(dec, want)
+    # the chunk past the first 32 on its own as well
+    e_tail = rel_err(dec[32:], want[32:])
+    print(f"{w.name}: decode of {B} sequences: max|d|/rms = {e:.3e} (sequences 32..39: {e_tail:.3e})")
+    assert e < TOL_DECODE_STEP and e_tail < TOL_DECODE_STEP
+
+
 def test_binding_rejects_mismatched_tensors():
     """The binding checks dtypes and shapes before any launch: an int64
     position array, a cache for another batch or max_seq, a wrong logits or
