@@ -338,7 +338,7 @@ struct DecodeWs {
   float *attn_part;   // key-range softmax states of the decode attention
 };
 
-constexpr int kDecMaxSeq = 2048;   // longest cache the decode path is validated for
+constexpr int kDecMaxSeq = kDecMaxCache;   // longest cache of the decode path
 // The skinny GEMMs carry the batch in the 32 rows of one matrix-core tile: a
 // step over more sequences runs in chunks of 32 (each chunk streams the
 // weights again).
@@ -373,7 +373,8 @@ DecodeWs carve_decode(Carve &cv, const llama_config *c, int batch) {
   w.ag_hi = cv.take<uint16_t>((size_t)batch * wmax);
   w.ag_lo = cv.take<uint16_t>((size_t)batch * wmax);
   w.rope_tab = cv.take<float2>((size_t)batch * hd / 2);
-  w.attn_part = cv.take<float>((size_t)batch * c->n_heads * kDecAttnMaxRanges * (hd + 2));
+  w.attn_part = cv.take<float>((size_t)batch * c->n_heads * kDecAttnMaxRanges * dec_attn_range_factor(c->max_seq) *
+                                (hd + 2));
   return w;
 }
 

@@ -464,7 +464,7 @@ DEV float lane_group_sum(float v) {
   return v;
 }
 
-constexpr int kMaxSeq = 2048;   // longest decode cache (positions) the attention kernel unrolls for
+constexpr int kMaxSeq = 2048;   // cache positions one set of key ranges unrolls for (longer caches: more ranges)
 
 // The new token's part of a decode attention workgroup (key/value head hk,
 // sequence b, key range rs): q of the G query heads hk*G .. hk*G+G-1, k and
@@ -535,7 +535,9 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
   __shared__ float sq[G][HD], sknew[HD], svnew[HD];
   __shared__ float gm[NG][G], gl[NG][G], snew[G];
   __shared__ float osum[NG][G][HD];
-  const int hk = blockIdx.x, b = blockIdx.y, rs = NS > 1 ? (int)blockIdx.z : 0;
+  // nr key ranges (gridDim.z): NS, or a multiple of it for caches longer
+  // than kMaxSeq, so that no range holds more than the unrolled ceil(kMaxSeq / NS) keys
+  const int hk = blockIdx.x, b = blockIdx.y, rs = blockIdx.z, nr = gridDim.z;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int p = d.pos[b];
   const bool ok = pos_ok(p, d.max_seq);
@@ -544,7 +546,7 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
   // cached keys 0..p-1 (key p is the new one); this range covers keys
   // k0 .. k0+nk-1, a multiple of KPS long except at the end
   const int nk_all = ok ? p : 0;
-  const int chunk = NS == 1 ? nk_all : ((nk_all + NS - 1) / NS + KPS - 1) / KPS * KPS;
+  const int chunk = nr == 1 ? nk_all : ((nk_all + nr - 1) / nr + KPS - 1) / KPS * KPS;
   const int k0 = min(rs * chunk, nk_all);
   const int nk = min(k0 + chunk, nk_all) - k0;
 
@@ -673,7 +675,7 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
       L += f * gl[gi][g];
       o += f * osum[gi][g][e];
     }
-    if (NS == 1) {
+    if (nr == 1) {
       const float v = ok ? o / L : __builtin_nanf("");
       u16 hi, lo;
       split_pair(v, hi, lo);
@@ -681,7 +683,7 @@ __global__ __launch_bounds__(256, HD == 128 ? 4 : 2) void dec_attn_kernel(const 
       a_hi[oo] = hi;
       a_lo[oo] = lo;
     } else {
-      float *st = opart + (((int64_t)b * d.n_heads + hk * G + g) * NS + rs) * (HD + 2);
+      float *st = opart + (((int64_t)b * d.n_heads + hk * G + g) * nr + rs) * (HD + 2);
       st[2 + e] = o;
       if (e == 0) {
         st[0] = M;
@@ -733,7 +735,9 @@ __global__ __launch_bounds__(512, 1) void dec_attn_mfma_kernel(const DecodeArgs 
   static_assert(NWV * G * HD * 4 <= (int)sizeof(vtile), "output sums fit the value tiles");
   float(*osum)[G][HD] = (float(*)[G][HD])vtile;
 
-  const int hk = blockIdx.x, b = blockIdx.y, rs = NS > 1 ? (int)blockIdx.z : 0;
+  // nr key ranges (gridDim.z): NS, or a multiple of it for caches longer
+  // than kMaxSeq, so that no range holds more than the unrolled ceil(kMaxSeq / NS) keys
+  const int hk = blockIdx.x, b = blockIdx.y, rs = blockIdx.z, nr = gridDim.z;
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int j = lane & 15, g4 = lane >> 4;   // operand column / row-block of the 16 x 16 products
   const int p = d.pos[b];
@@ -743,7 +747,7 @@ __global__ __launch_bounds__(512, 1) void dec_attn_mfma_kernel(const DecodeArgs 
   // cached keys 0..p-1: this range covers k0 .. k0+nk-1 (a multiple of NWV
   // chunks long except at the end), chunk c of it to wavefront c % NWV
   const int nk_all = ok ? p : 0;
-  const int chunk = NS == 1 ? nk_all : ((nk_all + NS - 1) / NS + NWV * CK - 1) / (NWV * CK) * (NWV * CK);
+  const int chunk = nr == 1 ? nk_all : ((nk_all + nr - 1) / nr + NWV * CK - 1) / (NWV * CK) * (NWV * CK);
   const int k0 = min(rs * chunk, nk_all);
   const int nk = min(k0 + chunk, nk_all) - k0;
   const int nch = (nk + CK - 1) / CK;
@@ -926,7 +930,7 @@ __global__ __launch_bounds__(512, 1) void dec_attn_mfma_kernel(const DecodeArgs 
       L += f * gl[gi][g];
       o += f * osum[gi][g][e];
     }
-    if (NS == 1) {
+    if (nr == 1) {
       const float v = ok ? o / L : __builtin_nanf("");
       u16 hi, lo;
       split_pair(v, hi, lo);
@@ -934,7 +938,7 @@ __global__ __launch_bounds__(512, 1) void dec_attn_mfma_kernel(const DecodeArgs 
       a_hi[oo] = hi;
       a_lo[oo] = lo;
     } else {
-      float *st = opart + (((int64_t)b * d.n_heads + hk * G + g) * NS + rs) * (HD + 2);
+      float *st = opart + (((int64_t)b * d.n_heads + hk * G + g) * nr + rs) * (HD + 2);
       st[2 + e] = o;
       if (e == 0) {
         st[0] = M;
@@ -980,15 +984,21 @@ int dec_attn_ranges(const DecodeArgs &d) {
   return ns;
 }
 
+// Key ranges per (key/value head, sequence) for a cache of max_seq
+// positions: ns (the occupancy choice) times one more per kMaxSeq positions,
+// so that a range never holds more keys than the ns-range kernel unrolls for.
+int dec_attn_range_factor(int max_seq) { return (max(max_seq, 1) + kMaxSeq - 1) / kMaxSeq; }
+
 template <int HD, int G>
 hipError_t dec_attn_launch_g(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
                              uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, int ns, hipStream_t s) {
-  dim3 grid(d.n_kv_heads, d.batch, ns);
+  const int nr = ns * dec_attn_range_factor(d.max_seq);
+  dim3 grid(d.n_kv_heads, d.batch, nr);
   switch (ns) {
     case 1:
       hipLaunchKernelGGL((dec_attn_kernel<HD, G, 1>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi,
                          a_lo, opart);
-      return hipGetLastError();
+      break;
     case 2:
       hipLaunchKernelGGL((dec_attn_kernel<HD, G, 2>), grid, dim3(256), 0, s, d, part, splits, ss, kc, vc, a_hi,
                          a_lo, opart);
@@ -1005,9 +1015,9 @@ hipError_t dec_attn_launch_g(const DecodeArgs &d, const float *part, int splits,
       return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || nr == 1) return e;
   const int n = d.batch * d.dim;
-  hipLaunchKernelGGL(dec_attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d, opart, ns, a_hi, a_lo);
+  hipLaunchKernelGGL(dec_attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d, opart, nr, a_hi, a_lo);
   return hipGetLastError();
 }
 
@@ -1025,14 +1035,14 @@ int dec_attn_mfma_ranges(const DecodeArgs &d) {
 template <int G>
 hipError_t dec_attn_mfma_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
                                 uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, hipStream_t s) {
-  const int ns = dec_attn_mfma_ranges(d);
-  if (ns > 1 && !opart) return hipErrorInvalidValue;
-  dim3 grid(d.n_kv_heads, d.batch, ns);
+  const int ns = dec_attn_mfma_ranges(d), nr = ns * dec_attn_range_factor(d.max_seq);
+  if (nr > 1 && !opart) return hipErrorInvalidValue;
+  dim3 grid(d.n_kv_heads, d.batch, nr);
   switch (ns) {
     case 1:
       hipLaunchKernelGGL((dec_attn_mfma_kernel<G, 1>), grid, dim3(512), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo,
                          opart);
-      return hipGetLastError();
+      break;
     case 2:
       hipLaunchKernelGGL((dec_attn_mfma_kernel<G, 2>), grid, dim3(512), 0, s, d, part, splits, ss, kc, vc, a_hi, a_lo,
                          opart);
@@ -1049,19 +1059,19 @@ hipError_t dec_attn_mfma_launch(const DecodeArgs &d, const float *part, int spli
       return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || nr == 1) return e;
   const int n = d.batch * d.dim;
-  hipLaunchKernelGGL(dec_attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d, opart, ns, a_hi, a_lo);
+  hipLaunchKernelGGL(dec_attn_combine_kernel, dim3((n + 255) / 256), dim3(256), 0, s, d, opart, nr, a_hi, a_lo);
   return hipGetLastError();
 }
 
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
                            uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, hipStream_t s) {
-  if (d.max_seq > kMaxSeq) return hipErrorInvalidValue;
+  if (d.max_seq > kDecMaxCache) return hipErrorInvalidValue;
   if (d.n_kv_heads <= 0 || d.n_heads % d.n_kv_heads) return hipErrorInvalidValue;
   const int group = d.n_heads / d.n_kv_heads;
   const int ns = dec_attn_ranges(d);
-  if (ns > 1 && !opart) return hipErrorInvalidValue;
+  if (ns * dec_attn_range_factor(d.max_seq) > 1 && !opart) return hipErrorInvalidValue;
   // grouped heads at head dim 128: the matrix-core kernel
   if (d.head_dim == 128 && group == 2) return dec_attn_mfma_launch<2>(d, part, splits, ss, kc, vc, a_hi, a_lo, opart, s);
   if (d.head_dim == 128 && group == 4) return dec_attn_mfma_launch<4>(d, part, splits, ss, kc, vc, a_hi, a_lo, opart, s);

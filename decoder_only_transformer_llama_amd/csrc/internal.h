@@ -232,10 +232,15 @@ hipError_t dec_embed_norm_launch(const DecodeArgs &d, const uint16_t *emb, const
                                  uint16_t *xg_lo, hipStream_t s);
 // Attention of one new token per sequence over the KV cache, fused with the
 // finish of the Q/K/V split-K partials (rstd, RoPE, cache append at pos[b]);
-// writes the head outputs as a bf16 pair [batch, dim]. max_seq <= 2048.
-// opart: [batch, n_heads, kDecAttnMaxRanges, head_dim + 2] fp32 states of the
-// key ranges (dec_attn_ranges(d) of them; unused with one range).
+// writes the head outputs as a bf16 pair [batch, dim]. max_seq <= kDecMaxCache.
+// opart: [batch, n_heads, kDecAttnMaxRanges * dec_attn_range_factor(max_seq),
+// head_dim + 2] fp32 states of the key ranges (unused with one range).
 constexpr int kDecAttnMaxRanges = 8;
+// Longest decode cache: a cache of max_seq positions takes
+// dec_attn_range_factor(max_seq) (one per 2048 positions) times the key
+// ranges, and opart room for that many.
+constexpr int kDecMaxCache = 16384;
+int dec_attn_range_factor(int max_seq);
 int dec_attn_ranges(const DecodeArgs &d);
 hipError_t dec_attn_launch(const DecodeArgs &d, const float *part, int splits, const float *ss, uint16_t *kc,
                            uint16_t *vc, uint16_t *a_hi, uint16_t *a_lo, float *opart, hipStream_t s);

@@ -265,7 +265,7 @@ int llama_model_forward(const llama_config *c, const llama_model_weights *w, con
  * final norm and head give logits [batch, vocab] f32. The caches have the
  * layout of llama_model_forward. A pos[b] outside [0, max_seq) cannot be
  * checked on the host: for such a row nothing is written to the cache and
- * its logits are NaN. max_seq <= 2048 (LLAMA_ERR_UNSUPPORTED above); any
+ * its logits are NaN. max_seq <= 16384 (LLAMA_ERR_UNSUPPORTED above); any
  * batch: more than 32 sequences run as consecutive chunks of 32 (the skinny
  * GEMMs carry the batch in one matrix-core tile's 32 rows), each chunk
  * streaming the weights again; the workspace is that of min(batch, 32).

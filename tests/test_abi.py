@@ -79,7 +79,9 @@ def test_workspace_size_and_validation():
     # more than 32 sequences run in chunks of 32 that reuse one chunk's workspace
     assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_DECODE, 33, 1, ctypes.byref(n)) == 0
     assert n.value == n32
-    assert lib.llama_workspace_size(ctypes.byref(_cfg(max_seq=4096)), L.OP_MODEL_DECODE, 4, 1,
+    # caches up to 16384 positions (more key ranges, more room for their states)
+    assert lib.llama_workspace_size(ctypes.byref(_cfg(max_seq=4096)), L.OP_MODEL_DECODE, 4, 1, ctypes.byref(n)) == 0
+    assert lib.llama_workspace_size(ctypes.byref(_cfg(max_seq=32768)), L.OP_MODEL_DECODE, 4, 1,
                                     ctypes.byref(n)) == L.LLAMA_ERR_UNSUPPORTED
     assert lib.llama_workspace_size(ctypes.byref(c), L.OP_MODEL_FORWARD, 1, 4096, ctypes.byref(n)) == \
         L.LLAMA_ERR_POSITION
@@ -128,7 +130,7 @@ def test_entry_points_reject_bad_arguments_before_any_launch():
                                    1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
     assert lib.llama_model_forward(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 1, 16, FAKE, FAKE, FAKE, FAKE,
                                    16, None) == L.LLAMA_ERR_WORKSPACE
-    assert lib.llama_model_decode(ctypes.byref(_cfg(max_seq=4096)), ctypes.byref(mw), FAKE, FAKE, 4, FAKE, FAKE,
+    assert lib.llama_model_decode(ctypes.byref(_cfg(max_seq=32768)), ctypes.byref(mw), FAKE, FAKE, 4, FAKE, FAKE,
                                   FAKE, FAKE, 1 << 40, None) == L.LLAMA_ERR_UNSUPPORTED
     assert lib.llama_model_decode(ctypes.byref(c), ctypes.byref(mw), FAKE, FAKE, 33, FAKE, FAKE, FAKE, FAKE,
                                   16, None) == L.LLAMA_ERR_WORKSPACE

@@ -7,6 +7,7 @@ attention normalises by RMS(v) instead (its output is a convex combination of
 v rows, whose own RMS shrinks with averaging). Outputs are pre-filled with NaN
 so a tile the kernels forget to write fails the comparison."""
 import ctypes
+import dataclasses
 import math
 
 import numpy as np
@@ -403,8 +404,10 @@ def test_block_row_scales(wid, numerics):
 
 
 # ---------------------------------------------------------------- model prefill + decode
-def small_model(wid=101, numerics=L.NUM_DEFAULT, n_kv_heads=None, layers=None):
+def small_model(wid=101, numerics=L.NUM_DEFAULT, n_kv_heads=None, layers=None, max_seq=None):
     w = I.workload(wid)
+    if max_seq is not None:
+        w = dataclasses.replace(w, max_seq=max_seq)
     layers = layers or [I.block_weights(w, l, device="cuda") for l in range(w.n_layers)]
     gl = I.model_globals(w, device="cuda")
     cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, n_layers=w.n_layers, vocab=w.vocab,
@@ -747,6 +750,34 @@ def test_decode_batch_above_32(wid):
     e_tail = rel_err(dec[32:], want[32:])
     print(f"{w.name}: decode of {B} sequences: max|d|/rms = {e:.3e} (sequences 32..39: {e_tail:.3e})")
     assert e < TOL_DECODE_STEP and e_tail < TOL_DECODE_STEP
+
+
+@pytest.mark.parametrize("wid", [101, 105])
+def test_decode_cache_beyond_2048(wid):
+    """A cache of 4608 positions: the decode attention runs three times the
+    key ranges (each holds no more keys than its unrolled loop covers) and
+    merges them in order. Prefill of 4400 tokens, then one step at positions
+    4400 and 3000, against the oracle continuing from the GPU's own cache."""
+    w, m, layers, gl = small_model(wid, max_seq=4608)
+    B, T = 2, 4400
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    m.forward(toks[:, :T].contiguous(), kc, vc)
+    pos = np.array([T, 3000])
+    dec = m.decode(toks[:, T].contiguous(), torch.tensor(pos, dtype=torch.int32, device="cuda"), kc, vc)
+    torch.cuda.synchronize()
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    gc = [tuple(O.f64(c[l].cpu()).copy() for c in (kc, vc)) for l in range(w.n_layers)]
+    for kg, vg in gc:
+        for b in range(B):
+            kg[b, :, pos[b]:] = 0
+            vg[b, :, pos[b]:] = 0
+    want = O.model_decode(toks[:, T].cpu().numpy(), pos, emb, lambda l: (lw[l], *gc[l]), w.n_layers, fn, out,
+                          w.n_heads, w.eps)
+    e = rel_err(dec, want)
+    print(f"{w.name}: decode with a {w.max_seq}-position cache at positions {pos.tolist()}: max|d|/rms = {e:.3e}")
+    assert e < TOL_DECODE_STEP
 
 
 def test_binding_rejects_mismatched_tensors():
