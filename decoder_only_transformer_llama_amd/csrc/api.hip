@@ -285,11 +285,14 @@ struct BlockWs {
   uint16_t *xg_hi, *xg_lo, *qh, *ql, *kh, *kl, *vth, *vtl, *a_hi, *a_lo, *u_hi, *u_lo;
   float *h, *rstd1, *rstd2;
   float *part;   // split-K partials [2][n][d] fp32: aliases qh..kl (dead after attention)
+  int *tile_flags;   // one per 256 x 128 output tile of an [n, d] product (fused split-K residual)
   // fp32 path
   float *z, *q, *k, *v, *att, *gate, *up;
 };
 
 int vt_stride_of(int seq) { return round_up(seq, 64); }
+// flags for the output tiles of an [n, d] product (256-row tiles, at least 128 wide)
+int tile_flag_count(int64_t n, int d) { return (int)(((n + 255) / 256) * ((d + 127) / 128)); }
 
 // kv_rows: key rows held per sequence (seq, or max_seq for a prefill that may
 // continue a cached prefix); the rope table covers as many positions.
@@ -318,6 +321,7 @@ BlockWs carve_block(Carve &cv, const llama_config *c, int batch, int seq, int kv
     b.h = cv.take<float>(n * d);
     b.u_hi = cv.take<uint16_t>(n * c->hidden);
     b.u_lo = cv.take<uint16_t>(n * c->hidden);
+    b.tile_flags = cv.take<int>(tile_flag_count(n, d));
   } else {
     b.z = cv.take<float>(n * d);
     b.q = cv.take<float>(n * d);
@@ -637,15 +641,37 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
 
   // post-norm: h = RMSNorm(x + attn Wo^T; g1) in place, fp32
   if (post) HIP_TRY(rmsnorm_launch(1, 1, b.h, w->attn_norm, b.h, M, d, c->norm_eps, s, 0), "attention norm");
+  // the down projection's tiling, and whether its two K ranges add the
+  // residual themselves (the ffn norm prep then clears their tile flags)
+  const ResidCfg dc = choose_resid(M, d, c->hidden, dpair);
+  GemmArgs dn{};
+  dn.M = M;
+  dn.N = d;
+  dn.K = c->hidden;
+  dn.A = b.u_hi;
+  dn.A_lo = dpair ? b.u_lo : nullptr;
+  dn.lda = c->hidden;
+  dn.b_mode = BMODE_PLAIN;
+  dn.B0 = (const uint16_t *)w->w_down;
+  dn.C = y;
+  dn.ldc = d;
+  dn.R = b.h;
+  dn.r_f32 = 1;
+  dn.k_splits = dc.splits;
+  dn.part = b.part;
+  const bool fuse_down = dc.splits == 2 && gemm_fused_split_ok(dn);
+  if (fuse_down) dn.tile_flags = b.tile_flags;
+  const int n_flags = fuse_down ? tile_flag_count(M, d) : 0;
   // z2 = RMSNorm(h; g2), operand reuses the x*g1 buffers
   const uint16_t *g2 = pre ? (const uint16_t *)w->ffn_norm : nullptr;
   if (oc.splits > 1)
     HIP_TRY(norm_prep_launch(x_dtype == LLAMA_F32, x, g2, M, d, c->norm_eps, b.rstd2, b.xg_hi,
-                             ffn_pair ? b.xg_lo : nullptr, s, b.part, oc.splits, b.h, ff16),
+                             ffn_pair ? b.xg_lo : nullptr, s, b.part, oc.splits, b.h, ff16, RopeRows{},
+                             b.tile_flags, n_flags),
             "ffn norm");
   else
     HIP_TRY(norm_prep_launch(1, b.h, g2, M, d, c->norm_eps, b.rstd2, b.xg_hi, ffn_pair ? b.xg_lo : nullptr, s,
-                             nullptr, 0, nullptr, ff16),
+                             nullptr, 0, nullptr, ff16, RopeRows{}, b.tile_flags, n_flags),
             "ffn norm");
   GemmArgs f{};
   f.M = M;
@@ -672,25 +698,10 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
     HIP_TRY(gemm_launch(fk, f, s), "gate/up projection");
   }
 
-  GemmArgs dn{};
-  dn.M = M;
-  dn.N = d;
-  dn.K = c->hidden;
-  dn.A = b.u_hi;
-  dn.A_lo = dpair ? b.u_lo : nullptr;
-  dn.lda = c->hidden;
-  dn.b_mode = BMODE_PLAIN;
-  dn.B0 = (const uint16_t *)w->w_down;
-  dn.C = y;
-  dn.ldc = d;
-  dn.R = b.h;
-  dn.r_f32 = 1;
-  const ResidCfg dc = choose_resid(M, d, c->hidden, dpair);
-  dn.k_splits = dc.splits;
-  dn.part = b.part;
   HIP_TRY(gemm_launch(GemmKey{dc.bn, dpair, dc.splits > 1 ? EPI_PARTIAL : EPI_RESID, df16 * wf}, dn, s),
           "down projection");
-  if (dc.splits > 1) HIP_TRY(resid_sum_launch(b.h, b.part, dc.splits, (int64_t)M * d, y, s), "down residual");
+  if (dc.splits > 1 && !fuse_down)
+    HIP_TRY(resid_sum_launch(b.h, b.part, dc.splits, (int64_t)M * d, y, s), "down residual");
   if (post) HIP_TRY(rmsnorm_launch(1, 1, y, w->ffn_norm, y, M, d, c->norm_eps, s, 0), "ffn norm");
   return LLAMA_OK;
 }

@@ -88,9 +88,12 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__
                                                         int64_t rows, int dim, float eps, float *__restrict__ rmul,
                                                         u16 *__restrict__ xg_hi, u16 *__restrict__ xg_lo,
                                                         const float *__restrict__ part, int n_parts,
-                                                        float *__restrict__ h_out, const RopeRows rope) {
+                                                        float *__restrict__ h_out, const RopeRows rope,
+                                                        int *__restrict__ zero, int n_zero) {
   const int lane = threadIdx.x & 63;
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i < n_zero; i += blockDim.x) zero[i] = 0;
   if (row >= rows) return;
   // table row p = row for the first rope.positions rows: the RoPE table is
   // built by this launch instead of one of its own
@@ -216,8 +219,9 @@ __global__ __launch_bounds__(256) void norm_prep_kernel(const void *__restrict__
 
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
                             float *rmul, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s, const float *part,
-                            int n_parts, float *h_out, int out_f16, RopeRows rope) {
+                            int n_parts, float *h_out, int out_f16, RopeRows rope, int *zero, int n_zero) {
   if (rows == 0) return hipSuccess;
+  if (n_zero < 0 || (n_zero > 0 && !zero)) return hipErrorInvalidValue;
   if (rope.positions > rows || (rope.positions > 0 && (!rope.tab || rope.hd <= 0))) return hipErrorInvalidValue;
   if (dim % 8) return hipErrorInvalidValue;
   const bool parts = part != nullptr && n_parts > 0;
@@ -229,7 +233,7 @@ hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_
 #define NP_CASE(F, O_, R, NC_)                                                                                    \
   if (!!in_f32 == F && out == O_ && parts == R && nc == NC_) {                                                   \
     hipLaunchKernelGGL((norm_prep_kernel<F, O_, R, NC_>), grid, dim3(256), 0, s, x, g, rows, dim, eps, rmul, xg_hi, \
-                       xg_lo, part, n_parts, h_out, rope);                                                        \
+                       xg_lo, part, n_parts, h_out, rope, zero, n_zero);                                          \
     return hipGetLastError();                                                                                   \
   }
 #define NP_CASES(NC_)                                                                                   \

@@ -154,6 +154,20 @@ DEV void interleave_loads() {
   if (NMF > NR + NLD) __builtin_amdgcn_sched_group_barrier(0x008, NMF - NR - NLD, ID);
 }
 
+// 16 bytes at byte offset off of base with device scope (cache policy sc1:
+// coherent across the XCDs' L2 caches without a cache-wide write-back or
+// invalidate), for data one workgroup hands to another within a launch.
+// base must be the same in every lane.
+constexpr int kCpolDevice = 16;   // sc1
+DEV void coherent_store16(void *base, uint32_t off, f32x4 v) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(base, 0, -1, 0x00020000);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCpolDevice);
+}
+DEV f32x4 coherent_load16(const void *base, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), 0, -1, 0x00020000);
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCpolDevice));
+}
+
 // F16 0: bf16 A (or pair) and bf16 B. F16 1: the A operand holds IEEE fp16
 // and the bf16 B fragments are converted to fp16 in registers (exactly, for
 // weights in fp16's normal range) before fp16 matrix-core products: 11-bit
@@ -669,6 +683,25 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   // lane.
   const uintptr_t base_bits = (uintptr_t)a.C | (uintptr_t)a.C_lo | (uintptr_t)a.R | (uintptr_t)a.part;
   if (EPI != EPI_SILU && a.N % 32 == 0 && a.ldc % 16 == 0 && base_bits % 16 == 0) {
+    // Split-K in two with the residual in the launch (tile_flags): range 0
+    // hands its partial to range 1 of the same tile through memory. Range 0's
+    // stores and the flag carry device scope (the sc1 cache policy), as do
+    // range 1's reads of them: they bypass the non-coherent per-XCD L2, so no
+    // cache-wide write-back or invalidate is needed. Range 1 has
+    // the higher workgroup id (blockIdx.y): every range 0 has been dispatched
+    // before it, and range 0 never waits, so the wait always ends; the spin
+    // is bounded all the same.
+    const bool fused = EPI == EPI_PARTIAL && a.tile_flags != nullptr;
+    const bool hand_over = fused && blockIdx.y == 0, take_over = fused && blockIdx.y == 1;
+    if (take_over) {
+      if (tid == 0) {
+        for (int spin = 0; spin < (1 << 24); ++spin) {
+          if (__hip_atomic_load(a.tile_flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+    }
     __builtin_amdgcn_s_barrier();  // all waves are done with the K-loop buffers
     constexpr int TQ = 40;         // row stride (floats): the two half-waves write disjoint banks
     float *tq = (float *)smem + wave * (32 * TQ);
@@ -682,12 +715,14 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
         // the residual rows of this block, loaded ahead of the transpose (the
         // fences around it would otherwise expose each load's latency);
         // rows and columns past the matrix read its first row instead
-        f32x4 res[4];
-        if (EPI == EPI_RESID) {
+        f32x4 res[4], p0[4];
+        if (EPI == EPI_RESID || take_over) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int row = rb + 8 * q + r8;
             const int64_t o = (row < a.M && col < a.N) ? (int64_t)row * a.ldc + col : 0;
+            if (take_over)   // range 0's partial of the same elements
+              p0[q] = coherent_load16(a.part, (row < a.M && col < a.N) ? (uint32_t)(row * a.N + col) * 4u : 0u);
             if (a.r_f32) {
               res[q] = *(const f32x4 *)((const float *)a.R + o);
             } else {
@@ -715,6 +750,14 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
           if (row >= a.M) continue;
           f32x4 x = v[q];
           x *= s_rstd[row - m0];
+          if (hand_over) {
+            coherent_store16(a.part, (uint32_t)(row * a.N + col) * 4u, x);
+            continue;
+          }
+          if (take_over) {   // the order of adding the ranges after the launch: (R + p0) + p1
+            *(f32x4 *)((float *)a.C + (int64_t)row * a.ldc + col) = (res[q] + p0[q]) + x;
+            continue;
+          }
           if (EPI == EPI_PARTIAL) {
             *(f32x4 *)(a.part + (int64_t)blockIdx.y * a.M * a.N + (int64_t)row * a.N + col) = x;
             continue;
@@ -732,6 +775,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
           }
         }
       }
+    }
+    if (hand_over) {
+      WAIT_VMCNT(0);     // this lane's partial has reached memory
+      __syncthreads();   // every lane's has
+      if (tid == 0) __hip_atomic_store(a.tile_flags + t, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     return;
   }
@@ -801,6 +849,8 @@ hipError_t gemm_launch_t(const GemmArgs &a, hipStream_t s) {
   const int ks = a.k_splits > 1 ? a.k_splits : 1;
   if (a.K % (G::BK * ks)) return hipErrorInvalidValue;
   if (ks > 1 && EPI != EPI_PARTIAL) return hipErrorInvalidValue;
+  if (a.tile_flags && (EPI != EPI_PARTIAL || ks != 2 || !a.R || !a.C || !gemm_fused_split_ok(a)))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_bf16_kernel<BN, APAIR, EPI, F16, BMT>), dim3(nb, ks), dim3(G::NW * 64), 0, s, a);
   return hipGetLastError();
 }

@@ -53,7 +53,21 @@ struct GemmArgs {
   // (chunk_start < 0) is computed as if it started at 0 and writes no cache.
   const int32_t *start_pos;
   int kv_rows;                   // rows per sequence of k (0: seq)
+  // EPI_PARTIAL with k_splits == 2 and tile_flags (one int per output tile,
+  // zero before the launch): range 0 stores its partial coherently and sets
+  // its tile's flag; range 1 waits for the flag, then writes
+  // C = (R + partial 0) + its own product (fp32, R fp32), the order of
+  // adding the ranges after the launch. Requires the row-contiguous epilogue
+  // (gemm_fused_split_ok).
+  int *tile_flags;
 };
+// The layouts the fused split-K residual runs with (those of the GEMM's
+// row-contiguous epilogue): N % 32 == 0, ldc % 16 == 0, 16-byte aligned
+// C, C_lo, R and part, and a partial below 4 GiB (32-bit buffer offsets).
+inline bool gemm_fused_split_ok(const GemmArgs &a) {
+  return a.N % 32 == 0 && a.ldc % 16 == 0 && (int64_t)a.M * a.N < (int64_t(1) << 30) &&   // 32-bit byte offsets
+         (((uintptr_t)a.C | (uintptr_t)a.C_lo | (uintptr_t)a.R | (uintptr_t)a.part) % 16) == 0;
+}
 
 // Position of the first token of sequence b's chunk of `seq` tokens:
 // start_pos[b] when 0 <= start_pos[b] and start_pos[b] + seq <= max_seq, -1
@@ -145,10 +159,12 @@ struct RopeRows {
   int positions = 0, hd = 0;
   double theta = 0.0;
 };
+// zero / n_zero: ints the launch also clears (flags a later kernel of the
+// same stream counts on starting at zero).
 hipError_t norm_prep_launch(int in_f32, const void *x, const uint16_t *g, int64_t rows, int dim, float eps,
                             float *rmul, uint16_t *xg_hi, uint16_t *xg_lo, hipStream_t s,
                             const float *part = nullptr, int n_parts = 0, float *h_out = nullptr,
-                            int out_f16 = 0, RopeRows rope = RopeRows{});
+                            int out_f16 = 0, RopeRows rope = RopeRows{}, int *zero = nullptr, int n_zero = 0);
 // Index of the largest logit per row (lowest among equals; -1 if the row has a NaN).
 hipError_t argmax_launch(const float *logits, int64_t rows, int vocab, int32_t *out, hipStream_t s);
 // y = r + part[0] + ... + part[n_parts-1], fp32, n elements (n % 4 == 0).

@@ -231,6 +231,33 @@ def test_block_small(wid):
     assert err < tol_of(w)
 
 
+@pytest.mark.parametrize("wid", [100, 103])
+def test_block_workspace_reuse_new_input(wid):
+    """Two calls of one block object (one workspace) on different inputs, the
+    second against the oracle. The down projection splits K in two and its
+    second range adds the first range's partial, read from memory it shares
+    with the other range's workgroup: a read served from a stale cache line
+    would hand over the first call's (or the attention's) values, which the
+    second call's oracle comparison sees."""
+    w = I.workload(wid)
+    wt = I.block_weights(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
+                       n_kv_heads=w.n_kv_heads)
+    blk = ops().Block(cfg, wt, w.batch, w.seq)
+    x1 = I.block_input(w, device="cuda")
+    x2 = (-0.5 * x1.float() + 0.25).to(x1.dtype)
+    y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
+    blk(x1, y)
+    y1 = y.clone()
+    blk(x2, y)
+    torch.cuda.synchronize()
+    hw = {k: host(v) for k, v in wt.items()}
+    e1 = rel_err(y1, O.block_forward(host(x1), hw, w.batch, w.seq, w.n_heads, w.eps, w.theta))
+    e2 = rel_err(y, O.block_forward(host(x2), hw, w.batch, w.seq, w.n_heads, w.eps, w.theta))
+    print(f"block {w.name}: first input {e1:.3e}, second input on the same workspace {e2:.3e}")
+    assert e1 < tol_of(w) and e2 < tol_of(w)
+
+
 @pytest.mark.parametrize("wid", [100, 103, 104])
 def test_block_all_pairs(wid):
     """Within the bound, and closer than with every operand a single bf16
