@@ -1122,6 +1122,43 @@ def test_block_hip_graph_replays_match_eager():
         assert not torch.equal(other, eager)
 
 
+def test_block_hip_graph_replays_match_eager():
+    """A block call captured in a HIP graph (its down projection hands the
+    first K range's partial to the second through per-tile flags that the
+    ffn norm prep clears in the same call): three replays, with eager calls
+    of the same block object on another input between them; every replay's
+    output is bitwise the eager call's."""
+    w = I.workload(100)
+    wt = I.block_weights(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta,
+                       n_kv_heads=w.n_kv_heads)
+    blk = ops().Block(cfg, wt, w.batch, w.seq)
+    x = I.block_input(w, device="cuda")
+    x_other = (0.5 * x.float() - 0.1).to(x.dtype)
+    y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
+    blk(x, y)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        blk(x, y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        blk(x, y)
+    y_other = torch.empty_like(y)
+    for i in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), i
+        blk(x_other, y_other)   # eager work on the same workspace between replays
+        torch.cuda.synchronize()
+        assert not torch.equal(y_other, eager)
+
+
 def test_decode_hip_graph_replays_match_eager():
     """A decode step captured in a HIP graph: three replays, each rewriting the
     same cache slot, with an eager decode on other caches (same workspace)
