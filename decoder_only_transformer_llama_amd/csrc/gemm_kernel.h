@@ -690,9 +690,11 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
     // cache-wide write-back or invalidate is needed. Range 1 has
     // the higher workgroup id (blockIdx.y): every range 0 has been dispatched
     // before it, and range 0 never waits, so the wait always ends; the spin
-    // is bounded all the same.
+    // is bounded all the same, and a tile whose partial never arrived is
+    // written as NaN rather than as a wrong sum.
     const bool fused = EPI == EPI_PARTIAL && a.tile_flags != nullptr;
     const bool hand_over = fused && blockIdx.y == 0, take_over = fused && blockIdx.y == 1;
+    bool handed = true;   // range 1: range 0's partial arrived (else the tile is written as NaN)
     if (take_over) {
       if (tid == 0) {
         for (int spin = 0; spin < (1 << 24); ++spin) {
@@ -701,6 +703,7 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
         }
       }
       __syncthreads();
+      handed = __hip_atomic_load(a.tile_flags + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
     }
     __builtin_amdgcn_s_barrier();  // all waves are done with the K-loop buffers
     constexpr int TQ = 40;         // row stride (floats): the two half-waves write disjoint banks
@@ -755,7 +758,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
             continue;
           }
           if (take_over) {   // the order of adding the ranges after the launch: (R + p0) + p1
-            *(f32x4 *)((float *)a.C + (int64_t)row * a.ldc + col) = (res[q] + p0[q]) + x;
+            const f32x4 yv = (res[q] + p0[q]) + x;
+            *(f32x4 *)((float *)a.C + (int64_t)row * a.ldc + col) = handed ? yv : f32x4{NAN, NAN, NAN, NAN};
             continue;
           }
           if (EPI == EPI_PARTIAL) {
