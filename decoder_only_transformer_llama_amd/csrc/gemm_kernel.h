@@ -307,23 +307,36 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   struct Frag {
     u32x4 a[G::TM], al[APAIR ? G::TM : 1], b[G::TN];   // raw bits: bf16, or fp16 per F16
   };
-  auto read_frag = [&](Frag &f, int kt, int ks) {
-    const u32x4 *sa = a_stage(kt);
-    const u32x4 *sal = sa + G::A_TILE;
-    const u32x4 *sb = b_stage(kt);
-    const int c = ks * 2 + g;
+  // A fragment's place in a stage is a lane part plus its 32-row block: the
+  // swizzle of row r depends on r mod 32 only (block and wavefront offsets
+  // are multiples of 32), so each 16-deep substep has one loop-invariant lane
+  // offset per operand, and the blocks are constant offsets from it. Per K
+  // step that leaves one address add per substep and operand (vector-ALU
+  // time adds to the matrix cores' on gfx950).
+  constexpr int NS = BK / 16;
+  uint32_t lane_a[NS], lane_b[NS];   // byte offsets within a stage
 #pragma unroll
-    for (int j = 0; j < G::TN; ++j) {
-      const int r = wn * G::WN + j * 32 + l32;
-      f.b[j] = sb[r * CH + (c ^ swz<CH>(r))];   // converted at use (F16 1), not here: the
-                                                  // LDS wait then stays next to the MFMAs
-    }
+  for (int ks = 0; ks < NS; ++ks) {
+    const int sw = (ks * 2 + g) ^ swz<CH>(l32);
+    lane_a[ks] = (uint32_t)(((wm * G::WM + l32) * CH + sw) * 16);
+    lane_b[ks] = (uint32_t)(((wn * G::WN + l32) * CH + sw) * 16);
+  }
+  constexpr int BLOCK_BYTES = 32 * CH * 16;   // one 32-row block of a stage
+  auto read_frag = [&](Frag &f, int kt, int ks) {
+    // the stages' byte offsets as scalars the compiler cannot fold into the
+    // lane offsets (it would keep one strength-reduced address per read)
+    const int ao = __builtin_amdgcn_readfirstlane((int)((const char *)a_stage(kt) - (const char *)smem));
+    const int bo = __builtin_amdgcn_readfirstlane((int)((const char *)b_stage(kt) - (const char *)smem));
+    const char *sa = (const char *)smem + ao + lane_a[ks];
+    const char *sb = (const char *)smem + bo + lane_b[ks];
+#pragma unroll
+    for (int j = 0; j < G::TN; ++j)
+      f.b[j] = *(const u32x4 *)(sb + j * BLOCK_BYTES);   // converted at use (F16 1), not here: the
+                                                          // LDS wait then stays next to the MFMAs
 #pragma unroll
     for (int i = 0; i < G::TM; ++i) {
-      const int r = wm * G::WM + i * 32 + l32;
-      const int off = r * CH + (c ^ swz<CH>(r));
-      f.a[i] = sa[off];
-      if (APAIR) f.al[i] = sal[off];
+      f.a[i] = *(const u32x4 *)(sa + i * BLOCK_BYTES);
+      if (APAIR) f.al[i] = *(const u32x4 *)(sa + G::A_TILE * 16 + i * BLOCK_BYTES);
     }
   };
   auto mma = [&](const Frag &f) {
@@ -352,7 +365,6 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
   // The buffer refilled at step kt held stage kt-1; every wavefront drained its
   // reads of it before the previous barrier. Loads past the last step re-read
   // the last step into buffers nobody reads, so the body has no branches.
-  constexpr int NS = BK / 16;
   static_assert(NS % 2 == 0, "the last substep's fragments are f[1]");
   // row statistic of tile row tid: loaded ahead of the prologue's tile loads,
   // so that waiting for it below overlaps them
