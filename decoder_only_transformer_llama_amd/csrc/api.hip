@@ -564,6 +564,10 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   q.vtl = b.vtl;
   q.rope_tab = b.rope_tab;
   q.attn_f16 = af16;
+  // fp16 attention operands: q leaves the epilogue already scaled by the
+  // attention's log2(e)/sqrt(hd), one fp16 rounding of the scaled value
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  q.q_mul = af16 ? scale_log2 : 0.f;
   q.seq = seq;
   q.n_heads = H;
   q.head_dim = hd;
@@ -610,7 +614,8 @@ int block_bf16(const llama_config *c, const llama_block_weights *w, int x_dtype,
   at.kv_dim = kvd;
   at.n_kv_heads = nkv;
   at.vt_stride = vts;
-  at.scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  at.scale_log2 = scale_log2;
+  at.q_scaled = af16;
   at.start_pos = start_pos;
   at.kv_rows = kv_rows;
   at.max_seq = max_seq;

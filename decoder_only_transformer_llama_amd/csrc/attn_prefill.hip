@@ -11,7 +11,8 @@
 // holds after the S^T product are exactly the eight consecutive keys it must
 // supply as the P^T operand of the next product: no register shuffles.
 //
-// Softmax is online in fp32 with exp2 and a log2(e)/sqrt(hd) prescale; masked
+// Softmax is online in fp32 with exp2 and a log2(e)/sqrt(hd) prescale (with
+// fp16 operands folded into q by the QKV epilogue); masked
 // keys get exactly zero weight; tiles entirely above the diagonal are never
 // loaded and fully masked 32-key halves are skipped per wavefront. Operands are
 // either bf16 (q/k and v optionally as hi/lo pairs: 3 and 2 matrix-core
@@ -21,6 +22,8 @@
 // Attention itself is the 2017 scaled-dot-product attention with a causal mask
 // (paperfordummies.in LLaMA page, "LLaMA is a pull request against the 2017
 // transformer": the attention is untouched; RoPE is applied to q and k before).
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -147,19 +150,35 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       ldst[qb] = KTILE * (QKPAIR ? 2 : 1) + part * VTILE + vb * 64;
     }
   }
-  auto issue = [&](int st_slot) {
+  // fp16 operands: a block's source offset is a lane part that stays fixed
+  // plus a scalar part per 32-key tile (K rows step kvd elements per key, v^T
+  // columns one), so a tile's loads take no vector arithmetic and no branch
+  // per block. Otherwise, and for a tile that runs past the last key, the
+  // offset is formed per lane, and K rows past the last key load that key
+  // instead (masked later).
+  uint32_t lvo[NQB], sst[NQB];
+#pragma unroll
+  for (int qb = 0; qb < NQB; ++qb) {
+    lvo[qb] = loff[qb] + (isk[qb] ? (uint32_t)(lrow[qb] * kvd * 2) : 0u);
+    sst[qb] = isk[qb] ? (uint32_t)(KT * kvd * 2) : (uint32_t)(KT * 2);
+  }
+  auto issue = [&](int st_slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       u32x4 *st = smem + (st_slot % NST) * STAGE + u * STAGE1;
       const int kt = min(st_slot * SUB + u, n_kt - 1);
+      if (F16 && kt * KT + KT <= nkeys) {   // (the bf16 pair forms lack the registers)
 #pragma unroll
-      for (int qb = 0; qb < NQB; ++qb) {
-        // K row: rows past the last key load a valid key (masked later); v^T: key columns
-        if (isk[qb])
-          buf_load_lds16(lbase[qb], loff[qb] + (uint32_t)(min(kt * KT + lrow[qb], nkeys - 1) * kvd * 2), 0,
-                         st + ldst[qb]);
-        else
-          buf_load_lds16(lbase[qb], loff[qb], (uint32_t)(kt * KT * 2), st + ldst[qb]);
+        for (int qb = 0; qb < NQB; ++qb) buf_load_lds16(lbase[qb], lvo[qb], (uint32_t)kt * sst[qb], st + ldst[qb]);
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < NQB; ++qb) {
+          if (isk[qb])
+            buf_load_lds16(lbase[qb], loff[qb] + (uint32_t)(min(kt * KT + lrow[qb], nkeys - 1) * kvd * 2), 0,
+                           st + ldst[qb]);
+          else
+            buf_load_lds16(lbase[qb], loff[qb], (uint32_t)(kt * KT * 2), st + ldst[qb]);
+        }
       }
     }
   };
@@ -177,13 +196,24 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     }
   }
 
+  const float c = a.scale_log2;
+  // fp16 operands: q arrives multiplied by c = log2(e)/sqrt(hd) (the QKV
+  // epilogue folds it in before its one fp16 rounding), so the score products
+  // come out in log2 units, and the running maximum (same units) is taken
+  // off by starting the score accumulators at -m: a key's exponent is then
+  // its accumulator as it stands.
+  f32x16 negm;
+  if constexpr (F16) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) negm[r] = 0.f;
+  }
   f32x16 acc_o[NEB];
 #pragma unroll
   for (int e = 0; e < NEB; ++e)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc_o[e][r] = 0.f;
+  // running maximum: of s*c with fp16 operands, of s with bf16 operands
   float m_run = -INFINITY, l_run = 0.f;
-  const float c = a.scale_log2;
   const int krow = perm23(l32);   // key (within the tile) this lane supplies as A-operand row
   for (int st = 1; st < NST - 1; ++st) issue(st);   // after the q fragments: they complete first
 
@@ -193,7 +223,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
   // two tiles' score chains alternate on the matrix cores, the v^T fragments
   // are read while the softmax runs, and the second tile's exponentials are
   // computed while the first tile's P^T products run.
-  auto f16_step = [&](const u32x4 *stg, int s0) {
+  auto f16_step = [&](const u32x4 *stg, int s0) __attribute__((always_inline)) {
     u32x4 kf[SUB][NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -201,13 +231,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
 #pragma unroll
       for (int u = 0; u < SUB; ++u) kf[u][kk] = stg[u * STAGE1 + so];
     }
+    // scores s*c - m (log2 units, relative to the running maximum)
     f32x16 sc[SUB];
 #pragma unroll
-    for (int u = 0; u < SUB; ++u)
+    for (int u = 0; u < SUB; ++u) sc[u] = mfma32h(as_f16x8(kf[u][0]), as_f16x8(qh[0]), negm);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[u][r] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
+    for (int kk = 1; kk < NKK; ++kk)
 #pragma unroll
       for (int u = 0; u < SUB; ++u) sc[u] = mfma32h(as_f16x8(kf[u][kk]), as_f16x8(qh[kk]), sc[u]);
     // every K fragment read ahead of the first product (left alone, the
@@ -251,26 +280,35 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
       mx = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
     }
-    // lazy rescaling, as below for bf16 operands
-    if (!__all((mx - m_run) * c <= kLazyRescale)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = __builtin_amdgcn_exp2f((m_run - (m_new == -INFINITY ? 0.f : m_new)) * c);   // -inf -> 0
+    // lazy rescaling, as below for bf16 operands; mx is already relative to
+    // the maximum the accumulators started from (0 while m_run = -inf, which
+    // always takes the update)
+    if (!__all(m_run > -INFINITY && mx <= kLazyRescale)) {
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
+      const float m_new = fmaxf(m_run, mx + m_use);
+      const float m_new_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new_use);   // -inf -> 0
+      const float d = m_use - m_new_use;
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
       for (int e = 0; e < NEB; ++e)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[e][r] *= alpha;
+#pragma unroll
+      for (int u = 0; u < SUB; ++u)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[u][r] += d;   // masked keys stay -inf
+#pragma unroll
+      for (int r = 0; r < 16; ++r) negm[r] = -m_new_use;
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    const float mc = -m_use * c;   // exponent (s - m) c as one fma: s c - m c
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
       float pr[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        pr[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][r], c, mc));   // exp2(-inf) = 0 for masked keys
+        pr[r] = __builtin_amdgcn_exp2f(sc[u][r]);   // exp2(-inf) = 0 for masked keys
         ps[r & 3] += pr[r];
       }
 #pragma unroll
@@ -283,21 +321,37 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(const AttnArgs a) 
     l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
   };
 
-  for (int step = 0; step < n_st; ++step) {
-    ATT_WAIT_VMCNT((NST - 2) * SUB * (NBLK / 4));   // this wavefront's loads of this step (and the q fragments)
-    __builtin_amdgcn_s_barrier();                   // everyone's; everyone is done with the previous step
+  // Waits for this wavefront's loads of `step` (and the q fragments), then
+  // for everyone's at the barrier (everyone is then done with the previous
+  // step), and issues the loads of a later step.
+  auto step_begin = [&](int step) __attribute__((always_inline)) {
+    ATT_WAIT_VMCNT((NST - 2) * SUB * (NBLK / 4));
+    __builtin_amdgcn_s_barrier();
     if (NST == 2) {
-      if (step + 1 < n_st) issue(step + 1);         // overwrites the buffer of the previous step
+      if (step + 1 < n_st) issue(step + 1);   // overwrites the buffer of the previous step
     } else {
       issue(step + NST - 1);
     }
+  };
+  if constexpr (F16) {
+    // Steps in pairs, so that each one's ring slot is a constant and the
+    // fragment reads take it as an instruction offset (no address arithmetic).
+    static_assert(NST == 2, "the step pairs alternate two ring slots");
+    auto f16_iter = [&](auto slot, int step) __attribute__((always_inline)) {
+      step_begin(step);
+      const int s0 = step * SUB * KT;
+      if (s0 > p0 + qwave_max) return;   // whole step above this wavefront's diagonal
+      f16_step(smem + decltype(slot)::value * STAGE, s0);
+    };
+    for (int step = 0; step < n_st; step += 2) {
+      f16_iter(std::integral_constant<int, 0>{}, step);
+      if (step + 1 < n_st) f16_iter(std::integral_constant<int, 1>{}, step + 1);
+    }
+  }
+  for (int step = 0; !F16 && step < n_st; ++step) {
+    step_begin(step);
     const int s0 = step * SUB * KT;
     if (s0 > p0 + qwave_max) continue;   // whole step above this wavefront's diagonal
-
-    if constexpr (F16) {
-      f16_step(smem + (step % NST) * STAGE, s0);
-      continue;
-    }
     // ---- bf16 operands, one tile per step. Scores S^T (32 keys x 32
     // queries): two accumulators (even and odd k-steps) so that two dependent
     // matrix-core chains of half the length run interleaved.
@@ -530,7 +584,7 @@ static hipError_t launch_t(const AttnArgs &a, hipStream_t s) {
 }
 
 hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, int f16, hipStream_t s) {
-  if (f16 && (qk_pair || v_pair)) return hipErrorInvalidValue;
+  if (f16 && (qk_pair || v_pair || !a.q_scaled)) return hipErrorInvalidValue;
   if (a.batch * a.seq == 0) return hipSuccess;
   if (a.start_pos && (a.kv_rows < a.seq || a.max_seq > a.kv_rows || a.vt_stride < a.kv_rows))
     return hipErrorInvalidValue;

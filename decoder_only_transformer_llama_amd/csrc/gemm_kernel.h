@@ -563,7 +563,8 @@ __global__ __launch_bounds__(kGemmWaves * 64, 1) void gemm_bf16_kernel(const Gem
       const int b = ok ? row / a.seq : 0;
       const int cs = ok ? chunk_start(a.start_pos, b, a.seq, a.max_seq) : 0;
       const int s = ok ? row - b * a.seq + max(cs, 0) : 0;   // the row's position
-      const float sc = s_rstd[min(row, a.M - 1) - m0];
+      // rstd, and for fp16 q the attention's score scale (a rotation commutes with it)
+      const float sc = s_rstd[min(row, a.M - 1) - m0] * (seg == 0 && a.q_mul != 0.f ? a.q_mul : 1.f);
       const float2 *tab = a.rope_tab + (int64_t)s * (a.head_dim >> 1);
       // k row: by position within the sequence's kv_rows when continuing a prefix
       const int64_t krow = a.start_pos ? (int64_t)b * a.kv_rows + s : row;

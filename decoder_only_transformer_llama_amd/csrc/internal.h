@@ -40,6 +40,8 @@ struct GemmArgs {
   uint16_t *qh, *ql, *kh, *kl;   // [M, dim] hi/lo of rotated q and k
   uint16_t *vth, *vtl;           // [batch, n_heads, head_dim, vt_stride] hi/lo of v (transposed)
   int attn_f16;                  // 1: qh, kh, vth hold fp16 (no lo parts written)
+  float q_mul;                   // with attn_f16: q is written times this factor (the
+                                 // attention's log2(e)/sqrt(head_dim)); 0 = none
   const float2 *rope_tab;        // [seq, head_dim/2] (cos, sin)
   int seq, n_heads, head_dim, dim;
   int kv_dim, n_kv_heads;        // width and heads of k and v (0: dim, n_heads)
@@ -113,6 +115,7 @@ struct AttnArgs {
   int kv_dim, n_kv_heads;              // k rows [batch*seq, kv_dim]; v^T [batch, n_kv_heads, head_dim, vt_stride]
   int vt_stride;                       // row stride of v^T (>= keys per sequence, multiple of 64)
   float scale_log2;                    // log2(e) / sqrt(head_dim)
+  int q_scaled;                        // q already carries scale_log2 (required with fp16 operands)
   // With start_pos, sequence b's queries are positions p0 .. p0+seq-1
   // (p0 = chunk_start(start_pos, b, seq, max_seq), 0 when negative) and its
   // keys are positions 0 .. p0+seq-1: k rows b * kv_rows + position, v^T
@@ -121,8 +124,9 @@ struct AttnArgs {
   int kv_rows;                         // rows per sequence of k (0: seq)
   int max_seq;
 };
-// f16: q, k, v^T hold IEEE fp16 (single, no lo parts) and the probabilities
-// are rounded to fp16; otherwise bf16 with optional hi/lo pairs.
+// f16: q, k, v^T hold IEEE fp16 (single, no lo parts), q already multiplied
+// by scale_log2 (q_scaled = 1, else hipErrorInvalidValue), and the
+// probabilities are rounded to fp16; otherwise bf16 with optional hi/lo pairs.
 hipError_t attn_prefill_launch(const AttnArgs &a, int qk_pair, int v_pair, int f16, hipStream_t s);
 // The cached prefix of a prefill chunk in the attention's operand layout: for
 // every sequence b with p0 = chunk_start(...) > 0, cache positions 0..p0-1 of
