@@ -231,6 +231,43 @@ def test_block_small(wid):
     assert err < tol_of(w)
 
 
+# Peaked attention over a long sequence: wq and wk scaled by 4.5 (scores up
+# to ~37 in log2 units) and wo by 6 (the attention branch's RMS is then about
+# 2/3 of x's, so its errors are not hidden under the residual), 4096 positions. In the fp16-operand
+# attention the running maximum of a query then moves by more than the lazy
+# rescale's 8 log2 units after its first 64 keys for a good share of the
+# queries, so the rescale path (O and l scaled, the score accumulators
+# shifted to the new maximum) runs many times per wavefront; the premise is
+# checked on the oracle's own q and k.
+def test_block_long_sequence_peaked_attention():
+    w = dataclasses.replace(I.workload(100), batch=1, seq=4096)
+    wt = I.block_weights(w, device="cuda")
+    for name, f in (("wq", 4.5), ("wk", 4.5), ("wo", 6.0)):
+        wt[name] = (wt[name].float() * f).to(wt[name].dtype)
+    x = I.block_input(w, device="cuda")
+    cfg = ops().config(w.dim, w.n_heads, w.hidden, dtype=w.torch_dtype, eps=w.eps, theta=w.theta)
+    y = torch.full((w.tokens, w.dim), float("nan"), device="cuda")
+    ops().Block(cfg, wt, w.batch, w.seq)(x, y)
+    torch.cuda.synchronize()
+    xh = host(x)
+    want, parts = O.block_forward(xh, {k: host(v) for k, v in wt.items()}, w.batch, w.seq, w.n_heads, w.eps,
+                                  w.theta, return_parts=True)
+    hd = w.head_dim
+    growth = []
+    for h in range(w.n_heads):
+        qs, ks = parts["q"][64::16, h * hd:(h + 1) * hd], parts["k"][:, h * hd:(h + 1) * hd]
+        sc = qs @ ks.T / math.sqrt(hd) * math.log2(math.e)
+        for r, i in enumerate(range(64, w.seq, 16)):
+            growth.append(sc[r, :i + 1].max() - sc[r, :64].max())
+    frac = float(np.mean(np.array(growth) > 8.0))
+    branch = float(np.sqrt(np.mean((parts["h"] - xh) ** 2)) / np.sqrt(np.mean(xh ** 2)))
+    err = rel_err(y, want)
+    print(f"peaked attention, seq {w.seq}: max|d|/rms = {err:.3e}; queries whose maximum grows past the lazy "
+          f"bound {frac:.2f}; attention branch / x = {branch:.2f}")
+    assert frac > 0.2 and branch > 0.5
+    assert err < TOL_BF16
+
+
 @pytest.mark.parametrize("wid", [100, 103])
 def test_block_workspace_reuse_new_input(wid):
     """Two calls of one block object (one workspace) on different inputs, the
