@@ -176,6 +176,29 @@ def test_causal_attn_bf16(B, S, H, hd):
         np.testing.assert_allclose(o[b * S].numpy(), host(v)[b * S], rtol=0, atol=2e-2)
 
 
+@pytest.mark.parametrize("S,hd", [(4096, 128), (1000, 64)])
+def test_causal_attn_bf16_peaked(S, hd):
+    """q times 8 (exact in bf16): scores ~N(0, 64), so a query's running
+    maximum keeps growing past the lazy-rescale bound (8 in log2 units) as
+    keys arrive and O, l and the reference maximum are rescaled many times;
+    the premise is counted on the inputs."""
+    w = I.Workload(906, "attn-peaked", dim=2 * hd, n_heads=2, hidden=0, batch=1, seq=S, dtype="bf16")
+    q, k, v = I.qkv_inputs(w, device="cuda")
+    q = q * 8
+    qh, kh = host(q), host(k)
+    growth = []
+    for h in range(2):
+        sc = qh[32::8, h * hd:(h + 1) * hd] @ kh[:, h * hd:(h + 1) * hd].T / math.sqrt(hd) * math.log2(math.e)
+        for r, i in enumerate(range(32, S, 8)):
+            growth.append(sc[r, :i + 1].max() - sc[r, :32].max())
+    assert float(np.mean(np.array(growth) > 8.0)) > 0.2
+    o = ops().causal_attn(q, k, v, 1, S, 2)
+    want = O.causal_attention(qh, kh, host(v), 1, S, 2)
+    err = rel_err(o, want, scale=float(np.sqrt(np.mean(host(v) ** 2))))
+    print(f"peaked causal attention S {S} hd {hd}: max|d|/rms(v) = {err:.3e}")
+    assert err < TOL_BF16
+
+
 @pytest.mark.parametrize("B,S,H,hd", [(2, 70, 2, 64), (1, 300, 2, 128), (1, 1, 1, 128), (3, 33, 1, 64),
                                      (1, 257, 1, 128)])
 def test_causal_attn_f32(B, S, H, hd):
