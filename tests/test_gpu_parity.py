@@ -867,6 +867,48 @@ def test_decode_cache_beyond_2048(wid):
     assert e < TOL_DECODE_STEP
 
 
+@pytest.mark.parametrize("wid", [101, 105])
+def test_decode_peaked_cache(wid):
+    """The decode attention's lazy rescale under peaked scores: after a
+    1500-token prefill every cached key is multiplied by 128 (exact in bf16),
+    so the scores over the cache spread 128x wider and a head's running
+    maximum keeps growing past the lazy bound (8 in log2 units) as its keys
+    stream in. One step at positions 1500 and 1200 against the oracle
+    continuing from the same cache; the premise is counted for layer 0 from
+    the oracle's own q."""
+    w, m, layers, gl = small_model(wid, max_seq=2048)
+    B, T = 2, 1500
+    toks = I.tokens(w, (B, T + 1), device="cuda")
+    kc, vc = m.new_cache(B, "cuda"), m.new_cache(B, "cuda")
+    m.forward(toks[:, :T].contiguous(), kc, vc)
+    kc.mul_(128)
+    pos = np.array([T, 1200])
+    dec = m.decode(toks[:, T].contiguous(), torch.tensor(pos, dtype=torch.int32, device="cuda"), kc, vc)
+    torch.cuda.synchronize()
+    lw = [{k: host(v) for k, v in lay.items()} for lay in layers]
+    emb, fn, out = host(gl["tok_embeddings"]), host(gl["final_norm"]), host(gl["output"])
+    gc = [tuple(O.f64(c[l].cpu()).copy() for c in (kc, vc)) for l in range(w.n_layers)]
+    for kg, vg in gc:
+        for b in range(B):
+            kg[b, :, pos[b]:] = 0
+            vg[b, :, pos[b]:] = 0
+    # premise, layer 0: q of the new tokens against the scaled cached keys
+    hd, tok = w.head_dim, toks[:, T].cpu().numpy()
+    q = O.rope(O.linear(O.rmsnorm(emb[tok], lw[0]["attn_norm"], w.eps), lw[0]["wq"]), pos, hd, w.theta)
+    grow = []
+    for b in range(B):
+        for h in range(w.n_heads):
+            kk = gc[0][0][b, h // (w.n_heads // w.kv_heads), :pos[b]]
+            sc = kk @ q[b, h * hd:(h + 1) * hd] / math.sqrt(hd) * math.log2(math.e)
+            grow.append(sc.max() - sc[:64].max())
+    assert float(np.mean(np.array(grow) > 8.0)) >= 0.5, grow
+    want = O.model_decode(tok, pos, emb, lambda l: (lw[l], *gc[l]), w.n_layers, fn, out, w.n_heads, w.eps)
+    e = rel_err(dec, want)
+    print(f"{w.name}: decode over a cache of keys x 128 at positions {pos.tolist()}: max|d|/rms = {e:.3e}; "
+          f"growth past the lazy bound in {np.mean(np.array(grow) > 8.0):.2f} of the layer-0 heads")
+    assert e < TOL_DECODE_STEP
+
+
 def test_binding_rejects_mismatched_tensors():
     """The binding checks dtypes and shapes before any launch: an int64
     position array, a cache for another batch or max_seq, a wrong logits or
